@@ -1,0 +1,100 @@
+"""fp64 CPU oracle for masked multi-head attention forward -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
+import this package. The product path (``scaled_dot_product_fwd_amd``) never imports it and
+shares no code with it.
+
+The arithmetic lives in ``attn_oracle.c`` (plain C, IEEE double, OpenMP over independent query
+rows); this module only builds that file with gcc and marshals numpy arrays into it. The C file's
+header states the definition it follows and the page passages it cites.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "attn_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(src: str = _SRC, out: str = _LIB_PATH) -> str:
+    """Compile the oracle with gcc (no fast-math: IEEE double semantics are the point)."""
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", src, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def load(path: str = _LIB_PATH) -> ctypes.CDLL:
+    lib = ctypes.CDLL(path)
+    f = lib.oracle_attn_fwd
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 5 + [
+        ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+        ctypes.c_int]
+    lib.oracle_max_threads.restype = ctypes.c_int
+    return lib
+
+
+def _get_lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or (
+                os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
+            build()
+        _lib = load()
+    return _lib
+
+
+def max_threads() -> int:
+    return int(_get_lib().oracle_max_threads())
+
+
+def attn_fwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal: bool,
+             valid_len: Optional[np.ndarray] = None, rows: Optional[np.ndarray] = None,
+             threads: int = 0, lib: Optional[ctypes.CDLL] = None
+             ) -> Tuple[np.ndarray, np.ndarray]:
+    """Attention forward in fp64.
+
+    q: [B,Hq,N,D] float64, k/v: [B,Hkv,N,D] float64, valid_len: int32[B] or None.
+    rows: optional int64 flat row indices (b*Hq + hq)*N + i; when given the outputs are
+    [len(rows), D] and [len(rows)], else [B,Hq,N,D] and [B,Hq,N].
+    Returns (O, LSE) as float64; LSE is the natural-log log-sum-exp (-inf for an empty row).
+    """
+    lib = lib or _get_lib()
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    B, Hq, N, D = q.shape
+    Bk, Hkv, Nk, Dk = k.shape
+    if (Bk, Nk, Dk) != (B, N, D) or v.shape != k.shape:
+        raise ValueError("shape mismatch: q %s k %s v %s" % (q.shape, k.shape, v.shape))
+    vl_ptr = None
+    if valid_len is not None:
+        valid_len = np.ascontiguousarray(valid_len, dtype=np.int32)
+        if valid_len.shape != (B,):
+            raise ValueError("valid_len must have shape [B]")
+        vl_ptr = valid_len.ctypes.data
+    if rows is None:
+        out = np.empty((B, Hq, N, D), np.float64)
+        lse = np.empty((B, Hq, N), np.float64)
+        rows_ptr, nrows = None, B * Hq * N
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        nrows = rows.shape[0]
+        out = np.empty((nrows, D), np.float64)
+        lse = np.empty((nrows,), np.float64)
+        rows_ptr = rows.ctypes.data
+    rc = lib.oracle_attn_fwd(q.ctypes.data, k.ctypes.data, v.ctypes.data, out.ctypes.data,
+                             lse.ctypes.data, B, Hq, Hkv, N, D, float(scale), int(bool(causal)),
+                             vl_ptr, rows_ptr, nrows, int(threads))
+    if rc != 0:
+        raise ValueError("oracle_attn_fwd rejected its arguments (rc=%d)" % rc)
+    return out, lse

@@ -1,0 +1,161 @@
+/*
+ * Reference oracle for masked multi-head attention forward -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the test suite, the smoke check and the benchmark's CPU-baseline leg may load this
+ * library. The product path (the HIP library) never links, loads or calls it, and shares no
+ * code, header or table with it.
+ *
+ * What it computes, for every requested query row (b, hq, i):
+ *
+ *   O[b,hq,i,:] = sum_{j in J} w_j V[b,kv,j,:],   w_j = exp(s_j - m) / l,
+ *   s_j = scale * <Q[b,hq,i,:], K[b,kv,j,:]>,      m = max_{j in J} s_j,
+ *   l   = sum_{j in J} exp(s_j - m),               LSE[b,hq,i] = m + ln(l),
+ *
+ * all in IEEE double precision, where
+ *   - kv = hq / (Hq / Hkv) with integer division: grouped-query heads share one key/value
+ *     head in consecutive groups, never interleaved ("Triton Cuda Attention", section
+ *     "GQA (Grouped-Query Attention)"; multi-query attention is the case Hkv = 1, section "MQA");
+ *   - J is the set of visible keys: key j is hidden when causal masking is on and j > i
+ *     (the masked multi-head attention CUDA article at wzjinhao.cn/news/73578, section 2.2,
+ *     causal mask; "Triton Cuda Attention", section "Causal Attention"), or when a per-batch
+ *     valid length is given and j >= valid_len[b] (same article, section 2.2, padding mask);
+ *     the two masks combine by intersection (same article, sections 1.3 and 2.2). valid_len
+ *     values outside [0, N] are clamped into it.
+ *   - The softmax is taken in the three passes the article's naive kernel uses (section 3.1):
+ *     first the row maximum, then the sum of exp(s - max), then the weighted sum of V divided
+ *     by that sum. The scores are kept from the first pass.
+ *   - A row with no visible key has O = 0 and LSE = -infinity (the article, section 3.2,
+ *     recommends a zero output for a fully masked row; the log of an empty sum is -inf).
+ *   - LSE is the natural-log log-sum-exp of the scaled scores. The Triton file
+ *     tiny_flash_attn_triton.py (kernel _fwd_kernel, the store of L) keeps the same quantity
+ *     in base 2 with log2(e) folded into the scores; here it is kept in base e.
+ *
+ * Inputs are the exact values the device path sees (16-bit inputs widened to double), so no
+ * rounding happens here beyond double-precision arithmetic.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include <omp.h>
+
+/* Is key j visible to query i? */
+static int key_visible(int64_t i, int64_t j, int causal, int64_t valid)
+{
+    if (causal && j > i)
+        return 0;
+    if (j >= valid)
+        return 0;
+    return 1;
+}
+
+/* One query row, three passes. scores is caller-provided scratch of N doubles. */
+static void attend_row(const double *q_row, const double *k_head, const double *v_head,
+                       int64_t N, int64_t D, double scale, int causal, int64_t valid, int64_t i,
+                       double *scores, double *o_row, double *lse_out)
+{
+    int64_t j, d, visible = 0;
+    double m = -INFINITY, l = 0.0;
+
+    /* pass 1: scores and their maximum */
+    for (j = 0; j < N; ++j) {
+        if (!key_visible(i, j, causal, valid))
+            continue;
+        const double *k_row = k_head + j * D;
+        double dot = 0.0;
+        for (d = 0; d < D; ++d)
+            dot += q_row[d] * k_row[d];
+        scores[j] = scale * dot;
+        if (scores[j] > m)
+            m = scores[j];
+        ++visible;
+    }
+    if (visible == 0) {
+        for (d = 0; d < D; ++d)
+            o_row[d] = 0.0;
+        *lse_out = -INFINITY;
+        return;
+    }
+    /* pass 2: sum of exponentials relative to the maximum */
+    for (j = 0; j < N; ++j) {
+        if (!key_visible(i, j, causal, valid))
+            continue;
+        l += exp(scores[j] - m);
+    }
+    /* pass 3: normalised weights applied to V */
+    for (d = 0; d < D; ++d)
+        o_row[d] = 0.0;
+    for (j = 0; j < N; ++j) {
+        if (!key_visible(i, j, causal, valid))
+            continue;
+        double w = exp(scores[j] - m) / l;
+        const double *v_row = v_head + j * D;
+        for (d = 0; d < D; ++d)
+            o_row[d] += w * v_row[d];
+    }
+    *lse_out = m + log(l);
+}
+
+/*
+ * q: [B,Hq,N,D], k and v: [B,Hkv,N,D], all contiguous doubles on the host.
+ * valid_len: int32[B] on the host, or NULL for no padding mask.
+ * rows: flat row indices r = (b*Hq + hq)*N + i, or NULL for all B*Hq*N rows in order.
+ * out: [nrows, D], lse: [nrows] (row t of the output belongs to rows[t]).
+ * threads <= 0 uses the OpenMP default. Returns 0, or -1 on bad arguments.
+ */
+int oracle_attn_fwd(const double *q, const double *k, const double *v, double *out, double *lse,
+                    int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D, double scale,
+                    int causal, const int32_t *valid_len, const int64_t *rows, int64_t nrows,
+                    int threads)
+{
+    if (!q || !k || !v || !out || !lse)
+        return -1;
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 || D <= 0 || Hq % Hkv != 0)
+        return -1;
+    if (rows == NULL)
+        nrows = B * Hq * N;
+    const int64_t group = Hq / Hkv;
+    int bad = 0;
+
+#pragma omp parallel num_threads(threads > 0 ? threads : omp_get_max_threads())
+    {
+        double *scores = (double *)malloc((size_t)N * sizeof(double));
+        if (!scores) {
+#pragma omp atomic write
+            bad = 1;
+        }
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t t = 0; t < nrows; ++t) {
+            if (!scores)
+                continue;
+            int64_t r = rows ? rows[t] : t;
+            if (r < 0 || r >= B * Hq * N) {
+#pragma omp atomic write
+                bad = 1;
+                continue;
+            }
+            int64_t i = r % N;
+            int64_t bh = r / N;
+            int64_t hq = bh % Hq;
+            int64_t b = bh / Hq;
+            int64_t kv = hq / group;
+            int64_t valid = N;
+            if (valid_len) {
+                valid = valid_len[b];
+                if (valid < 0)
+                    valid = 0;
+                if (valid > N)
+                    valid = N;
+            }
+            attend_row(q + r * D, k + (b * Hkv + kv) * N * D, v + (b * Hkv + kv) * N * D, N, D,
+                       scale, causal, valid, i, scores, out + t * D, lse + t);
+        }
+        free(scores);
+    }
+    return bad ? -1 : 0;
+}
+
+int oracle_max_threads(void)
+{
+    return omp_get_max_threads();
+}

@@ -1,0 +1,360 @@
+"""Checks that tie the fp64 oracle to facts other than itself.
+
+Every pin takes an oracle callable ``fn(q, k, v, scale, causal, valid_len=None, rows=None)``
+returning ``(O, LSE)`` in float64, so the same pins run against the real oracle and against
+copies of it with planted mistakes (test_oracle_mutants.py). The pins are:
+
+  * a library routine: torch's float64 CPU ``scaled_dot_product_attention`` (with its own
+    grouped-query handling, ``enable_gqa``) and ``torch.logsumexp`` over masked scores;
+  * identities: with V the identity matrix the output row is the weight vector, and each weight
+    equals exp(score - LSE); weights sum to 1 and are exactly 0 on hidden keys;
+  * closed forms: Q = 0 gives the mean of V over the visible keys and LSE = ln |J|; constant V
+    rows give that row; causal row 0 gives V[0] and LSE = scale*q0.k0; two keys give a
+    logistic mix; the worked examples in tests/golden;
+  * invariants: key permutation, causal row = attention over the prefix, valid_len = L equals
+    truncation to L, GQA equals repeating each KV head for its group of query heads, per-(b, h)
+    slices equal single-head calls, adding a constant to every score shifts only the LSE;
+  * special cases: fully masked rows give exactly 0 and -inf; very large scores stay finite.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _normal(rng, shape, std=1.0):
+    return rng.standard_normal(shape) * std
+
+
+def _visible_mask(B, N, causal, valid_len):
+    """Boolean [B, N(query), N(key)] visibility built with numpy primitives."""
+    vis = np.ones((B, N, N), dtype=bool)
+    if causal:
+        vis &= np.tril(np.ones((N, N), dtype=bool))[None]
+    if valid_len is not None:
+        vl = np.clip(np.asarray(valid_len), 0, N)
+        vis &= (np.arange(N)[None, None, :] < vl[:, None, None])
+    return vis
+
+
+def _tiny_configs():
+    for B, Hq, Hkv in ((1, 1, 1), (2, 2, 2), (2, 4, 2), (1, 4, 1), (2, 3, 3), (1, 6, 2)):
+        for N in (1, 2, 5, 9):
+            for D in (1, 3, 8):
+                for causal in (False, True):
+                    for padded in (False, True):
+                        yield B, Hq, Hkv, N, D, causal, padded
+
+
+def pin_library_sdpa(fn):
+    """Match torch's fp64 CPU SDPA (O) and torch.logsumexp (LSE) over tiny masked cases."""
+    count = 0
+    for idx, (B, Hq, Hkv, N, D, causal, padded) in enumerate(_tiny_configs()):
+        if idx % 3 and not (padded and causal):
+            continue  # keep the sweep small; every combination with both masks is kept
+        rng = _rng([7, idx])
+        q = _normal(rng, (B, Hq, N, D))
+        k = _normal(rng, (B, Hkv, N, D))
+        v = _normal(rng, (B, Hkv, N, D))
+        scale = float(rng.uniform(0.2, 1.5))
+        vl = rng.integers(0, N + 1, size=B).astype(np.int32) if padded else None
+        O, L = fn(q, k, v, scale, causal, vl)
+        vis = _visible_mask(B, N, causal, vl)
+        tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+        mask = torch.from_numpy(vis)[:, None]            # [B,1,N,N] broadcast over heads
+        ref = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=scale,
+                                             enable_gqa=(Hq != Hkv)).numpy()
+        g = Hq // Hkv
+        s = torch.matmul(tq, torch.repeat_interleave(tk, g, dim=1).transpose(-1, -2)) * scale
+        s = s.masked_fill(~mask, float("-inf"))
+        ref_lse = torch.logsumexp(s, dim=-1).numpy()
+        nonempty = np.broadcast_to(vis.any(-1)[:, None, :], (B, Hq, N))
+        assert np.all(np.isfinite(O)), "non-finite output"
+        np.testing.assert_allclose(O[nonempty], ref[nonempty], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(L[nonempty], ref_lse[nonempty], rtol=0, atol=1e-12)
+        assert np.all(O[~nonempty] == 0.0)
+        assert np.all(np.isneginf(L[~nonempty]))
+        count += 1
+    assert count > 20
+
+
+def pin_identity_weights(fn):
+    """V = identity: the output row is the weight vector; w_j = exp(s_j - LSE) on visible keys
+    and exactly 0 on hidden ones; weights sum to 1."""
+    for causal in (False, True):
+        for vl in (None, np.array([6, 3], np.int32)):
+            B, Hq, Hkv, N = 2, 4, 2, 7
+            D = N  # V is N x N so that V[j, :] is the j-th unit vector
+            rng = _rng([11, causal, vl is None])
+            q = _normal(rng, (B, Hq, N, D))
+            k = _normal(rng, (B, Hkv, N, D))
+            v = np.broadcast_to(np.eye(N), (B, Hkv, N, N)).copy()
+            scale = 0.7
+            O, L = fn(q, k, v, scale, causal, vl)
+            vis = _visible_mask(B, N, causal, vl)
+            g = Hq // Hkv
+            for b in range(B):
+                for h in range(Hq):
+                    s = scale * (q[b, h] @ k[b, h // g].T)        # [N, N] scores
+                    for i in range(N):
+                        w = O[b, h, i]
+                        if not vis[b, i].any():
+                            assert np.all(w == 0) and np.isneginf(L[b, h, i])
+                            continue
+                        assert np.all(w[~vis[b, i]] == 0.0), "weight on a hidden key"
+                        assert abs(w.sum() - 1.0) < 1e-12, "weights do not sum to 1"
+                        expect = np.exp(s[i, vis[b, i]] - L[b, h, i])
+                        np.testing.assert_allclose(w[vis[b, i]], expect, rtol=1e-12, atol=0)
+
+
+def pin_q_zero(fn):
+    """Q = 0: every visible score is 0, so O is the mean of V over J and LSE = ln |J|."""
+    B, Hq, Hkv, N, D = 2, 4, 2, 6, 5
+    rng = _rng(13)
+    k = _normal(rng, (B, Hkv, N, D))
+    v = _normal(rng, (B, Hkv, N, D))
+    q = np.zeros((B, Hq, N, D))
+    for causal in (False, True):
+        vl = np.array([4, 6], np.int32)
+        O, L = fn(q, k, v, 0.9, causal, vl)
+        for b in range(B):
+            for h in range(Hq):
+                for i in range(N):
+                    n = min(vl[b], i + 1) if causal else vl[b]
+                    np.testing.assert_allclose(O[b, h, i], v[b, h // 2, :n].mean(0), atol=1e-13)
+                    assert abs(L[b, h, i] - math.log(n)) < 1e-13
+
+
+def pin_constant_v(fn):
+    """Every V row of a head equal to c: the output is c on every non-empty row."""
+    B, Hq, Hkv, N, D = 1, 2, 1, 8, 4
+    rng = _rng(17)
+    q = _normal(rng, (B, Hq, N, D), 2.0)
+    k = _normal(rng, (B, Hkv, N, D), 2.0)
+    c = np.array([0.5, -1.25, 3.0, 7.5])
+    v = np.broadcast_to(c, (B, Hkv, N, D)).copy()
+    for causal in (False, True):
+        O, _ = fn(q, k, v, 1.0, causal, None)
+        np.testing.assert_allclose(O, np.broadcast_to(c, O.shape), rtol=1e-14, atol=1e-14)
+
+
+def pin_causal_first_row(fn):
+    """Causal row 0 sees only key 0: O = V[0] and LSE = scale * q0 . k0."""
+    B, Hq, Hkv, N, D = 2, 2, 1, 5, 6
+    rng = _rng(19)
+    q = _normal(rng, (B, Hq, N, D))
+    k = _normal(rng, (B, Hkv, N, D))
+    v = _normal(rng, (B, Hkv, N, D))
+    O, L = fn(q, k, v, 0.4, True, None)
+    for b in range(B):
+        for h in range(Hq):
+            np.testing.assert_allclose(O[b, h, 0], v[b, 0, 0], rtol=0, atol=1e-15)
+            assert abs(L[b, h, 0] - 0.4 * float(q[b, h, 0] @ k[b, 0, 0])) < 1e-13
+
+
+def pin_two_keys(fn):
+    """N = 2, no mask: O = sigmoid(s0 - s1) V0 + sigmoid(s1 - s0) V1, LSE = logaddexp(s0, s1)."""
+    B, Hq, Hkv, N, D = 1, 3, 3, 2, 4
+    rng = _rng(23)
+    q = _normal(rng, (B, Hq, N, D))
+    k = _normal(rng, (B, Hkv, N, D))
+    v = _normal(rng, (B, Hkv, N, D))
+    scale = 1.3
+    O, L = fn(q, k, v, scale, False, None)
+    for h in range(Hq):
+        for i in range(N):
+            s0 = scale * float(q[0, h, i] @ k[0, h, 0])
+            s1 = scale * float(q[0, h, i] @ k[0, h, 1])
+            a = 1.0 / (1.0 + math.exp(s1 - s0))
+            np.testing.assert_allclose(O[0, h, i], a * v[0, h, 0] + (1 - a) * v[0, h, 1],
+                                       rtol=0, atol=1e-14)
+            assert abs(L[0, h, i] - np.logaddexp(s0, s1)) < 1e-13
+
+
+def pin_empty_rows(fn):
+    """Rows with no visible key give exactly 0 and -inf; valid_len < 0 behaves as 0."""
+    B, Hq, Hkv, N, D = 3, 2, 2, 4, 3
+    rng = _rng(29)
+    q = _normal(rng, (B, Hq, N, D))
+    k = _normal(rng, (B, Hkv, N, D))
+    v = _normal(rng, (B, Hkv, N, D))
+    for causal in (False, True):
+        vl = np.array([0, -5, 2], np.int32)
+        O, L = fn(q, k, v, 1.0, causal, vl)
+        assert np.all(O[:2] == 0.0) and np.all(np.isneginf(L[:2]))
+        assert np.all(np.isfinite(O[2])) and np.all(np.isfinite(L[2]))
+        assert np.abs(O[2]).max() > 0
+
+
+def pin_key_permutation(fn):
+    """Without masks, permuting key/value rows together changes nothing."""
+    B, Hq, Hkv, N, D = 2, 2, 2, 9, 5
+    rng = _rng(31)
+    q = _normal(rng, (B, Hq, N, D))
+    k = _normal(rng, (B, Hkv, N, D))
+    v = _normal(rng, (B, Hkv, N, D))
+    perm = rng.permutation(N)
+    O1, L1 = fn(q, k, v, 0.8, False, None)
+    O2, L2 = fn(q, k[:, :, perm], v[:, :, perm], 0.8, False, None)
+    np.testing.assert_allclose(O1, O2, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(L1, L2, rtol=0, atol=1e-13)
+
+
+def pin_causal_prefix(fn):
+    """Causal row i equals unmasked attention of that query over keys 0..i."""
+    B, Hq, Hkv, N, D = 1, 2, 1, 7, 4
+    rng = _rng(37)
+    q = _normal(rng, (B, Hq, N, D))
+    k = _normal(rng, (B, Hkv, N, D))
+    v = _normal(rng, (B, Hkv, N, D))
+    O, L = fn(q, k, v, 0.6, True, None)
+    for i in range(N):
+        qi = np.repeat(q[:, :, i:i + 1], i + 1, axis=2)   # the query, repeated to length i + 1
+        Oi, Li = fn(qi, k[:, :, :i + 1], v[:, :, :i + 1], 0.6, False, None)
+        np.testing.assert_allclose(O[:, :, i], Oi[:, :, 0], rtol=0, atol=1e-14)
+        np.testing.assert_allclose(L[:, :, i], Li[:, :, 0], rtol=0, atol=1e-14)
+
+
+def pin_valid_len_truncation(fn):
+    """valid_len = L equals attention over K[:L], V[:L]; valid_len >= N equals no padding."""
+    B, Hq, Hkv, N, D = 1, 2, 2, 8, 3
+    rng = _rng(41)
+    q = _normal(rng, (B, Hq, N, D))
+    k = _normal(rng, (B, Hkv, N, D))
+    v = _normal(rng, (B, Hkv, N, D))
+    for Lv in (1, 3, 8):
+        O, L = fn(q, k, v, 1.1, False, np.array([Lv], np.int32))
+        Ot, Lt = fn(q[:, :, :Lv], k[:, :, :Lv], v[:, :, :Lv], 1.1, False, None)
+        np.testing.assert_allclose(O[:, :, :Lv], Ot, rtol=0, atol=1e-14)
+        np.testing.assert_allclose(L[:, :, :Lv], Lt, rtol=0, atol=1e-14)
+    On, Ln = fn(q, k, v, 1.1, True, None)
+    for Lv in (N, N + 5):
+        Op, Lp = fn(q, k, v, 1.1, True, np.array([Lv], np.int32))
+        np.testing.assert_array_equal(On, Op)
+        np.testing.assert_array_equal(Ln, Lp)
+
+
+def pin_gqa_repeat(fn):
+    """GQA equals MHA with each KV head repeated for its group of consecutive query heads, and
+    differs from the interleaved assignment."""
+    B, Hq, Hkv, N, D = 2, 6, 2, 5, 4
+    rng = _rng(43)
+    q = _normal(rng, (B, Hq, N, D))
+    k = _normal(rng, (B, Hkv, N, D))
+    v = _normal(rng, (B, Hkv, N, D))
+    g = Hq // Hkv
+    for causal in (False, True):
+        O, L = fn(q, k, v, 0.5, causal, None)
+        Or, Lr = fn(q, np.repeat(k, g, axis=1), np.repeat(v, g, axis=1), 0.5, causal, None)
+        np.testing.assert_allclose(O, Or, rtol=0, atol=1e-15)
+        np.testing.assert_allclose(L, Lr, rtol=0, atol=1e-15)
+        Oi, _ = fn(q, np.tile(k, (1, g, 1, 1)), np.tile(v, (1, g, 1, 1)), 0.5, causal, None)
+        assert np.abs(O - Oi).max() > 1e-3
+
+
+def pin_slices(fn):
+    """Each (b, hq) slice of a batched call equals a B = 1, single-head call on that slice, so
+    batch and head indices are neither swapped nor mixed."""
+    B, Hq, Hkv, N, D = 3, 4, 2, 5, 3
+    rng = _rng(47)
+    q = _normal(rng, (B, Hq, N, D))
+    k = _normal(rng, (B, Hkv, N, D))
+    v = _normal(rng, (B, Hkv, N, D))
+    vl = np.array([5, 2, 4], np.int32)
+    for causal in (False, True):
+        O, L = fn(q, k, v, 0.9, causal, vl)
+        for b in range(B):
+            for h in range(Hq):
+                kv = h // (Hq // Hkv)
+                Os, Ls = fn(q[b:b + 1, h:h + 1], k[b:b + 1, kv:kv + 1], v[b:b + 1, kv:kv + 1],
+                            0.9, causal, vl[b:b + 1])
+                np.testing.assert_array_equal(O[b, h], Os[0, 0])
+                np.testing.assert_array_equal(L[b, h], Ls[0, 0])
+
+
+def pin_score_shift(fn):
+    """Appending a column of ones to Q and a constant c to every key adds scale*c to every score:
+    O is unchanged and LSE moves by scale*c, even for shifts far beyond exp's range."""
+    B, Hq, Hkv, N, D = 1, 2, 1, 6, 3
+    rng = _rng(53)
+    q = _normal(rng, (B, Hq, N, D))
+    k = _normal(rng, (B, Hkv, N, D))
+    v = _normal(rng, (B, Hkv, N, D))
+    scale = 0.5
+    O, L = fn(q, k, v, scale, True, None)
+    for c in (3.0, -4000.0, 4000.0):
+        q2 = np.concatenate([q, np.ones((B, Hq, N, 1))], axis=-1)
+        k2 = np.concatenate([k, np.full((B, Hkv, N, 1), c)], axis=-1)
+        v2 = np.concatenate([v, np.zeros((B, Hkv, N, 1))], axis=-1)
+        O2, L2 = fn(q2, k2, v2, scale, True, None)
+        np.testing.assert_allclose(O2[..., :D], O, rtol=0, atol=1e-12)
+        assert np.all(O2[..., D] == 0.0)
+        np.testing.assert_allclose(L2 - scale * c, L, rtol=0, atol=1e-9 * max(1.0, abs(c)))
+
+
+def pin_large_scores(fn):
+    """Q scaled by 30: scores in the hundreds; the output stays finite and matches the library."""
+    B, Hq, Hkv, N, D = 1, 2, 2, 9, 8
+    rng = _rng(59)
+    q = _normal(rng, (B, Hq, N, D)) * 30
+    k = _normal(rng, (B, Hkv, N, D))
+    v = _normal(rng, (B, Hkv, N, D))
+    O, L = fn(q, k, v, 1.0, False, None)
+    assert np.all(np.isfinite(O)) and np.all(np.isfinite(L))
+    ref = F.scaled_dot_product_attention(*(torch.from_numpy(x) for x in (q, k, v)),
+                                         scale=1.0).numpy()
+    np.testing.assert_allclose(O, ref, rtol=0, atol=1e-12)
+
+
+def pin_rows_subset(fn):
+    """Asking for a subset of rows returns exactly those rows of the full result."""
+    B, Hq, Hkv, N, D = 2, 4, 1, 6, 3
+    rng = _rng(61)
+    q = _normal(rng, (B, Hq, N, D))
+    k = _normal(rng, (B, Hkv, N, D))
+    v = _normal(rng, (B, Hkv, N, D))
+    vl = np.array([3, 6], np.int32)
+    O, L = fn(q, k, v, 0.7, True, vl)
+    rows = np.array([0, 5, 7, 23, 30, 47, 13], np.int64)
+    Or, Lr = fn(q, k, v, 0.7, True, vl, rows=rows)
+    np.testing.assert_array_equal(Or, O.reshape(-1, D)[rows])
+    np.testing.assert_array_equal(Lr, L.reshape(-1)[rows])
+
+
+def pin_golden(fn):
+    """Hand-worked examples in tests/golden/closed_form_examples.json; expected values are closed
+    forms in e, evaluated here with math."""
+    with open(os.path.join(GOLDEN, "closed_form_examples.json")) as f:
+        examples = json.load(f)["examples"]
+    env = {"e": math.e, "log": math.log, "exp": math.exp, "inf": math.inf}
+    for ex in examples:
+        q = np.array(ex["q"], np.float64)
+        k = np.array(ex["k"], np.float64)
+        v = np.array(ex["v"], np.float64)
+        vl = None if ex["valid_len"] is None else np.array(ex["valid_len"], np.int32)
+        O, L = fn(q, k, v, ex["scale"], ex["causal"], vl)
+        exp_o = np.array([[[[eval(t, env) for t in row] for row in head] for head in bat]
+                          for bat in ex["expect_o"]], np.float64)
+        exp_l = np.array([[[eval(t, env) for t in head] for head in bat]
+                          for bat in ex["expect_lse"]], np.float64)
+        np.testing.assert_allclose(O, exp_o, rtol=0, atol=1e-14, err_msg=ex["name"])
+        fin = np.isfinite(exp_l)
+        np.testing.assert_allclose(L[fin], exp_l[fin], rtol=0, atol=1e-14, err_msg=ex["name"])
+        assert np.all(L[~fin] == exp_l[~fin]), ex["name"]
+
+
+ALL_PINS = [pin_library_sdpa, pin_identity_weights, pin_q_zero, pin_constant_v,
+            pin_causal_first_row, pin_two_keys, pin_empty_rows, pin_key_permutation,
+            pin_causal_prefix, pin_valid_len_truncation, pin_gqa_repeat, pin_slices,
+            pin_score_shift, pin_large_scores, pin_rows_subset, pin_golden]

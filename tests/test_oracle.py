@@ -1,0 +1,37 @@
+"""The fp64 oracle against its pins (CPU only)."""
+import numpy as np
+import pytest
+
+import oracle
+import oracle_pins
+
+
+def _fn(q, k, v, scale, causal, valid_len=None, rows=None):
+    return oracle.attn_fwd(q, k, v, scale, causal, valid_len, rows=rows, threads=2)
+
+
+@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda p: p.__name__)
+def test_pin(pin):
+    pin(_fn)
+
+
+def test_rejects_bad_arguments():
+    q = np.zeros((1, 3, 4, 2))
+    k = np.zeros((1, 2, 4, 2))
+    with pytest.raises(ValueError):
+        oracle.attn_fwd(q, k, k, 1.0, False)   # Hq % Hkv != 0
+    q = np.zeros((1, 2, 4, 2))
+    with pytest.raises(ValueError):
+        oracle.attn_fwd(q, k, k, 1.0, False, rows=np.array([8], np.int64))  # row out of range
+
+
+def test_thread_count_does_not_change_results():
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((2, 4, 33, 8))
+    k = rng.standard_normal((2, 2, 33, 8))
+    v = rng.standard_normal((2, 2, 33, 8))
+    vl = np.array([20, 33], np.int32)
+    O1, L1 = oracle.attn_fwd(q, k, v, 0.3, True, vl, threads=1)
+    O4, L4 = oracle.attn_fwd(q, k, v, 0.3, True, vl, threads=4)
+    np.testing.assert_array_equal(O1, O4)
+    np.testing.assert_array_equal(L1, L4)

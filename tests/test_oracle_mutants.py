@@ -1,0 +1,71 @@
+"""Plant plausible mistakes in copies of the oracle's C source and check that the pins catch
+every one of them (CPU only; the real oracle is never modified)."""
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "attn_oracle.c")
+
+# (name, original text, mutated text): each original must occur in the source.
+MUTANTS = [
+    ("gqa_interleaved", "int64_t kv = hq / group;", "int64_t kv = hq % Hkv;"),
+    ("causal_strict", "if (causal && j > i)", "if (causal && j >= i)"),
+    ("causal_reversed", "if (causal && j > i)", "if (causal && j < i)"),
+    ("padding_off_by_one", "if (j >= valid)", "if (j > valid)"),
+    ("padding_by_query", "if (j >= valid)", "if (i >= valid)"),
+    ("no_scale", "scores[j] = scale * dot;", "scores[j] = dot;"),
+    ("scale_twice", "scores[j] = scale * dot;", "scores[j] = scale * scale * dot;"),
+    ("no_max_shift", "l += exp(scores[j] - m);", "l += exp(scores[j]);"),
+    ("max_init_zero", "double m = -INFINITY, l = 0.0;", "double m = 0.0, l = 0.0;"),
+    ("sum_init_one", "double m = -INFINITY, l = 0.0;", "double m = -INFINITY, l = 1.0;"),
+    ("lse_without_max", "*lse_out = m + log(l);", "*lse_out = log(l);"),
+    ("lse_base2", "*lse_out = m + log(l);", "*lse_out = m + log2(l);"),
+    ("no_normalisation", "double w = exp(scores[j] - m) / l;", "double w = exp(scores[j] - m);"),
+    ("key_row_from_query_index", "const double *k_row = k_head + j * D;",
+     "const double *k_row = k_head + i * D;"),
+    ("value_row_from_query_index", "const double *v_row = v_head + j * D;",
+     "const double *v_row = v_head + i * D;"),
+    ("dot_drops_last_term", "for (d = 0; d < D; ++d)\n            dot +=",
+     "for (d = 0; d < D - 1; ++d)\n            dot +="),
+    ("empty_row_lse_zero", "*lse_out = -INFINITY;", "*lse_out = 0.0;"),
+    ("empty_row_not_zeroed", "o_row[d] = 0.0;\n        *lse_out", "o_row[d] = 1.0;\n        *lse_out"),
+    ("batch_index_swapped", "int64_t b = bh / Hq;", "int64_t b = bh % B;"),
+    ("head_index_swapped", "int64_t hq = bh % Hq;", "int64_t hq = bh / B % Hq;"),
+    ("no_valid_len_clamp_high", "if (valid > N)\n                    valid = N;",
+     "if (valid > N)\n                    valid = N - 1;"),
+    ("kv_head_stride_uses_hq", "k + (b * Hkv + kv) * N * D", "k + (b * Hq + kv) * N * D"),
+]
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(SRC) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name,orig,mut", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(source, name, orig, mut):
+    assert orig in source, "mutation site for %s no longer in the oracle source" % name
+    text = source.replace(orig, mut, 1)
+    with tempfile.TemporaryDirectory() as d:
+        src = os.path.join(d, "mutant.c")
+        with open(src, "w") as f:
+            f.write(text)
+        lib = oracle.load(oracle.build(src, os.path.join(d, "libmutant.so")))
+
+        def fn(q, k, v, scale, causal, valid_len=None, rows=None):
+            return oracle.attn_fwd(q, k, v, scale, causal, valid_len, rows=rows, threads=2,
+                                   lib=lib)
+
+        caught = []
+        for pin in oracle_pins.ALL_PINS:
+            try:
+                pin(fn)
+            except (AssertionError, ValueError, FloatingPointError) as e:
+                caught.append(pin.__name__)
+        assert caught, "no pin caught the planted mistake %s" % name
