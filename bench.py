@@ -1,0 +1,175 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention forward on one MI355X.
+
+One step = one attn_fwd call over the whole workload (all query tiles of all batches and heads),
+inputs resident in HBM before timing starts. Prints ONE JSON line on stdout; progress goes to
+stderr.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long_gqa] [--no-cpu-baseline]
+
+Throughput is the nominal forward flop count 4*B*Hq*N^2*D (halved under causal masking) per
+second. The roofline object reports the kernel's flop rate against the dense 16-bit MFMA peak,
+timed with HIP events on the stream the kernel is launched on; `traffic` is the HBM byte count
+from rocprofv3 counters recorded in profiles/ for the current kernel source (null if the kernel
+changed since). The cpu_baseline object times the fp64 oracle on a bounded sample of whole
+(batch, head) slices of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s, bf16 causal N=4096 D=128; % of MFMA dense peak"
+PEAK_TFLOPS_16BIT_DENSE = 2500.0   # MI355X published dense bf16/fp16 MFMA peak
+KERNEL_SRC = os.path.join(ROOT, "scaled_dot_product_fwd_amd", "csrc", "attn_fwd.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(msg):
+    sys.stderr.write(msg + "\n")
+    sys.stderr.flush()
+
+
+def flops(w) -> float:
+    f = 4.0 * w.B * w.Hq * w.N * w.N * w.D
+    return f / 2 if w.causal else f
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_for(workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they match this source."""
+    path = os.path.join(PROFILES, "traffic_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha256") != kernel_sha():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, case, target_s: float):
+    """Time the oracle on whole (b, hq) slices (so the causal row-length mix is the workload's),
+    sized to about target_s seconds; rate scaled by the exact flop share of the sample."""
+    import oracle
+    q, k, v = case.widened()
+    threads = oracle.max_threads()
+    heads_total = w.B * w.Hq
+    order = np.random.default_rng(0).permutation(heads_total)
+
+    def rows_of(heads):
+        return np.concatenate([np.arange(h * w.N, (h + 1) * w.N, dtype=np.int64) for h in heads])
+
+    t0 = time.perf_counter()
+    oracle.attn_fwd(q, k, v, case.scale, case.causal, case.valid_len, rows=rows_of(order[:1]))
+    t1 = time.perf_counter() - t0
+    nheads = int(max(1, min(heads_total, round(target_s / max(t1, 1e-3)))))
+    heads = order[:nheads]
+    t0 = time.perf_counter()
+    oracle.attn_fwd(q, k, v, case.scale, case.causal, case.valid_len, rows=rows_of(heads))
+    dt = time.perf_counter() - t0
+    sample_flops = flops(w) * nheads / heads_total
+    return {"value": sample_flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d of %d (batch, head) slices, all %d query rows each, %.1f s; "
+                      "flops scaled by the slice share" % (nheads, heads_total, w.N, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long_gqa")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import scaled_dot_product_fwd_amd as sdp
+    from scaled_dot_product_fwd_amd import inputs
+
+    w = inputs.WORKLOADS[args.workload]
+    log("workload %s: B=%d Hq=%d Hkv=%d N=%d D=%d %s causal=%s padded=%s" % (
+        w.name, w.B, w.Hq, w.Hkv, w.N, w.D, w.dtype, w.causal, w.padded))
+    case = inputs.make_workload(w)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float16
+
+    def dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(tdt).cuda()
+
+    q, k, v = dev(case.q_bits), dev(case.k_bits), dev(case.v_bits)
+    vl = torch.from_numpy(case.valid_len).cuda() if case.valid_len is not None else None
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        sdp.forward(q, k, v, causal=w.causal, valid_len=vl, scale=w.scale, out=out, lse=lse,
+                    stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("warmup done (%d steps)" % args.warmup)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_event = ev0.elapsed_time(ev1)
+    ms_per_step = ms_event / args.steps
+    log("timed %d steps: %.3f ms/step by HIP events, %.3f ms/step by host clock" % (
+        args.steps, ms_per_step, wall * 1e3 / args.steps))
+    if torch.isnan(out).any().item():
+        raise SystemExit("NaN in the output")
+
+    f = flops(w)
+    tflops = f / (ms_per_step * 1e-3) / 1e12
+    roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_TFLOPS_16BIT_DENSE,
+            "unit": "TFLOP/s", "frac": round(tflops / PEAK_TFLOPS_16BIT_DENSE, 4),
+            "traffic": traffic_for(w.name)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host (about %.0f s)" % args.cpu_seconds)
+        cpu = cpu_baseline(w, case, args.cpu_seconds)
+        cpu["value"] = float("%.6g" % cpu["value"])
+        log("cpu baseline: %s" % json.dumps(cpu))
+    line = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded iid N(0,1), rounded to %s)" % w.dtype,
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "D": w.D,
+                   "causal": w.causal, "padded": w.padded, "scale": w.scale,
+                   "flops_per_step": f},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,121 @@
+/*
+ * attn.h -- C ABI of libattn.so: fused masked multi-head attention forward on AMD Instinct
+ * MI355X (CDNA4, gfx950).
+ *
+ * Operation (what every entry point below computes). For batch b, query head hq and query
+ * row i:
+ *
+ *     O[b,hq,i,:] = softmax_j( scale * Q[b,hq,i,:] . K[b,kv,j,:] + mask(b,i,j) ) V[b,kv,j,:]
+ *     LSE[b,hq,i] = ln sum_{visible j} exp( scale * Q[b,hq,i,:] . K[b,kv,j,:] )
+ *
+ * - The formula softmax(Q K^T / sqrt(D) + Mask) V over [B,H,N,D] tensors is the one the masked
+ *   multi-head attention CUDA article (wzjinhao.cn/news/73578) writes down in section 2.1; the
+ *   scale is a caller argument here (the Triton file tiny_flash_attn_triton.py takes it as
+ *   sm_scale), and 1/sqrt(D) is the usual value.
+ * - The mask hides key j from query i when causal masking is on and j > i (article section 2.2,
+ *   causal mask; "Triton Cuda Attention", section "Causal Attention"), or when valid_len is given
+ *   and j >= valid_len[b] (article section 2.2, padding by per-sample valid length). Both may be
+ *   on at once; a key must pass both (article sections 1.3 and 2.2).
+ * - Grouped-query attention: query head hq reads key/value head kv = hq / (Hq / Hkv) (integer
+ *   division: consecutive query heads share a KV head), as "Triton Cuda Attention" prescribes
+ *   in section "GQA (Grouped-Query Attention)". Hkv = 1 is multi-query attention (section "MQA").
+ * - A query row that sees no key (for instance every row of a batch with valid_len[b] = 0) is
+ *   defined to output O = 0 exactly and LSE = -infinity, with no NaN (the article, section 3.2,
+ *   on fully masked rows).
+ * - LSE is the natural-log log-sum-exp of the row's visible scaled scores; a later backward pass
+ *   or a merge of partial results over key shards uses it (tiny_flash_attn_triton.py stores the
+ *   same quantity in base 2 "for backward").
+ * - The computation is the tiled online softmax of "Triton Cuda Attention" (section on the
+ *   online softmax core algorithm): the N x N score matrix never reaches memory.
+ *
+ * Numerics: 16-bit inputs, fp32 scores, softmax state and accumulation; the probabilities are
+ * rounded to the input type before they multiply V; O is rounded to nearest-even in the input
+ * type. Results are deterministic run to run for the same inputs and shapes.
+ *
+ * Threading: every call is independent and the library keeps no state between calls except
+ * compiled kernels; calls on different streams may run concurrently. The library allocates no
+ * memory.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of Q, K, V and O. */
+typedef enum {
+    ATTN_F16 = 0,  /* IEEE binary16 */
+    ATTN_BF16 = 1  /* bfloat16 */
+} attn_dtype_t;
+
+/* Return codes. Argument errors are detected on the host before anything is launched. */
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = -1,     /* q, k, v or out is NULL */
+    ATTN_ERR_SHAPE = -2,    /* B, Hq, Hkv or N < 1, Hq not a multiple of Hkv, or sizes beyond
+                               the limits below */
+    ATTN_ERR_HEAD_DIM = -3, /* D is not 64 or 128 */
+    ATTN_ERR_DTYPE = -4,    /* dtype is not ATTN_F16 or ATTN_BF16 */
+    ATTN_ERR_SCALE = -5,    /* scale is NaN or infinite */
+    ATTN_ERR_LAUNCH = -6,   /* the HIP runtime reported an error at launch; query HIP for it */
+    ATTN_ERR_ALIAS = -7     /* out or lse overlaps an input, or out overlaps lse */
+} attn_status_t;
+
+/* Size limits checked by attn_fwd_validate: N <= ATTN_MAX_N and
+ * B * Hq * ceil(N / 128) <= ATTN_MAX_TILES. */
+#define ATTN_MAX_N (1 << 24)
+#define ATTN_MAX_TILES 2147483647LL
+
+/*
+ * attn_fwd -- launch the attention forward described at the top of this file on `stream`.
+ *
+ *   q          device pointer, [B, Hq, N, D] elements of `dtype`, contiguous (row-major, D
+ *              fastest), 16-byte aligned.
+ *   k, v       device pointers, [B, Hkv, N, D] elements of `dtype`, contiguous, 16-byte aligned.
+ *              With Hkv = 1 this is the same memory as a [B, N, D] tensor.
+ *   out        device pointer, [B, Hq, N, D] elements of `dtype`, contiguous, 16-byte aligned;
+ *              written completely (including rows with no visible key). Must not overlap q, k,
+ *              v or lse.
+ *   lse        device pointer to [B, Hq, N] float32, contiguous; NULL means "do not write".
+ *   B, Hq, Hkv, N, D
+ *              batch, query heads, key/value heads, sequence length (queries and keys share it),
+ *              head dimension. Any N >= 1 is accepted; D must be 64 or 128.
+ *   scale      multiplier of the dot products (typically 1/sqrt(D)); any finite value.
+ *   causal     nonzero hides key j from query i when j > i.
+ *   valid_len  device pointer to int32[B], or NULL for no padding mask. Keys j >= valid_len[b]
+ *              are hidden for every query of batch b; values are clamped into [0, N]. Only keys
+ *              are masked: query rows at or beyond valid_len[b] are computed like any other row.
+ *   dtype      ATTN_F16 or ATTN_BF16.
+ *   stream     hipStream_t to launch on; NULL is the default stream.
+ *
+ * Ownership: the caller allocates and owns every buffer; the call is asynchronous and the
+ * buffers must stay valid until the stream has finished it. Returns ATTN_OK once the work is
+ * queued, an argument error (nothing launched, nothing written), or ATTN_ERR_LAUNCH.
+ */
+int attn_fwd(const void *q, const void *k, const void *v, void *out, float *lse, int B, int Hq,
+             int Hkv, int N, int D, float scale, int causal, const int32_t *valid_len, int dtype,
+             void *stream);
+
+/*
+ * attn_fwd_validate -- the argument check attn_fwd performs, on the host only: makes no HIP
+ * call and touches no memory behind the pointers (they are compared, never dereferenced).
+ * Same arguments and return codes as attn_fwd, except that it never returns ATTN_ERR_LAUNCH.
+ */
+int attn_fwd_validate(const void *q, const void *k, const void *v, const void *out,
+                      const float *lse, int B, int Hq, int Hkv, int N, int D, float scale,
+                      int causal, const int32_t *valid_len, int dtype);
+
+/* attn_status_string -- a static, NUL-terminated description of a return code (never NULL). */
+const char *attn_status_string(int status);
+
+/* attn_version -- the library's interface version, currently 1. */
+int attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */
