@@ -96,6 +96,9 @@ def main():
     ap.add_argument("--workload", default="long_gqa")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB three times (the "
+                         "reference kernel for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -103,6 +106,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copied %d MiB three times" % args.copy_calibration)
+        return
     import scaled_dot_product_fwd_amd as sdp
     from scaled_dot_product_fwd_amd import inputs
 

@@ -66,7 +66,7 @@ typedef enum {
 
 /* Size limits checked by attn_fwd_validate: N <= ATTN_MAX_N and
  * B * Hq * ceil(N / 128) <= ATTN_MAX_TILES. */
-#define ATTN_MAX_N (1 << 24)
+#define ATTN_MAX_N (1 << 22)
 #define ATTN_MAX_TILES 2147483647LL
 
 /*

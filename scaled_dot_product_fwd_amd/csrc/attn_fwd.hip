@@ -8,27 +8,37 @@
 // multi-head attention CUDA article, wzjinhao.cn/news/73578, section 4.3), and exponentials are
 // exp2 of scores pre-multiplied by scale*log2(e) ("Triton Cuda Attention", performance notes).
 //
-// CDNA4 mapping (measured lane layouts of v_mfma_f32_32x32x16_{bf16,f16}):
-//   * Scores are computed transposed, S^T = K Q^T, so the 32x32 MFMA output column that a lane
-//     holds is one query: lane l owns query (l % 32) and 16 of every 32 keys; lanes l and l^32
-//     share a query. Row max and row sum are therefore in-lane, plus one permlane32 swap.
-//   * Output is accumulated transposed too, O^T = V^T P^T: the S^T accumulator registers, rounded
-//     to 16 bits, are the B operand of the second MFMA directly (keys in the order the first
-//     MFMA's output layout gives them), and V^T fragments come from row-major V in LDS through
-//     the transposing LDS read ds_read_b64_tr_b16.
-//   * K and V tiles are double-buffered in LDS with padded rows (no bank conflicts for the
-//     128-bit K reads and the transposing V reads); the next tile's global loads are in flight
-//     while the current tile is computed.
+// CDNA4 mapping (lane layouts of v_mfma_f32_32x32x16_{bf16,f16} and ds_read_b64_tr_b16 were
+// measured on the device before use):
+//   * Scores are computed transposed, S^T = K Q^T, so the 32x32 MFMA output column a lane holds
+//     is one query: lane l owns query (l % 32) and 16 of every 32 keys; lanes l and l^32 share a
+//     query. Row max and row sum are in-lane, plus one permlane32 swap.
+//   * Output is accumulated transposed, O^T = V^T P^T: the S^T registers, rounded to 16 bits,
+//     are the B operand of the second MFMA directly (keys in the order the first MFMA's output
+//     layout gives them); V^T fragments come from row-major V in LDS through the transposing LDS
+//     read ds_read_b64_tr_b16.
+//   * K and V tiles go HBM -> LDS by buffer_load ... lds (no staging registers); the buffer
+//     range check returns zeros past the last key, so a ragged tail needs no branches. LDS rows
+//     are XOR-swizzled by 16-byte chunk so that the 128-bit K reads and the transposing V reads
+//     are free of bank conflicts.
+//   * K runs one tile ahead of V: while the MFMAs compute the scores of tile j+1, the VALU does
+//     the softmax of tile j, then P_j V_j accumulates. Each wave keeps two score tiles.
 //   * Causal and padding masks are implicit: tiles wholly above the diagonal or past valid_len
-//     are never loaded; only tiles that straddle a boundary apply a per-element mask.
+//     are never loaded; only tiles that straddle a boundary apply a per-element mask, on a
+//     separate (slower) code path.
 //   * The running maximum is only raised when a tile's maximum exceeds it by more than
 //     RESCALE_THRESHOLD (log2 units). Any reference value gives the same final O = acc / l and
 //     LSE = m + log2(l) as long as numerator and denominator share it; a bounded stale maximum
 //     only keeps probabilities below 2^RESCALE_THRESHOLD, and saves the accumulator rescale on
 //     most tiles.
+//   * Workgroups are ordered so that, when the KV heads divide evenly over the 8 XCDs, every
+//     query head of one KV head runs on the same XCD (its K/V stay in that XCD's L2), longest
+//     causal tiles first.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <math.h>
+
+#include <type_traits>
 
 #include "attn.h"
 
@@ -41,6 +51,7 @@ typedef float f32x8 __attribute__((__vector_size__(8 * sizeof(float))));
 typedef short i16x4 __attribute__((__vector_size__(4 * sizeof(short))));
 typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
 typedef uint32_t u32x2 __attribute__((__vector_size__(2 * sizeof(uint32_t))));
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kBM = 128;        // query rows per workgroup (32 per wave)
 constexpr int kBN = 64;         // keys per K/V tile
@@ -49,18 +60,19 @@ constexpr int kThreads = 64 * kWaves;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float RESCALE_THRESHOLD = 8.0f;
+constexpr int kBufferFlags = 0x00020000;   // raw buffer: dword data, range-checked
 
 template <int D>
-struct Tile {
-  static constexpr int KS = D + 8;    // K row stride in LDS (elements): rows 4 banks apart
-  static constexpr int VS = D + 16;   // V row stride in LDS (elements): rows 8 banks apart
-  static constexpr int K_ELEMS = kBN * KS;
-  static constexpr int V_ELEMS = kBN * VS;
-  static constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;
-  static constexpr int LDS_ELEMS = 2 * BUF_ELEMS;
-  static constexpr int CHUNKS = D / 8;                      // 16-byte chunks per row
-  static constexpr int LOADS = kBN * CHUNKS / kThreads;     // 16-byte loads per thread per tile
-  static constexpr int ROWS_PER_PASS = kThreads / CHUNKS;
+struct Geo {
+  static constexpr int CH = D / 8;                   // 16-byte chunks per row
+  static constexpr int ROW = 2 * D;                  // bytes per row
+  static constexpr int TILE = kBN * ROW;             // bytes per K or V tile
+  static constexpr int LOADS = TILE / 1024 / kWaves; // 1 KiB DMA blocks per wave per tile
+  static constexpr int RPB = 1024 / ROW;             // rows per 1 KiB block
+  static constexpr int KSTEPS = D / 16;              // k-steps of the score MFMA
+  static constexpr int OT = D / 32;                  // 32-row tiles of O^T
+  static constexpr int K0 = 0, K1 = TILE, V0 = 2 * TILE, V1 = 3 * TILE;
+  static constexpr int LDS = 4 * TILE;
 };
 
 struct Params {
@@ -73,8 +85,10 @@ struct Params {
   int B, Hq, Hkv, N;
   int group;         // Hq / Hkv
   int nqt;           // ceil(N / kBM)
+  int xcd_order;     // 1: KV heads divide evenly over the 8 XCDs
   float c;           // |scale| * log2(e)
   uint32_t qsign;    // 0x80008000 when scale < 0: Q is negated (exactly) instead
+  uint32_t qmask;    // 0 when scale == 0: all scores are exactly 0 (and c is set to 1)
 };
 
 template <int DT>
@@ -108,7 +122,7 @@ struct Mfma<ATTN_F16> {
   }
 };
 
-// Both members of the lane pair {l, l^32}: returns them in any order.
+// permlane32_swap(x, x) returns, in every lane, both members of the lane pair {l, l^32}.
 __device__ inline float pair_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -118,61 +132,111 @@ __device__ inline float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__device__ inline u32x2 lds_read_tr16(const uint16_t* p) {
+__device__ inline u32x2 lds_read_tr16(const unsigned char* p) {
   i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) i16x4*)(p));
   return __builtin_bit_cast(u32x2, v);
 }
 
+__device__ inline void wait_loads_and_lds() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+}
+
+// Per-wave, per-thread state of the main loop (registers).
 template <int D>
-__device__ inline void load_tile(const uint16_t* __restrict__ base, int row0, int N, int tid,
-                                 u32x4 (&reg)[Tile<D>::LOADS]) {
-  using T = Tile<D>;
-  const int c = tid % T::CHUNKS;
-  const int r = tid / T::CHUNKS;
+struct Frag {
+  uint32_t kaddr[4];   // LDS byte offsets of this lane's K fragments for k-steps 0..3
+  uint32_t vaddr[2];   // LDS byte offsets of this lane's V^T fragments for u = 0, 1
+};
+
+template <int DT, int D>
+__device__ inline void qk_tile(f32x16 (&s)[2], const unsigned char* kbuf, const Frag<D>& f,
+                               const u32x4 (&qf)[Geo<D>::KSTEPS]) {
+  using G = Geo<D>;
+  using M = Mfma<DT>;
 #pragma unroll
-  for (int i = 0; i < T::LOADS; ++i) {
-    const int row = row0 + r + i * T::ROWS_PER_PASS;
-    if (row < N)
-      reg[i] = *(const u32x4*)(base + (size_t)row * D + c * 8);
-    else
-      reg[i] = u32x4{0, 0, 0, 0};
+  for (int t = 0; t < 2; ++t) {
+    s[t] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < G::KSTEPS; ++ks) {
+      const u32x4 a = *(const u32x4*)(kbuf + f.kaddr[ks & 3] + (ks >> 2) * 128 + t * 32 * G::ROW);
+      s[t] = M::run(a, qf[ks], s[t]);
+    }
   }
 }
 
-template <int D>
-__device__ inline void store_tile(uint16_t* lds, int stride, int tid,
-                                  const u32x4 (&reg)[Tile<D>::LOADS]) {
-  using T = Tile<D>;
-  const int c = tid % T::CHUNKS;
-  const int r = tid / T::CHUNKS;
+// O^T += V^T P^T for the 16 keys of k-step s.
+template <int DT, int D>
+__device__ inline void pv_step(f32x16 (&acc)[Geo<D>::OT], const unsigned char* vbuf,
+                               const Frag<D>& f, int s, u32x4 pb) {
+  using G = Geo<D>;
+  using M = Mfma<DT>;
 #pragma unroll
-  for (int i = 0; i < T::LOADS; ++i)
-    *(u32x4*)(lds + (r + i * T::ROWS_PER_PASS) * stride + c * 8) = reg[i];
+  for (int u = 0; u < G::OT; ++u) {
+    const unsigned char* base = vbuf + f.vaddr[u & 1] + (u >> 1) * 128 + 16 * s * G::ROW;
+    const u32x2 lo = lds_read_tr16(base);
+    const u32x2 hi = lds_read_tr16(base + 8 * G::ROW);
+    acc[u] = M::run(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb, acc[u]);
+  }
+}
+
+// Raise the reference maximum if this tile's maximum exceeds it by more than the threshold.
+template <int D>
+__device__ inline void update_max(float mx, float c, float& m, float& l,
+                                  f32x16 (&acc)[Geo<D>::OT]) {
+  const float mt = (mx == -INFINITY) ? -INFINITY : mx * c;
+  const bool need = mt > m + RESCALE_THRESHOLD;
+  if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
+    const float mnew = need ? mt : m;
+    const float alpha = __builtin_amdgcn_exp2f(m - mnew);   // 0 when m = -inf
+    l *= alpha;
+#pragma unroll
+    for (int u = 0; u < Geo<D>::OT; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[u][r] *= alpha;
+    m = mnew;
+  }
 }
 
 template <int DT, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void attn_fwd_kernel(Params p) {
-  using T = Tile<D>;
+__device__ __forceinline__ void attn_fwd_body(const Params& p) {
+  using G = Geo<D>;
   using M = Mfma<DT>;
-  constexpr int KSTEPS = D / 16;   // k-steps of the score MFMA
-  constexpr int OT = D / 32;       // 32-row output tiles of O^T
-  __shared__ __attribute__((aligned(16))) uint16_t smem[T::LDS_ELEMS];
+  constexpr int KSTEPS = G::KSTEPS;
+  constexpr int OT = G::OT;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[G::LDS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int h = lane >> 5;          // which half of the wave (which 4-key group in each 8)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5;          // which half of the wave
   const int ql = lane & 31;
 
-  // Work decomposition: causal tiles in decreasing cost order (the longest start first).
-  const int BH = p.B * p.Hq;
-  const int bid = blockIdx.x;
-  const int qt = CAUSAL ? (p.nqt - 1 - bid / BH) : (bid / BH);
-  const int bh = bid % BH;
-  const int b = bh / p.Hq;
-  const int hq = bh - b * p.Hq;
+  // ---- work decomposition
+  int qt, b, hq;
+  {
+    const int wid = blockIdx.x;
+    if (p.xcd_order) {
+      const int xcd = wid & 7;
+      const int local = wid >> 3;
+      const int per_head = p.group * p.nqt;
+      const int head_local = local / per_head;
+      const int r = local - head_local * per_head;
+      const int kv_head = head_local * 8 + xcd;          // in [0, B * Hkv)
+      const int qi = r / p.group;
+      qt = CAUSAL ? p.nqt - 1 - qi : qi;
+      b = kv_head / p.Hkv;
+      hq = (kv_head - b * p.Hkv) * p.group + (r - qi * p.group);
+    } else {
+      const int BH = p.B * p.Hq;
+      const int qi = wid / BH;
+      const int bh = wid - qi * BH;
+      qt = CAUSAL ? p.nqt - 1 - qi : qi;
+      b = bh / p.Hq;
+      hq = bh - b * p.Hq;
+    }
+  }
+  const int bh = b * p.Hq + hq;
   const int kvh = hq / p.group;
   const int q0 = qt * kBM;
 
@@ -181,20 +245,72 @@ void attn_fwd_kernel(Params p) {
   int kv_stop = kv_end;
   if (CAUSAL) kv_stop = min(kv_stop, q0 + kBM);
   const int ntiles = (kv_stop + kBN - 1) / kBN;
-
-  const uint16_t* __restrict__ qbase = p.q + (size_t)bh * p.N * D;
-  const uint16_t* __restrict__ kbase = p.k + (size_t)(b * p.Hkv + kvh) * p.N * D;
-  const uint16_t* __restrict__ vbase = p.v + (size_t)(b * p.Hkv + kvh) * p.N * D;
-
-  // Q fragments: B operand of S^T = K Q^T. Lane l holds Q[row][16s + 8h .. +7].
   const int qa = q0 + wave * 32;            // first query of this wave
   const int qrow = qa + ql;
+
+  const size_t kv_off = (size_t)(b * p.Hkv + kvh) * p.N * D;
+  const uint32_t head_bytes = (uint32_t)p.N * G::ROW;
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + kv_off), (short)0, head_bytes, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + kv_off), (short)0, head_bytes, kBufferFlags);
+
+  // ---- DMA offsets: block (wave * LOADS + i) of a tile holds rows [blk * RPB, +RPB); lane
+  // writes LDS chunk (lane % CH) of row (lane / CH) and fetches the global chunk that the row's
+  // swizzle maps there (K: chunk ^ (row & 7); V: chunk ^ 2 * (row & 3)). Rows 8 apart share a
+  // swizzle, so block i's offsets are block (i % KP)'s plus a constant: KP = 8 / RPB blocks
+  // (K) and one block (V) need their own registers.
+  constexpr int KP = 8 / G::RPB;
+  uint32_t koff[KP], voff0;
+#pragma unroll
+  for (int i = 0; i < KP; ++i) {
+    const int row = (wave * G::LOADS + i) * G::RPB + lane / G::CH;
+    koff[i] = row * G::ROW + (((lane % G::CH) ^ (row & 7)) * 16);
+  }
+  {
+    const int row = wave * G::LOADS * G::RPB + lane / G::CH;
+    voff0 = row * G::ROW + (((lane % G::CH) ^ ((row & 3) << 1)) * 16);
+  }
+  auto dma = [&](int tile, int kdst, int vdst) {
+    const int soff = tile * G::TILE;
+#pragma unroll
+    for (int i = 0; i < G::LOADS; ++i) {
+      const int blk = (wave * G::LOADS + i) * 1024;
+      if (kdst >= 0)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(smem + kdst + blk), 16,
+                                                 koff[i % KP], soff + (i / KP) * KP * 1024, 0, 0);
+      if (vdst >= 0)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(smem + vdst + blk), 16,
+                                                 voff0, soff + i * 1024, 0, 0);
+    }
+  };
+
+  // ---- LDS fragment offsets (see the swizzles above)
+  Frag<D> f;
+  {
+    const int c = (ql >> 1) & 3;
+    const int hb = (h ^ ql) & 1;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) f.kaddr[s4] = ql * G::ROW + 16 * (2 * (s4 ^ c) + hb);
+    const int g = lane >> 4;
+    const int jj = lane & 15;
+    const int y = 2 * (jj >> 2);
+    const int x = 2 * (g & 1) + ((jj & 3) >> 1);
+    const int yb = (jj >> 3) & 1;
+    const int xy = (x ^ y) & 3;
+    const int base = (4 * (g >> 1) + (jj >> 2)) * G::ROW + 16 * xy + 8 * (jj & 1);
+    f.vaddr[0] = base + 64 * yb;
+    f.vaddr[1] = base + 64 * (1 - yb);
+  }
+
+  // ---- Q fragments: B operand of S^T = K Q^T. Lane l holds Q[row][16s + 8h .. +7].
+  const uint16_t* __restrict__ qbase = p.q + (size_t)bh * p.N * D;
   u32x4 qf[KSTEPS];
 #pragma unroll
   for (int s = 0; s < KSTEPS; ++s) {
     if (qrow < p.N) {
       qf[s] = *(const u32x4*)(qbase + (size_t)qrow * D + 16 * s + 8 * h);
-      qf[s] ^= p.qsign;
+      qf[s] = (qf[s] ^ p.qsign) & p.qmask;
     } else {
       qf[s] = u32x4{0, 0, 0, 0};
     }
@@ -207,112 +323,180 @@ void attn_fwd_kernel(Params p) {
   float l = 0.f;          // this lane's part of the running denominator
   const float c = p.c;
 
-  u32x4 kreg[T::LOADS], vreg[T::LOADS];
-  if (ntiles > 0) {
-    load_tile<D>(kbase, 0, p.N, tid, kreg);
-    load_tile<D>(vbase, 0, p.N, tid, vreg);
-    store_tile<D>(smem, T::KS, tid, kreg);
-    store_tile<D>(smem + T::K_ELEMS, T::VS, tid, vreg);
-  }
-  __syncthreads();
+  // Row maximum (raw score units, both lanes of a query pair) of a score tile.
+  auto rowmax = [&](const f32x16 (&sv)[2]) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sv[t][r]);
+    return pair_max(mx);
+  };
 
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    const uint16_t* ks = smem + buf * T::BUF_ELEMS;
-    const uint16_t* vs = ks + T::K_ELEMS;
-    const bool more = j + 1 < ntiles;
-    if (more) {
-      load_tile<D>(kbase, (j + 1) * kBN, p.N, tid, kreg);
-      load_tile<D>(vbase, (j + 1) * kBN, p.N, tid, vreg);
-    }
-    const int kb = j * kBN;
-    // Tile class for this wave's 32 queries.
-    const bool hidden = (CAUSAL && kb > qa + 31) || kb >= kv_end;
-    if (!hidden) {
-      const bool partial = (CAUSAL && kb + kBN - 1 > qa) || kb + kBN > kv_end;
-      // ---- S^T = K Q^T: two 32-key halves
-      f32x16 sv[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        sv[t] = f32x16{};
-        const uint16_t* krow = ks + (32 * t + ql) * T::KS + 8 * h;
-#pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) {
-          u32x4 a = *(const u32x4*)(krow + 16 * s);
-          sv[t] = M::run(a, qf[s], sv[t]);
-        }
-      }
-      // ---- mask (tiles that straddle the diagonal, valid_len or N only)
-      uint32_t vis0 = 0xffffffffu;   // bit (16 t + r): key visible
-      if (partial) {
-        vis0 = 0;
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kb + 32 * t + (r >> 2) * 8 + 4 * h + (r & 3);
-            const bool ok = key < kv_end && (!CAUSAL || key <= qrow);
-            vis0 |= (ok ? 1u : 0u) << (16 * t + r);
-            sv[t][r] = ok ? sv[t][r] : -INFINITY;
-          }
-      }
-      // ---- online softmax
-      float mx = -INFINITY;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sv[t][r]);
-      mx = pair_max(mx);
-      const float mt = (mx == -INFINITY) ? -INFINITY : mx * c;
-      const bool need = mt > m + RESCALE_THRESHOLD;
-      if (__builtin_amdgcn_ballot_w64(need)) {
-        const float mnew = need ? mt : m;
-        const float alpha = __builtin_amdgcn_exp2f(m - mnew);   // 0 when m = -inf
-        l *= alpha;
-#pragma unroll
-        for (int u = 0; u < OT; ++u)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[u][r] *= alpha;
-        m = mnew;
-      }
-      const float mneg = (m == -INFINITY) ? 0.f : -m;
-      f32x8 pv[4];
-      float lsum = 0.f;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[t][r], c, mneg));
-          if (partial) e = ((vis0 >> (16 * t + r)) & 1u) ? e : 0.f;
-          lsum += e;
-          pv[2 * t + (r >> 3)][r & 7] = e;
-        }
-      l += lsum;
-      // ---- O^T += V^T P^T over four 16-key steps
+  // Tile j: softmax, O += P V, and (HAS_NEXT) the scores of tile j+1, as an explicit program of
+  // 4 * SPS slots with one MFMA each (sched_barrier keeps the compiler from moving work across
+  // slots):
+  //   * the scores of tile j+1 (QK, both 32-key halves alternating so that consecutive MFMAs
+  //     are independent) and O += P_s V_s for the four 16-key steps s of tile j interleave, QPS
+  //     QK slots then OT PV slots per step;
+  //   * K and V fragments are read from LDS two slots of their kind ahead of their MFMA;
+  //   * the probabilities P_s of tile j are computed in the SPS slots before PV step s (P_0 in
+  //     the QK slots of step 0), so the exponentials run under the MFMAs;
+  //   * the row maximum of tile j+1 is taken under the last PV MFMAs.
+  // Scores of hidden keys arrive as -inf (see mask_tile), whose exponential is exactly 0;
+  // c > 0 always (scale 0 runs with Q = 0). mxc is the row maximum of tile j; mxn returns that
+  // of tile j+1 (before any masking of tile j+1).
+  auto tile = [&](auto has_next, const f32x16 (&sc)[2], float mxc, f32x16 (&sn)[2],
+                  float& mxn, const unsigned char* kbuf, const unsigned char* vbuf) {
+    constexpr bool HAS_NEXT = decltype(has_next)::value;
+    update_max<D>(mxc, c, m, l, acc);
+    const float mneg = (m == -INFINITY) ? 0.f : -m;
+    float lsum = 0.f;
+    auto prob = [&](f32x8& pe, int ps, int e) {
+      const float ex =
+          __builtin_amdgcn_exp2f(__builtin_fmaf(sc[ps >> 1][8 * (ps & 1) + e], c, mneg));
+      lsum += ex;
+      pe[e] = ex;
+    };
+    if (!HAS_NEXT) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const u32x4 pb = M::pack(pv[s]);
-        // V^T fragment for keys 16s + 8e' + 4h + (0..3), e' = 0, 1; lane group g of 16 lanes
-        // reads 4 rows x 16 columns.
-        const int g = lane >> 4;
-        const int jj = lane & 15;
-        const int row_a = 16 * s + 4 * (g >> 1) + (jj >> 2);
-        const int colb = 16 * (g & 1) + 4 * (jj & 3);
+        f32x8 pe;
 #pragma unroll
-        for (int u = 0; u < OT; ++u) {
-          const u32x2 lo = lds_read_tr16(vs + row_a * T::VS + 32 * u + colb);
-          const u32x2 hi = lds_read_tr16(vs + (row_a + 8) * T::VS + 32 * u + colb);
-          const u32x4 a = u32x4{lo[0], lo[1], hi[0], hi[1]};
-          acc[u] = M::run(a, pb, acc[u]);
-        }
+        for (int e = 0; e < 8; ++e) prob(pe, s, e);
+        pv_step<DT, D>(acc, vbuf, f, s, M::pack(pe));
       }
+      l += lsum;
+      return;
     }
-    if (more) {
-      uint16_t* nk = smem + (buf ^ 1) * T::BUF_ELEMS;
-      store_tile<D>(nk, T::KS, tid, kreg);
-      store_tile<D>(nk + T::K_ELEMS, T::VS, tid, vreg);
+    constexpr int NQK = 2 * KSTEPS;   // score MFMAs of one tile
+    constexpr int QPS = NQK / 4;      // ... per PV step
+    constexpr int SPS = QPS + OT;     // slots per PV step
+    u32x4 kf[NQK];
+    u32x4 vf[4 * OT];
+    u32x4 pb[4];
+    f32x8 pe;
+    float mx = -INFINITY;
+    auto kload = [&](int idx) {
+      const int t = idx & 1, ks = idx >> 1;
+      kf[idx] = *(const u32x4*)(kbuf + f.kaddr[ks & 3] + (ks >> 2) * 128 + t * 32 * G::ROW);
+    };
+    auto vload = [&](int pvi) {
+      const int s = pvi / OT, u = pvi % OT;
+      const unsigned char* base = vbuf + f.vaddr[u & 1] + (u >> 1) * 128 + 16 * s * G::ROW;
+      const u32x2 lo = lds_read_tr16(base);
+      const u32x2 hi = lds_read_tr16(base + 8 * G::ROW);
+      vf[pvi] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    };
+    kload(0);
+    kload(1);
+    vload(0);
+    vload(1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int g = 0; g < 4 * SPS; ++g) {
+      const int s = g / SPS, k = g % SPS;
+      if (k < QPS) {
+        const int idx = s * QPS + k;
+        if (idx + 2 < NQK) kload(idx + 2);
+        sn[idx & 1] = M::run(kf[idx], qf[idx >> 1], idx < 2 ? f32x16{} : sn[idx & 1]);
+      } else {
+        const int u = k - QPS, pvi = s * OT + u;
+        if (pvi + 2 < 4 * OT) vload(pvi + 2);
+        acc[u] = M::run(vf[pvi], pb[s], acc[u]);
+      }
+      int ps, e0, ne;
+      if (g < QPS) {
+        ps = 0;
+        ne = 8 / QPS;
+        e0 = g * ne;
+      } else {
+        ps = (g + OT) / SPS;
+        ne = 8 / SPS;
+        e0 = (g - (ps * SPS - OT)) * ne;
+      }
+      if (ps < 4) {
+#pragma unroll
+        for (int e = e0; e < e0 + ne; ++e) prob(pe, ps, e);
+        if (e0 + ne == 8) pb[ps] = M::pack(pe);
+      }
+      if (s == 3 && k >= QPS) {
+        const int u = k - QPS;
+        if (u == 0)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sn[0][r]);
+        if (u == OT / 2)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sn[1][r]);
+        if (u == OT - 1) mxn = pair_max(mx);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+    l += lsum;
+  };
+
+  // ---- prologue: K_0, V_0, K_1 in flight; scores of tile 0
+  if (ntiles > 0) dma(0, G::K0, G::V0);
+  if (ntiles > 1) dma(1, G::K1, -1);
+  wait_loads_and_lds();
+  __syncthreads();
+  f32x16 sA[2], sB[2];
+  float mxA = -INFINITY, mxB = -INFINITY;
+  if (ntiles > 0) {
+    qk_tile<DT, D>(sA, smem + G::K0, f, qf);
+    mxA = rowmax(sA);
+  }
+
+  // Tiles that straddle the causal diagonal (for this wave's 32 queries), valid_len or N: set
+  // the scores of hidden keys to -inf in place and recompute the row maximum. A tile wholly
+  // hidden from this wave (above its diagonal) becomes all -inf and adds exactly nothing.
+  // key = kb + 32t + 8(r/4) + 4h + r%4 is visible iff key - kb - 4h <= lim.
+  auto mask_tile = [&](f32x16 (&sc)[2], float& mxc, int kb) {
+    const bool full = (!CAUSAL || kb + kBN - 1 <= qa) && kb + kBN <= kv_end;
+    if (!full) {
+      int lim = kv_end - 1 - kb - 4 * h;
+      if (CAUSAL) lim = min(lim, qrow - kb - 4 * h);
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          sc[t][r] = (32 * t + 8 * (r >> 2) + (r & 3) <= lim) ? sc[t][r] : -INFINITY;
+      mxc = rowmax(sc);
+    }
+  };
+
+  // One iteration: tile j (parity P = j & 1) lives in K[P] / V[P] and its scores in cur;
+  // K_{j+1} is in K[P^1]. Every wave of the workgroup runs every tile, so the loop has one code
+  // path (apart from the rare masking and rescale branches).
+  auto step = [&](int j, auto parity, auto has_next, f32x16 (&cur)[2], float& mxc,
+                  f32x16 (&nxt)[2], float& mxn) {
+    constexpr int P = decltype(parity)::value;
+    constexpr int KCUR = P ? G::K1 : G::K0;
+    constexpr int KNXT = P ? G::K0 : G::K1;
+    constexpr int VCUR = P ? G::V1 : G::V0;
+    constexpr int VNXT = P ? G::V0 : G::V1;
+    wait_loads_and_lds();
     __syncthreads();
+    // K_{j+2} replaces K_j (its scores were computed last iteration); V_{j+1} replaces V_{j-1}.
+    if (j + 2 < ntiles) dma(j + 2, KCUR, -1);
+    if (j + 1 < ntiles) dma(j + 1, -1, VNXT);
+    mask_tile(cur, mxc, j * kBN);
+    tile(has_next, cur, mxc, nxt, mxn, smem + KNXT, smem + VCUR);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using T = std::true_type;
+  using F = std::false_type;
+  int j = 0;
+  for (; j + 2 < ntiles; j += 2) {
+    step(j, I0{}, T{}, sA, mxA, sB, mxB);
+    step(j + 1, I1{}, T{}, sB, mxB, sA, mxA);
+  }
+  if (j + 1 < ntiles) {
+    step(j, I0{}, T{}, sA, mxA, sB, mxB);
+    step(j + 1, I1{}, F{}, sB, mxB, sA, mxA);
+  } else if (j < ntiles) {
+    step(j, I0{}, F{}, sA, mxA, sB, mxB);
   }
 
   // ---- epilogue: O = acc / l (0 for a row with no visible key), LSE = m ln2 + ln l
@@ -335,6 +519,16 @@ void attn_fwd_kernel(Params p) {
     if (p.lse && h == 0)
       p.lse[(size_t)bh * p.N + qrow] = empty ? -INFINITY : m * kLn2 + logf(lt);
   }
+}
+
+// The body uses device-only types (buffer resources), so only the device pass compiles it;
+// the host pass needs no more than the kernel's signature to emit its launch stub.
+template <int DT, int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_kernel(Params p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  attn_fwd_body<DT, D, CAUSAL>(p);
+#endif
 }
 
 template <int DT, int D, bool CAUSAL>
@@ -403,8 +597,11 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* out, 
   p.N = N;
   p.group = Hq / Hkv;
   p.nqt = (N + kBM - 1) / kBM;
+  p.xcd_order = ((int64_t)B * Hkv) % 8 == 0 ? 1 : 0;
   p.c = fabsf(scale) * kLog2e;
   p.qsign = scale < 0.f ? 0x80008000u : 0u;
+  p.qmask = scale == 0.f ? 0u : 0xffffffffu;
+  if (scale == 0.f) p.c = 1.0f;
   const int64_t nwg = (int64_t)B * Hq * p.nqt;
   hipStream_t s = (hipStream_t)stream;
   const hipError_t e = dtype == ATTN_BF16 ? dispatch_d<ATTN_BF16>(p, D, causal != 0, nwg, s)

@@ -87,7 +87,7 @@ def test_validate_accepts_good_arguments(lib):
     (dict(N=0), sdp.ATTN_ERR_SHAPE),
     (dict(N=-3), sdp.ATTN_ERR_SHAPE),
     (dict(Hq=8, Hkv=3), sdp.ATTN_ERR_SHAPE),
-    (dict(N=(1 << 24) + 1), sdp.ATTN_ERR_SHAPE),
+    (dict(N=(1 << 22) + 1), sdp.ATTN_ERR_SHAPE),
     (dict(D=96), sdp.ATTN_ERR_HEAD_DIM),
     (dict(D=256), sdp.ATTN_ERR_HEAD_DIM),
     (dict(D=32), sdp.ATTN_ERR_HEAD_DIM),
