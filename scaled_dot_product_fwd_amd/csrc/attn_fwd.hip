@@ -73,6 +73,20 @@ struct Geo {
   static constexpr int OT = D / 32;                  // 32-row tiles of O^T
   static constexpr int K0 = 0, K1 = TILE, V0 = 2 * TILE, V1 = 3 * TILE;
   static constexpr int LDS = 4 * TILE;
+  // LDS row r of a tile stores global 16-byte chunk c at chunk c ^ swz(r). The swizzles keep
+  // every LDS read phase on distinct banks whether the LDS serves 128 or 256 bytes per clock:
+  //  * K is read as 16-byte A fragments, 16 consecutive rows at one logical chunk per phase:
+  //    the 16 rows must land in 16 distinct 16-byte bank slots (8 among rows 0..7).
+  //  * V is read with ds_read_b64_tr_b16: a 16-lane group reads 4 consecutive rows x 32 bytes,
+  //    a 32-lane half the same 4 rows x 64 bytes. XOR of the 32-byte pair index by
+  //    F = {0, 3, 5, 6}[r & 3] (D = 128) puts the 4 rows on distinct pairs mod 128 bytes and on
+  //    distinct 64-byte blocks mod 256 bytes; with 128-byte rows (D = 64) F = r & 3 does both.
+  __device__ static constexpr int kswz(int r) {
+    return D == 128 ? (r & 15) : ((r & 7) ^ ((r >> 3) & 1));
+  }
+  __device__ static constexpr int vswz(int r) {
+    return D == 128 ? 2 * ((0x6530 >> (4 * (r & 3))) & 15) : 2 * (r & 3);
+  }
 };
 
 struct Params {
@@ -145,8 +159,8 @@ __device__ inline void wait_loads_and_lds() {
 // Per-wave, per-thread state of the main loop (registers).
 template <int D>
 struct Frag {
-  uint32_t kaddr[4];   // LDS byte offsets of this lane's K fragments for k-steps 0..3
-  uint32_t vaddr[2];   // LDS byte offsets of this lane's V^T fragments for u = 0, 1
+  uint32_t kaddr[D / 16];   // LDS byte offsets of this lane's K fragment for each k-step
+  uint32_t vaddr[D / 32];   // LDS byte offsets of this lane's V^T fragment for each d-tile u
 };
 
 template <int DT, int D>
@@ -159,7 +173,7 @@ __device__ inline void qk_tile(f32x16 (&s)[2], const unsigned char* kbuf, const 
     s[t] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < G::KSTEPS; ++ks) {
-      const u32x4 a = *(const u32x4*)(kbuf + f.kaddr[ks & 3] + (ks >> 2) * 128 + t * 32 * G::ROW);
+      const u32x4 a = *(const u32x4*)(kbuf + f.kaddr[ks] + t * 32 * G::ROW);
       s[t] = M::run(a, qf[ks], s[t]);
     }
   }
@@ -173,7 +187,7 @@ __device__ inline void pv_step(f32x16 (&acc)[Geo<D>::OT], const unsigned char* v
   using M = Mfma<DT>;
 #pragma unroll
   for (int u = 0; u < G::OT; ++u) {
-    const unsigned char* base = vbuf + f.vaddr[u & 1] + (u >> 1) * 128 + 16 * s * G::ROW;
+    const unsigned char* base = vbuf + f.vaddr[u] + 16 * s * G::ROW;
     const u32x2 lo = lds_read_tr16(base);
     const u32x2 hi = lds_read_tr16(base + 8 * G::ROW);
     acc[u] = M::run(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb, acc[u]);
@@ -257,19 +271,16 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
 
   // ---- DMA offsets: block (wave * LOADS + i) of a tile holds rows [blk * RPB, +RPB); lane
   // writes LDS chunk (lane % CH) of row (lane / CH) and fetches the global chunk that the row's
-  // swizzle maps there (K: chunk ^ (row & 7); V: chunk ^ 2 * (row & 3)). Rows 8 apart share a
-  // swizzle, so block i's offsets are block (i % KP)'s plus a constant: KP = 8 / RPB blocks
-  // (K) and one block (V) need their own registers.
-  constexpr int KP = 8 / G::RPB;
-  uint32_t koff[KP], voff0;
+  // swizzle maps there. V's swizzle depends on row & 3 only, the same in every block.
+  uint32_t koff[G::LOADS], voff0;
 #pragma unroll
-  for (int i = 0; i < KP; ++i) {
+  for (int i = 0; i < G::LOADS; ++i) {
     const int row = (wave * G::LOADS + i) * G::RPB + lane / G::CH;
-    koff[i] = row * G::ROW + (((lane % G::CH) ^ (row & 7)) * 16);
+    koff[i] = row * G::ROW + (((lane % G::CH) ^ G::kswz(row)) * 16);
   }
   {
     const int row = wave * G::LOADS * G::RPB + lane / G::CH;
-    voff0 = row * G::ROW + (((lane % G::CH) ^ ((row & 3) << 1)) * 16);
+    voff0 = row * G::ROW + (((lane % G::CH) ^ G::vswz(row)) * 16);
   }
   auto dma = [&](int tile, int kdst, int vdst) {
     const int soff = tile * G::TILE;
@@ -278,29 +289,30 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
       const int blk = (wave * G::LOADS + i) * 1024;
       if (kdst >= 0)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(smem + kdst + blk), 16,
-                                                 koff[i % KP], soff + (i / KP) * KP * 1024, 0, 0);
+                                                 koff[i], soff, 0, 0);
       if (vdst >= 0)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(smem + vdst + blk), 16,
                                                  voff0, soff + i * 1024, 0, 0);
     }
   };
 
-  // ---- LDS fragment offsets (see the swizzles above)
+  // ---- LDS fragment offsets (see the swizzles in Geo)
   Frag<D> f;
   {
-    const int c = (ql >> 1) & 3;
-    const int hb = (h ^ ql) & 1;
+    // K: lane reads row ql (+32 for the second half), logical chunk 2s + h.
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) f.kaddr[s4] = ql * G::ROW + 16 * (2 * (s4 ^ c) + hb);
+    for (int ks = 0; ks < KSTEPS; ++ks)
+      f.kaddr[ks] = ql * G::ROW + 16 * ((2 * ks + h) ^ G::kswz(ql));
+    // V^T via ds_read_b64_tr_b16: lane 16g + jj reads row 4(g/2) + jj/4 (+16s, +8 for the
+    // second 4 keys), columns 32u + 16(g%2) + 4(jj%4) .. +3, i.e. logical chunk
+    // 4u + 2(g%2) + (jj%4)/2 and byte 8(jj%2) within it.
     const int g = lane >> 4;
     const int jj = lane & 15;
-    const int y = 2 * (jj >> 2);
-    const int x = 2 * (g & 1) + ((jj & 3) >> 1);
-    const int yb = (jj >> 3) & 1;
-    const int xy = (x ^ y) & 3;
-    const int base = (4 * (g >> 1) + (jj >> 2)) * G::ROW + 16 * xy + 8 * (jj & 1);
-    f.vaddr[0] = base + 64 * yb;
-    f.vaddr[1] = base + 64 * (1 - yb);
+    const int row = 4 * (g >> 1) + (jj >> 2);
+#pragma unroll
+    for (int u = 0; u < OT; ++u)
+      f.vaddr[u] = row * G::ROW + 16 * ((4 * u + 2 * (g & 1) + ((jj & 3) >> 1)) ^ G::vswz(row)) +
+                   8 * (jj & 1);
   }
 
   // ---- Q fragments: B operand of S^T = K Q^T. Lane l holds Q[row][16s + 8h .. +7].
@@ -339,7 +351,9 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
   //   * the scores of tile j+1 (QK, both 32-key halves alternating so that consecutive MFMAs
   //     are independent) and O += P_s V_s for the four 16-key steps s of tile j interleave, QPS
   //     QK slots then OT PV slots per step;
-  //   * K and V fragments are read from LDS two slots of their kind ahead of their MFMA;
+  //   * K and V fragments are read from LDS three slots of their kind ahead of their MFMA;
+  //   * the wave raises its issue priority for the program, so that of two waves sharing a
+  //     SIMD the one inside its MFMA stream is served first;
   //   * the probabilities P_s of tile j are computed in the SPS slots before PV step s (P_0 in
   //     the QK slots of step 0), so the exponentials run under the MFMAs;
   //   * the row maximum of tile j+1 is taken under the last PV MFMAs.
@@ -351,11 +365,17 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
     constexpr bool HAS_NEXT = decltype(has_next)::value;
     update_max<D>(mxc, c, m, l, acc);
     const float mneg = (m == -INFINITY) ? 0.f : -m;
-    float lsum = 0.f;
+    float lsum = 0.f, pend1 = 0.f, pend2 = 0.f;
     auto prob = [&](f32x8& pe, int ps, int e) {
       const float ex =
           __builtin_amdgcn_exp2f(__builtin_fmaf(sc[ps >> 1][8 * (ps & 1) + e], c, mneg));
-      lsum += ex;
+      // Add the exponential from two calls (slots) earlier, so that no instruction in a slot
+      // waits on one issued in the same slot, and keep the running sum here: otherwise the
+      // compiler sinks all the additions past the MFMA stream.
+      lsum += pend2;
+      pend2 = pend1;
+      pend1 = ex;
+      asm volatile("" : "+v"(lsum));
       pe[e] = ex;
     };
     if (!HAS_NEXT) {
@@ -366,7 +386,7 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
         for (int e = 0; e < 8; ++e) prob(pe, s, e);
         pv_step<DT, D>(acc, vbuf, f, s, M::pack(pe));
       }
-      l += lsum;
+      l += lsum + pend1 + pend2;
       return;
     }
     constexpr int NQK = 2 * KSTEPS;   // score MFMAs of one tile
@@ -379,30 +399,33 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
     float mx = -INFINITY;
     auto kload = [&](int idx) {
       const int t = idx & 1, ks = idx >> 1;
-      kf[idx] = *(const u32x4*)(kbuf + f.kaddr[ks & 3] + (ks >> 2) * 128 + t * 32 * G::ROW);
+      kf[idx] = *(const u32x4*)(kbuf + f.kaddr[ks] + t * 32 * G::ROW);
     };
     auto vload = [&](int pvi) {
       const int s = pvi / OT, u = pvi % OT;
-      const unsigned char* base = vbuf + f.vaddr[u & 1] + (u >> 1) * 128 + 16 * s * G::ROW;
+      const unsigned char* base = vbuf + f.vaddr[u] + 16 * s * G::ROW;
       const u32x2 lo = lds_read_tr16(base);
       const u32x2 hi = lds_read_tr16(base + 8 * G::ROW);
       vf[pvi] = u32x4{lo[0], lo[1], hi[0], hi[1]};
     };
+    __builtin_amdgcn_s_setprio(1);
     kload(0);
     kload(1);
+    kload(2);
     vload(0);
     vload(1);
+    vload(2);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int g = 0; g < 4 * SPS; ++g) {
       const int s = g / SPS, k = g % SPS;
       if (k < QPS) {
         const int idx = s * QPS + k;
-        if (idx + 2 < NQK) kload(idx + 2);
+        if (idx + 3 < NQK) kload(idx + 3);
         sn[idx & 1] = M::run(kf[idx], qf[idx >> 1], idx < 2 ? f32x16{} : sn[idx & 1]);
       } else {
         const int u = k - QPS, pvi = s * OT + u;
-        if (pvi + 2 < 4 * OT) vload(pvi + 2);
+        if (pvi + 3 < 4 * OT) vload(pvi + 3);
         acc[u] = M::run(vf[pvi], pb[s], acc[u]);
       }
       int ps, e0, ne;
@@ -432,7 +455,8 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    l += lsum;
+    __builtin_amdgcn_s_setprio(0);
+    l += lsum + pend1 + pend2;
   };
 
   // ---- prologue: K_0, V_0, K_1 in flight; scores of tile 0
