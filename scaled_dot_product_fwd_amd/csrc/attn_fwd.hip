@@ -315,18 +315,14 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
                    8 * (jj & 1);
   }
 
-  // ---- Q fragments: B operand of S^T = K Q^T. Lane l holds Q[row][16s + 8h .. +7].
-  const uint16_t* __restrict__ qbase = p.q + (size_t)bh * p.N * D;
+  // ---- Q fragments: B operand of S^T = K Q^T. Lane l holds Q[row][16s + 8h .. +7]. Rows past
+  // N read row N-1 (in bounds; their outputs are never stored). All loads are issued before
+  // any result is used (the sign/zero masks are applied after the prologue's wait).
+  const uint16_t* __restrict__ qsrc =
+      p.q + ((size_t)bh * p.N + min(qrow, p.N - 1)) * D + 8 * h;
   u32x4 qf[KSTEPS];
 #pragma unroll
-  for (int s = 0; s < KSTEPS; ++s) {
-    if (qrow < p.N) {
-      qf[s] = *(const u32x4*)(qbase + (size_t)qrow * D + 16 * s + 8 * h);
-      qf[s] = (qf[s] ^ p.qsign) & p.qmask;
-    } else {
-      qf[s] = u32x4{0, 0, 0, 0};
-    }
-  }
+  for (int s = 0; s < KSTEPS; ++s) qf[s] = *(const u32x4*)(qsrc + 16 * s);
 
   f32x16 acc[OT];
 #pragma unroll
@@ -463,6 +459,8 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
   if (ntiles > 0) dma(0, G::K0, G::V0);
   if (ntiles > 1) dma(1, G::K1, -1);
   wait_loads_and_lds();
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) qf[s] = (qf[s] ^ p.qsign) & p.qmask;
   __syncthreads();
   f32x16 sA[2], sB[2];
   float mxA = -INFINITY, mxB = -INFINITY;
@@ -523,26 +521,38 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
     step(j, I0{}, F{}, sA, mxA, sB, mxB);
   }
 
-  // ---- epilogue: O = acc / l (0 for a row with no visible key), LSE = m ln2 + ln l
+  // ---- epilogue: O = acc / l (0 for a row with no visible key), LSE = m ln2 + ln l.
+  // Each wave stages its 32 x D output rows in LDS (16-byte chunk c of row q at chunk
+  // c ^ (q % CH)), then writes whole rows with 16-byte stores: consecutive lanes cover
+  // consecutive bytes of a row.
   const float lt = pair_sum(l);
-  if (qrow < p.N) {
-    const bool empty = !(lt > 0.f);
-    const float inv = empty ? 0.f : 1.0f / lt;
-    uint16_t* orow = p.o + ((size_t)bh * p.N + qrow) * D;
+  const bool empty = !(lt > 0.f);
+  const float inv = empty ? 0.f : 1.0f / lt;
+  wait_loads_and_lds();
+  __syncthreads();   // every wave is done reading K/V from LDS
+  unsigned char* ost = smem + wave * 32 * G::ROW;
 #pragma unroll
-    for (int u = 0; u < OT; ++u)
+  for (int u = 0; u < OT; ++u)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int d0 = 32 * u + 8 * r4 + 4 * h;
-        uint32_t w0 = (uint32_t)M::round1(acc[u][4 * r4 + 0] * inv) |
-                      ((uint32_t)M::round1(acc[u][4 * r4 + 1] * inv) << 16);
-        uint32_t w1 = (uint32_t)M::round1(acc[u][4 * r4 + 2] * inv) |
-                      ((uint32_t)M::round1(acc[u][4 * r4 + 3] * inv) << 16);
-        *(u32x2*)(orow + d0) = u32x2{w0, w1};
-      }
-    if (p.lse && h == 0)
-      p.lse[(size_t)bh * p.N + qrow] = empty ? -INFINITY : m * kLn2 + logf(lt);
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int c = 4 * u + r4;   // chunk of d = 32u + 8 r4 + 4h .. +3
+      const uint32_t w0 = (uint32_t)M::round1(acc[u][4 * r4 + 0] * inv) |
+                          ((uint32_t)M::round1(acc[u][4 * r4 + 1] * inv) << 16);
+      const uint32_t w1 = (uint32_t)M::round1(acc[u][4 * r4 + 2] * inv) |
+                          ((uint32_t)M::round1(acc[u][4 * r4 + 3] * inv) << 16);
+      *(u32x2*)(ost + ql * G::ROW + 16 * (c ^ (ql & (G::CH - 1))) + 8 * h) = u32x2{w0, w1};
+    }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  constexpr int RPI = 64 / G::CH;   // rows per store instruction
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = i * RPI + lane / G::CH;
+    const int cc = lane % G::CH;
+    const u32x4 v = *(const u32x4*)(ost + r * G::ROW + 16 * (cc ^ (r & (G::CH - 1))));
+    if (qa + r < p.N) *(u32x4*)(p.o + ((size_t)bh * p.N + qa + r) * D + 8 * cc) = v;
   }
+  if (p.lse && h == 0 && qrow < p.N)
+    p.lse[(size_t)bh * p.N + qrow] = empty ? -INFINITY : m * kLn2 + logf(lt);
 }
 
 // The body uses device-only types (buffer resources), so only the device pass compiles it;
