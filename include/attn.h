@@ -61,11 +61,15 @@ typedef enum {
     ATTN_ERR_DTYPE = -4,    /* dtype is not ATTN_F16 or ATTN_BF16 */
     ATTN_ERR_SCALE = -5,    /* scale is NaN or infinite */
     ATTN_ERR_LAUNCH = -6,   /* the HIP runtime reported an error at launch; query HIP for it */
-    ATTN_ERR_ALIAS = -7     /* out or lse overlaps an input, or out overlaps lse */
+    ATTN_ERR_ALIAS = -7,    /* out or lse overlaps an input, or out overlaps lse */
+    ATTN_ERR_LAYOUT = -8    /* a pointer is not 16-byte aligned, a stride is negative or not a
+                               multiple of 8 elements, rows are less than D elements apart, or
+                               two output rows share memory */
 } attn_status_t;
 
 /* Size limits checked by attn_fwd_validate: N <= ATTN_MAX_N and
- * B * Hq * ceil(N / 128) <= ATTN_MAX_TILES. */
+ * B * Hq * ceil(N / 128) <= ATTN_MAX_TILES; with strides, also (N + 64) * (K or V row stride)
+ * * 2 + 2 * D < 2^31 (the bytes the kernel may address inside one K or V head). */
 #define ATTN_MAX_N (1 << 22)
 #define ATTN_MAX_TILES 2147483647LL
 
@@ -93,7 +97,8 @@ typedef enum {
  *
  * Ownership: the caller allocates and owns every buffer; the call is asynchronous and the
  * buffers must stay valid until the stream has finished it. Returns ATTN_OK once the work is
- * queued, an argument error (nothing launched, nothing written), or ATTN_ERR_LAUNCH.
+ * queued, an argument error (nothing launched, nothing written; a misaligned pointer is
+ * ATTN_ERR_LAYOUT), or ATTN_ERR_LAUNCH.
  */
 int attn_fwd(const void *q, const void *k, const void *v, void *out, float *lse, int B, int Hq,
              int Hkv, int N, int D, float scale, int causal, const int32_t *valid_len, int dtype,
@@ -108,10 +113,50 @@ int attn_fwd_validate(const void *q, const void *k, const void *v, const void *o
                       const float *lse, int B, int Hq, int Hkv, int N, int D, float scale,
                       int causal, const int32_t *valid_len, int dtype);
 
+/*
+ * attn_fwd_strided -- attn_fwd on tensors given by strides, e.g. Q, K, V and O stored as
+ * [B, N, H, D] (rows of all heads of one position together), rows padded past D, or K and V
+ * shared by every batch (batch stride 0). The Triton kernel of "Triton Cuda Attention" (its
+ * forward section) and tiny_flash_attn_triton.py take the same four tensors with full strides,
+ * and the masked multi-head attention CUDA article (section 2.1) names both the [B, N, H, D]
+ * and the [B, H, N, D] layouts.
+ *
+ *   q, k, v, out   device pointers as in attn_fwd, 16-byte aligned.
+ *   q_strides, k_strides, v_strides, out_strides
+ *                  host pointers to three int64 element strides each: batch, head, row (the
+ *                  sequence position). The D elements of a row are contiguous. Element
+ *                  (b, h, i, d) of a tensor is at ptr + b*s[0] + h*s[1] + i*s[2] + d. NULL means
+ *                  the contiguous [B, H, N, D] strides {H*N*D, N*D, D}. The arrays are read
+ *                  during the call only.
+ *   lse            as in attn_fwd: contiguous [B, Hq, N] float32 or NULL.
+ *   all else       as in attn_fwd.
+ *
+ * Every stride must be >= 0 and a multiple of 8 elements, and row strides >= D (ATTN_ERR_LAYOUT
+ * otherwise). Inputs may share memory with each other (for instance Q, K and V as views of one
+ * packed tensor, or a zero batch stride). The output's rows must be distinct (its strides,
+ * ordered, must each step past the extent of the smaller ones). For the alias check each tensor
+ * counts as the whole byte range from its pointer to the end of its last row, so out must lie
+ * outside the ranges of q, k, v and lse. Returns as attn_fwd.
+ */
+int attn_fwd_strided(const void *q, const int64_t *q_strides, const void *k,
+                     const int64_t *k_strides, const void *v, const int64_t *v_strides,
+                     void *out, const int64_t *out_strides, float *lse, int B, int Hq, int Hkv,
+                     int N, int D, float scale, int causal, const int32_t *valid_len, int dtype,
+                     void *stream);
+
+/* attn_fwd_strided_validate -- the host-only argument check of attn_fwd_strided (no HIP call,
+ * no pointer dereferenced except the three-element stride arrays). */
+int attn_fwd_strided_validate(const void *q, const int64_t *q_strides, const void *k,
+                              const int64_t *k_strides, const void *v,
+                              const int64_t *v_strides, const void *out,
+                              const int64_t *out_strides, const float *lse, int B, int Hq,
+                              int Hkv, int N, int D, float scale, int causal,
+                              const int32_t *valid_len, int dtype);
+
 /* attn_status_string -- a static, NUL-terminated description of a return code (never NULL). */
 const char *attn_status_string(int status);
 
-/* attn_version -- the library's interface version, currently 1. */
+/* attn_version -- the library's interface version, currently 2 (2 added attn_fwd_strided). */
 int attn_version(void);
 
 #ifdef __cplusplus

@@ -4,10 +4,12 @@ A thin ctypes binding over ``libattn.so`` (C ABI declared in ``include/attn.h``)
 the computation runs in the library's HIP kernels; this module only marshals arguments. There is
 no fallback: if the library is missing, calls raise ``ImportError``.
 
-Raw entry points (same names and argument order as the C ABI; pointers are integers):
-    attn_fwd, attn_fwd_validate, attn_status_string, attn_version
+Raw entry points (same names and argument order as the C ABI; pointers are integers, stride
+arguments are 3-sequences of element strides or None):
+    attn_fwd, attn_fwd_validate, attn_fwd_strided, attn_fwd_strided_validate,
+    attn_status_string, attn_version
 Convenience for torch tensors (device memory and streams only):
-    forward(q, k, v, causal=..., valid_len=None, scale=None, out=None, lse=None)
+    forward(q, k, v, causal=..., valid_len=None, scale=None, out=None, lse=None, layout="bhnd")
 """
 from __future__ import annotations
 
@@ -16,7 +18,8 @@ import os
 from typing import Optional, Tuple
 
 __all__ = ["ATTN_F16", "ATTN_BF16", "AttnError", "attn_fwd", "attn_fwd_validate",
-           "attn_status_string", "attn_version", "forward", "library_path", "load_library"]
+           "attn_fwd_strided", "attn_fwd_strided_validate", "attn_status_string",
+           "attn_version", "forward", "library_path", "load_library"]
 
 ATTN_F16 = 0
 ATTN_BF16 = 1
@@ -29,12 +32,14 @@ ATTN_ERR_DTYPE = -4
 ATTN_ERR_SCALE = -5
 ATTN_ERR_LAUNCH = -6
 ATTN_ERR_ALIAS = -7
+ATTN_ERR_LAYOUT = -8
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libattn.so")
 _lib: Optional[ctypes.CDLL] = None
 
 _c_int, _c_float, _vp = ctypes.c_int, ctypes.c_float, ctypes.c_void_p
+_i64p = ctypes.POINTER(ctypes.c_int64)
 
 
 class AttnError(RuntimeError):
@@ -64,6 +69,14 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_fwd_validate.restype = _c_int
     lib.attn_fwd_validate.argtypes = [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int,
                                       _c_int, _c_float, _c_int, _vp, _c_int]
+    lib.attn_fwd_strided.restype = _c_int
+    lib.attn_fwd_strided.argtypes = [_vp, _i64p, _vp, _i64p, _vp, _i64p, _vp, _i64p, _vp, _c_int,
+                                     _c_int, _c_int, _c_int, _c_int, _c_float, _c_int, _vp,
+                                     _c_int, _vp]
+    lib.attn_fwd_strided_validate.restype = _c_int
+    lib.attn_fwd_strided_validate.argtypes = [_vp, _i64p, _vp, _i64p, _vp, _i64p, _vp, _i64p,
+                                              _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                              _c_float, _c_int, _vp, _c_int]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_status_string.argtypes = [_c_int]
     lib.attn_version.restype = _c_int
@@ -89,6 +102,36 @@ def attn_fwd_validate(q: int, k: int, v: int, out: int, lse: Optional[int], B: i
                                             int(causal), valid_len, dtype)
 
 
+def _strides(st):
+    if st is None:
+        return None
+    st = tuple(int(x) for x in st)
+    if len(st) != 3:
+        raise ValueError("a stride argument has three entries (batch, head, row)")
+    return (ctypes.c_int64 * 3)(*st)
+
+
+def attn_fwd_strided(q: int, q_strides, k: int, k_strides, v: int, v_strides, out: int,
+                     out_strides, lse: Optional[int], B: int, Hq: int, Hkv: int, N: int, D: int,
+                     scale: float, causal: int, valid_len: Optional[int], dtype: int,
+                     stream: Optional[int]) -> int:
+    """C ``attn_fwd_strided``; strides are (batch, head, row) element strides or None."""
+    return load_library().attn_fwd_strided(q, _strides(q_strides), k, _strides(k_strides), v,
+                                           _strides(v_strides), out, _strides(out_strides), lse,
+                                           B, Hq, Hkv, N, D, scale, int(causal), valid_len,
+                                           dtype, stream)
+
+
+def attn_fwd_strided_validate(q: int, q_strides, k: int, k_strides, v: int, v_strides, out: int,
+                              out_strides, lse: Optional[int], B: int, Hq: int, Hkv: int,
+                              N: int, D: int, scale: float, causal: int,
+                              valid_len: Optional[int], dtype: int) -> int:
+    """C ``attn_fwd_strided_validate``: host-only argument check, no HIP call."""
+    return load_library().attn_fwd_strided_validate(
+        q, _strides(q_strides), k, _strides(k_strides), v, _strides(v_strides), out,
+        _strides(out_strides), lse, B, Hq, Hkv, N, D, scale, int(causal), valid_len, dtype)
+
+
 def attn_status_string(status: int) -> str:
     return load_library().attn_status_string(status).decode()
 
@@ -107,37 +150,50 @@ def _dtype_code(t) -> int:
 
 
 def forward(q, k, v, causal: bool, valid_len=None, scale: Optional[float] = None, out=None,
-            lse=None, want_lse: bool = True, stream=None) -> Tuple[object, Optional[object]]:
-    """Run attn_fwd on contiguous [B,H,N,D] torch tensors on the current (or given) stream.
+            lse=None, want_lse: bool = True, stream=None,
+            layout: str = "bhnd") -> Tuple[object, Optional[object]]:
+    """Run the attention forward on torch device tensors on the current (or given) stream.
 
-    Allocates ``out`` ([B,Hq,N,D], q's dtype) and ``lse`` ([B,Hq,N] float32) with torch when
-    they are not given. Returns (out, lse); lse is None when want_lse is False and none given.
+    ``layout`` names the order of the four dimensions of q, k, v and out: "bhnd" for
+    [B, H, N, D] (the default) or "bnhd" for [B, N, H, D]. Any strides are accepted as long as
+    the last (D) dimension is contiguous; contiguous [B, H, N, D] tensors take attn_fwd, all
+    others attn_fwd_strided (no copies either way).
+
+    Allocates ``out`` (q's shape, layout and dtype, contiguous) and ``lse`` ([B, Hq, N] float32)
+    with torch when they are not given. Returns (out, lse); lse is None when want_lse is False
+    and none was given.
     """
     import torch
+    if layout not in ("bhnd", "bnhd"):
+        raise ValueError("layout must be 'bhnd' or 'bnhd'")
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
-        raise ValueError("q, k, v must be 4-D [B, H, N, D]")
-    B, Hq, N, D = q.shape
-    Hkv = k.shape[1]
-    if tuple(k.shape) != (B, Hkv, N, D) or tuple(v.shape) != tuple(k.shape):
-        raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape),
-                                                              tuple(v.shape)))
-    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
-        raise ValueError("q, k, v must be contiguous")
+        raise ValueError("q, k, v must be 4-D")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k, v must share a dtype")
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
         raise ValueError("q, k, v must be device tensors")
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    # [B, H, N, D] views of every tensor
+    tr = (lambda t: t.transpose(1, 2)) if layout == "bnhd" else (lambda t: t)
+    qv, kv, vv, ov = tr(q), tr(k), tr(v), tr(out)
+    B, Hq, N, D = qv.shape
+    Hkv = kv.shape[1]
+    if tuple(kv.shape) != (B, Hkv, N, D) or tuple(vv.shape) != tuple(kv.shape):
+        raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape),
+                                                              tuple(v.shape)))
+    if tuple(ov.shape) != (B, Hq, N, D) or out.dtype != q.dtype or not out.is_cuda:
+        raise ValueError("out must be a device tensor of q's shape and dtype")
+    for name, t in (("q", qv), ("k", kv), ("v", vv), ("out", ov)):
+        if t.stride(3) != 1:
+            raise ValueError("%s: the D dimension must be contiguous" % name)
     if scale is None:
         scale = 1.0 / float(D) ** 0.5
-    if out is None:
-        out = torch.empty_like(q)
     if lse is None and want_lse:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
     if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, N)
                             or not lse.is_contiguous()):
         raise ValueError("lse must be a contiguous float32 [B, Hq, N] tensor")
-    if tuple(out.shape) != (B, Hq, N, D) or out.dtype != q.dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous [B, Hq, N, D] tensor of q's dtype")
     vl_ptr = None
     if valid_len is not None:
         if valid_len.dtype != torch.int32 or tuple(valid_len.shape) != (B,) or not valid_len.is_cuda:
@@ -145,9 +201,18 @@ def forward(q, k, v, causal: bool, valid_len=None, scale: Optional[float] = None
         vl_ptr = valid_len.data_ptr()
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    st = attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                  lse.data_ptr() if lse is not None else None, B, Hq, Hkv, N, D, float(scale),
-                  int(bool(causal)), vl_ptr, _dtype_code(q), stream.cuda_stream)
+    lse_ptr = lse.data_ptr() if lse is not None else None
+    if all(t.is_contiguous() for t in (qv, kv, vv, ov)):
+        st = attn_fwd(qv.data_ptr(), kv.data_ptr(), vv.data_ptr(), ov.data_ptr(), lse_ptr, B, Hq,
+                      Hkv, N, D, float(scale), int(bool(causal)), vl_ptr, _dtype_code(q),
+                      stream.cuda_stream)
+        where = "attn_fwd"
+    else:
+        st = attn_fwd_strided(qv.data_ptr(), qv.stride()[:3], kv.data_ptr(), kv.stride()[:3],
+                              vv.data_ptr(), vv.stride()[:3], ov.data_ptr(), ov.stride()[:3],
+                              lse_ptr, B, Hq, Hkv, N, D, float(scale), int(bool(causal)),
+                              vl_ptr, _dtype_code(q), stream.cuda_stream)
+        where = "attn_fwd_strided"
     if st != ATTN_OK:
-        raise AttnError(st)
+        raise AttnError(st, where)
     return out, lse

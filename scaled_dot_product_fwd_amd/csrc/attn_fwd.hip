@@ -100,6 +100,12 @@ struct Params {
   int group;         // Hq / Hkv
   int nqt;           // ceil(N / kBM)
   int xcd_order;     // 1: KV heads divide evenly over the 8 XCDs
+  // Element strides (batch, head, row) of Q, K, V and O; the D elements of a row are
+  // contiguous. Every stride is a multiple of 8 elements (16-byte rows).
+  int64_t qs_b, qs_h, qs_n;
+  int64_t ks_b, ks_h, ks_n;
+  int64_t vs_b, vs_h, vs_n;
+  int64_t os_b, os_h, os_n;
   float c;           // |scale| * log2(e)
   uint32_t qsign;    // 0x80008000 when scale < 0: Q is negated (exactly) instead
   uint32_t qmask;    // 0 when scale == 0: all scores are exactly 0 (and c is set to 1)
@@ -262,12 +268,15 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
   const int qa = q0 + wave * 32;            // first query of this wave
   const int qrow = qa + ql;
 
-  const size_t kv_off = (size_t)(b * p.Hkv + kvh) * p.N * D;
-  const uint32_t head_bytes = (uint32_t)p.N * G::ROW;
-  const __amdgpu_buffer_rsrc_t krs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + kv_off), (short)0, head_bytes, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t vrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + kv_off), (short)0, head_bytes, kBufferFlags);
+  // K and V of this (batch, KV head) as buffers spanning exactly its N rows: rows past N read
+  // as zeros. Row strides in bytes (the host keeps every span below 2^31 bytes).
+  const uint32_t krow = (uint32_t)p.ks_n * 2, vrow = (uint32_t)p.vs_n * 2;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.k + b * p.ks_b + kvh * p.ks_h), (short)0, (p.N - 1) * krow + G::ROW,
+      kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.v + b * p.vs_b + kvh * p.vs_h), (short)0, (p.N - 1) * vrow + G::ROW,
+      kBufferFlags);
 
   // ---- DMA offsets: block (wave * LOADS + i) of a tile holds rows [blk * RPB, +RPB); lane
   // writes LDS chunk (lane % CH) of row (lane / CH) and fetches the global chunk that the row's
@@ -276,23 +285,23 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
 #pragma unroll
   for (int i = 0; i < G::LOADS; ++i) {
     const int row = (wave * G::LOADS + i) * G::RPB + lane / G::CH;
-    koff[i] = row * G::ROW + (((lane % G::CH) ^ G::kswz(row)) * 16);
+    koff[i] = row * krow + (((lane % G::CH) ^ G::kswz(row)) * 16);
   }
   {
     const int row = wave * G::LOADS * G::RPB + lane / G::CH;
-    voff0 = row * G::ROW + (((lane % G::CH) ^ G::vswz(row)) * 16);
+    voff0 = row * vrow + (((lane % G::CH) ^ G::vswz(row)) * 16);
   }
   auto dma = [&](int tile, int kdst, int vdst) {
-    const int soff = tile * G::TILE;
+    const uint32_t row0 = (uint32_t)tile * kBN;
 #pragma unroll
     for (int i = 0; i < G::LOADS; ++i) {
       const int blk = (wave * G::LOADS + i) * 1024;
       if (kdst >= 0)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(smem + kdst + blk), 16,
-                                                 koff[i], soff, 0, 0);
+                                                 koff[i], row0 * krow, 0, 0);
       if (vdst >= 0)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(smem + vdst + blk), 16,
-                                                 voff0, soff + i * 1024, 0, 0);
+                                                 voff0, (row0 + i * G::RPB) * vrow, 0, 0);
     }
   };
 
@@ -319,7 +328,7 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
   // N read row N-1 (in bounds; their outputs are never stored). All loads are issued before
   // any result is used (the sign/zero masks are applied after the prologue's wait).
   const uint16_t* __restrict__ qsrc =
-      p.q + ((size_t)bh * p.N + min(qrow, p.N - 1)) * D + 8 * h;
+      p.q + b * p.qs_b + hq * p.qs_h + min(qrow, p.N - 1) * p.qs_n + 8 * h;
   u32x4 qf[KSTEPS];
 #pragma unroll
   for (int s = 0; s < KSTEPS; ++s) qf[s] = *(const u32x4*)(qsrc + 16 * s);
@@ -544,12 +553,13 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
     }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   constexpr int RPI = 64 / G::CH;   // rows per store instruction
+  uint16_t* const obase = p.o + b * p.os_b + hq * p.os_h;
 #pragma unroll
   for (int i = 0; i < 32 / RPI; ++i) {
     const int r = i * RPI + lane / G::CH;
     const int cc = lane % G::CH;
     const u32x4 v = *(const u32x4*)(ost + r * G::ROW + 16 * (cc ^ (r & (G::CH - 1))));
-    if (qa + r < p.N) *(u32x4*)(p.o + ((size_t)bh * p.N + qa + r) * D + 8 * cc) = v;
+    if (qa + r < p.N) *(u32x4*)(obase + (qa + r) * p.os_n + 8 * cc) = v;
   }
   if (p.lse && h == 0 && qrow < p.N)
     p.lse[(size_t)bh * p.N + qrow] = empty ? -INFINITY : m * kLn2 + logf(lt);
@@ -583,13 +593,55 @@ bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
   return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
 }
 
-}  // namespace
+// One [B, H, N, D] tensor as (batch, head, row) element strides; rows are D contiguous elements.
+struct Layout {
+  const void* ptr;
+  int64_t sb, sh, sn;
+  int64_t H;
+  // Bytes from ptr to the end of the last row.
+  int64_t span(int B, int N, int D) const {
+    return ((B - 1) * sb + (H - 1) * sh + (int64_t)(N - 1) * sn + D) * 2;
+  }
+};
 
-extern "C" int attn_fwd_validate(const void* q, const void* k, const void* v, const void* out,
-                                 const float* lse, int B, int Hq, int Hkv, int N, int D,
-                                 float scale, int causal, const int32_t* valid_len, int dtype) {
-  (void)causal;
-  if (!q || !k || !v || !out) return ATTN_ERR_NULL;
+Layout contiguous(const void* ptr, int H, int N, int D) {
+  return Layout{ptr, (int64_t)H * N * D, (int64_t)N * D, (int64_t)D, H};
+}
+
+Layout strided(const void* ptr, const int64_t* st, int H, int N, int D) {
+  if (!st) return contiguous(ptr, H, N, D);
+  return Layout{ptr, st[0], st[1], st[2], H};
+}
+
+// 16-byte aligned base, non-negative strides that are multiples of 8 elements, rows of at least
+// D elements apart.
+bool layout_ok(const Layout& t, int D) {
+  if ((uintptr_t)t.ptr % 16 != 0) return false;
+  if (t.sb < 0 || t.sh < 0 || t.sn < 0) return false;
+  if (t.sb % 8 || t.sh % 8 || t.sn % 8) return false;
+  return t.sn >= D;
+}
+
+// No two (batch, head, row) of the output share an element: ordered by stride, each dimension
+// of size > 1 steps past the whole extent of the dimensions below it.
+bool output_disjoint(const Layout& o, int B, int H, int N, int D) {
+  struct Dim { int64_t size, stride; } d[3] = {{B, o.sb}, {H, o.sh}, {N, o.sn}};
+  for (int i = 0; i < 3; ++i)
+    for (int j = i + 1; j < 3; ++j)
+      if (d[j].stride < d[i].stride) std::swap(d[i], d[j]);
+  int64_t extent = D;   // elements spanned by the dimensions below
+  for (int i = 0; i < 3; ++i) {
+    if (d[i].size <= 1) continue;
+    if (d[i].stride < extent) return false;
+    extent = (d[i].size - 1) * d[i].stride + extent;
+  }
+  return true;
+}
+
+int validate(const Layout& q, const Layout& k, const Layout& v, const Layout& o,
+             const float* lse, int B, int Hq, int Hkv, int N, int D, float scale,
+             const int32_t* valid_len, int dtype) {
+  if (!q.ptr || !k.ptr || !v.ptr || !o.ptr) return ATTN_ERR_NULL;
   if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
   if (N > ATTN_MAX_N) return ATTN_ERR_SHAPE;
   const int64_t ntiles = (int64_t)B * Hq * (((int64_t)N + kBM - 1) / kBM);
@@ -597,32 +649,38 @@ extern "C" int attn_fwd_validate(const void* q, const void* k, const void* v, co
   if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
   if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
   if (!isfinite(scale)) return ATTN_ERR_SCALE;
-  const int64_t qbytes = (int64_t)B * Hq * N * D * 2;
-  const int64_t kvbytes = (int64_t)B * Hkv * N * D * 2;
+  if (!layout_ok(q, D) || !layout_ok(k, D) || !layout_ok(v, D) || !layout_ok(o, D))
+    return ATTN_ERR_LAYOUT;
+  if (!output_disjoint(o, B, Hq, N, D)) return ATTN_ERR_LAYOUT;
+  // K and V of one head are read as 32-bit-addressed buffers, including up to one tile of rows
+  // past N.
+  const int64_t kv_reach = ((int64_t)N + kBN) * std::max(k.sn, v.sn) * 2 + 2 * D;
+  if (kv_reach > INT32_MAX) return ATTN_ERR_SHAPE;
+  const int64_t qbytes = q.span(B, N, D), kbytes = k.span(B, N, D), vbytes = v.span(B, N, D);
+  const int64_t obytes = o.span(B, N, D);
   const int64_t lbytes = (int64_t)B * Hq * N * 4;
-  if (overlaps(out, qbytes, q, qbytes) || overlaps(out, qbytes, k, kvbytes) ||
-      overlaps(out, qbytes, v, kvbytes))
+  if (overlaps(o.ptr, obytes, q.ptr, qbytes) || overlaps(o.ptr, obytes, k.ptr, kbytes) ||
+      overlaps(o.ptr, obytes, v.ptr, vbytes))
     return ATTN_ERR_ALIAS;
-  if (lse && (overlaps(lse, lbytes, q, qbytes) || overlaps(lse, lbytes, k, kvbytes) ||
-              overlaps(lse, lbytes, v, kvbytes) || overlaps(lse, lbytes, out, qbytes)))
+  if (lse && (overlaps(lse, lbytes, q.ptr, qbytes) || overlaps(lse, lbytes, k.ptr, kbytes) ||
+              overlaps(lse, lbytes, v.ptr, vbytes) || overlaps(lse, lbytes, o.ptr, obytes)))
     return ATTN_ERR_ALIAS;
-  if (valid_len && (overlaps(valid_len, (int64_t)B * 4, out, qbytes) ||
+  if (valid_len && (overlaps(valid_len, (int64_t)B * 4, o.ptr, obytes) ||
                     (lse && overlaps(valid_len, (int64_t)B * 4, lse, lbytes))))
     return ATTN_ERR_ALIAS;
   return ATTN_OK;
 }
 
-extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B,
-                        int Hq, int Hkv, int N, int D, float scale, int causal,
-                        const int32_t* valid_len, int dtype, void* stream) {
-  const int st =
-      attn_fwd_validate(q, k, v, out, lse, B, Hq, Hkv, N, D, scale, causal, valid_len, dtype);
+int run(const Layout& q, const Layout& k, const Layout& v, const Layout& o, float* lse, int B,
+        int Hq, int Hkv, int N, int D, float scale, int causal, const int32_t* valid_len,
+        int dtype, void* stream) {
+  const int st = validate(q, k, v, o, lse, B, Hq, Hkv, N, D, scale, valid_len, dtype);
   if (st != ATTN_OK) return st;
   Params p;
-  p.q = (const uint16_t*)q;
-  p.k = (const uint16_t*)k;
-  p.v = (const uint16_t*)v;
-  p.o = (uint16_t*)out;
+  p.q = (const uint16_t*)q.ptr;
+  p.k = (const uint16_t*)k.ptr;
+  p.v = (const uint16_t*)v.ptr;
+  p.o = (uint16_t*)o.ptr;
   p.lse = lse;
   p.valid_len = valid_len;
   p.B = B;
@@ -632,6 +690,10 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* out, 
   p.group = Hq / Hkv;
   p.nqt = (N + kBM - 1) / kBM;
   p.xcd_order = ((int64_t)B * Hkv) % 8 == 0 ? 1 : 0;
+  p.qs_b = q.sb; p.qs_h = q.sh; p.qs_n = q.sn;
+  p.ks_b = k.sb; p.ks_h = k.sh; p.ks_n = k.sn;
+  p.vs_b = v.sb; p.vs_h = v.sh; p.vs_n = v.sn;
+  p.os_b = o.sb; p.os_h = o.sh; p.os_n = o.sn;
   p.c = fabsf(scale) * kLog2e;
   p.qsign = scale < 0.f ? 0x80008000u : 0u;
   p.qmask = scale == 0.f ? 0u : 0xffffffffu;
@@ -641,6 +703,46 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* out, 
   const hipError_t e = dtype == ATTN_BF16 ? dispatch_d<ATTN_BF16>(p, D, causal != 0, nwg, s)
                                           : dispatch_d<ATTN_F16>(p, D, causal != 0, nwg, s);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" int attn_fwd_validate(const void* q, const void* k, const void* v, const void* out,
+                                 const float* lse, int B, int Hq, int Hkv, int N, int D,
+                                 float scale, int causal, const int32_t* valid_len, int dtype) {
+  (void)causal;
+  return validate(contiguous(q, Hq, N, D), contiguous(k, Hkv, N, D), contiguous(v, Hkv, N, D),
+                  contiguous(out, Hq, N, D), lse, B, Hq, Hkv, N, D, scale, valid_len, dtype);
+}
+
+extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                        int Hq, int Hkv, int N, int D, float scale, int causal,
+                        const int32_t* valid_len, int dtype, void* stream) {
+  return run(contiguous(q, Hq, N, D), contiguous(k, Hkv, N, D), contiguous(v, Hkv, N, D),
+             contiguous(out, Hq, N, D), lse, B, Hq, Hkv, N, D, scale, causal, valid_len, dtype,
+             stream);
+}
+
+extern "C" int attn_fwd_strided_validate(const void* q, const int64_t* q_strides, const void* k,
+                                         const int64_t* k_strides, const void* v,
+                                         const int64_t* v_strides, const void* out,
+                                         const int64_t* out_strides, const float* lse, int B,
+                                         int Hq, int Hkv, int N, int D, float scale, int causal,
+                                         const int32_t* valid_len, int dtype) {
+  (void)causal;
+  return validate(strided(q, q_strides, Hq, N, D), strided(k, k_strides, Hkv, N, D),
+                  strided(v, v_strides, Hkv, N, D), strided(out, out_strides, Hq, N, D), lse, B,
+                  Hq, Hkv, N, D, scale, valid_len, dtype);
+}
+
+extern "C" int attn_fwd_strided(const void* q, const int64_t* q_strides, const void* k,
+                                const int64_t* k_strides, const void* v,
+                                const int64_t* v_strides, void* out, const int64_t* out_strides,
+                                float* lse, int B, int Hq, int Hkv, int N, int D, float scale,
+                                int causal, const int32_t* valid_len, int dtype, void* stream) {
+  return run(strided(q, q_strides, Hq, N, D), strided(k, k_strides, Hkv, N, D),
+             strided(v, v_strides, Hkv, N, D), strided(out, out_strides, Hq, N, D), lse, B, Hq,
+             Hkv, N, D, scale, causal, valid_len, dtype, stream);
 }
 
 extern "C" const char* attn_status_string(int status) {
@@ -654,8 +756,11 @@ extern "C" const char* attn_status_string(int status) {
     case ATTN_ERR_SCALE: return "scale is not finite";
     case ATTN_ERR_LAUNCH: return "the HIP runtime reported an error at kernel launch";
     case ATTN_ERR_ALIAS: return "out or lse overlaps an input, or out overlaps lse";
+    case ATTN_ERR_LAYOUT:
+      return "bad layout: pointers must be 16-byte aligned, strides non-negative multiples of 8 "
+             "elements, rows at least D elements apart, and output rows distinct";
     default: return "unknown status";
   }
 }
 
-extern "C" int attn_version(void) { return 1; }
+extern "C" int attn_version(void) { return 2; }

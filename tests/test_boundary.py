@@ -27,8 +27,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["attn_fwd", "attn_fwd_validate", "attn_status_string",
-                                    "attn_version"]
+    assert declared_functions() == ["attn_fwd", "attn_fwd_strided", "attn_fwd_strided_validate",
+                                    "attn_fwd_validate", "attn_status_string", "attn_version"]
 
 
 def test_library_exports_every_declared_function(lib):
@@ -41,12 +41,13 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_version(lib):
-    assert sdp.attn_version() == 1
+    assert sdp.attn_version() == 2
 
 
 def test_status_strings(lib):
     codes = [sdp.ATTN_OK, sdp.ATTN_ERR_NULL, sdp.ATTN_ERR_SHAPE, sdp.ATTN_ERR_HEAD_DIM,
-             sdp.ATTN_ERR_DTYPE, sdp.ATTN_ERR_SCALE, sdp.ATTN_ERR_LAUNCH, sdp.ATTN_ERR_ALIAS]
+             sdp.ATTN_ERR_DTYPE, sdp.ATTN_ERR_SCALE, sdp.ATTN_ERR_LAUNCH, sdp.ATTN_ERR_ALIAS,
+             sdp.ATTN_ERR_LAYOUT]
     texts = [sdp.attn_status_string(c) for c in codes]
     assert len(set(texts)) == len(texts)
     assert sdp.attn_status_string(12345) == "unknown status"
@@ -96,7 +97,10 @@ def test_validate_accepts_good_arguments(lib):
     (dict(scale=float("nan")), sdp.ATTN_ERR_SCALE),
     (dict(scale=float("inf")), sdp.ATTN_ERR_SCALE),
     (dict(out=Q), sdp.ATTN_ERR_ALIAS),
-    (dict(out=K + 1000), sdp.ATTN_ERR_ALIAS),
+    (dict(out=K + 1024), sdp.ATTN_ERR_ALIAS),
+    (dict(out=K + 1000), sdp.ATTN_ERR_LAYOUT),   # misaligned before overlapping
+    (dict(q=Q + 8), sdp.ATTN_ERR_LAYOUT),
+    (dict(v=V + 2), sdp.ATTN_ERR_LAYOUT),
     (dict(lse=O + 64), sdp.ATTN_ERR_ALIAS),
     (dict(lse=V), sdp.ATTN_ERR_ALIAS),
     (dict(valid_len=O + 8), sdp.ATTN_ERR_ALIAS),
@@ -118,3 +122,65 @@ def test_forward_rejects_bad_tensors_before_any_call():
         sdp.forward(q, q[:, :, :4], q, causal=True)  # shape mismatch
     with pytest.raises(ValueError):
         sdp.forward(q[0], q, q, causal=True)         # not 4-D
+
+
+# ---- attn_fwd_strided_validate: layouts given by (batch, head, row) element strides
+SB, SH, SN = 2, 8, 1000   # shapes of the strided checks (B, Hq, N); Hkv = 2, D = 128
+
+
+def bhnd(H, N=SN, D=128):
+    return (H * N * D, N * D, D)
+
+
+def bnhd(H, N=SN, D=128):
+    return (N * H * D, D, H * D)
+
+
+def scall(**kw):
+    a = dict(q=Q, qs=bhnd(8), k=K, ks=bhnd(2), v=V, vs=bhnd(2), out=O, os=bhnd(8), lse=L, B=SB,
+             Hq=SH, Hkv=2, N=SN, D=128, scale=0.088, causal=1, valid_len=VL,
+             dtype=sdp.ATTN_BF16)
+    a.update(kw)
+    return sdp.attn_fwd_strided_validate(a["q"], a["qs"], a["k"], a["ks"], a["v"], a["vs"],
+                                         a["out"], a["os"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                                         a["N"], a["D"], a["scale"], a["causal"],
+                                         a["valid_len"], a["dtype"])
+
+
+def test_strided_validate_accepts(lib):
+    assert scall() == sdp.ATTN_OK
+    assert scall(qs=None, ks=None, vs=None, os=None) == sdp.ATTN_OK
+    assert scall(qs=bnhd(8), ks=bnhd(2), vs=bnhd(2), os=bnhd(8)) == sdp.ATTN_OK
+    # padded rows, K/V shared by every batch, Q/K/V as views of one packed [B, N, 3, H, D]
+    assert scall(qs=(8 * SN * 136, SN * 136, 136)) == sdp.ATTN_OK
+    assert scall(ks=(0, SN * 128, 128), vs=(0, SN * 128, 128)) == sdp.ATTN_OK
+    packed = (SN * 3 * 8 * 128, 128, 3 * 8 * 128)
+    assert scall(q=Q, k=Q + 8 * 256, v=Q + 16 * 256, qs=packed, ks=packed, vs=packed,
+                 Hkv=8) == sdp.ATTN_OK
+    # an output whose heads are outermost
+    assert scall(os=(SN * 128, SB * SN * 128, 128)) == sdp.ATTN_OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(qs=(-8, SN * 128, 128)), sdp.ATTN_ERR_LAYOUT),
+    (dict(ks=(2 * SN * 128, SN * 128, 132)), sdp.ATTN_ERR_LAYOUT),   # row stride not 8k
+    (dict(vs=(2 * SN * 128, 4, 128)), sdp.ATTN_ERR_LAYOUT),          # head stride not 8k
+    (dict(qs=(8 * SN * 128, SN * 128, 120)), sdp.ATTN_ERR_LAYOUT),   # rows overlap
+    (dict(os=(8 * SN * 128, SN * 128, 0)), sdp.ATTN_ERR_LAYOUT),     # output rows collide
+    (dict(os=(8 * SN * 128, 128, 128)), sdp.ATTN_ERR_LAYOUT),        # output heads collide
+    (dict(os=(0, SN * 128, 128)), sdp.ATTN_ERR_LAYOUT),              # output batches collide
+    (dict(out=O + 4), sdp.ATTN_ERR_LAYOUT),
+    (dict(ks=(0, 0, 1 << 20)), sdp.ATTN_ERR_SHAPE),                  # K head beyond 2^31 bytes
+    (dict(out=Q + 64 * 1024), sdp.ATTN_ERR_ALIAS),
+    (dict(out=K - 1024 * 1024), sdp.ATTN_ERR_ALIAS),                 # span reaches into K
+    (dict(lse=V + 4096), sdp.ATTN_ERR_ALIAS),
+    (dict(q=None), sdp.ATTN_ERR_NULL),
+    (dict(D=96), sdp.ATTN_ERR_HEAD_DIM),
+])
+def test_strided_validate_rejects(lib, kw, code):
+    assert scall(**kw) == code
+
+
+def test_strided_validate_needs_three_strides(lib):
+    with pytest.raises(ValueError):
+        scall(qs=(1, 2))

@@ -8,7 +8,8 @@ times.
 import numpy as np
 import pytest
 
-from gpu_util import compare, log, run_device, run_oracle, sample_rows
+from gpu_util import compare, from_device, log, run_device, run_oracle, sample_rows, to_device
+import scaled_dot_product_fwd_amd as sdp
 from scaled_dot_product_fwd_amd import inputs
 
 pytestmark = pytest.mark.gpu
@@ -36,6 +37,28 @@ SMALL = [
 def test_small_full(cfg):
     dtype, D, causal, padded, B, Hq, Hkv, N = cfg
     case = inputs.make_case(B, Hq, Hkv, N, D, dtype, causal, padded, seed=[101, D, N, B])
+    log("case %s valid_len %s" % (cfg, case.valid_len))
+    O, L = run_device(case)
+    O_ref, L_ref = run_oracle(case)
+    compare(case, O, L, O_ref, L_ref, tag=str(cfg))
+
+
+# More 128-query tiles (B * Hq * ceil(N / 128)) than the 512 workgroups the device holds at
+# once, every row compared: the XCD-grouped workgroup order (B * Hkv % 8 == 0) and the plain
+# one, padding with an empty batch (a tile with no visible key), odd and even tile counts.
+MANY = [
+    ("bf16", 128, True, True, 4, 16, 4, 1100),
+    ("f16", 64, False, True, 3, 24, 3, 1050),
+    ("bf16", 64, True, False, 2, 40, 8, 1000),
+    ("f16", 128, False, False, 9, 8, 1, 1000),
+]
+
+
+@pytest.mark.parametrize("cfg", MANY, ids=lambda c: "%s-D%d-c%d-p%d-B%d-H%d-%d-N%d" % c)
+def test_more_tiles_than_resident_workgroups(cfg):
+    dtype, D, causal, padded, B, Hq, Hkv, N = cfg
+    assert B * Hq * -(-N // 128) > 512
+    case = inputs.make_case(B, Hq, Hkv, N, D, dtype, causal, padded, seed=[103, D, N, B])
     log("case %s valid_len %s" % (cfg, case.valid_len))
     O, L = run_device(case)
     O_ref, L_ref = run_oracle(case)
@@ -168,3 +191,75 @@ def test_without_lse_and_on_side_stream():
     assert L is None
     O_ref, L_ref = run_oracle(case)
     compare(case, O, None, O_ref, L_ref, tag="no-lse side-stream")
+
+
+# ---- strided inputs and outputs (attn_fwd_strided): the same logical [B, H, N, D] values as
+# the oracle sees, stored in other layouts.
+def _dev(bits, dtype):
+    return to_device(bits, dtype)
+
+
+STRIDED = [
+    ("bnhd", "bf16", 128, True, True, 2, 8, 2, 333),
+    ("bnhd", "f16", 64, False, False, 3, 4, 4, 200),
+    ("padded_rows", "bf16", 64, True, True, 2, 6, 3, 257),
+    ("padded_rows", "f16", 128, False, True, 2, 2, 1, 130),
+    ("shared_kv", "bf16", 128, True, False, 3, 4, 2, 300),
+    ("packed_qkv", "f16", 128, True, True, 2, 4, 4, 190),
+    ("packed_qkv", "bf16", 64, False, False, 1, 8, 8, 64),
+    ("strided_out", "bf16", 128, True, False, 2, 4, 1, 270),
+]
+
+
+@pytest.mark.parametrize("cfg", STRIDED, ids=lambda c: "%s-%s-D%d-c%d-p%d-B%d-H%d-%d-N%d" % c)
+def test_strided_layouts(cfg):
+    import torch
+    mode, dtype, D, causal, padded, B, Hq, Hkv, N = cfg
+    case = inputs.make_case(B, Hq, Hkv, N, D, dtype, causal, padded, seed=[107, D, N, B])
+    if mode == "shared_kv":   # one K/V for every batch: the oracle sees it repeated
+        k1 = case.k_bits[:1].copy()
+        v1 = case.v_bits[:1].copy()
+        case.k_bits[:] = k1
+        case.v_bits[:] = v1
+    log("strided case %s valid_len %s" % (cfg, case.valid_len))
+    vl = None
+    if case.valid_len is not None:
+        vl = torch.from_numpy(case.valid_len.astype(np.int32)).cuda()
+    q = _dev(case.q_bits, dtype)
+    k = _dev(case.k_bits, dtype)
+    v = _dev(case.v_bits, dtype)
+    out = None
+    layout = "bhnd"
+    if mode == "bnhd":
+        q, k, v = (t.transpose(1, 2).contiguous() for t in (q, k, v))
+        layout = "bnhd"
+    elif mode == "padded_rows":
+        def pad(t, extra):
+            big = torch.full(t.shape[:3] + (t.shape[3] + extra,), float("nan"), dtype=t.dtype,
+                             device=t.device)
+            big[..., :t.shape[3]] = t
+            return big[..., :t.shape[3]]
+        q, k, v = pad(q, 8), pad(k, 24), pad(v, 16)
+        out = pad(torch.empty_like(q), 8)
+    elif mode == "shared_kv":
+        k = k[:1].expand(B, -1, -1, -1)
+        v = v[:1].expand(B, -1, -1, -1)
+    elif mode == "packed_qkv":
+        packed = torch.stack([t.transpose(1, 2) for t in (q, k, v)], dim=2).contiguous()
+        q, k, v = (packed[:, :, i].transpose(1, 2) for i in range(3))
+    elif mode == "strided_out":
+        big = torch.full((B, N, Hq, D + 8), float("nan"), dtype=q.dtype, device=q.device)
+        out = big[..., :D].transpose(1, 2)
+    o, lse = sdp.forward(q, k, v, causal=causal, valid_len=vl, scale=case.scale, out=out,
+                         layout=layout)
+    torch.cuda.synchronize()
+    if layout == "bnhd":
+        o = o.transpose(1, 2)
+    O = from_device(o, dtype)
+    L = lse.cpu().numpy().astype(np.float64)
+    O_ref, L_ref = run_oracle(case)
+    compare(case, O, L, O_ref, L_ref, tag=str(cfg))
+    if mode in ("padded_rows", "strided_out"):   # the padding around the output is untouched
+        base = out._base if out._base is not None else out
+        pad_cols = base[..., D:]
+        assert torch.isnan(pad_cols.float()).all()
