@@ -6,6 +6,9 @@ inputs resident in HBM before timing starts. Prints ONE JSON line on stdout; pro
 stderr.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long_gqa] [--no-cpu-baseline]
+                  [--layout bhnd|bnhd]
+
+--layout bnhd stores Q, K, V and O as [B, N, H, D] and runs the strided entry point on them.
 
 Throughput is the nominal forward flop count 4*B*Hq*N^2*D (halved under causal masking) per
 second. The roofline object reports the kernel's flop rate against the dense 16-bit MFMA peak,
@@ -96,6 +99,8 @@ def main():
     ap.add_argument("--workload", default="long_gqa")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--layout", choices=("bhnd", "bnhd"), default="bhnd",
+                    help="memory layout of Q, K, V and O")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (the "
                          "reference kernel for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE) and exit")
@@ -128,6 +133,8 @@ def main():
         return torch.from_numpy(bits.view(np.int16)).view(tdt).cuda()
 
     q, k, v = dev(case.q_bits), dev(case.k_bits), dev(case.v_bits)
+    if args.layout == "bnhd":
+        q, k, v = (t.transpose(1, 2).contiguous() for t in (q, k, v))
     vl = torch.from_numpy(case.valid_len).cuda() if case.valid_len is not None else None
     out = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device="cuda")
@@ -135,7 +142,7 @@ def main():
 
     def step():
         sdp.forward(q, k, v, causal=w.causal, valid_len=vl, scale=w.scale, out=out, lse=lse,
-                    stream=stream)
+                    stream=stream, layout=args.layout)
 
     for _ in range(args.warmup):
         step()
@@ -162,7 +169,7 @@ def main():
     tflops = f / (ms_per_step * 1e-3) / 1e12
     roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_TFLOPS_16BIT_DENSE,
             "unit": "TFLOP/s", "frac": round(tflops / PEAK_TFLOPS_16BIT_DENSE, 4),
-            "traffic": traffic_for(w.name)}
+            "traffic": traffic_for(w.name) if args.layout == "bhnd" else None}
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the oracle on the host (about %.0f s)" % args.cpu_seconds)
@@ -176,6 +183,7 @@ def main():
         "data": "synthetic (seeded iid N(0,1), rounded to %s)" % w.dtype,
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "D": w.D,
                    "causal": w.causal, "padded": w.padded, "scale": w.scale,
+                   "layout": args.layout,
                    "flops_per_step": f},
         "roofline": roof,
         "cpu_baseline": cpu,
