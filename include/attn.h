@@ -62,10 +62,19 @@ typedef enum {
     ATTN_ERR_SCALE = -5,    /* scale is NaN or infinite */
     ATTN_ERR_LAUNCH = -6,   /* the HIP runtime reported an error at launch; query HIP for it */
     ATTN_ERR_ALIAS = -7,    /* out or lse overlaps an input, or out overlaps lse */
-    ATTN_ERR_LAYOUT = -8    /* a pointer is not 16-byte aligned, a stride is negative or not a
+    ATTN_ERR_LAYOUT = -8,   /* a pointer is not 16-byte aligned, a stride is negative or not a
                                multiple of 8 elements, rows are less than D elements apart, or
-                               two output rows share memory */
+                               two output rows share memory; for a mask see attn_fwd_masked */
+    ATTN_ERR_MASK = -9      /* mask_type is not one of attn_mask_t */
 } attn_status_t;
+
+/* Explicit mask kinds of attn_fwd_masked. */
+typedef enum {
+    ATTN_MASK_NONE = 0,     /* no explicit mask (mask is ignored) */
+    ATTN_MASK_KEEP_U8 = 1,  /* uint8 [.., N, N]: nonzero keeps key j for query i, zero hides it */
+    ATTN_MASK_ADD = 2       /* [.., N, N] of the input dtype (fp16 / bf16), added to the scaled
+                               score; -inf hides the key */
+} attn_mask_t;
 
 /* Size limits checked by attn_fwd_validate: N <= ATTN_MAX_N and
  * B * Hq * ceil(N / 128) <= ATTN_MAX_TILES; with strides, also (N + 64) * (K or V row stride)
@@ -153,10 +162,53 @@ int attn_fwd_strided_validate(const void *q, const int64_t *q_strides, const voi
                               int Hkv, int N, int D, float scale, int causal,
                               const int32_t *valid_len, int dtype);
 
+/*
+ * attn_fwd_masked -- attn_fwd_strided with an explicit mask matrix as well. The masked multi-head
+ * attention CUDA article (section 2.2) gives the mask as a [B, N, N] matrix, either a boolean
+ * padding mask or, for combined masks, a float matrix that is 0 where the key is allowed and
+ * -inf (or a large negative value) where it is not, added to the score before the softmax; the
+ * article's formula (section 2.1) adds Mask to Q K^T / sqrt(D).
+ *
+ *   mask        device pointer, 16-byte aligned; element (b, hq, i, j) at
+ *               mask + b*ms[0] + hq*ms[1] + i*ms[2] + j (elements of the mask type).
+ *   mask_type   ATTN_MASK_KEEP_U8: key j is visible to query i only where the byte is nonzero.
+ *               ATTN_MASK_ADD: the element (in the input dtype) is added to scale * q.k; values
+ *               must be finite or -inf (a row whose visible keys all carry -inf, like an empty
+ *               row, gives O = 0 and LSE = -inf; LSE includes the added values).
+ *               ATTN_MASK_NONE: same as attn_fwd_strided.
+ *   mask_strides host pointer to three int64 element strides: batch, query head, query row
+ *               (the key index j is contiguous). NULL means a contiguous [B, N, N] mask shared
+ *               by every head: {N*N, 0, N}. Use 0 to broadcast a dimension. Strides must be >= 0
+ *               and multiples of 16 bytes, and the row stride >= N elements (a ragged N needs a
+ *               row padded to a multiple of 16 bytes); otherwise ATTN_ERR_LAYOUT. Also
+ *               (N + 128) * row stride bytes < 2^31 (else ATTN_ERR_SHAPE). Rows are read in
+ *               16-byte units: the bytes after element N-1 of a row up to the next 16-byte
+ *               boundary must be readable (they are inside the row stride) and are ignored.
+ *   all else    as in attn_fwd_strided.
+ *
+ * The explicit mask combines with causal and valid_len: a key is used only if all of them allow
+ * it (the article, section 1.3, on stacked masks). The mask may share memory with the inputs but
+ * not with out or lse (ATTN_ERR_ALIAS, by byte range). Returns as attn_fwd, or ATTN_ERR_MASK.
+ */
+int attn_fwd_masked(const void *q, const int64_t *q_strides, const void *k,
+                    const int64_t *k_strides, const void *v, const int64_t *v_strides, void *out,
+                    const int64_t *out_strides, float *lse, int B, int Hq, int Hkv, int N, int D,
+                    float scale, int causal, const int32_t *valid_len, const void *mask,
+                    int mask_type, const int64_t *mask_strides, int dtype, void *stream);
+
+/* attn_fwd_masked_validate -- the host-only argument check of attn_fwd_masked. */
+int attn_fwd_masked_validate(const void *q, const int64_t *q_strides, const void *k,
+                             const int64_t *k_strides, const void *v, const int64_t *v_strides,
+                             const void *out, const int64_t *out_strides, const float *lse,
+                             int B, int Hq, int Hkv, int N, int D, float scale, int causal,
+                             const int32_t *valid_len, const void *mask, int mask_type,
+                             const int64_t *mask_strides, int dtype);
+
 /* attn_status_string -- a static, NUL-terminated description of a return code (never NULL). */
 const char *attn_status_string(int status);
 
-/* attn_version -- the library's interface version, currently 2 (2 added attn_fwd_strided). */
+/* attn_version -- the library's interface version, currently 3 (2 added attn_fwd_strided, 3
+ * attn_fwd_masked). */
 int attn_version(void);
 
 #ifdef __cplusplus

@@ -39,6 +39,11 @@ def load(path: str = _LIB_PATH) -> ctypes.CDLL:
     f.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 5 + [
         ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
         ctypes.c_int]
+    g = lib.oracle_attn_fwd_masked
+    g.restype = ctypes.c_int
+    g.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 5 + [
+        ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int]
     lib.oracle_max_threads.restype = ctypes.c_int
     return lib
 
@@ -59,11 +64,13 @@ def max_threads() -> int:
 
 def attn_fwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal: bool,
              valid_len: Optional[np.ndarray] = None, rows: Optional[np.ndarray] = None,
-             threads: int = 0, lib: Optional[ctypes.CDLL] = None
-             ) -> Tuple[np.ndarray, np.ndarray]:
+             threads: int = 0, lib: Optional[ctypes.CDLL] = None, keep_mask=None,
+             add_mask=None) -> Tuple[np.ndarray, np.ndarray]:
     """Attention forward in fp64.
 
     q: [B,Hq,N,D] float64, k/v: [B,Hkv,N,D] float64, valid_len: int32[B] or None.
+    keep_mask (uint8/bool) or add_mask (float64): an explicit mask broadcastable to
+    [B,Hq,N,N] (at most one of them).
     rows: optional int64 flat row indices (b*Hq + hq)*N + i; when given the outputs are
     [len(rows), D] and [len(rows)], else [B,Hq,N,D] and [B,Hq,N].
     Returns (O, LSE) as float64; LSE is the natural-log log-sum-exp (-inf for an empty row).
@@ -92,9 +99,23 @@ def attn_fwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal: 
         out = np.empty((nrows, D), np.float64)
         lse = np.empty((nrows,), np.float64)
         rows_ptr = rows.ctypes.data
-    rc = lib.oracle_attn_fwd(q.ctypes.data, k.ctypes.data, v.ctypes.data, out.ctypes.data,
-                             lse.ctypes.data, B, Hq, Hkv, N, D, float(scale), int(bool(causal)),
-                             vl_ptr, rows_ptr, nrows, int(threads))
+    kind, mptr, mst = 0, None, None
+    if keep_mask is not None and add_mask is not None:
+        raise ValueError("give at most one of keep_mask and add_mask")
+    if keep_mask is not None or add_mask is not None:
+        kind = 1 if keep_mask is not None else 2
+        m = keep_mask if kind == 1 else add_mask
+        m = np.asarray(m, dtype=np.uint8 if kind == 1 else np.float64)
+        m = np.broadcast_to(m, (B, Hq, N, N))
+        if m.strides[3] != m.itemsize:
+            m = np.ascontiguousarray(m)
+        mask_arr = m   # keep alive during the call
+        mptr = mask_arr.ctypes.data
+        mst = (ctypes.c_int64 * 3)(*[st // m.itemsize for st in m.strides[:3]])
+    rc = lib.oracle_attn_fwd_masked(q.ctypes.data, k.ctypes.data, v.ctypes.data, out.ctypes.data,
+                                    lse.ctypes.data, B, Hq, Hkv, N, D, float(scale),
+                                    int(bool(causal)), vl_ptr, mptr, kind, mst, rows_ptr, nrows,
+                                    int(threads))
     if rc != 0:
         raise ValueError("oracle_attn_fwd rejected its arguments (rc=%d)" % rc)
     return out, lse

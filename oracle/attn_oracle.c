@@ -24,6 +24,14 @@
  *   - The softmax is taken in the three passes the article's naive kernel uses (section 3.1):
  *     first the row maximum, then the sum of exp(s - max), then the weighted sum of V divided
  *     by that sum. The scores are kept from the first pass.
+ *   - An explicit mask matrix, when given, is indexed [b, hq, i, j] (the article, section 2.1,
+ *     writes the mask as a [B, N, N] matrix broadcast over the scores; section 2.2 lists a
+ *     boolean padding mask and, for combined masks, a float matrix added to the score that is
+ *     0 where allowed and -inf or a large negative value where not):
+ *       keep mask (uint8): key j is visible only where the element is nonzero;
+ *       additive mask (double): the element is added to the scaled score s_j, and a key whose
+ *       element is -inf is not visible.
+ *     It combines with the causal and valid_len masks by intersection.
  *   - A row with no visible key has O = 0 and LSE = -infinity (the article, section 3.2,
  *     recommends a zero output for a fully masked row; the log of an empty sum is -inf).
  *   - LSE is the natural-log log-sum-exp of the scaled scores. The Triton file
@@ -39,12 +47,23 @@
 
 #include <omp.h>
 
+/* The explicit mask row of one query: kind 0 none, 1 keep (uint8), 2 additive (double). */
+typedef struct {
+    int kind;
+    const uint8_t *keep;
+    const double *add;
+} mask_row;
+
 /* Is key j visible to query i? */
-static int key_visible(int64_t i, int64_t j, int causal, int64_t valid)
+static int key_visible(int64_t i, int64_t j, int causal, int64_t valid, const mask_row *mr)
 {
     if (causal && j > i)
         return 0;
     if (j >= valid)
+        return 0;
+    if (mr->kind == 1 && mr->keep[j] == 0)
+        return 0;
+    if (mr->kind == 2 && mr->add[j] == -INFINITY)
         return 0;
     return 1;
 }
@@ -52,20 +71,22 @@ static int key_visible(int64_t i, int64_t j, int causal, int64_t valid)
 /* One query row, three passes. scores is caller-provided scratch of N doubles. */
 static void attend_row(const double *q_row, const double *k_head, const double *v_head,
                        int64_t N, int64_t D, double scale, int causal, int64_t valid, int64_t i,
-                       double *scores, double *o_row, double *lse_out)
+                       const mask_row *mr, double *scores, double *o_row, double *lse_out)
 {
     int64_t j, d, visible = 0;
     double m = -INFINITY, l = 0.0;
 
     /* pass 1: scores and their maximum */
     for (j = 0; j < N; ++j) {
-        if (!key_visible(i, j, causal, valid))
+        if (!key_visible(i, j, causal, valid, mr))
             continue;
         const double *k_row = k_head + j * D;
         double dot = 0.0;
         for (d = 0; d < D; ++d)
             dot += q_row[d] * k_row[d];
         scores[j] = scale * dot;
+        if (mr->kind == 2)
+            scores[j] += mr->add[j];
         if (scores[j] > m)
             m = scores[j];
         ++visible;
@@ -78,7 +99,7 @@ static void attend_row(const double *q_row, const double *k_head, const double *
     }
     /* pass 2: sum of exponentials relative to the maximum */
     for (j = 0; j < N; ++j) {
-        if (!key_visible(i, j, causal, valid))
+        if (!key_visible(i, j, causal, valid, mr))
             continue;
         l += exp(scores[j] - m);
     }
@@ -86,7 +107,7 @@ static void attend_row(const double *q_row, const double *k_head, const double *
     for (d = 0; d < D; ++d)
         o_row[d] = 0.0;
     for (j = 0; j < N; ++j) {
-        if (!key_visible(i, j, causal, valid))
+        if (!key_visible(i, j, causal, valid, mr))
             continue;
         double w = exp(scores[j] - m) / l;
         const double *v_row = v_head + j * D;
@@ -99,15 +120,21 @@ static void attend_row(const double *q_row, const double *k_head, const double *
 /*
  * q: [B,Hq,N,D], k and v: [B,Hkv,N,D], all contiguous doubles on the host.
  * valid_len: int32[B] on the host, or NULL for no padding mask.
+ * mask, mask_kind, mask_strides: the explicit mask (kind 0 none, 1 uint8 keep, 2 double
+ * additive) with element strides {batch, query head, query row}; element (b, hq, i, j) is at
+ * mask + b*s[0] + hq*s[1] + i*s[2] + j. Ignored for kind 0.
  * rows: flat row indices r = (b*Hq + hq)*N + i, or NULL for all B*Hq*N rows in order.
  * out: [nrows, D], lse: [nrows] (row t of the output belongs to rows[t]).
  * threads <= 0 uses the OpenMP default. Returns 0, or -1 on bad arguments.
  */
-int oracle_attn_fwd(const double *q, const double *k, const double *v, double *out, double *lse,
-                    int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D, double scale,
-                    int causal, const int32_t *valid_len, const int64_t *rows, int64_t nrows,
-                    int threads)
+int oracle_attn_fwd_masked(const double *q, const double *k, const double *v, double *out,
+                           double *lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D,
+                           double scale, int causal, const int32_t *valid_len, const void *mask,
+                           int mask_kind, const int64_t *mask_strides, const int64_t *rows,
+                           int64_t nrows, int threads)
 {
+    if (mask_kind < 0 || mask_kind > 2 || (mask_kind != 0 && (!mask || !mask_strides)))
+        return -1;
     if (!q || !k || !v || !out || !lse)
         return -1;
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 || D <= 0 || Hq % Hkv != 0)
@@ -147,12 +174,30 @@ int oracle_attn_fwd(const double *q, const double *k, const double *v, double *o
                 if (valid > N)
                     valid = N;
             }
+            mask_row mr = {mask_kind, NULL, NULL};
+            if (mask_kind != 0) {
+                int64_t off = b * mask_strides[0] + hq * mask_strides[1] + i * mask_strides[2];
+                if (mask_kind == 1)
+                    mr.keep = (const uint8_t *)mask + off;
+                else
+                    mr.add = (const double *)mask + off;
+            }
             attend_row(q + r * D, k + (b * Hkv + kv) * N * D, v + (b * Hkv + kv) * N * D, N, D,
-                       scale, causal, valid, i, scores, out + t * D, lse + t);
+                       scale, causal, valid, i, &mr, scores, out + t * D, lse + t);
         }
         free(scores);
     }
     return bad ? -1 : 0;
+}
+
+/* The same without an explicit mask. */
+int oracle_attn_fwd(const double *q, const double *k, const double *v, double *out, double *lse,
+                    int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t D, double scale,
+                    int causal, const int32_t *valid_len, const int64_t *rows, int64_t nrows,
+                    int threads)
+{
+    return oracle_attn_fwd_masked(q, k, v, out, lse, B, Hq, Hkv, N, D, scale, causal, valid_len,
+                                  NULL, 0, NULL, rows, nrows, threads);
 }
 
 int oracle_max_threads(void)

@@ -7,9 +7,10 @@ no fallback: if the library is missing, calls raise ``ImportError``.
 Raw entry points (same names and argument order as the C ABI; pointers are integers, stride
 arguments are 3-sequences of element strides or None):
     attn_fwd, attn_fwd_validate, attn_fwd_strided, attn_fwd_strided_validate,
-    attn_status_string, attn_version
+    attn_fwd_masked, attn_fwd_masked_validate, attn_status_string, attn_version
 Convenience for torch tensors (device memory and streams only):
-    forward(q, k, v, causal=..., valid_len=None, scale=None, out=None, lse=None, layout="bhnd")
+    forward(q, k, v, causal=..., valid_len=None, scale=None, out=None, lse=None, layout="bhnd",
+            attn_mask=None)
 """
 from __future__ import annotations
 
@@ -18,7 +19,8 @@ import os
 from typing import Optional, Tuple
 
 __all__ = ["ATTN_F16", "ATTN_BF16", "AttnError", "attn_fwd", "attn_fwd_validate",
-           "attn_fwd_strided", "attn_fwd_strided_validate", "attn_status_string",
+           "attn_fwd_strided", "attn_fwd_strided_validate", "attn_fwd_masked",
+           "attn_fwd_masked_validate", "attn_status_string",
            "attn_version", "forward", "library_path", "load_library"]
 
 ATTN_F16 = 0
@@ -33,6 +35,11 @@ ATTN_ERR_SCALE = -5
 ATTN_ERR_LAUNCH = -6
 ATTN_ERR_ALIAS = -7
 ATTN_ERR_LAYOUT = -8
+ATTN_ERR_MASK = -9
+
+ATTN_MASK_NONE = 0
+ATTN_MASK_KEEP_U8 = 1
+ATTN_MASK_ADD = 2
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libattn.so")
@@ -77,6 +84,14 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_fwd_strided_validate.argtypes = [_vp, _i64p, _vp, _i64p, _vp, _i64p, _vp, _i64p,
                                               _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                                               _c_float, _c_int, _vp, _c_int]
+    lib.attn_fwd_masked.restype = _c_int
+    lib.attn_fwd_masked.argtypes = [_vp, _i64p, _vp, _i64p, _vp, _i64p, _vp, _i64p, _vp, _c_int,
+                                    _c_int, _c_int, _c_int, _c_int, _c_float, _c_int, _vp, _vp,
+                                    _c_int, _i64p, _c_int, _vp]
+    lib.attn_fwd_masked_validate.restype = _c_int
+    lib.attn_fwd_masked_validate.argtypes = [_vp, _i64p, _vp, _i64p, _vp, _i64p, _vp, _i64p,
+                                             _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                             _c_float, _c_int, _vp, _vp, _c_int, _i64p, _c_int]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_status_string.argtypes = [_c_int]
     lib.attn_version.restype = _c_int
@@ -132,6 +147,29 @@ def attn_fwd_strided_validate(q: int, q_strides, k: int, k_strides, v: int, v_st
         _strides(out_strides), lse, B, Hq, Hkv, N, D, scale, int(causal), valid_len, dtype)
 
 
+def attn_fwd_masked(q: int, q_strides, k: int, k_strides, v: int, v_strides, out: int,
+                    out_strides, lse: Optional[int], B: int, Hq: int, Hkv: int, N: int, D: int,
+                    scale: float, causal: int, valid_len: Optional[int], mask: Optional[int],
+                    mask_type: int, mask_strides, dtype: int, stream: Optional[int]) -> int:
+    """C ``attn_fwd_masked``; mask_strides are (batch, head, row) element strides or None."""
+    return load_library().attn_fwd_masked(
+        q, _strides(q_strides), k, _strides(k_strides), v, _strides(v_strides), out,
+        _strides(out_strides), lse, B, Hq, Hkv, N, D, scale, int(causal), valid_len, mask,
+        mask_type, _strides(mask_strides), dtype, stream)
+
+
+def attn_fwd_masked_validate(q: int, q_strides, k: int, k_strides, v: int, v_strides, out: int,
+                             out_strides, lse: Optional[int], B: int, Hq: int, Hkv: int, N: int,
+                             D: int, scale: float, causal: int, valid_len: Optional[int],
+                             mask: Optional[int], mask_type: int, mask_strides,
+                             dtype: int) -> int:
+    """C ``attn_fwd_masked_validate``: host-only argument check, no HIP call."""
+    return load_library().attn_fwd_masked_validate(
+        q, _strides(q_strides), k, _strides(k_strides), v, _strides(v_strides), out,
+        _strides(out_strides), lse, B, Hq, Hkv, N, D, scale, int(causal), valid_len, mask,
+        mask_type, _strides(mask_strides), dtype)
+
+
 def attn_status_string(status: int) -> str:
     return load_library().attn_status_string(status).decode()
 
@@ -150,14 +188,21 @@ def _dtype_code(t) -> int:
 
 
 def forward(q, k, v, causal: bool, valid_len=None, scale: Optional[float] = None, out=None,
-            lse=None, want_lse: bool = True, stream=None,
-            layout: str = "bhnd") -> Tuple[object, Optional[object]]:
+            lse=None, want_lse: bool = True, stream=None, layout: str = "bhnd",
+            attn_mask=None) -> Tuple[object, Optional[object]]:
     """Run the attention forward on torch device tensors on the current (or given) stream.
 
     ``layout`` names the order of the four dimensions of q, k, v and out: "bhnd" for
     [B, H, N, D] (the default) or "bnhd" for [B, N, H, D]. Any strides are accepted as long as
     the last (D) dimension is contiguous; contiguous [B, H, N, D] tensors take attn_fwd, all
     others attn_fwd_strided (no copies either way).
+
+    ``attn_mask`` is an optional explicit mask over (query, key), broadcastable to
+    [B, Hq, N, N] (shapes [N, N], [B, N, N] or [B or 1, Hq or 1, N, N]; query rows and keys are
+    in sequence order whatever ``layout`` is): bool or uint8 keeps the key where nonzero, q's
+    dtype is added to the scaled score. Its key dimension must be contiguous and its rows
+    16-byte aligned (for a ragged N, a [.., N, Npad] view of a padded tensor works). It
+    combines with ``causal`` and ``valid_len``; the call then goes to attn_fwd_masked.
 
     Allocates ``out`` (q's shape, layout and dtype, contiguous) and ``lse`` ([B, Hq, N] float32)
     with torch when they are not given. Returns (out, lse); lse is None when want_lse is False
@@ -202,6 +247,35 @@ def forward(q, k, v, causal: bool, valid_len=None, scale: Optional[float] = None
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     lse_ptr = lse.data_ptr() if lse is not None else None
+    if attn_mask is not None:
+        m = attn_mask
+        if m.dtype == torch.bool:
+            m = m.view(torch.uint8)
+        if m.dtype == torch.uint8:
+            mtype = ATTN_MASK_KEEP_U8
+        elif m.dtype == q.dtype:
+            mtype = ATTN_MASK_ADD
+        else:
+            raise TypeError("attn_mask must be bool, uint8 or q's dtype, got %s" % m.dtype)
+        if not m.is_cuda:
+            raise ValueError("attn_mask must be a device tensor")
+        if m.dim() == 3:
+            m = m[:, None]
+        elif m.dim() == 2:
+            m = m[None, None]
+        if m.dim() != 4 or tuple(m.shape[-2:]) != (N, N):
+            raise ValueError("attn_mask must be broadcastable to [B, Hq, N, N]")
+        m = m.expand(B, Hq, N, N)
+        if m.stride(3) != 1:
+            raise ValueError("attn_mask: the key dimension must be contiguous")
+        st = attn_fwd_masked(qv.data_ptr(), qv.stride()[:3], kv.data_ptr(), kv.stride()[:3],
+                             vv.data_ptr(), vv.stride()[:3], ov.data_ptr(), ov.stride()[:3],
+                             lse_ptr, B, Hq, Hkv, N, D, float(scale), int(bool(causal)), vl_ptr,
+                             m.data_ptr(), mtype, m.stride()[:3], _dtype_code(q),
+                             stream.cuda_stream)
+        if st != ATTN_OK:
+            raise AttnError(st, "attn_fwd_masked")
+        return out, lse
     if all(t.is_contiguous() for t in (qv, kv, vv, ov)):
         st = attn_fwd(qv.data_ptr(), kv.data_ptr(), vv.data_ptr(), ov.data_ptr(), lse_ptr, B, Hq,
                       Hkv, N, D, float(scale), int(bool(causal)), vl_ptr, _dtype_code(q),

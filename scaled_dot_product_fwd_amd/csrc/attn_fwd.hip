@@ -89,6 +89,28 @@ struct Geo {
   }
 };
 
+// Explicit [B, H, N, N] masks (template parameter MK of the kernel).
+constexpr int kMaskNone = 0;   // causal and valid_len only
+constexpr int kMaskKeep = 1;   // uint8: nonzero = the key is visible to the query
+constexpr int kMaskAdd = 2;    // 16-bit (the input type): added to the scaled score
+
+// Each wave keeps the kBN-key slice of its 32 mask rows for the current tile in its own LDS
+// slot, fetched by DMA one tile ahead. Row r stores logical 16-byte chunk c at chunk
+// c ^ mswz(r); the swizzle depends on r % RPL only, so every DMA block uses the same lane
+// offsets.
+template <int MK>
+struct MaskGeo {
+  static constexpr int ES = MK == kMaskKeep ? 1 : 2;            // bytes per element
+  static constexpr int RB = kBN * ES;                           // bytes per row slice
+  static constexpr int CPR = RB / 16;                           // 16-byte chunks per row slice
+  static constexpr int WB = MK == kMaskNone ? 0 : 32 * RB;      // bytes per wave slot
+  static constexpr int LOADS = WB / 1024;                       // 1 KiB DMA blocks per slot
+  static constexpr int RPL = 1024 / RB;                         // rows per DMA block
+  __device__ static constexpr int mswz(int r) {
+    return MK == kMaskKeep ? ((r >> 2) & 3) : (r & 7);
+  }
+};
+
 struct Params {
   const uint16_t* q;
   const uint16_t* k;
@@ -106,6 +128,9 @@ struct Params {
   int64_t ks_b, ks_h, ks_n;
   int64_t vs_b, vs_h, vs_n;
   int64_t os_b, os_h, os_n;
+  const void* mask;  // explicit mask (kernels with MK != kMaskNone)
+  int64_t ms_b, ms_h, ms_n;   // its element strides (batch, query head, query row)
+  float mscale;      // log2(e) / c: an additive mask value in raw score units
   float c;           // |scale| * log2(e)
   uint32_t qsign;    // 0x80008000 when scale < 0: Q is negated (exactly) instead
   uint32_t qmask;    // 0 when scale == 0: all scores are exactly 0 (and c is set to 1)
@@ -207,8 +232,11 @@ __device__ inline void update_max(float mx, float c, float& m, float& l,
   const float mt = (mx == -INFINITY) ? -INFINITY : mx * c;
   const bool need = mt > m + RESCALE_THRESHOLD;
   if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
+    // Rows that keep their maximum keep their state (alpha = 1): one of them may still be at
+    // m = -inf (no visible key yet), where exp2(m - m) would be NaN. A raised row from
+    // m = -inf gets alpha = exp2(-inf) = 0.
     const float mnew = need ? mt : m;
-    const float alpha = __builtin_amdgcn_exp2f(m - mnew);   // 0 when m = -inf
+    const float alpha = need ? __builtin_amdgcn_exp2f(m - mnew) : 1.0f;
     l *= alpha;
 #pragma unroll
     for (int u = 0; u < Geo<D>::OT; ++u)
@@ -218,13 +246,15 @@ __device__ inline void update_max(float mx, float c, float& m, float& l,
   }
 }
 
-template <int DT, int D, bool CAUSAL>
+template <int DT, int D, bool CAUSAL, int MK>
 __device__ __forceinline__ void attn_fwd_body(const Params& p) {
   using G = Geo<D>;
   using M = Mfma<DT>;
+  using MG = MaskGeo<MK>;
   constexpr int KSTEPS = G::KSTEPS;
   constexpr int OT = G::OT;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[G::LDS];
+  constexpr int MOFF = G::LDS;   // mask slots follow the K/V tiles
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[G::LDS + kWaves * MG::WB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -302,6 +332,30 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
       if (vdst >= 0)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(smem + vdst + blk), 16,
                                                  voff0, (row0 + i * G::RPB) * vrow, 0, 0);
+    }
+  };
+
+  // ---- explicit mask: this wave's rows qa .. qa+31 of the (batch, query head) mask matrix as a
+  // buffer spanning its N rows, the last one up to its next 16-byte boundary (rows past N read
+  // as zeros; key columns past N are read but those keys are hidden anyway).
+  const uint32_t mrow = MK != kMaskNone ? (uint32_t)(p.ms_n * MG::ES) : 0;
+  const __amdgpu_buffer_rsrc_t mrs = __builtin_amdgcn_make_buffer_rsrc(
+      MK != kMaskNone ? (void*)((const unsigned char*)p.mask + (b * p.ms_b + hq * p.ms_h) * MG::ES)
+                      : (void*)p.q,
+      (short)0, MK != kMaskNone ? (p.N - 1) * mrow + ((p.N * MG::ES + 15) & ~15) : 0,
+      kBufferFlags);
+  uint32_t moff = 0;
+  if constexpr (MK != kMaskNone) {
+    const int r = lane / MG::CPR;            // row within a DMA block
+    moff = (uint32_t)(qa + r) * mrow + 16 * ((lane % MG::CPR) ^ MG::mswz(r));
+  }
+  auto mask_dma = [&](int tile) {
+    if constexpr (MK != kMaskNone) {
+#pragma unroll
+      for (int i = 0; i < MG::LOADS; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            mrs, (lds_void*)(smem + MOFF + wave * MG::WB + i * 1024), 16, moff,
+            (uint32_t)tile * MG::RB + (uint32_t)(i * MG::RPL) * mrow, 0, 0);
     }
   };
 
@@ -467,6 +521,7 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
   // ---- prologue: K_0, V_0, K_1 in flight; scores of tile 0
   if (ntiles > 0) dma(0, G::K0, G::V0);
   if (ntiles > 1) dma(1, G::K1, -1);
+  if (ntiles > 0) mask_dma(0);
   wait_loads_and_lds();
 #pragma unroll
   for (int s = 0; s < KSTEPS; ++s) qf[s] = (qf[s] ^ p.qsign) & p.qmask;
@@ -482,7 +537,53 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
   // the scores of hidden keys to -inf in place and recompute the row maximum. A tile wholly
   // hidden from this wave (above its diagonal) becomes all -inf and adds exactly nothing.
   // key = kb + 32t + 8(r/4) + 4h + r%4 is visible iff key - kb - 4h <= lim.
-  auto mask_tile = [&](f32x16 (&sc)[2], float& mxc, int kb) {
+  // With an explicit mask every tile takes the per-element path: the wave reads its mask slice
+  // of tile j from its LDS slot (the DMA of step j-1 has landed: the step's wait covered it),
+  // starts the DMA of tile j+1 into the same slot, and keeps a key iff the mask, causality and
+  // valid_len all allow it; an additive value is folded into the raw score before the selects,
+  // so that nothing from a hidden key (even a non-finite mask value) reaches the softmax.
+  auto mask_tile = [&](f32x16 (&sc)[2], float& mxc, int kb, int j) {
+    if constexpr (MK != kMaskNone) {
+      const unsigned char* mr = smem + MOFF + wave * MG::WB + ql * MG::RB;
+      uint32_t mw[8][2];
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        // keys 8g + 4h .. +3 of this query's row slice
+        if constexpr (MK == kMaskKeep) {
+          mw[g][0] = *(const uint32_t*)(mr + 16 * ((g >> 1) ^ MG::mswz(ql)) + 8 * (g & 1) +
+                                        4 * h);
+        } else {
+          const u32x2 w = *(const u32x2*)(mr + 16 * (g ^ MG::mswz(ql)) + 8 * h);
+          mw[g][0] = w[0];
+          mw[g][1] = w[1];
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (j + 1 < ntiles) mask_dma(j + 1);
+      int lim = kv_end - 1 - kb - 4 * h;
+      if (CAUSAL) lim = min(lim, qrow - kb - 4 * h);
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int g = 4 * t + (r >> 2), e = r & 3;
+          bool vis = 32 * t + 8 * (r >> 2) + e <= lim;
+          float x = sc[t][r];
+          if constexpr (MK == kMaskKeep) {
+            vis = vis && ((mw[g][0] >> (8 * e)) & 0xffu) != 0;
+          } else {
+            const uint32_t bits = (mw[g][e >> 1] >> (16 * (e & 1))) & 0xffffu;
+            const float a = DT == ATTN_BF16
+                                ? __uint_as_float(bits << 16)
+                                : (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+            x = __builtin_fmaf(a, p.mscale, x);
+          }
+          sc[t][r] = vis ? x : -INFINITY;
+        }
+      mxc = rowmax(sc);
+      return;
+    }
+    (void)j;
     const bool full = (!CAUSAL || kb + kBN - 1 <= qa) && kb + kBN <= kv_end;
     if (!full) {
       int lim = kv_end - 1 - kb - 4 * h;
@@ -511,7 +612,7 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
     // K_{j+2} replaces K_j (its scores were computed last iteration); V_{j+1} replaces V_{j-1}.
     if (j + 2 < ntiles) dma(j + 2, KCUR, -1);
     if (j + 1 < ntiles) dma(j + 1, -1, VNXT);
-    mask_tile(cur, mxc, j * kBN);
+    mask_tile(cur, mxc, j * kBN, j);
     tile(has_next, cur, mxc, nxt, mxn, smem + KNXT, smem + VCUR);
   };
   using I0 = std::integral_constant<int, 0>;
@@ -567,25 +668,34 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
 
 // The body uses device-only types (buffer resources), so only the device pass compiles it;
 // the host pass needs no more than the kernel's signature to emit its launch stub.
-template <int DT, int D, bool CAUSAL>
+template <int DT, int D, bool CAUSAL, int MK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(Params p) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  attn_fwd_body<DT, D, CAUSAL>(p);
+  attn_fwd_body<DT, D, CAUSAL, MK>(p);
 #endif
 }
 
-template <int DT, int D, bool CAUSAL>
+template <int DT, int D, bool CAUSAL, int MK>
 hipError_t launch(const Params& p, int64_t nwg, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_fwd_kernel<DT, D, CAUSAL>), dim3((unsigned)nwg), dim3(kThreads), 0,
-                     stream, p);
+  hipLaunchKernelGGL((attn_fwd_kernel<DT, D, CAUSAL, MK>), dim3((unsigned)nwg), dim3(kThreads),
+                     0, stream, p);
   return hipGetLastError();
 }
 
-template <int DT>
+template <int DT, int MK>
 hipError_t dispatch_d(const Params& p, int D, bool causal, int64_t nwg, hipStream_t s) {
-  if (D == 64) return causal ? launch<DT, 64, true>(p, nwg, s) : launch<DT, 64, false>(p, nwg, s);
-  return causal ? launch<DT, 128, true>(p, nwg, s) : launch<DT, 128, false>(p, nwg, s);
+  if (D == 64)
+    return causal ? launch<DT, 64, true, MK>(p, nwg, s) : launch<DT, 64, false, MK>(p, nwg, s);
+  return causal ? launch<DT, 128, true, MK>(p, nwg, s) : launch<DT, 128, false, MK>(p, nwg, s);
+}
+
+template <int DT>
+hipError_t dispatch_m(const Params& p, int D, bool causal, int mask_type, int64_t nwg,
+                      hipStream_t s) {
+  if (mask_type == ATTN_MASK_KEEP_U8) return dispatch_d<DT, kMaskKeep>(p, D, causal, nwg, s);
+  if (mask_type == ATTN_MASK_ADD) return dispatch_d<DT, kMaskAdd>(p, D, causal, nwg, s);
+  return dispatch_d<DT, kMaskNone>(p, D, causal, nwg, s);
 }
 
 bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
@@ -638,9 +748,18 @@ bool output_disjoint(const Layout& o, int B, int H, int N, int D) {
   return true;
 }
 
+// An explicit mask: element size es, strides (batch, query head, query row) in elements.
+struct MaskArg {
+  const void* ptr;
+  int type;
+  int64_t sb, sh, sn;
+};
+
+MaskArg no_mask() { return MaskArg{nullptr, ATTN_MASK_NONE, 0, 0, 0}; }
+
 int validate(const Layout& q, const Layout& k, const Layout& v, const Layout& o,
              const float* lse, int B, int Hq, int Hkv, int N, int D, float scale,
-             const int32_t* valid_len, int dtype) {
+             const int32_t* valid_len, int dtype, const MaskArg& mk = no_mask()) {
   if (!q.ptr || !k.ptr || !v.ptr || !o.ptr) return ATTN_ERR_NULL;
   if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
   if (N > ATTN_MAX_N) return ATTN_ERR_SHAPE;
@@ -668,13 +787,28 @@ int validate(const Layout& q, const Layout& k, const Layout& v, const Layout& o,
   if (valid_len && (overlaps(valid_len, (int64_t)B * 4, o.ptr, obytes) ||
                     (lse && overlaps(valid_len, (int64_t)B * 4, lse, lbytes))))
     return ATTN_ERR_ALIAS;
+  if (mk.type != ATTN_MASK_NONE) {
+    if (mk.type != ATTN_MASK_KEEP_U8 && mk.type != ATTN_MASK_ADD) return ATTN_ERR_MASK;
+    if (!mk.ptr) return ATTN_ERR_NULL;
+    const int64_t es = mk.type == ATTN_MASK_KEEP_U8 ? 1 : 2;
+    if ((uintptr_t)mk.ptr % 16 != 0 || mk.sb < 0 || mk.sh < 0 || mk.sn < N ||
+        (mk.sb * es) % 16 || (mk.sh * es) % 16 || (mk.sn * es) % 16)
+      return ATTN_ERR_LAYOUT;
+    // A wave's DMA addresses rows up to 127 past its first inside one 32-bit buffer.
+    if (((int64_t)N + kBM) * mk.sn * es > INT32_MAX) return ATTN_ERR_SHAPE;
+    // Rows are read in 16-byte units: the last row up to its next 16-byte boundary.
+    const int64_t mbytes =
+        ((B - 1) * mk.sb + (Hq - 1) * mk.sh + (int64_t)(N - 1) * mk.sn) * es + ((N * es + 15) & ~15);
+    if (overlaps(o.ptr, obytes, mk.ptr, mbytes) || (lse && overlaps(lse, lbytes, mk.ptr, mbytes)))
+      return ATTN_ERR_ALIAS;
+  }
   return ATTN_OK;
 }
 
 int run(const Layout& q, const Layout& k, const Layout& v, const Layout& o, float* lse, int B,
         int Hq, int Hkv, int N, int D, float scale, int causal, const int32_t* valid_len,
-        int dtype, void* stream) {
-  const int st = validate(q, k, v, o, lse, B, Hq, Hkv, N, D, scale, valid_len, dtype);
+        int dtype, void* stream, const MaskArg& mk = no_mask()) {
+  const int st = validate(q, k, v, o, lse, B, Hq, Hkv, N, D, scale, valid_len, dtype, mk);
   if (st != ATTN_OK) return st;
   Params p;
   p.q = (const uint16_t*)q.ptr;
@@ -694,14 +828,18 @@ int run(const Layout& q, const Layout& k, const Layout& v, const Layout& o, floa
   p.ks_b = k.sb; p.ks_h = k.sh; p.ks_n = k.sn;
   p.vs_b = v.sb; p.vs_h = v.sh; p.vs_n = v.sn;
   p.os_b = o.sb; p.os_h = o.sh; p.os_n = o.sn;
+  p.mask = mk.ptr;
+  p.ms_b = mk.sb; p.ms_h = mk.sh; p.ms_n = mk.sn;
   p.c = fabsf(scale) * kLog2e;
   p.qsign = scale < 0.f ? 0x80008000u : 0u;
   p.qmask = scale == 0.f ? 0u : 0xffffffffu;
   if (scale == 0.f) p.c = 1.0f;
+  p.mscale = kLog2e / p.c;
   const int64_t nwg = (int64_t)B * Hq * p.nqt;
   hipStream_t s = (hipStream_t)stream;
-  const hipError_t e = dtype == ATTN_BF16 ? dispatch_d<ATTN_BF16>(p, D, causal != 0, nwg, s)
-                                          : dispatch_d<ATTN_F16>(p, D, causal != 0, nwg, s);
+  const hipError_t e =
+      dtype == ATTN_BF16 ? dispatch_m<ATTN_BF16>(p, D, causal != 0, mk.type, nwg, s)
+                         : dispatch_m<ATTN_F16>(p, D, causal != 0, mk.type, nwg, s);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
@@ -745,6 +883,41 @@ extern "C" int attn_fwd_strided(const void* q, const int64_t* q_strides, const v
              Hkv, N, D, scale, causal, valid_len, dtype, stream);
 }
 
+namespace {
+
+MaskArg mask_arg(const void* mask, int mask_type, const int64_t* st, int N) {
+  if (st) return MaskArg{mask, mask_type, st[0], st[1], st[2]};
+  return MaskArg{mask, mask_type, (int64_t)N * N, 0, N};
+}
+
+}  // namespace
+
+extern "C" int attn_fwd_masked_validate(const void* q, const int64_t* q_strides, const void* k,
+                                        const int64_t* k_strides, const void* v,
+                                        const int64_t* v_strides, const void* out,
+                                        const int64_t* out_strides, const float* lse, int B,
+                                        int Hq, int Hkv, int N, int D, float scale, int causal,
+                                        const int32_t* valid_len, const void* mask,
+                                        int mask_type, const int64_t* mask_strides, int dtype) {
+  (void)causal;
+  return validate(strided(q, q_strides, Hq, N, D), strided(k, k_strides, Hkv, N, D),
+                  strided(v, v_strides, Hkv, N, D), strided(out, out_strides, Hq, N, D), lse, B,
+                  Hq, Hkv, N, D, scale, valid_len, dtype,
+                  mask_arg(mask, mask_type, mask_strides, N));
+}
+
+extern "C" int attn_fwd_masked(const void* q, const int64_t* q_strides, const void* k,
+                               const int64_t* k_strides, const void* v, const int64_t* v_strides,
+                               void* out, const int64_t* out_strides, float* lse, int B, int Hq,
+                               int Hkv, int N, int D, float scale, int causal,
+                               const int32_t* valid_len, const void* mask, int mask_type,
+                               const int64_t* mask_strides, int dtype, void* stream) {
+  return run(strided(q, q_strides, Hq, N, D), strided(k, k_strides, Hkv, N, D),
+             strided(v, v_strides, Hkv, N, D), strided(out, out_strides, Hq, N, D), lse, B, Hq,
+             Hkv, N, D, scale, causal, valid_len, dtype, stream,
+             mask_arg(mask, mask_type, mask_strides, N));
+}
+
 extern "C" const char* attn_status_string(int status) {
   switch (status) {
     case ATTN_OK: return "ok";
@@ -756,6 +929,7 @@ extern "C" const char* attn_status_string(int status) {
     case ATTN_ERR_SCALE: return "scale is not finite";
     case ATTN_ERR_LAUNCH: return "the HIP runtime reported an error at kernel launch";
     case ATTN_ERR_ALIAS: return "out or lse overlaps an input, or out overlaps lse";
+    case ATTN_ERR_MASK: return "unknown mask type";
     case ATTN_ERR_LAYOUT:
       return "bad layout: pointers must be 16-byte aligned, strides non-negative multiples of 8 "
              "elements, rows at least D elements apart, and output rows distinct";
@@ -763,4 +937,4 @@ extern "C" const char* attn_status_string(int status) {
   }
 }
 
-extern "C" int attn_version(void) { return 2; }
+extern "C" int attn_version(void) { return 3; }

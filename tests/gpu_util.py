@@ -57,6 +57,12 @@ def run_oracle(case: inputs.Case, rows=None, threads=0):
                            threads=threads)
 
 
+def run_oracle_masked(case: inputs.Case, keep_mask=None, add_mask=None, threads=0):
+    q, k, v = case.widened()
+    return oracle.attn_fwd(q, k, v, case.scale, case.causal, case.valid_len, threads=threads,
+                           keep_mask=keep_mask, add_mask=add_mask)
+
+
 def sample_rows(case: inputs.Case, per_head: int, seed=0) -> np.ndarray:
     """Flat row indices covering every (b, hq): the first and last rows, tile edges, the rows
     around valid_len[b], and random rows."""

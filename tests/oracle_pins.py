@@ -14,7 +14,10 @@ copies of it with planted mistakes (test_oracle_mutants.py). The pins are:
   * invariants: key permutation, causal row = attention over the prefix, valid_len = L equals
     truncation to L, GQA equals repeating each KV head for its group of query heads, per-(b, h)
     slices equal single-head calls, adding a constant to every score shifts only the LSE;
-  * special cases: fully masked rows give exactly 0 and -inf; very large scores stay finite.
+  * special cases: fully masked rows give exactly 0 and -inf; very large scores stay finite;
+  * explicit masks (MASK_PINS, for callables that also take keep_mask / add_mask): torch's SDPA
+    with boolean and float attn_mask, the identities that tie a mask to no mask, to causal
+    masking and to valid_len, and the closed form of an additive log-weight mask.
 """
 from __future__ import annotations
 
@@ -353,6 +356,107 @@ def pin_golden(fn):
         np.testing.assert_allclose(L[fin], exp_l[fin], rtol=0, atol=1e-14, err_msg=ex["name"])
         assert np.all(L[~fin] == exp_l[~fin]), ex["name"]
 
+
+# ---- explicit masks: pins take fn(..., keep_mask=None, add_mask=None) as well
+
+def _mask_case(seed, B=2, Hq=4, Hkv=2, N=7, D=5):
+    rng = _rng(seed)
+    return (rng, _normal(rng, (B, Hq, N, D)), _normal(rng, (B, Hkv, N, D)),
+            _normal(rng, (B, Hkv, N, D)))
+
+
+def pin_mask_library_sdpa(fn):
+    """Keep masks and additive masks, per (batch, head) and broadcast, with causal and valid_len:
+    match torch's fp64 CPU SDPA (a boolean attn_mask takes part where True, a float attn_mask is
+    added to the scaled scores) and torch.logsumexp of the masked scores."""
+    count = 0
+    for idx in range(12):
+        B, Hq, Hkv, N, D = (2, 4, 2, 9, 6) if idx % 2 else (1, 3, 1, 5, 4)
+        rng, q, k, v = _mask_case([31, idx], B, Hq, Hkv, N, D)
+        causal = bool(idx % 3 == 1)
+        vl = rng.integers(0, N + 1, size=B).astype(np.int32) if idx % 4 >= 2 else None
+        shape = (B, Hq, N, N) if idx % 5 else (1, 1, N, N)
+        scale = float(rng.uniform(0.3, 1.2))
+        if idx < 6:
+            keep = rng.random(shape) < 0.7
+            O, L = fn(q, k, v, scale, causal, vl, keep_mask=keep.astype(np.uint8))
+            tmask = torch.from_numpy(np.broadcast_to(keep, (B, Hq, N, N)).copy())
+            add = None
+        else:
+            add = rng.normal(0.0, 2.0, shape)
+            add[rng.random(shape) < 0.2] = -np.inf
+            O, L = fn(q, k, v, scale, causal, vl, add_mask=add)
+            tmask = torch.from_numpy(np.broadcast_to(np.isfinite(add), (B, Hq, N, N)).copy())
+        vis = torch.from_numpy(_visible_mask(B, N, causal, vl))[:, None] & tmask
+        tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+        g = Hq // Hkv
+        tk, tv = torch.repeat_interleave(tk, g, dim=1), torch.repeat_interleave(tv, g, dim=1)
+        if add is None:
+            ref = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=vis, scale=scale)
+            extra = 0.0
+        else:
+            fmask = torch.from_numpy(np.broadcast_to(add, (B, Hq, N, N)).copy())
+            fmask = fmask.masked_fill(~vis, float("-inf"))
+            ref = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=fmask, scale=scale)
+            extra = fmask
+        sc = torch.matmul(tq, tk.transpose(-1, -2)) * scale + extra
+        sc = sc.masked_fill(~vis, float("-inf"))
+        ref_lse = torch.logsumexp(sc, dim=-1).numpy()
+        nonempty = vis.any(-1).numpy()
+        ref = ref.numpy()
+        np.testing.assert_allclose(O[nonempty], ref[nonempty], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(L[nonempty], ref_lse[nonempty], rtol=0, atol=1e-12)
+        assert np.all(O[~nonempty] == 0.0) and np.all(np.isneginf(L[~nonempty]))
+        count += int((~nonempty).sum() > 0)
+    assert count >= 2, "no fully masked row was exercised"
+
+
+def pin_mask_identities(fn):
+    """An all-ones keep mask is no mask; a lower-triangular keep mask is causal masking; a
+    per-batch length mask is valid_len; an additive 0 is no mask; additive -inf where a keep
+    mask is 0 equals that keep mask; an additive constant per row leaves O and shifts LSE."""
+    rng, q, k, v = _mask_case([37])
+    B, Hq, N = 2, 4, 7
+    base_o, base_l = fn(q, k, v, 0.8, False)
+    for o, l in (fn(q, k, v, 0.8, False, keep_mask=np.ones((N, N), np.uint8)),
+                 fn(q, k, v, 0.8, False, add_mask=np.zeros((B, Hq, N, N)))):
+        np.testing.assert_array_equal(o, base_o)
+        np.testing.assert_array_equal(l, base_l)
+    co, cl = fn(q, k, v, 0.8, True)
+    to, tl = fn(q, k, v, 0.8, False, keep_mask=np.tril(np.ones((N, N), np.uint8)))
+    np.testing.assert_array_equal(to, co)
+    np.testing.assert_array_equal(tl, cl)
+    vl = np.array([4, 0], np.int32)
+    po, pl = fn(q, k, v, 0.8, True, vl)
+    lm = (np.arange(N)[None, None, None, :] < vl[:, None, None, None]).astype(np.uint8)
+    mo, ml = fn(q, k, v, 0.8, True, keep_mask=lm)
+    np.testing.assert_array_equal(mo, po)
+    np.testing.assert_array_equal(ml, pl)
+    keep = (rng.random((B, Hq, N, N)) < 0.6).astype(np.uint8)
+    ko, kl = fn(q, k, v, 0.8, False, keep_mask=keep)
+    ao, al = fn(q, k, v, 0.8, False, add_mask=np.where(keep > 0, 0.0, -np.inf))
+    np.testing.assert_array_equal(ao, ko)
+    np.testing.assert_array_equal(al, kl)
+    shift = rng.normal(0, 3, (B, Hq, N, 1))
+    so, sl = fn(q, k, v, 0.8, False, add_mask=np.broadcast_to(shift, (B, Hq, N, N)))
+    np.testing.assert_allclose(so, base_o, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(sl, base_l + shift[..., 0], rtol=0, atol=1e-12)
+
+
+def pin_mask_log_weights(fn):
+    """Additive mask ln w_j with w_j > 0: O = sum_j w_j e^{s_j} V_j / sum_j w_j e^{s_j} and
+    LSE = ln sum_j w_j e^{s_j}, evaluated directly for one head."""
+    rng, q, k, v = _mask_case([41], B=1, Hq=2, Hkv=1, N=6, D=3)
+    w = rng.uniform(0.05, 3.0, (1, 2, 6, 6))
+    O, L = fn(q, k, v, 0.6, False, add_mask=np.log(w))
+    for h in range(2):
+        for i in range(6):
+            e = w[0, h, i] * np.exp(0.6 * (k[0, 0] @ q[0, h, i]))
+            np.testing.assert_allclose(O[0, h, i], e @ v[0, 0] / e.sum(), rtol=0, atol=1e-12)
+            assert abs(L[0, h, i] - math.log(e.sum())) < 1e-12
+
+
+MASK_PINS = [pin_mask_library_sdpa, pin_mask_identities, pin_mask_log_weights]
 
 ALL_PINS = [pin_library_sdpa, pin_identity_weights, pin_q_zero, pin_constant_v,
             pin_causal_first_row, pin_two_keys, pin_empty_rows, pin_key_permutation,

@@ -27,7 +27,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["attn_fwd", "attn_fwd_strided", "attn_fwd_strided_validate",
+    assert declared_functions() == ["attn_fwd", "attn_fwd_masked", "attn_fwd_masked_validate",
+                                    "attn_fwd_strided", "attn_fwd_strided_validate",
                                     "attn_fwd_validate", "attn_status_string", "attn_version"]
 
 
@@ -41,13 +42,13 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_version(lib):
-    assert sdp.attn_version() == 2
+    assert sdp.attn_version() == 3
 
 
 def test_status_strings(lib):
     codes = [sdp.ATTN_OK, sdp.ATTN_ERR_NULL, sdp.ATTN_ERR_SHAPE, sdp.ATTN_ERR_HEAD_DIM,
              sdp.ATTN_ERR_DTYPE, sdp.ATTN_ERR_SCALE, sdp.ATTN_ERR_LAUNCH, sdp.ATTN_ERR_ALIAS,
-             sdp.ATTN_ERR_LAYOUT]
+             sdp.ATTN_ERR_LAYOUT, sdp.ATTN_ERR_MASK]
     texts = [sdp.attn_status_string(c) for c in codes]
     assert len(set(texts)) == len(texts)
     assert sdp.attn_status_string(12345) == "unknown status"
@@ -184,3 +185,45 @@ def test_strided_validate_rejects(lib, kw, code):
 def test_strided_validate_needs_three_strides(lib):
     with pytest.raises(ValueError):
         scall(qs=(1, 2))
+
+
+# ---- attn_fwd_masked_validate: explicit [B, H, N, N] masks
+MK = 13 * GB
+MN = 1024   # N of the mask checks (a multiple of 16, so contiguous rows are aligned)
+
+
+def mcall(**kw):
+    a = dict(mask=MK, mtype=sdp.ATTN_MASK_KEEP_U8, ms=None, N=MN, B=SB, Hq=SH, Hkv=2)
+    a.update(kw)
+    N, B, Hq, Hkv = a["N"], a["B"], a["Hq"], a["Hkv"]
+    return sdp.attn_fwd_masked_validate(Q, None, K, None, V, None, a.get("out", O), None,
+                                        a.get("lse", L), B, Hq, Hkv, N, 128, 0.088, 1, VL,
+                                        a["mask"], a["mtype"], a["ms"], sdp.ATTN_BF16)
+
+
+def test_masked_validate_accepts(lib):
+    assert mcall() == sdp.ATTN_OK                                   # [B, N, N] bytes
+    assert mcall(mtype=sdp.ATTN_MASK_ADD) == sdp.ATTN_OK            # [B, N, N] 16-bit
+    assert mcall(mtype=sdp.ATTN_MASK_NONE, mask=None) == sdp.ATTN_OK
+    assert mcall(ms=(0, 0, MN)) == sdp.ATTN_OK                      # one [N, N] for all
+    assert mcall(ms=(SH * MN * MN, MN * MN, MN)) == sdp.ATTN_OK     # per head
+    assert mcall(N=1000, ms=(1000 * 1008, 0, 1008)) == sdp.ATTN_OK  # ragged N, padded rows
+    assert mcall(N=1000, mtype=sdp.ATTN_MASK_ADD) == sdp.ATTN_OK    # 2000-byte rows
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(mtype=3), sdp.ATTN_ERR_MASK),
+    (dict(mtype=-1), sdp.ATTN_ERR_MASK),
+    (dict(mask=None), sdp.ATTN_ERR_NULL),
+    (dict(mask=MK + 8), sdp.ATTN_ERR_LAYOUT),
+    (dict(N=1000), sdp.ATTN_ERR_LAYOUT),                        # 1000-byte rows unaligned
+    (dict(N=1004, mtype=sdp.ATTN_MASK_ADD), sdp.ATTN_ERR_LAYOUT),
+    (dict(ms=(MN * MN, 0, MN - 16)), sdp.ATTN_ERR_LAYOUT),      # row stride < N
+    (dict(ms=(-MN * MN, 0, MN)), sdp.ATTN_ERR_LAYOUT),
+    (dict(ms=(MN * MN, 8, MN)), sdp.ATTN_ERR_LAYOUT),           # head stride not 16 bytes
+    (dict(ms=(0, 0, 1 << 22)), sdp.ATTN_ERR_SHAPE),             # rows beyond 2^31 bytes
+    (dict(out=MK + 4096), sdp.ATTN_ERR_ALIAS),
+    (dict(lse=MK + 65536), sdp.ATTN_ERR_ALIAS),
+])
+def test_masked_validate_rejects(lib, kw, code):
+    assert mcall(**kw) == code

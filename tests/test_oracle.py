@@ -6,11 +6,13 @@ import oracle
 import oracle_pins
 
 
-def _fn(q, k, v, scale, causal, valid_len=None, rows=None):
-    return oracle.attn_fwd(q, k, v, scale, causal, valid_len, rows=rows, threads=2)
+def _fn(q, k, v, scale, causal, valid_len=None, rows=None, keep_mask=None, add_mask=None):
+    return oracle.attn_fwd(q, k, v, scale, causal, valid_len, rows=rows, threads=2,
+                           keep_mask=keep_mask, add_mask=add_mask)
 
 
-@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda p: p.__name__)
+@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS + oracle_pins.MASK_PINS,
+                         ids=lambda p: p.__name__)
 def test_pin(pin):
     pin(_fn)
 

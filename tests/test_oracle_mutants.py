@@ -39,6 +39,18 @@ MUTANTS = [
     ("no_valid_len_clamp_high", "if (valid > N)\n                    valid = N;",
      "if (valid > N)\n                    valid = N - 1;"),
     ("kv_head_stride_uses_hq", "k + (b * Hkv + kv) * N * D", "k + (b * Hq + kv) * N * D"),
+    ("keep_mask_ignored", "if (mr->kind == 1 && mr->keep[j] == 0)", "if (0 && mr->keep[j] == 0)"),
+    ("keep_mask_inverted", "if (mr->kind == 1 && mr->keep[j] == 0)",
+     "if (mr->kind == 1 && mr->keep[j] != 0)"),
+    ("add_mask_ignored", "scores[j] += mr->add[j];", "scores[j] += 0.0;"),
+    ("add_mask_subtracted", "scores[j] += mr->add[j];", "scores[j] -= mr->add[j];"),
+    ("add_mask_scaled", "scores[j] += mr->add[j];", "scores[j] += scale * mr->add[j];"),
+    ("add_neginf_kept", "if (mr->kind == 2 && mr->add[j] == -INFINITY)", "if (0)"),
+    ("mask_row_ignored", "hq * mask_strides[1] + i * mask_strides[2]",
+     "hq * mask_strides[1] + 0 * mask_strides[2]"),
+    ("mask_head_ignored", "hq * mask_strides[1] + i * mask_strides[2]",
+     "0 * mask_strides[1] + i * mask_strides[2]"),
+    ("mask_batch_ignored", "int64_t off = b * mask_strides[0]", "int64_t off = 0 * mask_strides[0]"),
 ]
 
 
@@ -58,12 +70,13 @@ def test_mutant_is_caught(source, name, orig, mut):
             f.write(text)
         lib = oracle.load(oracle.build(src, os.path.join(d, "libmutant.so")))
 
-        def fn(q, k, v, scale, causal, valid_len=None, rows=None):
+        def fn(q, k, v, scale, causal, valid_len=None, rows=None, keep_mask=None,
+               add_mask=None):
             return oracle.attn_fwd(q, k, v, scale, causal, valid_len, rows=rows, threads=2,
-                                   lib=lib)
+                                   lib=lib, keep_mask=keep_mask, add_mask=add_mask)
 
         caught = []
-        for pin in oracle_pins.ALL_PINS:
+        for pin in oracle_pins.ALL_PINS + oracle_pins.MASK_PINS:
             try:
                 pin(fn)
             except (AssertionError, ValueError, FloatingPointError) as e:
