@@ -25,7 +25,11 @@
 //     the softmax of tile j, then P_j V_j accumulates. Each wave keeps two score tiles.
 //   * Causal and padding masks are implicit: tiles wholly above the diagonal or past valid_len
 //     are never loaded; only tiles that straddle a boundary apply a per-element mask, on a
-//     separate (slower) code path.
+//     separate (slower) code path. An explicit [B, H, N, N] keep or additive mask (the article,
+//     sections 2.1-2.2) is streamed per wave into LDS one tile ahead and applied on every tile.
+//   * Q, K, V and O are addressed through (batch, head, row) strides with contiguous rows, so
+//     [B, N, H, D] and other layouts need no copy ("Triton Cuda Attention"'s kernel takes the
+//     same strides).
 //   * The running maximum is only raised when a tile's maximum exceeds it by more than
 //     RESCALE_THRESHOLD (log2 units). Any reference value gives the same final O = acc / l and
 //     LSE = m + log2(l) as long as numerator and denominator share it; a bounded stale maximum
