@@ -44,6 +44,10 @@ def load(path: str = _LIB_PATH) -> ctypes.CDLL:
     g.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 5 + [
         ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int]
+    h = lib.oracle_attn_bwd
+    h.restype = ctypes.c_int
+    h.argtypes = [ctypes.c_void_p] * 7 + [ctypes.c_int64] * 5 + [
+        ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_int]
     lib.oracle_max_threads.restype = ctypes.c_int
     return lib
 
@@ -119,3 +123,31 @@ def attn_fwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal: 
     if rc != 0:
         raise ValueError("oracle_attn_fwd rejected its arguments (rc=%d)" % rc)
     return out, lse
+
+
+def attn_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray, scale: float,
+             causal: bool, valid_len: Optional[np.ndarray] = None, threads: int = 0,
+             lib: Optional[ctypes.CDLL] = None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Gradients (dQ, dK, dV) in fp64 of sum(O * dout) for the forward above (no mask but
+    causal / valid_len). q, dout: [B,Hq,N,D]; k, v: [B,Hkv,N,D]."""
+    lib = lib or _get_lib()
+    q, k, v, dout = (np.ascontiguousarray(x, dtype=np.float64) for x in (q, k, v, dout))
+    B, Hq, N, D = q.shape
+    Bk, Hkv, Nk, Dk = k.shape
+    if (Bk, Nk, Dk) != (B, N, D) or v.shape != k.shape or dout.shape != q.shape:
+        raise ValueError("shape mismatch")
+    vl_ptr = None
+    if valid_len is not None:
+        valid_len = np.ascontiguousarray(valid_len, dtype=np.int32)
+        if valid_len.shape != (B,):
+            raise ValueError("valid_len must have shape [B]")
+        vl_ptr = valid_len.ctypes.data
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dv = np.empty_like(v)
+    rc = lib.oracle_attn_bwd(q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data,
+                             dq.ctypes.data, dk.ctypes.data, dv.ctypes.data, B, Hq, Hkv, N, D,
+                             float(scale), int(bool(causal)), vl_ptr, int(threads))
+    if rc != 0:
+        raise ValueError("oracle_attn_bwd rejected its arguments (rc=%d)" % rc)
+    return dq, dk, dv

@@ -204,3 +204,117 @@ int oracle_max_threads(void)
 {
     return omp_get_max_threads();
 }
+
+
+/*
+ * Backward pass (test infrastructure only, like everything in this file): the exact gradients
+ * of the forward output O with respect to Q, K and V for an upstream gradient dO, i.e. of the
+ * scalar sum_{b,hq,i,d} O[b,hq,i,d] * dO[b,hq,i,d]. The pages give the forward only;
+ * tiny_flash_attn_triton.py keeps the log-sum-exp "for backward". The derivative of the
+ * definition above, with w_ij the softmax weights of row i over its visible keys J_i:
+ *
+ *   dV[b,kv,j]  = sum_{hq in group(kv)} sum_{i : j in J_i} w_ij dO[b,hq,i]
+ *   dP_ij       = <dO[b,hq,i], V[b,kv,j]>
+ *   D_i         = sum_{j in J_i} w_ij dP_ij
+ *   dS_ij       = w_ij (dP_ij - D_i)                 (derivative through the softmax)
+ *   dQ[b,hq,i]  = scale * sum_{j in J_i} dS_ij K[b,kv,j]
+ *   dK[b,kv,j]  = scale * sum_{hq in group(kv)} sum_{i : j in J_i} dS_ij Q[b,hq,i]
+ *
+ * Rows with no visible key contribute nothing and get dQ = 0. The weights are recomputed here
+ * in the three passes of the forward (no value from the device is used). Work is split over
+ * (batch, KV head), so that the dK and dV sums of one KV head belong to one thread.
+ * q, dout, dq: [B,Hq,N,D]; k, v, dk, dv: [B,Hkv,N,D]; contiguous doubles. Returns 0 or -1.
+ */
+int oracle_attn_bwd(const double *q, const double *k, const double *v, const double *dout,
+                    double *dq, double *dk, double *dv, int64_t B, int64_t Hq, int64_t Hkv,
+                    int64_t N, int64_t D, double scale, int causal, const int32_t *valid_len,
+                    int threads)
+{
+    if (!q || !k || !v || !dout || !dq || !dk || !dv)
+        return -1;
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 || D <= 0 || Hq % Hkv != 0)
+        return -1;
+    const int64_t group = Hq / Hkv;
+    int bad = 0;
+
+#pragma omp parallel num_threads(threads > 0 ? threads : omp_get_max_threads())
+    {
+        double *w = (double *)malloc((size_t)N * sizeof(double));
+        double *dp = (double *)malloc((size_t)N * sizeof(double));
+        if (!w || !dp) {
+#pragma omp atomic write
+            bad = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t bk = 0; bk < B * Hkv; ++bk) {
+            if (!w || !dp)
+                continue;
+            const int64_t b = bk / Hkv, kv = bk % Hkv;
+            const double *k_head = k + bk * N * D, *v_head = v + bk * N * D;
+            double *dk_head = dk + bk * N * D, *dv_head = dv + bk * N * D;
+            int64_t valid = N;
+            if (valid_len) {
+                valid = valid_len[b];
+                if (valid < 0)
+                    valid = 0;
+                if (valid > N)
+                    valid = N;
+            }
+            const mask_row none = {0, NULL, NULL};
+            for (int64_t x = 0; x < N * D; ++x)
+                dk_head[x] = dv_head[x] = 0.0;
+            for (int64_t hq = kv * group; hq < (kv + 1) * group; ++hq) {
+                const int64_t bh = b * Hq + hq;
+                for (int64_t i = 0; i < N; ++i) {
+                    const double *q_row = q + (bh * N + i) * D;
+                    const double *do_row = dout + (bh * N + i) * D;
+                    double *dq_row = dq + (bh * N + i) * D;
+                    int64_t j, d, visible = 0;
+                    double m = -INFINITY, l = 0.0, delta = 0.0;
+                    for (d = 0; d < D; ++d)
+                        dq_row[d] = 0.0;
+                    /* weights, as in the forward's three passes */
+                    for (j = 0; j < N; ++j) {
+                        if (!key_visible(i, j, causal, valid, &none))
+                            continue;
+                        double dot = 0.0;
+                        for (d = 0; d < D; ++d)
+                            dot += q_row[d] * k_head[j * D + d];
+                        w[j] = scale * dot;
+                        if (w[j] > m)
+                            m = w[j];
+                        ++visible;
+                    }
+                    if (visible == 0)
+                        continue;
+                    for (j = 0; j < N; ++j)
+                        if (key_visible(i, j, causal, valid, &none))
+                            l += exp(w[j] - m);
+                    for (j = 0; j < N; ++j) {
+                        if (!key_visible(i, j, causal, valid, &none))
+                            continue;
+                        w[j] = exp(w[j] - m) / l;
+                        double dot = 0.0;
+                        for (d = 0; d < D; ++d)
+                            dot += do_row[d] * v_head[j * D + d];
+                        dp[j] = dot;
+                        delta += w[j] * dot;
+                    }
+                    for (j = 0; j < N; ++j) {
+                        if (!key_visible(i, j, causal, valid, &none))
+                            continue;
+                        const double ds = w[j] * (dp[j] - delta);
+                        for (d = 0; d < D; ++d) {
+                            dq_row[d] += scale * ds * k_head[j * D + d];
+                            dk_head[j * D + d] += scale * ds * q_row[d];
+                            dv_head[j * D + d] += w[j] * do_row[d];
+                        }
+                    }
+                }
+            }
+        }
+        free(w);
+        free(dp);
+    }
+    return bad ? -1 : 0;
+}

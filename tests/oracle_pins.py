@@ -458,6 +458,98 @@ def pin_mask_log_weights(fn):
 
 MASK_PINS = [pin_mask_library_sdpa, pin_mask_identities, pin_mask_log_weights]
 
+# ---- backward: pins take fn_bwd(q, k, v, dout, scale, causal, valid_len=None) -> (dQ, dK, dV)
+# and (for the finite-difference pin) the forward callable fn.
+
+def pin_bwd_autograd(fn_bwd, fn=None):
+    """torch's fp64 autograd through scaled_dot_product_attention (its own GQA handling) with
+    causal and padding masks, on cases where every row sees a key."""
+    count = 0
+    for idx, (B, Hq, Hkv, N, D, causal, padded) in enumerate(_tiny_configs()):
+        if idx % 4:
+            continue
+        rng = _rng([43, idx])
+        q, k, v, do = (_normal(rng, s) for s in ((B, Hq, N, D), (B, Hkv, N, D), (B, Hkv, N, D),
+                                                 (B, Hq, N, D)))
+        scale = float(rng.uniform(0.2, 1.2))
+        vl = rng.integers(1, N + 1, size=B).astype(np.int32) if padded else None
+        dq, dk, dv = fn_bwd(q, k, v, do, scale, causal, vl)
+        vis = torch.from_numpy(_visible_mask(B, N, causal, vl))[:, None]
+        if not bool(vis.any(-1).all()):
+            continue
+        tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+        o = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=vis, scale=scale,
+                                           enable_gqa=(Hq != Hkv))
+        (o * torch.from_numpy(do)).sum().backward()
+        for got, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+            np.testing.assert_allclose(got, ref.numpy(), rtol=0, atol=1e-12)
+        count += 1
+    assert count > 10
+
+
+def pin_bwd_finite_difference(fn_bwd, fn):
+    """Central differences of sum(O * dO), O from the forward callable, on a tiny GQA case
+    with causal and padding masks."""
+    rng = _rng([47])
+    B, Hq, Hkv, N, D = 1, 2, 1, 5, 3
+    q, k, v, do = (_normal(rng, s) for s in ((B, Hq, N, D), (B, Hkv, N, D), (B, Hkv, N, D),
+                                             (B, Hq, N, D)))
+    vl = np.array([4], np.int32)
+    dq, dk, dv = fn_bwd(q, k, v, do, 0.8, True, vl)
+    h = 1e-6
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            old = x[idx]
+            x[idx] = old + h
+            lp = float((fn(q, k, v, 0.8, True, vl)[0] * do).sum())
+            x[idx] = old - h
+            lm = float((fn(q, k, v, 0.8, True, vl)[0] * do).sum())
+            x[idx] = old
+            num[idx] = (lp - lm) / (2 * h)
+        np.testing.assert_allclose(g, num, rtol=0, atol=1e-7)
+
+
+def pin_bwd_identities(fn_bwd, fn=None):
+    """Softmax rows sum to one, so sum_j dS_ij = 0: the dK of one KV head sums to zero over keys,
+    and the dV sums to the dO of its query heads' non-empty rows; hidden keys (past valid_len)
+    get dK = dV = 0; rows without a visible key get dQ = 0."""
+    rng = _rng([53])
+    B, Hq, Hkv, N, D = 2, 4, 2, 9, 6
+    q, k, v, do = (_normal(rng, s) for s in ((B, Hq, N, D), (B, Hkv, N, D), (B, Hkv, N, D),
+                                             (B, Hq, N, D)))
+    vl = np.array([6, 0], np.int32)
+    for causal in (False, True):
+        dq, dk, dv = fn_bwd(q, k, v, do, 0.6, causal, vl)
+        g = Hq // Hkv
+        for b in range(B):
+            for kv in range(Hkv):
+                np.testing.assert_allclose(dk[b, kv].sum(0), 0.0, atol=1e-12)
+                expect = np.zeros(D)
+                if vl[b] > 0:
+                    expect = do[b, kv * g:(kv + 1) * g].sum((0, 1))
+                np.testing.assert_allclose(dv[b, kv].sum(0), expect, atol=1e-12)
+                assert np.all(dk[b, kv, vl[b]:] == 0) and np.all(dv[b, kv, vl[b]:] == 0)
+        assert np.all(dq[1] == 0)     # batch 1 sees no key
+
+
+def pin_bwd_gqa_repeat(fn_bwd, fn=None):
+    """GQA equals MHA on K, V repeated over each group, with dK, dV summed over the group."""
+    rng = _rng([59])
+    B, Hq, Hkv, N, D = 2, 6, 2, 7, 4
+    q, k, v, do = (_normal(rng, s) for s in ((B, Hq, N, D), (B, Hkv, N, D), (B, Hkv, N, D),
+                                             (B, Hq, N, D)))
+    g = Hq // Hkv
+    dq, dk, dv = fn_bwd(q, k, v, do, 0.9, True, np.array([7, 3], np.int32))
+    rq, rk, rv = fn_bwd(q, np.repeat(k, g, axis=1), np.repeat(v, g, axis=1), do, 0.9, True,
+                        np.array([7, 3], np.int32))
+    np.testing.assert_allclose(dq, rq, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(dk, rk.reshape(B, Hkv, g, N, D).sum(2), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(dv, rv.reshape(B, Hkv, g, N, D).sum(2), rtol=0, atol=1e-13)
+
+
+BWD_PINS = [pin_bwd_autograd, pin_bwd_finite_difference, pin_bwd_identities, pin_bwd_gqa_repeat]
+
 ALL_PINS = [pin_library_sdpa, pin_identity_weights, pin_q_zero, pin_constant_v,
             pin_causal_first_row, pin_two_keys, pin_empty_rows, pin_key_permutation,
             pin_causal_prefix, pin_valid_len_truncation, pin_gqa_repeat, pin_slices,

@@ -37,3 +37,13 @@ def test_thread_count_does_not_change_results():
     O4, L4 = oracle.attn_fwd(q, k, v, 0.3, True, vl, threads=4)
     np.testing.assert_array_equal(O1, O4)
     np.testing.assert_array_equal(L1, L4)
+
+
+
+def _bwd(q, k, v, dout, scale, causal, valid_len=None):
+    return oracle.attn_bwd(q, k, v, dout, scale, causal, valid_len, threads=2)
+
+
+@pytest.mark.parametrize("pin", oracle_pins.BWD_PINS, ids=lambda p: p.__name__)
+def test_bwd_pin(pin):
+    pin(_bwd, _fn)

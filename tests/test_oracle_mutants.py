@@ -82,3 +82,51 @@ def test_mutant_is_caught(source, name, orig, mut):
             except (AssertionError, ValueError, FloatingPointError) as e:
                 caught.append(pin.__name__)
         assert caught, "no pin caught the planted mistake %s" % name
+
+
+# Planted mistakes in the backward (oracle_attn_bwd); the backward pins must catch each.
+BWD_MUTANTS = [
+    ("bwd_no_delta", "const double ds = w[j] * (dp[j] - delta);", "const double ds = w[j] * dp[j];"),
+    ("bwd_delta_sign", "const double ds = w[j] * (dp[j] - delta);",
+     "const double ds = w[j] * (dp[j] + delta);"),
+    ("bwd_dq_unscaled", "dq_row[d] += scale * ds * k_head[j * D + d];",
+     "dq_row[d] += ds * k_head[j * D + d];"),
+    ("bwd_dk_unscaled", "dk_head[j * D + d] += scale * ds * q_row[d];",
+     "dk_head[j * D + d] += ds * q_row[d];"),
+    ("bwd_dq_uses_v", "dq_row[d] += scale * ds * k_head[j * D + d];",
+     "dq_row[d] += scale * ds * v_head[j * D + d];"),
+    ("bwd_dv_uses_ds", "dv_head[j * D + d] += w[j] * do_row[d];",
+     "dv_head[j * D + d] += ds * do_row[d];"),
+    ("bwd_dp_uses_k", "dot += do_row[d] * v_head[j * D + d];",
+     "dot += do_row[d] * k_head[j * D + d];"),
+    ("bwd_delta_unweighted", "delta += w[j] * dot;", "delta += dot;"),
+    ("bwd_first_head_only", "for (int64_t hq = kv * group; hq < (kv + 1) * group; ++hq)",
+     "for (int64_t hq = kv * group; hq < kv * group + 1; ++hq)"),
+    ("bwd_unnormalised_weights", "w[j] = exp(w[j] - m) / l;", "w[j] = exp(w[j] - m);"),
+]
+
+
+@pytest.mark.parametrize("name,orig,mut", BWD_MUTANTS, ids=[m[0] for m in BWD_MUTANTS])
+def test_bwd_mutant_is_caught(source, name, orig, mut):
+    assert orig in source, "mutation site for %s no longer in the oracle source" % name
+    text = source.replace(orig, mut, 1)
+    with tempfile.TemporaryDirectory() as d:
+        src = os.path.join(d, "mutant.c")
+        with open(src, "w") as f:
+            f.write(text)
+        lib = oracle.load(oracle.build(src, os.path.join(d, "libmutant.so")))
+
+        def fn(q, k, v, scale, causal, valid_len=None, rows=None):
+            return oracle.attn_fwd(q, k, v, scale, causal, valid_len, rows=rows, threads=2,
+                                   lib=lib)
+
+        def fn_bwd(q, k, v, dout, scale, causal, valid_len=None):
+            return oracle.attn_bwd(q, k, v, dout, scale, causal, valid_len, threads=2, lib=lib)
+
+        caught = []
+        for pin in oracle_pins.BWD_PINS:
+            try:
+                pin(fn_bwd, fn)
+            except (AssertionError, ValueError, FloatingPointError):
+                caught.append(pin.__name__)
+        assert caught, "no pin caught the planted mistake %s" % name
