@@ -204,11 +204,49 @@ int attn_fwd_masked_validate(const void *q, const int64_t *q_strides, const void
                              const int32_t *valid_len, const void *mask, int mask_type,
                              const int64_t *mask_strides, int dtype);
 
+/*
+ * attn_bwd -- gradients of the attn_fwd output with respect to Q, K and V (contiguous tensors,
+ * no explicit mask), given the upstream gradient dO and the forward's own O and LSE.
+ * tiny_flash_attn_triton.py stores the log-sum-exp "for backward"; the pages stop at the
+ * forward, and this is the derivative of the forward's definition: with
+ * P = exp(scale * q.k - LSE) on the visible keys (the same causal / valid_len masks) and
+ * Delta_i = sum_d dO[i,d] O[i,d],
+ *
+ *     dV = P^T dO,   dP = dO V^T,   dS = P o (dP - Delta),   dQ = scale dS K,   dK = scale dS^T Q,
+ *
+ * dK and dV summed over the query heads sharing a KV head. LSE is treated as an auxiliary
+ * output (no gradient flows into it).
+ *
+ *   q, k, v      as in attn_fwd (device, [B,Hq,N,D] / [B,Hkv,N,D], contiguous, 16-byte aligned).
+ *   out, dout    device, [B,Hq,N,D] of dtype: the forward's O and the gradient of the loss in O.
+ *   lse          device float32 [B,Hq,N]: the forward's LSE (required).
+ *   dq           device output [B,Hq,N,D] of dtype; dk, dv: device outputs [B,Hkv,N,D] of dtype.
+ *                All written completely (rows with no visible key get dQ = 0; keys no query sees
+ *                get dK = dV = 0).
+ *   delta        device float32 [B,Hq,N] workspace owned by the caller; on return it holds
+ *                Delta (the library allocates nothing).
+ *   others       as in attn_fwd.
+ *
+ * Two kernels run on `stream` in order (dQ and Delta, then dK and dV). Outputs must not overlap
+ * any input, each other or valid_len (ATTN_ERR_ALIAS); misaligned pointers are
+ * ATTN_ERR_LAYOUT. Otherwise returns as attn_fwd.
+ */
+int attn_bwd(const void *q, const void *k, const void *v, const void *out, const void *dout,
+             const float *lse, void *dq, void *dk, void *dv, float *delta, int B, int Hq,
+             int Hkv, int N, int D, float scale, int causal, const int32_t *valid_len,
+             int dtype, void *stream);
+
+/* attn_bwd_validate -- the host-only argument check of attn_bwd. */
+int attn_bwd_validate(const void *q, const void *k, const void *v, const void *out,
+                      const void *dout, const float *lse, const void *dq, const void *dk,
+                      const void *dv, const float *delta, int B, int Hq, int Hkv, int N, int D,
+                      float scale, int causal, const int32_t *valid_len, int dtype);
+
 /* attn_status_string -- a static, NUL-terminated description of a return code (never NULL). */
 const char *attn_status_string(int status);
 
-/* attn_version -- the library's interface version, currently 3 (2 added attn_fwd_strided, 3
- * attn_fwd_masked). */
+/* attn_version -- the library's interface version, currently 4 (2 added attn_fwd_strided, 3
+ * attn_fwd_masked, 4 attn_bwd). */
 int attn_version(void);
 
 #ifdef __cplusplus

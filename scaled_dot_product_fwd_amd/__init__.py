@@ -7,10 +7,13 @@ no fallback: if the library is missing, calls raise ``ImportError``.
 Raw entry points (same names and argument order as the C ABI; pointers are integers, stride
 arguments are 3-sequences of element strides or None):
     attn_fwd, attn_fwd_validate, attn_fwd_strided, attn_fwd_strided_validate,
-    attn_fwd_masked, attn_fwd_masked_validate, attn_status_string, attn_version
+    attn_fwd_masked, attn_fwd_masked_validate, attn_bwd, attn_bwd_validate,
+    attn_status_string, attn_version
 Convenience for torch tensors (device memory and streams only):
     forward(q, k, v, causal=..., valid_len=None, scale=None, out=None, lse=None, layout="bhnd",
             attn_mask=None)
+    backward(q, k, v, out, dout, lse, causal=..., valid_len=None, scale=None)
+    attention(q, k, v, causal=..., valid_len=None, scale=None)   # torch autograd Function
 """
 from __future__ import annotations
 
@@ -20,7 +23,8 @@ from typing import Optional, Tuple
 
 __all__ = ["ATTN_F16", "ATTN_BF16", "AttnError", "attn_fwd", "attn_fwd_validate",
            "attn_fwd_strided", "attn_fwd_strided_validate", "attn_fwd_masked",
-           "attn_fwd_masked_validate", "attn_status_string",
+           "attn_fwd_masked_validate", "attn_bwd", "attn_bwd_validate", "attention",
+           "backward", "attn_status_string",
            "attn_version", "forward", "library_path", "load_library"]
 
 ATTN_F16 = 0
@@ -92,6 +96,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_fwd_masked_validate.argtypes = [_vp, _i64p, _vp, _i64p, _vp, _i64p, _vp, _i64p,
                                              _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                                              _c_float, _c_int, _vp, _vp, _c_int, _i64p, _c_int]
+    lib.attn_bwd.restype = _c_int
+    lib.attn_bwd.argtypes = [_vp] * 10 + [_c_int] * 5 + [_c_float, _c_int, _vp, _c_int, _vp]
+    lib.attn_bwd_validate.restype = _c_int
+    lib.attn_bwd_validate.argtypes = [_vp] * 10 + [_c_int] * 5 + [_c_float, _c_int, _vp, _c_int]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_status_string.argtypes = [_c_int]
     lib.attn_version.restype = _c_int
@@ -168,6 +176,22 @@ def attn_fwd_masked_validate(q: int, q_strides, k: int, k_strides, v: int, v_str
         q, _strides(q_strides), k, _strides(k_strides), v, _strides(v_strides), out,
         _strides(out_strides), lse, B, Hq, Hkv, N, D, scale, int(causal), valid_len, mask,
         mask_type, _strides(mask_strides), dtype)
+
+
+def attn_bwd(q: int, k: int, v: int, out: int, dout: int, lse: int, dq: int, dk: int, dv: int,
+             delta: int, B: int, Hq: int, Hkv: int, N: int, D: int, scale: float, causal: int,
+             valid_len: Optional[int], dtype: int, stream: Optional[int]) -> int:
+    """C ``attn_bwd``; pointers are device addresses as integers."""
+    return load_library().attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, N, D,
+                                   scale, int(causal), valid_len, dtype, stream)
+
+
+def attn_bwd_validate(q: int, k: int, v: int, out: int, dout: int, lse: int, dq: int, dk: int,
+                      dv: int, delta: int, B: int, Hq: int, Hkv: int, N: int, D: int,
+                      scale: float, causal: int, valid_len: Optional[int], dtype: int) -> int:
+    """C ``attn_bwd_validate``: host-only argument check, no HIP call."""
+    return load_library().attn_bwd_validate(q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq,
+                                            Hkv, N, D, scale, int(causal), valid_len, dtype)
 
 
 def attn_status_string(status: int) -> str:
@@ -290,3 +314,80 @@ def forward(q, k, v, causal: bool, valid_len=None, scale: Optional[float] = None
     if st != ATTN_OK:
         raise AttnError(st, where)
     return out, lse
+
+
+def backward(q, k, v, out, dout, lse, causal: bool, valid_len=None,
+             scale: Optional[float] = None, dq=None, dk=None, dv=None, delta=None, stream=None):
+    """Run attn_bwd on contiguous [B, H, N, D] torch device tensors; returns (dq, dk, dv).
+
+    ``out`` and ``lse`` are the forward's outputs for the same inputs; ``dout`` is the gradient
+    of the loss with respect to ``out``. Output tensors and the float32 [B, Hq, N] workspace
+    ``delta`` are allocated with torch when not given.
+    """
+    import torch
+    B, Hq, N, D = q.shape
+    Hkv = k.shape[1]
+    for name, t, shape in (("q", q, (B, Hq, N, D)), ("k", k, (B, Hkv, N, D)),
+                           ("v", v, (B, Hkv, N, D)), ("out", out, (B, Hq, N, D)),
+                           ("dout", dout, (B, Hq, N, D))):
+        if tuple(t.shape) != shape or t.dtype != q.dtype or not t.is_cuda:
+            raise ValueError("%s must be a device tensor of shape %s and q's dtype" % (name, shape))
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+    if lse is None or lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, N):
+        raise ValueError("lse must be the forward's float32 [B, Hq, N] tensor")
+    if scale is None:
+        scale = 1.0 / float(D) ** 0.5
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if delta is None:
+        delta = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    vl_ptr = None
+    if valid_len is not None:
+        if valid_len.dtype != torch.int32 or tuple(valid_len.shape) != (B,) or not valid_len.is_cuda:
+            raise ValueError("valid_len must be an int32 device tensor of shape [B]")
+        vl_ptr = valid_len.data_ptr()
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+                  lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                  B, Hq, Hkv, N, D, float(scale), int(bool(causal)), vl_ptr, _dtype_code(q),
+                  stream.cuda_stream)
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_bwd")
+    return dq, dk, dv
+
+
+def _autograd_function():
+    import torch
+
+    class _Attention(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, causal, valid_len, scale):
+            q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+            out, lse = forward(q, k, v, causal=causal, valid_len=valid_len, scale=scale)
+            ctx.save_for_backward(q, k, v, out, lse, valid_len)
+            ctx.causal, ctx.scale = causal, scale
+            return out
+
+        @staticmethod
+        def backward(ctx, dout):
+            q, k, v, out, lse, valid_len = ctx.saved_tensors
+            dq, dk, dv = backward(q, k, v, out, dout.contiguous(), lse, causal=ctx.causal,
+                                  valid_len=valid_len, scale=ctx.scale)
+            return dq, dk, dv, None, None, None
+
+    return _Attention
+
+
+_ATTENTION = None
+
+
+def attention(q, k, v, causal: bool, valid_len=None, scale: Optional[float] = None):
+    """Differentiable attention on [B, H, N, D] tensors: forward through attn_fwd, gradients
+    through attn_bwd (torch.autograd glue only)."""
+    global _ATTENTION
+    if _ATTENTION is None:
+        _ATTENTION = _autograd_function()
+    return _ATTENTION.apply(q, k, v, causal, valid_len, scale)

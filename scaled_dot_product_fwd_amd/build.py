@@ -10,7 +10,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "attn_fwd.hip")
+SRCS = [os.path.join(PKG, "csrc", "attn_fwd.hip"), os.path.join(PKG, "csrc", "attn_bwd.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -23,7 +23,7 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
 
 def build(out: str = LIB, extra_flags=()) -> str:
     tmp = out + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *FLAGS, *extra_flags, "-I", INCLUDE, SRC, "-o", tmp]
+    cmd = [HIPCC, *FLAGS, *extra_flags, "-I", INCLUDE, *SRCS, "-o", tmp]
     proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     # hipcc's host pass does not know the packed-fp32 target feature and says so; that is noise.
     lines = [ln for ln in proc.stdout.splitlines() if "packed-fp32-ops" not in ln]

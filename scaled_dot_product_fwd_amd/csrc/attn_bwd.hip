@@ -1,0 +1,617 @@
+// Backward of the fused attention forward for CDNA4 (gfx950), behind attn_bwd in attn.h.
+//
+// What it computes: the gradients of the forward output O with respect to Q, K and V for an
+// upstream gradient dO, using the forward's log-sum-exp L (tiny_flash_attn_triton.py keeps L
+// "for backward"; the forward stores it in base e). With the weights recomputed per tile as
+// P = exp(scale * q.k - L) on the visible keys (the same causal / valid_len masks as the
+// forward), and D_i = sum_d dO[i,d] * O[i,d]:
+//
+//   dP = dO V^T,   dS = P o (dP - D),   dQ = scale * dS K,   dK = scale * dS^T Q,   dV = P^T dO,
+//
+// with dK and dV summed over the query heads of each KV head (grouped-query attention, the
+// "Triton Cuda Attention" page's GQA section). Two kernels, launched in this order on the
+// caller's stream:
+//
+//   * bwd_dq: one workgroup per (batch, query head, 128-query tile), 4 waves x 32 queries, the
+//     forward's decomposition. Each wave holds its Q and dO fragments in registers, computes
+//     D = rowsum(dO o O) (stored to the caller's workspace for the second kernel), then streams
+//     64-key K/V tiles through LDS: S^T = K Q^T and dP^T = V dO^T on MFMA (lane = query, as in
+//     the forward), P and dS on the VALU, and dQ^T += K^T dS^T with K^T read through
+//     ds_read_b64_tr_b16. dQ is written once (no atomics).
+//   * bwd_dkdv: one workgroup per (batch, KV head, 128-key tile), 4 waves x 32 keys. Each wave
+//     keeps its keys' K fragments in registers and their V rows in LDS, and streams 32-query
+//     tiles of Q, dO, L and D of every query head of the group (only queries at or after the
+//     tile's first key under causal masking): S = Q K^T and dP = dO V^T (lane = key), P and dS
+//     on the VALU, dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read through
+//     ds_read_b64_tr_b16. dK and dV are written once.
+//
+// Inputs are contiguous [B, H, N, D] tensors of one 16-bit type; dQ, dK, dV are written in that
+// type (fp32 accumulation, round to nearest even). P and dS are rounded to the input type
+// before they enter an MFMA, as the forward rounds P.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "attn.h"
+#include "attn_common.h"
+
+namespace {
+
+using namespace attn_detail;
+
+constexpr int kQT = 32;   // queries per iteration of the dK/dV kernel
+
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* lse;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* delta;
+  const int32_t* valid_len;
+  int B, Hq, Hkv, N;
+  int group;       // Hq / Hkv
+  int nqt;         // ceil(N / kBM): query tiles of the dQ kernel
+  int nkt;         // ceil(N / kBM): key tiles of the dK/dV kernel
+  int xcd_order;   // 1: KV heads divide evenly over the 8 XCDs
+  float c;         // |scale| * log2(e)
+  float scale;     // the signed scale (dQ and dK carry it)
+  uint32_t qsign;  // 0x80008000 when scale < 0: one operand of the scores is negated instead
+  uint32_t qmask;  // 0 when scale == 0 (all scores are 0; c is 1)
+};
+
+// Row value of the log-sum-exp in log2 units; an empty row (L = -inf) has only hidden keys, and
+// 0 keeps exp2(-inf - 0) = 0 there instead of NaN.
+__device__ inline float lse_log2(float L) { return L == -INFINITY ? 0.f : L * kLog2e; }
+
+// Round 16 products dS (or P) of one lane, in the forward's key order, into the two 16-bit
+// operands of an MFMA k-step: block s holds elements 8s .. 8s+7.
+template <int DT>
+__device__ inline u32x4 pack8(const float (&x)[16], int s) {
+  f32x8 v;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = x[8 * s + e];
+  return Mfma<DT>::pack(v);
+}
+
+// Write a wave's 32 x D block, held transposed in acc (acc[u][4 r4 + e] is element
+// d = 32u + 8 r4 + 4h + e of row ql), as rows of `dst` (row stride D) through the wave's LDS
+// staging area `ost` (32 * ROW bytes). Rows at or past n are not written.
+template <int DT, int D>
+__device__ inline void store_rows(const f32x16 (&acc)[Geo<D>::OT], float mul,
+                                  unsigned char* ost, uint16_t* dst, int row0, int n, int lane) {
+  using G = Geo<D>;
+  using M = Mfma<DT>;
+  const int h = lane >> 5, ql = lane & 31;
+#pragma unroll
+  for (int u = 0; u < G::OT; ++u)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int c = 4 * u + r4;
+      const uint32_t w0 = (uint32_t)M::round1(acc[u][4 * r4 + 0] * mul) |
+                          ((uint32_t)M::round1(acc[u][4 * r4 + 1] * mul) << 16);
+      const uint32_t w1 = (uint32_t)M::round1(acc[u][4 * r4 + 2] * mul) |
+                          ((uint32_t)M::round1(acc[u][4 * r4 + 3] * mul) << 16);
+      *(u32x2*)(ost + ql * G::ROW + 16 * (c ^ (ql & (G::CH - 1))) + 8 * h) = u32x2{w0, w1};
+    }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  constexpr int RPI = 64 / G::CH;
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = i * RPI + lane / G::CH;
+    const int cc = lane % G::CH;
+    const u32x4 v = *(const u32x4*)(ost + r * G::ROW + 16 * (cc ^ (r & (G::CH - 1))));
+    if (row0 + r < n) *(u32x4*)(dst + (size_t)(row0 + r) * D + 8 * cc) = v;
+  }
+}
+
+// Lane offsets of ds_read_b64_tr_b16 reads of a transposed 32 x 16 operand from a row-major tile
+// stored with Geo<D>::vswz: lane 16g + jj reads row 4(g/2) + jj/4 (+16 per k-step, +8 for the
+// second 4 rows), columns 32u + 16(g%2) + 4(jj%4) .. +3 (the forward's V^T read).
+template <int D>
+__device__ inline uint32_t tr_offset(int lane, int u) {
+  using G = Geo<D>;
+  const int g = lane >> 4, jj = lane & 15;
+  const int row = 4 * (g >> 1) + (jj >> 2);
+  return row * G::ROW + 16 * ((4 * u + 2 * (g & 1) + ((jj & 3) >> 1)) ^ G::vswz(row)) +
+         8 * (jj & 1);
+}
+
+__device__ inline u32x4 tr_frag(const unsigned char* base, int rows8) {
+  const u32x2 lo = lds_read_tr16(base);
+  const u32x2 hi = lds_read_tr16(base + rows8);
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// ------------------------------------------------------------------------------------------
+// dQ (and D)
+// ------------------------------------------------------------------------------------------
+template <int DT, int D, bool CAUSAL>
+__device__ __forceinline__ void bwd_dq_body(const BwdParams& p) {
+  using G = Geo<D>;
+  using M = Mfma<DT>;
+  constexpr int KSTEPS = G::KSTEPS;
+  constexpr int OT = G::OT;
+  // K0 K1 V0 V1, 64-key tiles. K is stored with vswz (read both as rows and transposed), V
+  // with kswz (read as rows).
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[G::LDS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5;
+  const int ql = lane & 31;
+
+  int qt, b, hq;
+  {
+    const int wid = blockIdx.x;
+    if (p.xcd_order) {
+      const int xcd = wid & 7, local = wid >> 3;
+      const int per_head = p.group * p.nqt;
+      const int head_local = local / per_head;
+      const int r = local - head_local * per_head;
+      const int kv_head = head_local * 8 + xcd;
+      const int qi = r / p.group;
+      qt = CAUSAL ? p.nqt - 1 - qi : qi;
+      b = kv_head / p.Hkv;
+      hq = (kv_head - b * p.Hkv) * p.group + (r - qi * p.group);
+    } else {
+      const int BH = p.B * p.Hq;
+      const int qi = wid / BH, bh = wid - qi * BH;
+      qt = CAUSAL ? p.nqt - 1 - qi : qi;
+      b = bh / p.Hq;
+      hq = bh - b * p.Hq;
+    }
+  }
+  const int bh = b * p.Hq + hq;
+  const int kvh = hq / p.group;
+  const int q0 = qt * kBM;
+  int kv_end = p.N;
+  if (p.valid_len) kv_end = min(max(p.valid_len[b], 0), p.N);
+  int kv_stop = kv_end;
+  if (CAUSAL) kv_stop = min(kv_stop, q0 + kBM);
+  const int ntiles = (kv_stop + kBN - 1) / kBN;
+  const int qa = q0 + wave * 32;
+  const int qrow = qa + ql;
+  const int qr = min(qrow, p.N - 1);
+
+  const size_t kv_off = (size_t)(b * p.Hkv + kvh) * p.N * D;
+  const uint32_t head_bytes = (uint32_t)p.N * G::ROW;
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + kv_off), (short)0, head_bytes, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + kv_off), (short)0, head_bytes, kBufferFlags);
+  uint32_t kdma, vdma[G::LOADS];
+  {
+    const int row = wave * G::LOADS * G::RPB + lane / G::CH;
+    kdma = row * G::ROW + (((lane % G::CH) ^ G::vswz(row)) * 16);
+#pragma unroll
+    for (int i = 0; i < G::LOADS; ++i) {
+      const int r = (wave * G::LOADS + i) * G::RPB + lane / G::CH;
+      vdma[i] = r * G::ROW + (((lane % G::CH) ^ G::kswz(r)) * 16);
+    }
+  }
+  auto dma = [&](int tile, int kdst, int vdst) {
+    const int soff = tile * G::TILE;
+#pragma unroll
+    for (int i = 0; i < G::LOADS; ++i) {
+      const int blk = (wave * G::LOADS + i) * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(smem + kdst + blk), 16, kdma,
+                                               soff + i * 1024, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(smem + vdst + blk), 16, vdma[i],
+                                               soff, 0, 0);
+    }
+  };
+
+  // Fragment offsets: K rows (A of S^T), V rows (A of dP^T), K^T (A of dQ^T).
+  uint32_t kaddr[KSTEPS], vaddr[KSTEPS], taddr[OT];
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) {
+    kaddr[ks] = ql * G::ROW + 16 * ((2 * ks + h) ^ G::vswz(ql));
+    vaddr[ks] = ql * G::ROW + 16 * ((2 * ks + h) ^ G::kswz(ql));
+  }
+#pragma unroll
+  for (int u = 0; u < OT; ++u) taddr[u] = tr_offset<D>(lane, u);
+
+  if (ntiles > 0) dma(0, G::K0, G::V0);
+
+  // Q, dO and O of this lane's row (B-operand layout: Q[row][16s + 8h .. +7]).
+  const size_t rowoff = ((size_t)bh * p.N + qr) * D + 8 * h;
+  u32x4 qf[KSTEPS], dof[KSTEPS], of[KSTEPS];
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) {
+    qf[s] = *(const u32x4*)(p.q + rowoff + 16 * s);
+    dof[s] = *(const u32x4*)(p.dout + rowoff + 16 * s);
+    of[s] = *(const u32x4*)(p.o + rowoff + 16 * s);
+  }
+  const float L = lse_log2(p.lse[(size_t)bh * p.N + qr]);
+  // D = rowsum(dO o O): this lane's half of the row, then the lane pair.
+  float dsum = 0.f;
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t a = dof[s][w], o = of[s][w];
+      if (DT == ATTN_BF16) {
+        dsum = __builtin_fmaf(__uint_as_float(a << 16), __uint_as_float(o << 16), dsum);
+        dsum = __builtin_fmaf(__uint_as_float(a & 0xffff0000u), __uint_as_float(o & 0xffff0000u),
+                              dsum);
+      } else {
+        dsum = __builtin_fmaf((float)__builtin_bit_cast(_Float16, (uint16_t)(a & 0xffff)),
+                              (float)__builtin_bit_cast(_Float16, (uint16_t)(o & 0xffff)), dsum);
+        dsum = __builtin_fmaf((float)__builtin_bit_cast(_Float16, (uint16_t)(a >> 16)),
+                              (float)__builtin_bit_cast(_Float16, (uint16_t)(o >> 16)), dsum);
+      }
+    }
+  const float delta = pair_sum(dsum);
+  if (h == 0 && qrow < p.N) p.delta[(size_t)bh * p.N + qrow] = delta;
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) qf[s] = (qf[s] ^ p.qsign) & p.qmask;
+
+  f32x16 acc[OT];
+#pragma unroll
+  for (int u = 0; u < OT; ++u) acc[u] = f32x16{};
+  const float c = p.c;
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int P = j & 1;
+    const int kcur = P ? G::K1 : G::K0, vcur = P ? G::V1 : G::V0;
+    wait_loads_and_lds();
+    __syncthreads();
+    if (j + 1 < ntiles) dma(j + 1, P ? G::K0 : G::K1, P ? G::V0 : G::V1);
+    const unsigned char* kb = smem + kcur;
+    const unsigned char* vb = smem + vcur;
+    // S^T and dP^T for the tile's two 32-key halves
+    f32x16 sc[2], dp[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      sc[t] = f32x16{};
+      dp[t] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        sc[t] = M::run(*(const u32x4*)(kb + kaddr[ks] + t * 32 * G::ROW), qf[ks], sc[t]);
+        dp[t] = M::run(*(const u32x4*)(vb + vaddr[ks] + t * 32 * G::ROW), dof[ks], dp[t]);
+      }
+    }
+    // masks: key = kb0 + 32t + 8(r/4) + 4h + r%4
+    const int kb0 = j * kBN;
+    const bool full = (!CAUSAL || kb0 + kBN - 1 <= qa) && kb0 + kBN <= kv_end;
+    int lim = 1 << 30;
+    if (!full) {
+      lim = kv_end - 1 - kb0 - 4 * h;
+      if (CAUSAL) lim = min(lim, qrow - kb0 - 4 * h);
+    }
+    float ds[2][16];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][r], c, -L));
+        const float v = pr * (dp[t][r] - delta);
+        ds[t][r] = (32 * t + 8 * (r >> 2) + (r & 3) <= lim) ? v : 0.f;
+      }
+    // dQ^T += K^T dS^T, four 16-key k-steps
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const u32x4 bsd = pack8<DT>(ds[s >> 1], s & 1);
+#pragma unroll
+      for (int u = 0; u < OT; ++u)
+        acc[u] = M::run(tr_frag(kb + taddr[u] + 16 * s * G::ROW, 8 * G::ROW), bsd, acc[u]);
+    }
+  }
+
+  // dQ = scale * (dQ^T)^T, staged through LDS after every wave is done with the tiles.
+  wait_loads_and_lds();
+  __syncthreads();
+  store_rows<DT, D>(acc, p.scale, smem + wave * 32 * G::ROW, p.dq + (size_t)bh * p.N * D, qa,
+                    p.N, lane);
+}
+
+// ------------------------------------------------------------------------------------------
+// dK, dV
+// ------------------------------------------------------------------------------------------
+template <int D>
+struct BwdGeo {
+  using G = Geo<D>;
+  static constexpr int VREG = 128 * G::ROW;            // V rows of the workgroup's 128 keys
+  static constexpr int QTILE = kQT * G::ROW;           // one 32-row Q or dO tile
+  static constexpr int LD = 2048;                      // 1 KiB slots for L and D of one tile
+  static constexpr int BUF = 2 * QTILE + LD;           // one buffer: Q, dO, L, D
+  static constexpr int QB0 = VREG;                     // buffer 0
+  static constexpr int LDS = VREG + 2 * BUF;
+  static constexpr int QLOADS = QTILE / 1024 / kWaves; // 1 KiB DMA blocks per wave per tile
+  static_assert(QLOADS >= 1, "tile geometry");
+};
+
+template <int DT, int D, bool CAUSAL>
+__device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
+  using G = Geo<D>;
+  using BG = BwdGeo<D>;
+  using M = Mfma<DT>;
+  constexpr int KSTEPS = G::KSTEPS;
+  constexpr int OT = G::OT;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[BG::LDS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5;
+  const int ql = lane & 31;
+
+  // ---- work: (batch, KV head, 128-key tile); under causal masking the first key tiles see the
+  // most queries and run first.
+  int kt, b, kvh;
+  {
+    const int wid = blockIdx.x;
+    if (p.xcd_order) {
+      const int xcd = wid & 7, local = wid >> 3;
+      const int head_local = local / p.nkt;
+      kt = local - head_local * p.nkt;
+      const int kv_head = head_local * 8 + xcd;
+      b = kv_head / p.Hkv;
+      kvh = kv_head - b * p.Hkv;
+    } else {
+      const int BK = p.B * p.Hkv;
+      kt = wid / BK;
+      const int bk = wid - kt * BK;
+      b = bk / p.Hkv;
+      kvh = bk - b * p.Hkv;
+    }
+  }
+  const int k0 = kt * kBM;
+  const int kw = k0 + wave * 32;   // this wave's first key
+  const int key = kw + ql;         // this lane's key (MFMA output column)
+  int kv_end = p.N;
+  if (p.valid_len) kv_end = min(max(p.valid_len[b], 0), p.N);
+  const size_t kv_off = (size_t)(b * p.Hkv + kvh) * p.N * D;
+  unsigned char* vreg = smem + wave * 32 * G::ROW;   // this wave's 32 V rows
+
+  f32x16 dk[OT], dv[OT];
+#pragma unroll
+  for (int u = 0; u < OT; ++u) dk[u] = dv[u] = f32x16{};
+
+  const int qstart = CAUSAL ? k0 : 0;
+  const int ntq = k0 < kv_end ? (p.N - qstart + kQT - 1) / kQT : 0;   // query tiles per head
+  const int iters = ntq * p.group;
+
+  if (iters > 0) {
+    // K^T fragments of this lane's key (B operand: K[key][16s + 8h .. +7]), sign/zero applied.
+    u32x4 kf[KSTEPS];
+    {
+      const uint16_t* ksrc = p.k + kv_off + (size_t)min(key, p.N - 1) * D + 8 * h;
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) kf[s] = (*(const u32x4*)(ksrc + 16 * s) ^ p.qsign) & p.qmask;
+    }
+    // V rows of this wave's keys into its LDS rows (vswz layout, read as rows).
+    {
+      const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(p.v + kv_off), (short)0, (uint32_t)p.N * G::ROW, kBufferFlags);
+      const int row = lane / G::CH;
+      const uint32_t off = row * G::ROW + (((lane % G::CH) ^ G::vswz(row)) * 16);
+#pragma unroll
+      for (int i = 0; i < 32 / G::RPB; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(vreg + i * 1024), 16, off,
+                                                 (uint32_t)(kw + i * G::RPB) * G::ROW, 0, 0);
+    }
+    // DMA of iteration `it` (query head kvh * group + it / ntq, queries q0 .. q0+31) into
+    // buffer `buf`: Q and dO tiles (vswz layout), L and D (wave 0 and 1).
+    const int qrow_l = lane / G::CH;   // row within a 1 KiB block
+    const uint32_t qoff = qrow_l * G::ROW + (((lane % G::CH) ^ G::vswz(qrow_l)) * 16);
+    auto dma = [&](int it, int buf) {
+      const int g = it / ntq;
+      const int q0 = qstart + (it - g * ntq) * kQT;
+      const int bh = b * p.Hq + kvh * p.group + g;
+      const size_t hoff = (size_t)bh * p.N * D;
+      const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(p.q + hoff), (short)0, (uint32_t)p.N * G::ROW, kBufferFlags);
+      const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(p.dout + hoff), (short)0, (uint32_t)p.N * G::ROW, kBufferFlags);
+      unsigned char* base = smem + BG::QB0 + buf * BG::BUF;
+#pragma unroll
+      for (int i = 0; i < BG::QLOADS; ++i) {
+        const int blk = wave * BG::QLOADS + i;
+        const uint32_t soff = (uint32_t)(q0 + blk * G::RPB) * G::ROW;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void*)(base + blk * 1024), 16, qoff,
+                                                 soff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ors, (lds_void*)(base + BG::QTILE + blk * 1024),
+                                                 16, qoff, soff, 0, 0);
+      }
+      if (wave < 2) {
+        const float* src = wave == 0 ? p.lse : p.delta;
+        const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(src + (size_t)bh * p.N), (short)0, (uint32_t)p.N * 4, kBufferFlags);
+        // one dword per query row (lanes 0..31); a 16-byte load would straddle the end of the
+        // row range when N % 4 != 0. Lanes 32..63 are out of range and write zeros to bytes
+        // 128..255 of the wave's 1 KiB slot.
+        const uint32_t loff = lane < kQT ? (uint32_t)(q0 + lane) * 4 : 0x7ffffff0u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            lrs, (lds_void*)(base + 2 * BG::QTILE + wave * 1024), 4, loff, 0, 0, 0);
+      }
+    };
+
+    // Fragment offsets: rows of Q / dO / V (A of S and dP, B of dP), transposed Q / dO.
+    uint32_t raddr[KSTEPS], taddr[OT];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) raddr[ks] = ql * G::ROW + 16 * ((2 * ks + h) ^ G::vswz(ql));
+#pragma unroll
+    for (int u = 0; u < OT; ++u) taddr[u] = tr_offset<D>(lane, u);
+    const float c = p.c;
+
+    dma(0, 0);
+    for (int it = 0; it < iters; ++it) {
+      const int buf = it & 1;
+      wait_loads_and_lds();
+      __syncthreads();
+      if (it + 1 < iters) dma(it + 1, buf ^ 1);
+      const int q0 = qstart + (it % ntq) * kQT;
+      const unsigned char* qb = smem + BG::QB0 + buf * BG::BUF;
+      const unsigned char* ob = qb + BG::QTILE;
+      const float* lb = (const float*)(qb + 2 * BG::QTILE);
+      const float* db = (const float*)(qb + 2 * BG::QTILE + 1024);
+      // S = Q K^T and dP = dO V^T (rows: queries q0 + 8(r/4) + 4h + r%4; column: key)
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        s = M::run(*(const u32x4*)(qb + raddr[ks]), kf[ks], s);
+        dp = M::run(*(const u32x4*)(ob + raddr[ks]), *(const u32x4*)(vreg + raddr[ks]), dp);
+      }
+      float pr[16], ds[16];
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int qi0 = 8 * r4 + 4 * h;   // first of this group's 4 query rows in the tile
+        const f32x4 lv = *(const f32x4*)(lb + qi0);
+        const f32x4 dv4 = *(const f32x4*)(db + qi0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * r4 + e;
+          const int qi = q0 + qi0 + e;
+          const bool vis = (!CAUSAL || key <= qi) && key < kv_end && qi < p.N;
+          const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse_log2(lv[e])));
+          pr[r] = vis ? x : 0.f;
+          ds[r] = pr[r] * (dp[r] - dv4[e]);
+        }
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS over the two 16-query k-steps
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const u32x4 bp = pack8<DT>(pr, k2);
+        const u32x4 bs = pack8<DT>(ds, k2);
+#pragma unroll
+        for (int u = 0; u < OT; ++u) {
+          dv[u] = M::run(tr_frag(ob + taddr[u] + 16 * k2 * G::ROW, 8 * G::ROW), bp, dv[u]);
+          dk[u] = M::run(tr_frag(qb + taddr[u] + 16 * k2 * G::ROW, 8 * G::ROW), bs, dk[u]);
+        }
+      }
+    }
+    wait_loads_and_lds();
+  }
+  __syncthreads();
+  // dK = scale * (dK^T)^T, dV = (dV^T)^T; rows past N are not written. Staging reuses the Q/dO
+  // buffers (every wave is past its last read).
+  unsigned char* ost = smem + BG::QB0 + wave * 32 * G::ROW;
+  store_rows<DT, D>(dk, p.scale, ost, p.dk + kv_off, kw, p.N, lane);
+  store_rows<DT, D>(dv, 1.0f, ost, p.dv + kv_off, kw, p.N, lane);
+}
+
+template <int DT, int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_dq_kernel(BwdParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  bwd_dq_body<DT, D, CAUSAL>(p);
+#endif
+}
+
+template <int DT, int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_dkdv_kernel(BwdParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  bwd_dkdv_body<DT, D, CAUSAL>(p);
+#endif
+}
+
+template <int DT, int D, bool CAUSAL>
+hipError_t launch_bwd(const BwdParams& p, hipStream_t s) {
+  const int64_t nq = (int64_t)p.B * p.Hq * p.nqt;
+  const int64_t nk = (int64_t)p.B * p.Hkv * p.nkt;
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<DT, D, CAUSAL>), dim3((unsigned)nq), dim3(kThreads), 0,
+                     s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DT, D, CAUSAL>), dim3((unsigned)nk), dim3(kThreads),
+                     0, s, p);
+  return hipGetLastError();
+}
+
+template <int DT>
+hipError_t dispatch_bwd(const BwdParams& p, int D, bool causal, hipStream_t s) {
+  if (D == 64) return causal ? launch_bwd<DT, 64, true>(p, s) : launch_bwd<DT, 64, false>(p, s);
+  return causal ? launch_bwd<DT, 128, true>(p, s) : launch_bwd<DT, 128, false>(p, s);
+}
+
+bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+}  // namespace
+
+extern "C" int attn_bwd_validate(const void* q, const void* k, const void* v, const void* out,
+                                 const void* dout, const float* lse, const void* dq,
+                                 const void* dk, const void* dv, const float* delta, int B,
+                                 int Hq, int Hkv, int N, int D, float scale, int causal,
+                                 const int32_t* valid_len, int dtype) {
+  (void)causal;
+  if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv || !delta)
+    return ATTN_ERR_NULL;
+  if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+  if (N > ATTN_MAX_N) return ATTN_ERR_SHAPE;
+  if ((int64_t)B * Hq * (((int64_t)N + kBM - 1) / kBM) > ATTN_MAX_TILES) return ATTN_ERR_SHAPE;
+  if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
+  if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+  if (!isfinite(scale)) return ATTN_ERR_SCALE;
+  const void* ptrs16[] = {q, k, v, out, dout, dq, dk, dv};
+  for (const void* ptr : ptrs16)
+    if ((uintptr_t)ptr % 16 != 0) return ATTN_ERR_LAYOUT;
+  if ((uintptr_t)lse % 4 != 0 || (uintptr_t)delta % 4 != 0) return ATTN_ERR_LAYOUT;
+  const int64_t qb = (int64_t)B * Hq * N * D * 2, kb = (int64_t)B * Hkv * N * D * 2;
+  const int64_t lb = (int64_t)B * Hq * N * 4;
+  // Outputs: dq, dk, dv, delta; none may overlap an input or another output.
+  const void* outs[] = {dq, dk, dv, delta};
+  const int64_t osz[] = {qb, kb, kb, lb};
+  const void* ins[] = {q, k, v, out, dout, lse};
+  const int64_t isz[] = {qb, kb, kb, qb, qb, lb};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outs[i], osz[i], ins[j], isz[j])) return ATTN_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], osz[i], outs[j], osz[j])) return ATTN_ERR_ALIAS;
+    if (valid_len && overlaps(outs[i], osz[i], valid_len, (int64_t)B * 4)) return ATTN_ERR_ALIAS;
+  }
+  return ATTN_OK;
+}
+
+extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* out,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        float* delta, int B, int Hq, int Hkv, int N, int D, float scale,
+                        int causal, const int32_t* valid_len, int dtype, void* stream) {
+  const int st = attn_bwd_validate(q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, N, D,
+                                   scale, causal, valid_len, dtype);
+  if (st != ATTN_OK) return st;
+  BwdParams p;
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.o = (const uint16_t*)out;
+  p.dout = (const uint16_t*)dout;
+  p.lse = lse;
+  p.dq = (uint16_t*)dq;
+  p.dk = (uint16_t*)dk;
+  p.dv = (uint16_t*)dv;
+  p.delta = delta;
+  p.valid_len = valid_len;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.N = N;
+  p.group = Hq / Hkv;
+  p.nqt = (N + kBM - 1) / kBM;
+  p.nkt = (N + kBM - 1) / kBM;
+  p.xcd_order = ((int64_t)B * Hkv) % 8 == 0 ? 1 : 0;
+  p.c = fabsf(scale) * kLog2e;
+  p.scale = scale;
+  p.qsign = scale < 0.f ? 0x80008000u : 0u;
+  p.qmask = scale == 0.f ? 0u : 0xffffffffu;
+  if (scale == 0.f) p.c = 1.0f;
+  const hipStream_t s = (hipStream_t)stream;
+  const hipError_t e = dtype == ATTN_BF16 ? dispatch_bwd<ATTN_BF16>(p, D, causal != 0, s)
+                                          : dispatch_bwd<ATTN_F16>(p, D, causal != 0, s);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}

@@ -45,53 +45,13 @@
 #include <type_traits>
 
 #include "attn.h"
+#include "attn_common.h"
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
-typedef _Float16 f16x8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
-typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
-typedef float f32x8 __attribute__((__vector_size__(8 * sizeof(float))));
-typedef short i16x4 __attribute__((__vector_size__(4 * sizeof(short))));
-typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
-typedef uint32_t u32x2 __attribute__((__vector_size__(2 * sizeof(uint32_t))));
-typedef __attribute__((address_space(3))) void lds_void;
+using namespace attn_detail;
 
-constexpr int kBM = 128;        // query rows per workgroup (32 per wave)
-constexpr int kBN = 64;         // keys per K/V tile
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 constexpr float RESCALE_THRESHOLD = 8.0f;
-constexpr int kBufferFlags = 0x00020000;   // raw buffer: dword data, range-checked
-
-template <int D>
-struct Geo {
-  static constexpr int CH = D / 8;                   // 16-byte chunks per row
-  static constexpr int ROW = 2 * D;                  // bytes per row
-  static constexpr int TILE = kBN * ROW;             // bytes per K or V tile
-  static constexpr int LOADS = TILE / 1024 / kWaves; // 1 KiB DMA blocks per wave per tile
-  static constexpr int RPB = 1024 / ROW;             // rows per 1 KiB block
-  static constexpr int KSTEPS = D / 16;              // k-steps of the score MFMA
-  static constexpr int OT = D / 32;                  // 32-row tiles of O^T
-  static constexpr int K0 = 0, K1 = TILE, V0 = 2 * TILE, V1 = 3 * TILE;
-  static constexpr int LDS = 4 * TILE;
-  // LDS row r of a tile stores global 16-byte chunk c at chunk c ^ swz(r). The swizzles keep
-  // every LDS read phase on distinct banks whether the LDS serves 128 or 256 bytes per clock:
-  //  * K is read as 16-byte A fragments, 16 consecutive rows at one logical chunk per phase:
-  //    the 16 rows must land in 16 distinct 16-byte bank slots (8 among rows 0..7).
-  //  * V is read with ds_read_b64_tr_b16: a 16-lane group reads 4 consecutive rows x 32 bytes,
-  //    a 32-lane half the same 4 rows x 64 bytes. XOR of the 32-byte pair index by
-  //    F = {0, 3, 5, 6}[r & 3] (D = 128) puts the 4 rows on distinct pairs mod 128 bytes and on
-  //    distinct 64-byte blocks mod 256 bytes; with 128-byte rows (D = 64) F = r & 3 does both.
-  __device__ static constexpr int kswz(int r) {
-    return D == 128 ? (r & 15) : ((r & 7) ^ ((r >> 3) & 1));
-  }
-  __device__ static constexpr int vswz(int r) {
-    return D == 128 ? 2 * ((0x6530 >> (4 * (r & 3))) & 15) : 2 * (r & 3);
-  }
-};
 
 // Explicit [B, H, N, N] masks (template parameter MK of the kernel).
 constexpr int kMaskNone = 0;   // causal and valid_len only
@@ -138,64 +98,6 @@ struct Params {
   float c;           // |scale| * log2(e)
   uint32_t qsign;    // 0x80008000 when scale < 0: Q is negated (exactly) instead
   uint32_t qmask;    // 0 when scale == 0: all scores are exactly 0 (and c is set to 1)
-};
-
-template <int DT>
-struct Mfma;
-
-template <>
-struct Mfma<ATTN_BF16> {
-  __device__ static inline f32x16 run(u32x4 a, u32x4 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-  }
-  __device__ static inline u32x4 pack(f32x8 x) {
-    return __builtin_bit_cast(u32x4, __builtin_convertvector(x, bf16x8));
-  }
-  __device__ static inline uint16_t round1(float x) {
-    return __builtin_bit_cast(uint16_t, (__bf16)x);
-  }
-};
-
-template <>
-struct Mfma<ATTN_F16> {
-  __device__ static inline f32x16 run(u32x4 a, u32x4 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-  }
-  __device__ static inline u32x4 pack(f32x8 x) {
-    return __builtin_bit_cast(u32x4, __builtin_convertvector(x, f16x8));
-  }
-  __device__ static inline uint16_t round1(float x) {
-    return __builtin_bit_cast(uint16_t, (_Float16)x);
-  }
-};
-
-// permlane32_swap(x, x) returns, in every lane, both members of the lane pair {l, l^32}.
-__device__ inline float pair_max(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ inline float pair_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ inline u32x2 lds_read_tr16(const unsigned char* p) {
-  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) i16x4*)(p));
-  return __builtin_bit_cast(u32x2, v);
-}
-
-__device__ inline void wait_loads_and_lds() {
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-}
-
-// Per-wave, per-thread state of the main loop (registers).
-template <int D>
-struct Frag {
-  uint32_t kaddr[D / 16];   // LDS byte offsets of this lane's K fragment for each k-step
-  uint32_t vaddr[D / 32];   // LDS byte offsets of this lane's V^T fragment for each d-tile u
 };
 
 template <int DT, int D>
@@ -941,4 +843,4 @@ extern "C" const char* attn_status_string(int status) {
   }
 }
 
-extern "C" int attn_version(void) { return 3; }
+extern "C" int attn_version(void) { return 4; }

@@ -11,7 +11,9 @@ Recipe (one rule for every workload):
     optional standard deviation;
   * for padded workloads, then draw ``valid_len`` as ``integers(1, N + 1, size=B)`` (uniform in
     [1, N]) and set ``valid_len[0] = 0`` so that batch 0 has fully masked rows;
-  * round each float32 value to the nearest 16-bit value (ties to even) of the workload's type.
+  * round each float32 value to the nearest 16-bit value (ties to even) of the workload's type;
+  * for the backward pass, the upstream gradient dO comes from its own generator
+    ``default_rng([21, *seed])`` (``make_grad``), also iid N(0, 1) rounded to the same type.
 The device receives the 16-bit bit patterns; the oracle receives the same values widened
 exactly to float64.
 """
@@ -148,3 +150,12 @@ def make_case(B: int, Hq: int, Hkv: int, N: int, D: int, dtype: str, causal: boo
 def make_workload(w: Workload) -> Case:
     return make_case(w.B, w.Hq, w.Hkv, w.N, w.D, w.dtype, w.causal, w.padded, [20, w.c],
                      scale=w.scale)
+
+
+def make_grad(case: Case, seed) -> np.ndarray:
+    """The upstream gradient dO for a case: uint16 bits [B, Hq, N, D], iid N(0, 1) rounded to
+    the case's type, drawn from ``default_rng([21, *seed])`` (``seed`` an int or a list)."""
+    seed = list(seed) if isinstance(seed, (list, tuple)) else [seed]
+    rng = np.random.default_rng([21] + seed)
+    x = rng.standard_normal((case.B, case.Hq, case.N, case.D), dtype=np.float32)
+    return round_bits(x, case.dtype)

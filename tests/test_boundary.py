@@ -27,7 +27,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["attn_fwd", "attn_fwd_masked", "attn_fwd_masked_validate",
+    assert declared_functions() == ["attn_bwd", "attn_bwd_validate", "attn_fwd",
+                                    "attn_fwd_masked", "attn_fwd_masked_validate",
                                     "attn_fwd_strided", "attn_fwd_strided_validate",
                                     "attn_fwd_validate", "attn_status_string", "attn_version"]
 
@@ -42,7 +43,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_version(lib):
-    assert sdp.attn_version() == 3
+    assert sdp.attn_version() == 4
 
 
 def test_status_strings(lib):
@@ -227,3 +228,42 @@ def test_masked_validate_accepts(lib):
 ])
 def test_masked_validate_rejects(lib, kw, code):
     assert mcall(**kw) == code
+
+
+# ---- attn_bwd_validate
+DO, DQ, DK, DV, DL = 15 * GB, 17 * GB, 19 * GB, 21 * GB, 23 * GB
+
+
+def bcall(**kw):
+    a = dict(q=Q, k=K, v=V, out=O, dout=DO, lse=L, dq=DQ, dk=DK, dv=DV, delta=DL, B=2, Hq=8,
+             Hkv=2, N=1000, D=128, scale=0.088, causal=1, valid_len=VL, dtype=sdp.ATTN_BF16)
+    a.update(kw)
+    return sdp.attn_bwd_validate(a["q"], a["k"], a["v"], a["out"], a["dout"], a["lse"], a["dq"],
+                                 a["dk"], a["dv"], a["delta"], a["B"], a["Hq"], a["Hkv"],
+                                 a["N"], a["D"], a["scale"], a["causal"], a["valid_len"],
+                                 a["dtype"])
+
+
+def test_bwd_validate_accepts(lib):
+    assert bcall() == sdp.ATTN_OK
+    assert bcall(valid_len=None, D=64, dtype=sdp.ATTN_F16, causal=0, Hkv=8) == sdp.ATTN_OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(lse=None), sdp.ATTN_ERR_NULL),
+    (dict(delta=None), sdp.ATTN_ERR_NULL),
+    (dict(dout=None), sdp.ATTN_ERR_NULL),
+    (dict(Hq=8, Hkv=3), sdp.ATTN_ERR_SHAPE),
+    (dict(D=32), sdp.ATTN_ERR_HEAD_DIM),
+    (dict(dtype=7), sdp.ATTN_ERR_DTYPE),
+    (dict(scale=float("nan")), sdp.ATTN_ERR_SCALE),
+    (dict(dq=DQ + 8), sdp.ATTN_ERR_LAYOUT),
+    (dict(delta=DL + 2), sdp.ATTN_ERR_LAYOUT),
+    (dict(dq=Q + 1024), sdp.ATTN_ERR_ALIAS),            # dq overlaps q
+    (dict(dk=DQ + 4096), sdp.ATTN_ERR_ALIAS),           # dk overlaps dq
+    (dict(dv=DO), sdp.ATTN_ERR_ALIAS),                  # dv overlaps dout
+    (dict(delta=L + 64), sdp.ATTN_ERR_ALIAS),           # workspace overlaps lse
+    (dict(delta=VL - 64), sdp.ATTN_ERR_ALIAS),          # workspace overlaps valid_len
+])
+def test_bwd_validate_rejects(lib, kw, code):
+    assert bcall(**kw) == code

@@ -1,0 +1,222 @@
+"""Parity of the backward pass (attn_bwd through the C ABI) with the fp64 oracle's gradients.
+
+The device forward produces O and LSE; attn_bwd consumes them with the upstream gradient dO.
+The oracle recomputes everything from Q, K, V, dO in fp64. Each gradient tensor G is compared
+as max |G - G_ref| / max(max |G_ref|, GRAD_FLOOR) (relative to the tensor's largest gradient),
+within BWD_TOL;
+gradients that must vanish (rows with no visible key in dQ, keys no query sees in dK and dV)
+must be exactly 0, and Delta (the row sums of dO * O) within DELTA_TOL of the oracle's.
+"""
+import numpy as np
+import pytest
+
+from gpu_util import from_device, log, to_device
+import oracle
+import scaled_dot_product_fwd_amd as sdp
+from scaled_dot_product_fwd_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+BWD_TOL = {"bf16": 2e-2, "f16": 5e-3}
+# Normaliser floor: where every gradient of a tensor cancels to ~0 in exact arithmetic (one key
+# per row, so dS = P (dP - D) = 0), the device's rounding leaves values near 1e-7 that are
+# compared against this floor instead of against 0.
+GRAD_FLOOR = 1e-3
+DELTA_TOL = {"bf16": 2e-2, "f16": 5e-3}
+
+
+def run_bwd(case, dout_bits, dout_scale=1.0):
+    import torch
+    q = to_device(case.q_bits, case.dtype)
+    k = to_device(case.k_bits, case.dtype)
+    v = to_device(case.v_bits, case.dtype)
+    do = to_device(dout_bits, case.dtype)
+    vl = None
+    if case.valid_len is not None:
+        vl = torch.from_numpy(case.valid_len.astype(np.int32)).cuda()
+    out, lse = sdp.forward(q, k, v, causal=case.causal, valid_len=vl, scale=case.scale)
+    delta = torch.empty(lse.shape, dtype=torch.float32, device=q.device)
+    dq, dk, dv = sdp.backward(q, k, v, out, do, lse, causal=case.causal, valid_len=vl,
+                              scale=case.scale, delta=delta)
+    torch.cuda.synchronize()
+    return (from_device(dq, case.dtype), from_device(dk, case.dtype),
+            from_device(dv, case.dtype), delta.cpu().numpy().astype(np.float64),
+            from_device(out, case.dtype), lse.cpu().numpy().astype(np.float64))
+
+
+def visibility(case):
+    """(rows with a visible key [B,N], keys some query sees [B,N]) from causal / valid_len."""
+    N = case.N
+    valid = np.full(case.B, N, np.int64)
+    if case.valid_len is not None:
+        valid = np.clip(case.valid_len.astype(np.int64), 0, N)
+    idx = np.arange(N)
+    # padding hides keys j >= valid only; key 0 is visible to every row (also under the causal
+    # mask) once valid >= 1, and key j < valid is seen at least by query j
+    row_has = np.broadcast_to((valid >= 1)[:, None], (case.B, N))
+    key_seen = idx[None, :] < valid[:, None]
+    return row_has, key_seen
+
+
+def check_grad(name, got, ref, dtype, tag, zero=None):
+    assert np.isfinite(got).all(), "%s %s: non-finite values" % (tag, name)
+    if zero is not None and zero.any():
+        assert np.all(got[zero] == 0.0), "%s %s: gradients that must vanish are not 0" % (
+            tag, name)
+    scale = max(np.abs(ref).max(), GRAD_FLOOR)
+    err = np.abs(got - ref).max() if got.size else 0.0
+    rel = err / scale
+    assert rel <= BWD_TOL[dtype], "%s %s: max err %.3g = %.3g of max |ref| %.3g" % (
+        tag, name, err, rel, scale)
+    return rel
+
+
+def compare_case(case, dout_bits, tag):
+    dq, dk, dv, delta, O, L = run_bwd(case, dout_bits)
+    q, k, v = case.widened()
+    do = inputs.widen(dout_bits, case.dtype)
+    rq, rk, rv = oracle.attn_bwd(q, k, v, do, case.scale, case.causal, case.valid_len)
+    O_ref, _ = oracle.attn_fwd(q, k, v, case.scale, case.causal, case.valid_len)
+    row_has, key_seen = visibility(case)
+    zq = np.broadcast_to(~row_has[:, None, :, None], dq.shape)
+    zk = np.broadcast_to(~key_seen[:, None, :, None], dk.shape)
+    e = [check_grad("dQ", dq, rq, case.dtype, tag, zq),
+         check_grad("dK", dk, rk, case.dtype, tag, zk),
+         check_grad("dV", dv, rv, case.dtype, tag, zk)]
+    d_ref = (do * O_ref).sum(-1)
+    derr = np.abs(delta - d_ref).max()
+    dscale = max(np.abs(d_ref).max(), 1.0)
+    assert derr / dscale <= DELTA_TOL[case.dtype], "%s Delta err %.3g" % (tag, derr)
+    log("%s: rel err dQ %.2e dK %.2e dV %.2e Delta %.2e" % (tag, e[0], e[1], e[2],
+                                                             derr / dscale))
+    return e
+
+
+# (dtype, D, causal, padded, B, Hq, Hkv, N): ragged N, N below one tile, exact tiles, GQA, MQA.
+BWD_SMALL = [
+    ("f16", 64, False, False, 1, 2, 2, 128),
+    ("f16", 64, True, False, 2, 4, 4, 200),
+    ("bf16", 64, True, True, 3, 4, 2, 257),
+    ("bf16", 64, False, True, 2, 2, 1, 77),
+    ("f16", 64, True, True, 2, 6, 3, 1),
+    ("f16", 64, False, False, 1, 1, 1, 2),
+    ("bf16", 128, False, False, 1, 4, 4, 384),
+    ("bf16", 128, True, False, 2, 8, 2, 333),
+    ("f16", 128, True, True, 3, 4, 1, 300),
+    ("bf16", 128, False, True, 2, 4, 2, 129),
+    ("f16", 128, True, False, 1, 2, 2, 63),
+    ("bf16", 128, True, True, 2, 2, 2, 640),
+    ("bf16", 64, True, False, 1, 8, 1, 520),
+    ("bf16", 128, False, False, 1, 2, 1, 1),
+]
+
+
+@pytest.mark.parametrize("cfg", BWD_SMALL, ids=lambda c: "%s-D%d-c%d-p%d-B%d-H%d-%d-N%d" % c)
+def test_bwd_small_full(cfg):
+    dtype, D, causal, padded, B, Hq, Hkv, N = cfg
+    case = inputs.make_case(B, Hq, Hkv, N, D, dtype, causal, padded, seed=[201, D, N, B])
+    dout = inputs.make_grad(case, [201, D, N, B])
+    log("bwd case %s valid_len %s" % (cfg, case.valid_len))
+    compare_case(case, dout, str(cfg))
+
+
+# More query tiles and key tiles than the device holds workgroups at once, every element
+# compared: the XCD-grouped order (B * Hkv % 8 == 0) and the plain one, an empty batch.
+BWD_MANY = [
+    ("bf16", 128, True, True, 4, 16, 4, 1100),
+    ("f16", 64, False, True, 3, 24, 3, 1050),
+    ("bf16", 64, True, False, 2, 40, 8, 1000),
+]
+
+
+@pytest.mark.parametrize("cfg", BWD_MANY, ids=lambda c: "%s-D%d-c%d-p%d-B%d-H%d-%d-N%d" % c)
+def test_bwd_many_tiles(cfg):
+    dtype, D, causal, padded, B, Hq, Hkv, N = cfg
+    case = inputs.make_case(B, Hq, Hkv, N, D, dtype, causal, padded, seed=[203, D, N, B])
+    dout = inputs.make_grad(case, [203, D, N, B])
+    log("bwd case %s valid_len %s" % (cfg, case.valid_len))
+    compare_case(case, dout, str(cfg))
+
+
+def test_bwd_padding_edge_values():
+    """valid_len 0, negative, 1, exactly N and beyond N; causal and not."""
+    for causal in (False, True):
+        case = inputs.make_case(5, 4, 2, 200, 64, "f16", causal, True, seed=[205, causal],
+                                valid_len=np.array([0, -7, 1, 200, 4000], np.int32))
+        dout = inputs.make_grad(case, [205, causal])
+        log("bwd padding edges causal=%d" % causal)
+        compare_case(case, dout, "bwd padding-edges causal=%d" % causal)
+
+
+@pytest.mark.parametrize("scale", [-0.125, 0.0, 0.5, 2.0])
+def test_bwd_scale_values(scale):
+    case = inputs.make_case(1, 4, 2, 257, 64, "bf16", True, True, seed=[207, 1],
+                            scale=scale, valid_len=np.array([250], np.int32))
+    dout = inputs.make_grad(case, [207, 1])
+    log("bwd scale %g" % scale)
+    compare_case(case, dout, "bwd scale=%g" % scale)
+
+
+def test_bwd_rising_row_maximum():
+    """Keys scaled up along the sequence: rows whose maximum moves from tile to tile, so P
+    rebuilt from the forward's LSE must still match."""
+    case = inputs.make_case(1, 2, 2, 1024, 128, "f16", False, False, seed=209)
+    k = inputs.widen(case.k_bits, "f16")
+    k *= (1.0 + 12.0 * np.arange(case.N) / case.N)[None, None, :, None]
+    case.k_bits = inputs.round_bits(k.astype(np.float32), "f16")
+    dout = inputs.make_grad(case, 209)
+    for causal in (False, True):
+        case.causal = causal
+        log("bwd rising maximum causal=%d" % causal)
+        compare_case(case, dout, "bwd rising causal=%d" % causal)
+
+
+@pytest.mark.parametrize("name", ["long_gqa", "causal_padded"])
+def test_bwd_workload_slices(name):
+    """Full-size workload in the benchmark's launch configuration; the oracle recomputes the
+    gradients of eight (batch, KV head) groups, each with all its query heads."""
+    w = inputs.WORKLOADS[name]
+    case = inputs.make_workload(w)
+    dout = inputs.make_grad(case, [w.c])
+    log("bwd workload %s" % name)
+    dq, dk, dv, delta, O, L = run_bwd(case, dout)
+    for t in (dq, dk, dv, delta):
+        assert np.isfinite(t).all()
+    g = case.Hq // case.Hkv
+    picks = sorted({(0, 0), (case.B - 1, case.Hkv - 1)} |
+                   {(b % case.B, (3 * b + 1) % case.Hkv) for b in range(6)})[:8]
+    qs = np.stack([case.q_bits[b, h * g:(h + 1) * g] for b, h in picks])
+    ks = np.stack([case.k_bits[b, h:h + 1] for b, h in picks])
+    vs = np.stack([case.v_bits[b, h:h + 1] for b, h in picks])
+    ds = np.stack([dout[b, h * g:(h + 1) * g] for b, h in picks])
+    vl = None if case.valid_len is None else np.array([case.valid_len[b] for b, _ in picks],
+                                                      np.int32)
+    wd = lambda x: inputs.widen(x, case.dtype)
+    rq, rk, rv = oracle.attn_bwd(wd(qs), wd(ks), wd(vs), wd(ds), case.scale, case.causal, vl)
+    for s, (b, h) in enumerate(picks):
+        tag = "%s slice b=%d kv=%d" % (name, b, h)
+        e = [check_grad("dQ", dq[b, h * g:(h + 1) * g], rq[s], case.dtype, tag),
+             check_grad("dK", dk[b, h], rk[s, 0], case.dtype, tag),
+             check_grad("dV", dv[b, h], rv[s, 0], case.dtype, tag)]
+        log("%s: rel err dQ %.2e dK %.2e dV %.2e" % (tag, *e))
+
+
+def test_autograd_function_matches_entry_point():
+    """attention() (torch.autograd glue) returns exactly attn_bwd's gradients."""
+    import torch
+    case = inputs.make_case(2, 4, 2, 300, 128, "bf16", True, True, seed=211)
+    dout = to_device(inputs.make_grad(case, 211), "bf16")
+    q = to_device(case.q_bits, "bf16").requires_grad_()
+    k = to_device(case.k_bits, "bf16").requires_grad_()
+    v = to_device(case.v_bits, "bf16").requires_grad_()
+    vl = torch.from_numpy(case.valid_len).cuda()
+    out = sdp.attention(q, k, v, causal=True, valid_len=vl, scale=case.scale)
+    out.backward(dout)
+    o2, lse = sdp.forward(q.detach(), k.detach(), v.detach(), causal=True, valid_len=vl,
+                          scale=case.scale)
+    g = sdp.backward(q.detach(), k.detach(), v.detach(), o2, dout, lse, causal=True,
+                     valid_len=vl, scale=case.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out, o2)
+    for a, b in zip((q.grad, k.grad, v.grad), g):
+        assert torch.equal(a, b)
