@@ -6,7 +6,13 @@ inputs resident in HBM before timing starts. Prints ONE JSON line on stdout; pro
 stderr.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long_gqa] [--no-cpu-baseline]
-                  [--layout bhnd|bnhd]
+                  [--layout bhnd|bnhd] [--mask none|keep|add] [--backward]
+
+--backward times attn_bwd instead (one step = the dQ kernel and the dK/dV kernel over the whole
+workload, given O and LSE from one forward run before timing and a seeded dO), against the
+nominal backward flop count 2.5x the forward's (five N x N x D products: dV, dP, dQ, dK and the
+recomputed S); the kernels also recompute S and dP a second time, so the MFMA work they issue is
+7/5 of that count.
 
 --layout bnhd stores Q, K, V and O as [B, N, H, D] and runs the strided entry point on them.
 --mask keep adds an explicit [N, N] uint8 sliding-window mask (key j visible to query i when
@@ -36,6 +42,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOP/s, bf16 causal N=4096 D=128; % of MFMA dense peak"
+METRIC_BWD = "attention bwd TFLOP/s (nominal 2.5x forward flops), bf16 causal N=4096 D=128"
 PEAK_TFLOPS_16BIT_DENSE = 2500.0   # MI355X published dense bf16/fp16 MFMA peak
 KERNEL_SRC = os.path.join(ROOT, "scaled_dot_product_fwd_amd", "csrc", "attn_fwd.hip")
 PROFILES = os.path.join(ROOT, "profiles")
@@ -49,6 +56,10 @@ def log(msg):
 def flops(w) -> float:
     f = 4.0 * w.B * w.Hq * w.N * w.N * w.D
     return f / 2 if w.causal else f
+
+
+def flops_bwd(w) -> float:
+    return 2.5 * flops(w)
 
 
 def kernel_sha() -> str:
@@ -95,6 +106,42 @@ def cpu_baseline(w, case, target_s: float):
                       "flops scaled by the slice share" % (nheads, heads_total, w.N, dt)}
 
 
+def cpu_baseline_bwd(w, case, dout_bits, target_s: float):
+    """Time the oracle's backward on whole (batch, KV head) groups (every query head of the
+    group, all rows), sized to about target_s seconds; rate scaled by the groups' flop share."""
+    import oracle
+    from scaled_dot_product_fwd_amd import inputs
+    threads = oracle.max_threads()
+    g = w.Hq // w.Hkv
+    groups_total = w.B * w.Hkv
+    order = np.random.default_rng(0).permutation(groups_total)
+
+    def run(sel):
+        picks = [(int(x) // w.Hkv, int(x) % w.Hkv) for x in sel]
+        wd = lambda a: inputs.widen(a, w.dtype)
+        qs = wd(np.stack([case.q_bits[b, h * g:(h + 1) * g] for b, h in picks]))
+        ks = wd(np.stack([case.k_bits[b, h:h + 1] for b, h in picks]))
+        vs = wd(np.stack([case.v_bits[b, h:h + 1] for b, h in picks]))
+        ds = wd(np.stack([dout_bits[b, h * g:(h + 1) * g] for b, h in picks]))
+        vl = None if case.valid_len is None else case.valid_len[[b for b, _ in picks]]
+        t0 = time.perf_counter()
+        oracle.attn_bwd(qs, ks, vs, ds, case.scale, case.causal, vl, threads=threads)
+        return time.perf_counter() - t0
+
+    # groups run one per thread: time one round of `threads` groups, then size the sample
+    n = min(groups_total, threads)
+    t1 = run(order[:n])
+    rounds = int(max(1, min(groups_total // n, round(target_s / max(t1, 1e-3)))))
+    n = min(groups_total, rounds * n)
+    dt = run(order[:n])
+    sample_flops = flops_bwd(w) * n / groups_total
+    return {"value": sample_flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "backward of %d of %d (batch, KV head) groups (%d query heads, all %d rows "
+                      "each), %.1f s; flops scaled by the group share" % (
+                          n, groups_total, g, w.N, dt)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -109,6 +156,8 @@ def main():
                     help="memory layout of Q, K, V and O")
     ap.add_argument("--mask", choices=("none", "keep", "add"), default="none",
                     help="explicit mask to add (see the module docstring)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time attn_bwd (dQ, dK, dV) instead of the forward")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (the "
                          "reference kernel for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE) and exit")
@@ -160,6 +209,19 @@ def main():
         sdp.forward(q, k, v, causal=w.causal, valid_len=vl, scale=w.scale, out=out, lse=lse,
                     stream=stream, layout=args.layout, attn_mask=amask)
 
+    if args.backward:
+        if args.layout != "bhnd" or amask is not None:
+            raise SystemExit("--backward runs on the contiguous layout without explicit masks")
+        dout_bits = inputs.make_grad(case, [w.c])
+        dout = dev(dout_bits)
+        step()
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty((2,) + tuple(lse.shape), dtype=torch.float32, device="cuda")
+
+        def step():  # noqa: F811 -- the timed step is the backward
+            sdp.backward(q, k, v, out, dout, lse, causal=w.causal, valid_len=vl, scale=w.scale,
+                         dq=dq, dk=dk, dv=dv, ws=ws, stream=stream)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -180,26 +242,35 @@ def main():
         args.steps, ms_per_step, wall * 1e3 / args.steps))
     if torch.isnan(out).any().item():
         raise SystemExit("NaN in the output")
+    if args.backward and any(torch.isnan(t).any().item() for t in (dq, dk, dv)):
+        raise SystemExit("NaN in the gradients")
 
-    f = flops(w)
+    f = flops_bwd(w) if args.backward else flops(w)
     tflops = f / (ms_per_step * 1e-3) / 1e12
+    traffic = None
+    if not args.backward and args.layout == "bhnd" and amask is None:
+        traffic = traffic_for(w.name)
     roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_TFLOPS_16BIT_DENSE,
             "unit": "TFLOP/s", "frac": round(tflops / PEAK_TFLOPS_16BIT_DENSE, 4),
-            "traffic": traffic_for(w.name) if args.layout == "bhnd" and amask is None else None}
+            "traffic": traffic}
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the oracle on the host (about %.0f s)" % args.cpu_seconds)
-        cpu = cpu_baseline(w, case, args.cpu_seconds)
+        if args.backward:
+            cpu = cpu_baseline_bwd(w, case, dout_bits, args.cpu_seconds)
+        else:
+            cpu = cpu_baseline(w, case, args.cpu_seconds)
         cpu["value"] = float("%.6g" % cpu["value"])
         log("cpu baseline: %s" % json.dumps(cpu))
     line = {
-        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "metric": METRIC_BWD if args.backward else METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded iid N(0,1), rounded to %s)" % w.dtype,
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "D": w.D,
                    "causal": w.causal, "padded": w.padded, "scale": w.scale,
                    "layout": args.layout, "explicit_mask": args.mask,
+                   "pass": "backward" if args.backward else "forward",
                    "flops_per_step": f},
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -223,8 +223,9 @@ int attn_fwd_masked_validate(const void *q, const int64_t *q_strides, const void
  *   dq           device output [B,Hq,N,D] of dtype; dk, dv: device outputs [B,Hkv,N,D] of dtype.
  *                All written completely (rows with no visible key get dQ = 0; keys no query sees
  *                get dK = dV = 0).
- *   delta        device float32 [B,Hq,N] workspace owned by the caller; on return it holds
- *                Delta (the library allocates nothing).
+ *   ws           device float32 workspace of 2 * B * Hq * N values owned by the caller (the
+ *                library allocates nothing); on return ws[0 .. B*Hq*N) holds Delta [B,Hq,N] and
+ *                the rest the LSE in base 2 (LSE * log2 e, 0 for rows with no visible key).
  *   others       as in attn_fwd.
  *
  * Two kernels run on `stream` in order (dQ and Delta, then dK and dV). Outputs must not overlap
@@ -232,14 +233,14 @@ int attn_fwd_masked_validate(const void *q, const int64_t *q_strides, const void
  * ATTN_ERR_LAYOUT. Otherwise returns as attn_fwd.
  */
 int attn_bwd(const void *q, const void *k, const void *v, const void *out, const void *dout,
-             const float *lse, void *dq, void *dk, void *dv, float *delta, int B, int Hq,
+             const float *lse, void *dq, void *dk, void *dv, float *ws, int B, int Hq,
              int Hkv, int N, int D, float scale, int causal, const int32_t *valid_len,
              int dtype, void *stream);
 
 /* attn_bwd_validate -- the host-only argument check of attn_bwd. */
 int attn_bwd_validate(const void *q, const void *k, const void *v, const void *out,
                       const void *dout, const float *lse, const void *dq, const void *dk,
-                      const void *dv, const float *delta, int B, int Hq, int Hkv, int N, int D,
+                      const void *dv, const float *ws, int B, int Hq, int Hkv, int N, int D,
                       float scale, int causal, const int32_t *valid_len, int dtype);
 
 /* attn_status_string -- a static, NUL-terminated description of a return code (never NULL). */

@@ -179,18 +179,18 @@ def attn_fwd_masked_validate(q: int, q_strides, k: int, k_strides, v: int, v_str
 
 
 def attn_bwd(q: int, k: int, v: int, out: int, dout: int, lse: int, dq: int, dk: int, dv: int,
-             delta: int, B: int, Hq: int, Hkv: int, N: int, D: int, scale: float, causal: int,
+             ws: int, B: int, Hq: int, Hkv: int, N: int, D: int, scale: float, causal: int,
              valid_len: Optional[int], dtype: int, stream: Optional[int]) -> int:
     """C ``attn_bwd``; pointers are device addresses as integers."""
-    return load_library().attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, N, D,
+    return load_library().attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, ws, B, Hq, Hkv, N, D,
                                    scale, int(causal), valid_len, dtype, stream)
 
 
 def attn_bwd_validate(q: int, k: int, v: int, out: int, dout: int, lse: int, dq: int, dk: int,
-                      dv: int, delta: int, B: int, Hq: int, Hkv: int, N: int, D: int,
+                      dv: int, ws: int, B: int, Hq: int, Hkv: int, N: int, D: int,
                       scale: float, causal: int, valid_len: Optional[int], dtype: int) -> int:
     """C ``attn_bwd_validate``: host-only argument check, no HIP call."""
-    return load_library().attn_bwd_validate(q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq,
+    return load_library().attn_bwd_validate(q, k, v, out, dout, lse, dq, dk, dv, ws, B, Hq,
                                             Hkv, N, D, scale, int(causal), valid_len, dtype)
 
 
@@ -317,12 +317,13 @@ def forward(q, k, v, causal: bool, valid_len=None, scale: Optional[float] = None
 
 
 def backward(q, k, v, out, dout, lse, causal: bool, valid_len=None,
-             scale: Optional[float] = None, dq=None, dk=None, dv=None, delta=None, stream=None):
+             scale: Optional[float] = None, dq=None, dk=None, dv=None, ws=None, stream=None):
     """Run attn_bwd on contiguous [B, H, N, D] torch device tensors; returns (dq, dk, dv).
 
     ``out`` and ``lse`` are the forward's outputs for the same inputs; ``dout`` is the gradient
     of the loss with respect to ``out``. Output tensors and the float32 [B, Hq, N] workspace
-    ``delta`` are allocated with torch when not given.
+    ``ws`` ([2, B, Hq, N]: Delta, then the LSE in base 2) are allocated with torch when not
+    given.
     """
     import torch
     B, Hq, N, D = q.shape
@@ -341,8 +342,10 @@ def backward(q, k, v, out, dout, lse, causal: bool, valid_len=None,
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    if delta is None:
-        delta = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = torch.empty((2, B, Hq, N), dtype=torch.float32, device=q.device)
+    elif ws.dtype != torch.float32 or ws.numel() < 2 * B * Hq * N or not ws.is_contiguous():
+        raise ValueError("ws must be a contiguous float32 tensor of 2 * B * Hq * N values")
     vl_ptr = None
     if valid_len is not None:
         if valid_len.dtype != torch.int32 or tuple(valid_len.shape) != (B,) or not valid_len.is_cuda:
@@ -351,7 +354,7 @@ def backward(q, k, v, out, dout, lse, causal: bool, valid_len=None,
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     st = attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
-                  lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                  lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(),
                   B, Hq, Hkv, N, D, float(scale), int(bool(causal)), vl_ptr, _dtype_code(q),
                   stream.cuda_stream)
     if st != ATTN_OK:

@@ -14,13 +14,14 @@
 //
 //   * bwd_dq: one workgroup per (batch, query head, 128-query tile), 4 waves x 32 queries, the
 //     forward's decomposition. Each wave holds its Q and dO fragments in registers, computes
-//     D = rowsum(dO o O) (stored to the caller's workspace for the second kernel), then streams
+//     D = rowsum(dO o O) and stores it with L * log2(e) in the caller's workspace for the
+//     second kernel, then streams
 //     64-key K/V tiles through LDS: S^T = K Q^T and dP^T = V dO^T on MFMA (lane = query, as in
 //     the forward), P and dS on the VALU, and dQ^T += K^T dS^T with K^T read through
 //     ds_read_b64_tr_b16. dQ is written once (no atomics).
 //   * bwd_dkdv: one workgroup per (batch, KV head, 128-key tile), 4 waves x 32 keys. Each wave
 //     keeps its keys' K fragments in registers and their V rows in LDS, and streams 32-query
-//     tiles of Q, dO, L and D of every query head of the group (only queries at or after the
+//     tiles of Q, dO, L * log2(e) and D of every query head of the group (only queries at or after the
 //     tile's first key under causal masking): S = Q K^T and dP = dO V^T (lane = key), P and dS
 //     on the VALU, dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read through
 //     ds_read_b64_tr_b16. dK and dV are written once.
@@ -55,7 +56,8 @@ struct BwdParams {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
-  float* delta;
+  float* delta;    // workspace row 0: D = rowsum(dO o O)
+  float* lse2;     // workspace row 1: L * log2(e) (0 for rows with no visible key)
   const int32_t* valid_len;
   int B, Hq, Hkv, N;
   int group;       // Hq / Hkv
@@ -114,20 +116,23 @@ __device__ inline void store_rows(const f32x16 (&acc)[Geo<D>::OT], float mul,
 }
 
 // Lane offsets of ds_read_b64_tr_b16 reads of a transposed 32 x 16 operand from a row-major tile
-// stored with Geo<D>::vswz: lane 16g + jj reads row 4(g/2) + jj/4 (+16 per k-step, +8 for the
+// stored with Geo<D>::bswz: lane 16g + jj reads row 4(g/2) + jj/4 (+16 per k-step, +8 for the
 // second 4 rows), columns 32u + 16(g%2) + 4(jj%4) .. +3 (the forward's V^T read).
 template <int D>
 __device__ inline uint32_t tr_offset(int lane, int u) {
   using G = Geo<D>;
   const int g = lane >> 4, jj = lane & 15;
   const int row = 4 * (g >> 1) + (jj >> 2);
-  return row * G::ROW + 16 * ((4 * u + 2 * (g & 1) + ((jj & 3) >> 1)) ^ G::vswz(row)) +
+  return row * G::ROW + 16 * ((4 * u + 2 * (g & 1) + ((jj & 3) >> 1)) ^ G::bswz(row)) +
          8 * (jj & 1);
 }
 
-__device__ inline u32x4 tr_frag(const unsigned char* base, int rows8) {
-  const u32x2 lo = lds_read_tr16(base);
-  const u32x2 hi = lds_read_tr16(base + rows8);
+// The 8 values of a k-step: rows from `off` (a tr_offset plus whole 16-row steps) and the same
+// columns 8 rows further down. bswz(r + 8) = bswz(r) ^ 2, so the second read's chunk is the
+// first's with bit 1 flipped: byte offset ^ 32.
+__device__ inline u32x4 tr_frag(const unsigned char* tile, uint32_t off, int rows8) {
+  const u32x2 lo = lds_read_tr16(tile + off);
+  const u32x2 hi = lds_read_tr16(tile + ((off ^ 32u) + rows8));
   return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
@@ -140,7 +145,7 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p) {
   using M = Mfma<DT>;
   constexpr int KSTEPS = G::KSTEPS;
   constexpr int OT = G::OT;
-  // K0 K1 V0 V1, 64-key tiles. K is stored with vswz (read both as rows and transposed), V
+  // K0 K1 V0 V1, 64-key tiles. K is stored with bswz (read both as rows and transposed), V
   // with kswz (read as rows).
   __shared__ __attribute__((aligned(1024))) unsigned char smem[G::LDS];
 
@@ -150,19 +155,23 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p) {
   const int h = lane >> 5;
   const int ql = lane & 31;
 
+  // Work: (batch, query head, 128-query tile). Each XCD owns whole KV heads; within one it takes
+  // the tiles in order of decreasing work (the last query tile first under causal masking), for
+  // all its heads at once.
   int qt, b, hq;
   {
     const int wid = blockIdx.x;
     if (p.xcd_order) {
       const int xcd = wid & 7, local = wid >> 3;
-      const int per_head = p.group * p.nqt;
-      const int head_local = local / per_head;
-      const int r = local - head_local * per_head;
+      const int hpx = (p.B * p.Hkv) >> 3;   // KV heads per XCD
+      const int per_qi = hpx * p.group;
+      const int qi = local / per_qi;
+      const int r = local - qi * per_qi;
+      const int head_local = r / p.group;
       const int kv_head = head_local * 8 + xcd;
-      const int qi = r / p.group;
       qt = CAUSAL ? p.nqt - 1 - qi : qi;
       b = kv_head / p.Hkv;
-      hq = (kv_head - b * p.Hkv) * p.group + (r - qi * p.group);
+      hq = (kv_head - b * p.Hkv) * p.group + (r - head_local * p.group);
     } else {
       const int BH = p.B * p.Hq;
       const int qi = wid / BH, bh = wid - qi * BH;
@@ -189,23 +198,20 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p) {
       __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + kv_off), (short)0, head_bytes, kBufferFlags);
   const __amdgpu_buffer_rsrc_t vrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + kv_off), (short)0, head_bytes, kBufferFlags);
-  uint32_t kdma, vdma[G::LOADS];
-  {
-    const int row = wave * G::LOADS * G::RPB + lane / G::CH;
-    kdma = row * G::ROW + (((lane % G::CH) ^ G::vswz(row)) * 16);
+  uint32_t kdma[G::LOADS], vdma[G::LOADS];
 #pragma unroll
-    for (int i = 0; i < G::LOADS; ++i) {
-      const int r = (wave * G::LOADS + i) * G::RPB + lane / G::CH;
-      vdma[i] = r * G::ROW + (((lane % G::CH) ^ G::kswz(r)) * 16);
-    }
+  for (int i = 0; i < G::LOADS; ++i) {
+    const int r = (wave * G::LOADS + i) * G::RPB + lane / G::CH;
+    kdma[i] = r * G::ROW + (((lane % G::CH) ^ G::bswz(r)) * 16);
+    vdma[i] = r * G::ROW + (((lane % G::CH) ^ G::kswz(r)) * 16);
   }
   auto dma = [&](int tile, int kdst, int vdst) {
     const int soff = tile * G::TILE;
 #pragma unroll
     for (int i = 0; i < G::LOADS; ++i) {
       const int blk = (wave * G::LOADS + i) * 1024;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(smem + kdst + blk), 16, kdma,
-                                               soff + i * 1024, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(smem + kdst + blk), 16, kdma[i],
+                                               soff, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(smem + vdst + blk), 16, vdma[i],
                                                soff, 0, 0);
     }
@@ -215,7 +221,7 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p) {
   uint32_t kaddr[KSTEPS], vaddr[KSTEPS], taddr[OT];
 #pragma unroll
   for (int ks = 0; ks < KSTEPS; ++ks) {
-    kaddr[ks] = ql * G::ROW + 16 * ((2 * ks + h) ^ G::vswz(ql));
+    kaddr[ks] = ql * G::ROW + 16 * ((2 * ks + h) ^ G::bswz(ql));
     vaddr[ks] = ql * G::ROW + 16 * ((2 * ks + h) ^ G::kswz(ql));
   }
 #pragma unroll
@@ -252,7 +258,10 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p) {
       }
     }
   const float delta = pair_sum(dsum);
-  if (h == 0 && qrow < p.N) p.delta[(size_t)bh * p.N + qrow] = delta;
+  if (h == 0 && qrow < p.N) {
+    p.delta[(size_t)bh * p.N + qrow] = delta;
+    p.lse2[(size_t)bh * p.N + qrow] = L;
+  }
 #pragma unroll
   for (int s = 0; s < KSTEPS; ++s) qf[s] = (qf[s] ^ p.qsign) & p.qmask;
 
@@ -261,14 +270,13 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p) {
   for (int u = 0; u < OT; ++u) acc[u] = f32x16{};
   const float c = p.c;
 
-  for (int j = 0; j < ntiles; ++j) {
-    const int P = j & 1;
-    const int kcur = P ? G::K1 : G::K0, vcur = P ? G::V1 : G::V0;
+  auto step = [&](auto bufc, int j) {
+    constexpr int P = decltype(bufc)::value;
     wait_loads_and_lds();
     __syncthreads();
     if (j + 1 < ntiles) dma(j + 1, P ? G::K0 : G::K1, P ? G::V0 : G::V1);
-    const unsigned char* kb = smem + kcur;
-    const unsigned char* vb = smem + vcur;
+    const unsigned char* kb = smem + (P ? G::K1 : G::K0);
+    const unsigned char* vb = smem + (P ? G::V1 : G::V0);
     // S^T and dP^T for the tile's two 32-key halves
     f32x16 sc[2], dp[2];
 #pragma unroll
@@ -281,31 +289,41 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p) {
         dp[t] = M::run(*(const u32x4*)(vb + vaddr[ks] + t * 32 * G::ROW), dof[ks], dp[t]);
       }
     }
-    // masks: key = kb0 + 32t + 8(r/4) + 4h + r%4
+    // P and dS; keys kb0 + 32t + 8(r/4) + 4h + r%4 are tested only in tiles that reach past
+    // this wave's causal diagonal or the padding boundary (a hidden element's P may be inf:
+    // the select removes it).
     const int kb0 = j * kBN;
     const bool full = (!CAUSAL || kb0 + kBN - 1 <= qa) && kb0 + kBN <= kv_end;
-    int lim = 1 << 30;
-    if (!full) {
-      lim = kv_end - 1 - kb0 - 4 * h;
-      if (CAUSAL) lim = min(lim, qrow - kb0 - 4 * h);
-    }
     float ds[2][16];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][r], c, -L));
-        const float v = pr * (dp[t][r] - delta);
-        ds[t][r] = (32 * t + 8 * (r >> 2) + (r & 3) <= lim) ? v : 0.f;
+        ds[t][r] = pr * (dp[t][r] - delta);
       }
+    if (!full) {
+      int lim = kv_end - 1 - kb0 - 4 * h;
+      if (CAUSAL) lim = min(lim, qrow - kb0 - 4 * h);
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          ds[t][r] = (32 * t + 8 * (r >> 2) + (r & 3) <= lim) ? ds[t][r] : 0.f;
+    }
     // dQ^T += K^T dS^T, four 16-key k-steps
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const u32x4 bsd = pack8<DT>(ds[s >> 1], s & 1);
 #pragma unroll
       for (int u = 0; u < OT; ++u)
-        acc[u] = M::run(tr_frag(kb + taddr[u] + 16 * s * G::ROW, 8 * G::ROW), bsd, acc[u]);
+        acc[u] = M::run(tr_frag(kb, taddr[u] + 16 * s * G::ROW, 8 * G::ROW), bsd, acc[u]);
     }
+  };
+  // two tiles per trip, one per buffer, so that the buffer offsets are constants
+  for (int j = 0; j < ntiles; j += 2) {
+    step(std::integral_constant<int, 0>{}, j);
+    if (j + 1 < ntiles) step(std::integral_constant<int, 1>{}, j + 1);
   }
 
   // dQ = scale * (dQ^T)^T, staged through LDS after every wave is done with the tiles.
@@ -321,14 +339,16 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p) {
 template <int D>
 struct BwdGeo {
   using G = Geo<D>;
-  static constexpr int VREG = 128 * G::ROW;            // V rows of the workgroup's 128 keys
   static constexpr int QTILE = kQT * G::ROW;           // one 32-row Q or dO tile
   static constexpr int LD = 2048;                      // 1 KiB slots for L and D of one tile
   static constexpr int BUF = 2 * QTILE + LD;           // one buffer: Q, dO, L, D
-  static constexpr int QB0 = VREG;                     // buffer 0
-  static constexpr int LDS = VREG + 2 * BUF;
+  static constexpr int VREG = 2 * BUF;                 // V rows of the workgroup's 128 keys
+  static constexpr int LDS = VREG + 128 * G::ROW;
   static constexpr int QLOADS = QTILE / 1024 / kWaves; // 1 KiB DMA blocks per wave per tile
   static_assert(QLOADS >= 1, "tile geometry");
+  // buffers first, so that every Q / dO / L / D read is a fixed offset (16-bit immediate) from
+  // a per-lane base once the loop is unrolled over the two buffers
+  static_assert(BUF + QTILE + 24 * G::ROW <= 65535, "LDS offsets fit the immediate field");
 };
 
 template <int DT, int D, bool CAUSAL>
@@ -346,15 +366,17 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
   const int h = lane >> 5;
   const int ql = lane & 31;
 
-  // ---- work: (batch, KV head, 128-key tile); under causal masking the first key tiles see the
-  // most queries and run first.
+  // ---- work: (batch, KV head, 128-key tile). Each XCD owns whole KV heads; within one it
+  // takes the key tiles in order of decreasing work (under causal masking tile kt sees N - 128 kt
+  // queries), all its heads' tile 0 first: longest-first keeps the last workgroups short.
   int kt, b, kvh;
   {
     const int wid = blockIdx.x;
     if (p.xcd_order) {
       const int xcd = wid & 7, local = wid >> 3;
-      const int head_local = local / p.nkt;
-      kt = local - head_local * p.nkt;
+      const int hpx = (p.B * p.Hkv) >> 3;
+      kt = local / hpx;
+      const int head_local = local - kt * hpx;
       const int kv_head = head_local * 8 + xcd;
       b = kv_head / p.Hkv;
       kvh = kv_head - b * p.Hkv;
@@ -372,7 +394,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
   int kv_end = p.N;
   if (p.valid_len) kv_end = min(max(p.valid_len[b], 0), p.N);
   const size_t kv_off = (size_t)(b * p.Hkv + kvh) * p.N * D;
-  unsigned char* vreg = smem + wave * 32 * G::ROW;   // this wave's 32 V rows
+  unsigned char* vreg = smem + BG::VREG + wave * 32 * G::ROW;   // this wave's 32 V rows
 
   f32x16 dk[OT], dv[OT];
 #pragma unroll
@@ -390,42 +412,46 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) kf[s] = (*(const u32x4*)(ksrc + 16 * s) ^ p.qsign) & p.qmask;
     }
-    // V rows of this wave's keys into its LDS rows (vswz layout, read as rows).
+    // V rows of this wave's keys into its LDS rows (bswz layout like Q and dO, so that one set
+    // of row-fragment offsets serves all three).
     {
       const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(p.v + kv_off), (short)0, (uint32_t)p.N * G::ROW, kBufferFlags);
-      const int row = lane / G::CH;
-      const uint32_t off = row * G::ROW + (((lane % G::CH) ^ G::vswz(row)) * 16);
 #pragma unroll
-      for (int i = 0; i < 32 / G::RPB; ++i)
+      for (int i = 0; i < 32 / G::RPB; ++i) {
+        const int row = i * G::RPB + lane / G::CH;
+        const uint32_t off = (lane / G::CH) * G::ROW + (((lane % G::CH) ^ G::bswz(row)) * 16);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(vreg + i * 1024), 16, off,
                                                  (uint32_t)(kw + i * G::RPB) * G::ROW, 0, 0);
+      }
     }
-    // DMA of iteration `it` (query head kvh * group + it / ntq, queries q0 .. q0+31) into
-    // buffer `buf`: Q and dO tiles (vswz layout), L and D (wave 0 and 1).
-    const int qrow_l = lane / G::CH;   // row within a 1 KiB block
-    const uint32_t qoff = qrow_l * G::ROW + (((lane % G::CH) ^ G::vswz(qrow_l)) * 16);
-    auto dma = [&](int it, int buf) {
-      const int g = it / ntq;
-      const int q0 = qstart + (it - g * ntq) * kQT;
+    // DMA of the iteration over query head kvh * group + g, queries q0 .. q0+31, into buffer
+    // `buf`: Q and dO tiles (bswz layout), L and D (wave 0 and 1).
+    uint32_t qoff[BG::QLOADS];
+#pragma unroll
+    for (int i = 0; i < BG::QLOADS; ++i) {
+      const int row = (wave * BG::QLOADS + i) * G::RPB + lane / G::CH;   // row in the tile
+      qoff[i] = (lane / G::CH) * G::ROW + (((lane % G::CH) ^ G::bswz(row)) * 16);
+    }
+    auto dma = [&](int g, int q0, int buf) {
       const int bh = b * p.Hq + kvh * p.group + g;
       const size_t hoff = (size_t)bh * p.N * D;
       const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(p.q + hoff), (short)0, (uint32_t)p.N * G::ROW, kBufferFlags);
       const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(p.dout + hoff), (short)0, (uint32_t)p.N * G::ROW, kBufferFlags);
-      unsigned char* base = smem + BG::QB0 + buf * BG::BUF;
+      unsigned char* base = smem + buf * BG::BUF;
 #pragma unroll
       for (int i = 0; i < BG::QLOADS; ++i) {
         const int blk = wave * BG::QLOADS + i;
         const uint32_t soff = (uint32_t)(q0 + blk * G::RPB) * G::ROW;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void*)(base + blk * 1024), 16, qoff,
-                                                 soff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void*)(base + blk * 1024), 16,
+                                                 qoff[i], soff, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ors, (lds_void*)(base + BG::QTILE + blk * 1024),
-                                                 16, qoff, soff, 0, 0);
+                                                 16, qoff[i], soff, 0, 0);
       }
       if (wave < 2) {
-        const float* src = wave == 0 ? p.lse : p.delta;
+        const float* src = wave == 0 ? p.lse2 : p.delta;
         const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(src + (size_t)bh * p.N), (short)0, (uint32_t)p.N * 4, kBufferFlags);
         // one dword per query row (lanes 0..31); a 16-byte load would straddle the end of the
@@ -440,19 +466,34 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
     // Fragment offsets: rows of Q / dO / V (A of S and dP, B of dP), transposed Q / dO.
     uint32_t raddr[KSTEPS], taddr[OT];
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) raddr[ks] = ql * G::ROW + 16 * ((2 * ks + h) ^ G::vswz(ql));
+    for (int ks = 0; ks < KSTEPS; ++ks) raddr[ks] = ql * G::ROW + 16 * ((2 * ks + h) ^ G::bswz(ql));
 #pragma unroll
     for (int u = 0; u < OT; ++u) taddr[u] = tr_offset<D>(lane, u);
     const float c = p.c;
 
-    dma(0, 0);
-    for (int it = 0; it < iters; ++it) {
-      const int buf = it & 1;
+    // Iteration order: query head by query head, each from qstart up. (Sweeping the tiles in
+    // lockstep across the key-tile workgroups, every head at each tile, cut the HBM traffic by
+    // 3x but ran ~10 % slower under causal masking.)
+    // State: (g, q0) of the tile being computed and of the next one to fetch.
+    int g_cur = 0, q_cur = qstart, g_nxt = 0, q_nxt = qstart;
+    auto advance = [&](int& g, int& q0) {
+      q0 += kQT;
+      if (q0 >= p.N) { q0 = qstart; ++g; }
+    };
+    dma(g_nxt, q_nxt, 0);
+    advance(g_nxt, q_nxt);
+
+    auto step = [&](auto bufc, int it) {
+      constexpr int buf = decltype(bufc)::value;
       wait_loads_and_lds();
       __syncthreads();
-      if (it + 1 < iters) dma(it + 1, buf ^ 1);
-      const int q0 = qstart + (it % ntq) * kQT;
-      const unsigned char* qb = smem + BG::QB0 + buf * BG::BUF;
+      if (it + 1 < iters) {
+        dma(g_nxt, q_nxt, buf ^ 1);
+        advance(g_nxt, q_nxt);
+      }
+      const int q0 = q_cur;
+      advance(g_cur, q_cur);
+      const unsigned char* qb = smem + buf * BG::BUF;
       const unsigned char* ob = qb + BG::QTILE;
       const float* lb = (const float*)(qb + 2 * BG::QTILE);
       const float* db = (const float*)(qb + 2 * BG::QTILE + 1024);
@@ -463,6 +504,11 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
         s = M::run(*(const u32x4*)(qb + raddr[ks]), kf[ks], s);
         dp = M::run(*(const u32x4*)(ob + raddr[ks]), *(const u32x4*)(vreg + raddr[ks]), dp);
       }
+      // P and dS. The wave's 32 keys are all visible to the tile's 32 queries unless the tile
+      // touches the causal diagonal, the padding boundary or the end of the sequence; only then
+      // is each element tested. A hidden element may have L = -inf (a row with no visible key)
+      // and so x = inf: the select, not a product, removes it.
+      const bool full = (!CAUSAL || q0 >= kw + 31) && kw + 32 <= kv_end && q0 + kQT <= p.N;
       float pr[16], ds[16];
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
@@ -472,12 +518,18 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * r4 + e;
-          const int qi = q0 + qi0 + e;
-          const bool vis = (!CAUSAL || key <= qi) && key < kv_end && qi < p.N;
-          const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse_log2(lv[e])));
-          pr[r] = vis ? x : 0.f;
-          ds[r] = pr[r] * (dp[r] - dv4[e]);
+          pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lv[e]));
         }
+        if (!full) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int qi = q0 + qi0 + e;
+            const bool vis = (!CAUSAL || key <= qi) && key < kv_end && qi < p.N;
+            pr[4 * r4 + e] = vis ? pr[4 * r4 + e] : 0.f;
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ds[4 * r4 + e] = pr[4 * r4 + e] * (dp[4 * r4 + e] - dv4[e]);
       }
       // dV^T += dO^T P and dK^T += Q^T dS over the two 16-query k-steps
 #pragma unroll
@@ -486,17 +538,22 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
         const u32x4 bs = pack8<DT>(ds, k2);
 #pragma unroll
         for (int u = 0; u < OT; ++u) {
-          dv[u] = M::run(tr_frag(ob + taddr[u] + 16 * k2 * G::ROW, 8 * G::ROW), bp, dv[u]);
-          dk[u] = M::run(tr_frag(qb + taddr[u] + 16 * k2 * G::ROW, 8 * G::ROW), bs, dk[u]);
+          dv[u] = M::run(tr_frag(ob, taddr[u] + 16 * k2 * G::ROW, 8 * G::ROW), bp, dv[u]);
+          dk[u] = M::run(tr_frag(qb, taddr[u] + 16 * k2 * G::ROW, 8 * G::ROW), bs, dk[u]);
         }
       }
+    };
+    // two iterations per trip, one per buffer, so that the buffer offsets are constants
+    for (int it = 0; it < iters; it += 2) {
+      step(std::integral_constant<int, 0>{}, it);
+      if (it + 1 < iters) step(std::integral_constant<int, 1>{}, it + 1);
     }
     wait_loads_and_lds();
   }
   __syncthreads();
   // dK = scale * (dK^T)^T, dV = (dV^T)^T; rows past N are not written. Staging reuses the Q/dO
   // buffers (every wave is past its last read).
-  unsigned char* ost = smem + BG::QB0 + wave * 32 * G::ROW;
+  unsigned char* ost = smem + wave * 32 * G::ROW;
   store_rows<DT, D>(dk, p.scale, ost, p.dk + kv_off, kw, p.N, lane);
   store_rows<DT, D>(dv, 1.0f, ost, p.dv + kv_off, kw, p.N, lane);
 }
@@ -545,11 +602,11 @@ bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
 
 extern "C" int attn_bwd_validate(const void* q, const void* k, const void* v, const void* out,
                                  const void* dout, const float* lse, const void* dq,
-                                 const void* dk, const void* dv, const float* delta, int B,
+                                 const void* dk, const void* dv, const float* ws, int B,
                                  int Hq, int Hkv, int N, int D, float scale, int causal,
                                  const int32_t* valid_len, int dtype) {
   (void)causal;
-  if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv || !delta)
+  if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv || !ws)
     return ATTN_ERR_NULL;
   if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
   if (N > ATTN_MAX_N) return ATTN_ERR_SHAPE;
@@ -560,12 +617,12 @@ extern "C" int attn_bwd_validate(const void* q, const void* k, const void* v, co
   const void* ptrs16[] = {q, k, v, out, dout, dq, dk, dv};
   for (const void* ptr : ptrs16)
     if ((uintptr_t)ptr % 16 != 0) return ATTN_ERR_LAYOUT;
-  if ((uintptr_t)lse % 4 != 0 || (uintptr_t)delta % 4 != 0) return ATTN_ERR_LAYOUT;
+  if ((uintptr_t)lse % 4 != 0 || (uintptr_t)ws % 4 != 0) return ATTN_ERR_LAYOUT;
   const int64_t qb = (int64_t)B * Hq * N * D * 2, kb = (int64_t)B * Hkv * N * D * 2;
   const int64_t lb = (int64_t)B * Hq * N * 4;
-  // Outputs: dq, dk, dv, delta; none may overlap an input or another output.
-  const void* outs[] = {dq, dk, dv, delta};
-  const int64_t osz[] = {qb, kb, kb, lb};
+  // Outputs: dq, dk, dv and the workspace; none may overlap an input or another output.
+  const void* outs[] = {dq, dk, dv, ws};
+  const int64_t osz[] = {qb, kb, kb, 2 * lb};
   const void* ins[] = {q, k, v, out, dout, lse};
   const int64_t isz[] = {qb, kb, kb, qb, qb, lb};
   for (int i = 0; i < 4; ++i) {
@@ -580,9 +637,9 @@ extern "C" int attn_bwd_validate(const void* q, const void* k, const void* v, co
 
 extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* out,
                         const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                        float* delta, int B, int Hq, int Hkv, int N, int D, float scale,
+                        float* ws, int B, int Hq, int Hkv, int N, int D, float scale,
                         int causal, const int32_t* valid_len, int dtype, void* stream) {
-  const int st = attn_bwd_validate(q, k, v, out, dout, lse, dq, dk, dv, delta, B, Hq, Hkv, N, D,
+  const int st = attn_bwd_validate(q, k, v, out, dout, lse, dq, dk, dv, ws, B, Hq, Hkv, N, D,
                                    scale, causal, valid_len, dtype);
   if (st != ATTN_OK) return st;
   BwdParams p;
@@ -595,7 +652,8 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
   p.dq = (uint16_t*)dq;
   p.dk = (uint16_t*)dk;
   p.dv = (uint16_t*)dv;
-  p.delta = delta;
+  p.delta = ws;
+  p.lse2 = ws + (size_t)B * Hq * N;
   p.valid_len = valid_len;
   p.B = B;
   p.Hq = Hq;

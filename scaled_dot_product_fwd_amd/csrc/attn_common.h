@@ -52,6 +52,16 @@ struct Geo {
   __device__ static constexpr int vswz(int r) {
     return D == 128 ? 2 * ((0x6530 >> (4 * (r & 3))) & 15) : 2 * (r & 3);
   }
+  //  * A tile read both ways (the backward's K, Q and dO) needs both properties: vswz's pair
+  //    XOR on r & 3 for the transposed reads, plus bits that tell apart the 4-row groups of 16
+  //    rows for the row reads: the chunk's low bit flips with (r >> 2) & 1 (rows 4..7 of 8 use
+  //    the other chunk of each pair) and the pair XOR gains (r >> 3) & 1, which maps the
+  //    even-parity set {0, 3, 5, 6} (D = 128) onto the odd one, or shifts F = r & 3 (D = 64).
+  //    Rows r and r + 8 therefore differ by chunk XOR 2; rows r and r + 16 share the swizzle.
+  __device__ static constexpr int bswz(int r) {
+    return D == 128 ? 2 * (((0x6530 >> (4 * (r & 3))) & 15) ^ ((r >> 3) & 1)) + ((r >> 2) & 1)
+                    : 2 * ((r & 3) ^ ((r >> 3) & 1)) + ((r >> 2) & 1);
+  }
 };
 
 template <int DT>

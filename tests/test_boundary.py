@@ -235,11 +235,11 @@ DO, DQ, DK, DV, DL = 15 * GB, 17 * GB, 19 * GB, 21 * GB, 23 * GB
 
 
 def bcall(**kw):
-    a = dict(q=Q, k=K, v=V, out=O, dout=DO, lse=L, dq=DQ, dk=DK, dv=DV, delta=DL, B=2, Hq=8,
+    a = dict(q=Q, k=K, v=V, out=O, dout=DO, lse=L, dq=DQ, dk=DK, dv=DV, ws=DL, B=2, Hq=8,
              Hkv=2, N=1000, D=128, scale=0.088, causal=1, valid_len=VL, dtype=sdp.ATTN_BF16)
     a.update(kw)
     return sdp.attn_bwd_validate(a["q"], a["k"], a["v"], a["out"], a["dout"], a["lse"], a["dq"],
-                                 a["dk"], a["dv"], a["delta"], a["B"], a["Hq"], a["Hkv"],
+                                 a["dk"], a["dv"], a["ws"], a["B"], a["Hq"], a["Hkv"],
                                  a["N"], a["D"], a["scale"], a["causal"], a["valid_len"],
                                  a["dtype"])
 
@@ -251,19 +251,20 @@ def test_bwd_validate_accepts(lib):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(lse=None), sdp.ATTN_ERR_NULL),
-    (dict(delta=None), sdp.ATTN_ERR_NULL),
+    (dict(ws=None), sdp.ATTN_ERR_NULL),
     (dict(dout=None), sdp.ATTN_ERR_NULL),
     (dict(Hq=8, Hkv=3), sdp.ATTN_ERR_SHAPE),
     (dict(D=32), sdp.ATTN_ERR_HEAD_DIM),
     (dict(dtype=7), sdp.ATTN_ERR_DTYPE),
     (dict(scale=float("nan")), sdp.ATTN_ERR_SCALE),
     (dict(dq=DQ + 8), sdp.ATTN_ERR_LAYOUT),
-    (dict(delta=DL + 2), sdp.ATTN_ERR_LAYOUT),
+    (dict(ws=DL + 2), sdp.ATTN_ERR_LAYOUT),
     (dict(dq=Q + 1024), sdp.ATTN_ERR_ALIAS),            # dq overlaps q
     (dict(dk=DQ + 4096), sdp.ATTN_ERR_ALIAS),           # dk overlaps dq
     (dict(dv=DO), sdp.ATTN_ERR_ALIAS),                  # dv overlaps dout
-    (dict(delta=L + 64), sdp.ATTN_ERR_ALIAS),           # workspace overlaps lse
-    (dict(delta=VL - 64), sdp.ATTN_ERR_ALIAS),          # workspace overlaps valid_len
+    (dict(ws=L + 64), sdp.ATTN_ERR_ALIAS),              # workspace overlaps lse
+    (dict(ws=VL - 64), sdp.ATTN_ERR_ALIAS),             # workspace overlaps valid_len
+    (dict(ws=L - 2 * 2 * 8 * 1000 * 4 + 4), sdp.ATTN_ERR_ALIAS),   # its second row overlaps lse
 ])
 def test_bwd_validate_rejects(lib, kw, code):
     assert bcall(**kw) == code

@@ -35,13 +35,18 @@ def run_bwd(case, dout_bits, dout_scale=1.0):
     if case.valid_len is not None:
         vl = torch.from_numpy(case.valid_len.astype(np.int32)).cuda()
     out, lse = sdp.forward(q, k, v, causal=case.causal, valid_len=vl, scale=case.scale)
-    delta = torch.empty(lse.shape, dtype=torch.float32, device=q.device)
+    ws = torch.empty((2,) + tuple(lse.shape), dtype=torch.float32, device=q.device)
     dq, dk, dv = sdp.backward(q, k, v, out, do, lse, causal=case.causal, valid_len=vl,
-                              scale=case.scale, delta=delta)
+                              scale=case.scale, ws=ws)
     torch.cuda.synchronize()
+    L = lse.cpu().numpy()
+    # the workspace's second row is the device's LSE in base 2 (0 on empty rows)
+    l2 = ws[1].cpu().numpy()
+    want = np.where(np.isneginf(L), np.float32(0), L * np.float32(1.4426950408889634))
+    assert np.allclose(l2, want, rtol=1e-6, atol=0), "workspace LSE row"
     return (from_device(dq, case.dtype), from_device(dk, case.dtype),
-            from_device(dv, case.dtype), delta.cpu().numpy().astype(np.float64),
-            from_device(out, case.dtype), lse.cpu().numpy().astype(np.float64))
+            from_device(dv, case.dtype), ws[0].cpu().numpy().astype(np.float64),
+            from_device(out, case.dtype), L.astype(np.float64))
 
 
 def visibility(case):
