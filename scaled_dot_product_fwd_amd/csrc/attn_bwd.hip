@@ -155,23 +155,22 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p) {
   const int h = lane >> 5;
   const int ql = lane & 31;
 
-  // Work: (batch, query head, 128-query tile). Each XCD owns whole KV heads; within one it takes
-  // the tiles in order of decreasing work (the last query tile first under causal masking), for
-  // all its heads at once.
+  // Work: (batch, query head, 128-query tile), the forward's order: each XCD owns whole KV heads
+  // and takes them one after the other, the query heads of one KV head side by side (they read
+  // the same K and V tiles from L2) and the longest tiles first under causal masking.
   int qt, b, hq;
   {
     const int wid = blockIdx.x;
     if (p.xcd_order) {
       const int xcd = wid & 7, local = wid >> 3;
-      const int hpx = (p.B * p.Hkv) >> 3;   // KV heads per XCD
-      const int per_qi = hpx * p.group;
-      const int qi = local / per_qi;
-      const int r = local - qi * per_qi;
-      const int head_local = r / p.group;
+      const int per_head = p.group * p.nqt;
+      const int head_local = local / per_head;
+      const int r = local - head_local * per_head;
       const int kv_head = head_local * 8 + xcd;
+      const int qi = r / p.group;
       qt = CAUSAL ? p.nqt - 1 - qi : qi;
       b = kv_head / p.Hkv;
-      hq = (kv_head - b * p.Hkv) * p.group + (r - head_local * p.group);
+      hq = (kv_head - b * p.Hkv) * p.group + (r - qi * p.group);
     } else {
       const int BH = p.B * p.Hq;
       const int qi = wid / BH, bh = wid - qi * BH;
@@ -366,17 +365,22 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
   const int h = lane >> 5;
   const int ql = lane & 31;
 
-  // ---- work: (batch, KV head, 128-key tile). Each XCD owns whole KV heads; within one it
-  // takes the key tiles in order of decreasing work (under causal masking tile kt sees N - 128 kt
-  // queries), all its heads' tile 0 first: longest-first keeps the last workgroups short.
+  // ---- work: (batch, KV head, 128-key tile). Each XCD owns whole KV heads and takes them in
+  // blocks of two; within a block the key tiles go in order of decreasing work (under causal
+  // masking tile kt sees N - 128 kt queries), both heads' tile 0 first. Longest-first keeps the
+  // XCD's last workgroups short (one KV head after the other left a ~20 % tail); blocks of two
+  // keep the Q / dO working set to two KV heads.
   int kt, b, kvh;
   {
     const int wid = blockIdx.x;
     if (p.xcd_order) {
       const int xcd = wid & 7, local = wid >> 3;
       const int hpx = (p.B * p.Hkv) >> 3;
-      kt = local / hpx;
-      const int head_local = local - kt * hpx;
+      const int blk = (hpx & 1) ? 1 : 2;
+      const int pair = local / (blk * p.nkt);
+      const int r = local - pair * blk * p.nkt;
+      kt = r / blk;
+      const int head_local = pair * blk + (r - kt * blk);
       const int kv_head = head_local * 8 + xcd;
       b = kv_head / p.Hkv;
       kvh = kv_head - b * p.Hkv;
