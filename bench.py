@@ -45,6 +45,7 @@ METRIC = "attention fwd TFLOP/s, bf16 causal N=4096 D=128; % of MFMA dense peak"
 METRIC_BWD = "attention bwd TFLOP/s (nominal 2.5x forward flops), bf16 causal N=4096 D=128"
 PEAK_TFLOPS_16BIT_DENSE = 2500.0   # MI355X published dense bf16/fp16 MFMA peak
 KERNEL_SRC = os.path.join(ROOT, "scaled_dot_product_fwd_amd", "csrc", "attn_fwd.hip")
+KERNEL_SRC_BWD = os.path.join(ROOT, "scaled_dot_product_fwd_amd", "csrc", "attn_bwd.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -62,19 +63,21 @@ def flops_bwd(w) -> float:
     return 2.5 * flops(w)
 
 
-def kernel_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
+def kernel_sha(src: str = KERNEL_SRC) -> str:
+    with open(src, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def traffic_for(workload: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they match this source."""
-    path = os.path.join(PROFILES, "traffic_%s.json" % workload)
+def traffic_for(workload: str, backward: bool = False):
+    """HBM bytes per launch (per attn_bwd call with backward) from committed rocprofv3 counter
+    runs, if they were taken on this kernel source."""
+    name = "traffic_%s%s.json" % (workload, "_bwd" if backward else "")
+    path = os.path.join(PROFILES, name)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_sha256") != kernel_sha():
+    if t.get("kernel_source_sha256") != kernel_sha(KERNEL_SRC_BWD if backward else KERNEL_SRC):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -248,8 +251,8 @@ def main():
     f = flops_bwd(w) if args.backward else flops(w)
     tflops = f / (ms_per_step * 1e-3) / 1e12
     traffic = None
-    if not args.backward and args.layout == "bhnd" and amask is None:
-        traffic = traffic_for(w.name)
+    if args.layout == "bhnd" and amask is None:
+        traffic = traffic_for(w.name, backward=args.backward)
     roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_TFLOPS_16BIT_DENSE,
             "unit": "TFLOP/s", "frac": round(tflops / PEAK_TFLOPS_16BIT_DENSE, 4),
             "traffic": traffic}
