@@ -57,7 +57,7 @@ typedef enum {
     ATTN_ERR_NULL = -1,     /* q, k, v or out is NULL */
     ATTN_ERR_SHAPE = -2,    /* B, Hq, Hkv or N < 1, Hq not a multiple of Hkv, or sizes beyond
                                the limits below */
-    ATTN_ERR_HEAD_DIM = -3, /* D is not 64 or 128 */
+    ATTN_ERR_HEAD_DIM = -3, /* D is not supported (see attn_fwd / attn_bwd) */
     ATTN_ERR_DTYPE = -4,    /* dtype is not ATTN_F16 or ATTN_BF16 */
     ATTN_ERR_SCALE = -5,    /* scale is NaN or infinite */
     ATTN_ERR_LAUNCH = -6,   /* the HIP runtime reported an error at launch; query HIP for it */
@@ -95,7 +95,8 @@ typedef enum {
  *   lse        device pointer to [B, Hq, N] float32, contiguous; NULL means "do not write".
  *   B, Hq, Hkv, N, D
  *              batch, query heads, key/value heads, sequence length (queries and keys share it),
- *              head dimension. Any N >= 1 is accepted; D must be 64 or 128.
+ *              head dimension. Any N >= 1 is accepted; D must be 16, 32, 64 or 128
+ *              (attn_bwd: 64 or 128).
  *   scale      multiplier of the dot products (typically 1/sqrt(D)); any finite value.
  *   causal     nonzero hides key j from query i when j > i.
  *   valid_len  device pointer to int32[B], or NULL for no padding mask. Keys j >= valid_len[b]

@@ -152,8 +152,14 @@ __device__ inline void update_max(float mx, float c, float& m, float& l,
   }
 }
 
-template <int DT, int D, bool CAUSAL, int MK>
+// DH is the head dimension of the tensors; head dimensions below 64 run the D = 64 geometry with
+// the missing 16-byte chunks of every row zero-filled (their lanes' loads are out of range) and
+// never stored: zero chunks add nothing to Q.K and give zero O columns. The work per score is
+// then that of D = 64, which is bound by the softmax's VALU work, not by the MFMAs.
+template <int DT, int DH, bool CAUSAL, int MK>
 __device__ __forceinline__ void attn_fwd_body(const Params& p) {
+  constexpr int D = DH < 64 ? 64 : DH;   // geometry
+  constexpr int DCH = DH / 8;            // 16-byte chunks of a row that exist
   using G = Geo<D>;
   using M = Mfma<DT>;
   using MG = MaskGeo<MK>;
@@ -208,11 +214,14 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
   // as zeros. Row strides in bytes (the host keeps every span below 2^31 bytes).
   const uint32_t krow = (uint32_t)p.ks_n * 2, vrow = (uint32_t)p.vs_n * 2;
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.k + b * p.ks_b + kvh * p.ks_h), (short)0, (p.N - 1) * krow + G::ROW,
+      (void*)(p.k + b * p.ks_b + kvh * p.ks_h), (short)0, (p.N - 1) * krow + 2 * DH,
       kBufferFlags);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.v + b * p.vs_b + kvh * p.vs_h), (short)0, (p.N - 1) * vrow + G::ROW,
+      (void*)(p.v + b * p.vs_b + kvh * p.vs_h), (short)0, (p.N - 1) * vrow + 2 * DH,
       kBufferFlags);
+  // A lane whose global chunk does not exist (DH < 64) fetches from 2^31, past every buffer
+  // (the host keeps each span and scalar tile offset below 2^31), and so writes zeros to LDS.
+  constexpr uint32_t kNoChunk = 0x80000000u;
 
   // ---- DMA offsets: block (wave * LOADS + i) of a tile holds rows [blk * RPB, +RPB); lane
   // writes LDS chunk (lane % CH) of row (lane / CH) and fetches the global chunk that the row's
@@ -221,11 +230,13 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
 #pragma unroll
   for (int i = 0; i < G::LOADS; ++i) {
     const int row = (wave * G::LOADS + i) * G::RPB + lane / G::CH;
-    koff[i] = row * krow + (((lane % G::CH) ^ G::kswz(row)) * 16);
+    const int gc = (lane % G::CH) ^ G::kswz(row);
+    koff[i] = (DCH < G::CH && gc >= DCH) ? kNoChunk : row * krow + gc * 16;
   }
   {
     const int row = wave * G::LOADS * G::RPB + lane / G::CH;
-    voff0 = row * vrow + (((lane % G::CH) ^ G::vswz(row)) * 16);
+    const int gc = (lane % G::CH) ^ G::vswz(row);
+    voff0 = (DCH < G::CH && gc >= DCH) ? kNoChunk : row * vrow + gc * 16;
   }
   auto dma = [&](int tile, int kdst, int vdst) {
     const uint32_t row0 = (uint32_t)tile * kBN;
@@ -291,7 +302,8 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
       p.q + b * p.qs_b + hq * p.qs_h + min(qrow, p.N - 1) * p.qs_n + 8 * h;
   u32x4 qf[KSTEPS];
 #pragma unroll
-  for (int s = 0; s < KSTEPS; ++s) qf[s] = *(const u32x4*)(qsrc + 16 * s);
+  for (int s = 0; s < KSTEPS; ++s)
+    qf[s] = (DCH < G::CH && 2 * s + h >= DCH) ? u32x4{} : *(const u32x4*)(qsrc + 16 * s);
 
   f32x16 acc[OT];
 #pragma unroll
@@ -566,7 +578,8 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
     const int r = i * RPI + lane / G::CH;
     const int cc = lane % G::CH;
     const u32x4 v = *(const u32x4*)(ost + r * G::ROW + 16 * (cc ^ (r & (G::CH - 1))));
-    if (qa + r < p.N) *(u32x4*)(obase + (qa + r) * p.os_n + 8 * cc) = v;
+    if (qa + r < p.N && (DCH == G::CH || cc < DCH))
+      *(u32x4*)(obase + (qa + r) * p.os_n + 8 * cc) = v;
   }
   if (p.lse && h == 0 && qrow < p.N)
     p.lse[(size_t)bh * p.N + qrow] = empty ? -INFINITY : m * kLn2 + logf(lt);
@@ -591,9 +604,16 @@ hipError_t launch(const Params& p, int64_t nwg, hipStream_t stream) {
 
 template <int DT, int MK>
 hipError_t dispatch_d(const Params& p, int D, bool causal, int64_t nwg, hipStream_t s) {
-  if (D == 64)
-    return causal ? launch<DT, 64, true, MK>(p, nwg, s) : launch<DT, 64, false, MK>(p, nwg, s);
-  return causal ? launch<DT, 128, true, MK>(p, nwg, s) : launch<DT, 128, false, MK>(p, nwg, s);
+  switch (D) {
+    case 16:
+      return causal ? launch<DT, 16, true, MK>(p, nwg, s) : launch<DT, 16, false, MK>(p, nwg, s);
+    case 32:
+      return causal ? launch<DT, 32, true, MK>(p, nwg, s) : launch<DT, 32, false, MK>(p, nwg, s);
+    case 64:
+      return causal ? launch<DT, 64, true, MK>(p, nwg, s) : launch<DT, 64, false, MK>(p, nwg, s);
+    default:
+      return causal ? launch<DT, 128, true, MK>(p, nwg, s) : launch<DT, 128, false, MK>(p, nwg, s);
+  }
 }
 
 template <int DT>
@@ -671,7 +691,7 @@ int validate(const Layout& q, const Layout& k, const Layout& v, const Layout& o,
   if (N > ATTN_MAX_N) return ATTN_ERR_SHAPE;
   const int64_t ntiles = (int64_t)B * Hq * (((int64_t)N + kBM - 1) / kBM);
   if (ntiles > ATTN_MAX_TILES) return ATTN_ERR_SHAPE;
-  if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
+  if (D != 16 && D != 32 && D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
   if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
   if (!isfinite(scale)) return ATTN_ERR_SCALE;
   if (!layout_ok(q, D) || !layout_ok(k, D) || !layout_ok(v, D) || !layout_ok(o, D))

@@ -77,6 +77,8 @@ def test_validate_accepts_good_arguments(lib):
     assert call(N=1) == sdp.ATTN_OK
     assert call(scale=0.0) == sdp.ATTN_OK
     assert call(scale=-0.5) == sdp.ATTN_OK
+    assert call(D=16) == sdp.ATTN_OK
+    assert call(D=32, dtype=sdp.ATTN_F16) == sdp.ATTN_OK
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -93,7 +95,8 @@ def test_validate_accepts_good_arguments(lib):
     (dict(N=(1 << 22) + 1), sdp.ATTN_ERR_SHAPE),
     (dict(D=96), sdp.ATTN_ERR_HEAD_DIM),
     (dict(D=256), sdp.ATTN_ERR_HEAD_DIM),
-    (dict(D=32), sdp.ATTN_ERR_HEAD_DIM),
+    (dict(D=48), sdp.ATTN_ERR_HEAD_DIM),
+    (dict(D=8), sdp.ATTN_ERR_HEAD_DIM),
     (dict(dtype=2), sdp.ATTN_ERR_DTYPE),
     (dict(dtype=-1), sdp.ATTN_ERR_DTYPE),
     (dict(scale=float("nan")), sdp.ATTN_ERR_SCALE),

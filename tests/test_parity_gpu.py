@@ -44,6 +44,30 @@ def test_small_full(cfg):
     compare(case, O, L, O_ref, L_ref, tag=str(cfg))
 
 
+# Head dimensions below 64 (zero-padded to the D = 64 geometry inside the kernel): ragged N,
+# GQA / MQA, causal and padded, both types, every row compared.
+SMALL_D = [
+    ("f16", 16, False, False, 1, 2, 2, 128),
+    ("bf16", 16, True, True, 3, 4, 2, 257),
+    ("f16", 16, True, False, 2, 8, 1, 1000),
+    ("bf16", 16, False, True, 2, 2, 1, 1),
+    ("f16", 32, True, True, 2, 6, 3, 300),
+    ("bf16", 32, False, False, 1, 4, 4, 65),
+    ("bf16", 32, True, False, 2, 8, 2, 1100),
+    ("f16", 32, False, True, 4, 2, 2, 513),
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL_D, ids=lambda c: "%s-D%d-c%d-p%d-B%d-H%d-%d-N%d" % c)
+def test_small_head_dims(cfg):
+    dtype, D, causal, padded, B, Hq, Hkv, N = cfg
+    case = inputs.make_case(B, Hq, Hkv, N, D, dtype, causal, padded, seed=[115, D, N, B])
+    log("case %s valid_len %s" % (cfg, case.valid_len))
+    O, L = run_device(case)
+    O_ref, L_ref = run_oracle(case)
+    compare(case, O, L, O_ref, L_ref, tag=str(cfg))
+
+
 # More 128-query tiles (B * Hq * ceil(N / 128)) than the 512 workgroups the device holds at
 # once, every row compared: the XCD-grouped workgroup order (B * Hkv % 8 == 0) and the plain
 # one, padding with an empty batch (a tile with no visible key), odd and even tile counts.
@@ -209,6 +233,9 @@ STRIDED = [
     ("packed_qkv", "f16", 128, True, True, 2, 4, 4, 190),
     ("packed_qkv", "bf16", 64, False, False, 1, 8, 8, 64),
     ("strided_out", "bf16", 128, True, False, 2, 4, 1, 270),
+    ("bnhd", "bf16", 32, True, True, 2, 4, 2, 200),
+    ("padded_rows", "f16", 16, False, False, 2, 4, 1, 150),
+    ("packed_qkv", "bf16", 16, True, False, 1, 4, 4, 100),
 ]
 
 
@@ -280,6 +307,8 @@ MASKED = [
     ("add", "large_negative", "f16", 128, False, False, 1, 2, 2, 64),
     # rows whose first tiles are wholly hidden while other rows of the wave rescale
     ("add", "window_neginf", "bf16", 128, False, False, 2, 4, 4, 300),
+    ("keep", "random_bh", "f16", 16, True, True, 2, 4, 2, 200),
+    ("add", "alibi", "bf16", 32, False, False, 2, 4, 1, 300),
 ]
 
 
