@@ -14,6 +14,8 @@ nominal backward flop count 2.5x the forward's (five N x N x D products: dV, dP,
 recomputed S); the kernels also recompute S and dP a second time, so the MFMA work they issue is
 7/5 of that count.
 
+--head-dim D replaces the workload's head dimension (16, 32, 64, 128 or 256; scale 1/sqrt(D));
+the flop count follows D.
 --layout bnhd stores Q, K, V and O as [B, N, H, D] and runs the strided entry point on them.
 --mask keep adds an explicit [N, N] uint8 sliding-window mask (key j visible to query i when
 |i - j| < 2048) and --mask add an [N, N] additive mask of the input dtype (-|i - j| / 256), both
@@ -159,6 +161,8 @@ def main():
                     help="memory layout of Q, K, V and O")
     ap.add_argument("--mask", choices=("none", "keep", "add"), default="none",
                     help="explicit mask to add (see the module docstring)")
+    ap.add_argument("--head-dim", type=int, default=0, metavar="D",
+                    help="replace the workload's head dimension")
     ap.add_argument("--backward", action="store_true",
                     help="time attn_bwd (dQ, dK, dV) instead of the forward")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -184,6 +188,9 @@ def main():
     from scaled_dot_product_fwd_amd import inputs
 
     w = inputs.WORKLOADS[args.workload]
+    if args.head_dim:
+        import dataclasses
+        w = dataclasses.replace(w, D=args.head_dim)
     log("workload %s: B=%d Hq=%d Hkv=%d N=%d D=%d %s causal=%s padded=%s" % (
         w.name, w.B, w.Hq, w.Hkv, w.N, w.D, w.dtype, w.causal, w.padded))
     case = inputs.make_workload(w)
@@ -251,7 +258,7 @@ def main():
     f = flops_bwd(w) if args.backward else flops(w)
     tflops = f / (ms_per_step * 1e-3) / 1e12
     traffic = None
-    if args.layout == "bhnd" and amask is None:
+    if args.layout == "bhnd" and amask is None and not args.head_dim:
         traffic = traffic_for(w.name, backward=args.backward)
     roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_TFLOPS_16BIT_DENSE,
             "unit": "TFLOP/s", "frac": round(tflops / PEAK_TFLOPS_16BIT_DENSE, 4),

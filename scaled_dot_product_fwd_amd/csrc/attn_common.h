@@ -46,11 +46,13 @@ struct Geo {
   //    a 32-lane half the same 4 rows x 64 bytes. XOR of the 32-byte pair index by
   //    F = {0, 3, 5, 6}[r & 3] (D = 128) puts the 4 rows on distinct pairs mod 128 bytes and on
   //    distinct 64-byte blocks mod 256 bytes; with 128-byte rows (D = 64) F = r & 3 does both.
+  //  Rows of 256 bytes or more (D >= 128) start on the same bank; rows of 128 bytes (D = 64)
+  //  alternate between the two halves of the 256-byte bank set.
   __device__ static constexpr int kswz(int r) {
-    return D == 128 ? (r & 15) : ((r & 7) ^ ((r >> 3) & 1));
+    return D >= 128 ? (r & 15) : ((r & 7) ^ ((r >> 3) & 1));
   }
   __device__ static constexpr int vswz(int r) {
-    return D == 128 ? 2 * ((0x6530 >> (4 * (r & 3))) & 15) : 2 * (r & 3);
+    return D >= 128 ? 2 * ((0x6530 >> (4 * (r & 3))) & 15) : 2 * (r & 3);
   }
   //  * A tile read both ways (the backward's K, Q and dO) needs both properties: vswz's pair
   //    XOR on r & 3 for the transposed reads, plus bits that tell apart the 4-row groups of 16
@@ -59,7 +61,7 @@ struct Geo {
   //    even-parity set {0, 3, 5, 6} (D = 128) onto the odd one, or shifts F = r & 3 (D = 64).
   //    Rows r and r + 8 therefore differ by chunk XOR 2; rows r and r + 16 share the swizzle.
   __device__ static constexpr int bswz(int r) {
-    return D == 128 ? 2 * (((0x6530 >> (4 * (r & 3))) & 15) ^ ((r >> 3) & 1)) + ((r >> 2) & 1)
+    return D >= 128 ? 2 * (((0x6530 >> (4 * (r & 3))) & 15) ^ ((r >> 3) & 1)) + ((r >> 2) & 1)
                     : 2 * ((r & 3) ^ ((r >> 3) & 1)) + ((r >> 2) & 1);
   }
 };

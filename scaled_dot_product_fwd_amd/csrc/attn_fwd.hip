@@ -226,17 +226,22 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
   // ---- DMA offsets: block (wave * LOADS + i) of a tile holds rows [blk * RPB, +RPB); lane
   // writes LDS chunk (lane % CH) of row (lane / CH) and fetches the global chunk that the row's
   // swizzle maps there. V's swizzle depends on row & 3 only, the same in every block.
-  uint32_t koff[G::LOADS], voff0;
+  // With 512-byte rows (D = 256) a block holds 2 rows and V's swizzle differs between blocks:
+  // one V offset per block then.
+  constexpr bool VSHARED = G::RPB % 4 == 0;
+  uint32_t koff[G::LOADS], voff[VSHARED ? 1 : G::LOADS];
 #pragma unroll
   for (int i = 0; i < G::LOADS; ++i) {
     const int row = (wave * G::LOADS + i) * G::RPB + lane / G::CH;
     const int gc = (lane % G::CH) ^ G::kswz(row);
     koff[i] = (DCH < G::CH && gc >= DCH) ? kNoChunk : row * krow + gc * 16;
   }
-  {
-    const int row = wave * G::LOADS * G::RPB + lane / G::CH;
+#pragma unroll
+  for (int i = 0; i < (VSHARED ? 1 : G::LOADS); ++i) {
+    // VSHARED: block 0's row, the blocks' row offsets go into the scalar offset
+    const int row = (wave * G::LOADS + i) * G::RPB + lane / G::CH;
     const int gc = (lane % G::CH) ^ G::vswz(row);
-    voff0 = (DCH < G::CH && gc >= DCH) ? kNoChunk : row * vrow + gc * 16;
+    voff[i] = (DCH < G::CH && gc >= DCH) ? kNoChunk : row * vrow + gc * 16;
   }
   auto dma = [&](int tile, int kdst, int vdst) {
     const uint32_t row0 = (uint32_t)tile * kBN;
@@ -248,7 +253,8 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
                                                  koff[i], row0 * krow, 0, 0);
       if (vdst >= 0)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(smem + vdst + blk), 16,
-                                                 voff0, (row0 + i * G::RPB) * vrow, 0, 0);
+                                                 voff[VSHARED ? 0 : i],
+                                                 (row0 + (VSHARED ? i * G::RPB : 0)) * vrow, 0, 0);
     }
   };
 
@@ -412,10 +418,10 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
         e0 = g * ne;
       } else {
         ps = (g + OT) / SPS;
-        ne = 8 / SPS;
+        ne = SPS <= 8 ? 8 / SPS : 1;   // D = 256: one per slot in the first 8 of SPS = 16
         e0 = (g - (ps * SPS - OT)) * ne;
       }
-      if (ps < 4) {
+      if (ps < 4 && e0 < 8) {
 #pragma unroll
         for (int e = e0; e < e0 + ne; ++e) prob(pe, ps, e);
         if (e0 + ne == 8) pb[ps] = M::pack(pe);
@@ -436,9 +442,9 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
     l += lsum + pend1 + pend2;
   };
 
-  // ---- prologue: K_0, V_0, K_1 in flight; scores of tile 0
+  // ---- prologue: K_0, V_0 (and, software-pipelined, K_1) in flight; scores of tile 0
   if (ntiles > 0) dma(0, G::K0, G::V0);
-  if (ntiles > 1) dma(1, G::K1, -1);
+  if (D <= 128 && ntiles > 1) dma(1, G::K1, -1);
   if (ntiles > 0) mask_dma(0);
   wait_loads_and_lds();
 #pragma unroll
@@ -446,7 +452,7 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
   __syncthreads();
   f32x16 sA[2], sB[2];
   float mxA = -INFINITY, mxB = -INFINITY;
-  if (ntiles > 0) {
+  if (D <= 128 && ntiles > 0) {
     qk_tile<DT, D>(sA, smem + G::K0, f, qf);
     mxA = rowmax(sA);
   }
@@ -537,16 +543,36 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
   using I1 = std::integral_constant<int, 1>;
   using T = std::true_type;
   using F = std::false_type;
-  int j = 0;
-  for (; j + 2 < ntiles; j += 2) {
-    step(j, I0{}, T{}, sA, mxA, sB, mxB);
-    step(j + 1, I1{}, T{}, sB, mxB, sA, mxA);
-  }
-  if (j + 1 < ntiles) {
-    step(j, I0{}, T{}, sA, mxA, sB, mxB);
-    step(j + 1, I1{}, F{}, sB, mxB, sA, mxA);
-  } else if (j < ntiles) {
-    step(j, I0{}, F{}, sA, mxA, sB, mxB);
+  if constexpr (D > 128) {
+    // 512-byte rows: the next tile's scores do not fit beside the 128 accumulator and 64 Q
+    // registers, so each step computes its own scores, then the softmax and P V, while the DMA
+    // of the next tile's K and V runs.
+    auto step1 = [&](int j, auto parity) {
+      constexpr int P = decltype(parity)::value;
+      wait_loads_and_lds();
+      __syncthreads();
+      if (j + 1 < ntiles) dma(j + 1, P ? G::K0 : G::K1, P ? G::V0 : G::V1);
+      qk_tile<DT, D>(sA, smem + (P ? G::K1 : G::K0), f, qf);
+      mxA = rowmax(sA);
+      mask_tile(sA, mxA, j * kBN, j);
+      tile(F{}, sA, mxA, sB, mxB, nullptr, smem + (P ? G::V1 : G::V0));
+    };
+    for (int j = 0; j < ntiles; j += 2) {
+      step1(j, I0{});
+      if (j + 1 < ntiles) step1(j + 1, I1{});
+    }
+  } else {
+    int j = 0;
+    for (; j + 2 < ntiles; j += 2) {
+      step(j, I0{}, T{}, sA, mxA, sB, mxB);
+      step(j + 1, I1{}, T{}, sB, mxB, sA, mxA);
+    }
+    if (j + 1 < ntiles) {
+      step(j, I0{}, T{}, sA, mxA, sB, mxB);
+      step(j + 1, I1{}, F{}, sB, mxB, sA, mxA);
+    } else if (j < ntiles) {
+      step(j, I0{}, F{}, sA, mxA, sB, mxB);
+    }
   }
 
   // ---- epilogue: O = acc / l (0 for a row with no visible key), LSE = m ln2 + ln l.
@@ -587,8 +613,11 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
 
 // The body uses device-only types (buffer resources), so only the device pass compiles it;
 // the host pass needs no more than the kernel's signature to emit its launch stub.
+// D = 256 holds 128 KiB of K/V tiles in LDS, one workgroup per CU: one wave per SIMD, which may
+// then use the whole register file (256 VGPRs + 256 AGPRs).
 template <int DT, int D, bool CAUSAL, int MK>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(D > 128 ? 1 : 2, D > 128 ? 1 : 2)))
 void attn_fwd_kernel(Params p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   attn_fwd_body<DT, D, CAUSAL, MK>(p);
@@ -611,6 +640,8 @@ hipError_t dispatch_d(const Params& p, int D, bool causal, int64_t nwg, hipStrea
       return causal ? launch<DT, 32, true, MK>(p, nwg, s) : launch<DT, 32, false, MK>(p, nwg, s);
     case 64:
       return causal ? launch<DT, 64, true, MK>(p, nwg, s) : launch<DT, 64, false, MK>(p, nwg, s);
+    case 256:
+      return causal ? launch<DT, 256, true, MK>(p, nwg, s) : launch<DT, 256, false, MK>(p, nwg, s);
     default:
       return causal ? launch<DT, 128, true, MK>(p, nwg, s) : launch<DT, 128, false, MK>(p, nwg, s);
   }
@@ -691,7 +722,7 @@ int validate(const Layout& q, const Layout& k, const Layout& v, const Layout& o,
   if (N > ATTN_MAX_N) return ATTN_ERR_SHAPE;
   const int64_t ntiles = (int64_t)B * Hq * (((int64_t)N + kBM - 1) / kBM);
   if (ntiles > ATTN_MAX_TILES) return ATTN_ERR_SHAPE;
-  if (D != 16 && D != 32 && D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
+  if (D != 16 && D != 32 && D != 64 && D != 128 && D != 256) return ATTN_ERR_HEAD_DIM;
   if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
   if (!isfinite(scale)) return ATTN_ERR_SCALE;
   if (!layout_ok(q, D) || !layout_ok(k, D) || !layout_ok(v, D) || !layout_ok(o, D))

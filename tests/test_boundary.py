@@ -79,6 +79,7 @@ def test_validate_accepts_good_arguments(lib):
     assert call(scale=-0.5) == sdp.ATTN_OK
     assert call(D=16) == sdp.ATTN_OK
     assert call(D=32, dtype=sdp.ATTN_F16) == sdp.ATTN_OK
+    assert call(D=256) == sdp.ATTN_OK
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -94,7 +95,7 @@ def test_validate_accepts_good_arguments(lib):
     (dict(Hq=8, Hkv=3), sdp.ATTN_ERR_SHAPE),
     (dict(N=(1 << 22) + 1), sdp.ATTN_ERR_SHAPE),
     (dict(D=96), sdp.ATTN_ERR_HEAD_DIM),
-    (dict(D=256), sdp.ATTN_ERR_HEAD_DIM),
+    (dict(D=512), sdp.ATTN_ERR_HEAD_DIM),
     (dict(D=48), sdp.ATTN_ERR_HEAD_DIM),
     (dict(D=8), sdp.ATTN_ERR_HEAD_DIM),
     (dict(dtype=2), sdp.ATTN_ERR_DTYPE),

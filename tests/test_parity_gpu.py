@@ -44,8 +44,9 @@ def test_small_full(cfg):
     compare(case, O, L, O_ref, L_ref, tag=str(cfg))
 
 
-# Head dimensions below 64 (zero-padded to the D = 64 geometry inside the kernel): ragged N,
-# GQA / MQA, causal and padded, both types, every row compared.
+# Head dimensions 16 and 32 (zero-padded to the D = 64 geometry inside the kernel) and 256 (one
+# workgroup per CU, unpipelined loop): ragged N, GQA / MQA, causal and padded, both types, every
+# row compared.
 SMALL_D = [
     ("f16", 16, False, False, 1, 2, 2, 128),
     ("bf16", 16, True, True, 3, 4, 2, 257),
@@ -55,6 +56,11 @@ SMALL_D = [
     ("bf16", 32, False, False, 1, 4, 4, 65),
     ("bf16", 32, True, False, 2, 8, 2, 1100),
     ("f16", 32, False, True, 4, 2, 2, 513),
+    ("bf16", 256, True, True, 3, 4, 2, 257),
+    ("f16", 256, False, False, 1, 4, 4, 200),
+    ("bf16", 256, True, False, 2, 8, 1, 1000),
+    ("f16", 256, True, True, 2, 6, 3, 65),
+    ("bf16", 256, False, True, 2, 2, 2, 1),
 ]
 
 
@@ -236,6 +242,8 @@ STRIDED = [
     ("bnhd", "bf16", 32, True, True, 2, 4, 2, 200),
     ("padded_rows", "f16", 16, False, False, 2, 4, 1, 150),
     ("packed_qkv", "bf16", 16, True, False, 1, 4, 4, 100),
+    ("bnhd", "f16", 256, True, False, 2, 4, 2, 300),
+    ("padded_rows", "bf16", 256, False, True, 2, 2, 1, 130),
 ]
 
 
@@ -309,6 +317,8 @@ MASKED = [
     ("add", "window_neginf", "bf16", 128, False, False, 2, 4, 4, 300),
     ("keep", "random_bh", "f16", 16, True, True, 2, 4, 2, 200),
     ("add", "alibi", "bf16", 32, False, False, 2, 4, 1, 300),
+    ("keep", "window", "bf16", 256, True, False, 2, 4, 2, 300),
+    ("add", "random_bh", "f16", 256, False, True, 2, 2, 1, 200),
 ]
 
 
