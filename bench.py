@@ -14,6 +14,8 @@ nominal backward flop count 2.5x the forward's (five N x N x D products: dV, dP,
 recomputed S); the kernels also recompute S and dP a second time, so the MFMA work they issue is
 7/5 of that count.
 
+--dtype f32|f16|bf16 replaces the workload's input type (f32: fp32 products on the fp32 matrix
+cores, against their 157.3 TFLOP/s dense peak).
 --head-dim D replaces the workload's head dimension (16, 32, 64, 128 or 256; scale 1/sqrt(D));
 the flop count follows D.
 --layout bnhd stores Q, K, V and O as [B, N, H, D] and runs the strided entry point on them.
@@ -46,6 +48,7 @@ sys.path.insert(0, ROOT)
 METRIC = "attention fwd TFLOP/s, bf16 causal N=4096 D=128; % of MFMA dense peak"
 METRIC_BWD = "attention bwd TFLOP/s (nominal 2.5x forward flops), bf16 causal N=4096 D=128"
 PEAK_TFLOPS_16BIT_DENSE = 2500.0   # MI355X published dense bf16/fp16 MFMA peak
+PEAK_TFLOPS_F32_DENSE = 157.3      # MI355X published dense fp32 MFMA peak
 KERNEL_SRC = os.path.join(ROOT, "scaled_dot_product_fwd_amd", "csrc", "attn_fwd.hip")
 KERNEL_SRC_BWD = os.path.join(ROOT, "scaled_dot_product_fwd_amd", "csrc", "attn_bwd.hip")
 PROFILES = os.path.join(ROOT, "profiles")
@@ -161,6 +164,8 @@ def main():
                     help="memory layout of Q, K, V and O")
     ap.add_argument("--mask", choices=("none", "keep", "add"), default="none",
                     help="explicit mask to add (see the module docstring)")
+    ap.add_argument("--dtype", choices=("f16", "bf16", "f32"), default=None,
+                    help="replace the workload's input type")
     ap.add_argument("--head-dim", type=int, default=0, metavar="D",
                     help="replace the workload's head dimension")
     ap.add_argument("--backward", action="store_true",
@@ -188,15 +193,19 @@ def main():
     from scaled_dot_product_fwd_amd import inputs
 
     w = inputs.WORKLOADS[args.workload]
+    import dataclasses
     if args.head_dim:
-        import dataclasses
         w = dataclasses.replace(w, D=args.head_dim)
+    if args.dtype:
+        w = dataclasses.replace(w, dtype=args.dtype)
     log("workload %s: B=%d Hq=%d Hkv=%d N=%d D=%d %s causal=%s padded=%s" % (
         w.name, w.B, w.Hq, w.Hkv, w.N, w.D, w.dtype, w.causal, w.padded))
     case = inputs.make_workload(w)
-    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float16
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[w.dtype]
 
     def dev(bits):
+        if w.dtype == "f32":
+            return torch.from_numpy(bits.view(np.float32)).cuda()
         return torch.from_numpy(bits.view(np.int16)).view(tdt).cuda()
 
     q, k, v = dev(case.q_bits), dev(case.k_bits), dev(case.v_bits)
@@ -258,10 +267,11 @@ def main():
     f = flops_bwd(w) if args.backward else flops(w)
     tflops = f / (ms_per_step * 1e-3) / 1e12
     traffic = None
-    if args.layout == "bhnd" and amask is None and not args.head_dim:
+    if args.layout == "bhnd" and amask is None and not args.head_dim and not args.dtype:
         traffic = traffic_for(w.name, backward=args.backward)
-    roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_TFLOPS_16BIT_DENSE,
-            "unit": "TFLOP/s", "frac": round(tflops / PEAK_TFLOPS_16BIT_DENSE, 4),
+    peak = PEAK_TFLOPS_F32_DENSE if w.dtype == "f32" else PEAK_TFLOPS_16BIT_DENSE
+    roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
+            "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
             "traffic": traffic}
     cpu = None
     if not args.no_cpu_baseline:

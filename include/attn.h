@@ -48,7 +48,8 @@ extern "C" {
 /* Element type of Q, K, V and O. */
 typedef enum {
     ATTN_F16 = 0,  /* IEEE binary16 */
-    ATTN_BF16 = 1  /* bfloat16 */
+    ATTN_BF16 = 1, /* bfloat16 */
+    ATTN_F32 = 2   /* IEEE binary32: attn_fwd and attn_fwd_strided only, D in {32, 64, 128} */
 } attn_dtype_t;
 
 /* Return codes. Argument errors are detected on the host before anything is launched. */
@@ -58,12 +59,12 @@ typedef enum {
     ATTN_ERR_SHAPE = -2,    /* B, Hq, Hkv or N < 1, Hq not a multiple of Hkv, or sizes beyond
                                the limits below */
     ATTN_ERR_HEAD_DIM = -3, /* D is not supported (see attn_fwd / attn_bwd) */
-    ATTN_ERR_DTYPE = -4,    /* dtype is not ATTN_F16 or ATTN_BF16 */
+    ATTN_ERR_DTYPE = -4,    /* dtype not supported by this entry point */
     ATTN_ERR_SCALE = -5,    /* scale is NaN or infinite */
     ATTN_ERR_LAUNCH = -6,   /* the HIP runtime reported an error at launch; query HIP for it */
     ATTN_ERR_ALIAS = -7,    /* out or lse overlaps an input, or out overlaps lse */
     ATTN_ERR_LAYOUT = -8,   /* a pointer is not 16-byte aligned, a stride is negative or not a
-                               multiple of 8 elements, rows are less than D elements apart, or
+                               multiple of 16 bytes, rows are less than D elements apart, or
                                two output rows share memory; for a mask see attn_fwd_masked */
     ATTN_ERR_MASK = -9      /* mask_type is not one of attn_mask_t */
 } attn_status_t;
@@ -77,8 +78,8 @@ typedef enum {
 } attn_mask_t;
 
 /* Size limits checked by attn_fwd_validate: N <= ATTN_MAX_N and
- * B * Hq * ceil(N / 128) <= ATTN_MAX_TILES; with strides, also (N + 64) * (K or V row stride)
- * * 2 + 2 * D < 2^31 (the bytes the kernel may address inside one K or V head). */
+ * B * Hq * ceil(N / 128) <= ATTN_MAX_TILES; with strides, also ((N + 64) * (K or V row stride)
+ * + D) * (element size) < 2^31 (the bytes the kernel may address inside one K or V head). */
 #define ATTN_MAX_N (1 << 22)
 #define ATTN_MAX_TILES 2147483647LL
 
@@ -95,14 +96,17 @@ typedef enum {
  *   lse        device pointer to [B, Hq, N] float32, contiguous; NULL means "do not write".
  *   B, Hq, Hkv, N, D
  *              batch, query heads, key/value heads, sequence length (queries and keys share it),
- *              head dimension. Any N >= 1 is accepted; D must be 16, 32, 64 or 128
- *              (attn_bwd: 64 or 128).
+ *              head dimension. Any N >= 1 is accepted; D must be 16, 32, 64, 128 or 256 for
+ *              16-bit types, 32, 64 or 128 for ATTN_F32 (attn_bwd: 64 or 128).
  *   scale      multiplier of the dot products (typically 1/sqrt(D)); any finite value.
  *   causal     nonzero hides key j from query i when j > i.
  *   valid_len  device pointer to int32[B], or NULL for no padding mask. Keys j >= valid_len[b]
  *              are hidden for every query of batch b; values are clamped into [0, N]. Only keys
  *              are masked: query rows at or beyond valid_len[b] are computed like any other row.
- *   dtype      ATTN_F16 or ATTN_BF16.
+ *   dtype      ATTN_F16 or ATTN_BF16: 16-bit Q, K, V, O; scores, softmax and accumulation in
+ *              fp32; P is rounded to the input type before P V (as the Triton pages do).
+ *              ATTN_F32: fp32 Q, K, V, O and fp32 products throughout (the article's kernels
+ *              work in fp32), on the fp32 matrix cores; nothing is rounded to 16 bits.
  *   stream     hipStream_t to launch on; NULL is the default stream.
  *
  * Ownership: the caller allocates and owns every buffer; the call is asynchronous and the

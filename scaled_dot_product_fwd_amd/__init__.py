@@ -21,7 +21,7 @@ import ctypes
 import os
 from typing import Optional, Tuple
 
-__all__ = ["ATTN_F16", "ATTN_BF16", "AttnError", "attn_fwd", "attn_fwd_validate",
+__all__ = ["ATTN_F16", "ATTN_BF16", "ATTN_F32", "AttnError", "attn_fwd", "attn_fwd_validate",
            "attn_fwd_strided", "attn_fwd_strided_validate", "attn_fwd_masked",
            "attn_fwd_masked_validate", "attn_bwd", "attn_bwd_validate", "attention",
            "backward", "attn_status_string",
@@ -29,6 +29,7 @@ __all__ = ["ATTN_F16", "ATTN_BF16", "AttnError", "attn_fwd", "attn_fwd_validate"
 
 ATTN_F16 = 0
 ATTN_BF16 = 1
+ATTN_F32 = 2
 
 ATTN_OK = 0
 ATTN_ERR_NULL = -1
@@ -208,7 +209,9 @@ def _dtype_code(t) -> int:
         return ATTN_BF16
     if t.dtype == torch.float16:
         return ATTN_F16
-    raise TypeError("q/k/v must be float16 or bfloat16, got %s" % t.dtype)
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    raise TypeError("q/k/v must be float16, bfloat16 or float32, got %s" % t.dtype)
 
 
 def forward(q, k, v, causal: bool, valid_len=None, scale: Optional[float] = None, out=None,

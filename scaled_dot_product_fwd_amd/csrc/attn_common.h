@@ -124,4 +124,27 @@ struct Frag {
   uint32_t vaddr[D / 32];   // LDS byte offsets of this lane's V^T fragment for each d-tile u
 };
 
+// fp32 forward (attn_fwd_f32.hip): validated arguments, strides in elements.
+struct F32Params {
+  const float* q;
+  const float* k;
+  const float* v;
+  float* o;
+  float* lse;
+  const int32_t* valid_len;
+  int B, Hq, Hkv, N;
+  int group;         // Hq / Hkv
+  int nqt;           // ceil(N / kBM)
+  int xcd_order;     // 1: KV heads divide evenly over the 8 XCDs
+  int64_t qs_b, qs_h, qs_n;
+  int64_t ks_b, ks_h, ks_n;
+  int64_t vs_b, vs_h, vs_n;
+  int64_t os_b, os_h, os_n;
+  float c;           // |scale| * log2(e) (1 when scale == 0)
+  float qmul;        // sign of scale, 0 when scale == 0: multiplies Q (exact)
+};
+
+// Queue the fp32 forward for D in {32, 64, 128}.
+hipError_t launch_fwd_f32(const F32Params& p, int D, bool causal, hipStream_t stream);
+
 }  // namespace attn_detail

@@ -665,9 +665,9 @@ struct Layout {
   const void* ptr;
   int64_t sb, sh, sn;
   int64_t H;
-  // Bytes from ptr to the end of the last row.
-  int64_t span(int B, int N, int D) const {
-    return ((B - 1) * sb + (H - 1) * sh + (int64_t)(N - 1) * sn + D) * 2;
+  // Bytes from ptr to the end of the last row (elements of es bytes).
+  int64_t span(int B, int N, int D, int es) const {
+    return ((B - 1) * sb + (H - 1) * sh + (int64_t)(N - 1) * sn + D) * es;
   }
 };
 
@@ -680,12 +680,13 @@ Layout strided(const void* ptr, const int64_t* st, int H, int N, int D) {
   return Layout{ptr, st[0], st[1], st[2], H};
 }
 
-// 16-byte aligned base, non-negative strides that are multiples of 8 elements, rows of at least
+// 16-byte aligned base, non-negative strides that are multiples of 16 bytes, rows of at least
 // D elements apart.
-bool layout_ok(const Layout& t, int D) {
+bool layout_ok(const Layout& t, int D, int es) {
+  const int64_t g = 16 / es;   // elements per 16 bytes
   if ((uintptr_t)t.ptr % 16 != 0) return false;
   if (t.sb < 0 || t.sh < 0 || t.sn < 0) return false;
-  if (t.sb % 8 || t.sh % 8 || t.sn % 8) return false;
+  if (t.sb % g || t.sh % g || t.sn % g) return false;
   return t.sn >= D;
 }
 
@@ -722,18 +723,22 @@ int validate(const Layout& q, const Layout& k, const Layout& v, const Layout& o,
   if (N > ATTN_MAX_N) return ATTN_ERR_SHAPE;
   const int64_t ntiles = (int64_t)B * Hq * (((int64_t)N + kBM - 1) / kBM);
   if (ntiles > ATTN_MAX_TILES) return ATTN_ERR_SHAPE;
-  if (D != 16 && D != 32 && D != 64 && D != 128 && D != 256) return ATTN_ERR_HEAD_DIM;
-  if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+  if (dtype != ATTN_F16 && dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_DTYPE;
+  if (dtype == ATTN_F32 && mk.type != ATTN_MASK_NONE) return ATTN_ERR_DTYPE;
+  if (dtype == ATTN_F32 ? (D != 32 && D != 64 && D != 128)
+                        : (D != 16 && D != 32 && D != 64 && D != 128 && D != 256))
+    return ATTN_ERR_HEAD_DIM;
   if (!isfinite(scale)) return ATTN_ERR_SCALE;
-  if (!layout_ok(q, D) || !layout_ok(k, D) || !layout_ok(v, D) || !layout_ok(o, D))
+  const int es = dtype == ATTN_F32 ? 4 : 2;
+  if (!layout_ok(q, D, es) || !layout_ok(k, D, es) || !layout_ok(v, D, es) || !layout_ok(o, D, es))
     return ATTN_ERR_LAYOUT;
   if (!output_disjoint(o, B, Hq, N, D)) return ATTN_ERR_LAYOUT;
   // K and V of one head are read as 32-bit-addressed buffers, including up to one tile of rows
   // past N.
-  const int64_t kv_reach = ((int64_t)N + kBN) * std::max(k.sn, v.sn) * 2 + 2 * D;
+  const int64_t kv_reach = ((int64_t)N + kBN) * std::max(k.sn, v.sn) * es + es * D;
   if (kv_reach > INT32_MAX) return ATTN_ERR_SHAPE;
-  const int64_t qbytes = q.span(B, N, D), kbytes = k.span(B, N, D), vbytes = v.span(B, N, D);
-  const int64_t obytes = o.span(B, N, D);
+  const int64_t qbytes = q.span(B, N, D, es), kbytes = k.span(B, N, D, es);
+  const int64_t vbytes = v.span(B, N, D, es), obytes = o.span(B, N, D, es);
   const int64_t lbytes = (int64_t)B * Hq * N * 4;
   if (overlaps(o.ptr, obytes, q.ptr, qbytes) || overlaps(o.ptr, obytes, k.ptr, kbytes) ||
       overlaps(o.ptr, obytes, v.ptr, vbytes))
@@ -747,15 +752,15 @@ int validate(const Layout& q, const Layout& k, const Layout& v, const Layout& o,
   if (mk.type != ATTN_MASK_NONE) {
     if (mk.type != ATTN_MASK_KEEP_U8 && mk.type != ATTN_MASK_ADD) return ATTN_ERR_MASK;
     if (!mk.ptr) return ATTN_ERR_NULL;
-    const int64_t es = mk.type == ATTN_MASK_KEEP_U8 ? 1 : 2;
+    const int64_t mes = mk.type == ATTN_MASK_KEEP_U8 ? 1 : 2;
     if ((uintptr_t)mk.ptr % 16 != 0 || mk.sb < 0 || mk.sh < 0 || mk.sn < N ||
-        (mk.sb * es) % 16 || (mk.sh * es) % 16 || (mk.sn * es) % 16)
+        (mk.sb * mes) % 16 || (mk.sh * mes) % 16 || (mk.sn * mes) % 16)
       return ATTN_ERR_LAYOUT;
     // A wave's DMA addresses rows up to 127 past its first inside one 32-bit buffer.
-    if (((int64_t)N + kBM) * mk.sn * es > INT32_MAX) return ATTN_ERR_SHAPE;
+    if (((int64_t)N + kBM) * mk.sn * mes > INT32_MAX) return ATTN_ERR_SHAPE;
     // Rows are read in 16-byte units: the last row up to its next 16-byte boundary.
     const int64_t mbytes =
-        ((B - 1) * mk.sb + (Hq - 1) * mk.sh + (int64_t)(N - 1) * mk.sn) * es + ((N * es + 15) & ~15);
+        ((B - 1) * mk.sb + (Hq - 1) * mk.sh + (int64_t)(N - 1) * mk.sn) * mes + ((N * mes + 15) & ~15);
     if (overlaps(o.ptr, obytes, mk.ptr, mbytes) || (lse && overlaps(lse, lbytes, mk.ptr, mbytes)))
       return ATTN_ERR_ALIAS;
   }
@@ -767,6 +772,30 @@ int run(const Layout& q, const Layout& k, const Layout& v, const Layout& o, floa
         int dtype, void* stream, const MaskArg& mk = no_mask()) {
   const int st = validate(q, k, v, o, lse, B, Hq, Hkv, N, D, scale, valid_len, dtype, mk);
   if (st != ATTN_OK) return st;
+  if (dtype == ATTN_F32) {
+    F32Params f;
+    f.q = (const float*)q.ptr;
+    f.k = (const float*)k.ptr;
+    f.v = (const float*)v.ptr;
+    f.o = (float*)o.ptr;
+    f.lse = lse;
+    f.valid_len = valid_len;
+    f.B = B;
+    f.Hq = Hq;
+    f.Hkv = Hkv;
+    f.N = N;
+    f.group = Hq / Hkv;
+    f.nqt = (N + kBM - 1) / kBM;
+    f.xcd_order = ((int64_t)B * Hkv) % 8 == 0 ? 1 : 0;
+    f.qs_b = q.sb; f.qs_h = q.sh; f.qs_n = q.sn;
+    f.ks_b = k.sb; f.ks_h = k.sh; f.ks_n = k.sn;
+    f.vs_b = v.sb; f.vs_h = v.sh; f.vs_n = v.sn;
+    f.os_b = o.sb; f.os_h = o.sh; f.os_n = o.sn;
+    f.c = scale == 0.f ? 1.0f : fabsf(scale) * kLog2e;
+    f.qmul = scale < 0.f ? -1.0f : (scale == 0.f ? 0.0f : 1.0f);
+    const hipError_t e = launch_fwd_f32(f, D, causal != 0, (hipStream_t)stream);
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+  }
   Params p;
   p.q = (const uint16_t*)q.ptr;
   p.k = (const uint16_t*)k.ptr;

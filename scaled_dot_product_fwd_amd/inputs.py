@@ -11,7 +11,8 @@ Recipe (one rule for every workload):
     optional standard deviation;
   * for padded workloads, then draw ``valid_len`` as ``integers(1, N + 1, size=B)`` (uniform in
     [1, N]) and set ``valid_len[0] = 0`` so that batch 0 has fully masked rows;
-  * round each float32 value to the nearest 16-bit value (ties to even) of the workload's type;
+  * round each float32 value to the nearest 16-bit value (ties to even) of the workload's type
+    (fp32 cases keep the float32 draws as they are);
   * for the backward pass, the upstream gradient dO comes from its own generator
     ``default_rng([21, *seed])`` (``make_grad``), also iid N(0, 1) rounded to the same type.
 The device receives the 16-bit bit patterns; the oracle receives the same values widened
@@ -24,7 +25,7 @@ from typing import Dict, Optional
 
 import numpy as np
 
-DTYPES = ("f16", "bf16")
+DTYPES = ("f16", "bf16", "f32")
 
 
 def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -43,15 +44,20 @@ def round_to_f16_bits(x: np.ndarray) -> np.ndarray:
 
 
 def round_bits(x: np.ndarray, dtype: str) -> np.ndarray:
+    """float32 values -> bit patterns of `dtype` (uint16, or uint32 for f32, which is exact)."""
     if dtype == "bf16":
         return round_to_bf16_bits(x)
     if dtype == "f16":
         return round_to_f16_bits(x)
+    if dtype == "f32":
+        return np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
     raise ValueError("dtype must be one of %s" % (DTYPES,))
 
 
 def widen(bits: np.ndarray, dtype: str) -> np.ndarray:
-    """16-bit patterns -> exact float64 values."""
+    """Bit patterns of `dtype` -> exact float64 values."""
+    if dtype == "f32":
+        return np.ascontiguousarray(bits, dtype=np.uint32).view(np.float32).astype(np.float64)
     bits = np.ascontiguousarray(bits, dtype=np.uint16)
     if dtype == "bf16":
         return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
@@ -108,9 +114,9 @@ class Case:
     dtype: str
     causal: bool
     scale: float
-    q_bits: np.ndarray            # uint16 [B,Hq,N,D]
-    k_bits: np.ndarray            # uint16 [B,Hkv,N,D]
-    v_bits: np.ndarray            # uint16 [B,Hkv,N,D]
+    q_bits: np.ndarray            # uint16 [B,Hq,N,D] (uint32 for f32)
+    k_bits: np.ndarray            # uint16 [B,Hkv,N,D] (uint32 for f32)
+    v_bits: np.ndarray            # uint16 [B,Hkv,N,D] (uint32 for f32)
     valid_len: Optional[np.ndarray]  # int32 [B] or None
 
     def widened(self):

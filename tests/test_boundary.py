@@ -80,6 +80,8 @@ def test_validate_accepts_good_arguments(lib):
     assert call(D=16) == sdp.ATTN_OK
     assert call(D=32, dtype=sdp.ATTN_F16) == sdp.ATTN_OK
     assert call(D=256) == sdp.ATTN_OK
+    for d in (32, 64, 128):
+        assert call(D=d, dtype=sdp.ATTN_F32) == sdp.ATTN_OK
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -98,7 +100,9 @@ def test_validate_accepts_good_arguments(lib):
     (dict(D=512), sdp.ATTN_ERR_HEAD_DIM),
     (dict(D=48), sdp.ATTN_ERR_HEAD_DIM),
     (dict(D=8), sdp.ATTN_ERR_HEAD_DIM),
-    (dict(dtype=2), sdp.ATTN_ERR_DTYPE),
+    (dict(dtype=3), sdp.ATTN_ERR_DTYPE),
+    (dict(dtype=sdp.ATTN_F32, D=16), sdp.ATTN_ERR_HEAD_DIM),
+    (dict(dtype=sdp.ATTN_F32, D=256), sdp.ATTN_ERR_HEAD_DIM),
     (dict(dtype=-1), sdp.ATTN_ERR_DTYPE),
     (dict(scale=float("nan")), sdp.ATTN_ERR_SCALE),
     (dict(scale=float("inf")), sdp.ATTN_ERR_SCALE),
@@ -272,3 +276,20 @@ def test_bwd_validate_accepts(lib):
 ])
 def test_bwd_validate_rejects(lib, kw, code):
     assert bcall(**kw) == code
+
+
+def test_f32_layouts(lib):
+    """fp32 rows: strides in multiples of 4 elements (16 bytes), spans of 4-byte elements."""
+    f32 = sdp.ATTN_F32
+    assert scall(dtype=f32, qs=(8 * SN * 132, SN * 132, 132)) == sdp.ATTN_OK
+    assert scall(dtype=f32, qs=(8 * SN * 130, SN * 130, 130)) == sdp.ATTN_ERR_LAYOUT
+    # a 16-bit stride of 136 elements is fine, 132 is not a multiple of 8
+    assert scall(qs=(8 * SN * 132, SN * 132, 132)) == sdp.ATTN_ERR_LAYOUT
+    # out placed right after a 16-bit-sized q overlaps q once elements are 4 bytes
+    qbytes16 = 2 * 8 * 1000 * 128 * 2
+    assert call(out=Q + qbytes16) == sdp.ATTN_OK
+    assert call(out=Q + qbytes16, dtype=f32) == sdp.ATTN_ERR_ALIAS
+    # explicit masks are 16-bit only
+    assert sdp.attn_fwd_masked_validate(Q, None, K, None, V, None, O, None, L, SB, SH, 2, MN, 128,
+                                        0.088, 1, VL, MK, sdp.ATTN_MASK_KEEP_U8, None,
+                                        f32) == sdp.ATTN_ERR_DTYPE

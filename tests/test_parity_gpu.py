@@ -74,6 +74,62 @@ def test_small_head_dims(cfg):
     compare(case, O, L, O_ref, L_ref, tag=str(cfg))
 
 
+# fp32 inputs (fp32 products on the fp32 matrix cores): head dims 32 / 64 / 128, ragged N,
+# GQA / MQA, causal and padded, a grid larger than the resident workgroups, every row compared.
+SMALL_F32 = [
+    (32, False, False, 1, 2, 2, 128),
+    (64, True, True, 3, 4, 2, 257),
+    (128, True, False, 2, 8, 2, 333),
+    (128, False, True, 2, 4, 1, 1000),
+    (64, False, False, 1, 1, 1, 1),
+    (32, True, True, 2, 6, 3, 300),
+    (128, True, True, 4, 16, 4, 1100),
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL_F32, ids=lambda c: "f32-D%d-c%d-p%d-B%d-H%d-%d-N%d" % c)
+def test_f32_inputs(cfg):
+    D, causal, padded, B, Hq, Hkv, N = cfg
+    case = inputs.make_case(B, Hq, Hkv, N, D, "f32", causal, padded, seed=[117, D, N, B])
+    log("f32 case %s valid_len %s" % (cfg, case.valid_len))
+    O, L = run_device(case)
+    O_ref, L_ref = run_oracle(case)
+    compare(case, O, L, O_ref, L_ref, tag="f32 " + str(cfg))
+
+
+@pytest.mark.parametrize("scale", [-0.125, 0.0, 2.0])
+def test_f32_scale_values(scale):
+    case = inputs.make_case(1, 4, 2, 257, 64, "f32", True, True, seed=[119, 1], scale=scale,
+                            valid_len=np.array([250], np.int32))
+    O, L = run_device(case)
+    O_ref, L_ref = run_oracle(case)
+    compare(case, O, L, O_ref, L_ref, tag="f32 scale=%g" % scale)
+
+
+def test_f32_rising_row_maximum():
+    case = inputs.make_case(1, 2, 2, 1024, 128, "f32", False, False, seed=121)
+    k = inputs.widen(case.k_bits, "f32")
+    k *= (1.0 + 12.0 * np.arange(case.N) / case.N)[None, None, :, None]
+    case.k_bits = inputs.round_bits(k.astype(np.float32), "f32")
+    for causal in (False, True):
+        case.causal = causal
+        O, L = run_device(case)
+        O_ref, L_ref = run_oracle(case)
+        compare(case, O, L, O_ref, L_ref, tag="f32 rising causal=%d" % causal)
+
+
+def test_f32_headline_shape_sampled():
+    """The headline shape (B=8, Hq=32, Hkv=8, N=4096, D=128, causal) in fp32, sampled rows."""
+    w = inputs.WORKLOADS["long_gqa"]
+    case = inputs.make_case(w.B, w.Hq, w.Hkv, w.N, w.D, "f32", w.causal, w.padded,
+                            seed=[20, w.c], scale=w.scale)
+    rows = sample_rows(case, per_head=12, seed=w.c)
+    log("f32 long_gqa (%d sampled rows)" % len(rows))
+    O, L = run_device(case)
+    O_ref, L_ref = run_oracle(case, rows=rows)
+    compare(case, O, L, O_ref, L_ref, rows=rows, tag="f32 long_gqa")
+
+
 # More 128-query tiles (B * Hq * ceil(N / 128)) than the 512 workgroups the device holds at
 # once, every row compared: the XCD-grouped workgroup order (B * Hkv % 8 == 0) and the plain
 # one, padding with an empty batch (a tile with no visible key), odd and even tile counts.
@@ -244,6 +300,9 @@ STRIDED = [
     ("packed_qkv", "bf16", 16, True, False, 1, 4, 4, 100),
     ("bnhd", "f16", 256, True, False, 2, 4, 2, 300),
     ("padded_rows", "bf16", 256, False, True, 2, 2, 1, 130),
+    ("bnhd", "f32", 128, True, True, 2, 4, 2, 200),
+    ("padded_rows", "f32", 64, False, False, 2, 4, 1, 150),
+    ("packed_qkv", "f32", 32, True, False, 1, 4, 4, 100),
 ]
 
 
