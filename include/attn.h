@@ -49,7 +49,7 @@ extern "C" {
 typedef enum {
     ATTN_F16 = 0,  /* IEEE binary16 */
     ATTN_BF16 = 1, /* bfloat16 */
-    ATTN_F32 = 2   /* IEEE binary32: attn_fwd and attn_fwd_strided only, D in {32, 64, 128} */
+    ATTN_F32 = 2   /* IEEE binary32: attn_fwd and attn_fwd_strided only */
 } attn_dtype_t;
 
 /* Return codes. Argument errors are detected on the host before anything is launched. */
@@ -96,8 +96,8 @@ typedef enum {
  *   lse        device pointer to [B, Hq, N] float32, contiguous; NULL means "do not write".
  *   B, Hq, Hkv, N, D
  *              batch, query heads, key/value heads, sequence length (queries and keys share it),
- *              head dimension. Any N >= 1 is accepted; D must be 16, 32, 64, 128 or 256 for
- *              16-bit types, 32, 64 or 128 for ATTN_F32 (attn_bwd: 64 or 128).
+ *              head dimension. Any N >= 1 is accepted; D must be 16, 32, 64, 128 or 256
+ *              (attn_bwd: 64 or 128).
  *   scale      multiplier of the dot products (typically 1/sqrt(D)); any finite value.
  *   causal     nonzero hides key j from query i when j > i.
  *   valid_len  device pointer to int32[B], or NULL for no padding mask. Keys j >= valid_len[b]

@@ -144,7 +144,7 @@ struct F32Params {
   float qmul;        // sign of scale, 0 when scale == 0: multiplies Q (exact)
 };
 
-// Queue the fp32 forward for D in {32, 64, 128}.
+// Queue the fp32 forward for D in {16, 32, 64, 128, 256}.
 hipError_t launch_fwd_f32(const F32Params& p, int D, bool causal, hipStream_t stream);
 
 }  // namespace attn_detail

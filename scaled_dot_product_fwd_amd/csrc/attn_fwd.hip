@@ -725,9 +725,7 @@ int validate(const Layout& q, const Layout& k, const Layout& v, const Layout& o,
   if (ntiles > ATTN_MAX_TILES) return ATTN_ERR_SHAPE;
   if (dtype != ATTN_F16 && dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_DTYPE;
   if (dtype == ATTN_F32 && mk.type != ATTN_MASK_NONE) return ATTN_ERR_DTYPE;
-  if (dtype == ATTN_F32 ? (D != 32 && D != 64 && D != 128)
-                        : (D != 16 && D != 32 && D != 64 && D != 128 && D != 256))
-    return ATTN_ERR_HEAD_DIM;
+  if (D != 16 && D != 32 && D != 64 && D != 128 && D != 256) return ATTN_ERR_HEAD_DIM;
   if (!isfinite(scale)) return ATTN_ERR_SCALE;
   const int es = dtype == ATTN_F32 ? 4 : 2;
   if (!layout_ok(q, D, es) || !layout_ok(k, D, es) || !layout_ok(v, D, es) || !layout_ok(o, D, es))

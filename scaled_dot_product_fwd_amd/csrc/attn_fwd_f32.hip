@@ -56,8 +56,12 @@ __device__ inline f32x16 mfma_f32(float a, float b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
-template <int D, bool CAUSAL>
+// DH is the tensors' head dimension; DH = 16 runs the D = 32 geometry with the missing 16-byte
+// chunks of every row zero-filled (their DMA lanes fetch out of range) and never stored.
+template <int DH, bool CAUSAL>
 __device__ __forceinline__ void fwd_f32_body(const F32Params& p) {
+  constexpr int D = DH < 32 ? 32 : DH;   // geometry
+  constexpr int DCH = DH / 4;            // 16-byte chunks of a row that exist
   using G = G32<D>;
   constexpr int QT = G::QT;
   constexpr int OT = G::OT;
@@ -103,19 +107,21 @@ __device__ __forceinline__ void fwd_f32_body(const F32Params& p) {
   // K and V of this (batch, KV head) as buffers spanning its N rows (rows past N read as 0).
   const uint32_t krow = (uint32_t)p.ks_n * 4, vrow = (uint32_t)p.vs_n * 4;
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.k + b * p.ks_b + kvh * p.ks_h), (short)0, (p.N - 1) * krow + G::ROW,
+      (void*)(p.k + b * p.ks_b + kvh * p.ks_h), (short)0, (p.N - 1) * krow + 4 * DH,
       kBufferFlags);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.v + b * p.vs_b + kvh * p.vs_h), (short)0, (p.N - 1) * vrow + G::ROW,
+      (void*)(p.v + b * p.vs_b + kvh * p.vs_h), (short)0, (p.N - 1) * vrow + 4 * DH,
       kBufferFlags);
+  constexpr uint32_t kNoChunk = 0x80000000u;   // past every buffer (spans stay below 2^31)
   // Block (wave * LOADS + i) of a tile holds rows [blk * RPB, +RPB); the lane writes LDS chunk
   // (lane % CH) of row (lane / CH) and fetches the global chunk its row's swizzle maps there.
   uint32_t koff[G::LOADS], voff[G::LOADS];
 #pragma unroll
   for (int i = 0; i < G::LOADS; ++i) {
     const int row = (wave * G::LOADS + i) * G::RPB + lane / G::CH;
-    koff[i] = row * krow + (((lane % G::CH) ^ G::kswz(row)) * 16);
-    voff[i] = row * vrow + (((lane % G::CH) ^ G::vswz(row)) * 16);
+    const int kc = (lane % G::CH) ^ G::kswz(row), vc = (lane % G::CH) ^ G::vswz(row);
+    koff[i] = (DCH < G::CH && kc >= DCH) ? kNoChunk : row * krow + kc * 16;
+    voff[i] = (DCH < G::CH && vc >= DCH) ? kNoChunk : row * vrow + vc * 16;
   }
   auto dma = [&](int tile, int kdst, int vdst) {
     const uint32_t row0 = (uint32_t)tile * kKT;
@@ -136,7 +142,7 @@ __device__ __forceinline__ void fwd_f32_body(const F32Params& p) {
   f32x4 qf[QT];
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
-    const f32x4 x = *(const f32x4*)(qsrc + 8 * t);
+    const f32x4 x = (DCH < G::CH && 2 * t + h >= DCH) ? f32x4{} : *(const f32x4*)(qsrc + 8 * t);
 #pragma unroll
     for (int e = 0; e < 4; ++e) qf[t][e] = x[e] * p.qmul;
   }
@@ -218,6 +224,7 @@ __device__ __forceinline__ void fwd_f32_body(const F32Params& p) {
     for (int u = 0; u < OT; ++u)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
+        if (32 * u + 8 * r4 + 4 * h >= DH) continue;   // chunks past DH do not exist
         f32x4 w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) w[e] = acc[u][4 * r4 + e] * inv;
@@ -228,8 +235,11 @@ __device__ __forceinline__ void fwd_f32_body(const F32Params& p) {
   }
 }
 
+// D = 256 holds 128 KiB of tiles in LDS (one workgroup per CU): one wave per SIMD, with the
+// whole register file for its 128 Q and 128 accumulator registers.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(D > 128 ? 1 : 2, D > 128 ? 1 : 2)))
 void attn_fwd_f32_kernel(F32Params p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   fwd_f32_body<D, CAUSAL>(p);
@@ -248,7 +258,9 @@ hipError_t launch_d(const F32Params& p, hipStream_t s) {
 
 hipError_t launch_fwd_f32(const F32Params& p, int D, bool causal, hipStream_t s) {
   switch (D) {
+    case 16: return causal ? launch_d<16, true>(p, s) : launch_d<16, false>(p, s);
     case 32: return causal ? launch_d<32, true>(p, s) : launch_d<32, false>(p, s);
+    case 256: return causal ? launch_d<256, true>(p, s) : launch_d<256, false>(p, s);
     case 64: return causal ? launch_d<64, true>(p, s) : launch_d<64, false>(p, s);
     default: return causal ? launch_d<128, true>(p, s) : launch_d<128, false>(p, s);
   }

@@ -74,7 +74,7 @@ def test_small_head_dims(cfg):
     compare(case, O, L, O_ref, L_ref, tag=str(cfg))
 
 
-# fp32 inputs (fp32 products on the fp32 matrix cores): head dims 32 / 64 / 128, ragged N,
+# fp32 inputs (fp32 products on the fp32 matrix cores): head dims 16 ... 256, ragged N,
 # GQA / MQA, causal and padded, a grid larger than the resident workgroups, every row compared.
 SMALL_F32 = [
     (32, False, False, 1, 2, 2, 128),
@@ -84,6 +84,11 @@ SMALL_F32 = [
     (64, False, False, 1, 1, 1, 1),
     (32, True, True, 2, 6, 3, 300),
     (128, True, True, 4, 16, 4, 1100),
+    (16, True, True, 3, 4, 2, 257),
+    (16, False, False, 2, 8, 1, 1000),
+    (256, True, False, 2, 4, 2, 333),
+    (256, False, True, 2, 6, 3, 200),
+    (256, True, True, 1, 2, 1, 1),
 ]
 
 
@@ -303,6 +308,8 @@ STRIDED = [
     ("bnhd", "f32", 128, True, True, 2, 4, 2, 200),
     ("padded_rows", "f32", 64, False, False, 2, 4, 1, 150),
     ("packed_qkv", "f32", 32, True, False, 1, 4, 4, 100),
+    ("bnhd", "f32", 256, False, True, 2, 2, 1, 130),
+    ("padded_rows", "f32", 16, True, False, 2, 4, 2, 90),
 ]
 
 
