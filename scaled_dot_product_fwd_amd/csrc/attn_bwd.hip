@@ -43,6 +43,9 @@ namespace {
 using namespace attn_detail;
 
 constexpr int kQT = 32;   // queries per iteration of the dK/dV kernel
+// DMA voffset of a lane whose row chunk does not exist (head dims below 64): past every buffer
+// (each spans at most N * 2 * DH < 2^31 bytes), so the range check writes zeros to LDS.
+constexpr uint32_t kNoChunk = 0x80000000u;
 
 typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 
@@ -85,9 +88,10 @@ __device__ inline u32x4 pack8(const float (&x)[16], int s) {
 }
 
 // Write a wave's 32 x D block, held transposed in acc (acc[u][4 r4 + e] is element
-// d = 32u + 8 r4 + 4h + e of row ql), as rows of `dst` (row stride D) through the wave's LDS
-// staging area `ost` (32 * ROW bytes). Rows at or past n are not written.
-template <int DT, int D>
+// d = 32u + 8 r4 + 4h + e of row ql), as rows of `dst` (row stride DH <= D: the 16-byte chunks
+// past DH are not written) through the wave's LDS staging area `ost` (32 * ROW bytes). Rows at
+// or past n are not written.
+template <int DT, int D, int DH = D>
 __device__ inline void store_rows(const f32x16 (&acc)[Geo<D>::OT], float mul,
                                   unsigned char* ost, uint16_t* dst, int row0, int n, int lane) {
   using G = Geo<D>;
@@ -111,7 +115,7 @@ __device__ inline void store_rows(const f32x16 (&acc)[Geo<D>::OT], float mul,
     const int r = i * RPI + lane / G::CH;
     const int cc = lane % G::CH;
     const u32x4 v = *(const u32x4*)(ost + r * G::ROW + 16 * (cc ^ (r & (G::CH - 1))));
-    if (row0 + r < n) *(u32x4*)(dst + (size_t)(row0 + r) * D + 8 * cc) = v;
+    if (row0 + r < n && (DH == D || cc < DH / 8)) *(u32x4*)(dst + (size_t)(row0 + r) * DH + 8 * cc) = v;
   }
 }
 
@@ -139,8 +143,14 @@ __device__ inline u32x4 tr_frag(const unsigned char* tile, uint32_t off, int row
 // ------------------------------------------------------------------------------------------
 // dQ (and D)
 // ------------------------------------------------------------------------------------------
-template <int DT, int D, bool CAUSAL>
+// DH is the tensors' head dimension; DH < 64 runs the D = 64 geometry with the missing 16-byte
+// chunks of every row zero (out-of-range DMA lanes, zero registers) and never stored. The
+// tensors are contiguous, so their row stride RS (bytes) is known at compile time.
+template <int DT, int DH, bool CAUSAL>
 __device__ __forceinline__ void bwd_dq_body(const BwdParams& p) {
+  constexpr int D = DH < 64 ? 64 : DH;
+  constexpr int DCH = DH / 8;
+  constexpr int RS = 2 * DH;
   using G = Geo<D>;
   using M = Mfma<DT>;
   constexpr int KSTEPS = G::KSTEPS;
@@ -191,8 +201,8 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p) {
   const int qrow = qa + ql;
   const int qr = min(qrow, p.N - 1);
 
-  const size_t kv_off = (size_t)(b * p.Hkv + kvh) * p.N * D;
-  const uint32_t head_bytes = (uint32_t)p.N * G::ROW;
+  const size_t kv_off = (size_t)(b * p.Hkv + kvh) * p.N * DH;
+  const uint32_t head_bytes = (uint32_t)p.N * RS;
   const __amdgpu_buffer_rsrc_t krs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + kv_off), (short)0, head_bytes, kBufferFlags);
   const __amdgpu_buffer_rsrc_t vrs =
@@ -201,11 +211,12 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p) {
 #pragma unroll
   for (int i = 0; i < G::LOADS; ++i) {
     const int r = (wave * G::LOADS + i) * G::RPB + lane / G::CH;
-    kdma[i] = r * G::ROW + (((lane % G::CH) ^ G::bswz(r)) * 16);
-    vdma[i] = r * G::ROW + (((lane % G::CH) ^ G::kswz(r)) * 16);
+    const int kc = (lane % G::CH) ^ G::bswz(r), vc = (lane % G::CH) ^ G::kswz(r);
+    kdma[i] = (DCH < G::CH && kc >= DCH) ? kNoChunk : r * RS + kc * 16;
+    vdma[i] = (DCH < G::CH && vc >= DCH) ? kNoChunk : r * RS + vc * 16;
   }
   auto dma = [&](int tile, int kdst, int vdst) {
-    const int soff = tile * G::TILE;
+    const int soff = tile * kBN * RS;
 #pragma unroll
     for (int i = 0; i < G::LOADS; ++i) {
       const int blk = (wave * G::LOADS + i) * 1024;
@@ -229,13 +240,14 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p) {
   if (ntiles > 0) dma(0, G::K0, G::V0);
 
   // Q, dO and O of this lane's row (B-operand layout: Q[row][16s + 8h .. +7]).
-  const size_t rowoff = ((size_t)bh * p.N + qr) * D + 8 * h;
+  const size_t rowoff = ((size_t)bh * p.N + qr) * DH + 8 * h;
   u32x4 qf[KSTEPS], dof[KSTEPS], of[KSTEPS];
 #pragma unroll
   for (int s = 0; s < KSTEPS; ++s) {
-    qf[s] = *(const u32x4*)(p.q + rowoff + 16 * s);
-    dof[s] = *(const u32x4*)(p.dout + rowoff + 16 * s);
-    of[s] = *(const u32x4*)(p.o + rowoff + 16 * s);
+    const bool ok = DCH == G::CH || 2 * s + h < DCH;
+    qf[s] = ok ? *(const u32x4*)(p.q + rowoff + 16 * s) : u32x4{};
+    dof[s] = ok ? *(const u32x4*)(p.dout + rowoff + 16 * s) : u32x4{};
+    of[s] = ok ? *(const u32x4*)(p.o + rowoff + 16 * s) : u32x4{};
   }
   const float L = lse_log2(p.lse[(size_t)bh * p.N + qr]);
   // D = rowsum(dO o O): this lane's half of the row, then the lane pair.
@@ -328,8 +340,8 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p) {
   // dQ = scale * (dQ^T)^T, staged through LDS after every wave is done with the tiles.
   wait_loads_and_lds();
   __syncthreads();
-  store_rows<DT, D>(acc, p.scale, smem + wave * 32 * G::ROW, p.dq + (size_t)bh * p.N * D, qa,
-                    p.N, lane);
+  store_rows<DT, D, DH>(acc, p.scale, smem + wave * 32 * G::ROW, p.dq + (size_t)bh * p.N * DH,
+                        qa, p.N, lane);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -350,8 +362,11 @@ struct BwdGeo {
   static_assert(BUF + QTILE + 24 * G::ROW <= 65535, "LDS offsets fit the immediate field");
 };
 
-template <int DT, int D, bool CAUSAL>
+template <int DT, int DH, bool CAUSAL>
 __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
+  constexpr int D = DH < 64 ? 64 : DH;   // geometry (as in the dQ kernel)
+  constexpr int DCH = DH / 8;
+  constexpr int RS = 2 * DH;
   using G = Geo<D>;
   using BG = BwdGeo<D>;
   using M = Mfma<DT>;
@@ -397,7 +412,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
   const int key = kw + ql;         // this lane's key (MFMA output column)
   int kv_end = p.N;
   if (p.valid_len) kv_end = min(max(p.valid_len[b], 0), p.N);
-  const size_t kv_off = (size_t)(b * p.Hkv + kvh) * p.N * D;
+  const size_t kv_off = (size_t)(b * p.Hkv + kvh) * p.N * DH;
   unsigned char* vreg = smem + BG::VREG + wave * 32 * G::ROW;   // this wave's 32 V rows
 
   f32x16 dk[OT], dv[OT];
@@ -412,21 +427,26 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
     // K^T fragments of this lane's key (B operand: K[key][16s + 8h .. +7]), sign/zero applied.
     u32x4 kf[KSTEPS];
     {
-      const uint16_t* ksrc = p.k + kv_off + (size_t)min(key, p.N - 1) * D + 8 * h;
+      const uint16_t* ksrc = p.k + kv_off + (size_t)min(key, p.N - 1) * DH + 8 * h;
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) kf[s] = (*(const u32x4*)(ksrc + 16 * s) ^ p.qsign) & p.qmask;
+      for (int s = 0; s < KSTEPS; ++s)
+        kf[s] = (DCH == G::CH || 2 * s + h < DCH)
+                    ? (*(const u32x4*)(ksrc + 16 * s) ^ p.qsign) & p.qmask
+                    : u32x4{};
     }
     // V rows of this wave's keys into its LDS rows (bswz layout like Q and dO, so that one set
     // of row-fragment offsets serves all three).
     {
       const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(p.v + kv_off), (short)0, (uint32_t)p.N * G::ROW, kBufferFlags);
+          (void*)(p.v + kv_off), (short)0, (uint32_t)p.N * RS, kBufferFlags);
 #pragma unroll
       for (int i = 0; i < 32 / G::RPB; ++i) {
         const int row = i * G::RPB + lane / G::CH;
-        const uint32_t off = (lane / G::CH) * G::ROW + (((lane % G::CH) ^ G::bswz(row)) * 16);
+        const int vc = (lane % G::CH) ^ G::bswz(row);
+        const uint32_t off =
+            (DCH < G::CH && vc >= DCH) ? kNoChunk : (lane / G::CH) * RS + vc * 16;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(vreg + i * 1024), 16, off,
-                                                 (uint32_t)(kw + i * G::RPB) * G::ROW, 0, 0);
+                                                 (uint32_t)(kw + i * G::RPB) * RS, 0, 0);
       }
     }
     // DMA of the iteration over query head kvh * group + g, queries q0 .. q0+31, into buffer
@@ -435,20 +455,21 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
 #pragma unroll
     for (int i = 0; i < BG::QLOADS; ++i) {
       const int row = (wave * BG::QLOADS + i) * G::RPB + lane / G::CH;   // row in the tile
-      qoff[i] = (lane / G::CH) * G::ROW + (((lane % G::CH) ^ G::bswz(row)) * 16);
+      const int qc = (lane % G::CH) ^ G::bswz(row);
+      qoff[i] = (DCH < G::CH && qc >= DCH) ? kNoChunk : (lane / G::CH) * RS + qc * 16;
     }
     auto dma = [&](int g, int q0, int buf) {
       const int bh = b * p.Hq + kvh * p.group + g;
-      const size_t hoff = (size_t)bh * p.N * D;
+      const size_t hoff = (size_t)bh * p.N * DH;
       const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(p.q + hoff), (short)0, (uint32_t)p.N * G::ROW, kBufferFlags);
+          (void*)(p.q + hoff), (short)0, (uint32_t)p.N * RS, kBufferFlags);
       const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(p.dout + hoff), (short)0, (uint32_t)p.N * G::ROW, kBufferFlags);
+          (void*)(p.dout + hoff), (short)0, (uint32_t)p.N * RS, kBufferFlags);
       unsigned char* base = smem + buf * BG::BUF;
 #pragma unroll
       for (int i = 0; i < BG::QLOADS; ++i) {
         const int blk = wave * BG::QLOADS + i;
-        const uint32_t soff = (uint32_t)(q0 + blk * G::RPB) * G::ROW;
+        const uint32_t soff = (uint32_t)(q0 + blk * G::RPB) * RS;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void*)(base + blk * 1024), 16,
                                                  qoff[i], soff, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ors, (lds_void*)(base + BG::QTILE + blk * 1024),
@@ -558,8 +579,8 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
   // dK = scale * (dK^T)^T, dV = (dV^T)^T; rows past N are not written. Staging reuses the Q/dO
   // buffers (every wave is past its last read).
   unsigned char* ost = smem + wave * 32 * G::ROW;
-  store_rows<DT, D>(dk, p.scale, ost, p.dk + kv_off, kw, p.N, lane);
-  store_rows<DT, D>(dv, 1.0f, ost, p.dv + kv_off, kw, p.N, lane);
+  store_rows<DT, D, DH>(dk, p.scale, ost, p.dk + kv_off, kw, p.N, lane);
+  store_rows<DT, D, DH>(dv, 1.0f, ost, p.dv + kv_off, kw, p.N, lane);
 }
 
 template <int DT, int D, bool CAUSAL>
@@ -593,6 +614,8 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t s) {
 
 template <int DT>
 hipError_t dispatch_bwd(const BwdParams& p, int D, bool causal, hipStream_t s) {
+  if (D == 16) return causal ? launch_bwd<DT, 16, true>(p, s) : launch_bwd<DT, 16, false>(p, s);
+  if (D == 32) return causal ? launch_bwd<DT, 32, true>(p, s) : launch_bwd<DT, 32, false>(p, s);
   if (D == 64) return causal ? launch_bwd<DT, 64, true>(p, s) : launch_bwd<DT, 64, false>(p, s);
   return causal ? launch_bwd<DT, 128, true>(p, s) : launch_bwd<DT, 128, false>(p, s);
 }
@@ -615,7 +638,7 @@ extern "C" int attn_bwd_validate(const void* q, const void* k, const void* v, co
   if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
   if (N > ATTN_MAX_N) return ATTN_ERR_SHAPE;
   if ((int64_t)B * Hq * (((int64_t)N + kBM - 1) / kBM) > ATTN_MAX_TILES) return ATTN_ERR_SHAPE;
-  if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
+  if (D != 16 && D != 32 && D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
   if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
   if (!isfinite(scale)) return ATTN_ERR_SCALE;
   const void* ptrs16[] = {q, k, v, out, dout, dq, dk, dv};

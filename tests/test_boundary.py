@@ -254,6 +254,8 @@ def bcall(**kw):
 def test_bwd_validate_accepts(lib):
     assert bcall() == sdp.ATTN_OK
     assert bcall(valid_len=None, D=64, dtype=sdp.ATTN_F16, causal=0, Hkv=8) == sdp.ATTN_OK
+    assert bcall(D=16) == sdp.ATTN_OK
+    assert bcall(D=32) == sdp.ATTN_OK
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -261,8 +263,10 @@ def test_bwd_validate_accepts(lib):
     (dict(ws=None), sdp.ATTN_ERR_NULL),
     (dict(dout=None), sdp.ATTN_ERR_NULL),
     (dict(Hq=8, Hkv=3), sdp.ATTN_ERR_SHAPE),
-    (dict(D=32), sdp.ATTN_ERR_HEAD_DIM),
+    (dict(D=256), sdp.ATTN_ERR_HEAD_DIM),
+    (dict(D=48), sdp.ATTN_ERR_HEAD_DIM),
     (dict(dtype=7), sdp.ATTN_ERR_DTYPE),
+    (dict(dtype=sdp.ATTN_F32), sdp.ATTN_ERR_DTYPE),
     (dict(scale=float("nan")), sdp.ATTN_ERR_SCALE),
     (dict(dq=DQ + 8), sdp.ATTN_ERR_LAYOUT),
     (dict(ws=DL + 2), sdp.ATTN_ERR_LAYOUT),

@@ -97,7 +97,8 @@ def compare_case(case, dout_bits, tag):
     return e
 
 
-# (dtype, D, causal, padded, B, Hq, Hkv, N): ragged N, N below one tile, exact tiles, GQA, MQA.
+# (dtype, D, causal, padded, B, Hq, Hkv, N): ragged N, N below one tile, exact tiles, GQA, MQA,
+# head dims 16 / 32 (the D = 64 geometry with zero-filled chunks) and 64 / 128.
 BWD_SMALL = [
     ("f16", 64, False, False, 1, 2, 2, 128),
     ("f16", 64, True, False, 2, 4, 4, 200),
@@ -113,6 +114,11 @@ BWD_SMALL = [
     ("bf16", 128, True, True, 2, 2, 2, 640),
     ("bf16", 64, True, False, 1, 8, 1, 520),
     ("bf16", 128, False, False, 1, 2, 1, 1),
+    ("f16", 16, True, True, 3, 4, 2, 257),
+    ("bf16", 16, False, False, 1, 4, 4, 300),
+    ("bf16", 32, True, False, 2, 8, 2, 333),
+    ("f16", 32, False, True, 2, 6, 3, 1000),
+    ("bf16", 16, True, False, 2, 2, 1, 1),
 ]
 
 
