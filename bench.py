@@ -68,6 +68,21 @@ def flops_bwd(w) -> float:
     return 2.5 * flops(w)
 
 
+def effective_flops(w, valid_len) -> float:
+    """4 * D flops per (query, visible key) pair actually computed: with padding, sum over the
+    batches of the visible pairs of every query row (causal: min(i + 1, valid) keys for row i)."""
+    N = w.N
+    total = 0
+    for b in range(w.B):
+        v = N if valid_len is None else min(max(int(valid_len[b]), 0), N)
+        if w.causal:
+            # rows i < v see i + 1 keys, rows i >= v see v keys
+            total += v * (v + 1) // 2 + (N - v) * v
+        else:
+            total += N * v
+    return 4.0 * w.D * w.Hq * total
+
+
 def kernel_sha(src: str = KERNEL_SRC) -> str:
     with open(src, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
@@ -291,7 +306,10 @@ def main():
                    "causal": w.causal, "padded": w.padded, "scale": w.scale,
                    "layout": args.layout, "explicit_mask": args.mask,
                    "pass": "backward" if args.backward else "forward",
-                   "flops_per_step": f},
+                   "flops_per_step": f,
+                   "effective_flops_per_step": (
+                       (2.5 if args.backward else 1.0) * effective_flops(w, case.valid_len)
+                       if w.padded else None)},
         "roofline": roof,
         "cpu_baseline": cpu,
     }
