@@ -145,8 +145,8 @@ int attn_fwd_validate(const void *q, const void *k, const void *v, const void *o
  *   lse            as in attn_fwd: contiguous [B, Hq, N] float32 or NULL.
  *   all else       as in attn_fwd.
  *
- * Every stride must be >= 0 and a multiple of 8 elements, and row strides >= D (ATTN_ERR_LAYOUT
- * otherwise). Inputs may share memory with each other (for instance Q, K and V as views of one
+ * Every stride must be >= 0 and a multiple of 16 bytes (8 elements of a 16-bit type, 4 of fp32),
+ * and row strides >= D (ATTN_ERR_LAYOUT otherwise). Inputs may share memory with each other (for instance Q, K and V as views of one
  * packed tensor, or a zero batch stride). The output's rows must be distinct (its strides,
  * ordered, must each step past the extent of the smaller ones). For the alias check each tensor
  * counts as the whole byte range from its pointer to the end of its last row, so out must lie
@@ -248,11 +248,40 @@ int attn_bwd_validate(const void *q, const void *k, const void *v, const void *o
                       const void *dv, const float *ws, int B, int Hq, int Hkv, int N, int D,
                       float scale, int causal, const int32_t *valid_len, int dtype);
 
+/*
+ * attn_bwd_strided -- attn_bwd on tensors given by (batch, head, row) element strides, as in
+ * attn_fwd_strided (every stride a non-negative multiple of 8 elements, rows of D contiguous
+ * elements, 16-byte aligned; NULL strides mean contiguous [B, H, N, D]; row strides up to
+ * (2^31 - 2D) / (2 (N + 128)) elements). This covers the
+ * [B, N, H, D] layout of "Triton Cuda Attention"'s host code and the article's §2.1 without
+ * transposes. dq, dk and dv may use layouts of their own; each of their rows must be distinct
+ * (ATTN_ERR_LAYOUT otherwise), and no output may overlap an input or another output
+ * (ATTN_ERR_ALIAS). lse and ws stay contiguous [B, Hq, N] / [2, B, Hq, N] float32 arrays.
+ */
+int attn_bwd_strided(const void *q, const int64_t *q_strides, const void *k,
+                     const int64_t *k_strides, const void *v, const int64_t *v_strides,
+                     const void *out, const int64_t *out_strides, const void *dout,
+                     const int64_t *dout_strides, const float *lse, void *dq,
+                     const int64_t *dq_strides, void *dk, const int64_t *dk_strides, void *dv,
+                     const int64_t *dv_strides, float *ws, int B, int Hq, int Hkv, int N, int D,
+                     float scale, int causal, const int32_t *valid_len, int dtype, void *stream);
+
+/* attn_bwd_strided_validate -- the host-only argument check of attn_bwd_strided. */
+int attn_bwd_strided_validate(const void *q, const int64_t *q_strides, const void *k,
+                              const int64_t *k_strides, const void *v, const int64_t *v_strides,
+                              const void *out, const int64_t *out_strides, const void *dout,
+                              const int64_t *dout_strides, const float *lse, const void *dq,
+                              const int64_t *dq_strides, const void *dk,
+                              const int64_t *dk_strides, const void *dv,
+                              const int64_t *dv_strides, const float *ws, int B, int Hq, int Hkv,
+                              int N, int D, float scale, int causal, const int32_t *valid_len,
+                              int dtype);
+
 /* attn_status_string -- a static, NUL-terminated description of a return code (never NULL). */
 const char *attn_status_string(int status);
 
-/* attn_version -- the library's interface version, currently 4 (2 added attn_fwd_strided, 3
- * attn_fwd_masked, 4 attn_bwd). */
+/* attn_version -- the library's interface version, currently 5 (2 added attn_fwd_strided, 3
+ * attn_fwd_masked, 4 attn_bwd, 5 attn_bwd_strided). */
 int attn_version(void);
 
 #ifdef __cplusplus

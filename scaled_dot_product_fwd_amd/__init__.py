@@ -7,7 +7,8 @@ no fallback: if the library is missing, calls raise ``ImportError``.
 Raw entry points (same names and argument order as the C ABI; pointers are integers, stride
 arguments are 3-sequences of element strides or None):
     attn_fwd, attn_fwd_validate, attn_fwd_strided, attn_fwd_strided_validate,
-    attn_fwd_masked, attn_fwd_masked_validate, attn_bwd, attn_bwd_validate,
+    attn_fwd_masked, attn_fwd_masked_validate, attn_bwd, attn_bwd_validate, attn_bwd_strided,
+    attn_bwd_strided_validate,
     attn_status_string, attn_version
 Convenience for torch tensors (device memory and streams only):
     forward(q, k, v, causal=..., valid_len=None, scale=None, out=None, lse=None, layout="bhnd",
@@ -23,7 +24,8 @@ from typing import Optional, Tuple
 
 __all__ = ["ATTN_F16", "ATTN_BF16", "ATTN_F32", "AttnError", "attn_fwd", "attn_fwd_validate",
            "attn_fwd_strided", "attn_fwd_strided_validate", "attn_fwd_masked",
-           "attn_fwd_masked_validate", "attn_bwd", "attn_bwd_validate", "attention",
+           "attn_fwd_masked_validate", "attn_bwd", "attn_bwd_validate", "attn_bwd_strided",
+           "attn_bwd_strided_validate", "attention",
            "backward", "attn_status_string",
            "attn_version", "forward", "library_path", "load_library"]
 
@@ -101,6 +103,13 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_bwd.argtypes = [_vp] * 10 + [_c_int] * 5 + [_c_float, _c_int, _vp, _c_int, _vp]
     lib.attn_bwd_validate.restype = _c_int
     lib.attn_bwd_validate.argtypes = [_vp] * 10 + [_c_int] * 5 + [_c_float, _c_int, _vp, _c_int]
+    lib.attn_bwd_strided.restype = _c_int
+    lib.attn_bwd_strided.argtypes = ([_vp, _i64p] * 5 + [_vp] + [_vp, _i64p] * 3 + [_vp] +
+                                     [_c_int] * 5 + [_c_float, _c_int, _vp, _c_int, _vp])
+    lib.attn_bwd_strided_validate.restype = _c_int
+    lib.attn_bwd_strided_validate.argtypes = ([_vp, _i64p] * 5 + [_vp] + [_vp, _i64p] * 3 +
+                                              [_vp] + [_c_int] * 5 + [_c_float, _c_int, _vp,
+                                                                      _c_int])
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_status_string.argtypes = [_c_int]
     lib.attn_version.restype = _c_int
@@ -193,6 +202,28 @@ def attn_bwd_validate(q: int, k: int, v: int, out: int, dout: int, lse: int, dq:
     """C ``attn_bwd_validate``: host-only argument check, no HIP call."""
     return load_library().attn_bwd_validate(q, k, v, out, dout, lse, dq, dk, dv, ws, B, Hq,
                                             Hkv, N, D, scale, int(causal), valid_len, dtype)
+
+
+def attn_bwd_strided(q, q_strides, k, k_strides, v, v_strides, out, out_strides, dout,
+                     dout_strides, lse, dq, dq_strides, dk, dk_strides, dv, dv_strides, ws, B, Hq,
+                     Hkv, N, D, scale, causal, valid_len, dtype, stream) -> int:
+    """C ``attn_bwd_strided``; pointers as integers, strides as 3-sequences or None."""
+    return load_library().attn_bwd_strided(
+        q, _strides(q_strides), k, _strides(k_strides), v, _strides(v_strides), out,
+        _strides(out_strides), dout, _strides(dout_strides), lse, dq, _strides(dq_strides), dk,
+        _strides(dk_strides), dv, _strides(dv_strides), ws, B, Hq, Hkv, N, D, scale, int(causal),
+        valid_len, dtype, stream)
+
+
+def attn_bwd_strided_validate(q, q_strides, k, k_strides, v, v_strides, out, out_strides, dout,
+                              dout_strides, lse, dq, dq_strides, dk, dk_strides, dv, dv_strides,
+                              ws, B, Hq, Hkv, N, D, scale, causal, valid_len, dtype) -> int:
+    """C ``attn_bwd_strided_validate``: host-only argument check, no HIP call."""
+    return load_library().attn_bwd_strided_validate(
+        q, _strides(q_strides), k, _strides(k_strides), v, _strides(v_strides), out,
+        _strides(out_strides), dout, _strides(dout_strides), lse, dq, _strides(dq_strides), dk,
+        _strides(dk_strides), dv, _strides(dv_strides), ws, B, Hq, Hkv, N, D, scale, int(causal),
+        valid_len, dtype)
 
 
 def attn_status_string(status: int) -> str:
@@ -320,31 +351,47 @@ def forward(q, k, v, causal: bool, valid_len=None, scale: Optional[float] = None
 
 
 def backward(q, k, v, out, dout, lse, causal: bool, valid_len=None,
-             scale: Optional[float] = None, dq=None, dk=None, dv=None, ws=None, stream=None):
-    """Run attn_bwd on contiguous [B, H, N, D] torch device tensors; returns (dq, dk, dv).
+             scale: Optional[float] = None, dq=None, dk=None, dv=None, ws=None, stream=None,
+             layout: str = "bhnd"):
+    """Run the attention backward on torch device tensors; returns (dq, dk, dv).
 
     ``out`` and ``lse`` are the forward's outputs for the same inputs; ``dout`` is the gradient
-    of the loss with respect to ``out``. Output tensors and the float32 [B, Hq, N] workspace
-    ``ws`` ([2, B, Hq, N]: Delta, then the LSE in base 2) are allocated with torch when not
-    given.
+    of the loss with respect to ``out``. ``layout`` names the dimension order of q, k, v, out,
+    dout and the gradients ("bhnd" = [B, H, N, D], "bnhd" = [B, N, H, D]); any strides with a
+    contiguous D dimension are accepted (contiguous [B, H, N, D] tensors take attn_bwd, others
+    attn_bwd_strided, with no copies). Gradients (each in its input's layout) and the float32
+    workspace ``ws`` ([2, B, Hq, N]: Delta, then the LSE in base 2) are allocated with torch when
+    not given.
     """
     import torch
-    B, Hq, N, D = q.shape
-    Hkv = k.shape[1]
-    for name, t, shape in (("q", q, (B, Hq, N, D)), ("k", k, (B, Hkv, N, D)),
-                           ("v", v, (B, Hkv, N, D)), ("out", out, (B, Hq, N, D)),
-                           ("dout", dout, (B, Hq, N, D))):
+    if layout not in ("bhnd", "bnhd"):
+        raise ValueError("layout must be 'bhnd' or 'bnhd'")
+    tr = (lambda t: t.transpose(1, 2)) if layout == "bnhd" else (lambda t: t)
+    qv, kv, vv, ov, gv = tr(q), tr(k), tr(v), tr(out), tr(dout)
+    B, Hq, N, D = qv.shape
+    Hkv = kv.shape[1]
+    for name, t, shape in (("q", qv, (B, Hq, N, D)), ("k", kv, (B, Hkv, N, D)),
+                           ("v", vv, (B, Hkv, N, D)), ("out", ov, (B, Hq, N, D)),
+                           ("dout", gv, (B, Hq, N, D))):
         if tuple(t.shape) != shape or t.dtype != q.dtype or not t.is_cuda:
             raise ValueError("%s must be a device tensor of shape %s and q's dtype" % (name, shape))
-        if not t.is_contiguous():
-            raise ValueError("%s must be contiguous" % name)
+        if t.stride(3) != 1:
+            raise ValueError("%s: the D dimension must be contiguous" % name)
     if lse is None or lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, N):
         raise ValueError("lse must be the forward's float32 [B, Hq, N] tensor")
+    if not lse.is_contiguous():
+        raise ValueError("lse must be contiguous")
     if scale is None:
         scale = 1.0 / float(D) ** 0.5
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    dq = torch.empty_like(q, memory_format=torch.contiguous_format) if dq is None else dq
+    dk = torch.empty_like(k, memory_format=torch.contiguous_format) if dk is None else dk
+    dv = torch.empty_like(v, memory_format=torch.contiguous_format) if dv is None else dv
+    dqv, dkv, dvv = tr(dq), tr(dk), tr(dv)
+    for name, t, shape in (("dq", dqv, (B, Hq, N, D)), ("dk", dkv, (B, Hkv, N, D)),
+                           ("dv", dvv, (B, Hkv, N, D))):
+        if tuple(t.shape) != shape or t.dtype != q.dtype or not t.is_cuda or t.stride(3) != 1:
+            raise ValueError("%s must be a device tensor of shape %s, q's dtype, D contiguous"
+                             % (name, shape))
     if ws is None:
         ws = torch.empty((2, B, Hq, N), dtype=torch.float32, device=q.device)
     elif ws.dtype != torch.float32 or ws.numel() < 2 * B * Hq * N or not ws.is_contiguous():
@@ -356,12 +403,23 @@ def backward(q, k, v, out, dout, lse, causal: bool, valid_len=None,
         vl_ptr = valid_len.data_ptr()
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    st = attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
-                  lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(),
-                  B, Hq, Hkv, N, D, float(scale), int(bool(causal)), vl_ptr, _dtype_code(q),
-                  stream.cuda_stream)
+    views = (qv, kv, vv, ov, gv, dqv, dkv, dvv)
+    if all(t.is_contiguous() for t in views):
+        st = attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+                      lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(),
+                      B, Hq, Hkv, N, D, float(scale), int(bool(causal)), vl_ptr,
+                      _dtype_code(q), stream.cuda_stream)
+        name = "attn_bwd"
+    else:
+        st = attn_bwd_strided(
+            qv.data_ptr(), qv.stride()[:3], kv.data_ptr(), kv.stride()[:3], vv.data_ptr(),
+            vv.stride()[:3], ov.data_ptr(), ov.stride()[:3], gv.data_ptr(), gv.stride()[:3],
+            lse.data_ptr(), dqv.data_ptr(), dqv.stride()[:3], dkv.data_ptr(), dkv.stride()[:3],
+            dvv.data_ptr(), dvv.stride()[:3], ws.data_ptr(), B, Hq, Hkv, N, D, float(scale),
+            int(bool(causal)), vl_ptr, _dtype_code(q), stream.cuda_stream)
+        name = "attn_bwd_strided"
     if st != ATTN_OK:
-        raise AttnError(st, "attn_bwd")
+        raise AttnError(st, name)
     return dq, dk, dv
 
 
@@ -370,19 +428,21 @@ def _autograd_function():
 
     class _Attention(torch.autograd.Function):
         @staticmethod
-        def forward(ctx, q, k, v, causal, valid_len, scale):
-            q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
-            out, lse = forward(q, k, v, causal=causal, valid_len=valid_len, scale=scale)
+        def forward(ctx, q, k, v, causal, valid_len, scale, layout):
+            out, lse = forward(q, k, v, causal=causal, valid_len=valid_len, scale=scale,
+                               layout=layout)
             ctx.save_for_backward(q, k, v, out, lse, valid_len)
-            ctx.causal, ctx.scale = causal, scale
+            ctx.causal, ctx.scale, ctx.layout = causal, scale, layout
             return out
 
         @staticmethod
         def backward(ctx, dout):
             q, k, v, out, lse, valid_len = ctx.saved_tensors
-            dq, dk, dv = backward(q, k, v, out, dout.contiguous(), lse, causal=ctx.causal,
-                                  valid_len=valid_len, scale=ctx.scale)
-            return dq, dk, dv, None, None, None
+            if dout.stride(-1) != 1 or 0 in dout.stride():
+                dout = dout.contiguous()   # e.g. a broadcast gradient
+            dq, dk, dv = backward(q, k, v, out, dout, lse, causal=ctx.causal,
+                                  valid_len=valid_len, scale=ctx.scale, layout=ctx.layout)
+            return dq, dk, dv, None, None, None, None
 
     return _Attention
 
@@ -390,10 +450,12 @@ def _autograd_function():
 _ATTENTION = None
 
 
-def attention(q, k, v, causal: bool, valid_len=None, scale: Optional[float] = None):
-    """Differentiable attention on [B, H, N, D] tensors: forward through attn_fwd, gradients
-    through attn_bwd (torch.autograd glue only)."""
+def attention(q, k, v, causal: bool, valid_len=None, scale: Optional[float] = None,
+              layout: str = "bhnd"):
+    """Differentiable attention on [B, H, N, D] (or, with layout="bnhd", [B, N, H, D]) tensors:
+    forward through attn_fwd, gradients through attn_bwd (torch.autograd glue only; strided
+    inputs are used in place)."""
     global _ATTENTION
     if _ATTENTION is None:
         _ATTENTION = _autograd_function()
-    return _ATTENTION.apply(q, k, v, causal, valid_len, scale)
+    return _ATTENTION.apply(q, k, v, causal, valid_len, scale, layout)

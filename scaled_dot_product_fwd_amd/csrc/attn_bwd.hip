@@ -44,7 +44,8 @@ using namespace attn_detail;
 
 constexpr int kQT = 32;   // queries per iteration of the dK/dV kernel
 // DMA voffset of a lane whose row chunk does not exist (head dims below 64): past every buffer
-// (each spans at most N * 2 * DH < 2^31 bytes), so the range check writes zeros to LDS.
+// (the host keeps each span and scalar row offset below 2^31 bytes), so the range check writes
+// zeros to LDS.
 constexpr uint32_t kNoChunk = 0x80000000u;
 
 typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
@@ -71,6 +72,15 @@ struct BwdParams {
   float scale;     // the signed scale (dQ and dK carry it)
   uint32_t qsign;  // 0x80008000 when scale < 0: one operand of the scores is negated instead
   uint32_t qmask;  // 0 when scale == 0 (all scores are 0; c is 1)
+  // Element strides (batch, head, row) of Q, K, V, O, dO, dQ, dK, dV; rows are contiguous.
+  int64_t qs_b, qs_h, qs_n;
+  int64_t ks_b, ks_h, ks_n;
+  int64_t vs_b, vs_h, vs_n;
+  int64_t os_b, os_h, os_n;
+  int64_t gs_b, gs_h, gs_n;
+  int64_t dqs_b, dqs_h, dqs_n;
+  int64_t dks_b, dks_h, dks_n;
+  int64_t dvs_b, dvs_h, dvs_n;
 };
 
 // Row value of the log-sum-exp in log2 units; an empty row (L = -inf) has only hidden keys, and
@@ -88,12 +98,13 @@ __device__ inline u32x4 pack8(const float (&x)[16], int s) {
 }
 
 // Write a wave's 32 x D block, held transposed in acc (acc[u][4 r4 + e] is element
-// d = 32u + 8 r4 + 4h + e of row ql), as rows of `dst` (row stride DH <= D: the 16-byte chunks
-// past DH are not written) through the wave's LDS staging area `ost` (32 * ROW bytes). Rows at
-// or past n are not written.
+// d = 32u + 8 r4 + 4h + e of row ql), as rows of `dst` (rows `rs` elements apart; DH <= D
+// elements each: the 16-byte chunks past DH are not written) through the wave's LDS staging
+// area `ost` (32 * ROW bytes). Rows at or past n are not written.
 template <int DT, int D, int DH = D>
 __device__ inline void store_rows(const f32x16 (&acc)[Geo<D>::OT], float mul,
-                                  unsigned char* ost, uint16_t* dst, int row0, int n, int lane) {
+                                  unsigned char* ost, uint16_t* dst, int64_t rs, int row0, int n,
+                                  int lane) {
   using G = Geo<D>;
   using M = Mfma<DT>;
   const int h = lane >> 5, ql = lane & 31;
@@ -115,7 +126,7 @@ __device__ inline void store_rows(const f32x16 (&acc)[Geo<D>::OT], float mul,
     const int r = i * RPI + lane / G::CH;
     const int cc = lane % G::CH;
     const u32x4 v = *(const u32x4*)(ost + r * G::ROW + 16 * (cc ^ (r & (G::CH - 1))));
-    if (row0 + r < n && (DH == D || cc < DH / 8)) *(u32x4*)(dst + (size_t)(row0 + r) * DH + 8 * cc) = v;
+    if (row0 + r < n && (DH == D || cc < DH / 8)) *(u32x4*)(dst + (row0 + r) * rs + 8 * cc) = v;
   }
 }
 
@@ -144,13 +155,11 @@ __device__ inline u32x4 tr_frag(const unsigned char* tile, uint32_t off, int row
 // dQ (and D)
 // ------------------------------------------------------------------------------------------
 // DH is the tensors' head dimension; DH < 64 runs the D = 64 geometry with the missing 16-byte
-// chunks of every row zero (out-of-range DMA lanes, zero registers) and never stored. The
-// tensors are contiguous, so their row stride RS (bytes) is known at compile time.
+// chunks of every row zero (out-of-range DMA lanes, zero registers) and never stored.
 template <int DT, int DH, bool CAUSAL>
 __device__ __forceinline__ void bwd_dq_body(const BwdParams& p) {
   constexpr int D = DH < 64 ? 64 : DH;
   constexpr int DCH = DH / 8;
-  constexpr int RS = 2 * DH;
   using G = Geo<D>;
   using M = Mfma<DT>;
   constexpr int KSTEPS = G::KSTEPS;
@@ -201,29 +210,31 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p) {
   const int qrow = qa + ql;
   const int qr = min(qrow, p.N - 1);
 
-  const size_t kv_off = (size_t)(b * p.Hkv + kvh) * p.N * DH;
-  const uint32_t head_bytes = (uint32_t)p.N * RS;
-  const __amdgpu_buffer_rsrc_t krs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + kv_off), (short)0, head_bytes, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t vrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + kv_off), (short)0, head_bytes, kBufferFlags);
+  // K and V of this (batch, KV head) as buffers spanning its N rows (rows past N read as 0).
+  const uint32_t krow = (uint32_t)p.ks_n * 2, vrow = (uint32_t)p.vs_n * 2;   // bytes
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.k + b * p.ks_b + kvh * p.ks_h), (short)0, (p.N - 1) * krow + 2 * DH,
+      kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.v + b * p.vs_b + kvh * p.vs_h), (short)0, (p.N - 1) * vrow + 2 * DH,
+      kBufferFlags);
   uint32_t kdma[G::LOADS], vdma[G::LOADS];
 #pragma unroll
   for (int i = 0; i < G::LOADS; ++i) {
     const int r = (wave * G::LOADS + i) * G::RPB + lane / G::CH;
     const int kc = (lane % G::CH) ^ G::bswz(r), vc = (lane % G::CH) ^ G::kswz(r);
-    kdma[i] = (DCH < G::CH && kc >= DCH) ? kNoChunk : r * RS + kc * 16;
-    vdma[i] = (DCH < G::CH && vc >= DCH) ? kNoChunk : r * RS + vc * 16;
+    kdma[i] = (DCH < G::CH && kc >= DCH) ? kNoChunk : r * krow + kc * 16;
+    vdma[i] = (DCH < G::CH && vc >= DCH) ? kNoChunk : r * vrow + vc * 16;
   }
   auto dma = [&](int tile, int kdst, int vdst) {
-    const int soff = tile * kBN * RS;
+    const uint32_t row0 = (uint32_t)tile * kBN;
 #pragma unroll
     for (int i = 0; i < G::LOADS; ++i) {
       const int blk = (wave * G::LOADS + i) * 1024;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(smem + kdst + blk), 16, kdma[i],
-                                               soff, 0, 0);
+                                               row0 * krow, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(smem + vdst + blk), 16, vdma[i],
-                                               soff, 0, 0);
+                                               row0 * vrow, 0, 0);
     }
   };
 
@@ -240,14 +251,16 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p) {
   if (ntiles > 0) dma(0, G::K0, G::V0);
 
   // Q, dO and O of this lane's row (B-operand layout: Q[row][16s + 8h .. +7]).
-  const size_t rowoff = ((size_t)bh * p.N + qr) * DH + 8 * h;
+  const uint16_t* qsrc = p.q + b * p.qs_b + hq * p.qs_h + qr * p.qs_n + 8 * h;
+  const uint16_t* gsrc = p.dout + b * p.gs_b + hq * p.gs_h + qr * p.gs_n + 8 * h;
+  const uint16_t* osrc = p.o + b * p.os_b + hq * p.os_h + qr * p.os_n + 8 * h;
   u32x4 qf[KSTEPS], dof[KSTEPS], of[KSTEPS];
 #pragma unroll
   for (int s = 0; s < KSTEPS; ++s) {
     const bool ok = DCH == G::CH || 2 * s + h < DCH;
-    qf[s] = ok ? *(const u32x4*)(p.q + rowoff + 16 * s) : u32x4{};
-    dof[s] = ok ? *(const u32x4*)(p.dout + rowoff + 16 * s) : u32x4{};
-    of[s] = ok ? *(const u32x4*)(p.o + rowoff + 16 * s) : u32x4{};
+    qf[s] = ok ? *(const u32x4*)(qsrc + 16 * s) : u32x4{};
+    dof[s] = ok ? *(const u32x4*)(gsrc + 16 * s) : u32x4{};
+    of[s] = ok ? *(const u32x4*)(osrc + 16 * s) : u32x4{};
   }
   const float L = lse_log2(p.lse[(size_t)bh * p.N + qr]);
   // D = rowsum(dO o O): this lane's half of the row, then the lane pair.
@@ -340,8 +353,8 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p) {
   // dQ = scale * (dQ^T)^T, staged through LDS after every wave is done with the tiles.
   wait_loads_and_lds();
   __syncthreads();
-  store_rows<DT, D, DH>(acc, p.scale, smem + wave * 32 * G::ROW, p.dq + (size_t)bh * p.N * DH,
-                        qa, p.N, lane);
+  store_rows<DT, D, DH>(acc, p.scale, smem + wave * 32 * G::ROW,
+                        p.dq + b * p.dqs_b + hq * p.dqs_h, p.dqs_n, qa, p.N, lane);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -366,7 +379,6 @@ template <int DT, int DH, bool CAUSAL>
 __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
   constexpr int D = DH < 64 ? 64 : DH;   // geometry (as in the dQ kernel)
   constexpr int DCH = DH / 8;
-  constexpr int RS = 2 * DH;
   using G = Geo<D>;
   using BG = BwdGeo<D>;
   using M = Mfma<DT>;
@@ -412,7 +424,6 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
   const int key = kw + ql;         // this lane's key (MFMA output column)
   int kv_end = p.N;
   if (p.valid_len) kv_end = min(max(p.valid_len[b], 0), p.N);
-  const size_t kv_off = (size_t)(b * p.Hkv + kvh) * p.N * DH;
   unsigned char* vreg = smem + BG::VREG + wave * 32 * G::ROW;   // this wave's 32 V rows
 
   f32x16 dk[OT], dv[OT];
@@ -427,7 +438,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
     // K^T fragments of this lane's key (B operand: K[key][16s + 8h .. +7]), sign/zero applied.
     u32x4 kf[KSTEPS];
     {
-      const uint16_t* ksrc = p.k + kv_off + (size_t)min(key, p.N - 1) * DH + 8 * h;
+      const uint16_t* ksrc = p.k + b * p.ks_b + kvh * p.ks_h + min(key, p.N - 1) * p.ks_n + 8 * h;
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s)
         kf[s] = (DCH == G::CH || 2 * s + h < DCH)
@@ -437,43 +448,52 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
     // V rows of this wave's keys into its LDS rows (bswz layout like Q and dO, so that one set
     // of row-fragment offsets serves all three).
     {
+      const uint32_t vrow = (uint32_t)p.vs_n * 2;
       const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(p.v + kv_off), (short)0, (uint32_t)p.N * RS, kBufferFlags);
+          (void*)(p.v + b * p.vs_b + kvh * p.vs_h), (short)0, (p.N - 1) * vrow + 2 * DH,
+          kBufferFlags);
 #pragma unroll
       for (int i = 0; i < 32 / G::RPB; ++i) {
         const int row = i * G::RPB + lane / G::CH;
         const int vc = (lane % G::CH) ^ G::bswz(row);
         const uint32_t off =
-            (DCH < G::CH && vc >= DCH) ? kNoChunk : (lane / G::CH) * RS + vc * 16;
+            (DCH < G::CH && vc >= DCH) ? kNoChunk : (lane / G::CH) * vrow + vc * 16;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(vreg + i * 1024), 16, off,
-                                                 (uint32_t)(kw + i * G::RPB) * RS, 0, 0);
+                                                 (uint32_t)(kw + i * G::RPB) * vrow, 0, 0);
       }
     }
     // DMA of the iteration over query head kvh * group + g, queries q0 .. q0+31, into buffer
     // `buf`: Q and dO tiles (bswz layout), L and D (wave 0 and 1).
-    uint32_t qoff[BG::QLOADS];
+    // Q and dO rows may have different strides: one chunk position per block, the row offsets
+    // applied per tensor.
+    const uint32_t qrowb = (uint32_t)p.qs_n * 2, growb = (uint32_t)p.gs_n * 2;
+    uint32_t qoff[BG::QLOADS], goff[BG::QLOADS];
 #pragma unroll
     for (int i = 0; i < BG::QLOADS; ++i) {
       const int row = (wave * BG::QLOADS + i) * G::RPB + lane / G::CH;   // row in the tile
       const int qc = (lane % G::CH) ^ G::bswz(row);
-      qoff[i] = (DCH < G::CH && qc >= DCH) ? kNoChunk : (lane / G::CH) * RS + qc * 16;
+      const bool none = DCH < G::CH && qc >= DCH;
+      qoff[i] = none ? kNoChunk : (lane / G::CH) * qrowb + qc * 16;
+      goff[i] = none ? kNoChunk : (lane / G::CH) * growb + qc * 16;
     }
     auto dma = [&](int g, int q0, int buf) {
-      const int bh = b * p.Hq + kvh * p.group + g;
-      const size_t hoff = (size_t)bh * p.N * DH;
+      const int hq = kvh * p.group + g;
+      const int bh = b * p.Hq + hq;
       const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(p.q + hoff), (short)0, (uint32_t)p.N * RS, kBufferFlags);
+          (void*)(p.q + b * p.qs_b + hq * p.qs_h), (short)0, (p.N - 1) * qrowb + 2 * DH,
+          kBufferFlags);
       const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(p.dout + hoff), (short)0, (uint32_t)p.N * RS, kBufferFlags);
+          (void*)(p.dout + b * p.gs_b + hq * p.gs_h), (short)0, (p.N - 1) * growb + 2 * DH,
+          kBufferFlags);
       unsigned char* base = smem + buf * BG::BUF;
 #pragma unroll
       for (int i = 0; i < BG::QLOADS; ++i) {
         const int blk = wave * BG::QLOADS + i;
-        const uint32_t soff = (uint32_t)(q0 + blk * G::RPB) * RS;
+        const uint32_t r0 = (uint32_t)(q0 + blk * G::RPB);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void*)(base + blk * 1024), 16,
-                                                 qoff[i], soff, 0, 0);
+                                                 qoff[i], r0 * qrowb, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ors, (lds_void*)(base + BG::QTILE + blk * 1024),
-                                                 16, qoff[i], soff, 0, 0);
+                                                 16, goff[i], r0 * growb, 0, 0);
       }
       if (wave < 2) {
         const float* src = wave == 0 ? p.lse2 : p.delta;
@@ -579,8 +599,10 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
   // dK = scale * (dK^T)^T, dV = (dV^T)^T; rows past N are not written. Staging reuses the Q/dO
   // buffers (every wave is past its last read).
   unsigned char* ost = smem + wave * 32 * G::ROW;
-  store_rows<DT, D, DH>(dk, p.scale, ost, p.dk + kv_off, kw, p.N, lane);
-  store_rows<DT, D, DH>(dv, 1.0f, ost, p.dv + kv_off, kw, p.N, lane);
+  store_rows<DT, D, DH>(dk, p.scale, ost, p.dk + b * p.dks_b + kvh * p.dks_h, p.dks_n, kw, p.N,
+                        lane);
+  store_rows<DT, D, DH>(dv, 1.0f, ost, p.dv + b * p.dvs_b + kvh * p.dvs_h, p.dvs_n, kw, p.N,
+                        lane);
 }
 
 template <int DT, int D, bool CAUSAL>
@@ -620,38 +642,53 @@ hipError_t dispatch_bwd(const BwdParams& p, int D, bool causal, hipStream_t s) {
   return causal ? launch_bwd<DT, 128, true>(p, s) : launch_bwd<DT, 128, false>(p, s);
 }
 
-bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
-  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
-  return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+// The eight [B, H, N, D] tensors of a backward call.
+struct BwdLayouts {
+  Layout q, k, v, o, dout, dq, dk, dv;
+};
+
+BwdLayouts bwd_layouts(const void* q, const int64_t* qs, const void* k, const int64_t* ks,
+                       const void* v, const int64_t* vs, const void* o, const int64_t* os,
+                       const void* dout, const int64_t* gs, const void* dq, const int64_t* dqs,
+                       const void* dk, const int64_t* dks, const void* dv, const int64_t* dvs,
+                       int Hq, int Hkv, int N, int D) {
+  return BwdLayouts{strided(q, qs, Hq, N, D),     strided(k, ks, Hkv, N, D),
+                    strided(v, vs, Hkv, N, D),    strided(o, os, Hq, N, D),
+                    strided(dout, gs, Hq, N, D),  strided(dq, dqs, Hq, N, D),
+                    strided(dk, dks, Hkv, N, D),  strided(dv, dvs, Hkv, N, D)};
 }
 
-}  // namespace
-
-extern "C" int attn_bwd_validate(const void* q, const void* k, const void* v, const void* out,
-                                 const void* dout, const float* lse, const void* dq,
-                                 const void* dk, const void* dv, const float* ws, int B,
-                                 int Hq, int Hkv, int N, int D, float scale, int causal,
-                                 const int32_t* valid_len, int dtype) {
-  (void)causal;
-  if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv || !ws)
-    return ATTN_ERR_NULL;
+int bwd_validate(const BwdLayouts& t, const float* lse, const float* ws, int B, int Hq, int Hkv,
+                 int N, int D, float scale, const int32_t* valid_len, int dtype) {
+  const Layout* all[] = {&t.q, &t.k, &t.v, &t.o, &t.dout, &t.dq, &t.dk, &t.dv};
+  for (const Layout* l : all)
+    if (!l->ptr) return ATTN_ERR_NULL;
+  if (!lse || !ws) return ATTN_ERR_NULL;
   if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
   if (N > ATTN_MAX_N) return ATTN_ERR_SHAPE;
   if ((int64_t)B * Hq * (((int64_t)N + kBM - 1) / kBM) > ATTN_MAX_TILES) return ATTN_ERR_SHAPE;
   if (D != 16 && D != 32 && D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
   if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
   if (!isfinite(scale)) return ATTN_ERR_SCALE;
-  const void* ptrs16[] = {q, k, v, out, dout, dq, dk, dv};
-  for (const void* ptr : ptrs16)
-    if ((uintptr_t)ptr % 16 != 0) return ATTN_ERR_LAYOUT;
+  for (const Layout* l : all)
+    if (!layout_ok(*l, D, 2)) return ATTN_ERR_LAYOUT;
   if ((uintptr_t)lse % 4 != 0 || (uintptr_t)ws % 4 != 0) return ATTN_ERR_LAYOUT;
-  const int64_t qb = (int64_t)B * Hq * N * D * 2, kb = (int64_t)B * Hkv * N * D * 2;
+  if (!output_disjoint(t.dq, B, Hq, N, D) || !output_disjoint(t.dk, B, Hkv, N, D) ||
+      !output_disjoint(t.dv, B, Hkv, N, D))
+    return ATTN_ERR_LAYOUT;
+  // K, V, Q and dO of one head are read as 32-bit-addressed buffers, with scalar row offsets up
+  // to one tile past N.
+  int64_t smax = 0;
+  for (const Layout* l : {&t.q, &t.k, &t.v, &t.dout}) smax = l->sn > smax ? l->sn : smax;
+  if (((int64_t)N + kBM) * smax * 2 + 2 * D > INT32_MAX) return ATTN_ERR_SHAPE;
+  // Outputs (dq, dk, dv and the workspace) overlap no input and no other output.
   const int64_t lb = (int64_t)B * Hq * N * 4;
-  // Outputs: dq, dk, dv and the workspace; none may overlap an input or another output.
-  const void* outs[] = {dq, dk, dv, ws};
-  const int64_t osz[] = {qb, kb, kb, 2 * lb};
-  const void* ins[] = {q, k, v, out, dout, lse};
-  const int64_t isz[] = {qb, kb, kb, qb, qb, lb};
+  const void* outs[] = {t.dq.ptr, t.dk.ptr, t.dv.ptr, ws};
+  const int64_t osz[] = {t.dq.span(B, N, D, 2), t.dk.span(B, N, D, 2), t.dv.span(B, N, D, 2),
+                         2 * lb};
+  const void* ins[] = {t.q.ptr, t.k.ptr, t.v.ptr, t.o.ptr, t.dout.ptr, lse};
+  const int64_t isz[] = {t.q.span(B, N, D, 2), t.k.span(B, N, D, 2), t.v.span(B, N, D, 2),
+                         t.o.span(B, N, D, 2), t.dout.span(B, N, D, 2), lb};
   for (int i = 0; i < 4; ++i) {
     for (int j = 0; j < 6; ++j)
       if (overlaps(outs[i], osz[i], ins[j], isz[j])) return ATTN_ERR_ALIAS;
@@ -662,23 +699,20 @@ extern "C" int attn_bwd_validate(const void* q, const void* k, const void* v, co
   return ATTN_OK;
 }
 
-extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* out,
-                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                        float* ws, int B, int Hq, int Hkv, int N, int D, float scale,
-                        int causal, const int32_t* valid_len, int dtype, void* stream) {
-  const int st = attn_bwd_validate(q, k, v, out, dout, lse, dq, dk, dv, ws, B, Hq, Hkv, N, D,
-                                   scale, causal, valid_len, dtype);
+int bwd_run(const BwdLayouts& t, const float* lse, float* ws, int B, int Hq, int Hkv, int N,
+            int D, float scale, int causal, const int32_t* valid_len, int dtype, void* stream) {
+  const int st = bwd_validate(t, lse, ws, B, Hq, Hkv, N, D, scale, valid_len, dtype);
   if (st != ATTN_OK) return st;
   BwdParams p;
-  p.q = (const uint16_t*)q;
-  p.k = (const uint16_t*)k;
-  p.v = (const uint16_t*)v;
-  p.o = (const uint16_t*)out;
-  p.dout = (const uint16_t*)dout;
+  p.q = (const uint16_t*)t.q.ptr;
+  p.k = (const uint16_t*)t.k.ptr;
+  p.v = (const uint16_t*)t.v.ptr;
+  p.o = (const uint16_t*)t.o.ptr;
+  p.dout = (const uint16_t*)t.dout.ptr;
   p.lse = lse;
-  p.dq = (uint16_t*)dq;
-  p.dk = (uint16_t*)dk;
-  p.dv = (uint16_t*)dv;
+  p.dq = (uint16_t*)t.dq.ptr;
+  p.dk = (uint16_t*)t.dk.ptr;
+  p.dv = (uint16_t*)t.dv.ptr;
   p.delta = ws;
   p.lse2 = ws + (size_t)B * Hq * N;
   p.valid_len = valid_len;
@@ -695,8 +729,65 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
   p.qsign = scale < 0.f ? 0x80008000u : 0u;
   p.qmask = scale == 0.f ? 0u : 0xffffffffu;
   if (scale == 0.f) p.c = 1.0f;
+  p.qs_b = t.q.sb; p.qs_h = t.q.sh; p.qs_n = t.q.sn;
+  p.ks_b = t.k.sb; p.ks_h = t.k.sh; p.ks_n = t.k.sn;
+  p.vs_b = t.v.sb; p.vs_h = t.v.sh; p.vs_n = t.v.sn;
+  p.os_b = t.o.sb; p.os_h = t.o.sh; p.os_n = t.o.sn;
+  p.gs_b = t.dout.sb; p.gs_h = t.dout.sh; p.gs_n = t.dout.sn;
+  p.dqs_b = t.dq.sb; p.dqs_h = t.dq.sh; p.dqs_n = t.dq.sn;
+  p.dks_b = t.dk.sb; p.dks_h = t.dk.sh; p.dks_n = t.dk.sn;
+  p.dvs_b = t.dv.sb; p.dvs_h = t.dv.sh; p.dvs_n = t.dv.sn;
   const hipStream_t s = (hipStream_t)stream;
   const hipError_t e = dtype == ATTN_BF16 ? dispatch_bwd<ATTN_BF16>(p, D, causal != 0, s)
                                           : dispatch_bwd<ATTN_F16>(p, D, causal != 0, s);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" int attn_bwd_validate(const void* q, const void* k, const void* v, const void* out,
+                                 const void* dout, const float* lse, const void* dq,
+                                 const void* dk, const void* dv, const float* ws, int B,
+                                 int Hq, int Hkv, int N, int D, float scale, int causal,
+                                 const int32_t* valid_len, int dtype) {
+  (void)causal;
+  return bwd_validate(bwd_layouts(q, nullptr, k, nullptr, v, nullptr, out, nullptr, dout,
+                                  nullptr, dq, nullptr, dk, nullptr, dv, nullptr, Hq, Hkv, N, D),
+                      lse, ws, B, Hq, Hkv, N, D, scale, valid_len, dtype);
+}
+
+extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* out,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        float* ws, int B, int Hq, int Hkv, int N, int D, float scale,
+                        int causal, const int32_t* valid_len, int dtype, void* stream) {
+  return bwd_run(bwd_layouts(q, nullptr, k, nullptr, v, nullptr, out, nullptr, dout, nullptr,
+                             dq, nullptr, dk, nullptr, dv, nullptr, Hq, Hkv, N, D),
+                 lse, ws, B, Hq, Hkv, N, D, scale, causal, valid_len, dtype, stream);
+}
+
+extern "C" int attn_bwd_strided_validate(
+    const void* q, const int64_t* q_strides, const void* k, const int64_t* k_strides,
+    const void* v, const int64_t* v_strides, const void* out, const int64_t* out_strides,
+    const void* dout, const int64_t* dout_strides, const float* lse, const void* dq,
+    const int64_t* dq_strides, const void* dk, const int64_t* dk_strides, const void* dv,
+    const int64_t* dv_strides, const float* ws, int B, int Hq, int Hkv, int N, int D,
+    float scale, int causal, const int32_t* valid_len, int dtype) {
+  (void)causal;
+  return bwd_validate(bwd_layouts(q, q_strides, k, k_strides, v, v_strides, out, out_strides,
+                                  dout, dout_strides, dq, dq_strides, dk, dk_strides, dv,
+                                  dv_strides, Hq, Hkv, N, D),
+                      lse, ws, B, Hq, Hkv, N, D, scale, valid_len, dtype);
+}
+
+extern "C" int attn_bwd_strided(
+    const void* q, const int64_t* q_strides, const void* k, const int64_t* k_strides,
+    const void* v, const int64_t* v_strides, const void* out, const int64_t* out_strides,
+    const void* dout, const int64_t* dout_strides, const float* lse, void* dq,
+    const int64_t* dq_strides, void* dk, const int64_t* dk_strides, void* dv,
+    const int64_t* dv_strides, float* ws, int B, int Hq, int Hkv, int N, int D, float scale,
+    int causal, const int32_t* valid_len, int dtype, void* stream) {
+  return bwd_run(bwd_layouts(q, q_strides, k, k_strides, v, v_strides, out, out_strides, dout,
+                             dout_strides, dq, dq_strides, dk, dk_strides, dv, dv_strides, Hq,
+                             Hkv, N, D),
+                 lse, ws, B, Hq, Hkv, N, D, scale, causal, valid_len, dtype, stream);
 }

@@ -655,57 +655,6 @@ hipError_t dispatch_m(const Params& p, int D, bool causal, int mask_type, int64_
   return dispatch_d<DT, kMaskNone>(p, D, causal, nwg, s);
 }
 
-bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
-  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
-  return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
-}
-
-// One [B, H, N, D] tensor as (batch, head, row) element strides; rows are D contiguous elements.
-struct Layout {
-  const void* ptr;
-  int64_t sb, sh, sn;
-  int64_t H;
-  // Bytes from ptr to the end of the last row (elements of es bytes).
-  int64_t span(int B, int N, int D, int es) const {
-    return ((B - 1) * sb + (H - 1) * sh + (int64_t)(N - 1) * sn + D) * es;
-  }
-};
-
-Layout contiguous(const void* ptr, int H, int N, int D) {
-  return Layout{ptr, (int64_t)H * N * D, (int64_t)N * D, (int64_t)D, H};
-}
-
-Layout strided(const void* ptr, const int64_t* st, int H, int N, int D) {
-  if (!st) return contiguous(ptr, H, N, D);
-  return Layout{ptr, st[0], st[1], st[2], H};
-}
-
-// 16-byte aligned base, non-negative strides that are multiples of 16 bytes, rows of at least
-// D elements apart.
-bool layout_ok(const Layout& t, int D, int es) {
-  const int64_t g = 16 / es;   // elements per 16 bytes
-  if ((uintptr_t)t.ptr % 16 != 0) return false;
-  if (t.sb < 0 || t.sh < 0 || t.sn < 0) return false;
-  if (t.sb % g || t.sh % g || t.sn % g) return false;
-  return t.sn >= D;
-}
-
-// No two (batch, head, row) of the output share an element: ordered by stride, each dimension
-// of size > 1 steps past the whole extent of the dimensions below it.
-bool output_disjoint(const Layout& o, int B, int H, int N, int D) {
-  struct Dim { int64_t size, stride; } d[3] = {{B, o.sb}, {H, o.sh}, {N, o.sn}};
-  for (int i = 0; i < 3; ++i)
-    for (int j = i + 1; j < 3; ++j)
-      if (d[j].stride < d[i].stride) std::swap(d[i], d[j]);
-  int64_t extent = D;   // elements spanned by the dimensions below
-  for (int i = 0; i < 3; ++i) {
-    if (d[i].size <= 1) continue;
-    if (d[i].stride < extent) return false;
-    extent = (d[i].size - 1) * d[i].stride + extent;
-  }
-  return true;
-}
-
 // An explicit mask: element size es, strides (batch, query head, query row) in elements.
 struct MaskArg {
   const void* ptr;
@@ -921,4 +870,4 @@ extern "C" const char* attn_status_string(int status) {
   }
 }
 
-extern "C" int attn_version(void) { return 4; }
+extern "C" int attn_version(void) { return 5; }

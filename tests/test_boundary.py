@@ -27,7 +27,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["attn_bwd", "attn_bwd_validate", "attn_fwd",
+    assert declared_functions() == ["attn_bwd", "attn_bwd_strided", "attn_bwd_strided_validate",
+                                    "attn_bwd_validate", "attn_fwd",
                                     "attn_fwd_masked", "attn_fwd_masked_validate",
                                     "attn_fwd_strided", "attn_fwd_strided_validate",
                                     "attn_fwd_validate", "attn_status_string", "attn_version"]
@@ -43,7 +44,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_version(lib):
-    assert sdp.attn_version() == 4
+    assert sdp.attn_version() == 5
 
 
 def test_status_strings(lib):
@@ -296,3 +297,38 @@ def test_f32_layouts(lib):
     assert sdp.attn_fwd_masked_validate(Q, None, K, None, V, None, O, None, L, SB, SH, 2, MN, 128,
                                         0.088, 1, VL, MK, sdp.ATTN_MASK_KEEP_U8, None,
                                         f32) == sdp.ATTN_ERR_DTYPE
+
+
+# ---- attn_bwd_strided_validate
+def bscall(**kw):
+    a = dict(q=Q, qs=None, k=K, ks=None, v=V, vs=None, out=O, os=None, dout=DO, gs=None, lse=L,
+             dq=DQ, dqs=None, dk=DK, dks=None, dv=DV, dvs=None, ws=DL, B=2, Hq=8, Hkv=2, N=1000,
+             D=128, scale=0.088, causal=1, valid_len=VL, dtype=sdp.ATTN_BF16)
+    a.update(kw)
+    return sdp.attn_bwd_strided_validate(
+        a["q"], a["qs"], a["k"], a["ks"], a["v"], a["vs"], a["out"], a["os"], a["dout"], a["gs"],
+        a["lse"], a["dq"], a["dqs"], a["dk"], a["dks"], a["dv"], a["dvs"], a["ws"], a["B"],
+        a["Hq"], a["Hkv"], a["N"], a["D"], a["scale"], a["causal"], a["valid_len"], a["dtype"])
+
+
+def test_bwd_strided_validate(lib):
+    def bnhd_(H, N=1000, D=128):
+        return (N * H * D, D, H * D)
+    assert bscall() == sdp.ATTN_OK
+    # every tensor [B, N, H, D]
+    assert bscall(qs=bnhd_(8), ks=bnhd_(2), vs=bnhd_(2), os=bnhd_(8), gs=bnhd_(8),
+                  dqs=bnhd_(8), dks=bnhd_(2), dvs=bnhd_(2)) == sdp.ATTN_OK
+    # padded input rows; a transposed dO
+    assert bscall(qs=(8 * 1000 * 136, 1000 * 136, 136), gs=bnhd_(8)) == sdp.ATTN_OK
+    # a row stride that is not a multiple of 8 elements, a negative stride
+    assert bscall(ks=(2 * 1000 * 132, 1000 * 132, 132)) == sdp.ATTN_ERR_LAYOUT
+    assert bscall(vs=(-1000 * 128 * 2, 1000 * 128, 128)) == sdp.ATTN_ERR_LAYOUT
+    # gradient rows that collide (head stride 0), rows closer than D
+    assert bscall(dqs=(1000 * 128, 0, 128)) == sdp.ATTN_ERR_LAYOUT
+    assert bscall(dks=(2 * 1000 * 64, 1000 * 64, 64)) == sdp.ATTN_ERR_LAYOUT
+    # a strided dk whose span reaches into v
+    assert bscall(dk=V - 1024, dks=bnhd_(2)) == sdp.ATTN_ERR_ALIAS
+    # K and V shared by the batches (zero batch stride) are fine as inputs
+    assert bscall(ks=(0, 1000 * 128, 128), vs=(0, 1000 * 128, 128)) == sdp.ATTN_OK
+    # a row stride so large that a head no longer fits 32-bit buffer offsets
+    assert bscall(ks=(0, 0, 1 << 20)) == sdp.ATTN_ERR_SHAPE

@@ -231,3 +231,75 @@ def test_autograd_function_matches_entry_point():
     assert torch.equal(out, o2)
     for a, b in zip((q.grad, k.grad, v.grad), g):
         assert torch.equal(a, b)
+
+
+# ---- strided tensors (attn_bwd_strided): the same logical values in other layouts
+BWD_STRIDED = [
+    ("bnhd", "bf16", 128, True, True, 2, 8, 2, 300),
+    ("bnhd", "f16", 64, False, False, 2, 4, 4, 200),
+    ("padded_rows", "bf16", 64, True, False, 2, 6, 3, 257),
+    ("packed_qkv", "f16", 128, True, True, 2, 4, 4, 190),
+    ("transposed_dout", "bf16", 32, True, True, 3, 4, 2, 150),
+]
+
+
+@pytest.mark.parametrize("cfg", BWD_STRIDED, ids=lambda c: "%s-%s-D%d-c%d-p%d-B%d-H%d-%d-N%d" % c)
+def test_bwd_strided_layouts(cfg):
+    import torch
+    mode, dtype, D, causal, padded, B, Hq, Hkv, N = cfg
+    case = inputs.make_case(B, Hq, Hkv, N, D, dtype, causal, padded, seed=[213, D, N, B])
+    dout_bits = inputs.make_grad(case, [213, D, N, B])
+    log("bwd strided case %s valid_len %s" % (cfg, case.valid_len))
+    q, k, v = (to_device(x, dtype) for x in (case.q_bits, case.k_bits, case.v_bits))
+    do = to_device(dout_bits, dtype)
+    vl = None
+    if case.valid_len is not None:
+        vl = torch.from_numpy(case.valid_len.astype(np.int32)).cuda()
+    layout = "bhnd"
+    if mode == "bnhd":
+        q, k, v, do = (t.transpose(1, 2).contiguous() for t in (q, k, v, do))
+        layout = "bnhd"
+    elif mode == "padded_rows":
+        def pad(t, extra):
+            big = torch.full(t.shape[:3] + (t.shape[3] + extra,), float("nan"), dtype=t.dtype,
+                             device=t.device)
+            big[..., :t.shape[3]] = t
+            return big[..., :t.shape[3]]
+        q, k, v, do = pad(q, 8), pad(k, 24), pad(v, 16), pad(do, 8)
+    elif mode == "packed_qkv":
+        packed = torch.stack([t.transpose(1, 2) for t in (q, k, v)], dim=2).contiguous()
+        q, k, v = (packed[:, :, i].transpose(1, 2) for i in range(3))
+    elif mode == "transposed_dout":
+        do = do.transpose(1, 2).contiguous().transpose(1, 2)   # [B, H, N, D] view of [B, N, H, D]
+    out, lse = sdp.forward(q, k, v, causal=causal, valid_len=vl, scale=case.scale, layout=layout)
+    dq, dk, dv = sdp.backward(q, k, v, out, do, lse, causal=causal, valid_len=vl,
+                              scale=case.scale, layout=layout)
+    torch.cuda.synchronize()
+    if layout == "bnhd":
+        dq, dk, dv = (t.transpose(1, 2) for t in (dq, dk, dv))
+    got = [from_device(t, dtype) for t in (dq, dk, dv)]
+    qw, kw, vw = case.widened()
+    rq, rk, rv = oracle.attn_bwd(qw, kw, vw, inputs.widen(dout_bits, dtype), case.scale, causal,
+                                 case.valid_len)
+    e = [check_grad(n, g, r, dtype, str(cfg)) for n, g, r in zip(("dQ", "dK", "dV"), got,
+                                                                   (rq, rk, rv))]
+    log("%s: rel err dQ %.2e dK %.2e dV %.2e" % (cfg, *e))
+
+
+def test_autograd_bnhd_matches_contiguous():
+    """attention(layout="bnhd") on [B, N, H, D] tensors gives the gradients of the contiguous
+    [B, H, N, D] call, transposed (same kernels, other strides: bitwise equal)."""
+    import torch
+    case = inputs.make_case(2, 4, 2, 300, 64, "f16", True, False, seed=215)
+    dout = to_device(inputs.make_grad(case, 215), "f16")
+    base = [to_device(x, "f16") for x in (case.q_bits, case.k_bits, case.v_bits)]
+    a = [t.clone().requires_grad_() for t in base]
+    b = [t.transpose(1, 2).contiguous().requires_grad_() for t in base]
+    oa = sdp.attention(*a, causal=True, scale=case.scale)
+    oa.backward(dout)
+    ob = sdp.attention(*b, causal=True, scale=case.scale, layout="bnhd")
+    ob.backward(dout.transpose(1, 2))
+    torch.cuda.synchronize()
+    assert torch.equal(oa, ob.transpose(1, 2))
+    for x, y in zip(a, b):
+        assert torch.equal(x.grad, y.grad.transpose(1, 2))
