@@ -332,3 +332,21 @@ def test_bwd_strided_validate(lib):
     assert bscall(ks=(0, 1000 * 128, 128), vs=(0, 1000 * 128, 128)) == sdp.ATTN_OK
     # a row stride so large that a head no longer fits 32-bit buffer offsets
     assert bscall(ks=(0, 0, 1 << 20)) == sdp.ATTN_ERR_SHAPE
+
+
+def test_no_fallback_path():
+    """The product path fails loudly: a missing library is an ImportError, CPU tensors are
+    rejected, and no module of the package refers to the oracle."""
+    with pytest.raises(ImportError):
+        sdp.load_library(os.path.join(os.path.dirname(sdp.library_path()), "missing_libattn.so"))
+    import torch
+    x = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        sdp.forward(x, x, x, causal=True)
+    pkg = os.path.dirname(sdp.__file__)
+    pattern = re.compile(r"^\s*(import\s+oracle|from\s+oracle\b)|liboracle|attn_oracle", re.M)
+    for root, _, files in os.walk(pkg):
+        for name in files:
+            if name.endswith((".py", ".hip", ".h")):
+                text = open(os.path.join(root, name)).read()
+                assert not pattern.search(text), "%s uses the oracle" % name
