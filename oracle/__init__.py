@@ -48,6 +48,11 @@ def load(path: str = _LIB_PATH) -> ctypes.CDLL:
     h.restype = ctypes.c_int
     h.argtypes = [ctypes.c_void_p] * 7 + [ctypes.c_int64] * 5 + [
         ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_int]
+    hm = lib.oracle_attn_bwd_masked
+    hm.restype = ctypes.c_int
+    hm.argtypes = [ctypes.c_void_p] * 7 + [ctypes.c_int64] * 5 + [
+        ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+        ctypes.c_void_p, ctypes.c_int]
     lib.oracle_max_threads.restype = ctypes.c_int
     return lib
 
@@ -64,6 +69,21 @@ def _get_lib() -> ctypes.CDLL:
 
 def max_threads() -> int:
     return int(_get_lib().oracle_max_threads())
+
+
+def _mask_arg(keep_mask, add_mask, B, Hq, N):
+    """(kind, array, element strides) of an explicit mask broadcast to [B, Hq, N, N]."""
+    if keep_mask is not None and add_mask is not None:
+        raise ValueError("give at most one of keep_mask and add_mask")
+    if keep_mask is None and add_mask is None:
+        return 0, None, None
+    kind = 1 if keep_mask is not None else 2
+    m = keep_mask if kind == 1 else add_mask
+    m = np.asarray(m, dtype=np.uint8 if kind == 1 else np.float64)
+    m = np.broadcast_to(m, (B, Hq, N, N))
+    if m.strides[3] != m.itemsize:
+        m = np.ascontiguousarray(m)
+    return kind, m, (ctypes.c_int64 * 3)(*[st // m.itemsize for st in m.strides[:3]])
 
 
 def attn_fwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal: bool,
@@ -103,19 +123,8 @@ def attn_fwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal: 
         out = np.empty((nrows, D), np.float64)
         lse = np.empty((nrows,), np.float64)
         rows_ptr = rows.ctypes.data
-    kind, mptr, mst = 0, None, None
-    if keep_mask is not None and add_mask is not None:
-        raise ValueError("give at most one of keep_mask and add_mask")
-    if keep_mask is not None or add_mask is not None:
-        kind = 1 if keep_mask is not None else 2
-        m = keep_mask if kind == 1 else add_mask
-        m = np.asarray(m, dtype=np.uint8 if kind == 1 else np.float64)
-        m = np.broadcast_to(m, (B, Hq, N, N))
-        if m.strides[3] != m.itemsize:
-            m = np.ascontiguousarray(m)
-        mask_arr = m   # keep alive during the call
-        mptr = mask_arr.ctypes.data
-        mst = (ctypes.c_int64 * 3)(*[st // m.itemsize for st in m.strides[:3]])
+    kind, mask_arr, mst = _mask_arg(keep_mask, add_mask, B, Hq, N)
+    mptr = mask_arr.ctypes.data if mask_arr is not None else None
     rc = lib.oracle_attn_fwd_masked(q.ctypes.data, k.ctypes.data, v.ctypes.data, out.ctypes.data,
                                     lse.ctypes.data, B, Hq, Hkv, N, D, float(scale),
                                     int(bool(causal)), vl_ptr, mptr, kind, mst, rows_ptr, nrows,
@@ -127,9 +136,11 @@ def attn_fwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float, causal: 
 
 def attn_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray, scale: float,
              causal: bool, valid_len: Optional[np.ndarray] = None, threads: int = 0,
-             lib: Optional[ctypes.CDLL] = None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
-    """Gradients (dQ, dK, dV) in fp64 of sum(O * dout) for the forward above (no mask but
-    causal / valid_len). q, dout: [B,Hq,N,D]; k, v: [B,Hkv,N,D]."""
+             lib: Optional[ctypes.CDLL] = None, keep_mask=None,
+             add_mask=None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Gradients (dQ, dK, dV) in fp64 of sum(O * dout) for the forward above (causal /
+    valid_len and an optional explicit mask as in attn_fwd). q, dout: [B,Hq,N,D];
+    k, v: [B,Hkv,N,D]."""
     lib = lib or _get_lib()
     q, k, v, dout = (np.ascontiguousarray(x, dtype=np.float64) for x in (q, k, v, dout))
     B, Hq, N, D = q.shape
@@ -145,9 +156,12 @@ def attn_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray, scal
     dq = np.empty_like(q)
     dk = np.empty_like(k)
     dv = np.empty_like(v)
-    rc = lib.oracle_attn_bwd(q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data,
-                             dq.ctypes.data, dk.ctypes.data, dv.ctypes.data, B, Hq, Hkv, N, D,
-                             float(scale), int(bool(causal)), vl_ptr, int(threads))
+    kind, mask_arr, mst = _mask_arg(keep_mask, add_mask, B, Hq, N)
+    mptr = mask_arr.ctypes.data if mask_arr is not None else None
+    rc = lib.oracle_attn_bwd_masked(q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                    dout.ctypes.data, dq.ctypes.data, dk.ctypes.data,
+                                    dv.ctypes.data, B, Hq, Hkv, N, D, float(scale),
+                                    int(bool(causal)), vl_ptr, mptr, kind, mst, int(threads))
     if rc != 0:
         raise ValueError("oracle_attn_bwd rejected its arguments (rc=%d)" % rc)
     return dq, dk, dv

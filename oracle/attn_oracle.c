@@ -224,12 +224,21 @@ int oracle_max_threads(void)
  * in the three passes of the forward (no value from the device is used). Work is split over
  * (batch, KV head), so that the dK and dV sums of one KV head belong to one thread.
  * q, dout, dq: [B,Hq,N,D]; k, v, dk, dv: [B,Hkv,N,D]; contiguous doubles. Returns 0 or -1.
+ *
+ * With an explicit mask (as in oracle_attn_fwd_masked: kind 1 keep bytes, kind 2 additive
+ * doubles, element strides (batch, query head, query row), keys contiguous) the visible sets
+ * J_i and the scores are the masked forward's: an additive value a_ij enters the score as
+ * s_ij = scale q.k + a_ij (so w_ij includes it) and is a constant: dS_ij and every gradient keep
+ * the forms above, with dQ and dK carrying only the scale of the q.k term.
  */
-int oracle_attn_bwd(const double *q, const double *k, const double *v, const double *dout,
-                    double *dq, double *dk, double *dv, int64_t B, int64_t Hq, int64_t Hkv,
-                    int64_t N, int64_t D, double scale, int causal, const int32_t *valid_len,
-                    int threads)
+int oracle_attn_bwd_masked(const double *q, const double *k, const double *v,
+                           const double *dout, double *dq, double *dk, double *dv, int64_t B,
+                           int64_t Hq, int64_t Hkv, int64_t N, int64_t D, double scale,
+                           int causal, const int32_t *valid_len, const void *mask, int mask_kind,
+                           const int64_t *mask_strides, int threads)
 {
+    if (mask_kind < 0 || mask_kind > 2 || (mask_kind != 0 && (!mask || !mask_strides)))
+        return -1;
     if (!q || !k || !v || !dout || !dq || !dk || !dv)
         return -1;
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 || D <= 0 || Hq % Hkv != 0)
@@ -260,7 +269,6 @@ int oracle_attn_bwd(const double *q, const double *k, const double *v, const dou
                 if (valid > N)
                     valid = N;
             }
-            const mask_row none = {0, NULL, NULL};
             for (int64_t x = 0; x < N * D; ++x)
                 dk_head[x] = dv_head[x] = 0.0;
             for (int64_t hq = kv * group; hq < (kv + 1) * group; ++hq) {
@@ -271,16 +279,28 @@ int oracle_attn_bwd(const double *q, const double *k, const double *v, const dou
                     double *dq_row = dq + (bh * N + i) * D;
                     int64_t j, d, visible = 0;
                     double m = -INFINITY, l = 0.0, delta = 0.0;
+                    mask_row mr = {mask_kind, NULL, NULL};
+                    if (mask_kind != 0) {
+                        int64_t off = b * mask_strides[0] + hq * mask_strides[1] +
+                                      i * mask_strides[2];
+                        if (mask_kind == 1)
+                            mr.keep = (const uint8_t *)mask + off;
+                        else
+                            mr.add = (const double *)mask + off;
+                    }
+                    const mask_row *mrp = &mr;
                     for (d = 0; d < D; ++d)
                         dq_row[d] = 0.0;
                     /* weights, as in the forward's three passes */
                     for (j = 0; j < N; ++j) {
-                        if (!key_visible(i, j, causal, valid, &none))
+                        if (!key_visible(i, j, causal, valid, mrp))
                             continue;
                         double dot = 0.0;
                         for (d = 0; d < D; ++d)
                             dot += q_row[d] * k_head[j * D + d];
                         w[j] = scale * dot;
+                        if (mask_kind == 2)
+                            w[j] += mr.add[j];
                         if (w[j] > m)
                             m = w[j];
                         ++visible;
@@ -288,10 +308,10 @@ int oracle_attn_bwd(const double *q, const double *k, const double *v, const dou
                     if (visible == 0)
                         continue;
                     for (j = 0; j < N; ++j)
-                        if (key_visible(i, j, causal, valid, &none))
+                        if (key_visible(i, j, causal, valid, mrp))
                             l += exp(w[j] - m);
                     for (j = 0; j < N; ++j) {
-                        if (!key_visible(i, j, causal, valid, &none))
+                        if (!key_visible(i, j, causal, valid, mrp))
                             continue;
                         w[j] = exp(w[j] - m) / l;
                         double dot = 0.0;
@@ -301,7 +321,7 @@ int oracle_attn_bwd(const double *q, const double *k, const double *v, const dou
                         delta += w[j] * dot;
                     }
                     for (j = 0; j < N; ++j) {
-                        if (!key_visible(i, j, causal, valid, &none))
+                        if (!key_visible(i, j, causal, valid, mrp))
                             continue;
                         const double ds = w[j] * (dp[j] - delta);
                         for (d = 0; d < D; ++d) {
@@ -317,4 +337,13 @@ int oracle_attn_bwd(const double *q, const double *k, const double *v, const dou
         free(dp);
     }
     return bad ? -1 : 0;
+}
+
+int oracle_attn_bwd(const double *q, const double *k, const double *v, const double *dout,
+                    double *dq, double *dk, double *dv, int64_t B, int64_t Hq, int64_t Hkv,
+                    int64_t N, int64_t D, double scale, int causal, const int32_t *valid_len,
+                    int threads)
+{
+    return oracle_attn_bwd_masked(q, k, v, dout, dq, dk, dv, B, Hq, Hkv, N, D, scale, causal,
+                                  valid_len, NULL, 0, NULL, threads);
 }

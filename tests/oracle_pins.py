@@ -17,7 +17,12 @@ copies of it with planted mistakes (test_oracle_mutants.py). The pins are:
   * special cases: fully masked rows give exactly 0 and -inf; very large scores stay finite;
   * explicit masks (MASK_PINS, for callables that also take keep_mask / add_mask): torch's SDPA
     with boolean and float attn_mask, the identities that tie a mask to no mask, to causal
-    masking and to valid_len, and the closed form of an additive log-weight mask.
+    masking and to valid_len, and the closed form of an additive log-weight mask;
+  * the backward (BWD_PINS, BWD_MASK_PINS, for gradient callables ``fn_bwd(q, k, v, dout, scale,
+    causal, valid_len=None, **mask)``): torch's fp64 autograd through SDPA (with causal, padding,
+    GQA and explicit masks), central finite differences through the forward oracle, the zero-sum
+    and exact-zero identities, GQA = repeated KV heads, and the mask identities (no-op masks,
+    causal as a mask, keep = additive -inf, per-row shift invariance).
 """
 from __future__ import annotations
 
@@ -548,7 +553,99 @@ def pin_bwd_gqa_repeat(fn_bwd, fn=None):
     np.testing.assert_allclose(dv, rv.reshape(B, Hkv, g, N, D).sum(2), rtol=0, atol=1e-13)
 
 
+def _mask_grad_case(seed, kind, B=2, Hq=4, Hkv=2, N=7, D=5, shape=None):
+    """A masked backward case where every row keeps key 0 (no empty rows, which torch's SDPA
+    turns into NaN): (rng, q, k, v, dout, mask)."""
+    rng = _rng(seed)
+    q, k, v, do = (_normal(rng, s) for s in ((B, Hq, N, D), (B, Hkv, N, D), (B, Hkv, N, D),
+                                             (B, Hq, N, D)))
+    shape = shape or (B, Hq, N, N)
+    if kind == "keep":
+        m = (rng.random(shape) < 0.6).astype(np.uint8)
+        m[..., 0] = 1
+    else:
+        m = rng.normal(0.0, 2.0, shape)
+        m[rng.random(shape) < 0.25] = -np.inf
+        m[..., 0] = rng.normal(0.0, 1.0, shape[:-1])
+    return rng, q, k, v, do, m
+
+
+def pin_bwd_mask_autograd(fn_bwd, fn=None):
+    """Keep and additive masks (per (batch, head) and broadcast), with causal and valid_len:
+    match torch's fp64 autograd through scaled_dot_product_attention given the combined mask as
+    its attn_mask (boolean: takes part where True; float: added to the scaled scores)."""
+    for idx in range(8):
+        kind = "keep" if idx % 2 == 0 else "add"
+        B, Hq, Hkv, N, D = (2, 4, 2, 7, 5) if idx < 4 else (1, 3, 1, 9, 3)
+        shape = (B, Hq, N, N) if idx % 3 else (1, 1, N, N)
+        rng, q, k, v, do, m = _mask_grad_case([61, idx], kind, B, Hq, Hkv, N, D, shape)
+        causal = bool(idx % 4 >= 2)
+        vl = rng.integers(1, N + 1, size=B).astype(np.int32) if idx in (1, 2, 5, 6) else None
+        scale = float(rng.uniform(0.3, 1.2))
+        kw = {"keep_mask": m} if kind == "keep" else {"add_mask": m}
+        dq, dk, dv = fn_bwd(q, k, v, do, scale, causal, vl, **kw)
+        vis = torch.from_numpy(_visible_mask(B, N, causal, vl))[:, None]
+        mb = np.broadcast_to(m, (B, Hq, N, N)).copy()
+        if kind == "keep":
+            tmask = vis & torch.from_numpy(mb.astype(bool))
+        else:
+            tmask = torch.from_numpy(mb).masked_fill(~vis, float("-inf"))
+        tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+        o = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=tmask, scale=scale,
+                                           enable_gqa=(Hq != Hkv))
+        (o * torch.from_numpy(do)).sum().backward()
+        for got, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+            np.testing.assert_allclose(got, ref.numpy(), rtol=0, atol=1e-12)
+
+
+def pin_bwd_mask_identities(fn_bwd, fn=None):
+    """An all-ones keep mask or an additive 0 gives the unmasked gradients; a lower-triangular
+    keep mask gives the causal ones; additive -inf where a keep mask is 0 gives that keep mask's;
+    an additive constant per query row changes no gradient (softmax shift invariance)."""
+    rng, q, k, v, do, keep = _mask_grad_case([67], "keep")
+    B, Hq, N = q.shape[0], q.shape[1], q.shape[2]
+    base = fn_bwd(q, k, v, do, 0.7, False)
+    causal = fn_bwd(q, k, v, do, 0.7, True)
+    vl = np.array([5, 3], np.int32)
+
+    def same(a, b):
+        for x, y in zip(a, b):
+            np.testing.assert_allclose(x, y, rtol=0, atol=1e-12)
+
+    same(fn_bwd(q, k, v, do, 0.7, False, keep_mask=np.ones((N, N), np.uint8)), base)
+    same(fn_bwd(q, k, v, do, 0.7, False, add_mask=np.zeros((B, Hq, N, N))), base)
+    same(fn_bwd(q, k, v, do, 0.7, False, keep_mask=np.tril(np.ones((N, N), np.uint8))), causal)
+    add = np.where(keep.astype(bool), 0.0, -np.inf)
+    same(fn_bwd(q, k, v, do, 0.7, True, vl, add_mask=add),
+         fn_bwd(q, k, v, do, 0.7, True, vl, keep_mask=keep))
+    shift = rng.normal(0.0, 3.0, (B, Hq, N, 1)) * np.ones((1, 1, 1, N))
+    same(fn_bwd(q, k, v, do, 0.7, True, vl, add_mask=shift), fn_bwd(q, k, v, do, 0.7, True, vl))
+
+
+def pin_bwd_mask_finite_difference(fn_bwd, fn):
+    """Central differences of sum(O * dO) through the masked forward callable, with a keep mask
+    and with an additive mask, on a tiny causal GQA case."""
+    for kind in ("keep", "add"):
+        rng, q, k, v, do, m = _mask_grad_case([71, len(kind)], kind, 1, 2, 1, 5, 3)
+        kw = {"keep_mask": m} if kind == "keep" else {"add_mask": m}
+        dq, dk, dv = fn_bwd(q, k, v, do, 0.8, True, None, **kw)
+        h = 1e-6
+        for x, g in ((q, dq), (k, dk), (v, dv)):
+            num = np.zeros_like(x)
+            for idx in np.ndindex(x.shape):
+                keep = x[idx]
+                x[idx] = keep + h
+                op = fn(q, k, v, 0.8, True, None, **kw)[0]
+                x[idx] = keep - h
+                om = fn(q, k, v, 0.8, True, None, **kw)[0]
+                x[idx] = keep
+                num[idx] = ((op - om) * do).sum() / (2 * h)
+            np.testing.assert_allclose(g, num, rtol=0, atol=1e-6)
+
+
+
 BWD_PINS = [pin_bwd_autograd, pin_bwd_finite_difference, pin_bwd_identities, pin_bwd_gqa_repeat]
+BWD_MASK_PINS = [pin_bwd_mask_autograd, pin_bwd_mask_identities, pin_bwd_mask_finite_difference]
 
 ALL_PINS = [pin_library_sdpa, pin_identity_weights, pin_q_zero, pin_constant_v,
             pin_causal_first_row, pin_two_keys, pin_empty_rows, pin_key_permutation,

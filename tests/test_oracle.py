@@ -40,10 +40,11 @@ def test_thread_count_does_not_change_results():
 
 
 
-def _bwd(q, k, v, dout, scale, causal, valid_len=None):
-    return oracle.attn_bwd(q, k, v, dout, scale, causal, valid_len, threads=2)
+def _bwd(q, k, v, dout, scale, causal, valid_len=None, **mask):
+    return oracle.attn_bwd(q, k, v, dout, scale, causal, valid_len, threads=2, **mask)
 
 
-@pytest.mark.parametrize("pin", oracle_pins.BWD_PINS, ids=lambda p: p.__name__)
+@pytest.mark.parametrize("pin", oracle_pins.BWD_PINS + oracle_pins.BWD_MASK_PINS,
+                         ids=lambda p: p.__name__)
 def test_bwd_pin(pin):
     pin(_bwd, _fn)

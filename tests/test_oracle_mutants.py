@@ -103,6 +103,17 @@ BWD_MUTANTS = [
     ("bwd_first_head_only", "for (int64_t hq = kv * group; hq < (kv + 1) * group; ++hq)",
      "for (int64_t hq = kv * group; hq < kv * group + 1; ++hq)"),
     ("bwd_unnormalised_weights", "w[j] = exp(w[j] - m) / l;", "w[j] = exp(w[j] - m);"),
+    # explicit masks in the backward
+    ("bwd_mask_ignored", "const mask_row *mrp = &mr;",
+     "const mask_row none = {0, NULL, NULL};\n                    const mask_row *mrp = &none;"),
+    ("bwd_add_mask_dropped", "                            w[j] += mr.add[j];",
+     "                            w[j] += 0.0;"),
+    ("bwd_add_mask_subtracted", "                            w[j] += mr.add[j];",
+     "                            w[j] -= mr.add[j];"),
+    ("bwd_mask_row_index", "                                      i * mask_strides[2];",
+     "                                      0 * mask_strides[2];"),
+    ("bwd_mask_head_index", "int64_t off = b * mask_strides[0] + hq * mask_strides[1] +\n",
+     "int64_t off = b * mask_strides[0] + 0 * mask_strides[1] +\n"),
 ]
 
 
@@ -116,15 +127,16 @@ def test_bwd_mutant_is_caught(source, name, orig, mut):
             f.write(text)
         lib = oracle.load(oracle.build(src, os.path.join(d, "libmutant.so")))
 
-        def fn(q, k, v, scale, causal, valid_len=None, rows=None):
+        def fn(q, k, v, scale, causal, valid_len=None, rows=None, **mask):
             return oracle.attn_fwd(q, k, v, scale, causal, valid_len, rows=rows, threads=2,
-                                   lib=lib)
+                                   lib=lib, **mask)
 
-        def fn_bwd(q, k, v, dout, scale, causal, valid_len=None):
-            return oracle.attn_bwd(q, k, v, dout, scale, causal, valid_len, threads=2, lib=lib)
+        def fn_bwd(q, k, v, dout, scale, causal, valid_len=None, **mask):
+            return oracle.attn_bwd(q, k, v, dout, scale, causal, valid_len, threads=2, lib=lib,
+                                   **mask)
 
         caught = []
-        for pin in oracle_pins.BWD_PINS:
+        for pin in oracle_pins.BWD_PINS + oracle_pins.BWD_MASK_PINS:
             try:
                 pin(fn_bwd, fn)
             except (AssertionError, ValueError, FloatingPointError):
