@@ -277,11 +277,39 @@ int attn_bwd_strided_validate(const void *q, const int64_t *q_strides, const voi
                               int N, int D, float scale, int causal, const int32_t *valid_len,
                               int dtype);
 
+/*
+ * attn_bwd_masked -- attn_bwd_strided plus the explicit mask of attn_fwd_masked (the same mask,
+ * type and strides the forward was given; the article's §2.1-2.2 masks): the gradients of that
+ * masked forward. The mask is a constant (no gradient). Returns as attn_bwd_strided; mask
+ * errors as attn_fwd_masked (ATTN_ERR_MASK, ATTN_ERR_NULL, ATTN_ERR_LAYOUT, ATTN_ERR_SHAPE, and
+ * ATTN_ERR_ALIAS when an output overlaps the mask).
+ */
+int attn_bwd_masked(const void *q, const int64_t *q_strides, const void *k,
+                    const int64_t *k_strides, const void *v, const int64_t *v_strides,
+                    const void *out, const int64_t *out_strides, const void *dout,
+                    const int64_t *dout_strides, const float *lse, void *dq,
+                    const int64_t *dq_strides, void *dk, const int64_t *dk_strides, void *dv,
+                    const int64_t *dv_strides, float *ws, int B, int Hq, int Hkv, int N, int D,
+                    float scale, int causal, const int32_t *valid_len, const void *mask,
+                    int mask_type, const int64_t *mask_strides, int dtype, void *stream);
+
+/* attn_bwd_masked_validate -- the host-only argument check of attn_bwd_masked. */
+int attn_bwd_masked_validate(const void *q, const int64_t *q_strides, const void *k,
+                             const int64_t *k_strides, const void *v, const int64_t *v_strides,
+                             const void *out, const int64_t *out_strides, const void *dout,
+                             const int64_t *dout_strides, const float *lse, const void *dq,
+                             const int64_t *dq_strides, const void *dk,
+                             const int64_t *dk_strides, const void *dv,
+                             const int64_t *dv_strides, const float *ws, int B, int Hq, int Hkv,
+                             int N, int D, float scale, int causal, const int32_t *valid_len,
+                             const void *mask, int mask_type, const int64_t *mask_strides,
+                             int dtype);
+
 /* attn_status_string -- a static, NUL-terminated description of a return code (never NULL). */
 const char *attn_status_string(int status);
 
-/* attn_version -- the library's interface version, currently 5 (2 added attn_fwd_strided, 3
- * attn_fwd_masked, 4 attn_bwd, 5 attn_bwd_strided). */
+/* attn_version -- the library's interface version, currently 6 (2 added attn_fwd_strided, 3
+ * attn_fwd_masked, 4 attn_bwd, 5 attn_bwd_strided, 6 attn_bwd_masked). */
 int attn_version(void);
 
 #ifdef __cplusplus

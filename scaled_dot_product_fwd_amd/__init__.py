@@ -8,7 +8,7 @@ Raw entry points (same names and argument order as the C ABI; pointers are integ
 arguments are 3-sequences of element strides or None):
     attn_fwd, attn_fwd_validate, attn_fwd_strided, attn_fwd_strided_validate,
     attn_fwd_masked, attn_fwd_masked_validate, attn_bwd, attn_bwd_validate, attn_bwd_strided,
-    attn_bwd_strided_validate,
+    attn_bwd_strided_validate, attn_bwd_masked, attn_bwd_masked_validate,
     attn_status_string, attn_version
 Convenience for torch tensors (device memory and streams only):
     forward(q, k, v, causal=..., valid_len=None, scale=None, out=None, lse=None, layout="bhnd",
@@ -25,7 +25,8 @@ from typing import Optional, Tuple
 __all__ = ["ATTN_F16", "ATTN_BF16", "ATTN_F32", "AttnError", "attn_fwd", "attn_fwd_validate",
            "attn_fwd_strided", "attn_fwd_strided_validate", "attn_fwd_masked",
            "attn_fwd_masked_validate", "attn_bwd", "attn_bwd_validate", "attn_bwd_strided",
-           "attn_bwd_strided_validate", "attention",
+           "attn_bwd_strided_validate", "attn_bwd_masked", "attn_bwd_masked_validate",
+           "attention",
            "backward", "attn_status_string",
            "attn_version", "forward", "library_path", "load_library"]
 
@@ -110,6 +111,14 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_bwd_strided_validate.argtypes = ([_vp, _i64p] * 5 + [_vp] + [_vp, _i64p] * 3 +
                                               [_vp] + [_c_int] * 5 + [_c_float, _c_int, _vp,
                                                                       _c_int])
+    lib.attn_bwd_masked.restype = _c_int
+    lib.attn_bwd_masked.argtypes = ([_vp, _i64p] * 5 + [_vp] + [_vp, _i64p] * 3 + [_vp] +
+                                    [_c_int] * 5 + [_c_float, _c_int, _vp, _vp, _c_int, _i64p,
+                                                    _c_int, _vp])
+    lib.attn_bwd_masked_validate.restype = _c_int
+    lib.attn_bwd_masked_validate.argtypes = ([_vp, _i64p] * 5 + [_vp] + [_vp, _i64p] * 3 +
+                                             [_vp] + [_c_int] * 5 + [_c_float, _c_int, _vp, _vp,
+                                                                     _c_int, _i64p, _c_int])
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_status_string.argtypes = [_c_int]
     lib.attn_version.restype = _c_int
@@ -226,6 +235,30 @@ def attn_bwd_strided_validate(q, q_strides, k, k_strides, v, v_strides, out, out
         valid_len, dtype)
 
 
+def attn_bwd_masked(q, q_strides, k, k_strides, v, v_strides, out, out_strides, dout,
+                    dout_strides, lse, dq, dq_strides, dk, dk_strides, dv, dv_strides, ws, B, Hq,
+                    Hkv, N, D, scale, causal, valid_len, mask, mask_type, mask_strides, dtype,
+                    stream) -> int:
+    """C ``attn_bwd_masked``; pointers as integers, strides as 3-sequences or None."""
+    return load_library().attn_bwd_masked(
+        q, _strides(q_strides), k, _strides(k_strides), v, _strides(v_strides), out,
+        _strides(out_strides), dout, _strides(dout_strides), lse, dq, _strides(dq_strides), dk,
+        _strides(dk_strides), dv, _strides(dv_strides), ws, B, Hq, Hkv, N, D, scale, int(causal),
+        valid_len, mask, mask_type, _strides(mask_strides), dtype, stream)
+
+
+def attn_bwd_masked_validate(q, q_strides, k, k_strides, v, v_strides, out, out_strides, dout,
+                             dout_strides, lse, dq, dq_strides, dk, dk_strides, dv, dv_strides,
+                             ws, B, Hq, Hkv, N, D, scale, causal, valid_len, mask, mask_type,
+                             mask_strides, dtype) -> int:
+    """C ``attn_bwd_masked_validate``: host-only argument check, no HIP call."""
+    return load_library().attn_bwd_masked_validate(
+        q, _strides(q_strides), k, _strides(k_strides), v, _strides(v_strides), out,
+        _strides(out_strides), dout, _strides(dout_strides), lse, dq, _strides(dq_strides), dk,
+        _strides(dk_strides), dv, _strides(dv_strides), ws, B, Hq, Hkv, N, D, scale, int(causal),
+        valid_len, mask, mask_type, _strides(mask_strides), dtype)
+
+
 def attn_status_string(status: int) -> str:
     return load_library().attn_status_string(status).decode()
 
@@ -243,6 +276,33 @@ def _dtype_code(t) -> int:
     if t.dtype == torch.float32:
         return ATTN_F32
     raise TypeError("q/k/v must be float16, bfloat16 or float32, got %s" % t.dtype)
+
+
+def _mask_view(attn_mask, dtype, B, Hq, N):
+    """(a [B, Hq, N, N] view of attn_mask, its attn_mask_t): bool / uint8 keep masks, masks of
+    the inputs' dtype are additive; 2-D and 3-D masks broadcast over batch and heads."""
+    import torch
+    m = attn_mask
+    if m.dtype == torch.bool:
+        m = m.view(torch.uint8)
+    if m.dtype == torch.uint8:
+        mtype = ATTN_MASK_KEEP_U8
+    elif m.dtype == dtype:
+        mtype = ATTN_MASK_ADD
+    else:
+        raise TypeError("attn_mask must be bool, uint8 or q's dtype, got %s" % m.dtype)
+    if not m.is_cuda:
+        raise ValueError("attn_mask must be a device tensor")
+    if m.dim() == 3:
+        m = m[:, None]
+    elif m.dim() == 2:
+        m = m[None, None]
+    if m.dim() != 4 or tuple(m.shape[-2:]) != (N, N):
+        raise ValueError("attn_mask must be broadcastable to [B, Hq, N, N]")
+    m = m.expand(B, Hq, N, N)
+    if m.stride(3) != 1:
+        raise ValueError("attn_mask: the key dimension must be contiguous")
+    return m, mtype
 
 
 def forward(q, k, v, causal: bool, valid_len=None, scale: Optional[float] = None, out=None,
@@ -306,26 +366,7 @@ def forward(q, k, v, causal: bool, valid_len=None, scale: Optional[float] = None
         stream = torch.cuda.current_stream(q.device)
     lse_ptr = lse.data_ptr() if lse is not None else None
     if attn_mask is not None:
-        m = attn_mask
-        if m.dtype == torch.bool:
-            m = m.view(torch.uint8)
-        if m.dtype == torch.uint8:
-            mtype = ATTN_MASK_KEEP_U8
-        elif m.dtype == q.dtype:
-            mtype = ATTN_MASK_ADD
-        else:
-            raise TypeError("attn_mask must be bool, uint8 or q's dtype, got %s" % m.dtype)
-        if not m.is_cuda:
-            raise ValueError("attn_mask must be a device tensor")
-        if m.dim() == 3:
-            m = m[:, None]
-        elif m.dim() == 2:
-            m = m[None, None]
-        if m.dim() != 4 or tuple(m.shape[-2:]) != (N, N):
-            raise ValueError("attn_mask must be broadcastable to [B, Hq, N, N]")
-        m = m.expand(B, Hq, N, N)
-        if m.stride(3) != 1:
-            raise ValueError("attn_mask: the key dimension must be contiguous")
+        m, mtype = _mask_view(attn_mask, q.dtype, B, Hq, N)
         st = attn_fwd_masked(qv.data_ptr(), qv.stride()[:3], kv.data_ptr(), kv.stride()[:3],
                              vv.data_ptr(), vv.stride()[:3], ov.data_ptr(), ov.stride()[:3],
                              lse_ptr, B, Hq, Hkv, N, D, float(scale), int(bool(causal)), vl_ptr,
@@ -352,16 +393,17 @@ def forward(q, k, v, causal: bool, valid_len=None, scale: Optional[float] = None
 
 def backward(q, k, v, out, dout, lse, causal: bool, valid_len=None,
              scale: Optional[float] = None, dq=None, dk=None, dv=None, ws=None, stream=None,
-             layout: str = "bhnd"):
+             layout: str = "bhnd", attn_mask=None):
     """Run the attention backward on torch device tensors; returns (dq, dk, dv).
 
     ``out`` and ``lse`` are the forward's outputs for the same inputs; ``dout`` is the gradient
     of the loss with respect to ``out``. ``layout`` names the dimension order of q, k, v, out,
     dout and the gradients ("bhnd" = [B, H, N, D], "bnhd" = [B, N, H, D]); any strides with a
     contiguous D dimension are accepted (contiguous [B, H, N, D] tensors take attn_bwd, others
-    attn_bwd_strided, with no copies). Gradients (each in its input's layout) and the float32
-    workspace ``ws`` ([2, B, Hq, N]: Delta, then the LSE in base 2) are allocated with torch when
-    not given.
+    attn_bwd_strided, with no copies). ``attn_mask`` is the forward's explicit mask (as in
+    forward(); the call then goes to attn_bwd_masked). Gradients (each in its input's layout)
+    and the float32 workspace ``ws`` ([2, B, Hq, N]: Delta, then the LSE in base 2) are
+    allocated with torch when not given.
     """
     import torch
     if layout not in ("bhnd", "bnhd"):
@@ -404,7 +446,17 @@ def backward(q, k, v, out, dout, lse, causal: bool, valid_len=None,
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     views = (qv, kv, vv, ov, gv, dqv, dkv, dvv)
-    if all(t.is_contiguous() for t in views):
+    if attn_mask is not None:
+        m, mtype = _mask_view(attn_mask, q.dtype, B, Hq, N)
+        st = attn_bwd_masked(
+            qv.data_ptr(), qv.stride()[:3], kv.data_ptr(), kv.stride()[:3], vv.data_ptr(),
+            vv.stride()[:3], ov.data_ptr(), ov.stride()[:3], gv.data_ptr(), gv.stride()[:3],
+            lse.data_ptr(), dqv.data_ptr(), dqv.stride()[:3], dkv.data_ptr(), dkv.stride()[:3],
+            dvv.data_ptr(), dvv.stride()[:3], ws.data_ptr(), B, Hq, Hkv, N, D, float(scale),
+            int(bool(causal)), vl_ptr, m.data_ptr(), mtype, m.stride()[:3], _dtype_code(q),
+            stream.cuda_stream)
+        name = "attn_bwd_masked"
+    elif all(t.is_contiguous() for t in views):
         st = attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
                       lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(),
                       B, Hq, Hkv, N, D, float(scale), int(bool(causal)), vl_ptr,
@@ -428,21 +480,22 @@ def _autograd_function():
 
     class _Attention(torch.autograd.Function):
         @staticmethod
-        def forward(ctx, q, k, v, causal, valid_len, scale, layout):
+        def forward(ctx, q, k, v, causal, valid_len, scale, layout, attn_mask):
             out, lse = forward(q, k, v, causal=causal, valid_len=valid_len, scale=scale,
-                               layout=layout)
-            ctx.save_for_backward(q, k, v, out, lse, valid_len)
+                               layout=layout, attn_mask=attn_mask)
+            ctx.save_for_backward(q, k, v, out, lse, valid_len, attn_mask)
             ctx.causal, ctx.scale, ctx.layout = causal, scale, layout
             return out
 
         @staticmethod
         def backward(ctx, dout):
-            q, k, v, out, lse, valid_len = ctx.saved_tensors
+            q, k, v, out, lse, valid_len, attn_mask = ctx.saved_tensors
             if dout.stride(-1) != 1 or 0 in dout.stride():
                 dout = dout.contiguous()   # e.g. a broadcast gradient
             dq, dk, dv = backward(q, k, v, out, dout, lse, causal=ctx.causal,
-                                  valid_len=valid_len, scale=ctx.scale, layout=ctx.layout)
-            return dq, dk, dv, None, None, None, None
+                                  valid_len=valid_len, scale=ctx.scale, layout=ctx.layout,
+                                  attn_mask=attn_mask)
+            return dq, dk, dv, None, None, None, None, None
 
     return _Attention
 
@@ -451,11 +504,11 @@ _ATTENTION = None
 
 
 def attention(q, k, v, causal: bool, valid_len=None, scale: Optional[float] = None,
-              layout: str = "bhnd"):
+              layout: str = "bhnd", attn_mask=None):
     """Differentiable attention on [B, H, N, D] (or, with layout="bnhd", [B, N, H, D]) tensors:
     forward through attn_fwd, gradients through attn_bwd (torch.autograd glue only; strided
     inputs are used in place)."""
     global _ATTENTION
     if _ATTENTION is None:
         _ATTENTION = _autograd_function()
-    return _ATTENTION.apply(q, k, v, causal, valid_len, scale, layout)
+    return _ATTENTION.apply(q, k, v, causal, valid_len, scale, layout, attn_mask)

@@ -81,7 +81,28 @@ struct BwdParams {
   int64_t dqs_b, dqs_h, dqs_n;
   int64_t dks_b, dks_h, dks_n;
   int64_t dvs_b, dvs_h, dvs_n;
+  // Explicit mask (kernels with MK != kMaskNone): element strides (batch, query head, query row)
+  const void* mask;
+  int64_t ms_b, ms_h, ms_n;
+  float mscale;    // log2(e) / c: an additive mask value in raw score units
 };
+
+// The 4 keys 8g + 4h .. +3 of one mask row as read from a slot: uint8 bytes (keep) or 16-bit
+// values of the input type (additive), element e of the group.
+template <int DT, int MK>
+__device__ inline bool mask_keep(const uint32_t (&w)[2], int e) {
+  return MK != kMaskKeep || ((w[0] >> (8 * e)) & 0xffu) != 0;
+}
+template <int DT, int MK>
+__device__ inline float mask_add(const uint32_t (&w)[2], int e) {
+  if constexpr (MK != kMaskAdd) {
+    return 0.f;
+  } else {
+    const uint32_t bits = (w[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+    return DT == ATTN_BF16 ? __uint_as_float(bits << 16)
+                           : (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+  }
+}
 
 // Row value of the log-sum-exp in log2 units; an empty row (L = -inf) has only hidden keys, and
 // 0 keeps exp2(-inf - 0) = 0 there instead of NaN.
@@ -156,17 +177,19 @@ __device__ inline u32x4 tr_frag(const unsigned char* tile, uint32_t off, int row
 // ------------------------------------------------------------------------------------------
 // DH is the tensors' head dimension; DH < 64 runs the D = 64 geometry with the missing 16-byte
 // chunks of every row zero (out-of-range DMA lanes, zero registers) and never stored.
-template <int DT, int DH, bool CAUSAL>
+template <int DT, int DH, bool CAUSAL, int MK>
 __device__ __forceinline__ void bwd_dq_body(const BwdParams& p) {
   constexpr int D = DH < 64 ? 64 : DH;
   constexpr int DCH = DH / 8;
   using G = Geo<D>;
+  using MG = MaskGeo<MK>;
+  constexpr int MOFF = G::LDS;   // per-wave mask slots follow the K/V tiles
   using M = Mfma<DT>;
   constexpr int KSTEPS = G::KSTEPS;
   constexpr int OT = G::OT;
   // K0 K1 V0 V1, 64-key tiles. K is stored with bswz (read both as rows and transposed), V
   // with kswz (read as rows).
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[G::LDS];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[G::LDS + kWaves * MG::WB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -238,6 +261,30 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p) {
     }
   };
 
+  // Explicit mask: this wave's rows qa .. qa+31 of the (batch, query head) mask matrix, the 64
+  // keys of a tile per row, in the wave's LDS slot one tile ahead (the forward's scheme: the
+  // step's wait covers the DMA, the slot is refilled right after it has been read).
+  const uint32_t mrow = MK != kMaskNone ? (uint32_t)(p.ms_n * MG::ES) : 0;
+  const __amdgpu_buffer_rsrc_t mrs = __builtin_amdgcn_make_buffer_rsrc(
+      MK != kMaskNone ? (void*)((const unsigned char*)p.mask + (b * p.ms_b + hq * p.ms_h) * MG::ES)
+                      : (void*)p.q,
+      (short)0, MK != kMaskNone ? (p.N - 1) * mrow + ((p.N * MG::ES + 15) & ~15) : 0,
+      kBufferFlags);
+  uint32_t moff = 0;
+  if constexpr (MK != kMaskNone) {
+    const int r = lane / MG::CPR;
+    moff = (uint32_t)(qa + r) * mrow + 16 * ((lane % MG::CPR) ^ MG::mswz(r));
+  }
+  auto mask_dma = [&](int tile) {
+    if constexpr (MK != kMaskNone) {
+#pragma unroll
+      for (int i = 0; i < MG::LOADS; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            mrs, (lds_void*)(smem + MOFF + wave * MG::WB + i * 1024), 16, moff,
+            (uint32_t)tile * MG::RB + (uint32_t)(i * MG::RPL) * mrow, 0, 0);
+    }
+  };
+
   // Fragment offsets: K rows (A of S^T), V rows (A of dP^T), K^T (A of dQ^T).
   uint32_t kaddr[KSTEPS], vaddr[KSTEPS], taddr[OT];
 #pragma unroll
@@ -248,7 +295,10 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p) {
 #pragma unroll
   for (int u = 0; u < OT; ++u) taddr[u] = tr_offset<D>(lane, u);
 
-  if (ntiles > 0) dma(0, G::K0, G::V0);
+  if (ntiles > 0) {
+    dma(0, G::K0, G::V0);
+    mask_dma(0);
+  }
 
   // Q, dO and O of this lane's row (B-operand layout: Q[row][16s + 8h .. +7]).
   const uint16_t* qsrc = p.q + b * p.qs_b + hq * p.qs_h + qr * p.qs_n + 8 * h;
@@ -301,6 +351,26 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p) {
     if (j + 1 < ntiles) dma(j + 1, P ? G::K0 : G::K1, P ? G::V0 : G::V1);
     const unsigned char* kb = smem + (P ? G::K1 : G::K0);
     const unsigned char* vb = smem + (P ? G::V1 : G::V0);
+    // this tile's mask slice (keys 8g + 4h .. +3 of the lane's query row), then the next
+    // tile's DMA into the same slot
+    uint32_t mw[8][2];
+    if constexpr (MK != kMaskNone) {
+      const unsigned char* mr = smem + MOFF + wave * MG::WB + ql * MG::RB;
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        if constexpr (MK == kMaskKeep) {
+          mw[g][0] = *(const uint32_t*)(mr + 16 * ((g >> 1) ^ MG::mswz(ql)) + 8 * (g & 1) +
+                                        4 * h);
+          mw[g][1] = 0;
+        } else {
+          const u32x2 w = *(const u32x2*)(mr + 16 * (g ^ MG::mswz(ql)) + 8 * h);
+          mw[g][0] = w[0];
+          mw[g][1] = w[1];
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (j + 1 < ntiles) mask_dma(j + 1);
+    }
     // S^T and dP^T for the tile's two 32-key halves
     f32x16 sc[2], dp[2];
 #pragma unroll
@@ -317,14 +387,19 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p) {
     // this wave's causal diagonal or the padding boundary (a hidden element's P may be inf:
     // the select removes it).
     const int kb0 = j * kBN;
-    const bool full = (!CAUSAL || kb0 + kBN - 1 <= qa) && kb0 + kBN <= kv_end;
+    const bool full = MK == kMaskNone && (!CAUSAL || kb0 + kBN - 1 <= qa) && kb0 + kBN <= kv_end;
     float ds[2][16];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][r], c, -L));
+        float x = sc[t][r];
+        if constexpr (MK == kMaskAdd)
+          x = __builtin_fmaf(mask_add<DT, MK>(mw[4 * t + (r >> 2)], r & 3), p.mscale, x);
+        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(x, c, -L));
         ds[t][r] = pr * (dp[t][r] - delta);
+        if constexpr (MK == kMaskKeep)
+          ds[t][r] = mask_keep<DT, MK>(mw[4 * t + (r >> 2)], r & 3) ? ds[t][r] : 0.f;
       }
     if (!full) {
       int lim = kv_end - 1 - kb0 - 4 * h;
@@ -375,16 +450,30 @@ struct BwdGeo {
   static_assert(BUF + QTILE + 24 * G::ROW <= 65535, "LDS offsets fit the immediate field");
 };
 
-template <int DT, int DH, bool CAUSAL>
+// Mask slot of a dK/dV wave: the 32 query rows x 32 keys of one iteration, row-major (keys of a
+// row contiguous), refilled one iteration ahead.
+template <int MK>
+struct KMaskGeo {
+  static constexpr int ES = MaskGeo<MK>::ES;
+  static constexpr int RB = 32 * ES;                          // bytes per row slice
+  static constexpr int CPR = RB / 16;                         // 16-byte chunks per row slice
+  static constexpr int WB = MK == kMaskNone ? 0 : kQT * RB;   // bytes per wave slot
+  static constexpr int LOADS = WB / 1024;
+  static constexpr int RPL = 1024 / RB;                       // rows per DMA block
+};
+
+template <int DT, int DH, bool CAUSAL, int MK>
 __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
   constexpr int D = DH < 64 ? 64 : DH;   // geometry (as in the dQ kernel)
   constexpr int DCH = DH / 8;
   using G = Geo<D>;
   using BG = BwdGeo<D>;
+  using KM = KMaskGeo<MK>;
+  constexpr int MOFF = BG::LDS;   // per-wave mask slots follow the tiles and V rows
   using M = Mfma<DT>;
   constexpr int KSTEPS = G::KSTEPS;
   constexpr int OT = G::OT;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[BG::LDS];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[BG::LDS + kWaves * KM::WB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -516,6 +605,27 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
     for (int u = 0; u < OT; ++u) taddr[u] = tr_offset<D>(lane, u);
     const float c = p.c;
 
+    // Explicit mask: rows q0 .. q0+31 (query head g) x this wave's keys kw .. kw+31 into the
+    // wave's slot; lane L of block i writes row i * RPL + L / CPR, chunk L % CPR.
+    const uint32_t mrow = MK != kMaskNone ? (uint32_t)(p.ms_n * KM::ES) : 0;
+    const uint32_t mlane = MK != kMaskNone
+                               ? (uint32_t)(lane / KM::CPR) * mrow + (uint32_t)kw * KM::ES +
+                                     16 * (lane % KM::CPR)
+                               : 0;
+    auto mask_dma = [&](int g, int q0) {
+      if constexpr (MK != kMaskNone) {
+        const int hq = kvh * p.group + g;
+        const __amdgpu_buffer_rsrc_t mrs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)((const unsigned char*)p.mask + (b * p.ms_b + hq * p.ms_h) * KM::ES),
+            (short)0, (p.N - 1) * mrow + ((p.N * KM::ES + 15) & ~15), kBufferFlags);
+#pragma unroll
+        for (int i = 0; i < KM::LOADS; ++i)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              mrs, (lds_void*)(smem + MOFF + wave * KM::WB + i * 1024), 16, mlane,
+              (uint32_t)(q0 + i * KM::RPL) * mrow, 0, 0);
+      }
+    };
+
     // Iteration order: query head by query head, each from qstart up. (Sweeping the tiles in
     // lockstep across the key-tile workgroups, every head at each tile, cut the HBM traffic by
     // 3x but ran ~10 % slower under causal masking.)
@@ -526,18 +636,39 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
       if (q0 >= p.N) { q0 = qstart; ++g; }
     };
     dma(g_nxt, q_nxt, 0);
+    mask_dma(g_nxt, q_nxt);
     advance(g_nxt, q_nxt);
 
     auto step = [&](auto bufc, int it) {
       constexpr int buf = decltype(bufc)::value;
       wait_loads_and_lds();
       __syncthreads();
+      const int gn = g_nxt, qn = q_nxt;   // the next iteration's tile
       if (it + 1 < iters) {
-        dma(g_nxt, q_nxt, buf ^ 1);
+        dma(gn, qn, buf ^ 1);
         advance(g_nxt, q_nxt);
       }
       const int q0 = q_cur;
       advance(g_cur, q_cur);
+      // this iteration's mask values (query rows 8 (r/4) + 4h + r%4 of the tile, the lane's
+      // key), then the next iteration's DMA into the same slot. Keep masks are packed into
+      // one bit per element, additive values two per register.
+      uint32_t kbits = 0, mv[8];
+      if constexpr (MK != kMaskNone) {
+        const unsigned char* ms = smem + MOFF + wave * KM::WB + KM::ES * ql;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qi = 8 * (r >> 2) + 4 * h + (r & 3);
+          if constexpr (MK == kMaskKeep) {
+            kbits |= (ms[qi * KM::RB] != 0 ? 1u : 0u) << r;
+          } else {
+            const uint32_t x = *(const uint16_t*)(ms + qi * KM::RB);
+            mv[r >> 1] = (r & 1) ? (mv[r >> 1] | (x << 16)) : x;
+          }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (it + 1 < iters) mask_dma(gn, qn);
+      }
       const unsigned char* qb = smem + buf * BG::BUF;
       const unsigned char* ob = qb + BG::QTILE;
       const float* lb = (const float*)(qb + 2 * BG::QTILE);
@@ -553,7 +684,8 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
       // touches the causal diagonal, the padding boundary or the end of the sequence; only then
       // is each element tested. A hidden element may have L = -inf (a row with no visible key)
       // and so x = inf: the select, not a product, removes it.
-      const bool full = (!CAUSAL || q0 >= kw + 31) && kw + 32 <= kv_end && q0 + kQT <= p.N;
+      const bool full = MK == kMaskNone && (!CAUSAL || q0 >= kw + 31) && kw + 32 <= kv_end &&
+                        q0 + kQT <= p.N;
       float pr[16], ds[16];
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
@@ -563,13 +695,21 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * r4 + e;
-          pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lv[e]));
+          float x = s[r];
+          if constexpr (MK == kMaskAdd) {
+            const uint32_t bits = (mv[r >> 1] >> (16 * (r & 1))) & 0xffffu;
+            const float a = DT == ATTN_BF16 ? __uint_as_float(bits << 16)
+                                            : (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+            x = __builtin_fmaf(a, p.mscale, x);
+          }
+          pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(x, c, -lv[e]));
         }
         if (!full) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int qi = q0 + qi0 + e;
-            const bool vis = (!CAUSAL || key <= qi) && key < kv_end && qi < p.N;
+            bool vis = (!CAUSAL || key <= qi) && key < kv_end && qi < p.N;
+            if constexpr (MK == kMaskKeep) vis = vis && ((kbits >> (4 * r4 + e)) & 1u);
             pr[4 * r4 + e] = vis ? pr[4 * r4 + e] : 0.f;
           }
         }
@@ -605,41 +745,54 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
                         lane);
 }
 
-template <int DT, int D, bool CAUSAL>
+template <int DT, int D, bool CAUSAL, int MK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dq_kernel(BwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  bwd_dq_body<DT, D, CAUSAL>(p);
+  bwd_dq_body<DT, D, CAUSAL, MK>(p);
 #endif
 }
 
-template <int DT, int D, bool CAUSAL>
+template <int DT, int D, bool CAUSAL, int MK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dkdv_kernel(BwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  bwd_dkdv_body<DT, D, CAUSAL>(p);
+  bwd_dkdv_body<DT, D, CAUSAL, MK>(p);
 #endif
 }
 
-template <int DT, int D, bool CAUSAL>
+template <int DT, int D, bool CAUSAL, int MK>
 hipError_t launch_bwd(const BwdParams& p, hipStream_t s) {
   const int64_t nq = (int64_t)p.B * p.Hq * p.nqt;
   const int64_t nk = (int64_t)p.B * p.Hkv * p.nkt;
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<DT, D, CAUSAL>), dim3((unsigned)nq), dim3(kThreads), 0,
-                     s, p);
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<DT, D, CAUSAL, MK>), dim3((unsigned)nq),
+                     dim3(kThreads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DT, D, CAUSAL>), dim3((unsigned)nk), dim3(kThreads),
-                     0, s, p);
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DT, D, CAUSAL, MK>), dim3((unsigned)nk),
+                     dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
+template <int DT, int MK>
+hipError_t dispatch_bwd_d(const BwdParams& p, int D, bool causal, hipStream_t s) {
+  switch (D) {
+    case 16:
+      return causal ? launch_bwd<DT, 16, true, MK>(p, s) : launch_bwd<DT, 16, false, MK>(p, s);
+    case 32:
+      return causal ? launch_bwd<DT, 32, true, MK>(p, s) : launch_bwd<DT, 32, false, MK>(p, s);
+    case 64:
+      return causal ? launch_bwd<DT, 64, true, MK>(p, s) : launch_bwd<DT, 64, false, MK>(p, s);
+    default:
+      return causal ? launch_bwd<DT, 128, true, MK>(p, s) : launch_bwd<DT, 128, false, MK>(p, s);
+  }
+}
+
 template <int DT>
-hipError_t dispatch_bwd(const BwdParams& p, int D, bool causal, hipStream_t s) {
-  if (D == 16) return causal ? launch_bwd<DT, 16, true>(p, s) : launch_bwd<DT, 16, false>(p, s);
-  if (D == 32) return causal ? launch_bwd<DT, 32, true>(p, s) : launch_bwd<DT, 32, false>(p, s);
-  if (D == 64) return causal ? launch_bwd<DT, 64, true>(p, s) : launch_bwd<DT, 64, false>(p, s);
-  return causal ? launch_bwd<DT, 128, true>(p, s) : launch_bwd<DT, 128, false>(p, s);
+hipError_t dispatch_bwd(const BwdParams& p, int D, bool causal, int mask_type, hipStream_t s) {
+  if (mask_type == ATTN_MASK_KEEP_U8) return dispatch_bwd_d<DT, kMaskKeep>(p, D, causal, s);
+  if (mask_type == ATTN_MASK_ADD) return dispatch_bwd_d<DT, kMaskAdd>(p, D, causal, s);
+  return dispatch_bwd_d<DT, kMaskNone>(p, D, causal, s);
 }
 
 // The eight [B, H, N, D] tensors of a backward call.
@@ -659,7 +812,8 @@ BwdLayouts bwd_layouts(const void* q, const int64_t* qs, const void* k, const in
 }
 
 int bwd_validate(const BwdLayouts& t, const float* lse, const float* ws, int B, int Hq, int Hkv,
-                 int N, int D, float scale, const int32_t* valid_len, int dtype) {
+                 int N, int D, float scale, const int32_t* valid_len, int dtype,
+                 const MaskArg& mk = no_mask()) {
   const Layout* all[] = {&t.q, &t.k, &t.v, &t.o, &t.dout, &t.dq, &t.dk, &t.dv};
   for (const Layout* l : all)
     if (!l->ptr) return ATTN_ERR_NULL;
@@ -696,12 +850,20 @@ int bwd_validate(const BwdLayouts& t, const float* lse, const float* ws, int B, 
       if (overlaps(outs[i], osz[i], outs[j], osz[j])) return ATTN_ERR_ALIAS;
     if (valid_len && overlaps(outs[i], osz[i], valid_len, (int64_t)B * 4)) return ATTN_ERR_ALIAS;
   }
+  if (mk.type != ATTN_MASK_NONE) {
+    const int ms = mask_status(mk, N);
+    if (ms != ATTN_OK) return ms;
+    const int64_t mbytes = mask_span(mk, B, Hq, N);
+    for (int i = 0; i < 4; ++i)
+      if (overlaps(outs[i], osz[i], mk.ptr, mbytes)) return ATTN_ERR_ALIAS;
+  }
   return ATTN_OK;
 }
 
 int bwd_run(const BwdLayouts& t, const float* lse, float* ws, int B, int Hq, int Hkv, int N,
-            int D, float scale, int causal, const int32_t* valid_len, int dtype, void* stream) {
-  const int st = bwd_validate(t, lse, ws, B, Hq, Hkv, N, D, scale, valid_len, dtype);
+            int D, float scale, int causal, const int32_t* valid_len, int dtype, void* stream,
+            const MaskArg& mk = no_mask()) {
+  const int st = bwd_validate(t, lse, ws, B, Hq, Hkv, N, D, scale, valid_len, dtype, mk);
   if (st != ATTN_OK) return st;
   BwdParams p;
   p.q = (const uint16_t*)t.q.ptr;
@@ -737,9 +899,13 @@ int bwd_run(const BwdLayouts& t, const float* lse, float* ws, int B, int Hq, int
   p.dqs_b = t.dq.sb; p.dqs_h = t.dq.sh; p.dqs_n = t.dq.sn;
   p.dks_b = t.dk.sb; p.dks_h = t.dk.sh; p.dks_n = t.dk.sn;
   p.dvs_b = t.dv.sb; p.dvs_h = t.dv.sh; p.dvs_n = t.dv.sn;
+  p.mask = mk.ptr;
+  p.ms_b = mk.sb; p.ms_h = mk.sh; p.ms_n = mk.sn;
+  p.mscale = kLog2e / p.c;
   const hipStream_t s = (hipStream_t)stream;
-  const hipError_t e = dtype == ATTN_BF16 ? dispatch_bwd<ATTN_BF16>(p, D, causal != 0, s)
-                                          : dispatch_bwd<ATTN_F16>(p, D, causal != 0, s);
+  const hipError_t e =
+      dtype == ATTN_BF16 ? dispatch_bwd<ATTN_BF16>(p, D, causal != 0, mk.type, s)
+                         : dispatch_bwd<ATTN_F16>(p, D, causal != 0, mk.type, s);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
@@ -790,4 +956,35 @@ extern "C" int attn_bwd_strided(
                              dout_strides, dq, dq_strides, dk, dk_strides, dv, dv_strides, Hq,
                              Hkv, N, D),
                  lse, ws, B, Hq, Hkv, N, D, scale, causal, valid_len, dtype, stream);
+}
+
+extern "C" int attn_bwd_masked_validate(
+    const void* q, const int64_t* q_strides, const void* k, const int64_t* k_strides,
+    const void* v, const int64_t* v_strides, const void* out, const int64_t* out_strides,
+    const void* dout, const int64_t* dout_strides, const float* lse, const void* dq,
+    const int64_t* dq_strides, const void* dk, const int64_t* dk_strides, const void* dv,
+    const int64_t* dv_strides, const float* ws, int B, int Hq, int Hkv, int N, int D,
+    float scale, int causal, const int32_t* valid_len, const void* mask, int mask_type,
+    const int64_t* mask_strides, int dtype) {
+  (void)causal;
+  return bwd_validate(bwd_layouts(q, q_strides, k, k_strides, v, v_strides, out, out_strides,
+                                  dout, dout_strides, dq, dq_strides, dk, dk_strides, dv,
+                                  dv_strides, Hq, Hkv, N, D),
+                      lse, ws, B, Hq, Hkv, N, D, scale, valid_len, dtype,
+                      mask_arg(mask, mask_type, mask_strides, N));
+}
+
+extern "C" int attn_bwd_masked(
+    const void* q, const int64_t* q_strides, const void* k, const int64_t* k_strides,
+    const void* v, const int64_t* v_strides, const void* out, const int64_t* out_strides,
+    const void* dout, const int64_t* dout_strides, const float* lse, void* dq,
+    const int64_t* dq_strides, void* dk, const int64_t* dk_strides, void* dv,
+    const int64_t* dv_strides, float* ws, int B, int Hq, int Hkv, int N, int D, float scale,
+    int causal, const int32_t* valid_len, const void* mask, int mask_type,
+    const int64_t* mask_strides, int dtype, void* stream) {
+  return bwd_run(bwd_layouts(q, q_strides, k, k_strides, v, v_strides, out, out_strides, dout,
+                             dout_strides, dq, dq_strides, dk, dk_strides, dv, dv_strides, Hq,
+                             Hkv, N, D),
+                 lse, ws, B, Hq, Hkv, N, D, scale, causal, valid_len, dtype, stream,
+                 mask_arg(mask, mask_type, mask_strides, N));
 }

@@ -66,6 +66,28 @@ struct Geo {
   }
 };
 
+// Explicit [B, H, N, N] masks (template parameter MK of the kernel).
+constexpr int kMaskNone = 0;   // causal and valid_len only
+constexpr int kMaskKeep = 1;   // uint8: nonzero = the key is visible to the query
+constexpr int kMaskAdd = 2;    // 16-bit (the input type): added to the scaled score
+
+// Each wave keeps the kBN-key slice of its 32 mask rows for the current tile in its own LDS
+// slot, fetched by DMA one tile ahead. Row r stores logical 16-byte chunk c at chunk
+// c ^ mswz(r); the swizzle depends on r % RPL only, so every DMA block uses the same lane
+// offsets.
+template <int MK>
+struct MaskGeo {
+  static constexpr int ES = MK == kMaskKeep ? 1 : 2;            // bytes per element
+  static constexpr int RB = kBN * ES;                           // bytes per row slice
+  static constexpr int CPR = RB / 16;                           // 16-byte chunks per row slice
+  static constexpr int WB = MK == kMaskNone ? 0 : 32 * RB;      // bytes per wave slot
+  static constexpr int LOADS = WB / 1024;                       // 1 KiB DMA blocks per slot
+  static constexpr int RPL = 1024 / RB;                         // rows per DMA block
+  __device__ static constexpr int mswz(int r) {
+    return MK == kMaskKeep ? ((r >> 2) & 3) : (r & 7);
+  }
+};
+
 template <int DT>
 struct Mfma;
 
@@ -179,6 +201,42 @@ inline bool output_disjoint(const Layout& o, int B, int H, int N, int D) {
     extent = (d[i].size - 1) * d[i].stride + extent;
   }
   return true;
+}
+
+// An explicit mask: element strides (batch, query head, query row); keys contiguous.
+struct MaskArg {
+  const void* ptr;
+  int type;
+  int64_t sb, sh, sn;
+};
+
+inline MaskArg no_mask() { return MaskArg{nullptr, ATTN_MASK_NONE, 0, 0, 0}; }
+
+// NULL strides mean one [B, N, N] mask shared by the heads.
+inline MaskArg mask_arg(const void* mask, int mask_type, const int64_t* st, int N) {
+  if (st) return MaskArg{mask, mask_type, st[0], st[1], st[2]};
+  return MaskArg{mask, mask_type, (int64_t)N * N, 0, N};
+}
+
+// Type, pointer, layout and size checks of a mask (not its aliasing).
+inline int mask_status(const MaskArg& mk, int N) {
+  if (mk.type != ATTN_MASK_KEEP_U8 && mk.type != ATTN_MASK_ADD) return ATTN_ERR_MASK;
+  if (!mk.ptr) return ATTN_ERR_NULL;
+  const int64_t es = mk.type == ATTN_MASK_KEEP_U8 ? 1 : 2;
+  if ((uintptr_t)mk.ptr % 16 != 0 || mk.sb < 0 || mk.sh < 0 || mk.sn < N ||
+      (mk.sb * es) % 16 || (mk.sh * es) % 16 || (mk.sn * es) % 16)
+    return ATTN_ERR_LAYOUT;
+  // A wave's DMA addresses rows up to 127 past its first inside one 32-bit buffer.
+  if (((int64_t)N + kBM) * mk.sn * es > INT32_MAX) return ATTN_ERR_SHAPE;
+  return ATTN_OK;
+}
+
+// Bytes a mask's reads may touch: rows are read in 16-byte units, the last row up to its next
+// 16-byte boundary.
+inline int64_t mask_span(const MaskArg& mk, int B, int Hq, int N) {
+  const int64_t es = mk.type == ATTN_MASK_KEEP_U8 ? 1 : 2;
+  return ((B - 1) * mk.sb + (Hq - 1) * mk.sh + (int64_t)(N - 1) * mk.sn) * es +
+         ((N * es + 15) & ~15);
 }
 
 // fp32 forward (attn_fwd_f32.hip): validated arguments, strides in elements.

@@ -53,28 +53,6 @@ using namespace attn_detail;
 
 constexpr float RESCALE_THRESHOLD = 8.0f;
 
-// Explicit [B, H, N, N] masks (template parameter MK of the kernel).
-constexpr int kMaskNone = 0;   // causal and valid_len only
-constexpr int kMaskKeep = 1;   // uint8: nonzero = the key is visible to the query
-constexpr int kMaskAdd = 2;    // 16-bit (the input type): added to the scaled score
-
-// Each wave keeps the kBN-key slice of its 32 mask rows for the current tile in its own LDS
-// slot, fetched by DMA one tile ahead. Row r stores logical 16-byte chunk c at chunk
-// c ^ mswz(r); the swizzle depends on r % RPL only, so every DMA block uses the same lane
-// offsets.
-template <int MK>
-struct MaskGeo {
-  static constexpr int ES = MK == kMaskKeep ? 1 : 2;            // bytes per element
-  static constexpr int RB = kBN * ES;                           // bytes per row slice
-  static constexpr int CPR = RB / 16;                           // 16-byte chunks per row slice
-  static constexpr int WB = MK == kMaskNone ? 0 : 32 * RB;      // bytes per wave slot
-  static constexpr int LOADS = WB / 1024;                       // 1 KiB DMA blocks per slot
-  static constexpr int RPL = 1024 / RB;                         // rows per DMA block
-  __device__ static constexpr int mswz(int r) {
-    return MK == kMaskKeep ? ((r >> 2) & 3) : (r & 7);
-  }
-};
-
 struct Params {
   const uint16_t* q;
   const uint16_t* k;
@@ -655,15 +633,6 @@ hipError_t dispatch_m(const Params& p, int D, bool causal, int mask_type, int64_
   return dispatch_d<DT, kMaskNone>(p, D, causal, nwg, s);
 }
 
-// An explicit mask: element size es, strides (batch, query head, query row) in elements.
-struct MaskArg {
-  const void* ptr;
-  int type;
-  int64_t sb, sh, sn;
-};
-
-MaskArg no_mask() { return MaskArg{nullptr, ATTN_MASK_NONE, 0, 0, 0}; }
-
 int validate(const Layout& q, const Layout& k, const Layout& v, const Layout& o,
              const float* lse, int B, int Hq, int Hkv, int N, int D, float scale,
              const int32_t* valid_len, int dtype, const MaskArg& mk = no_mask()) {
@@ -697,17 +666,9 @@ int validate(const Layout& q, const Layout& k, const Layout& v, const Layout& o,
                     (lse && overlaps(valid_len, (int64_t)B * 4, lse, lbytes))))
     return ATTN_ERR_ALIAS;
   if (mk.type != ATTN_MASK_NONE) {
-    if (mk.type != ATTN_MASK_KEEP_U8 && mk.type != ATTN_MASK_ADD) return ATTN_ERR_MASK;
-    if (!mk.ptr) return ATTN_ERR_NULL;
-    const int64_t mes = mk.type == ATTN_MASK_KEEP_U8 ? 1 : 2;
-    if ((uintptr_t)mk.ptr % 16 != 0 || mk.sb < 0 || mk.sh < 0 || mk.sn < N ||
-        (mk.sb * mes) % 16 || (mk.sh * mes) % 16 || (mk.sn * mes) % 16)
-      return ATTN_ERR_LAYOUT;
-    // A wave's DMA addresses rows up to 127 past its first inside one 32-bit buffer.
-    if (((int64_t)N + kBM) * mk.sn * mes > INT32_MAX) return ATTN_ERR_SHAPE;
-    // Rows are read in 16-byte units: the last row up to its next 16-byte boundary.
-    const int64_t mbytes =
-        ((B - 1) * mk.sb + (Hq - 1) * mk.sh + (int64_t)(N - 1) * mk.sn) * mes + ((N * mes + 15) & ~15);
+    const int ms = mask_status(mk, N);
+    if (ms != ATTN_OK) return ms;
+    const int64_t mbytes = mask_span(mk, B, Hq, N);
     if (overlaps(o.ptr, obytes, mk.ptr, mbytes) || (lse && overlaps(lse, lbytes, mk.ptr, mbytes)))
       return ATTN_ERR_ALIAS;
   }
@@ -818,10 +779,6 @@ extern "C" int attn_fwd_strided(const void* q, const int64_t* q_strides, const v
 
 namespace {
 
-MaskArg mask_arg(const void* mask, int mask_type, const int64_t* st, int N) {
-  if (st) return MaskArg{mask, mask_type, st[0], st[1], st[2]};
-  return MaskArg{mask, mask_type, (int64_t)N * N, 0, N};
-}
 
 }  // namespace
 
@@ -870,4 +827,4 @@ extern "C" const char* attn_status_string(int status) {
   }
 }
 
-extern "C" int attn_version(void) { return 5; }
+extern "C" int attn_version(void) { return 6; }

@@ -119,3 +119,57 @@ def compare(case: inputs.Case, O, L, O_ref, L_ref, rows=None, tag=""):
     log("%s: max|dO| %.3g  max|dLSE| %.3g  rows %d (empty %d)" % (
         tag, err, lerr, O.shape[0], int(empty.sum())))
     return err, lerr
+
+
+def mask_values(kind, pattern, dtype, B, Hq, N, rng):
+    """Mask values as [B or 1, Hq or 1, N, N] (uint8 keep, or 16-bit bits for additive)."""
+    i = np.arange(N)[:, None]
+    j = np.arange(N)[None, :]
+    if kind == "keep":
+        if pattern == "random_bh":
+            return (rng.random((B, Hq, N, N)) < 0.7).astype(np.uint8)
+        if pattern == "random_b":
+            return (rng.random((B, 1, N, N)) < 0.6).astype(np.uint8)
+        if pattern == "window":
+            return (np.abs(i - j) < 40).astype(np.uint8)[None, None]
+        if pattern == "empty_rows":
+            m = (rng.random((B, Hq, N, N)) < 0.5).astype(np.uint8)
+            m[:, :, ::7] = 0          # every 7th query sees nothing
+            return m
+    x = None
+    if pattern == "random_bh":
+        x = rng.normal(0.0, 2.0, (B, Hq, N, N)).astype(np.float32)
+        x[rng.random(x.shape) < 0.25] = -np.inf
+    elif pattern == "random_b":
+        x = rng.normal(0.0, 1.0, (B, 1, N, N)).astype(np.float32)
+        x[rng.random(x.shape) < 0.3] = -np.inf
+    elif pattern == "alibi":
+        slopes = 2.0 ** (-8.0 * (np.arange(Hq) + 1) / Hq)
+        x = (-slopes[:, None, None] * np.abs(i - j)[None]).astype(np.float32)[None]
+    elif pattern == "window_neginf":
+        x = np.where(np.abs(i - j) < 50, 0.0, -np.inf).astype(np.float32)[None, None]
+    elif pattern == "large_negative":
+        x = np.where(rng.random((1, Hq, N, N)) < 0.5, -1.0e4, 0.0).astype(np.float32)
+    return inputs.round_bits(x, dtype)
+
+
+def device_mask(kind, pattern, dtype, mv, N):
+    """The device view of mask values from mask_values: rows padded to 16 bytes (a
+    [.., N, Npad] view, as the layout rules require); [B, N, N] when shared by the heads and
+    [N, N] (bool) for the shared window."""
+    import torch
+    es = 1 if kind == "keep" else 2
+    npad = -(-N * es // 16) * 16 // es
+    host = np.zeros(mv.shape[:3] + (npad,), mv.dtype)
+    host[..., :N] = mv
+    t = torch.from_numpy(host.view(np.int16) if kind == "add" else host).cuda()
+    if kind == "add":
+        t = t.view(torch.bfloat16 if dtype == "bf16" else torch.float16)
+    else:
+        t = t.view(torch.bool) if pattern == "window" else t
+    dmask = t[..., :N]
+    if dmask.shape[1] == 1 and pattern != "window":
+        dmask = dmask[:, 0]                       # [B, N, N]: shared by the heads
+    elif pattern == "window":
+        dmask = dmask[0, 0]                       # [N, N]: shared by everything
+    return dmask

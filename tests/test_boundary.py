@@ -27,7 +27,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["attn_bwd", "attn_bwd_strided", "attn_bwd_strided_validate",
+    assert declared_functions() == ["attn_bwd", "attn_bwd_masked", "attn_bwd_masked_validate",
+                                    "attn_bwd_strided", "attn_bwd_strided_validate",
                                     "attn_bwd_validate", "attn_fwd",
                                     "attn_fwd_masked", "attn_fwd_masked_validate",
                                     "attn_fwd_strided", "attn_fwd_strided_validate",
@@ -44,7 +45,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_version(lib):
-    assert sdp.attn_version() == 5
+    assert sdp.attn_version() == 6
 
 
 def test_status_strings(lib):
@@ -350,3 +351,28 @@ def test_no_fallback_path():
             if name.endswith((".py", ".hip", ".h")):
                 text = open(os.path.join(root, name)).read()
                 assert not pattern.search(text), "%s uses the oracle" % name
+
+
+# ---- attn_bwd_masked_validate
+def bmcall(**kw):
+    a = dict(mask=MK, mtype=sdp.ATTN_MASK_KEEP_U8, ms=None, N=MN, dq=DQ, ws=DL)
+    a.update(kw)
+    N = a["N"]
+    return sdp.attn_bwd_masked_validate(Q, None, K, None, V, None, O, None, DO, None, L, a["dq"],
+                                        None, DK, None, DV, None, a["ws"], SB, SH, 2, N, 128,
+                                        0.088, 1, VL, a["mask"], a["mtype"], a["ms"],
+                                        sdp.ATTN_BF16)
+
+
+def test_bwd_masked_validate(lib):
+    assert bmcall() == sdp.ATTN_OK
+    assert bmcall(mtype=sdp.ATTN_MASK_ADD) == sdp.ATTN_OK
+    assert bmcall(mtype=sdp.ATTN_MASK_NONE, mask=None) == sdp.ATTN_OK
+    assert bmcall(ms=(0, MN * MN, MN)) == sdp.ATTN_OK                 # [Hq, N, N] per head
+    assert bmcall(mtype=5) == sdp.ATTN_ERR_MASK
+    assert bmcall(mask=None) == sdp.ATTN_ERR_NULL
+    assert bmcall(mask=MK + 8) == sdp.ATTN_ERR_LAYOUT                 # misaligned
+    assert bmcall(ms=(MN * MN, 0, MN - 16)) == sdp.ATTN_ERR_LAYOUT      # rows closer than N
+    assert bmcall(ms=(0, 0, 1 << 21)) == sdp.ATTN_ERR_SHAPE             # rows past 32-bit reach
+    assert bmcall(dq=MK + 1024) == sdp.ATTN_ERR_ALIAS                   # dq overlaps the mask
+    assert bmcall(ws=MK - 1024) == sdp.ATTN_ERR_ALIAS                   # workspace overlaps it

@@ -303,3 +303,72 @@ def test_autograd_bnhd_matches_contiguous():
     assert torch.equal(oa, ob.transpose(1, 2))
     for x, y in zip(a, b):
         assert torch.equal(x.grad, y.grad.transpose(1, 2))
+
+
+# ---- explicit masks (attn_bwd_masked): the forward's masks, the oracle's masked gradients
+BWD_MASKED = [
+    # (kind, pattern, dtype, D, causal, padded, B, Hq, Hkv, N)
+    ("keep", "random_bh", "bf16", 128, True, True, 2, 4, 2, 300),
+    ("keep", "window", "f16", 64, False, False, 2, 4, 4, 256),
+    ("keep", "random_b", "f16", 128, False, True, 3, 2, 1, 333),
+    ("keep", "empty_rows", "bf16", 64, True, False, 1, 4, 2, 130),
+    ("add", "random_bh", "bf16", 128, True, False, 2, 4, 2, 257),
+    ("add", "alibi", "bf16", 64, True, True, 2, 8, 2, 512),
+    ("add", "random_b", "f16", 64, False, True, 2, 4, 1, 200),
+    ("add", "window_neginf", "bf16", 128, False, False, 2, 4, 4, 300),
+    ("keep", "random_bh", "f16", 32, True, False, 2, 4, 2, 200),
+    ("add", "alibi", "bf16", 16, False, True, 2, 4, 1, 150),
+]
+
+
+@pytest.mark.parametrize("cfg", BWD_MASKED,
+                         ids=lambda c: "%s-%s-%s-D%d-c%d-p%d-B%d-H%d-%d-N%d" % c)
+def test_bwd_explicit_masks(cfg):
+    import torch
+    from gpu_util import device_mask, mask_values
+    kind, pattern, dtype, D, causal, padded, B, Hq, Hkv, N = cfg
+    case = inputs.make_case(B, Hq, Hkv, N, D, dtype, causal, padded, seed=[217, D, N, B])
+    dout_bits = inputs.make_grad(case, [217, D, N, B])
+    rng = np.random.default_rng([219, D, N, B])
+    mv = mask_values(kind, pattern, dtype, B, Hq, N, rng)
+    log("bwd masked case %s valid_len %s mask %s" % (cfg, case.valid_len, mv.shape))
+    dmask = device_mask(kind, pattern, dtype, mv, N)
+    vl = None
+    if case.valid_len is not None:
+        vl = torch.from_numpy(case.valid_len.astype(np.int32)).cuda()
+    q, k, v = (to_device(x, dtype) for x in (case.q_bits, case.k_bits, case.v_bits))
+    do = to_device(dout_bits, dtype)
+    out, lse = sdp.forward(q, k, v, causal=causal, valid_len=vl, scale=case.scale,
+                           attn_mask=dmask)
+    dq, dk, dv = sdp.backward(q, k, v, out, do, lse, causal=causal, valid_len=vl,
+                              scale=case.scale, attn_mask=dmask)
+    torch.cuda.synchronize()
+    got = [from_device(t, dtype) for t in (dq, dk, dv)]
+    qw, kw, vw = case.widened()
+    mk = {"keep_mask": mv} if kind == "keep" else {"add_mask": inputs.widen(mv, dtype)}
+    rq, rk, rv = oracle.attn_bwd(qw, kw, vw, inputs.widen(dout_bits, dtype), case.scale, causal,
+                                 case.valid_len, **mk)
+    e = [check_grad(n, g, r, dtype, str(cfg)) for n, g, r in zip(("dQ", "dK", "dV"), got,
+                                                                   (rq, rk, rv))]
+    log("%s: rel err dQ %.2e dK %.2e dV %.2e" % (cfg, *e))
+
+
+def test_autograd_with_mask_matches_entry_point():
+    """attention(attn_mask=...) returns exactly the masked entry points' output and gradients."""
+    import torch
+    from gpu_util import device_mask, mask_values
+    case = inputs.make_case(2, 4, 2, 200, 64, "bf16", True, False, seed=221)
+    rng = np.random.default_rng(223)
+    mv = mask_values("add", "alibi", "bf16", 2, 4, 200, rng)
+    dmask = device_mask("add", "alibi", "bf16", mv, 200)
+    dout = to_device(inputs.make_grad(case, 221), "bf16")
+    base = [to_device(x, "bf16") for x in (case.q_bits, case.k_bits, case.v_bits)]
+    a = [t.clone().requires_grad_() for t in base]
+    o = sdp.attention(*a, causal=True, scale=case.scale, attn_mask=dmask)
+    o.backward(dout)
+    o2, lse = sdp.forward(*base, causal=True, scale=case.scale, attn_mask=dmask)
+    g = sdp.backward(*base, o2, dout, lse, causal=True, scale=case.scale, attn_mask=dmask)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2)
+    for x, y in zip(a, g):
+        assert torch.equal(x.grad, y)
