@@ -298,8 +298,12 @@ def main():
             cpu = cpu_baseline(w, case, args.cpu_seconds)
         cpu["value"] = float("%.6g" % cpu["value"])
         log("cpu baseline: %s" % json.dumps(cpu))
+    metric = METRIC_BWD if args.backward else METRIC
+    # another workload, or a --dtype / --head-dim variant, names its own type and shape
+    metric = metric.replace("bf16 causal N=4096 D=128", "%s %sN=%d D=%d" % (
+        w.dtype, "causal " if w.causal else "", w.N, w.D))
     line = {
-        "metric": METRIC_BWD if args.backward else METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "metric": metric, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded iid N(0,1), rounded to %s)" % w.dtype,

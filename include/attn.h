@@ -49,7 +49,7 @@ extern "C" {
 typedef enum {
     ATTN_F16 = 0,  /* IEEE binary16 */
     ATTN_BF16 = 1, /* bfloat16 */
-    ATTN_F32 = 2   /* IEEE binary32: attn_fwd and attn_fwd_strided only */
+    ATTN_F32 = 2   /* IEEE binary32: every entry point except the masked ones */
 } attn_dtype_t;
 
 /* Return codes. Argument errors are detected on the host before anything is launched. */
@@ -231,6 +231,9 @@ int attn_fwd_masked_validate(const void *q, const int64_t *q_strides, const void
  *   ws           device float32 workspace of 2 * B * Hq * N values owned by the caller (the
  *                library allocates nothing); on return ws[0 .. B*Hq*N) holds Delta [B,Hq,N] and
  *                the rest the LSE in base 2 (LSE * log2 e, 0 for rows with no visible key).
+ *   dtype        ATTN_F16 / ATTN_BF16: P and dS are rounded to the input type before their
+ *                products (as the forward rounds P), accumulation in fp32, gradients rounded to
+ *                the input type. ATTN_F32: fp32 tensors and fp32 products throughout.
  *   others       as in attn_fwd.
  *
  * Two kernels run on `stream` in order (dQ and Delta, then dK and dV). Outputs must not overlap
@@ -280,7 +283,8 @@ int attn_bwd_strided_validate(const void *q, const int64_t *q_strides, const voi
 /*
  * attn_bwd_masked -- attn_bwd_strided plus the explicit mask of attn_fwd_masked (the same mask,
  * type and strides the forward was given; the article's §2.1-2.2 masks): the gradients of that
- * masked forward. The mask is a constant (no gradient). Returns as attn_bwd_strided; mask
+ * masked forward. The mask is a constant (no gradient). dtype ATTN_F16 or ATTN_BF16 only
+ * (ATTN_F32 is ATTN_ERR_DTYPE, as in attn_fwd_masked). Returns as attn_bwd_strided; mask
  * errors as attn_fwd_masked (ATTN_ERR_MASK, ATTN_ERR_NULL, ATTN_ERR_LAYOUT, ATTN_ERR_SHAPE, and
  * ATTN_ERR_ALIAS when an output overlaps the mask).
  */
@@ -308,8 +312,9 @@ int attn_bwd_masked_validate(const void *q, const int64_t *q_strides, const void
 /* attn_status_string -- a static, NUL-terminated description of a return code (never NULL). */
 const char *attn_status_string(int status);
 
-/* attn_version -- the library's interface version, currently 6 (2 added attn_fwd_strided, 3
- * attn_fwd_masked, 4 attn_bwd, 5 attn_bwd_strided, 6 attn_bwd_masked). */
+/* attn_version -- the library's interface version, currently 7 (2 added attn_fwd_strided, 3
+ * attn_fwd_masked, 4 attn_bwd, 5 attn_bwd_strided, 6 attn_bwd_masked, 7 ATTN_F32 in attn_bwd
+ * and attn_bwd_strided). */
 int attn_version(void);
 
 #ifdef __cplusplus

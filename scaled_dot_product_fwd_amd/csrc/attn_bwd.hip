@@ -822,10 +822,12 @@ int bwd_validate(const BwdLayouts& t, const float* lse, const float* ws, int B, 
   if (N > ATTN_MAX_N) return ATTN_ERR_SHAPE;
   if ((int64_t)B * Hq * (((int64_t)N + kBM - 1) / kBM) > ATTN_MAX_TILES) return ATTN_ERR_SHAPE;
   if (D != 16 && D != 32 && D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
-  if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+  if (dtype != ATTN_F16 && dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_DTYPE;
+  if (dtype == ATTN_F32 && mk.type != ATTN_MASK_NONE) return ATTN_ERR_DTYPE;
   if (!isfinite(scale)) return ATTN_ERR_SCALE;
+  const int es = dtype == ATTN_F32 ? 4 : 2;   // bytes per element
   for (const Layout* l : all)
-    if (!layout_ok(*l, D, 2)) return ATTN_ERR_LAYOUT;
+    if (!layout_ok(*l, D, es)) return ATTN_ERR_LAYOUT;
   if ((uintptr_t)lse % 4 != 0 || (uintptr_t)ws % 4 != 0) return ATTN_ERR_LAYOUT;
   if (!output_disjoint(t.dq, B, Hq, N, D) || !output_disjoint(t.dk, B, Hkv, N, D) ||
       !output_disjoint(t.dv, B, Hkv, N, D))
@@ -834,15 +836,15 @@ int bwd_validate(const BwdLayouts& t, const float* lse, const float* ws, int B, 
   // to one tile past N.
   int64_t smax = 0;
   for (const Layout* l : {&t.q, &t.k, &t.v, &t.dout}) smax = l->sn > smax ? l->sn : smax;
-  if (((int64_t)N + kBM) * smax * 2 + 2 * D > INT32_MAX) return ATTN_ERR_SHAPE;
+  if (((int64_t)N + kBM) * smax * es + es * D > INT32_MAX) return ATTN_ERR_SHAPE;
   // Outputs (dq, dk, dv and the workspace) overlap no input and no other output.
   const int64_t lb = (int64_t)B * Hq * N * 4;
   const void* outs[] = {t.dq.ptr, t.dk.ptr, t.dv.ptr, ws};
-  const int64_t osz[] = {t.dq.span(B, N, D, 2), t.dk.span(B, N, D, 2), t.dv.span(B, N, D, 2),
-                         2 * lb};
+  const int64_t osz[] = {t.dq.span(B, N, D, es), t.dk.span(B, N, D, es),
+                         t.dv.span(B, N, D, es), 2 * lb};
   const void* ins[] = {t.q.ptr, t.k.ptr, t.v.ptr, t.o.ptr, t.dout.ptr, lse};
-  const int64_t isz[] = {t.q.span(B, N, D, 2), t.k.span(B, N, D, 2), t.v.span(B, N, D, 2),
-                         t.o.span(B, N, D, 2), t.dout.span(B, N, D, 2), lb};
+  const int64_t isz[] = {t.q.span(B, N, D, es), t.k.span(B, N, D, es), t.v.span(B, N, D, es),
+                         t.o.span(B, N, D, es), t.dout.span(B, N, D, es), lb};
   for (int i = 0; i < 4; ++i) {
     for (int j = 0; j < 6; ++j)
       if (overlaps(outs[i], osz[i], ins[j], isz[j])) return ATTN_ERR_ALIAS;
@@ -865,6 +867,42 @@ int bwd_run(const BwdLayouts& t, const float* lse, float* ws, int B, int Hq, int
             const MaskArg& mk = no_mask()) {
   const int st = bwd_validate(t, lse, ws, B, Hq, Hkv, N, D, scale, valid_len, dtype, mk);
   if (st != ATTN_OK) return st;
+  if (dtype == ATTN_F32) {
+    F32BwdParams f;
+    f.q = (const float*)t.q.ptr;
+    f.k = (const float*)t.k.ptr;
+    f.v = (const float*)t.v.ptr;
+    f.o = (const float*)t.o.ptr;
+    f.dout = (const float*)t.dout.ptr;
+    f.lse = lse;
+    f.dq = (float*)t.dq.ptr;
+    f.dk = (float*)t.dk.ptr;
+    f.dv = (float*)t.dv.ptr;
+    f.delta = ws;
+    f.lse2 = ws + (size_t)B * Hq * N;
+    f.valid_len = valid_len;
+    f.B = B;
+    f.Hq = Hq;
+    f.Hkv = Hkv;
+    f.N = N;
+    f.group = Hq / Hkv;
+    f.nqt = (N + kBM - 1) / kBM;
+    f.nkt = (N + kBM - 1) / kBM;
+    f.xcd_order = ((int64_t)B * Hkv) % 8 == 0 ? 1 : 0;
+    f.qs_b = t.q.sb; f.qs_h = t.q.sh; f.qs_n = t.q.sn;
+    f.ks_b = t.k.sb; f.ks_h = t.k.sh; f.ks_n = t.k.sn;
+    f.vs_b = t.v.sb; f.vs_h = t.v.sh; f.vs_n = t.v.sn;
+    f.os_b = t.o.sb; f.os_h = t.o.sh; f.os_n = t.o.sn;
+    f.gs_b = t.dout.sb; f.gs_h = t.dout.sh; f.gs_n = t.dout.sn;
+    f.dqs_b = t.dq.sb; f.dqs_h = t.dq.sh; f.dqs_n = t.dq.sn;
+    f.dks_b = t.dk.sb; f.dks_h = t.dk.sh; f.dks_n = t.dk.sn;
+    f.dvs_b = t.dv.sb; f.dvs_h = t.dv.sh; f.dvs_n = t.dv.sn;
+    f.c = scale == 0.f ? 1.0f : fabsf(scale) * kLog2e;
+    f.qmul = scale < 0.f ? -1.0f : (scale == 0.f ? 0.0f : 1.0f);
+    f.scale = scale;
+    const hipError_t e = launch_bwd_f32(f, D, causal != 0, (hipStream_t)stream);
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+  }
   BwdParams p;
   p.q = (const uint16_t*)t.q.ptr;
   p.k = (const uint16_t*)t.k.ptr;

@@ -262,4 +262,38 @@ struct F32Params {
 // Queue the fp32 forward for D in {16, 32, 64, 128, 256}.
 hipError_t launch_fwd_f32(const F32Params& p, int D, bool causal, hipStream_t stream);
 
+// fp32 backward (attn_bwd_f32.hip): validated arguments, strides in elements.
+struct F32BwdParams {
+  const float* q;
+  const float* k;
+  const float* v;
+  const float* o;
+  const float* dout;
+  const float* lse;
+  float* dq;
+  float* dk;
+  float* dv;
+  float* delta;      // workspace row 0: D = rowsum(dO o O)
+  float* lse2;       // workspace row 1: L * log2(e) (0 for rows with no visible key)
+  const int32_t* valid_len;
+  int B, Hq, Hkv, N;
+  int group;         // Hq / Hkv
+  int nqt, nkt;      // ceil(N / kBM): query tiles (dQ kernel), key tiles (dK/dV kernel)
+  int xcd_order;     // 1: KV heads divide evenly over the 8 XCDs
+  int64_t qs_b, qs_h, qs_n;
+  int64_t ks_b, ks_h, ks_n;
+  int64_t vs_b, vs_h, vs_n;
+  int64_t os_b, os_h, os_n;
+  int64_t gs_b, gs_h, gs_n;
+  int64_t dqs_b, dqs_h, dqs_n;
+  int64_t dks_b, dks_h, dks_n;
+  int64_t dvs_b, dvs_h, dvs_n;
+  float c;           // |scale| * log2(e) (1 when scale == 0)
+  float qmul;        // sign of scale, 0 when scale == 0: multiplies one operand of the scores
+  float scale;       // the signed scale (dQ and dK carry it)
+};
+
+// Queue the fp32 backward (dQ kernel, then dK/dV kernel) for D in {16, 32, 64, 128}.
+hipError_t launch_bwd_f32(const F32BwdParams& p, int D, bool causal, hipStream_t stream);
+
 }  // namespace attn_detail

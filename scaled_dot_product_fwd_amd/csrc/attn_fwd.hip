@@ -827,4 +827,4 @@ extern "C" const char* attn_status_string(int status) {
   }
 }
 
-extern "C" int attn_version(void) { return 6; }
+extern "C" int attn_version(void) { return 7; }

@@ -159,8 +159,9 @@ def make_workload(w: Workload) -> Case:
 
 
 def make_grad(case: Case, seed) -> np.ndarray:
-    """The upstream gradient dO for a case: uint16 bits [B, Hq, N, D], iid N(0, 1) rounded to
-    the case's type, drawn from ``default_rng([21, *seed])`` (``seed`` an int or a list)."""
+    """The upstream gradient dO for a case: bits of the case's type [B, Hq, N, D] (uint16, or
+    uint32 for f32), iid N(0, 1) rounded to that type, drawn from ``default_rng([21, *seed])``
+    (``seed`` an int or a list)."""
     seed = list(seed) if isinstance(seed, (list, tuple)) else [seed]
     rng = np.random.default_rng([21] + seed)
     x = rng.standard_normal((case.B, case.Hq, case.N, case.D), dtype=np.float32)

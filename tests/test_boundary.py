@@ -45,7 +45,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_version(lib):
-    assert sdp.attn_version() == 6
+    assert sdp.attn_version() == 7
 
 
 def test_status_strings(lib):
@@ -258,6 +258,8 @@ def test_bwd_validate_accepts(lib):
     assert bcall(valid_len=None, D=64, dtype=sdp.ATTN_F16, causal=0, Hkv=8) == sdp.ATTN_OK
     assert bcall(D=16) == sdp.ATTN_OK
     assert bcall(D=32) == sdp.ATTN_OK
+    for d in (16, 32, 64, 128):
+        assert bcall(D=d, dtype=sdp.ATTN_F32) == sdp.ATTN_OK
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -268,8 +270,10 @@ def test_bwd_validate_accepts(lib):
     (dict(D=256), sdp.ATTN_ERR_HEAD_DIM),
     (dict(D=48), sdp.ATTN_ERR_HEAD_DIM),
     (dict(dtype=7), sdp.ATTN_ERR_DTYPE),
-    (dict(dtype=sdp.ATTN_F32), sdp.ATTN_ERR_DTYPE),
+    (dict(dtype=sdp.ATTN_F32, D=256), sdp.ATTN_ERR_HEAD_DIM),
     (dict(scale=float("nan")), sdp.ATTN_ERR_SCALE),
+    # dq right after a 16-bit-sized q overlaps q once elements are 4 bytes
+    (dict(dq=Q + 2 * 8 * 1000 * 128 * 2, dtype=sdp.ATTN_F32), sdp.ATTN_ERR_ALIAS),
     (dict(dq=DQ + 8), sdp.ATTN_ERR_LAYOUT),
     (dict(ws=DL + 2), sdp.ATTN_ERR_LAYOUT),
     (dict(dq=Q + 1024), sdp.ATTN_ERR_ALIAS),            # dq overlaps q
@@ -355,13 +359,14 @@ def test_no_fallback_path():
 
 # ---- attn_bwd_masked_validate
 def bmcall(**kw):
-    a = dict(mask=MK, mtype=sdp.ATTN_MASK_KEEP_U8, ms=None, N=MN, dq=DQ, ws=DL)
+    a = dict(mask=MK, mtype=sdp.ATTN_MASK_KEEP_U8, ms=None, N=MN, dq=DQ, ws=DL,
+             dtype=sdp.ATTN_BF16)
     a.update(kw)
     N = a["N"]
     return sdp.attn_bwd_masked_validate(Q, None, K, None, V, None, O, None, DO, None, L, a["dq"],
                                         None, DK, None, DV, None, a["ws"], SB, SH, 2, N, 128,
                                         0.088, 1, VL, a["mask"], a["mtype"], a["ms"],
-                                        sdp.ATTN_BF16)
+                                        a["dtype"])
 
 
 def test_bwd_masked_validate(lib):
@@ -370,6 +375,8 @@ def test_bwd_masked_validate(lib):
     assert bmcall(mtype=sdp.ATTN_MASK_NONE, mask=None) == sdp.ATTN_OK
     assert bmcall(ms=(0, MN * MN, MN)) == sdp.ATTN_OK                 # [Hq, N, N] per head
     assert bmcall(mtype=5) == sdp.ATTN_ERR_MASK
+    assert bmcall(dtype=sdp.ATTN_F32) == sdp.ATTN_ERR_DTYPE             # masks are 16-bit only
+    assert bmcall(mtype=sdp.ATTN_MASK_NONE, mask=None, dtype=sdp.ATTN_F32) == sdp.ATTN_OK
     assert bmcall(mask=None) == sdp.ATTN_ERR_NULL
     assert bmcall(mask=MK + 8) == sdp.ATTN_ERR_LAYOUT                 # misaligned
     assert bmcall(ms=(MN * MN, 0, MN - 16)) == sdp.ATTN_ERR_LAYOUT      # rows closer than N

@@ -17,12 +17,17 @@ from scaled_dot_product_fwd_amd import inputs
 
 pytestmark = pytest.mark.gpu
 
-BWD_TOL = {"bf16": 2e-2, "f16": 5e-3}
+# fp32: every product and sum in fp32 (no 16-bit rounding of P or dS); 1e-4 of the largest
+# gradient leaves room for fp32 accumulation over a few thousand keys (~1e-6 relative each).
+BWD_TOL = {"bf16": 2e-2, "f16": 5e-3, "f32": 1e-4}
 # Normaliser floor: where every gradient of a tensor cancels to ~0 in exact arithmetic (one key
 # per row, so dS = P (dP - D) = 0), the device's rounding leaves values near 1e-7 that are
-# compared against this floor instead of against 0.
-GRAD_FLOOR = 1e-3
-DELTA_TOL = {"bf16": 2e-2, "f16": 5e-3}
+# compared against this floor instead of against 0. In fp32 the residue of that cancellation is
+# the rounding of dP and D themselves (|dO| |v| ~ sqrt(D) times ~1e-7: ~2e-6 in dQ, and dK, dV
+# sum it over every query row of the group, ~5e-6 at 200 rows), so a fully cancelling fp32
+# tensor is held to 1e-5 absolute: a floor of 1e-5 / 1e-4.
+GRAD_FLOOR = {"bf16": 1e-3, "f16": 1e-3, "f32": 1e-1}
+DELTA_TOL = {"bf16": 2e-2, "f16": 5e-3, "f32": 1e-4}
 
 
 def run_bwd(case, dout_bits, dout_scale=1.0):
@@ -68,7 +73,7 @@ def check_grad(name, got, ref, dtype, tag, zero=None):
     if zero is not None and zero.any():
         assert np.all(got[zero] == 0.0), "%s %s: gradients that must vanish are not 0" % (
             tag, name)
-    scale = max(np.abs(ref).max(), GRAD_FLOOR)
+    scale = max(np.abs(ref).max(), GRAD_FLOOR[dtype])
     err = np.abs(got - ref).max() if got.size else 0.0
     rel = err / scale
     assert rel <= BWD_TOL[dtype], "%s %s: max err %.3g = %.3g of max |ref| %.3g" % (
@@ -119,6 +124,16 @@ BWD_SMALL = [
     ("bf16", 32, True, False, 2, 8, 2, 333),
     ("f16", 32, False, True, 2, 6, 3, 1000),
     ("bf16", 16, True, False, 2, 2, 1, 1),
+    # fp32 (attn_bwd_f32.hip): head dims 16 (the D = 32 geometry, half zeros), 32, 64, 128
+    ("f32", 128, True, False, 2, 8, 2, 333),
+    ("f32", 128, False, True, 2, 4, 2, 129),
+    ("f32", 64, True, True, 3, 4, 2, 257),
+    ("f32", 64, False, False, 1, 2, 2, 128),
+    ("f32", 32, True, False, 2, 8, 2, 333),
+    ("f32", 32, False, True, 2, 6, 3, 100),
+    ("f32", 16, True, True, 3, 4, 2, 257),
+    ("f32", 16, False, False, 1, 4, 4, 300),
+    ("f32", 128, True, True, 2, 6, 3, 1),
 ]
 
 
@@ -137,6 +152,8 @@ BWD_MANY = [
     ("bf16", 128, True, True, 4, 16, 4, 1100),
     ("f16", 64, False, True, 3, 24, 3, 1050),
     ("bf16", 64, True, False, 2, 40, 8, 1000),
+    ("f32", 128, True, True, 4, 16, 4, 1100),
+    ("f32", 64, False, False, 3, 24, 3, 700),
 ]
 
 
@@ -168,6 +185,25 @@ def test_bwd_scale_values(scale):
     compare_case(case, dout, "bwd scale=%g" % scale)
 
 
+@pytest.mark.parametrize("scale", [-0.125, 0.0, 2.0])
+def test_bwd_f32_scale_values(scale):
+    case = inputs.make_case(1, 4, 2, 200, 128, "f32", True, True, seed=[225, 1],
+                            scale=scale, valid_len=np.array([190], np.int32))
+    dout = inputs.make_grad(case, [225, 1])
+    log("bwd f32 scale %g" % scale)
+    compare_case(case, dout, "bwd f32 scale=%g" % scale)
+
+
+def test_bwd_f32_padding_edge_values():
+    """fp32: valid_len 0, negative, 1, exactly N and beyond N; causal and not."""
+    for causal in (False, True):
+        case = inputs.make_case(5, 4, 2, 150, 64, "f32", causal, True, seed=[227, causal],
+                                valid_len=np.array([0, -7, 1, 150, 4000], np.int32))
+        dout = inputs.make_grad(case, [227, causal])
+        log("bwd f32 padding edges causal=%d" % causal)
+        compare_case(case, dout, "bwd f32 padding-edges causal=%d" % causal)
+
+
 def test_bwd_rising_row_maximum():
     """Keys scaled up along the sequence: rows whose maximum moves from tile to tile, so P
     rebuilt from the forward's LSE must still match."""
@@ -182,12 +218,16 @@ def test_bwd_rising_row_maximum():
         compare_case(case, dout, "bwd rising causal=%d" % causal)
 
 
-@pytest.mark.parametrize("name", ["long_gqa", "causal_padded"])
+@pytest.mark.parametrize("name", ["long_gqa", "causal_padded", "long_gqa_f32"])
 def test_bwd_workload_slices(name):
     """Full-size workload in the benchmark's launch configuration; the oracle recomputes the
     gradients of eight (batch, KV head) groups, each with all its query heads."""
-    w = inputs.WORKLOADS[name]
-    case = inputs.make_workload(w)
+    w = inputs.WORKLOADS[name.replace("_f32", "")]
+    if name.endswith("_f32"):
+        case = inputs.make_case(w.B, w.Hq, w.Hkv, w.N, w.D, "f32", w.causal, w.padded,
+                                seed=[20, w.c], scale=w.scale)
+    else:
+        case = inputs.make_workload(w)
     dout = inputs.make_grad(case, [w.c])
     log("bwd workload %s" % name)
     dq, dk, dv, delta, O, L = run_bwd(case, dout)
@@ -233,9 +273,29 @@ def test_autograd_function_matches_entry_point():
         assert torch.equal(a, b)
 
 
+def test_autograd_f32_matches_entry_point():
+    """attention() on fp32 tensors returns exactly attn_bwd's fp32 gradients."""
+    import torch
+    case = inputs.make_case(2, 4, 2, 300, 64, "f32", True, True, seed=229)
+    dout = to_device(inputs.make_grad(case, 229), "f32")
+    base = [to_device(x, "f32") for x in (case.q_bits, case.k_bits, case.v_bits)]
+    a = [t.clone().requires_grad_() for t in base]
+    vl = torch.from_numpy(case.valid_len).cuda()
+    out = sdp.attention(*a, causal=True, valid_len=vl, scale=case.scale)
+    out.backward(dout)
+    o2, lse = sdp.forward(*base, causal=True, valid_len=vl, scale=case.scale)
+    g = sdp.backward(*base, o2, dout, lse, causal=True, valid_len=vl, scale=case.scale)
+    torch.cuda.synchronize()
+    assert out.dtype == torch.float32 and torch.equal(out, o2)
+    for x, y in zip(a, g):
+        assert y.dtype == torch.float32 and torch.equal(x.grad, y)
+
+
 # ---- strided tensors (attn_bwd_strided): the same logical values in other layouts
 BWD_STRIDED = [
     ("bnhd", "bf16", 128, True, True, 2, 8, 2, 300),
+    ("bnhd", "f32", 128, True, False, 2, 4, 2, 200),
+    ("padded_rows", "f32", 64, False, True, 2, 4, 4, 130),
     ("bnhd", "f16", 64, False, False, 2, 4, 4, 200),
     ("padded_rows", "bf16", 64, True, False, 2, 6, 3, 257),
     ("packed_qkv", "f16", 128, True, True, 2, 4, 4, 190),
