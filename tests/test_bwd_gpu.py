@@ -204,6 +204,61 @@ def test_bwd_f32_padding_edge_values():
         compare_case(case, dout, "bwd f32 padding-edges causal=%d" % causal)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bwd_deterministic(dtype):
+    """No atomics: two calls give bitwise equal gradients and workspace."""
+    case = inputs.make_case(2, 8, 2, 700, 128, dtype, True, True, seed=[231, len(dtype)])
+    dout = inputs.make_grad(case, [231, len(dtype)])
+    a = run_bwd(case, dout)
+    b = run_bwd(case, dout)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_bwd_guard_regions_untouched():
+    """dq, dk, dv and ws are views into larger buffers filled with a sentinel: nothing outside
+    the views may change, and the gradients inside still match the oracle."""
+    import torch
+    case = inputs.make_case(2, 4, 2, 333, 64, "f16", True, True, seed=233)
+    dout_bits = inputs.make_grad(case, 233)
+    q, k, v = (to_device(x, "f16") for x in (case.q_bits, case.k_bits, case.v_bits))
+    do = to_device(dout_bits, "f16")
+    vl = torch.from_numpy(case.valid_len).cuda()
+    out, lse = sdp.forward(q, k, v, causal=True, valid_len=vl, scale=case.scale)
+    pad = 4096
+
+    def guarded(shape, dtype, value):
+        n = int(np.prod(shape))
+        buf = torch.full((n + 2 * pad,), value, dtype=dtype, device="cuda")
+        return buf, buf[pad:pad + n].view(shape), n, value
+
+    g = [guarded(tuple(q.shape), torch.float16, 1234.0),
+         guarded(tuple(k.shape), torch.float16, -55.0),
+         guarded(tuple(v.shape), torch.float16, 99.0),
+         guarded((2,) + tuple(lse.shape), torch.float32, 777.0)]
+    sdp.backward(q, k, v, out, do, lse, causal=True, valid_len=vl, scale=case.scale,
+                 dq=g[0][1], dk=g[1][1], dv=g[2][1], ws=g[3][1])
+    torch.cuda.synchronize()
+    for buf, _, n, value in g:
+        assert torch.all(buf[:pad] == value) and torch.all(buf[pad + n:] == value)
+    qw, kw, vw = case.widened()
+    ref = oracle.attn_bwd(qw, kw, vw, inputs.widen(dout_bits, "f16"), case.scale, True,
+                          case.valid_len)
+    for name, (_, view, _, _), r in zip(("dQ", "dK", "dV"), g[:3], ref):
+        check_grad(name, from_device(view, "f16"), r, "f16", "guarded")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_bwd_on_side_stream(dtype):
+    """forward and backward queued on a non-default stream (torch's current stream)."""
+    import torch
+    case = inputs.make_case(1, 4, 4, 300, 128, dtype, True, False, seed=[235, len(dtype)])
+    dout = inputs.make_grad(case, [235, len(dtype)])
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        compare_case(case, dout, "side stream %s" % dtype)
+
+
 def test_bwd_rising_row_maximum():
     """Keys scaled up along the sequence: rows whose maximum moves from tile to tile, so P
     rebuilt from the forward's LSE must still match."""
