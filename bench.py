@@ -250,7 +250,9 @@ def main():
             dout = dout.transpose(1, 2).contiguous()
         step()
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-        ws = torch.empty((2,) + tuple(lse.shape), dtype=torch.float32, device="cuda")
+        # the workspace with room for the dK/dV split (attn_bwd_ws) where the shape wants one
+        ws = torch.empty((sdp.attn_bwd_workspace_floats(w.B, w.Hq, w.Hkv, w.N, w.D),),
+                         dtype=torch.float32, device="cuda")
 
         def step():  # noqa: F811 -- the timed step is the backward
             sdp.backward(q, k, v, out, dout, lse, causal=w.causal, valid_len=vl, scale=w.scale,

@@ -66,7 +66,8 @@ typedef enum {
     ATTN_ERR_LAYOUT = -8,   /* a pointer is not 16-byte aligned, a stride is negative or not a
                                multiple of 16 bytes, rows are less than D elements apart, or
                                two output rows share memory; for a mask see attn_fwd_masked */
-    ATTN_ERR_MASK = -9      /* mask_type is not one of attn_mask_t */
+    ATTN_ERR_MASK = -9,     /* mask_type is not one of attn_mask_t */
+    ATTN_ERR_WORKSPACE = -10 /* attn_bwd_ws: ws_floats is below 2 * B * Hq * N */
 } attn_status_t;
 
 /* Explicit mask kinds of attn_fwd_masked. */
@@ -309,12 +310,56 @@ int attn_bwd_masked_validate(const void *q, const int64_t *q_strides, const void
                              const void *mask, int mask_type, const int64_t *mask_strides,
                              int dtype);
 
+/*
+ * attn_bwd_ws -- attn_bwd_masked with the workspace's size, so that the library may use more of
+ * it: with room for fp32 partial sums the dK/dV kernel splits each 128-key tile's (query head,
+ * query tile) iterations over up to 16 workgroups (enough for at least 1024 workgroups), and a
+ * third kernel adds the parts in a fixed order (deterministic) and rounds once. This fills the
+ * device where few key tiles exist (MQA, short sequences, small batches). mask_type
+ * ATTN_MASK_NONE (mask and mask_strides ignored) gives attn_bwd_strided; NULL strides mean
+ * contiguous tensors, as there.
+ *
+ *   ws, ws_floats  device float32 workspace of ws_floats values (>= 2 * B * Hq * N, else
+ *                  ATTN_ERR_WORKSPACE); attn_bwd_workspace_floats gives the size that allows
+ *                  the split, smaller sizes use a smaller split or none. On return ws holds
+ *                  Delta and the base-2 LSE as in attn_bwd; the partial sums follow from the
+ *                  next 16-byte boundary and are scratch.
+ *   others         as in attn_bwd_masked (dtype ATTN_F32 only with ATTN_MASK_NONE).
+ */
+int attn_bwd_ws(const void *q, const int64_t *q_strides, const void *k,
+                const int64_t *k_strides, const void *v, const int64_t *v_strides,
+                const void *out, const int64_t *out_strides, const void *dout,
+                const int64_t *dout_strides, const float *lse, void *dq,
+                const int64_t *dq_strides, void *dk, const int64_t *dk_strides, void *dv,
+                const int64_t *dv_strides, float *ws, int64_t ws_floats, int B, int Hq,
+                int Hkv, int N, int D, float scale, int causal, const int32_t *valid_len,
+                const void *mask, int mask_type, const int64_t *mask_strides, int dtype,
+                void *stream);
+
+/* attn_bwd_ws_validate -- the host-only argument check of attn_bwd_ws. */
+int attn_bwd_ws_validate(const void *q, const int64_t *q_strides, const void *k,
+                         const int64_t *k_strides, const void *v, const int64_t *v_strides,
+                         const void *out, const int64_t *out_strides, const void *dout,
+                         const int64_t *dout_strides, const float *lse, const void *dq,
+                         const int64_t *dq_strides, const void *dk, const int64_t *dk_strides,
+                         const void *dv, const int64_t *dv_strides, const float *ws,
+                         int64_t ws_floats, int B, int Hq, int Hkv, int N, int D, float scale,
+                         int causal, const int32_t *valid_len, const void *mask, int mask_type,
+                         const int64_t *mask_strides, int dtype);
+
+/*
+ * attn_bwd_workspace_floats -- the workspace size (float32 values) with which attn_bwd_ws uses
+ * its full split for these sizes: 2 * B * Hq * N when no split is needed, else that plus
+ * 4 + 2 * split * B * Hkv * N * D. -1 when a size is below 1. Host only.
+ */
+int64_t attn_bwd_workspace_floats(int B, int Hq, int Hkv, int N, int D);
+
 /* attn_status_string -- a static, NUL-terminated description of a return code (never NULL). */
 const char *attn_status_string(int status);
 
-/* attn_version -- the library's interface version, currently 7 (2 added attn_fwd_strided, 3
+/* attn_version -- the library's interface version, currently 8 (2 added attn_fwd_strided, 3
  * attn_fwd_masked, 4 attn_bwd, 5 attn_bwd_strided, 6 attn_bwd_masked, 7 ATTN_F32 in attn_bwd
- * and attn_bwd_strided). */
+ * and attn_bwd_strided, 8 attn_bwd_ws and attn_bwd_workspace_floats). */
 int attn_version(void);
 
 #ifdef __cplusplus

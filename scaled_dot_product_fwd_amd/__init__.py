@@ -26,7 +26,7 @@ __all__ = ["ATTN_F16", "ATTN_BF16", "ATTN_F32", "AttnError", "attn_fwd", "attn_f
            "attn_fwd_strided", "attn_fwd_strided_validate", "attn_fwd_masked",
            "attn_fwd_masked_validate", "attn_bwd", "attn_bwd_validate", "attn_bwd_strided",
            "attn_bwd_strided_validate", "attn_bwd_masked", "attn_bwd_masked_validate",
-           "attention",
+           "attn_bwd_ws", "attn_bwd_ws_validate", "attn_bwd_workspace_floats", "attention",
            "backward", "attn_status_string",
            "attn_version", "forward", "library_path", "load_library"]
 
@@ -44,6 +44,7 @@ ATTN_ERR_LAUNCH = -6
 ATTN_ERR_ALIAS = -7
 ATTN_ERR_LAYOUT = -8
 ATTN_ERR_MASK = -9
+ATTN_ERR_WORKSPACE = -10
 
 ATTN_MASK_NONE = 0
 ATTN_MASK_KEEP_U8 = 1
@@ -119,6 +120,16 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_bwd_masked_validate.argtypes = ([_vp, _i64p] * 5 + [_vp] + [_vp, _i64p] * 3 +
                                              [_vp] + [_c_int] * 5 + [_c_float, _c_int, _vp, _vp,
                                                                      _c_int, _i64p, _c_int])
+    lib.attn_bwd_ws.restype = _c_int
+    lib.attn_bwd_ws.argtypes = ([_vp, _i64p] * 5 + [_vp] + [_vp, _i64p] * 3 + [_vp, ctypes.c_int64]
+                                + [_c_int] * 5 + [_c_float, _c_int, _vp, _vp, _c_int, _i64p,
+                                                  _c_int, _vp])
+    lib.attn_bwd_ws_validate.restype = _c_int
+    lib.attn_bwd_ws_validate.argtypes = ([_vp, _i64p] * 5 + [_vp] + [_vp, _i64p] * 3 +
+                                         [_vp, ctypes.c_int64] + [_c_int] * 5 +
+                                         [_c_float, _c_int, _vp, _vp, _c_int, _i64p, _c_int])
+    lib.attn_bwd_workspace_floats.restype = ctypes.c_int64
+    lib.attn_bwd_workspace_floats.argtypes = [_c_int] * 5
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_status_string.argtypes = [_c_int]
     lib.attn_version.restype = _c_int
@@ -257,6 +268,35 @@ def attn_bwd_masked_validate(q, q_strides, k, k_strides, v, v_strides, out, out_
         _strides(out_strides), dout, _strides(dout_strides), lse, dq, _strides(dq_strides), dk,
         _strides(dk_strides), dv, _strides(dv_strides), ws, B, Hq, Hkv, N, D, scale, int(causal),
         valid_len, mask, mask_type, _strides(mask_strides), dtype)
+
+
+def attn_bwd_ws(q, q_strides, k, k_strides, v, v_strides, out, out_strides, dout, dout_strides,
+                lse, dq, dq_strides, dk, dk_strides, dv, dv_strides, ws, ws_floats, B, Hq, Hkv, N,
+                D, scale, causal, valid_len, mask, mask_type, mask_strides, dtype,
+                stream) -> int:
+    """C ``attn_bwd_ws``; pointers as integers, strides as 3-sequences or None."""
+    return load_library().attn_bwd_ws(
+        q, _strides(q_strides), k, _strides(k_strides), v, _strides(v_strides), out,
+        _strides(out_strides), dout, _strides(dout_strides), lse, dq, _strides(dq_strides), dk,
+        _strides(dk_strides), dv, _strides(dv_strides), ws, ws_floats, B, Hq, Hkv, N, D, scale,
+        int(causal), valid_len, mask, mask_type, _strides(mask_strides), dtype, stream)
+
+
+def attn_bwd_ws_validate(q, q_strides, k, k_strides, v, v_strides, out, out_strides, dout,
+                         dout_strides, lse, dq, dq_strides, dk, dk_strides, dv, dv_strides, ws,
+                         ws_floats, B, Hq, Hkv, N, D, scale, causal, valid_len, mask, mask_type,
+                         mask_strides, dtype) -> int:
+    """C ``attn_bwd_ws_validate``: host-only argument check, no HIP call."""
+    return load_library().attn_bwd_ws_validate(
+        q, _strides(q_strides), k, _strides(k_strides), v, _strides(v_strides), out,
+        _strides(out_strides), dout, _strides(dout_strides), lse, dq, _strides(dq_strides), dk,
+        _strides(dk_strides), dv, _strides(dv_strides), ws, ws_floats, B, Hq, Hkv, N, D, scale,
+        int(causal), valid_len, mask, mask_type, _strides(mask_strides), dtype)
+
+
+def attn_bwd_workspace_floats(B: int, Hq: int, Hkv: int, N: int, D: int) -> int:
+    """C ``attn_bwd_workspace_floats``: float32 values of the workspace attn_bwd_ws splits with."""
+    return load_library().attn_bwd_workspace_floats(B, Hq, Hkv, N, D)
 
 
 def attn_status_string(status: int) -> str:
@@ -402,8 +442,10 @@ def backward(q, k, v, out, dout, lse, causal: bool, valid_len=None,
     contiguous D dimension are accepted (contiguous [B, H, N, D] tensors take attn_bwd, others
     attn_bwd_strided, with no copies). ``attn_mask`` is the forward's explicit mask (as in
     forward(); the call then goes to attn_bwd_masked). Gradients (each in its input's layout)
-    and the float32 workspace ``ws`` ([2, B, Hq, N]: Delta, then the LSE in base 2) are
-    allocated with torch when not given.
+    and the float32 workspace ``ws`` are allocated with torch when not given. A workspace of
+    exactly 2 * B * Hq * N values (Delta, then the LSE in base 2) takes attn_bwd /
+    attn_bwd_strided / attn_bwd_masked; an allocated or larger one (attn_bwd_workspace_floats
+    values) takes attn_bwd_ws, which may split the dK/dV work over more workgroups.
     """
     import torch
     if layout not in ("bhnd", "bnhd"):
@@ -435,7 +477,8 @@ def backward(q, k, v, out, dout, lse, causal: bool, valid_len=None,
             raise ValueError("%s must be a device tensor of shape %s, q's dtype, D contiguous"
                              % (name, shape))
     if ws is None:
-        ws = torch.empty((2, B, Hq, N), dtype=torch.float32, device=q.device)
+        ws = torch.empty((attn_bwd_workspace_floats(B, Hq, Hkv, N, D),), dtype=torch.float32,
+                         device=q.device)
     elif ws.dtype != torch.float32 or ws.numel() < 2 * B * Hq * N or not ws.is_contiguous():
         raise ValueError("ws must be a contiguous float32 tensor of 2 * B * Hq * N values")
     vl_ptr = None
@@ -446,7 +489,19 @@ def backward(q, k, v, out, dout, lse, causal: bool, valid_len=None,
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     views = (qv, kv, vv, ov, gv, dqv, dkv, dvv)
-    if attn_mask is not None:
+    if ws.numel() > 2 * B * Hq * N:
+        m, mtype = None, ATTN_MASK_NONE
+        if attn_mask is not None:
+            m, mtype = _mask_view(attn_mask, q.dtype, B, Hq, N)
+        st = attn_bwd_ws(
+            qv.data_ptr(), qv.stride()[:3], kv.data_ptr(), kv.stride()[:3], vv.data_ptr(),
+            vv.stride()[:3], ov.data_ptr(), ov.stride()[:3], gv.data_ptr(), gv.stride()[:3],
+            lse.data_ptr(), dqv.data_ptr(), dqv.stride()[:3], dkv.data_ptr(), dkv.stride()[:3],
+            dvv.data_ptr(), dvv.stride()[:3], ws.data_ptr(), ws.numel(), B, Hq, Hkv, N, D,
+            float(scale), int(bool(causal)), vl_ptr, None if m is None else m.data_ptr(), mtype,
+            None if m is None else m.stride()[:3], _dtype_code(q), stream.cuda_stream)
+        name = "attn_bwd_ws"
+    elif attn_mask is not None:
         m, mtype = _mask_view(attn_mask, q.dtype, B, Hq, N)
         st = attn_bwd_masked(
             qv.data_ptr(), qv.stride()[:3], kv.data_ptr(), kv.stride()[:3], vv.data_ptr(),

@@ -13,7 +13,8 @@ import tempfile
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRCS = [os.path.join(PKG, "csrc", name)
-        for name in ("attn_fwd.hip", "attn_fwd_f32.hip", "attn_bwd.hip", "attn_bwd_f32.hip")]
+        for name in ("attn_fwd.hip", "attn_fwd_f32.hip", "attn_bwd.hip", "attn_bwd_f32.hip",
+                     "attn_api.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -85,6 +85,11 @@ struct BwdParams {
   const void* mask;
   int64_t ms_b, ms_h, ms_n;
   float mscale;    // log2(e) / c: an additive mask value in raw score units
+  // Split of each key tile's (query head, query tile) iterations over `split` workgroups
+  // (1: none). With split > 1 the dK/dV kernel writes fp32 partial sums (dK already scaled)
+  // to part[2][split][B][Hkv][N][DH] and bwd_reduce adds them in split order.
+  int split;
+  float* part;
 };
 
 // The 4 keys 8g + 4h .. +3 of one mask row as read from a slot: uint8 bytes (keep) or 16-bit
@@ -148,6 +153,67 @@ __device__ inline void store_rows(const f32x16 (&acc)[Geo<D>::OT], float mul,
     const int cc = lane % G::CH;
     const u32x4 v = *(const u32x4*)(ost + r * G::ROW + 16 * (cc ^ (r & (G::CH - 1))));
     if (row0 + r < n && (DH == D || cc < DH / 8)) *(u32x4*)(dst + (row0 + r) * rs + 8 * cc) = v;
+  }
+}
+
+// Write one row of a wave's transposed fp32 block (acc[u][4 r4 + e] is element 32u + 8 r4 +
+// 4h + e of the lane's row) times `mul` to `dst` (DH <= D elements; chunks past DH are skipped).
+template <int D, int DH>
+__device__ inline void store_part(const f32x16 (&acc)[Geo<D>::OT], float mul, float* dst, int h) {
+#pragma unroll
+  for (int u = 0; u < Geo<D>::OT; ++u)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      if (32 * u + 8 * r4 + 4 * h >= DH) continue;
+      f32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = acc[u][4 * r4 + e] * mul;
+      *(f32x4*)(dst + 32 * u + 8 * r4 + 4 * h) = w;
+    }
+}
+
+// Sum of the split parts of dK and dV in part order, rounded once to the output type.
+struct ReduceParams {
+  const float* part;
+  void* dk;
+  void* dv;
+  int B, Hkv, N, DH, split;
+  int64_t dks_b, dks_h, dks_n;
+  int64_t dvs_b, dvs_h, dvs_n;
+};
+
+template <int DT>
+__global__ __launch_bounds__(256) void attn_bwd_reduce_kernel(ReduceParams p) {
+  const int C = p.DH / 4;   // 4-element chunks per row
+  const int64_t rows = (int64_t)p.B * p.Hkv * p.N;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * C) return;
+  const int64_t row = i / C;
+  const int c = (int)(i - row * C);
+  const int n = (int)(row % p.N);
+  const int64_t bk = row / p.N;
+  const int kvh = (int)(bk % p.Hkv), b = (int)(bk / p.Hkv);
+  const size_t plane = (size_t)rows * p.DH;
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    const float* src = p.part + (size_t)which * p.split * plane + (size_t)row * p.DH + 4 * c;
+    f32x4 acc = *(const f32x4*)src;
+    for (int s = 1; s < p.split; ++s) {
+      const f32x4 x = *(const f32x4*)(src + (size_t)s * plane);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += x[e];
+    }
+    const int64_t off = which == 0 ? b * p.dks_b + kvh * p.dks_h + n * p.dks_n
+                                   : b * p.dvs_b + kvh * p.dvs_h + n * p.dvs_n;
+    void* dst = which == 0 ? p.dk : p.dv;
+    if constexpr (DT == ATTN_F32) {
+      *(f32x4*)((float*)dst + off + 4 * c) = acc;
+    } else {
+      using M = Mfma<DT>;
+      const uint32_t w0 = (uint32_t)M::round1(acc[0]) | ((uint32_t)M::round1(acc[1]) << 16);
+      const uint32_t w1 = (uint32_t)M::round1(acc[2]) | ((uint32_t)M::round1(acc[3]) << 16);
+      *(u32x2*)((uint16_t*)dst + off + 4 * c) = u32x2{w0, w1};
+    }
   }
 }
 
@@ -486,11 +552,13 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
   // masking tile kt sees N - 128 kt queries), both heads' tile 0 first. Longest-first keeps the
   // XCD's last workgroups short (one KV head after the other left a ~20 % tail); blocks of two
   // keep the Q / dO working set to two KV heads.
-  int kt, b, kvh;
+  int kt, b, kvh, sp;
   {
-    const int wid = blockIdx.x;
+    // consecutive workgroups of one XCD take the `split` parts of one key tile
     if (p.xcd_order) {
-      const int xcd = wid & 7, local = wid >> 3;
+      const int xcd = blockIdx.x & 7, local0 = blockIdx.x >> 3;
+      const int local = local0 / p.split;
+      sp = local0 - local * p.split;
       const int hpx = (p.B * p.Hkv) >> 3;
       const int blk = (hpx & 1) ? 1 : 2;
       const int pair = local / (blk * p.nkt);
@@ -501,6 +569,8 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
       b = kv_head / p.Hkv;
       kvh = kv_head - b * p.Hkv;
     } else {
+      const int wid = blockIdx.x / p.split;
+      sp = blockIdx.x - wid * p.split;
       const int BK = p.B * p.Hkv;
       kt = wid / BK;
       const int bk = wid - kt * BK;
@@ -521,7 +591,11 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
 
   const int qstart = CAUSAL ? k0 : 0;
   const int ntq = k0 < kv_end ? (p.N - qstart + kQT - 1) / kQT : 0;   // query tiles per head
-  const int iters = ntq * p.group;
+  // this workgroup's share [it0, it0 + iters) of the key tile's ntq * group iterations (query
+  // head major, query tile minor)
+  const int total = ntq * p.group;
+  const int it0 = (int)((int64_t)total * sp / p.split);
+  const int iters = (int)((int64_t)total * (sp + 1) / p.split) - it0;
 
   if (iters > 0) {
     // K^T fragments of this lane's key (B operand: K[key][16s + 8h .. +7]), sign/zero applied.
@@ -630,7 +704,8 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
     // lockstep across the key-tile workgroups, every head at each tile, cut the HBM traffic by
     // 3x but ran ~10 % slower under causal masking.)
     // State: (g, q0) of the tile being computed and of the next one to fetch.
-    int g_cur = 0, q_cur = qstart, g_nxt = 0, q_nxt = qstart;
+    const int g0 = it0 / ntq, qs0 = qstart + (it0 - g0 * ntq) * kQT;
+    int g_cur = g0, q_cur = qs0, g_nxt = g0, q_nxt = qs0;
     auto advance = [&](int& g, int& q0) {
       q0 += kQT;
       if (q0 >= p.N) { q0 = qstart; ++g; }
@@ -735,6 +810,16 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
     }
     wait_loads_and_lds();
   }
+  if (p.split > 1) {
+    // fp32 partial sums of this part; rows past N are not written
+    const size_t plane = (size_t)p.B * p.Hkv * p.N * DH;
+    float* pk = p.part + (size_t)sp * plane + ((size_t)b * p.Hkv + kvh) * p.N * DH;
+    if (key < p.N) {
+      store_part<D, DH>(dk, p.scale, pk + (size_t)key * DH, h);
+      store_part<D, DH>(dv, 1.0f, pk + (size_t)p.split * plane + (size_t)key * DH, h);
+    }
+    return;
+  }
   __syncthreads();
   // dK = scale * (dK^T)^T, dV = (dV^T)^T; rows past N are not written. Staging reuses the Q/dO
   // buffers (every wave is past its last read).
@@ -764,7 +849,7 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
 template <int DT, int D, bool CAUSAL, int MK>
 hipError_t launch_bwd(const BwdParams& p, hipStream_t s) {
   const int64_t nq = (int64_t)p.B * p.Hq * p.nqt;
-  const int64_t nk = (int64_t)p.B * p.Hkv * p.nkt;
+  const int64_t nk = (int64_t)p.B * p.Hkv * p.nkt * p.split;
   hipLaunchKernelGGL((attn_bwd_dq_kernel<DT, D, CAUSAL, MK>), dim3((unsigned)nq),
                      dim3(kThreads), 0, s, p);
   hipError_t e = hipGetLastError();
@@ -811,8 +896,37 @@ BwdLayouts bwd_layouts(const void* q, const int64_t* qs, const void* k, const in
                     strided(dk, dks, Hkv, N, D),  strided(dv, dvs, Hkv, N, D)};
 }
 
-int bwd_validate(const BwdLayouts& t, const float* lse, const float* ws, int B, int Hq, int Hkv,
-                 int N, int D, float scale, const int32_t* valid_len, int dtype,
+// Workspace of a backward call: Delta and the base-2 LSE (2 B Hq N floats), then, when the
+// dK/dV kernel splits each key tile's iterations over `split` workgroups, the fp32 partial sums
+// [2][split][B][Hkv][N][D] from the next 16-byte boundary.
+int64_t ws_base_floats(int B, int Hq, int N) { return 2 * (int64_t)B * Hq * N; }
+
+int64_t ws_floats_for(int B, int Hq, int Hkv, int N, int D, int split) {
+  const int64_t base = ws_base_floats(B, Hq, N);
+  if (split <= 1) return base;
+  return base + 4 + 2 * (int64_t)split * B * Hkv * N * D;
+}
+
+// Parts per key tile: powers of two up to 16 until there are at least 1024 dK/dV workgroups
+// (twice the 512 the device holds at once), as long as a part keeps about 32 iterations of a
+// key tile's average (half of its group * N / 32 query tiles) to pay for writing and reading
+// its partial sums, and as far as the workspace holds them.
+int bwd_split(int B, int Hq, int Hkv, int N, int D, int64_t ws_floats) {
+  const int64_t tiles = (int64_t)B * Hkv * ((N + kBM - 1) / kBM);
+  const int64_t avg_iters = (int64_t)(Hq / Hkv) * ((N + kQT - 1) / kQT) / 2;
+  int split = 1;
+  while (split < 16 && tiles * split < 1024 && avg_iters / (2 * split) >= 32) split *= 2;
+  while (split > 1 && ws_floats_for(B, Hq, Hkv, N, D, split) > ws_floats) split /= 2;
+  return split;
+}
+
+float* part_base(float* ws, int B, int Hq, int N) {
+  const uintptr_t a = (uintptr_t)(ws + ws_base_floats(B, Hq, N));
+  return (float*)((a + 15) & ~(uintptr_t)15);
+}
+
+int bwd_validate(const BwdLayouts& t, const float* lse, const float* ws, int64_t ws_floats, int B,
+                 int Hq, int Hkv, int N, int D, float scale, const int32_t* valid_len, int dtype,
                  const MaskArg& mk = no_mask()) {
   const Layout* all[] = {&t.q, &t.k, &t.v, &t.o, &t.dout, &t.dq, &t.dk, &t.dv};
   for (const Layout* l : all)
@@ -829,6 +943,7 @@ int bwd_validate(const BwdLayouts& t, const float* lse, const float* ws, int B, 
   for (const Layout* l : all)
     if (!layout_ok(*l, D, es)) return ATTN_ERR_LAYOUT;
   if ((uintptr_t)lse % 4 != 0 || (uintptr_t)ws % 4 != 0) return ATTN_ERR_LAYOUT;
+  if (ws_floats < ws_base_floats(B, Hq, N)) return ATTN_ERR_WORKSPACE;
   if (!output_disjoint(t.dq, B, Hq, N, D) || !output_disjoint(t.dk, B, Hkv, N, D) ||
       !output_disjoint(t.dv, B, Hkv, N, D))
     return ATTN_ERR_LAYOUT;
@@ -837,11 +952,13 @@ int bwd_validate(const BwdLayouts& t, const float* lse, const float* ws, int B, 
   int64_t smax = 0;
   for (const Layout* l : {&t.q, &t.k, &t.v, &t.dout}) smax = l->sn > smax ? l->sn : smax;
   if (((int64_t)N + kBM) * smax * es + es * D > INT32_MAX) return ATTN_ERR_SHAPE;
-  // Outputs (dq, dk, dv and the workspace) overlap no input and no other output.
+  // Outputs (dq, dk, dv and the part of the workspace this call uses) overlap no input and no
+  // other output.
   const int64_t lb = (int64_t)B * Hq * N * 4;
+  const int split = bwd_split(B, Hq, Hkv, N, D, ws_floats);
   const void* outs[] = {t.dq.ptr, t.dk.ptr, t.dv.ptr, ws};
   const int64_t osz[] = {t.dq.span(B, N, D, es), t.dk.span(B, N, D, es),
-                         t.dv.span(B, N, D, es), 2 * lb};
+                         t.dv.span(B, N, D, es), ws_floats_for(B, Hq, Hkv, N, D, split) * 4};
   const void* ins[] = {t.q.ptr, t.k.ptr, t.v.ptr, t.o.ptr, t.dout.ptr, lse};
   const int64_t isz[] = {t.q.span(B, N, D, es), t.k.span(B, N, D, es), t.v.span(B, N, D, es),
                          t.o.span(B, N, D, es), t.dout.span(B, N, D, es), lb};
@@ -862,11 +979,40 @@ int bwd_validate(const BwdLayouts& t, const float* lse, const float* ws, int B, 
   return ATTN_OK;
 }
 
-int bwd_run(const BwdLayouts& t, const float* lse, float* ws, int B, int Hq, int Hkv, int N,
-            int D, float scale, int causal, const int32_t* valid_len, int dtype, void* stream,
-            const MaskArg& mk = no_mask()) {
-  const int st = bwd_validate(t, lse, ws, B, Hq, Hkv, N, D, scale, valid_len, dtype, mk);
+// Queue the sum of the split parts into dk and dv.
+hipError_t launch_reduce(const BwdLayouts& t, const float* part, int B, int Hkv, int N, int D,
+                         int split, int dtype, hipStream_t s) {
+  ReduceParams r;
+  r.part = part;
+  r.dk = (void*)t.dk.ptr;
+  r.dv = (void*)t.dv.ptr;
+  r.B = B;
+  r.Hkv = Hkv;
+  r.N = N;
+  r.DH = D;
+  r.split = split;
+  r.dks_b = t.dk.sb; r.dks_h = t.dk.sh; r.dks_n = t.dk.sn;
+  r.dvs_b = t.dv.sb; r.dvs_h = t.dv.sh; r.dvs_n = t.dv.sn;
+  const int64_t n = (int64_t)B * Hkv * N * (D / 4);
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (dtype == ATTN_F32)
+    hipLaunchKernelGGL(attn_bwd_reduce_kernel<ATTN_F32>, grid, dim3(256), 0, s, r);
+  else if (dtype == ATTN_BF16)
+    hipLaunchKernelGGL(attn_bwd_reduce_kernel<ATTN_BF16>, grid, dim3(256), 0, s, r);
+  else
+    hipLaunchKernelGGL(attn_bwd_reduce_kernel<ATTN_F16>, grid, dim3(256), 0, s, r);
+  return hipGetLastError();
+}
+
+int bwd_run(const BwdLayouts& t, const float* lse, float* ws, int64_t ws_floats, int B, int Hq,
+            int Hkv, int N, int D, float scale, int causal, const int32_t* valid_len, int dtype,
+            void* stream, const MaskArg& mk = no_mask()) {
+  const int st =
+      bwd_validate(t, lse, ws, ws_floats, B, Hq, Hkv, N, D, scale, valid_len, dtype, mk);
   if (st != ATTN_OK) return st;
+  const int split = bwd_split(B, Hq, Hkv, N, D, ws_floats);
+  float* const part = split > 1 ? part_base(ws, B, Hq, N) : nullptr;
+  const hipStream_t hs = (hipStream_t)stream;
   if (dtype == ATTN_F32) {
     F32BwdParams f;
     f.q = (const float*)t.q.ptr;
@@ -900,7 +1046,10 @@ int bwd_run(const BwdLayouts& t, const float* lse, float* ws, int B, int Hq, int
     f.c = scale == 0.f ? 1.0f : fabsf(scale) * kLog2e;
     f.qmul = scale < 0.f ? -1.0f : (scale == 0.f ? 0.0f : 1.0f);
     f.scale = scale;
-    const hipError_t e = launch_bwd_f32(f, D, causal != 0, (hipStream_t)stream);
+    f.split = split;
+    f.part = part;
+    hipError_t e = launch_bwd_f32(f, D, causal != 0, hs);
+    if (e == hipSuccess && split > 1) e = launch_reduce(t, part, B, Hkv, N, D, split, dtype, hs);
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
   }
   BwdParams p;
@@ -940,10 +1089,11 @@ int bwd_run(const BwdLayouts& t, const float* lse, float* ws, int B, int Hq, int
   p.mask = mk.ptr;
   p.ms_b = mk.sb; p.ms_h = mk.sh; p.ms_n = mk.sn;
   p.mscale = kLog2e / p.c;
-  const hipStream_t s = (hipStream_t)stream;
-  const hipError_t e =
-      dtype == ATTN_BF16 ? dispatch_bwd<ATTN_BF16>(p, D, causal != 0, mk.type, s)
-                         : dispatch_bwd<ATTN_F16>(p, D, causal != 0, mk.type, s);
+  p.split = split;
+  p.part = part;
+  hipError_t e = dtype == ATTN_BF16 ? dispatch_bwd<ATTN_BF16>(p, D, causal != 0, mk.type, hs)
+                                    : dispatch_bwd<ATTN_F16>(p, D, causal != 0, mk.type, hs);
+  if (e == hipSuccess && split > 1) e = launch_reduce(t, part, B, Hkv, N, D, split, dtype, hs);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
@@ -957,7 +1107,8 @@ extern "C" int attn_bwd_validate(const void* q, const void* k, const void* v, co
   (void)causal;
   return bwd_validate(bwd_layouts(q, nullptr, k, nullptr, v, nullptr, out, nullptr, dout,
                                   nullptr, dq, nullptr, dk, nullptr, dv, nullptr, Hq, Hkv, N, D),
-                      lse, ws, B, Hq, Hkv, N, D, scale, valid_len, dtype);
+                      lse, ws, ws_base_floats(B, Hq, N), B, Hq, Hkv, N, D, scale, valid_len,
+                      dtype);
 }
 
 extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* out,
@@ -966,7 +1117,8 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
                         int causal, const int32_t* valid_len, int dtype, void* stream) {
   return bwd_run(bwd_layouts(q, nullptr, k, nullptr, v, nullptr, out, nullptr, dout, nullptr,
                              dq, nullptr, dk, nullptr, dv, nullptr, Hq, Hkv, N, D),
-                 lse, ws, B, Hq, Hkv, N, D, scale, causal, valid_len, dtype, stream);
+                 lse, ws, ws_base_floats(B, Hq, N), B, Hq, Hkv, N, D, scale, causal, valid_len,
+                 dtype, stream);
 }
 
 extern "C" int attn_bwd_strided_validate(
@@ -980,7 +1132,8 @@ extern "C" int attn_bwd_strided_validate(
   return bwd_validate(bwd_layouts(q, q_strides, k, k_strides, v, v_strides, out, out_strides,
                                   dout, dout_strides, dq, dq_strides, dk, dk_strides, dv,
                                   dv_strides, Hq, Hkv, N, D),
-                      lse, ws, B, Hq, Hkv, N, D, scale, valid_len, dtype);
+                      lse, ws, ws_base_floats(B, Hq, N), B, Hq, Hkv, N, D, scale, valid_len,
+                      dtype);
 }
 
 extern "C" int attn_bwd_strided(
@@ -993,7 +1146,8 @@ extern "C" int attn_bwd_strided(
   return bwd_run(bwd_layouts(q, q_strides, k, k_strides, v, v_strides, out, out_strides, dout,
                              dout_strides, dq, dq_strides, dk, dk_strides, dv, dv_strides, Hq,
                              Hkv, N, D),
-                 lse, ws, B, Hq, Hkv, N, D, scale, causal, valid_len, dtype, stream);
+                 lse, ws, ws_base_floats(B, Hq, N), B, Hq, Hkv, N, D, scale, causal, valid_len,
+                 dtype, stream);
 }
 
 extern "C" int attn_bwd_masked_validate(
@@ -1008,8 +1162,8 @@ extern "C" int attn_bwd_masked_validate(
   return bwd_validate(bwd_layouts(q, q_strides, k, k_strides, v, v_strides, out, out_strides,
                                   dout, dout_strides, dq, dq_strides, dk, dk_strides, dv,
                                   dv_strides, Hq, Hkv, N, D),
-                      lse, ws, B, Hq, Hkv, N, D, scale, valid_len, dtype,
-                      mask_arg(mask, mask_type, mask_strides, N));
+                      lse, ws, ws_base_floats(B, Hq, N), B, Hq, Hkv, N, D, scale, valid_len,
+                      dtype, mask_arg(mask, mask_type, mask_strides, N));
 }
 
 extern "C" int attn_bwd_masked(
@@ -1023,6 +1177,42 @@ extern "C" int attn_bwd_masked(
   return bwd_run(bwd_layouts(q, q_strides, k, k_strides, v, v_strides, out, out_strides, dout,
                              dout_strides, dq, dq_strides, dk, dk_strides, dv, dv_strides, Hq,
                              Hkv, N, D),
-                 lse, ws, B, Hq, Hkv, N, D, scale, causal, valid_len, dtype, stream,
+                 lse, ws, ws_base_floats(B, Hq, N), B, Hq, Hkv, N, D, scale, causal, valid_len,
+                 dtype, stream, mask_arg(mask, mask_type, mask_strides, N));
+}
+
+extern "C" int64_t attn_bwd_workspace_floats(int B, int Hq, int Hkv, int N, int D) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || D < 1) return -1;
+  return ws_floats_for(B, Hq, Hkv, N, D, bwd_split(B, Hq, Hkv, N, D, INT64_MAX));
+}
+
+extern "C" int attn_bwd_ws_validate(
+    const void* q, const int64_t* q_strides, const void* k, const int64_t* k_strides,
+    const void* v, const int64_t* v_strides, const void* out, const int64_t* out_strides,
+    const void* dout, const int64_t* dout_strides, const float* lse, const void* dq,
+    const int64_t* dq_strides, const void* dk, const int64_t* dk_strides, const void* dv,
+    const int64_t* dv_strides, const float* ws, int64_t ws_floats, int B, int Hq, int Hkv,
+    int N, int D, float scale, int causal, const int32_t* valid_len, const void* mask,
+    int mask_type, const int64_t* mask_strides, int dtype) {
+  (void)causal;
+  return bwd_validate(bwd_layouts(q, q_strides, k, k_strides, v, v_strides, out, out_strides,
+                                  dout, dout_strides, dq, dq_strides, dk, dk_strides, dv,
+                                  dv_strides, Hq, Hkv, N, D),
+                      lse, ws, ws_floats, B, Hq, Hkv, N, D, scale, valid_len, dtype,
+                      mask_arg(mask, mask_type, mask_strides, N));
+}
+
+extern "C" int attn_bwd_ws(
+    const void* q, const int64_t* q_strides, const void* k, const int64_t* k_strides,
+    const void* v, const int64_t* v_strides, const void* out, const int64_t* out_strides,
+    const void* dout, const int64_t* dout_strides, const float* lse, void* dq,
+    const int64_t* dq_strides, void* dk, const int64_t* dk_strides, void* dv,
+    const int64_t* dv_strides, float* ws, int64_t ws_floats, int B, int Hq, int Hkv, int N,
+    int D, float scale, int causal, const int32_t* valid_len, const void* mask, int mask_type,
+    const int64_t* mask_strides, int dtype, void* stream) {
+  return bwd_run(bwd_layouts(q, q_strides, k, k_strides, v, v_strides, out, out_strides, dout,
+                             dout_strides, dq, dq_strides, dk, dk_strides, dv, dv_strides, Hq,
+                             Hkv, N, D),
+                 lse, ws, ws_floats, B, Hq, Hkv, N, D, scale, causal, valid_len, dtype, stream,
                  mask_arg(mask, mask_type, mask_strides, N));
 }

@@ -314,11 +314,13 @@ __device__ __forceinline__ void dkdv_f32_body(const F32BwdParams& p) {
 
   // (batch, KV head, 128-key tile): each XCD owns whole KV heads, in blocks of two, longest key
   // tiles first under causal masking (the 16-bit dK/dV kernel's order).
-  int kt, b, kvh;
+  int kt, b, kvh, sp;
   {
-    const int wid = blockIdx.x;
+    // consecutive workgroups of one XCD take the `split` parts of one key tile
     if (p.xcd_order) {
-      const int xcd = wid & 7, local = wid >> 3;
+      const int xcd = blockIdx.x & 7, local0 = blockIdx.x >> 3;
+      const int local = local0 / p.split;
+      sp = local0 - local * p.split;
       const int hpx = (p.B * p.Hkv) >> 3;
       const int blk = (hpx & 1) ? 1 : 2;
       const int pair = local / (blk * p.nkt);
@@ -329,6 +331,8 @@ __device__ __forceinline__ void dkdv_f32_body(const F32BwdParams& p) {
       b = kv_head / p.Hkv;
       kvh = kv_head - b * p.Hkv;
     } else {
+      const int wid = blockIdx.x / p.split;
+      sp = blockIdx.x - wid * p.split;
       const int BK = p.B * p.Hkv;
       kt = wid / BK;
       const int bk = wid - kt * BK;
@@ -348,7 +352,10 @@ __device__ __forceinline__ void dkdv_f32_body(const F32BwdParams& p) {
 
   const int qstart = CAUSAL ? k0 : 0;
   const int ntq = k0 < kv_end ? (p.N - qstart + kT - 1) / kT : 0;
-  const int iters = ntq * p.group;
+  // this workgroup's share [it0, it0 + iters) of the key tile's ntq * group iterations
+  const int total = ntq * p.group;
+  const int it0 = (int)((int64_t)total * sp / p.split);
+  const int iters = (int)((int64_t)total * (sp + 1) / p.split) - it0;
 
   if (iters > 0) {
     // K (times the scale's sign, 0 for scale 0) and V of this lane's key: B operands of S and dP.
@@ -408,7 +415,8 @@ __device__ __forceinline__ void dkdv_f32_body(const F32BwdParams& p) {
     Offsets<D> off;
     off.init(lane);
     const float c = p.c;
-    int g_cur = 0, q_cur = qstart, g_nxt = 0, q_nxt = qstart;
+    const int g0 = it0 / ntq, qs0 = qstart + (it0 - g0 * ntq) * kT;
+    int g_cur = g0, q_cur = qs0, g_nxt = g0, q_nxt = qs0;
     auto advance = [&](int& g, int& q0) {
       q0 += kT;
       if (q0 >= p.N) { q0 = qstart; ++g; }
@@ -480,8 +488,16 @@ __device__ __forceinline__ void dkdv_f32_body(const F32BwdParams& p) {
     wait_loads_and_lds();
   }
   if (key < p.N) {
-    store_row<D, DH>(dk, p.scale, p.dk + b * p.dks_b + kvh * p.dks_h + key * p.dks_n, h);
-    store_row<D, DH>(dv, 1.0f, p.dv + b * p.dvs_b + kvh * p.dvs_h + key * p.dvs_n, h);
+    if (p.split > 1) {
+      // fp32 partial sums of this part, added in part order by the reduction kernel
+      const size_t plane = (size_t)p.B * p.Hkv * p.N * DH;
+      float* pk = p.part + (size_t)sp * plane + (((size_t)b * p.Hkv + kvh) * p.N + key) * DH;
+      store_row<D, DH>(dk, p.scale, pk, h);
+      store_row<D, DH>(dv, 1.0f, pk + (size_t)p.split * plane, h);
+    } else {
+      store_row<D, DH>(dk, p.scale, p.dk + b * p.dks_b + kvh * p.dks_h + key * p.dks_n, h);
+      store_row<D, DH>(dv, 1.0f, p.dv + b * p.dvs_b + kvh * p.dvs_h + key * p.dvs_n, h);
+    }
   }
 }
 
@@ -508,7 +524,7 @@ void attn_bwd_f32_dkdv_kernel(F32BwdParams p) {
 template <int D, bool CAUSAL>
 hipError_t launch_d(const F32BwdParams& p, hipStream_t s) {
   const int64_t nq = (int64_t)p.B * p.Hq * p.nqt;
-  const int64_t nk = (int64_t)p.B * p.Hkv * p.nkt;
+  const int64_t nk = (int64_t)p.B * p.Hkv * p.nkt * p.split;
   hipLaunchKernelGGL((attn_bwd_f32_dq_kernel<D, CAUSAL>), dim3((unsigned)nq), dim3(kThreads), 0,
                      s, p);
   hipError_t e = hipGetLastError();

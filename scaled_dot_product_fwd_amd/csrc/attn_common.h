@@ -291,6 +291,8 @@ struct F32BwdParams {
   float c;           // |scale| * log2(e) (1 when scale == 0)
   float qmul;        // sign of scale, 0 when scale == 0: multiplies one operand of the scores
   float scale;       // the signed scale (dQ and dK carry it)
+  int split;         // parts per key tile of the dK/dV kernel (1: none; else fp32 partials)
+  float* part;       // [2][split][B][Hkv][N][D] partial sums (split > 1)
 };
 
 // Queue the fp32 backward (dQ kernel, then dK/dV kernel) for D in {16, 32, 64, 128}.

@@ -807,24 +807,3 @@ extern "C" int attn_fwd_masked(const void* q, const int64_t* q_strides, const vo
              Hkv, N, D, scale, causal, valid_len, dtype, stream,
              mask_arg(mask, mask_type, mask_strides, N));
 }
-
-extern "C" const char* attn_status_string(int status) {
-  switch (status) {
-    case ATTN_OK: return "ok";
-    case ATTN_ERR_NULL: return "a required pointer (q, k, v or out) is NULL";
-    case ATTN_ERR_SHAPE:
-      return "bad shape: B, Hq, Hkv and N must be >= 1, Hq a multiple of Hkv, within size limits";
-    case ATTN_ERR_HEAD_DIM: return "unsupported head dimension: D must be 64 or 128";
-    case ATTN_ERR_DTYPE: return "unsupported dtype: must be ATTN_F16 or ATTN_BF16";
-    case ATTN_ERR_SCALE: return "scale is not finite";
-    case ATTN_ERR_LAUNCH: return "the HIP runtime reported an error at kernel launch";
-    case ATTN_ERR_ALIAS: return "out or lse overlaps an input, or out overlaps lse";
-    case ATTN_ERR_MASK: return "unknown mask type";
-    case ATTN_ERR_LAYOUT:
-      return "bad layout: pointers must be 16-byte aligned, strides non-negative multiples of 8 "
-             "elements, rows at least D elements apart, and output rows distinct";
-    default: return "unknown status";
-  }
-}
-
-extern "C" int attn_version(void) { return 7; }

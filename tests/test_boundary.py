@@ -29,7 +29,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["attn_bwd", "attn_bwd_masked", "attn_bwd_masked_validate",
                                     "attn_bwd_strided", "attn_bwd_strided_validate",
-                                    "attn_bwd_validate", "attn_fwd",
+                                    "attn_bwd_validate", "attn_bwd_workspace_floats",
+                                    "attn_bwd_ws", "attn_bwd_ws_validate", "attn_fwd",
                                     "attn_fwd_masked", "attn_fwd_masked_validate",
                                     "attn_fwd_strided", "attn_fwd_strided_validate",
                                     "attn_fwd_validate", "attn_status_string", "attn_version"]
@@ -45,7 +46,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_version(lib):
-    assert sdp.attn_version() == 7
+    assert sdp.attn_version() == 8
 
 
 def test_status_strings(lib):
@@ -383,3 +384,48 @@ def test_bwd_masked_validate(lib):
     assert bmcall(ms=(0, 0, 1 << 21)) == sdp.ATTN_ERR_SHAPE             # rows past 32-bit reach
     assert bmcall(dq=MK + 1024) == sdp.ATTN_ERR_ALIAS                   # dq overlaps the mask
     assert bmcall(ws=MK - 1024) == sdp.ATTN_ERR_ALIAS                   # workspace overlaps it
+
+
+# ---- attn_bwd_ws_validate and attn_bwd_workspace_floats
+def wcall(**kw):
+    a = dict(ws=DL, n=None, B=2, Hq=8, Hkv=2, N=1000, D=128, dq=DQ, dtype=sdp.ATTN_BF16,
+             mask=None, mtype=sdp.ATTN_MASK_NONE)
+    a.update(kw)
+    n = a["n"] if a["n"] is not None else 2 * a["B"] * a["Hq"] * a["N"]
+    return sdp.attn_bwd_ws_validate(Q, None, K, None, V, None, O, None, DO, None, L, a["dq"], None,
+                                    DK, None, DV, None, a["ws"], n, a["B"], a["Hq"], a["Hkv"],
+                                    a["N"], a["D"], 0.088, 1, VL, a["mask"], a["mtype"], None,
+                                    a["dtype"])
+
+
+def test_bwd_workspace_floats(lib):
+    # enough key tiles: no split, the minimal workspace
+    assert sdp.attn_bwd_workspace_floats(8, 32, 8, 4096, 128) == 2 * 8 * 32 * 4096
+    # MQA with a long group: 128 key tiles split 8 ways
+    assert sdp.attn_bwd_workspace_floats(1, 32, 1, 16384, 128) == (
+        2 * 32 * 16384 + 4 + 2 * 8 * 16384 * 128)
+    # short groups do not pay for partial sums
+    assert sdp.attn_bwd_workspace_floats(2, 8, 8, 1024, 64) == 2 * 2 * 8 * 1024
+    assert sdp.attn_bwd_workspace_floats(0, 8, 8, 1024, 64) == -1
+
+
+def test_bwd_ws_validate(lib):
+    base = 2 * 2 * 8 * 1000
+    big = sdp.attn_bwd_workspace_floats(2, 8, 2, 1000, 128)
+    assert big > base
+    assert wcall() == sdp.ATTN_OK
+    assert wcall(n=big) == sdp.ATTN_OK
+    assert wcall(n=base - 1) == sdp.ATTN_ERR_WORKSPACE
+    assert wcall(n=0) == sdp.ATTN_ERR_WORKSPACE
+    assert wcall(dtype=sdp.ATTN_F32, n=big) == sdp.ATTN_OK
+    assert wcall(dtype=sdp.ATTN_F32, mask=MK, mtype=sdp.ATTN_MASK_KEEP_U8) == sdp.ATTN_ERR_DTYPE
+    assert wcall(mask=MK, mtype=sdp.ATTN_MASK_KEEP_U8, N=MN) == sdp.ATTN_OK
+    assert wcall(mtype=7, mask=MK) == sdp.ATTN_ERR_MASK
+    # dq right after the minimal workspace: fine when only that is used, an overlap with the
+    # partial sums once the workspace is large enough to split
+    after = DL + 4 * base
+    assert wcall(dq=after) == sdp.ATTN_OK
+    assert wcall(dq=after, n=big) == sdp.ATTN_ERR_ALIAS
+    # exactly the split's size uses the partial sums; one float less drops the split
+    assert wcall(dq=after, n=base + 4 + 2 * 2 * 2 * 2 * 1000 * 128) == sdp.ATTN_ERR_ALIAS
+    assert wcall(dq=after, n=base + 4 + 2 * 2 * 2 * 2 * 1000 * 128 - 1) == sdp.ATTN_OK

@@ -30,7 +30,10 @@ GRAD_FLOOR = {"bf16": 1e-3, "f16": 1e-3, "f32": 1e-1}
 DELTA_TOL = {"bf16": 2e-2, "f16": 5e-3, "f32": 1e-4}
 
 
-def run_bwd(case, dout_bits, dout_scale=1.0):
+def run_bwd(case, dout_bits, dout_scale=1.0, split_ws=False):
+    """Forward, then backward through backward(); split_ws passes the workspace size of
+    attn_bwd_workspace_floats (attn_bwd_ws, the dK/dV split where the shape wants one) instead
+    of the minimal 2 * B * Hq * N values (attn_bwd)."""
     import torch
     q = to_device(case.q_bits, case.dtype)
     k = to_device(case.k_bits, case.dtype)
@@ -40,12 +43,16 @@ def run_bwd(case, dout_bits, dout_scale=1.0):
     if case.valid_len is not None:
         vl = torch.from_numpy(case.valid_len.astype(np.int32)).cuda()
     out, lse = sdp.forward(q, k, v, causal=case.causal, valid_len=vl, scale=case.scale)
-    ws = torch.empty((2,) + tuple(lse.shape), dtype=torch.float32, device=q.device)
+    base = 2 * lse.numel()
+    n_ws = sdp.attn_bwd_workspace_floats(case.B, case.Hq, case.Hkv, case.N, case.D) \
+        if split_ws else base
+    ws = torch.empty((n_ws,), dtype=torch.float32, device=q.device)
     dq, dk, dv = sdp.backward(q, k, v, out, do, lse, causal=case.causal, valid_len=vl,
                               scale=case.scale, ws=ws)
     torch.cuda.synchronize()
     L = lse.cpu().numpy()
     # the workspace's second row is the device's LSE in base 2 (0 on empty rows)
+    ws = ws[:base].view((2,) + tuple(lse.shape))
     l2 = ws[1].cpu().numpy()
     want = np.where(np.isneginf(L), np.float32(0), L * np.float32(1.4426950408889634))
     assert np.allclose(l2, want, rtol=1e-6, atol=0), "workspace LSE row"
@@ -81,8 +88,8 @@ def check_grad(name, got, ref, dtype, tag, zero=None):
     return rel
 
 
-def compare_case(case, dout_bits, tag):
-    dq, dk, dv, delta, O, L = run_bwd(case, dout_bits)
+def compare_case(case, dout_bits, tag, split_ws=False):
+    dq, dk, dv, delta, O, L = run_bwd(case, dout_bits, split_ws=split_ws)
     q, k, v = case.widened()
     do = inputs.widen(dout_bits, case.dtype)
     rq, rk, rv = oracle.attn_bwd(q, k, v, do, case.scale, case.causal, case.valid_len)
@@ -257,6 +264,80 @@ def test_bwd_on_side_stream(dtype):
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
         compare_case(case, dout, "side stream %s" % dtype)
+
+
+# ---- the dK/dV split of attn_bwd_ws: key tiles whose (query head, query tile) iterations are
+# shared by several workgroups, partial sums added in a fixed order. Shapes with few key tiles
+# and long groups (MQA), where attn_bwd_workspace_floats asks for a split of 2 to 16.
+BWD_SPLIT = [
+    # (dtype, D, causal, padded, B, Hq, Hkv, N)
+    ("bf16", 64, True, False, 1, 8, 1, 1024),
+    ("f16", 128, False, True, 2, 16, 2, 700),
+    ("bf16", 128, True, False, 1, 32, 1, 2048),
+    ("f16", 32, True, False, 1, 16, 1, 1500),
+    ("f32", 64, True, False, 1, 8, 1, 1024),
+    ("f32", 128, False, True, 2, 16, 2, 700),
+]
+
+
+def split_of(case):
+    f = sdp.attn_bwd_workspace_floats(case.B, case.Hq, case.Hkv, case.N, case.D)
+    base = 2 * case.B * case.Hq * case.N
+    return 1 if f == base else (f - base - 4) // (2 * case.B * case.Hkv * case.N * case.D)
+
+
+@pytest.mark.parametrize("cfg", BWD_SPLIT, ids=lambda c: "%s-D%d-c%d-p%d-B%d-H%d-%d-N%d" % c)
+def test_bwd_split_parts(cfg):
+    dtype, D, causal, padded, B, Hq, Hkv, N = cfg
+    case = inputs.make_case(B, Hq, Hkv, N, D, dtype, causal, padded, seed=[237, D, N, B])
+    dout = inputs.make_grad(case, [237, D, N, B])
+    S = split_of(case)
+    assert S > 1, "shape %s does not split" % (cfg,)
+    log("bwd split case %s (%d parts) valid_len %s" % (cfg, S, case.valid_len))
+    compare_case(case, dout, "%s split %d" % (cfg, S), split_ws=True)
+
+
+def test_bwd_split_deterministic_and_close_to_unsplit():
+    """The split path is deterministic too, and agrees with the unsplit kernels to rounding."""
+    case = inputs.make_case(1, 16, 1, 1500, 128, "bf16", True, False, seed=239)
+    dout = inputs.make_grad(case, 239)
+    assert split_of(case) > 1
+    a = run_bwd(case, dout, split_ws=True)
+    b = run_bwd(case, dout, split_ws=True)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    c = run_bwd(case, dout)
+    for name, x, y in zip(("dQ", "dK", "dV"), a[:3], c[:3]):
+        rel = np.abs(x - y).max() / max(np.abs(y).max(), GRAD_FLOOR["bf16"])
+        log("split vs unsplit %s: %.2e" % (name, rel))
+        assert rel <= BWD_TOL["bf16"]
+    assert np.array_equal(a[0], c[0])   # dQ does not depend on the split
+
+
+def test_bwd_split_masked_and_strided():
+    """attn_bwd_ws with an explicit mask and [B, N, H, D] tensors, split 4."""
+    import torch
+    from gpu_util import device_mask, mask_values
+    case = inputs.make_case(1, 8, 1, 1024, 64, "bf16", True, False, seed=241)
+    assert split_of(case) > 1
+    dout_bits = inputs.make_grad(case, 241)
+    rng = np.random.default_rng(243)
+    mv = mask_values("add", "alibi", "bf16", 1, 8, 1024, rng)
+    dmask = device_mask("add", "alibi", "bf16", mv, 1024)
+    q, k, v, do = (to_device(x, "bf16").transpose(1, 2).contiguous()
+                   for x in (case.q_bits, case.k_bits, case.v_bits, dout_bits))
+    out, lse = sdp.forward(q, k, v, causal=True, scale=case.scale, layout="bnhd",
+                           attn_mask=dmask)
+    dq, dk, dv = sdp.backward(q, k, v, out, do, lse, causal=True, scale=case.scale,
+                              layout="bnhd", attn_mask=dmask)
+    torch.cuda.synchronize()
+    got = [from_device(t.transpose(1, 2), "bf16") for t in (dq, dk, dv)]
+    qw, kw, vw = case.widened()
+    ref = oracle.attn_bwd(qw, kw, vw, inputs.widen(dout_bits, "bf16"), case.scale, True, None,
+                          add_mask=inputs.widen(mv, "bf16"))
+    e = [check_grad(n, g, r, "bf16", "split masked bnhd") for n, g, r in
+         zip(("dQ", "dK", "dV"), got, ref)]
+    log("split masked bnhd: rel err dQ %.2e dK %.2e dV %.2e" % tuple(e))
 
 
 def test_bwd_rising_row_maximum():
