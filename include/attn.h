@@ -98,7 +98,7 @@ typedef enum {
  *   B, Hq, Hkv, N, D
  *              batch, query heads, key/value heads, sequence length (queries and keys share it),
  *              head dimension. Any N >= 1 is accepted; D must be 16, 32, 64, 128 or 256
- *              (attn_bwd: 16, 32, 64 or 128).
+ *              (attn_bwd: 16, 32, 64, 128, and 256 for 16-bit types).
  *   scale      multiplier of the dot products (typically 1/sqrt(D)); any finite value.
  *   causal     nonzero hides key j from query i when j > i.
  *   valid_len  device pointer to int32[B], or NULL for no padding mask. Keys j >= valid_len[b]

@@ -123,22 +123,33 @@ __device__ inline u32x4 pack8(const float (&x)[16], int s) {
   return Mfma<DT>::pack(v);
 }
 
+// Head-dimension parts: at D = 256 the backward's accumulators (dQ, or dK and dV) of a whole
+// row do not fit beside the operands, so each kernel runs twice, accumulating the columns
+// [128 p, 128 p + 128) of part p and recomputing S and dP; smaller head dims run one part.
+template <int D>
+struct Parts {
+  static constexpr int NP = D > 128 ? 2 : 1;    // parts
+  static constexpr int OT = Geo<D>::OT / NP;    // 32-column accumulator tiles per part
+};
+
 // Write a wave's 32 x D block, held transposed in acc (acc[u][4 r4 + e] is element
-// d = 32u + 8 r4 + 4h + e of row ql), as rows of `dst` (rows `rs` elements apart; DH <= D
-// elements each: the 16-byte chunks past DH are not written) through the wave's LDS staging
-// area `ost` (32 * ROW bytes). Rows at or past n are not written.
-template <int DT, int D, int DH = D>
-__device__ inline void store_rows(const f32x16 (&acc)[Geo<D>::OT], float mul,
+// d = 32 (U0 + u) + 8 r4 + 4h + e of row ql; U0 = PART * Parts<D>::OT), as rows of `dst` (rows
+// `rs` elements apart; DH <= D elements each: the 16-byte chunks past DH, and those of other
+// parts, are not written) through the wave's LDS staging area `ost` (32 * ROW bytes). Rows at
+// or past n are not written.
+template <int DT, int D, int DH = D, int PART = 0>
+__device__ inline void store_rows(const f32x16 (&acc)[Parts<D>::OT], float mul,
                                   unsigned char* ost, uint16_t* dst, int64_t rs, int row0, int n,
                                   int lane) {
   using G = Geo<D>;
   using M = Mfma<DT>;
+  constexpr int NT = Parts<D>::OT, U0 = PART * NT;
   const int h = lane >> 5, ql = lane & 31;
 #pragma unroll
-  for (int u = 0; u < G::OT; ++u)
+  for (int u = 0; u < NT; ++u)
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
-      const int c = 4 * u + r4;
+      const int c = 4 * (U0 + u) + r4;
       const uint32_t w0 = (uint32_t)M::round1(acc[u][4 * r4 + 0] * mul) |
                           ((uint32_t)M::round1(acc[u][4 * r4 + 1] * mul) << 16);
       const uint32_t w1 = (uint32_t)M::round1(acc[u][4 * r4 + 2] * mul) |
@@ -152,23 +163,29 @@ __device__ inline void store_rows(const f32x16 (&acc)[Geo<D>::OT], float mul,
     const int r = i * RPI + lane / G::CH;
     const int cc = lane % G::CH;
     const u32x4 v = *(const u32x4*)(ost + r * G::ROW + 16 * (cc ^ (r & (G::CH - 1))));
-    if (row0 + r < n && (DH == D || cc < DH / 8)) *(u32x4*)(dst + (row0 + r) * rs + 8 * cc) = v;
+    const bool mine = Parts<D>::NP == 1 || (cc >= 4 * U0 && cc < 4 * (U0 + NT));
+    if (row0 + r < n && mine && (DH == D || cc < DH / 8))
+      *(u32x4*)(dst + (row0 + r) * rs + 8 * cc) = v;
   }
 }
 
-// Write one row of a wave's transposed fp32 block (acc[u][4 r4 + e] is element 32u + 8 r4 +
-// 4h + e of the lane's row) times `mul` to `dst` (DH <= D elements; chunks past DH are skipped).
-template <int D, int DH>
-__device__ inline void store_part(const f32x16 (&acc)[Geo<D>::OT], float mul, float* dst, int h) {
+// Write one row of a wave's transposed fp32 block (acc[u][4 r4 + e] is element 32 (U0 + u) +
+// 8 r4 + 4h + e of the lane's row) times `mul` to `dst` (DH <= D elements; chunks past DH are
+// skipped).
+template <int D, int DH, int PART = 0>
+__device__ inline void store_part(const f32x16 (&acc)[Parts<D>::OT], float mul, float* dst,
+                                  int h) {
+  constexpr int U0 = PART * Parts<D>::OT;
 #pragma unroll
-  for (int u = 0; u < Geo<D>::OT; ++u)
+  for (int u = 0; u < Parts<D>::OT; ++u)
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
-      if (32 * u + 8 * r4 + 4 * h >= DH) continue;
+      const int d = 32 * (U0 + u) + 8 * r4 + 4 * h;
+      if (d >= DH) continue;
       f32x4 w;
 #pragma unroll
       for (int e = 0; e < 4; ++e) w[e] = acc[u][4 * r4 + e] * mul;
-      *(f32x4*)(dst + 32 * u + 8 * r4 + 4 * h) = w;
+      *(f32x4*)(dst + d) = w;
     }
 }
 
@@ -243,7 +260,7 @@ __device__ inline u32x4 tr_frag(const unsigned char* tile, uint32_t off, int row
 // ------------------------------------------------------------------------------------------
 // DH is the tensors' head dimension; DH < 64 runs the D = 64 geometry with the missing 16-byte
 // chunks of every row zero (out-of-range DMA lanes, zero registers) and never stored.
-template <int DT, int DH, bool CAUSAL, int MK>
+template <int DT, int DH, bool CAUSAL, int MK, int PART>
 __device__ __forceinline__ void bwd_dq_body(const BwdParams& p) {
   constexpr int D = DH < 64 ? 64 : DH;
   constexpr int DCH = DH / 8;
@@ -252,7 +269,8 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p) {
   constexpr int MOFF = G::LDS;   // per-wave mask slots follow the K/V tiles
   using M = Mfma<DT>;
   constexpr int KSTEPS = G::KSTEPS;
-  constexpr int OT = G::OT;
+  constexpr int OT = Parts<D>::OT;          // dQ^T tiles of this part
+  constexpr int U0 = PART * OT;             // its first
   // K0 K1 V0 V1, 64-key tiles. K is stored with bswz (read both as rows and transposed), V
   // with kswz (read as rows).
   __shared__ __attribute__((aligned(1024))) unsigned char smem[G::LDS + kWaves * MG::WB];
@@ -359,7 +377,7 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p) {
     vaddr[ks] = ql * G::ROW + 16 * ((2 * ks + h) ^ G::kswz(ql));
   }
 #pragma unroll
-  for (int u = 0; u < OT; ++u) taddr[u] = tr_offset<D>(lane, u);
+  for (int u = 0; u < OT; ++u) taddr[u] = tr_offset<D>(lane, U0 + u);
 
   if (ntiles > 0) {
     dma(0, G::K0, G::V0);
@@ -398,7 +416,7 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p) {
       }
     }
   const float delta = pair_sum(dsum);
-  if (h == 0 && qrow < p.N) {
+  if (PART == 0 && h == 0 && qrow < p.N) {
     p.delta[(size_t)bh * p.N + qrow] = delta;
     p.lse2[(size_t)bh * p.N + qrow] = L;
   }
@@ -494,8 +512,8 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p) {
   // dQ = scale * (dQ^T)^T, staged through LDS after every wave is done with the tiles.
   wait_loads_and_lds();
   __syncthreads();
-  store_rows<DT, D, DH>(acc, p.scale, smem + wave * 32 * G::ROW,
-                        p.dq + b * p.dqs_b + hq * p.dqs_h, p.dqs_n, qa, p.N, lane);
+  store_rows<DT, D, DH, PART>(acc, p.scale, smem + wave * 32 * G::ROW,
+                              p.dq + b * p.dqs_b + hq * p.dqs_h, p.dqs_n, qa, p.N, lane);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -528,7 +546,7 @@ struct KMaskGeo {
   static constexpr int RPL = 1024 / RB;                       // rows per DMA block
 };
 
-template <int DT, int DH, bool CAUSAL, int MK>
+template <int DT, int DH, bool CAUSAL, int MK, int PART>
 __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
   constexpr int D = DH < 64 ? 64 : DH;   // geometry (as in the dQ kernel)
   constexpr int DCH = DH / 8;
@@ -538,7 +556,8 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
   constexpr int MOFF = BG::LDS;   // per-wave mask slots follow the tiles and V rows
   using M = Mfma<DT>;
   constexpr int KSTEPS = G::KSTEPS;
-  constexpr int OT = G::OT;
+  constexpr int OT = Parts<D>::OT;          // dK^T / dV^T tiles of this part
+  constexpr int U0 = PART * OT;             // its first
   __shared__ __attribute__((aligned(1024))) unsigned char smem[BG::LDS + kWaves * KM::WB];
 
   const int tid = threadIdx.x;
@@ -676,7 +695,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) raddr[ks] = ql * G::ROW + 16 * ((2 * ks + h) ^ G::bswz(ql));
 #pragma unroll
-    for (int u = 0; u < OT; ++u) taddr[u] = tr_offset<D>(lane, u);
+    for (int u = 0; u < OT; ++u) taddr[u] = tr_offset<D>(lane, U0 + u);
     const float c = p.c;
 
     // Explicit mask: rows q0 .. q0+31 (query head g) x this wave's keys kw .. kw+31 into the
@@ -815,8 +834,8 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
     const size_t plane = (size_t)p.B * p.Hkv * p.N * DH;
     float* pk = p.part + (size_t)sp * plane + ((size_t)b * p.Hkv + kvh) * p.N * DH;
     if (key < p.N) {
-      store_part<D, DH>(dk, p.scale, pk + (size_t)key * DH, h);
-      store_part<D, DH>(dv, 1.0f, pk + (size_t)p.split * plane + (size_t)key * DH, h);
+      store_part<D, DH, PART>(dk, p.scale, pk + (size_t)key * DH, h);
+      store_part<D, DH, PART>(dv, 1.0f, pk + (size_t)p.split * plane + (size_t)key * DH, h);
     }
     return;
   }
@@ -824,38 +843,52 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
   // dK = scale * (dK^T)^T, dV = (dV^T)^T; rows past N are not written. Staging reuses the Q/dO
   // buffers (every wave is past its last read).
   unsigned char* ost = smem + wave * 32 * G::ROW;
-  store_rows<DT, D, DH>(dk, p.scale, ost, p.dk + b * p.dks_b + kvh * p.dks_h, p.dks_n, kw, p.N,
+  store_rows<DT, D, DH, PART>(dk, p.scale, ost, p.dk + b * p.dks_b + kvh * p.dks_h, p.dks_n, kw,
+                              p.N,
                         lane);
-  store_rows<DT, D, DH>(dv, 1.0f, ost, p.dv + b * p.dvs_b + kvh * p.dvs_h, p.dvs_n, kw, p.N,
+  store_rows<DT, D, DH, PART>(dv, 1.0f, ost, p.dv + b * p.dvs_b + kvh * p.dvs_h, p.dvs_n, kw,
+                              p.N,
                         lane);
 }
 
-template <int DT, int D, bool CAUSAL, int MK>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// D = 256 holds 128 KiB of tiles in LDS: one workgroup per CU, one wave per SIMD with the
+// whole register file.
+template <int DT, int D, bool CAUSAL, int MK, int PART>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(D > 128 ? 1 : 2, D > 128 ? 1 : 2)))
 void attn_bwd_dq_kernel(BwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  bwd_dq_body<DT, D, CAUSAL, MK>(p);
+  bwd_dq_body<DT, D, CAUSAL, MK, PART>(p);
 #endif
 }
 
-template <int DT, int D, bool CAUSAL, int MK>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int DT, int D, bool CAUSAL, int MK, int PART>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(D > 128 ? 1 : 2, D > 128 ? 1 : 2)))
 void attn_bwd_dkdv_kernel(BwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  bwd_dkdv_body<DT, D, CAUSAL, MK>(p);
+  bwd_dkdv_body<DT, D, CAUSAL, MK, PART>(p);
 #endif
 }
 
+// The dQ kernel's parts, then the dK/dV kernel's (it reads the workspace the first dQ part
+// writes).
 template <int DT, int D, bool CAUSAL, int MK>
 hipError_t launch_bwd(const BwdParams& p, hipStream_t s) {
   const int64_t nq = (int64_t)p.B * p.Hq * p.nqt;
   const int64_t nk = (int64_t)p.B * p.Hkv * p.nkt * p.split;
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<DT, D, CAUSAL, MK>), dim3((unsigned)nq),
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<DT, D, CAUSAL, MK, 0>), dim3((unsigned)nq),
                      dim3(kThreads), 0, s, p);
+  if constexpr (Parts<D>::NP > 1)
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<DT, D, CAUSAL, MK, 1>), dim3((unsigned)nq),
+                       dim3(kThreads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DT, D, CAUSAL, MK>), dim3((unsigned)nk),
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DT, D, CAUSAL, MK, 0>), dim3((unsigned)nk),
                      dim3(kThreads), 0, s, p);
+  if constexpr (Parts<D>::NP > 1)
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DT, D, CAUSAL, MK, 1>), dim3((unsigned)nk),
+                       dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
@@ -868,6 +901,8 @@ hipError_t dispatch_bwd_d(const BwdParams& p, int D, bool causal, hipStream_t s)
       return causal ? launch_bwd<DT, 32, true, MK>(p, s) : launch_bwd<DT, 32, false, MK>(p, s);
     case 64:
       return causal ? launch_bwd<DT, 64, true, MK>(p, s) : launch_bwd<DT, 64, false, MK>(p, s);
+    case 256:
+      return causal ? launch_bwd<DT, 256, true, MK>(p, s) : launch_bwd<DT, 256, false, MK>(p, s);
     default:
       return causal ? launch_bwd<DT, 128, true, MK>(p, s) : launch_bwd<DT, 128, false, MK>(p, s);
   }
@@ -935,7 +970,8 @@ int bwd_validate(const BwdLayouts& t, const float* lse, const float* ws, int64_t
   if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
   if (N > ATTN_MAX_N) return ATTN_ERR_SHAPE;
   if ((int64_t)B * Hq * (((int64_t)N + kBM - 1) / kBM) > ATTN_MAX_TILES) return ATTN_ERR_SHAPE;
-  if (D != 16 && D != 32 && D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
+  if (D != 16 && D != 32 && D != 64 && D != 128 && !(D == 256 && dtype != ATTN_F32))
+    return ATTN_ERR_HEAD_DIM;
   if (dtype != ATTN_F16 && dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_DTYPE;
   if (dtype == ATTN_F32 && mk.type != ATTN_MASK_NONE) return ATTN_ERR_DTYPE;
   if (!isfinite(scale)) return ATTN_ERR_SCALE;

@@ -259,6 +259,8 @@ def test_bwd_validate_accepts(lib):
     assert bcall(valid_len=None, D=64, dtype=sdp.ATTN_F16, causal=0, Hkv=8) == sdp.ATTN_OK
     assert bcall(D=16) == sdp.ATTN_OK
     assert bcall(D=32) == sdp.ATTN_OK
+    assert bcall(D=256) == sdp.ATTN_OK
+    assert bcall(D=256, dtype=sdp.ATTN_F16) == sdp.ATTN_OK
     for d in (16, 32, 64, 128):
         assert bcall(D=d, dtype=sdp.ATTN_F32) == sdp.ATTN_OK
 
@@ -268,7 +270,7 @@ def test_bwd_validate_accepts(lib):
     (dict(ws=None), sdp.ATTN_ERR_NULL),
     (dict(dout=None), sdp.ATTN_ERR_NULL),
     (dict(Hq=8, Hkv=3), sdp.ATTN_ERR_SHAPE),
-    (dict(D=256), sdp.ATTN_ERR_HEAD_DIM),
+    (dict(D=512), sdp.ATTN_ERR_HEAD_DIM),
     (dict(D=48), sdp.ATTN_ERR_HEAD_DIM),
     (dict(dtype=7), sdp.ATTN_ERR_DTYPE),
     (dict(dtype=sdp.ATTN_F32, D=256), sdp.ATTN_ERR_HEAD_DIM),

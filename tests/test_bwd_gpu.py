@@ -141,6 +141,11 @@ BWD_SMALL = [
     ("f32", 16, True, True, 3, 4, 2, 257),
     ("f32", 16, False, False, 1, 4, 4, 300),
     ("f32", 128, True, True, 2, 6, 3, 1),
+    # D = 256 (16-bit): two head-dimension parts per kernel
+    ("bf16", 256, True, False, 2, 8, 2, 333),
+    ("f16", 256, False, True, 2, 4, 2, 257),
+    ("bf16", 256, True, True, 3, 4, 1, 130),
+    ("f16", 256, True, False, 1, 2, 2, 1),
 ]
 
 
@@ -161,6 +166,7 @@ BWD_MANY = [
     ("bf16", 64, True, False, 2, 40, 8, 1000),
     ("f32", 128, True, True, 4, 16, 4, 1100),
     ("f32", 64, False, False, 3, 24, 3, 700),
+    ("bf16", 256, True, True, 4, 16, 4, 600),
 ]
 
 
@@ -277,6 +283,7 @@ BWD_SPLIT = [
     ("f16", 32, True, False, 1, 16, 1, 1500),
     ("f32", 64, True, False, 1, 8, 1, 1024),
     ("f32", 128, False, True, 2, 16, 2, 700),
+    ("bf16", 256, True, False, 1, 16, 1, 1024),
 ]
 
 
@@ -431,6 +438,7 @@ def test_autograd_f32_matches_entry_point():
 BWD_STRIDED = [
     ("bnhd", "bf16", 128, True, True, 2, 8, 2, 300),
     ("bnhd", "f32", 128, True, False, 2, 4, 2, 200),
+    ("bnhd", "bf16", 256, True, True, 2, 4, 2, 200),
     ("padded_rows", "f32", 64, False, True, 2, 4, 4, 130),
     ("bnhd", "f16", 64, False, False, 2, 4, 4, 200),
     ("padded_rows", "bf16", 64, True, False, 2, 6, 3, 257),
@@ -514,6 +522,8 @@ BWD_MASKED = [
     ("add", "window_neginf", "bf16", 128, False, False, 2, 4, 4, 300),
     ("keep", "random_bh", "f16", 32, True, False, 2, 4, 2, 200),
     ("add", "alibi", "bf16", 16, False, True, 2, 4, 1, 150),
+    ("keep", "random_bh", "bf16", 256, True, True, 2, 4, 2, 200),
+    ("add", "window_neginf", "f16", 256, False, False, 2, 2, 1, 150),
 ]
 
 
