@@ -237,9 +237,9 @@ int attn_fwd_masked_validate(const void *q, const int64_t *q_strides, const void
  *                the input type. ATTN_F32: fp32 tensors and fp32 products throughout.
  *   others       as in attn_fwd.
  *
- * Two kernels run on `stream` in order (dQ and Delta, then dK and dV). Outputs must not overlap
- * any input, each other or valid_len (ATTN_ERR_ALIAS); misaligned pointers are
- * ATTN_ERR_LAYOUT. Otherwise returns as attn_fwd.
+ * Kernels run on `stream` in order (dQ and Delta, then dK and dV; each in two head-dimension
+ * halves at D = 256). Outputs must not overlap any input, each other or valid_len
+ * (ATTN_ERR_ALIAS); misaligned pointers are ATTN_ERR_LAYOUT. Otherwise returns as attn_fwd.
  */
 int attn_bwd(const void *q, const void *k, const void *v, const void *out, const void *dout,
              const float *lse, void *dq, void *dk, void *dv, float *ws, int B, int Hq,
