@@ -338,10 +338,8 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p) {
 #pragma unroll
     for (int i = 0; i < G::LOADS; ++i) {
       const int blk = (wave * G::LOADS + i) * 1024;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(smem + kdst + blk), 16, kdma[i],
-                                               row0 * krow, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(smem + vdst + blk), 16, vdma[i],
-                                               row0 * vrow, 0, 0);
+      dma16<false>(krs, smem + kdst + blk, kdma[i], row0 * krow);
+      dma16<false>(vrs, smem + vdst + blk, vdma[i], row0 * vrow);
     }
   };
 
@@ -363,9 +361,8 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p) {
     if constexpr (MK != kMaskNone) {
 #pragma unroll
       for (int i = 0; i < MG::LOADS; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            mrs, (lds_void*)(smem + MOFF + wave * MG::WB + i * 1024), 16, moff,
-            (uint32_t)tile * MG::RB + (uint32_t)(i * MG::RPL) * mrow, 0, 0);
+        dma16<false>(mrs, smem + MOFF + wave * MG::WB + i * 1024, moff,
+              (uint32_t)tile * MG::RB + (uint32_t)(i * MG::RPL) * mrow);
     }
   };
 
@@ -640,8 +637,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
         const int vc = (lane % G::CH) ^ G::bswz(row);
         const uint32_t off =
             (DCH < G::CH && vc >= DCH) ? kNoChunk : (lane / G::CH) * vrow + vc * 16;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(vreg + i * 1024), 16, off,
-                                                 (uint32_t)(kw + i * G::RPB) * vrow, 0, 0);
+        dma16<false>(vrs, vreg + i * 1024, off, (uint32_t)(kw + i * G::RPB) * vrow);
       }
     }
     // DMA of the iteration over query head kvh * group + g, queries q0 .. q0+31, into buffer
@@ -672,10 +668,8 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
       for (int i = 0; i < BG::QLOADS; ++i) {
         const int blk = wave * BG::QLOADS + i;
         const uint32_t r0 = (uint32_t)(q0 + blk * G::RPB);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void*)(base + blk * 1024), 16,
-                                                 qoff[i], r0 * qrowb, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ors, (lds_void*)(base + BG::QTILE + blk * 1024),
-                                                 16, goff[i], r0 * growb, 0, 0);
+        dma16<false>(qrs, base + blk * 1024, qoff[i], r0 * qrowb);
+        dma16<false>(ors, base + BG::QTILE + blk * 1024, goff[i], r0 * growb);
       }
       if (wave < 2) {
         const float* src = wave == 0 ? p.lse2 : p.delta;
@@ -685,8 +679,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
         // row range when N % 4 != 0. Lanes 32..63 are out of range and write zeros to bytes
         // 128..255 of the wave's 1 KiB slot.
         const uint32_t loff = lane < kQT ? (uint32_t)(q0 + lane) * 4 : 0x7ffffff0u;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            lrs, (lds_void*)(base + 2 * BG::QTILE + wave * 1024), 4, loff, 0, 0, 0);
+        dma4<false>(lrs, base + 2 * BG::QTILE + wave * 1024, loff, 0);
       }
     };
 
@@ -713,9 +706,8 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
             (short)0, (p.N - 1) * mrow + ((p.N * KM::ES + 15) & ~15), kBufferFlags);
 #pragma unroll
         for (int i = 0; i < KM::LOADS; ++i)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              mrs, (lds_void*)(smem + MOFF + wave * KM::WB + i * 1024), 16, mlane,
-              (uint32_t)(q0 + i * KM::RPL) * mrow, 0, 0);
+          dma16<false>(mrs, smem + MOFF + wave * KM::WB + i * 1024, mlane,
+                (uint32_t)(q0 + i * KM::RPL) * mrow);
       }
     };
 

@@ -139,6 +139,43 @@ __device__ inline void wait_loads_and_lds() {
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
 }
 
+// Buffer loads into LDS (16 or 4 bytes per lane, to `lds` + lane * bytes), issued through inline
+// asm rather than the buffer-load-to-LDS builtin: the compiler cannot tell a later
+// ds_read_b64_tr_b16 apart from the DMA's destination and, for the builtin, waits for the whole
+// DMA before the first such read (measured: the forward's V reads stalled on every tile's
+// prefetch). Callers order the DMA themselves with an explicit vmcnt wait before reading the
+// destination (wait_loads_and_lds at the top of every loop step). M0 holds the LDS address; no
+// other code in these kernels uses M0.
+__device__ inline uint32_t lds_addr(const unsigned char* lds) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const unsigned char*)lds);
+}
+
+// ASM = false keeps the builtin where the wait costs nothing measurable: loops that compute for
+// long enough between a DMA and their first transposed read (the backward's S and dP products,
+// the unpipelined D = 256 forward), where the asm form only adds scalar registers (spills at
+// D = 256). One kernel uses one form only, since with the builtin the compiler assumes M0 keeps
+// the value it set.
+template <bool ASM = true>
+__device__ inline void dma16(__amdgpu_buffer_rsrc_t rs, unsigned char* lds, uint32_t voff,
+                             uint32_t soff) {
+  if constexpr (ASM)
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(lds_addr(lds)), "v"(voff), "s"(rs), "s"(soff) : "memory");
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds, 16, voff, soff, 0, 0);
+}
+
+template <bool ASM = true>
+__device__ inline void dma4(__amdgpu_buffer_rsrc_t rs, unsigned char* lds, uint32_t voff,
+                            uint32_t soff) {
+  if constexpr (ASM)
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                 :: "s"(lds_addr(lds)), "v"(voff), "s"(rs), "s"(soff) : "memory");
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds, 4, voff, soff, 0, 0);
+}
+
 // Per-wave, per-thread state of the main loop (registers).
 template <int D>
 struct Frag {

@@ -226,13 +226,10 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
 #pragma unroll
     for (int i = 0; i < G::LOADS; ++i) {
       const int blk = (wave * G::LOADS + i) * 1024;
-      if (kdst >= 0)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(smem + kdst + blk), 16,
-                                                 koff[i], row0 * krow, 0, 0);
+      if (kdst >= 0) dma16<(D <= 128)>(krs, smem + kdst + blk, koff[i], row0 * krow);
       if (vdst >= 0)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(smem + vdst + blk), 16,
-                                                 voff[VSHARED ? 0 : i],
-                                                 (row0 + (VSHARED ? i * G::RPB : 0)) * vrow, 0, 0);
+        dma16<(D <= 128)>(vrs, smem + vdst + blk, voff[VSHARED ? 0 : i],
+              (row0 + (VSHARED ? i * G::RPB : 0)) * vrow);
     }
   };
 
@@ -254,9 +251,8 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
     if constexpr (MK != kMaskNone) {
 #pragma unroll
       for (int i = 0; i < MG::LOADS; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            mrs, (lds_void*)(smem + MOFF + wave * MG::WB + i * 1024), 16, moff,
-            (uint32_t)tile * MG::RB + (uint32_t)(i * MG::RPL) * mrow, 0, 0);
+        dma16<(D <= 128)>(mrs, smem + MOFF + wave * MG::WB + i * 1024, moff,
+              (uint32_t)tile * MG::RB + (uint32_t)(i * MG::RPL) * mrow);
     }
   };
 
