@@ -556,8 +556,11 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
   const float lt = pair_sum(l);
   const bool empty = !(lt > 0.f);
   const float inv = empty ? 0.f : 1.0f / lt;
+  // D <= 128: the staging rows lie in the K buffers, which the last step does not read and
+  // which every wave finished reading before that step's barrier; larger head dims read K in
+  // their last step and wait for every wave here.
   wait_loads_and_lds();
-  __syncthreads();   // every wave is done reading K/V from LDS
+  if constexpr (D > 128) __syncthreads();
   unsigned char* ost = smem + wave * 32 * G::ROW;
 #pragma unroll
   for (int u = 0; u < OT; ++u)
