@@ -79,10 +79,12 @@ typedef enum {
 } attn_mask_t;
 
 /* Size limits checked by attn_fwd_validate: N <= ATTN_MAX_N and
- * B * Hq * ceil(N / 128) <= ATTN_MAX_TILES; with strides, also ((N + 64) * (K or V row stride)
- * + D) * (element size) < 2^31 (the bytes the kernel may address inside one K or V head). */
+ * B * Hq * ceil(N / 128) <= ATTN_MAX_TILES (one workgroup of 256 work-items per 128-row tile,
+ * and one launch holds fewer than 2^32 work-items); with strides, also ((N + 64) * (K or V row
+ * stride) + D) * (element size) < 2^31 (the bytes the kernel may address inside one K or V
+ * head). */
 #define ATTN_MAX_N (1 << 22)
-#define ATTN_MAX_TILES 2147483647LL
+#define ATTN_MAX_TILES 16777215LL
 
 /*
  * attn_fwd -- launch the attention forward described at the top of this file on `stream`.
@@ -357,9 +359,10 @@ int64_t attn_bwd_workspace_floats(int B, int Hq, int Hkv, int N, int D);
 /* attn_status_string -- a static, NUL-terminated description of a return code (never NULL). */
 const char *attn_status_string(int status);
 
-/* attn_version -- the library's interface version, currently 8 (2 added attn_fwd_strided, 3
+/* attn_version -- the library's interface version, currently 9 (2 added attn_fwd_strided, 3
  * attn_fwd_masked, 4 attn_bwd, 5 attn_bwd_strided, 6 attn_bwd_masked, 7 ATTN_F32 in attn_bwd
- * and attn_bwd_strided, 8 attn_bwd_ws and attn_bwd_workspace_floats). */
+ * and attn_bwd_strided, 8 attn_bwd_ws and attn_bwd_workspace_floats, 9 lowered ATTN_MAX_TILES
+ * to what one launch can hold). */
 int attn_version(void);
 
 #ifdef __cplusplus

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_version(lib):
-    assert sdp.attn_version() == 8
+    assert sdp.attn_version() == 9
 
 
 def test_status_strings(lib):
@@ -119,6 +119,25 @@ def test_validate_accepts_good_arguments(lib):
 ])
 def test_validate_rejects(lib, kw, code):
     assert call(**kw) == code
+
+
+def test_validate_size_limits(lib):
+    """The largest shapes: N = 2^22 fits while K/V heads stay within 2^31 bytes, and a launch
+    holds at most 2^24 - 1 workgroups of 128 query rows."""
+    one = dict(B=1, Hq=1, Hkv=1, N=1 << 22, valid_len=None)
+    assert call(D=128, **one) == sdp.ATTN_OK
+    assert call(D=64, dtype=sdp.ATTN_F32, **one) == sdp.ATTN_OK
+    assert call(D=256, **one) == sdp.ATTN_ERR_SHAPE          # a K head of 2 GiB
+    assert call(D=128, dtype=sdp.ATTN_F32, **one) == sdp.ATTN_ERR_SHAPE
+    # Pointers 1 TiB apart so that no span overlaps: 2^24 - 1 tiles pass, 2^24 do not.
+    T = 1 << 40
+    far = dict(q=T, k=2 * T, v=3 * T, out=4 * T, lse=5 * T, valid_len=6 * T, Hq=1, Hkv=1,
+               N=128, D=16)
+    assert call(B=(1 << 24) - 1, **far) == sdp.ATTN_OK
+    assert call(B=1 << 24, **far) == sdp.ATTN_ERR_SHAPE
+    assert call(B=1 << 16, **dict(far, Hq=256, Hkv=256)) == sdp.ATTN_ERR_SHAPE
+    assert call(B=1 << 10, **dict(far, Hq=128, Hkv=1, N=1 << 14)) == sdp.ATTN_ERR_SHAPE
+    assert call(B=1 << 10, **dict(far, Hq=128, Hkv=1, N=(1 << 14) - 128)) == sdp.ATTN_OK
 
 
 def test_validate_order_null_before_shape(lib):
@@ -263,6 +282,19 @@ def test_bwd_validate_accepts(lib):
     assert bcall(D=256, dtype=sdp.ATTN_F16) == sdp.ATTN_OK
     for d in (16, 32, 64, 128):
         assert bcall(D=d, dtype=sdp.ATTN_F32) == sdp.ATTN_OK
+
+
+def test_bwd_validate_size_limits(lib):
+    """As in the forward: at most 2^24 - 1 tiles of 128 rows per launch (pointers 1 TiB apart,
+    so that no span overlaps)."""
+    T = 1 << 40
+    far = dict(q=T, k=2 * T, v=3 * T, out=4 * T, dout=5 * T, lse=6 * T, dq=7 * T, dk=8 * T,
+               dv=9 * T, ws=10 * T, valid_len=11 * T, Hq=1, Hkv=1, N=128, D=16)
+    assert bcall(B=(1 << 24) - 1, **far) == sdp.ATTN_OK
+    assert bcall(B=1 << 24, **far) == sdp.ATTN_ERR_SHAPE
+    one = dict(B=1, Hq=1, Hkv=1, N=1 << 22, valid_len=None)
+    assert bcall(D=128, **one) == sdp.ATTN_OK
+    assert bcall(D=128, **dict(one, N=(1 << 22) + 1)) == sdp.ATTN_ERR_SHAPE
 
 
 @pytest.mark.parametrize("kw,code", [
