@@ -151,7 +151,7 @@ int oracle_attn_fwd_masked(const double *q, const double *k, const double *v, do
 #pragma omp atomic write
             bad = 1;
         }
-#pragma omp for schedule(dynamic, 16)
+#pragma omp for schedule(dynamic, 1)
         for (int64_t t = 0; t < nrows; ++t) {
             if (!scores)
                 continue;
