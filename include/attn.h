@@ -49,7 +49,7 @@ extern "C" {
 typedef enum {
     ATTN_F16 = 0,  /* IEEE binary16 */
     ATTN_BF16 = 1, /* bfloat16 */
-    ATTN_F32 = 2   /* IEEE binary32: every entry point except the masked ones */
+    ATTN_F32 = 2   /* IEEE binary32: every entry point except attn_bwd_masked with a mask */
 } attn_dtype_t;
 
 /* Return codes. Argument errors are detected on the host before anything is launched. */
@@ -180,7 +180,8 @@ int attn_fwd_strided_validate(const void *q, const int64_t *q_strides, const voi
  *   mask        device pointer, 16-byte aligned; element (b, hq, i, j) at
  *               mask + b*ms[0] + hq*ms[1] + i*ms[2] + j (elements of the mask type).
  *   mask_type   ATTN_MASK_KEEP_U8: key j is visible to query i only where the byte is nonzero.
- *               ATTN_MASK_ADD: the element (in the input dtype) is added to scale * q.k; values
+ *               ATTN_MASK_ADD: the element (in the input dtype: fp16, bf16, or fp32 with
+ *               ATTN_F32 inputs) is added to scale * q.k; values
  *               must be finite or -inf (a row whose visible keys all carry -inf, like an empty
  *               row, gives O = 0 and LSE = -inf; LSE includes the added values).
  *               ATTN_MASK_NONE: same as attn_fwd_strided.
@@ -286,8 +287,8 @@ int attn_bwd_strided_validate(const void *q, const int64_t *q_strides, const voi
 /*
  * attn_bwd_masked -- attn_bwd_strided plus the explicit mask of attn_fwd_masked (the same mask,
  * type and strides the forward was given; the article's §2.1-2.2 masks): the gradients of that
- * masked forward. The mask is a constant (no gradient). dtype ATTN_F16 or ATTN_BF16 only
- * (ATTN_F32 is ATTN_ERR_DTYPE, as in attn_fwd_masked). Returns as attn_bwd_strided; mask
+ * masked forward. The mask is a constant (no gradient). dtype ATTN_F16 or ATTN_BF16 with a mask
+ * (ATTN_F32 with a mask is ATTN_ERR_DTYPE). Returns as attn_bwd_strided; mask
  * errors as attn_fwd_masked (ATTN_ERR_MASK, ATTN_ERR_NULL, ATTN_ERR_LAYOUT, ATTN_ERR_SHAPE, and
  * ATTN_ERR_ALIAS when an output overlaps the mask).
  */
@@ -359,10 +360,10 @@ int64_t attn_bwd_workspace_floats(int B, int Hq, int Hkv, int N, int D);
 /* attn_status_string -- a static, NUL-terminated description of a return code (never NULL). */
 const char *attn_status_string(int status);
 
-/* attn_version -- the library's interface version, currently 9 (2 added attn_fwd_strided, 3
+/* attn_version -- the library's interface version, currently 10 (2 added attn_fwd_strided, 3
  * attn_fwd_masked, 4 attn_bwd, 5 attn_bwd_strided, 6 attn_bwd_masked, 7 ATTN_F32 in attn_bwd
  * and attn_bwd_strided, 8 attn_bwd_ws and attn_bwd_workspace_floats, 9 lowered ATTN_MAX_TILES
- * to what one launch can hold). */
+ * to what one launch can hold, 10 ATTN_F32 in attn_fwd_masked). */
 int attn_version(void);
 
 #ifdef __cplusplus

@@ -69,7 +69,7 @@ struct Geo {
 // Explicit [B, H, N, N] masks (template parameter MK of the kernel).
 constexpr int kMaskNone = 0;   // causal and valid_len only
 constexpr int kMaskKeep = 1;   // uint8: nonzero = the key is visible to the query
-constexpr int kMaskAdd = 2;    // 16-bit (the input type): added to the scaled score
+constexpr int kMaskAdd = 2;    // the input type (16-bit, or fp32): added to the scaled score
 
 // Each wave keeps the kBN-key slice of its 32 mask rows for the current tile in its own LDS
 // slot, fetched by DMA one tile ahead. Row r stores logical 16-byte chunk c at chunk
@@ -255,11 +255,16 @@ inline MaskArg mask_arg(const void* mask, int mask_type, const int64_t* st, int 
   return MaskArg{mask, mask_type, (int64_t)N * N, 0, N};
 }
 
+// Bytes per mask element: keep masks are uint8, additive masks have the inputs' type.
+inline int64_t mask_es(int type, int dtype) {
+  return type == ATTN_MASK_KEEP_U8 ? 1 : (dtype == ATTN_F32 ? 4 : 2);
+}
+
 // Type, pointer, layout and size checks of a mask (not its aliasing).
-inline int mask_status(const MaskArg& mk, int N) {
+inline int mask_status(const MaskArg& mk, int N, int dtype = ATTN_BF16) {
   if (mk.type != ATTN_MASK_KEEP_U8 && mk.type != ATTN_MASK_ADD) return ATTN_ERR_MASK;
   if (!mk.ptr) return ATTN_ERR_NULL;
-  const int64_t es = mk.type == ATTN_MASK_KEEP_U8 ? 1 : 2;
+  const int64_t es = mask_es(mk.type, dtype);
   if ((uintptr_t)mk.ptr % 16 != 0 || mk.sb < 0 || mk.sh < 0 || mk.sn < N ||
       (mk.sb * es) % 16 || (mk.sh * es) % 16 || (mk.sn * es) % 16)
     return ATTN_ERR_LAYOUT;
@@ -270,8 +275,8 @@ inline int mask_status(const MaskArg& mk, int N) {
 
 // Bytes a mask's reads may touch: rows are read in 16-byte units, the last row up to its next
 // 16-byte boundary.
-inline int64_t mask_span(const MaskArg& mk, int B, int Hq, int N) {
-  const int64_t es = mk.type == ATTN_MASK_KEEP_U8 ? 1 : 2;
+inline int64_t mask_span(const MaskArg& mk, int B, int Hq, int N, int dtype = ATTN_BF16) {
+  const int64_t es = mask_es(mk.type, dtype);
   return ((B - 1) * mk.sb + (Hq - 1) * mk.sh + (int64_t)(N - 1) * mk.sn) * es +
          ((N * es + 15) & ~15);
 }
@@ -294,10 +299,14 @@ struct F32Params {
   int64_t os_b, os_h, os_n;
   float c;           // |scale| * log2(e) (1 when scale == 0)
   float qmul;        // sign of scale, 0 when scale == 0: multiplies Q (exact)
+  const void* mask;  // explicit mask: uint8 keep or fp32 additive (attn_fwd_masked)
+  int64_t ms_b, ms_h, ms_n;   // its element strides (batch, query head, query row)
+  float mscale;      // log2(e) / c: an additive mask value in raw score units
 };
 
-// Queue the fp32 forward for D in {16, 32, 64, 128, 256}.
-hipError_t launch_fwd_f32(const F32Params& p, int D, bool causal, hipStream_t stream);
+// Queue the fp32 forward for D in {16, 32, 64, 128, 256} and mask_type an attn_mask_t.
+hipError_t launch_fwd_f32(const F32Params& p, int D, bool causal, int mask_type,
+                          hipStream_t stream);
 
 // fp32 backward (attn_bwd_f32.hip): validated arguments, strides in elements.
 struct F32BwdParams {

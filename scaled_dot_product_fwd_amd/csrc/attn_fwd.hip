@@ -641,7 +641,6 @@ int validate(const Layout& q, const Layout& k, const Layout& v, const Layout& o,
   const int64_t ntiles = (int64_t)B * Hq * (((int64_t)N + kBM - 1) / kBM);
   if (ntiles > ATTN_MAX_TILES) return ATTN_ERR_SHAPE;
   if (dtype != ATTN_F16 && dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_DTYPE;
-  if (dtype == ATTN_F32 && mk.type != ATTN_MASK_NONE) return ATTN_ERR_DTYPE;
   if (D != 16 && D != 32 && D != 64 && D != 128 && D != 256) return ATTN_ERR_HEAD_DIM;
   if (!isfinite(scale)) return ATTN_ERR_SCALE;
   const int es = dtype == ATTN_F32 ? 4 : 2;
@@ -665,9 +664,9 @@ int validate(const Layout& q, const Layout& k, const Layout& v, const Layout& o,
                     (lse && overlaps(valid_len, (int64_t)B * 4, lse, lbytes))))
     return ATTN_ERR_ALIAS;
   if (mk.type != ATTN_MASK_NONE) {
-    const int ms = mask_status(mk, N);
+    const int ms = mask_status(mk, N, dtype);
     if (ms != ATTN_OK) return ms;
-    const int64_t mbytes = mask_span(mk, B, Hq, N);
+    const int64_t mbytes = mask_span(mk, B, Hq, N, dtype);
     if (overlaps(o.ptr, obytes, mk.ptr, mbytes) || (lse && overlaps(lse, lbytes, mk.ptr, mbytes)))
       return ATTN_ERR_ALIAS;
   }
@@ -700,7 +699,10 @@ int run(const Layout& q, const Layout& k, const Layout& v, const Layout& o, floa
     f.os_b = o.sb; f.os_h = o.sh; f.os_n = o.sn;
     f.c = scale == 0.f ? 1.0f : fabsf(scale) * kLog2e;
     f.qmul = scale < 0.f ? -1.0f : (scale == 0.f ? 0.0f : 1.0f);
-    const hipError_t e = launch_fwd_f32(f, D, causal != 0, (hipStream_t)stream);
+    f.mask = mk.ptr;
+    f.ms_b = mk.sb; f.ms_h = mk.sh; f.ms_n = mk.sn;
+    f.mscale = kLog2e / f.c;
+    const hipError_t e = launch_fwd_f32(f, D, causal != 0, mk.type, (hipStream_t)stream);
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
   }
   Params p;

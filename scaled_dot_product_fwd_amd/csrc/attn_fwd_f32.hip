@@ -58,7 +58,8 @@ __device__ inline f32x16 mfma_f32(float a, float b, const f32x16& c) {
 
 // DH is the tensors' head dimension; DH = 16 runs the D = 32 geometry with the missing 16-byte
 // chunks of every row zero-filled (their DMA lanes fetch out of range) and never stored.
-template <int DH, bool CAUSAL>
+// MK: kMaskNone, or an explicit uint8 keep / fp32 additive mask (attn_fwd_masked).
+template <int DH, bool CAUSAL, int MK>
 __device__ __forceinline__ void fwd_f32_body(const F32Params& p) {
   constexpr int D = DH < 32 ? 32 : DH;   // geometry
   constexpr int DCH = DH / 4;            // 16-byte chunks of a row that exist
@@ -156,6 +157,38 @@ __device__ __forceinline__ void fwd_f32_body(const F32Params& p) {
     return key * G::ROW + 16 * ((8 * u + (ql >> 2)) ^ G::vswz(key)) + 4 * (ql & 3);
   };
 
+  // Explicit mask: the lane reads its query's row of the (batch, query head) plane (rows past N
+  // read row N - 1, never stored) as a range-checked buffer that ends at the last row's 16-byte
+  // boundary (a dword or 16-byte load that crosses the end reads as 0, which would hide keys
+  // below N), for the keys of its score registers:
+  // kb0 + 8g + 4h + e is byte e of word g (keep) or word 4g + e (additive). A tile's words are
+  // loaded at the top of its step, before the next tile's DMA, so that their wait (after the
+  // score MFMAs) leaves that DMA in flight.
+  constexpr int MES = MK == kMaskKeep ? 1 : 4;        // bytes per mask element
+  constexpr int MW = MK == kMaskAdd ? 16 : 4;         // mask words per lane and tile
+  const __amdgpu_buffer_rsrc_t mrs = __builtin_amdgcn_make_buffer_rsrc(
+      MK != kMaskNone ? (void*)((const unsigned char*)p.mask + (b * p.ms_b + hq * p.ms_h) * MES)
+                      : (void*)p.q,
+      (short)0,
+      MK != kMaskNone ? (uint32_t)((int64_t)(p.N - 1) * p.ms_n * MES + ((p.N * MES + 15) & ~15))
+                      : 0u,
+      kBufferFlags);
+  const uint32_t moff =
+      MK != kMaskNone ? (uint32_t)(min(qrow, p.N - 1) * p.ms_n + 4 * h) * MES : 0u;
+  auto mask_load = [&](int tile, uint32_t (&w)[MW]) {
+    const uint32_t base = moff + (uint32_t)tile * kKT * MES;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      if constexpr (MK == kMaskKeep) {
+        w[g] = __builtin_amdgcn_raw_buffer_load_b32(mrs, base + 8 * g, 0, 0);
+      } else {
+        const auto x = __builtin_amdgcn_raw_buffer_load_b128(mrs, base + 32 * g, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[4 * g + e] = x[e];
+      }
+    }
+  };
+
   f32x16 acc[OT];
 #pragma unroll
   for (int u = 0; u < OT; ++u) acc[u] = f32x16{};
@@ -167,7 +200,17 @@ __device__ __forceinline__ void fwd_f32_body(const F32Params& p) {
     const int P = j & 1;
     wait_loads_and_lds();
     __syncthreads();
-    if (j + 1 < ntiles) dma(j + 1, P ? G::K0 : G::K1, P ? G::V0 : G::V1);
+    uint32_t mw[MW];
+    if constexpr (MK != kMaskNone) {
+      mask_load(j, mw);
+      // Issued after the mask words (the scheduler may not swap them) and on every step (the
+      // last one reloads its own tile into the idle buffer), so that the wait for the mask words
+      // counts the same loads on every step and leaves the DMA in flight.
+      __builtin_amdgcn_sched_barrier(0);
+      dma(min(j + 1, ntiles - 1), P ? G::K0 : G::K1, P ? G::V0 : G::V1);
+    } else if (j + 1 < ntiles) {
+      dma(j + 1, P ? G::K0 : G::K1, P ? G::V0 : G::V1);
+    }
     const unsigned char* kb = smem + (P ? G::K1 : G::K0);
     const unsigned char* vb = smem + (P ? G::V1 : G::V0);
     // scores of keys kb0 + 8(r/4) + 4h + r%4 for this lane's query
@@ -180,7 +223,24 @@ __device__ __forceinline__ void fwd_f32_body(const F32Params& p) {
     }
     const int kb0 = j * kKT;
     const bool full = (!CAUSAL || kb0 + kKT - 1 <= qa) && kb0 + kKT <= kv_end;
-    if (!full) {
+    if constexpr (MK != kMaskNone) {
+      // Every tile: the additive value is folded into the raw score first, then keys hidden by
+      // the mask, causality or valid_len become -inf (a non-finite value on a hidden key never
+      // reaches the softmax).
+      int lim = kv_end - 1 - kb0 - 4 * h;
+      if (CAUSAL) lim = min(lim, qrow - kb0 - 4 * h);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int g = r >> 2, e = r & 3;
+        bool vis = 8 * g + e <= lim;
+        float x = sc[r];
+        if constexpr (MK == kMaskKeep)
+          vis = vis && ((mw[g] >> (8 * e)) & 0xffu) != 0;
+        else
+          x = __builtin_fmaf(__uint_as_float(mw[r]), p.mscale, x);
+        sc[r] = vis ? x : -INFINITY;
+      }
+    } else if (!full) {
       int lim = kv_end - 1 - kb0 - 4 * h;
       if (CAUSAL) lim = min(lim, qrow - kb0 - 4 * h);
 #pragma unroll
@@ -214,6 +274,9 @@ __device__ __forceinline__ void fwd_f32_body(const F32Params& p) {
         acc[u] = mfma_f32(*(const float*)(vb + vaddr(s, u)), pr[s], acc[u]);
   }
 
+  // The last step's reload lands before the workgroup's LDS can be handed to another.
+  if constexpr (MK != kMaskNone) wait_loads_and_lds();
+
   // O = acc / l (0 for a row with no visible key); lane holds O[qrow][32u + 8 r4 + 4h .. +3].
   const float lt = pair_sum(l);
   const bool empty = !(lt > 0.f);
@@ -237,33 +300,40 @@ __device__ __forceinline__ void fwd_f32_body(const F32Params& p) {
 
 // D = 256 holds 128 KiB of tiles in LDS (one workgroup per CU): one wave per SIMD, with the
 // whole register file for its 128 Q and 128 accumulator registers.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int MK>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(D > 128 ? 1 : 2, D > 128 ? 1 : 2)))
 void attn_fwd_f32_kernel(F32Params p) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  fwd_f32_body<D, CAUSAL>(p);
+  fwd_f32_body<D, CAUSAL, MK>(p);
 #endif
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int MK>
 hipError_t launch_d(const F32Params& p, hipStream_t s) {
   const int64_t nwg = (int64_t)p.B * p.Hq * p.nqt;
-  hipLaunchKernelGGL((attn_fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)nwg), dim3(kThreads), 0, s,
-                     p);
+  hipLaunchKernelGGL((attn_fwd_f32_kernel<D, CAUSAL, MK>), dim3((unsigned)nwg), dim3(kThreads),
+                     0, s, p);
   return hipGetLastError();
+}
+
+template <int MK>
+hipError_t launch_m(const F32Params& p, int D, bool causal, hipStream_t s) {
+  switch (D) {
+    case 16: return causal ? launch_d<16, true, MK>(p, s) : launch_d<16, false, MK>(p, s);
+    case 32: return causal ? launch_d<32, true, MK>(p, s) : launch_d<32, false, MK>(p, s);
+    case 256: return causal ? launch_d<256, true, MK>(p, s) : launch_d<256, false, MK>(p, s);
+    case 64: return causal ? launch_d<64, true, MK>(p, s) : launch_d<64, false, MK>(p, s);
+    default: return causal ? launch_d<128, true, MK>(p, s) : launch_d<128, false, MK>(p, s);
+  }
 }
 
 }  // namespace
 
-hipError_t launch_fwd_f32(const F32Params& p, int D, bool causal, hipStream_t s) {
-  switch (D) {
-    case 16: return causal ? launch_d<16, true>(p, s) : launch_d<16, false>(p, s);
-    case 32: return causal ? launch_d<32, true>(p, s) : launch_d<32, false>(p, s);
-    case 256: return causal ? launch_d<256, true>(p, s) : launch_d<256, false>(p, s);
-    case 64: return causal ? launch_d<64, true>(p, s) : launch_d<64, false>(p, s);
-    default: return causal ? launch_d<128, true>(p, s) : launch_d<128, false>(p, s);
-  }
+hipError_t launch_fwd_f32(const F32Params& p, int D, bool causal, int mask_type, hipStream_t s) {
+  if (mask_type == ATTN_MASK_KEEP_U8) return launch_m<kMaskKeep>(p, D, causal, s);
+  if (mask_type == ATTN_MASK_ADD) return launch_m<kMaskAdd>(p, D, causal, s);
+  return launch_m<kMaskNone>(p, D, causal, s);
 }
 
 }  // namespace attn_detail

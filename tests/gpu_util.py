@@ -156,15 +156,17 @@ def mask_values(kind, pattern, dtype, B, Hq, N, rng):
 def device_mask(kind, pattern, dtype, mv, N):
     """The device view of mask values from mask_values: rows padded to 16 bytes (a
     [.., N, Npad] view, as the layout rules require); [B, N, N] when shared by the heads and
-    [N, N] (bool) for the shared window."""
+    [N, N] (bool) for the shared window. Additive masks have the inputs' type (fp32 for f32)."""
     import torch
-    es = 1 if kind == "keep" else 2
+    es = 1 if kind == "keep" else (4 if dtype == "f32" else 2)
     npad = -(-N * es // 16) * 16 // es
     host = np.zeros(mv.shape[:3] + (npad,), mv.dtype)
     host[..., :N] = mv
-    t = torch.from_numpy(host.view(np.int16) if kind == "add" else host).cuda()
     if kind == "add":
-        t = t.view(torch.bfloat16 if dtype == "bf16" else torch.float16)
+        host = host.view(np.int32 if dtype == "f32" else np.int16)
+    t = torch.from_numpy(host).cuda()
+    if kind == "add":
+        t = t.view({"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype])
     else:
         t = t.view(torch.bool) if pattern == "window" else t
     dmask = t[..., :N]

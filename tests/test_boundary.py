@@ -46,7 +46,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_version(lib):
-    assert sdp.attn_version() == 9
+    assert sdp.attn_version() == 10
 
 
 def test_status_strings(lib):
@@ -228,7 +228,26 @@ def mcall(**kw):
     N, B, Hq, Hkv = a["N"], a["B"], a["Hq"], a["Hkv"]
     return sdp.attn_fwd_masked_validate(Q, None, K, None, V, None, a.get("out", O), None,
                                         a.get("lse", L), B, Hq, Hkv, N, 128, 0.088, 1, VL,
-                                        a["mask"], a["mtype"], a["ms"], sdp.ATTN_BF16)
+                                        a["mask"], a["mtype"], a["ms"],
+                                        a.get("dtype", sdp.ATTN_BF16))
+
+
+def test_masked_validate_f32(lib):
+    """fp32 inputs take uint8 keep masks and fp32 additive masks (4-byte elements: rows 16-byte
+    aligned at 4 elements, twice the bytes of a 16-bit mask)."""
+    f32, add = sdp.ATTN_F32, sdp.ATTN_MASK_ADD
+    assert mcall(dtype=f32) == sdp.ATTN_OK
+    assert mcall(dtype=f32, mtype=add) == sdp.ATTN_OK
+    assert mcall(dtype=f32, mtype=add, ms=(SH * MN * MN, MN * MN, MN)) == sdp.ATTN_OK
+    padded = dict(mtype=add, ms=(MN * (MN + 4), 0, MN + 4))
+    assert mcall(**padded) == sdp.ATTN_ERR_LAYOUT                   # 2056-byte rows
+    assert mcall(dtype=f32, **padded) == sdp.ATTN_OK                # 4112-byte rows
+    far_rows = dict(mtype=add, ms=(0, 0, 1 << 19))
+    assert mcall(**far_rows) == sdp.ATTN_OK
+    assert mcall(dtype=f32, **far_rows) == sdp.ATTN_ERR_SHAPE      # rows past 2^31 bytes
+    after16 = dict(mtype=add, out=MK + SB * MN * MN * 2)            # just past a 16-bit mask
+    assert mcall(**after16) == sdp.ATTN_OK
+    assert mcall(dtype=f32, **after16) == sdp.ATTN_ERR_ALIAS
 
 
 def test_masked_validate_accepts(lib):
@@ -333,10 +352,10 @@ def test_f32_layouts(lib):
     qbytes16 = 2 * 8 * 1000 * 128 * 2
     assert call(out=Q + qbytes16) == sdp.ATTN_OK
     assert call(out=Q + qbytes16, dtype=f32) == sdp.ATTN_ERR_ALIAS
-    # explicit masks are 16-bit only
+    # the forward takes explicit masks with fp32 inputs too
     assert sdp.attn_fwd_masked_validate(Q, None, K, None, V, None, O, None, L, SB, SH, 2, MN, 128,
                                         0.088, 1, VL, MK, sdp.ATTN_MASK_KEEP_U8, None,
-                                        f32) == sdp.ATTN_ERR_DTYPE
+                                        f32) == sdp.ATTN_OK
 
 
 # ---- attn_bwd_strided_validate

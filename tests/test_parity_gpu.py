@@ -385,6 +385,18 @@ MASKED = [
     ("add", "alibi", "bf16", 32, False, False, 2, 4, 1, 300),
     ("keep", "window", "bf16", 256, True, False, 2, 4, 2, 300),
     ("add", "random_bh", "f16", 256, False, True, 2, 2, 1, 200),
+    # fp32 inputs: uint8 keep masks and fp32 additive masks
+    ("keep", "random_bh", "f32", 128, True, True, 2, 4, 2, 300),
+    ("keep", "window", "f32", 64, False, False, 2, 4, 4, 256),
+    ("keep", "empty_rows", "f32", 32, True, False, 1, 4, 2, 130),
+    ("keep", "random_b", "f32", 16, False, True, 3, 2, 1, 200),
+    ("add", "random_bh", "f32", 128, True, False, 2, 4, 2, 257),
+    ("add", "alibi", "f32", 64, True, True, 2, 8, 2, 512),
+    ("add", "window_neginf", "f32", 128, False, False, 2, 4, 4, 300),
+    ("add", "large_negative", "f32", 32, False, False, 1, 2, 2, 64),
+    ("add", "random_b", "f32", 16, True, True, 2, 4, 1, 100),
+    ("keep", "random_bh", "f32", 256, True, True, 2, 2, 1, 200),
+    ("add", "alibi", "f32", 256, False, False, 1, 4, 2, 300),
 ]
 
 
