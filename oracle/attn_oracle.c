@@ -143,6 +143,9 @@ int oracle_attn_fwd_masked(const double *q, const double *k, const double *v, do
         nrows = B * Hq * N;
     const int64_t group = Hq / Hkv;
     int bad = 0;
+    /* Rows go to threads in chunks of 16 consecutive ones; a short list of rows (a sample of a
+     * long sequence) one at a time, so that it still spreads over the threads. */
+    const int chunk = nrows >= 1024 ? 16 : 1;
 
 #pragma omp parallel num_threads(threads > 0 ? threads : omp_get_max_threads())
     {
@@ -151,7 +154,7 @@ int oracle_attn_fwd_masked(const double *q, const double *k, const double *v, do
 #pragma omp atomic write
             bad = 1;
         }
-#pragma omp for schedule(dynamic, 1)
+#pragma omp for schedule(dynamic, chunk)
         for (int64_t t = 0; t < nrows; ++t) {
             if (!scores)
                 continue;
