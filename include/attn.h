@@ -49,7 +49,7 @@ extern "C" {
 typedef enum {
     ATTN_F16 = 0,  /* IEEE binary16 */
     ATTN_BF16 = 1, /* bfloat16 */
-    ATTN_F32 = 2   /* IEEE binary32: every entry point except attn_bwd_masked with a mask */
+    ATTN_F32 = 2   /* IEEE binary32: every entry point */
 } attn_dtype_t;
 
 /* Return codes. Argument errors are detected on the host before anything is launched. */
@@ -287,8 +287,8 @@ int attn_bwd_strided_validate(const void *q, const int64_t *q_strides, const voi
 /*
  * attn_bwd_masked -- attn_bwd_strided plus the explicit mask of attn_fwd_masked (the same mask,
  * type and strides the forward was given; the article's §2.1-2.2 masks): the gradients of that
- * masked forward. The mask is a constant (no gradient). dtype ATTN_F16 or ATTN_BF16 with a mask
- * (ATTN_F32 with a mask is ATTN_ERR_DTYPE). Returns as attn_bwd_strided; mask
+ * masked forward. The mask is a constant (no gradient). Any dtype (with ATTN_F32 an additive
+ * mask is fp32, as in the forward). Returns as attn_bwd_strided; mask
  * errors as attn_fwd_masked (ATTN_ERR_MASK, ATTN_ERR_NULL, ATTN_ERR_LAYOUT, ATTN_ERR_SHAPE, and
  * ATTN_ERR_ALIAS when an output overlaps the mask).
  */
@@ -327,7 +327,7 @@ int attn_bwd_masked_validate(const void *q, const int64_t *q_strides, const void
  *                  the split, smaller sizes use a smaller split or none. On return ws holds
  *                  Delta and the base-2 LSE as in attn_bwd; the partial sums follow from the
  *                  next 16-byte boundary and are scratch.
- *   others         as in attn_bwd_masked (dtype ATTN_F32 only with ATTN_MASK_NONE).
+ *   others         as in attn_bwd_masked.
  */
 int attn_bwd_ws(const void *q, const int64_t *q_strides, const void *k,
                 const int64_t *k_strides, const void *v, const int64_t *v_strides,
@@ -360,10 +360,11 @@ int64_t attn_bwd_workspace_floats(int B, int Hq, int Hkv, int N, int D);
 /* attn_status_string -- a static, NUL-terminated description of a return code (never NULL). */
 const char *attn_status_string(int status);
 
-/* attn_version -- the library's interface version, currently 10 (2 added attn_fwd_strided, 3
+/* attn_version -- the library's interface version, currently 11 (2 added attn_fwd_strided, 3
  * attn_fwd_masked, 4 attn_bwd, 5 attn_bwd_strided, 6 attn_bwd_masked, 7 ATTN_F32 in attn_bwd
  * and attn_bwd_strided, 8 attn_bwd_ws and attn_bwd_workspace_floats, 9 lowered ATTN_MAX_TILES
- * to what one launch can hold, 10 ATTN_F32 in attn_fwd_masked). */
+ * to what one launch can hold, 10 ATTN_F32 in attn_fwd_masked, 11 ATTN_F32 with a mask in
+ * attn_bwd_masked and attn_bwd_ws). */
 int attn_version(void);
 
 #ifdef __cplusplus

@@ -965,7 +965,6 @@ int bwd_validate(const BwdLayouts& t, const float* lse, const float* ws, int64_t
   if (D != 16 && D != 32 && D != 64 && D != 128 && !(D == 256 && dtype != ATTN_F32))
     return ATTN_ERR_HEAD_DIM;
   if (dtype != ATTN_F16 && dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_DTYPE;
-  if (dtype == ATTN_F32 && mk.type != ATTN_MASK_NONE) return ATTN_ERR_DTYPE;
   if (!isfinite(scale)) return ATTN_ERR_SCALE;
   const int es = dtype == ATTN_F32 ? 4 : 2;   // bytes per element
   for (const Layout* l : all)
@@ -998,9 +997,9 @@ int bwd_validate(const BwdLayouts& t, const float* lse, const float* ws, int64_t
     if (valid_len && overlaps(outs[i], osz[i], valid_len, (int64_t)B * 4)) return ATTN_ERR_ALIAS;
   }
   if (mk.type != ATTN_MASK_NONE) {
-    const int ms = mask_status(mk, N);
+    const int ms = mask_status(mk, N, dtype);
     if (ms != ATTN_OK) return ms;
-    const int64_t mbytes = mask_span(mk, B, Hq, N);
+    const int64_t mbytes = mask_span(mk, B, Hq, N, dtype);
     for (int i = 0; i < 4; ++i)
       if (overlaps(outs[i], osz[i], mk.ptr, mbytes)) return ATTN_ERR_ALIAS;
   }
@@ -1076,7 +1075,10 @@ int bwd_run(const BwdLayouts& t, const float* lse, float* ws, int64_t ws_floats,
     f.scale = scale;
     f.split = split;
     f.part = part;
-    hipError_t e = launch_bwd_f32(f, D, causal != 0, hs);
+    f.mask = mk.ptr;
+    f.ms_b = mk.sb; f.ms_h = mk.sh; f.ms_n = mk.sn;
+    f.mscale = kLog2e / f.c;
+    hipError_t e = launch_bwd_f32(f, D, causal != 0, mk.type, hs);
     if (e == hipSuccess && split > 1) e = launch_reduce(t, part, B, Hkv, N, D, split, dtype, hs);
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
   }

@@ -134,10 +134,25 @@ __device__ inline void store_row(const f32x16 (&acc)[B32<D>::OT], float mul, flo
     }
 }
 
+// The forward's explicit mask (MK: kMaskKeep uint8, kMaskAdd fp32; kMaskNone for none): the
+// (batch, query head) plane as a range-checked buffer ending at its last row's 16-byte boundary
+// (a load that crosses a buffer's end reads as 0, which would hide keys below N).
+template <int MK>
+__device__ inline __amdgpu_buffer_rsrc_t mask_plane(const F32BwdParams& p, int b, int hq) {
+  constexpr int MES = MK == kMaskKeep ? 1 : 4;
+  return __builtin_amdgcn_make_buffer_rsrc(
+      MK != kMaskNone ? (void*)((const unsigned char*)p.mask + (b * p.ms_b + hq * p.ms_h) * MES)
+                      : (void*)p.q,
+      (short)0,
+      MK != kMaskNone ? (uint32_t)((int64_t)(p.N - 1) * p.ms_n * MES + ((p.N * MES + 15) & ~15))
+                      : 0u,
+      kBufferFlags);
+}
+
 // ------------------------------------------------------------------------------------------
 // dQ (and D, L2)
 // ------------------------------------------------------------------------------------------
-template <int DH, bool CAUSAL>
+template <int DH, bool CAUSAL, int MK>
 __device__ __forceinline__ void dq_f32_body(const F32BwdParams& p) {
   constexpr int D = DH < 32 ? 32 : DH;   // geometry; DH = 16 zero-fills half of every row
   constexpr int DCH = DH / 4;
@@ -244,12 +259,38 @@ __device__ __forceinline__ void dq_f32_body(const F32BwdParams& p) {
 #pragma unroll
   for (int u = 0; u < OT; ++u) acc[u] = f32x16{};
   const float c = p.c;
+  // Explicit mask: the words of this lane's query row for the keys of its score registers,
+  // kb0 + 8g + 4h + e = byte e of word g (keep) or word 4g + e (additive).
+  constexpr int MES = MK == kMaskKeep ? 1 : 4;
+  constexpr int MW = MK == kMaskAdd ? 16 : 4;
+  const __amdgpu_buffer_rsrc_t mrs = mask_plane<MK>(p, b, hq);
+  const uint32_t moff = MK != kMaskNone ? (uint32_t)(qr * p.ms_n + 4 * h) * MES : 0u;
 
   auto step = [&](auto bufc, int j) {
     constexpr int P = decltype(bufc)::value;
     wait_loads_and_lds();
     __syncthreads();
-    if (j + 1 < ntiles) dma(j + 1, P ? K0 : K1, P ? V0 : V1);
+    uint32_t mw[MW];
+    if constexpr (MK != kMaskNone) {
+      const uint32_t base = moff + (uint32_t)j * kT * MES;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        if constexpr (MK == kMaskKeep) {
+          mw[g] = __builtin_amdgcn_raw_buffer_load_b32(mrs, base + 8 * g, 0, 0);
+        } else {
+          const auto x = __builtin_amdgcn_raw_buffer_load_b128(mrs, base + 32 * g, 0, 0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) mw[4 * g + e] = x[e];
+        }
+      }
+      // The DMA goes out after the mask words (no reordering) and on every step (the last one
+      // reloads its own tile into the idle buffer), so that the wait for the words leaves it in
+      // flight.
+      __builtin_amdgcn_sched_barrier(0);
+      dma(min(j + 1, ntiles - 1), P ? K0 : K1, P ? V0 : V1);
+    } else if (j + 1 < ntiles) {
+      dma(j + 1, P ? K0 : K1, P ? V0 : V1);
+    }
     const unsigned char* kb = smem + (P ? K1 : K0);
     const unsigned char* vb = smem + (P ? V1 : V0);
     // S^T and dP^T: lane holds keys kb0 + 8(r/4) + 4h + r%4 of its query
@@ -269,10 +310,28 @@ __device__ __forceinline__ void dq_f32_body(const F32BwdParams& p) {
     const int kb0 = j * kT;
     const bool full = (!CAUSAL || kb0 + kT - 1 <= qa) && kb0 + kT <= kv_end;
     float ds[16];
+    if constexpr (MK != kMaskNone) {
+      // every tile: the additive value enters the score, hidden keys get dS = 0
+      int lim = kv_end - 1 - kb0 - 4 * h;
+      if (CAUSAL) lim = min(lim, qrow - kb0 - 4 * h);
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      ds[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], c, -L2)) * (dp[r] - delta);
-    if (!full) {
+      for (int r = 0; r < 16; ++r) {
+        const int g = r >> 2, e = r & 3;
+        bool vis = 8 * g + e <= lim;
+        float x = sc[r];
+        if constexpr (MK == kMaskKeep)
+          vis = vis && ((mw[g] >> (8 * e)) & 0xffu) != 0;
+        else
+          x = __builtin_fmaf(__uint_as_float(mw[r]), p.mscale, x);
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(x, c, -L2));
+        ds[r] = vis ? pv * (dp[r] - delta) : 0.f;
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        ds[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], c, -L2)) * (dp[r] - delta);
+    }
+    if (MK == kMaskNone && !full) {
       int lim = kv_end - 1 - kb0 - 4 * h;
       if (CAUSAL) lim = min(lim, qrow - kb0 - 4 * h);
 #pragma unroll
@@ -289,6 +348,8 @@ __device__ __forceinline__ void dq_f32_body(const F32BwdParams& p) {
     step(std::integral_constant<int, 0>{}, j);
     if (j + 1 < ntiles) step(std::integral_constant<int, 1>{}, j + 1);
   }
+  // the last step's reload lands before the workgroup's LDS can be handed to another
+  if constexpr (MK != kMaskNone) wait_loads_and_lds();
   if (qrow < p.N)
     store_row<D, DH>(acc, p.scale, p.dq + b * p.dqs_b + hq * p.dqs_h + qrow * p.dqs_n, h);
 }
@@ -296,7 +357,7 @@ __device__ __forceinline__ void dq_f32_body(const F32BwdParams& p) {
 // ------------------------------------------------------------------------------------------
 // dK, dV
 // ------------------------------------------------------------------------------------------
-template <int DH, bool CAUSAL>
+template <int DH, bool CAUSAL, int MK>
 __device__ __forceinline__ void dkdv_f32_body(const F32BwdParams& p) {
   constexpr int D = DH < 32 ? 32 : DH;
   constexpr int DCH = DH / 4;
@@ -424,15 +485,37 @@ __device__ __forceinline__ void dkdv_f32_body(const F32BwdParams& p) {
     dma(g_nxt, q_nxt, 0);
     advance(g_nxt, q_nxt);
 
+    // Explicit mask: element (query q0 + 8(r/4) + 4h + r%4, this lane's key) per score register.
+    constexpr int MES = MK == kMaskKeep ? 1 : 4;
+    const uint32_t mrowb = MK != kMaskNone ? (uint32_t)(p.ms_n * MES) : 0u;
+    const uint32_t mcol = (uint32_t)key * MES;   // keys past N are hidden below
     auto step = [&](auto bufc, int it) {
       constexpr int buf = decltype(bufc)::value;
       wait_loads_and_lds();
       __syncthreads();
-      if (it + 1 < iters) {
+      const int q0 = q_cur;
+      uint32_t mw[16];
+      if constexpr (MK != kMaskNone) {
+        const __amdgpu_buffer_rsrc_t mrs = mask_plane<MK>(p, b, kvh * p.group + g_cur);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t moff = (uint32_t)(q0 + 8 * (r >> 2) + 4 * h + (r & 3)) * mrowb + mcol;
+          if constexpr (MK == kMaskKeep)
+            mw[r] = __builtin_amdgcn_raw_buffer_load_b8(mrs, moff, 0, 0);
+          else
+            mw[r] = __builtin_amdgcn_raw_buffer_load_b32(mrs, moff, 0, 0);
+        }
+        // The DMA goes out after the mask words (no reordering) and on every step (the last one
+        // reloads its own tile into the idle buffer), so that the wait for the words leaves it
+        // in flight.
+        __builtin_amdgcn_sched_barrier(0);
+        const bool more = it + 1 < iters;   // one DMA call without a branch around it
+        dma(more ? g_nxt : g_cur, more ? q_nxt : q0, buf ^ 1);
+        if (more) advance(g_nxt, q_nxt);
+      } else if (it + 1 < iters) {
         dma(g_nxt, q_nxt, buf ^ 1);
         advance(g_nxt, q_nxt);
       }
-      const int q0 = q_cur;
       advance(g_cur, q_cur);
       const unsigned char* qb = smem + buf * BUF;
       const unsigned char* ob = qb + G::TILE;
@@ -463,10 +546,13 @@ __device__ __forceinline__ void dkdv_f32_body(const F32BwdParams& p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * r4 + e;
-          pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lv[e]));
-          if (!full) {
+          float x = s[r];
+          if constexpr (MK == kMaskAdd) x = __builtin_fmaf(__uint_as_float(mw[r]), p.mscale, x);
+          pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(x, c, -lv[e]));
+          if (MK != kMaskNone || !full) {
             const int qi = q0 + qi0 + e;
-            const bool vis = (!CAUSAL || key <= qi) && key < kv_end && qi < p.N;
+            bool vis = (!CAUSAL || key <= qi) && key < kv_end && qi < p.N;
+            if constexpr (MK == kMaskKeep) vis = vis && mw[r] != 0;
             pr[r] = vis ? pr[r] : 0.f;
           }
           ds[r] = pr[r] * (dp[r] - dv4[e]);
@@ -503,46 +589,54 @@ __device__ __forceinline__ void dkdv_f32_body(const F32BwdParams& p) {
 
 // D = 128 keeps 192 (dQ) and 256 (dK/dV) registers of row fragments and accumulators per lane:
 // one wave per SIMD with the whole register file. Smaller head dims run two.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int MK>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(D > 64 ? 1 : 2, D > 64 ? 1 : 2)))
 void attn_bwd_f32_dq_kernel(F32BwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  dq_f32_body<D, CAUSAL>(p);
+  dq_f32_body<D, CAUSAL, MK>(p);
 #endif
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int MK>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(D > 64 ? 1 : 2, D > 64 ? 1 : 2)))
 void attn_bwd_f32_dkdv_kernel(F32BwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  dkdv_f32_body<D, CAUSAL>(p);
+  dkdv_f32_body<D, CAUSAL, MK>(p);
 #endif
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int MK>
 hipError_t launch_d(const F32BwdParams& p, hipStream_t s) {
   const int64_t nq = (int64_t)p.B * p.Hq * p.nqt;
   const int64_t nk = (int64_t)p.B * p.Hkv * p.nkt * p.split;
-  hipLaunchKernelGGL((attn_bwd_f32_dq_kernel<D, CAUSAL>), dim3((unsigned)nq), dim3(kThreads), 0,
-                     s, p);
+  hipLaunchKernelGGL((attn_bwd_f32_dq_kernel<D, CAUSAL, MK>), dim3((unsigned)nq),
+                     dim3(kThreads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_bwd_f32_dkdv_kernel<D, CAUSAL>), dim3((unsigned)nk), dim3(kThreads),
-                     0, s, p);
+  hipLaunchKernelGGL((attn_bwd_f32_dkdv_kernel<D, CAUSAL, MK>), dim3((unsigned)nk),
+                     dim3(kThreads), 0, s, p);
   return hipGetLastError();
+}
+
+template <int MK>
+hipError_t launch_m(const F32BwdParams& p, int D, bool causal, hipStream_t s) {
+  switch (D) {
+    case 16: return causal ? launch_d<16, true, MK>(p, s) : launch_d<16, false, MK>(p, s);
+    case 32: return causal ? launch_d<32, true, MK>(p, s) : launch_d<32, false, MK>(p, s);
+    case 64: return causal ? launch_d<64, true, MK>(p, s) : launch_d<64, false, MK>(p, s);
+    default: return causal ? launch_d<128, true, MK>(p, s) : launch_d<128, false, MK>(p, s);
+  }
 }
 
 }  // namespace
 
-hipError_t launch_bwd_f32(const F32BwdParams& p, int D, bool causal, hipStream_t s) {
-  switch (D) {
-    case 16: return causal ? launch_d<16, true>(p, s) : launch_d<16, false>(p, s);
-    case 32: return causal ? launch_d<32, true>(p, s) : launch_d<32, false>(p, s);
-    case 64: return causal ? launch_d<64, true>(p, s) : launch_d<64, false>(p, s);
-    default: return causal ? launch_d<128, true>(p, s) : launch_d<128, false>(p, s);
-  }
+hipError_t launch_bwd_f32(const F32BwdParams& p, int D, bool causal, int mask_type,
+                          hipStream_t s) {
+  if (mask_type == ATTN_MASK_KEEP_U8) return launch_m<kMaskKeep>(p, D, causal, s);
+  if (mask_type == ATTN_MASK_ADD) return launch_m<kMaskAdd>(p, D, causal, s);
+  return launch_m<kMaskNone>(p, D, causal, s);
 }
 
 }  // namespace attn_detail

@@ -339,9 +339,14 @@ struct F32BwdParams {
   float scale;       // the signed scale (dQ and dK carry it)
   int split;         // parts per key tile of the dK/dV kernel (1: none; else fp32 partials)
   float* part;       // [2][split][B][Hkv][N][D] partial sums (split > 1)
+  const void* mask;  // the forward's explicit mask: uint8 keep or fp32 additive
+  int64_t ms_b, ms_h, ms_n;   // its element strides (batch, query head, query row)
+  float mscale;      // log2(e) / c: an additive mask value in raw score units
 };
 
-// Queue the fp32 backward (dQ kernel, then dK/dV kernel) for D in {16, 32, 64, 128}.
-hipError_t launch_bwd_f32(const F32BwdParams& p, int D, bool causal, hipStream_t stream);
+// Queue the fp32 backward (dQ kernel, then dK/dV kernel) for D in {16, 32, 64, 128} and
+// mask_type an attn_mask_t.
+hipError_t launch_bwd_f32(const F32BwdParams& p, int D, bool causal, int mask_type,
+                          hipStream_t stream);
 
 }  // namespace attn_detail

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_version(lib):
-    assert sdp.attn_version() == 10
+    assert sdp.attn_version() == 11
 
 
 def test_status_strings(lib):
@@ -429,7 +429,13 @@ def test_bwd_masked_validate(lib):
     assert bmcall(mtype=sdp.ATTN_MASK_NONE, mask=None) == sdp.ATTN_OK
     assert bmcall(ms=(0, MN * MN, MN)) == sdp.ATTN_OK                 # [Hq, N, N] per head
     assert bmcall(mtype=5) == sdp.ATTN_ERR_MASK
-    assert bmcall(dtype=sdp.ATTN_F32) == sdp.ATTN_ERR_DTYPE             # masks are 16-bit only
+    assert bmcall(dtype=sdp.ATTN_F32) == sdp.ATTN_OK                    # fp32 with a keep mask
+    add = sdp.ATTN_MASK_ADD
+    assert bmcall(dtype=sdp.ATTN_F32, mtype=add) == sdp.ATTN_OK         # and an fp32 additive one
+    assert bmcall(mtype=add, ms=(0, 0, 1 << 19)) == sdp.ATTN_OK
+    assert bmcall(dtype=sdp.ATTN_F32, mtype=add, ms=(0, 0, 1 << 19)) == sdp.ATTN_ERR_SHAPE
+    assert bmcall(dtype=sdp.ATTN_F32, mtype=add, ms=(MN * (MN + 4), 0, MN + 4)) == sdp.ATTN_OK
+    assert bmcall(mtype=add, ms=(MN * (MN + 4), 0, MN + 4)) == sdp.ATTN_ERR_LAYOUT
     assert bmcall(mtype=sdp.ATTN_MASK_NONE, mask=None, dtype=sdp.ATTN_F32) == sdp.ATTN_OK
     assert bmcall(mask=None) == sdp.ATTN_ERR_NULL
     assert bmcall(mask=MK + 8) == sdp.ATTN_ERR_LAYOUT                 # misaligned
@@ -471,7 +477,9 @@ def test_bwd_ws_validate(lib):
     assert wcall(n=base - 1) == sdp.ATTN_ERR_WORKSPACE
     assert wcall(n=0) == sdp.ATTN_ERR_WORKSPACE
     assert wcall(dtype=sdp.ATTN_F32, n=big) == sdp.ATTN_OK
-    assert wcall(dtype=sdp.ATTN_F32, mask=MK, mtype=sdp.ATTN_MASK_KEEP_U8) == sdp.ATTN_ERR_DTYPE
+    f32keep = dict(dtype=sdp.ATTN_F32, mask=MK, mtype=sdp.ATTN_MASK_KEEP_U8)
+    assert wcall(N=1024, **f32keep) == sdp.ATTN_OK
+    assert wcall(**f32keep) == sdp.ATTN_ERR_LAYOUT          # 1000-byte mask rows
     assert wcall(mask=MK, mtype=sdp.ATTN_MASK_KEEP_U8, N=MN) == sdp.ATTN_OK
     assert wcall(mtype=7, mask=MK) == sdp.ATTN_ERR_MASK
     # dq right after the minimal workspace: fine when only that is used, an overlap with the

@@ -347,6 +347,34 @@ def test_bwd_split_masked_and_strided():
     log("split masked bnhd: rel err dQ %.2e dK %.2e dV %.2e" % tuple(e))
 
 
+@pytest.mark.parametrize("kind", ["keep", "add"])
+def test_bwd_f32_split_masked(kind):
+    """fp32 tensors, an explicit mask and the split dK/dV work (attn_bwd_ws, MQA)."""
+    import torch
+    from gpu_util import device_mask, mask_values
+    case = inputs.make_case(1, 8, 1, 1024, 64, "f32", True, False, seed=245)
+    assert split_of(case) > 1
+    dout_bits = inputs.make_grad(case, 245)
+    rng = np.random.default_rng(247)
+    pattern = "random_bh" if kind == "keep" else "alibi"
+    mv = mask_values(kind, pattern, "f32", 1, 8, 1024, rng)
+    dmask = device_mask(kind, pattern, "f32", mv, 1024)
+    q, k, v, do = (to_device(x, "f32") for x in (case.q_bits, case.k_bits, case.v_bits,
+                                                  dout_bits))
+    out, lse = sdp.forward(q, k, v, causal=True, scale=case.scale, attn_mask=dmask)
+    dq, dk, dv = sdp.backward(q, k, v, out, do, lse, causal=True, scale=case.scale,
+                              attn_mask=dmask)
+    torch.cuda.synchronize()
+    got = [from_device(t, "f32") for t in (dq, dk, dv)]
+    qw, kw, vw = case.widened()
+    mk = {"keep_mask": mv} if kind == "keep" else {"add_mask": inputs.widen(mv, "f32")}
+    ref = oracle.attn_bwd(qw, kw, vw, inputs.widen(dout_bits, "f32"), case.scale, True, None,
+                          **mk)
+    e = [check_grad(n, g, r, "f32", "f32 split masked " + kind) for n, g, r in
+         zip(("dQ", "dK", "dV"), got, ref)]
+    log("f32 split masked %s: rel err dQ %.2e dK %.2e dV %.2e" % (kind, *e))
+
+
 def test_bwd_rising_row_maximum():
     """Keys scaled up along the sequence: rows whose maximum moves from tile to tile, so P
     rebuilt from the forward's LSE must still match."""
@@ -524,6 +552,14 @@ BWD_MASKED = [
     ("add", "alibi", "bf16", 16, False, True, 2, 4, 1, 150),
     ("keep", "random_bh", "bf16", 256, True, True, 2, 4, 2, 200),
     ("add", "window_neginf", "f16", 256, False, False, 2, 2, 1, 150),
+    # fp32 tensors: uint8 keep masks and fp32 additive masks
+    ("keep", "random_bh", "f32", 128, True, True, 2, 4, 2, 300),
+    ("keep", "empty_rows", "f32", 64, True, False, 1, 4, 2, 130),
+    ("keep", "window", "f32", 32, False, False, 2, 4, 4, 256),
+    ("add", "random_bh", "f32", 128, True, False, 2, 4, 2, 257),
+    ("add", "alibi", "f32", 64, True, True, 2, 8, 2, 200),
+    ("add", "window_neginf", "f32", 16, False, False, 2, 2, 1, 150),
+    ("add", "large_negative", "f32", 128, False, True, 1, 2, 2, 100),
 ]
 
 
