@@ -190,7 +190,7 @@ def main():
                          "reference kernel for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only; there is no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
