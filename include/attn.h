@@ -100,7 +100,7 @@ typedef enum {
  *   B, Hq, Hkv, N, D
  *              batch, query heads, key/value heads, sequence length (queries and keys share it),
  *              head dimension. Any N >= 1 is accepted; D must be 16, 32, 64, 128 or 256
- *              (attn_bwd: 16, 32, 64, 128, and 256 for 16-bit types).
+ *              (attn_bwd too).
  *   scale      multiplier of the dot products (typically 1/sqrt(D)); any finite value.
  *   causal     nonzero hides key j from query i when j > i.
  *   valid_len  device pointer to int32[B], or NULL for no padding mask. Keys j >= valid_len[b]
@@ -240,8 +240,9 @@ int attn_fwd_masked_validate(const void *q, const int64_t *q_strides, const void
  *                the input type. ATTN_F32: fp32 tensors and fp32 products throughout.
  *   others       as in attn_fwd.
  *
- * Kernels run on `stream` in order (dQ and Delta, then dK and dV; each in two head-dimension
- * halves at D = 256). Outputs must not overlap any input, each other or valid_len
+ * Kernels run on `stream` in order (dQ and Delta, then dK and dV; at D = 256 each in parts
+ * over the head dimension: two halves for 16-bit tensors, for fp32 two (dQ) and four (dK, dV)).
+ * Outputs must not overlap any input, each other or valid_len
  * (ATTN_ERR_ALIAS); misaligned pointers are ATTN_ERR_LAYOUT. Otherwise returns as attn_fwd.
  */
 int attn_bwd(const void *q, const void *k, const void *v, const void *out, const void *dout,
@@ -360,11 +361,11 @@ int64_t attn_bwd_workspace_floats(int B, int Hq, int Hkv, int N, int D);
 /* attn_status_string -- a static, NUL-terminated description of a return code (never NULL). */
 const char *attn_status_string(int status);
 
-/* attn_version -- the library's interface version, currently 11 (2 added attn_fwd_strided, 3
+/* attn_version -- the library's interface version, currently 12 (2 added attn_fwd_strided, 3
  * attn_fwd_masked, 4 attn_bwd, 5 attn_bwd_strided, 6 attn_bwd_masked, 7 ATTN_F32 in attn_bwd
  * and attn_bwd_strided, 8 attn_bwd_ws and attn_bwd_workspace_floats, 9 lowered ATTN_MAX_TILES
  * to what one launch can hold, 10 ATTN_F32 in attn_fwd_masked, 11 ATTN_F32 with a mask in
- * attn_bwd_masked and attn_bwd_ws). */
+ * attn_bwd_masked and attn_bwd_ws, 12 ATTN_F32 at D = 256 in the backward). */
 int attn_version(void);
 
 #ifdef __cplusplus

@@ -23,4 +23,4 @@ extern "C" const char* attn_status_string(int status) {
   }
 }
 
-extern "C" int attn_version(void) { return 11; }
+extern "C" int attn_version(void) { return 12; }

@@ -962,8 +962,7 @@ int bwd_validate(const BwdLayouts& t, const float* lse, const float* ws, int64_t
   if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
   if (N > ATTN_MAX_N) return ATTN_ERR_SHAPE;
   if ((int64_t)B * Hq * (((int64_t)N + kBM - 1) / kBM) > ATTN_MAX_TILES) return ATTN_ERR_SHAPE;
-  if (D != 16 && D != 32 && D != 64 && D != 128 && !(D == 256 && dtype != ATTN_F32))
-    return ATTN_ERR_HEAD_DIM;
+  if (D != 16 && D != 32 && D != 64 && D != 128 && D != 256) return ATTN_ERR_HEAD_DIM;
   if (dtype != ATTN_F16 && dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_DTYPE;
   if (!isfinite(scale)) return ATTN_ERR_SCALE;
   const int es = dtype == ATTN_F32 ? 4 : 2;   // bytes per element

@@ -118,21 +118,33 @@ __device__ inline uint32_t dma_lane(int wave, int i, int lane, uint32_t rowbytes
   return (uint32_t)(rel ? lane / G::CH : r) * rowbytes + c * 16;
 }
 
-// Store a wave's 32 x DH block held transposed (acc[u][4 r4 + e] is element 32u + 8 r4 + 4h + e
-// of row `row`), times `mul`.
-template <int D, int DH>
-__device__ inline void store_row(const f32x16 (&acc)[B32<D>::OT], float mul, float* dst, int h) {
+// Store a wave's 32 x DH block held transposed (acc[u][4 r4 + e] is element
+// 32 (U0 + u) + 8 r4 + 4h + e of row `row`, for the UN 32-column tiles from U0), times `mul`.
+template <int D, int DH, int U0 = 0, int UN = B32<D>::OT>
+__device__ inline void store_row(const f32x16 (&acc)[UN], float mul, float* dst, int h) {
 #pragma unroll
-  for (int u = 0; u < B32<D>::OT; ++u)
+  for (int u = 0; u < UN; ++u)
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
-      if (32 * u + 8 * r4 + 4 * h >= DH) continue;
+      const int col = 32 * (U0 + u) + 8 * r4 + 4 * h;
+      if (col >= DH) continue;
       f32x4 w;
 #pragma unroll
       for (int e = 0; e < 4; ++e) w[e] = acc[u][4 * r4 + e] * mul;
-      *(f32x4*)(dst + 32 * u + 8 * r4 + 4 * h) = w;
+      *(f32x4*)(dst + col) = w;
     }
 }
+
+// D = 256 does not fit its row fragments and accumulators in the register file: each kernel
+// runs as NP launches (PART 0 .. NP-1), each recomputing the scores and accumulating, then
+// storing, 1/NP of the output columns. PART -1: one launch, all columns.
+template <int D, int PART, int NP>
+struct Cols {
+  static constexpr int UN = PART < 0 ? B32<D>::OT : B32<D>::OT / NP;   // 32-column tiles held
+  static constexpr int U0 = PART < 0 ? 0 : PART * UN;                 // first of them
+};
+constexpr int kPartsDq = 2;     // dQ kernel at D = 256: Q, dO rows + half of dQ
+constexpr int kPartsDkdv = 4;   // dK/dV kernel at D = 256: K, V rows + a quarter of dK, dV
 
 // The forward's explicit mask (MK: kMaskKeep uint8, kMaskAdd fp32; kMaskNone for none): the
 // (batch, query head) plane as a range-checked buffer ending at its last row's 16-byte boundary
@@ -152,7 +164,7 @@ __device__ inline __amdgpu_buffer_rsrc_t mask_plane(const F32BwdParams& p, int b
 // ------------------------------------------------------------------------------------------
 // dQ (and D, L2)
 // ------------------------------------------------------------------------------------------
-template <int DH, bool CAUSAL, int MK>
+template <int DH, bool CAUSAL, int MK, int PART>
 __device__ __forceinline__ void dq_f32_body(const F32BwdParams& p) {
   constexpr int D = DH < 32 ? 32 : DH;   // geometry; DH = 16 zero-fills half of every row
   constexpr int DCH = DH / 4;
@@ -255,9 +267,10 @@ __device__ __forceinline__ void dq_f32_body(const F32BwdParams& p) {
 
   Offsets<D> off;
   off.init(lane);
-  f32x16 acc[OT];
+  constexpr int UN = Cols<D, PART, kPartsDq>::UN, U0 = Cols<D, PART, kPartsDq>::U0;
+  f32x16 acc[UN];
 #pragma unroll
-  for (int u = 0; u < OT; ++u) acc[u] = f32x16{};
+  for (int u = 0; u < UN; ++u) acc[u] = f32x16{};
   const float c = p.c;
   // Explicit mask: the words of this lane's query row for the keys of its score registers,
   // kb0 + 8g + 4h + e = byte e of word g (keep) or word 4g + e (additive).
@@ -341,8 +354,8 @@ __device__ __forceinline__ void dq_f32_body(const F32BwdParams& p) {
 #pragma unroll
     for (int s = 0; s < 16; ++s)
 #pragma unroll
-      for (int u = 0; u < OT; ++u)
-        acc[u] = mfma_f32(*(const float*)(kb + off.elem(s, u)), ds[s], acc[u]);
+      for (int u = 0; u < UN; ++u)
+        acc[u] = mfma_f32(*(const float*)(kb + off.elem(s, U0 + u)), ds[s], acc[u]);
   };
   for (int j = 0; j < ntiles; j += 2) {
     step(std::integral_constant<int, 0>{}, j);
@@ -351,13 +364,14 @@ __device__ __forceinline__ void dq_f32_body(const F32BwdParams& p) {
   // the last step's reload lands before the workgroup's LDS can be handed to another
   if constexpr (MK != kMaskNone) wait_loads_and_lds();
   if (qrow < p.N)
-    store_row<D, DH>(acc, p.scale, p.dq + b * p.dqs_b + hq * p.dqs_h + qrow * p.dqs_n, h);
+    store_row<D, DH, U0, UN>(acc, p.scale, p.dq + b * p.dqs_b + hq * p.dqs_h + qrow * p.dqs_n,
+                             h);
 }
 
 // ------------------------------------------------------------------------------------------
 // dK, dV
 // ------------------------------------------------------------------------------------------
-template <int DH, bool CAUSAL, int MK>
+template <int DH, bool CAUSAL, int MK, int PART>
 __device__ __forceinline__ void dkdv_f32_body(const F32BwdParams& p) {
   constexpr int D = DH < 32 ? 32 : DH;
   constexpr int DCH = DH / 4;
@@ -407,9 +421,10 @@ __device__ __forceinline__ void dkdv_f32_body(const F32BwdParams& p) {
   int kv_end = p.N;
   if (p.valid_len) kv_end = min(max(p.valid_len[b], 0), p.N);
 
-  f32x16 dk[OT], dv[OT];
+  constexpr int UN = Cols<D, PART, kPartsDkdv>::UN, U0 = Cols<D, PART, kPartsDkdv>::U0;
+  f32x16 dk[UN], dv[UN];
 #pragma unroll
-  for (int u = 0; u < OT; ++u) dk[u] = dv[u] = f32x16{};
+  for (int u = 0; u < UN; ++u) dk[u] = dv[u] = f32x16{};
 
   const int qstart = CAUSAL ? k0 : 0;
   const int ntq = k0 < kv_end ? (p.N - qstart + kT - 1) / kT : 0;
@@ -562,9 +577,9 @@ __device__ __forceinline__ void dkdv_f32_body(const F32BwdParams& p) {
 #pragma unroll
       for (int k = 0; k < 16; ++k)
 #pragma unroll
-        for (int u = 0; u < OT; ++u) {
-          dv[u] = mfma_f32(*(const float*)(ob + off.elem(k, u)), pr[k], dv[u]);
-          dk[u] = mfma_f32(*(const float*)(qb + off.elem(k, u)), ds[k], dk[u]);
+        for (int u = 0; u < UN; ++u) {
+          dv[u] = mfma_f32(*(const float*)(ob + off.elem(k, U0 + u)), pr[k], dv[u]);
+          dk[u] = mfma_f32(*(const float*)(qb + off.elem(k, U0 + u)), ds[k], dk[u]);
         }
     };
     for (int it = 0; it < iters; it += 2) {
@@ -578,45 +593,67 @@ __device__ __forceinline__ void dkdv_f32_body(const F32BwdParams& p) {
       // fp32 partial sums of this part, added in part order by the reduction kernel
       const size_t plane = (size_t)p.B * p.Hkv * p.N * DH;
       float* pk = p.part + (size_t)sp * plane + (((size_t)b * p.Hkv + kvh) * p.N + key) * DH;
-      store_row<D, DH>(dk, p.scale, pk, h);
-      store_row<D, DH>(dv, 1.0f, pk + (size_t)p.split * plane, h);
+      store_row<D, DH, U0, UN>(dk, p.scale, pk, h);
+      store_row<D, DH, U0, UN>(dv, 1.0f, pk + (size_t)p.split * plane, h);
     } else {
-      store_row<D, DH>(dk, p.scale, p.dk + b * p.dks_b + kvh * p.dks_h + key * p.dks_n, h);
-      store_row<D, DH>(dv, 1.0f, p.dv + b * p.dvs_b + kvh * p.dvs_h + key * p.dvs_n, h);
+      store_row<D, DH, U0, UN>(dk, p.scale,
+                               p.dk + b * p.dks_b + kvh * p.dks_h + key * p.dks_n, h);
+      store_row<D, DH, U0, UN>(dv, 1.0f, p.dv + b * p.dvs_b + kvh * p.dvs_h + key * p.dvs_n,
+                               h);
     }
   }
 }
 
 // D = 128 keeps 192 (dQ) and 256 (dK/dV) registers of row fragments and accumulators per lane:
 // one wave per SIMD with the whole register file. Smaller head dims run two.
-template <int D, bool CAUSAL, int MK>
+template <int D, bool CAUSAL, int MK, int PART>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(D > 64 ? 1 : 2, D > 64 ? 1 : 2)))
 void attn_bwd_f32_dq_kernel(F32BwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  dq_f32_body<D, CAUSAL, MK>(p);
+  dq_f32_body<D, CAUSAL, MK, PART>(p);
 #endif
 }
 
-template <int D, bool CAUSAL, int MK>
+template <int D, bool CAUSAL, int MK, int PART>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(D > 64 ? 1 : 2, D > 64 ? 1 : 2)))
 void attn_bwd_f32_dkdv_kernel(F32BwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  dkdv_f32_body<D, CAUSAL, MK>(p);
+  dkdv_f32_body<D, CAUSAL, MK, PART>(p);
 #endif
 }
 
+// The dQ launches (which also write D and L2) precede the dK/dV launches that read them.
 template <int D, bool CAUSAL, int MK>
 hipError_t launch_d(const F32BwdParams& p, hipStream_t s) {
   const int64_t nq = (int64_t)p.B * p.Hq * p.nqt;
   const int64_t nk = (int64_t)p.B * p.Hkv * p.nkt * p.split;
-  hipLaunchKernelGGL((attn_bwd_f32_dq_kernel<D, CAUSAL, MK>), dim3((unsigned)nq),
-                     dim3(kThreads), 0, s, p);
+  if constexpr (D > 128) {
+    hipLaunchKernelGGL((attn_bwd_f32_dq_kernel<D, CAUSAL, MK, 0>), dim3((unsigned)nq),
+                       dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((attn_bwd_f32_dq_kernel<D, CAUSAL, MK, 1>), dim3((unsigned)nq),
+                       dim3(kThreads), 0, s, p);
+    static_assert(kPartsDq == 2 && kPartsDkdv == 4, "launches below");
+  } else {
+    hipLaunchKernelGGL((attn_bwd_f32_dq_kernel<D, CAUSAL, MK, -1>), dim3((unsigned)nq),
+                       dim3(kThreads), 0, s, p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_bwd_f32_dkdv_kernel<D, CAUSAL, MK>), dim3((unsigned)nk),
-                     dim3(kThreads), 0, s, p);
+  if constexpr (D > 128) {
+    hipLaunchKernelGGL((attn_bwd_f32_dkdv_kernel<D, CAUSAL, MK, 0>), dim3((unsigned)nk),
+                       dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((attn_bwd_f32_dkdv_kernel<D, CAUSAL, MK, 1>), dim3((unsigned)nk),
+                       dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((attn_bwd_f32_dkdv_kernel<D, CAUSAL, MK, 2>), dim3((unsigned)nk),
+                       dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((attn_bwd_f32_dkdv_kernel<D, CAUSAL, MK, 3>), dim3((unsigned)nk),
+                       dim3(kThreads), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((attn_bwd_f32_dkdv_kernel<D, CAUSAL, MK, -1>), dim3((unsigned)nk),
+                       dim3(kThreads), 0, s, p);
+  }
   return hipGetLastError();
 }
 
@@ -626,6 +663,7 @@ hipError_t launch_m(const F32BwdParams& p, int D, bool causal, hipStream_t s) {
     case 16: return causal ? launch_d<16, true, MK>(p, s) : launch_d<16, false, MK>(p, s);
     case 32: return causal ? launch_d<32, true, MK>(p, s) : launch_d<32, false, MK>(p, s);
     case 64: return causal ? launch_d<64, true, MK>(p, s) : launch_d<64, false, MK>(p, s);
+    case 256: return causal ? launch_d<256, true, MK>(p, s) : launch_d<256, false, MK>(p, s);
     default: return causal ? launch_d<128, true, MK>(p, s) : launch_d<128, false, MK>(p, s);
   }
 }

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_version(lib):
-    assert sdp.attn_version() == 11
+    assert sdp.attn_version() == 12
 
 
 def test_status_strings(lib):
@@ -299,6 +299,7 @@ def test_bwd_validate_accepts(lib):
     assert bcall(D=32) == sdp.ATTN_OK
     assert bcall(D=256) == sdp.ATTN_OK
     assert bcall(D=256, dtype=sdp.ATTN_F16) == sdp.ATTN_OK
+    assert bcall(D=256, dtype=sdp.ATTN_F32) == sdp.ATTN_OK
     for d in (16, 32, 64, 128):
         assert bcall(D=d, dtype=sdp.ATTN_F32) == sdp.ATTN_OK
 
@@ -324,7 +325,6 @@ def test_bwd_validate_size_limits(lib):
     (dict(D=512), sdp.ATTN_ERR_HEAD_DIM),
     (dict(D=48), sdp.ATTN_ERR_HEAD_DIM),
     (dict(dtype=7), sdp.ATTN_ERR_DTYPE),
-    (dict(dtype=sdp.ATTN_F32, D=256), sdp.ATTN_ERR_HEAD_DIM),
     (dict(scale=float("nan")), sdp.ATTN_ERR_SCALE),
     # dq right after a 16-bit-sized q overlaps q once elements are 4 bytes
     (dict(dq=Q + 2 * 8 * 1000 * 128 * 2, dtype=sdp.ATTN_F32), sdp.ATTN_ERR_ALIAS),

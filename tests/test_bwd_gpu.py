@@ -146,6 +146,11 @@ BWD_SMALL = [
     ("f16", 256, False, True, 2, 4, 2, 257),
     ("bf16", 256, True, True, 3, 4, 1, 130),
     ("f16", 256, True, False, 1, 2, 2, 1),
+    # D = 256 (fp32): two (dQ) and four (dK/dV) head-dimension parts
+    ("f32", 256, True, False, 2, 8, 2, 333),
+    ("f32", 256, False, True, 2, 4, 2, 257),
+    ("f32", 256, True, True, 3, 4, 1, 130),
+    ("f32", 256, True, False, 1, 2, 2, 1),
 ]
 
 
@@ -167,6 +172,7 @@ BWD_MANY = [
     ("f32", 128, True, True, 4, 16, 4, 1100),
     ("f32", 64, False, False, 3, 24, 3, 700),
     ("bf16", 256, True, True, 4, 16, 4, 600),
+    ("f32", 256, True, True, 4, 16, 4, 600),
 ]
 
 
@@ -284,6 +290,7 @@ BWD_SPLIT = [
     ("f32", 64, True, False, 1, 8, 1, 1024),
     ("f32", 128, False, True, 2, 16, 2, 700),
     ("bf16", 256, True, False, 1, 16, 1, 1024),
+    ("f32", 256, True, False, 1, 16, 1, 1024),
 ]
 
 
@@ -467,6 +474,7 @@ BWD_STRIDED = [
     ("bnhd", "bf16", 128, True, True, 2, 8, 2, 300),
     ("bnhd", "f32", 128, True, False, 2, 4, 2, 200),
     ("bnhd", "bf16", 256, True, True, 2, 4, 2, 200),
+    ("bnhd", "f32", 256, False, True, 2, 4, 2, 200),
     ("padded_rows", "f32", 64, False, True, 2, 4, 4, 130),
     ("bnhd", "f16", 64, False, False, 2, 4, 4, 200),
     ("padded_rows", "bf16", 64, True, False, 2, 6, 3, 257),
@@ -560,6 +568,8 @@ BWD_MASKED = [
     ("add", "alibi", "f32", 64, True, True, 2, 8, 2, 200),
     ("add", "window_neginf", "f32", 16, False, False, 2, 2, 1, 150),
     ("add", "large_negative", "f32", 128, False, True, 1, 2, 2, 100),
+    ("keep", "random_bh", "f32", 256, True, True, 2, 4, 2, 200),
+    ("add", "alibi", "f32", 256, False, False, 2, 4, 1, 150),
 ]
 
 
