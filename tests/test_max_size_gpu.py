@@ -131,3 +131,47 @@ def test_max_length_padded_gqa(cfg):
     O_ref, L_ref = run_oracle(short, rows=rows2)
     compare(case, O, L, O_ref, L_ref, tag="max-length padded %s" % dtype)
     assert np.all(np.isneginf(L[bh < Hq]))          # batch 0: no visible key
+
+
+def test_max_length_backward_padded():
+    """The backward at N = 1024 x 4093 = 4,191,232 rows (just under 2^22; a whole number of
+    blocks), 2 query heads over 1 KV head, D = 64, without the causal mask, valid_len 1000.
+    Every row sees the same 1000 keys, so a row repeats the gradient terms of the block row it
+    copies: dQ of row i is the block's dQ of row i mod 4093, dK and dV of a key below
+    valid_len are 1024 times the block's, and keys past valid_len get exactly 0. The block
+    itself (N = 4093) is what the oracle runs."""
+    import torch
+    import oracle
+    from test_bwd_gpu import check_grad
+    M, D, dtype, VL = 1024, 64, "bf16", 1000
+    N = M * P
+    vl = np.array([VL], np.int32)
+    block = inputs.make_case(1, 2, 1, P, D, dtype, False, True, seed=[142, 1], valid_len=vl)
+    dout_block = inputs.make_grad(block, [142, 1])
+    rep = lambda x: np.tile(x, (1, 1, M, 1))   # noqa: E731
+    log("max-length backward: N=%d D=%d valid_len=%d" % (N, D, VL))
+    q, k, v, do = (to_device(rep(x), dtype) for x in (block.q_bits, block.k_bits, block.v_bits,
+                                                      dout_block))
+    vl_dev = torch.from_numpy(vl).cuda()
+    out, lse = sdp.forward(q, k, v, causal=False, valid_len=vl_dev, scale=block.scale)
+    dq, dk, dv = sdp.backward(q, k, v, out, do, lse, causal=False, valid_len=vl_dev,
+                              scale=block.scale)
+    torch.cuda.synchronize()
+    assert dk[:, :, VL:].abs().max().item() == 0.0 and dv[:, :, VL:].abs().max().item() == 0.0
+    rng = np.random.default_rng(9)
+    rows = np.union1d(np.array([0, 1, 127, 128, P - 1, P, N // 2, N - 2, N - 1]),
+                      rng.integers(0, N, size=24))
+    idx = torch.from_numpy(rows).cuda()
+    got_q = from_device(dq.index_select(2, idx), dtype)
+    got_k = from_device(dk[:, :, :VL], dtype)
+    got_v = from_device(dv[:, :, :VL], dtype)
+    del q, k, v, do, out, lse, dq, dk, dv
+    torch.cuda.empty_cache()
+
+    qw, kw, vw = block.widened()
+    rq, rk, rv = oracle.attn_bwd(qw, kw, vw, inputs.widen(dout_block, dtype), block.scale,
+                                 False, vl)
+    e = [check_grad("dQ", got_q, rq[:, :, rows % P], dtype, "max-length backward"),
+         check_grad("dK", got_k, M * rk[:, :, :VL], dtype, "max-length backward"),
+         check_grad("dV", got_v, M * rv[:, :, :VL], dtype, "max-length backward")]
+    log("max-length backward: rel err dQ %.2e dK %.2e dV %.2e" % tuple(e))
