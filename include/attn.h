@@ -28,9 +28,10 @@
  * - The computation is the tiled online softmax of "Triton Cuda Attention" (section on the
  *   online softmax core algorithm): the N x N score matrix never reaches memory.
  *
- * Numerics: 16-bit inputs, fp32 scores, softmax state and accumulation; the probabilities are
- * rounded to the input type before they multiply V; O is rounded to nearest-even in the input
- * type. Results are deterministic run to run for the same inputs and shapes.
+ * Numerics: 16-bit inputs with fp32 scores, softmax state and accumulation; the probabilities
+ * are rounded to the input type before they multiply V; O is rounded to nearest-even in the
+ * input type. fp32 inputs (ATTN_F32) stay fp32 throughout. Results are deterministic run to run
+ * for the same inputs and shapes.
  *
  * Threading: every call is independent and the library keeps no state between calls except
  * compiled kernels; calls on different streams may run concurrently. The library allocates no
@@ -59,7 +60,7 @@ typedef enum {
     ATTN_ERR_SHAPE = -2,    /* B, Hq, Hkv or N < 1, Hq not a multiple of Hkv, or sizes beyond
                                the limits below */
     ATTN_ERR_HEAD_DIM = -3, /* D is not supported (see attn_fwd / attn_bwd) */
-    ATTN_ERR_DTYPE = -4,    /* dtype not supported by this entry point */
+    ATTN_ERR_DTYPE = -4,    /* dtype is not one of attn_dtype_t */
     ATTN_ERR_SCALE = -5,    /* scale is NaN or infinite */
     ATTN_ERR_LAUNCH = -6,   /* the HIP runtime reported an error at launch; query HIP for it */
     ATTN_ERR_ALIAS = -7,    /* out or lse overlaps an input, or out overlaps lse */
