@@ -25,10 +25,11 @@ shared by every batch and head and combined with the workload's own masks; the f
 the nominal one.
 
 Throughput is the nominal forward flop count 4*B*Hq*N^2*D (halved under causal masking) per
-second. The roofline object reports the kernel's flop rate against the dense 16-bit MFMA peak,
-timed with HIP events on the stream the kernel is launched on; `traffic` is the HBM byte count
-from rocprofv3 counters recorded in profiles/ for the current kernel source (null if the kernel
-changed since). The cpu_baseline object times the fp64 oracle on a bounded sample of whole
+second, at the median of the K per-launch times measured with HIP events on the stream the
+kernel is launched on (the mean, min, max and the host clock are in the `timing` object). The
+roofline object reports that flop rate against the dense 16-bit MFMA peak; `traffic` is the HBM
+byte count from rocprofv3 counters recorded in profiles/ for the current sources (null if any of
+them changed since). The cpu_baseline object times the fp64 oracle on a bounded sample of whole
 (batch, head) slices of the same workload on the host cores.
 """
 from __future__ import annotations
@@ -49,8 +50,19 @@ METRIC = "attention fwd TFLOP/s, bf16 causal N=4096 D=128; % of MFMA dense peak"
 METRIC_BWD = "attention bwd TFLOP/s (nominal 2.5x forward flops), bf16 causal N=4096 D=128"
 PEAK_TFLOPS_16BIT_DENSE = 2500.0   # MI355X published dense bf16/fp16 MFMA peak
 PEAK_TFLOPS_F32_DENSE = 157.3      # MI355X published dense fp32 MFMA peak
-KERNEL_SRC = os.path.join(ROOT, "scaled_dot_product_fwd_amd", "csrc", "attn_fwd.hip")
-KERNEL_SRC_BWD = os.path.join(ROOT, "scaled_dot_product_fwd_amd", "csrc", "attn_bwd.hip")
+PEAK_SOURCE = ("AMD's published MI355X dense (no sparsity) MFMA peaks: 2.5 PFLOP/s bf16/fp16, "
+               "157.3 TFLOP/s fp32")
+CSRC = os.path.join(ROOT, "scaled_dot_product_fwd_amd", "csrc")
+KERNEL_SRC = os.path.join(CSRC, "attn_fwd.hip")
+KERNEL_SRC_BWD = os.path.join(CSRC, "attn_bwd.hip")
+# The sources each kind of kernel is compiled from: its own file, the shared device header and
+# the C ABI header. A recorded profile belongs to the sources whose fingerprint it names.
+SOURCES = {
+    "fwd": ["attn_fwd.hip", "attn_common.h", "attn.h"],
+    "fwd_f32": ["attn_fwd_f32.hip", "attn_common.h", "attn.h"],
+    "bwd": ["attn_bwd.hip", "attn_common.h", "attn.h"],
+    "bwd_f32": ["attn_bwd_f32.hip", "attn_common.h", "attn.h"],
+}
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -83,21 +95,29 @@ def effective_flops(w, valid_len) -> float:
     return 4.0 * w.D * w.Hq * total
 
 
-def kernel_sha(src: str = KERNEL_SRC) -> str:
-    with open(src, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def source_fingerprint(kind: str) -> str:
+    """sha256 over the names and contents of the sources a kind of kernel is built from."""
+    h = hashlib.sha256()
+    for name in SOURCES[kind]:
+        path = os.path.join(ROOT, "include", name) if name.endswith("attn.h") else \
+            os.path.join(CSRC, name)
+        with open(path, "rb") as f:
+            data = f.read()
+        h.update(name.encode() + b"\0" + str(len(data)).encode() + b"\0" + data)
+    return h.hexdigest()
 
 
 def traffic_for(workload: str, backward: bool = False):
     """HBM bytes per launch (per attn_bwd call with backward) from committed rocprofv3 counter
-    runs, if they were taken on this kernel source."""
+    runs, if they were taken on the current sources."""
     name = "traffic_%s%s.json" % (workload, "_bwd" if backward else "")
     path = os.path.join(PROFILES, name)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_sha256") != kernel_sha(KERNEL_SRC_BWD if backward else KERNEL_SRC):
+    fp = t.get("source_fingerprint") or {}
+    if fp.get("sha256") != source_fingerprint(fp.get("kind", "bwd" if backward else "fwd")):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -185,6 +205,8 @@ def main():
                     help="replace the workload's head dimension")
     ap.add_argument("--backward", action="store_true",
                     help="time attn_bwd (dQ, dK, dV) instead of the forward")
+    ap.add_argument("--log-launches", action="store_true",
+                    help="also print every timed launch's time (ms) to stderr")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (the "
                          "reference kernel for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE) and exit")
@@ -263,20 +285,27 @@ def main():
         step()
     torch.cuda.synchronize()
     log("warmup done (%d steps)" % args.warmup)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    # One HIP event between consecutive launches on the kernel's stream: K per-launch times. The
+    # step time is their median (robust to the first launches, which run while the device's
+    # clock is still rising); the mean and the host clock around the whole region are reported
+    # beside it.
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
+    evs[0].record(stream)
+    for i in range(args.steps):
         step()
-    ev1.record(stream)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_event = ev0.elapsed_time(ev1)
-    ms_per_step = ms_event / args.steps
-    log("timed %d steps: %.3f ms/step by HIP events, %.3f ms/step by host clock" % (
-        args.steps, ms_per_step, wall * 1e3 / args.steps))
+    per = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
+    ms_per_step = float(np.median(per))
+    ms_mean = float(per.mean())
+    if args.log_launches:
+        log("per-launch ms: " + " ".join("%.4f" % x for x in per))
+    log("timed %d steps: median %.4f ms, mean %.4f ms, min %.4f, max %.4f ms per step by HIP "
+        "events; %.4f ms/step by host clock" % (args.steps, ms_per_step, ms_mean, per.min(),
+                                                per.max(), wall * 1e3 / args.steps))
     if torch.isnan(out).any().item():
         raise SystemExit("NaN in the output")
     if args.backward and any(torch.isnan(t).any().item() for t in (dq, dk, dv)):
@@ -290,7 +319,7 @@ def main():
     peak = PEAK_TFLOPS_F32_DENSE if w.dtype == "f32" else PEAK_TFLOPS_16BIT_DENSE
     roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
             "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
-            "traffic": traffic}
+            "traffic": traffic, "peak_source": PEAK_SOURCE}
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the oracle on the host (about %.0f s)" % args.cpu_seconds)
@@ -319,6 +348,11 @@ def main():
                        if w.padded else None)},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "timing": {"statistic": "median of per-launch HIP event times",
+                   "median_ms": round(ms_per_step, 5), "mean_ms": round(ms_mean, 5),
+                   "min_ms": round(float(per.min()), 5), "max_ms": round(float(per.max()), 5),
+                   "mean_tflops": round(f / (ms_mean * 1e-3) / 1e12, 2),
+                   "host_ms_per_step": round(wall * 1e3 / args.steps, 5)},
     }
     print(json.dumps(line))
 

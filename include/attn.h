@@ -6,7 +6,11 @@
  * row i:
  *
  *     O[b,hq,i,:] = softmax_j( scale * Q[b,hq,i,:] . K[b,kv,j,:] + mask(b,i,j) ) V[b,kv,j,:]
- *     LSE[b,hq,i] = ln sum_{visible j} exp( scale * Q[b,hq,i,:] . K[b,kv,j,:] )
+ *     LSE[b,hq,i] = ln sum_{visible j} exp( scale * Q[b,hq,i,:] . K[b,kv,j,:] + add(b,hq,i,j) )
+ *
+ * where mask(b,i,j) is 0 for a visible key and -infinity for a hidden one (the causal and
+ * valid_len masks below, and attn_fwd_masked's keep mask), and add(b,hq,i,j) is the additive
+ * mask of attn_fwd_masked (0 everywhere else); the softmax is taken over the visible keys.
  *
  * - The formula softmax(Q K^T / sqrt(D) + Mask) V over [B,H,N,D] tensors is the one the masked
  *   multi-head attention CUDA article (wzjinhao.cn/news/73578) writes down in section 2.1; the
@@ -53,7 +57,13 @@ typedef enum {
     ATTN_F32 = 2   /* IEEE binary32: every entry point */
 } attn_dtype_t;
 
-/* Return codes. Argument errors are detected on the host before anything is launched. */
+/* Return codes. Argument errors are detected on the host before anything is launched, so a
+ * call either queues work or fails without touching memory: the launch-configuration failures
+ * the masked multi-head attention CUDA article lists (section 5.2: an invalid configuration
+ * from too many threads per block or too much shared memory; section 6.2, its symptom table:
+ * launch failures, and wrong outputs from tensors indexed with the wrong layout) surface here as
+ * ATTN_ERR_SHAPE, ATTN_ERR_HEAD_DIM and ATTN_ERR_LAYOUT before any launch, and a failure the
+ * HIP runtime reports at launch as ATTN_ERR_LAUNCH. attn_status_string describes each code. */
 typedef enum {
     ATTN_OK = 0,
     ATTN_ERR_NULL = -1,     /* q, k, v or out is NULL */
@@ -75,8 +85,8 @@ typedef enum {
 typedef enum {
     ATTN_MASK_NONE = 0,     /* no explicit mask (mask is ignored) */
     ATTN_MASK_KEEP_U8 = 1,  /* uint8 [.., N, N]: nonzero keeps key j for query i, zero hides it */
-    ATTN_MASK_ADD = 2       /* [.., N, N] of the input dtype (fp16 / bf16), added to the scaled
-                               score; -inf hides the key */
+    ATTN_MASK_ADD = 2       /* [.., N, N] of the input dtype (fp16 or bf16; fp32 for ATTN_F32
+                               inputs), added to the scaled score; -inf hides the key */
 } attn_mask_t;
 
 /* Size limits checked by attn_fwd_validate: N <= ATTN_MAX_N and
@@ -359,7 +369,9 @@ int attn_bwd_ws_validate(const void *q, const int64_t *q_strides, const void *k,
  */
 int64_t attn_bwd_workspace_floats(int B, int Hq, int Hkv, int N, int D);
 
-/* attn_status_string -- a static, NUL-terminated description of a return code (never NULL). */
+/* attn_status_string -- a static, NUL-terminated description of a return code (never NULL);
+ * the error codes and the failure modes they stand for are listed at attn_status_t (the
+ * article's sections 5.2 and 6.2 on launch configuration and failure symptoms). */
 const char *attn_status_string(int status);
 
 /* attn_version -- the library's interface version, currently 12 (2 added attn_fwd_strided, 3

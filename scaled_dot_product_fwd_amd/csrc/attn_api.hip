@@ -1,4 +1,7 @@
-// Status strings and the interface version of the C ABI in attn.h (host code only).
+// Status strings and the interface version of the C ABI in attn.h (host code only). The codes
+// are the argument and launch failures the masked multi-head attention CUDA article describes
+// (section 5.2, launch configuration; section 6.2, its table of failure symptoms), reported
+// before anything is launched.
 #include "attn.h"
 
 extern "C" const char* attn_status_string(int status) {
@@ -8,9 +11,9 @@ extern "C" const char* attn_status_string(int status) {
     case ATTN_ERR_SHAPE:
       return "bad shape: B, Hq, Hkv and N must be >= 1, Hq a multiple of Hkv, within size limits";
     case ATTN_ERR_HEAD_DIM:
-      return "unsupported head dimension: D must be 16, 32, 64, 128 or 256 (backward: up to 128)";
+      return "unsupported head dimension: D must be 16, 32, 64, 128 or 256";
     case ATTN_ERR_DTYPE:
-      return "unsupported dtype: ATTN_F16, ATTN_BF16 or ATTN_F32 (explicit masks: 16-bit only)";
+      return "unsupported dtype: ATTN_F16, ATTN_BF16 or ATTN_F32";
     case ATTN_ERR_SCALE: return "scale is not finite";
     case ATTN_ERR_LAUNCH: return "the HIP runtime reported an error at kernel launch";
     case ATTN_ERR_ALIAS: return "an output overlaps an input or another output";

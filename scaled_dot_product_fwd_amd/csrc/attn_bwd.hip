@@ -26,9 +26,10 @@
 //     on the VALU, dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read through
 //     ds_read_b64_tr_b16. dK and dV are written once.
 //
-// Inputs are contiguous [B, H, N, D] tensors of one 16-bit type; dQ, dK, dV are written in that
-// type (fp32 accumulation, round to nearest even). P and dS are rounded to the input type
-// before they enter an MFMA, as the forward rounds P.
+// Inputs are [B, H, N, D] tensors of one 16-bit type given by (batch, head, row) strides with
+// contiguous rows (contiguous tensors are the default); dQ, dK, dV are written in that type
+// through strides of their own (fp32 accumulation, round to nearest even). P and dS are rounded
+// to the input type before they enter an MFMA, as the forward rounds P.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -338,8 +339,8 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p) {
 #pragma unroll
     for (int i = 0; i < G::LOADS; ++i) {
       const int blk = (wave * G::LOADS + i) * 1024;
-      dma16<false>(krs, smem + kdst + blk, kdma[i], row0 * krow);
-      dma16<false>(vrs, smem + vdst + blk, vdma[i], row0 * vrow);
+      dma16(krs, smem + kdst + blk, kdma[i], row0 * krow);
+      dma16(vrs, smem + vdst + blk, vdma[i], row0 * vrow);
     }
   };
 
@@ -361,7 +362,7 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p) {
     if constexpr (MK != kMaskNone) {
 #pragma unroll
       for (int i = 0; i < MG::LOADS; ++i)
-        dma16<false>(mrs, smem + MOFF + wave * MG::WB + i * 1024, moff,
+        dma16(mrs, smem + MOFF + wave * MG::WB + i * 1024, moff,
               (uint32_t)tile * MG::RB + (uint32_t)(i * MG::RPL) * mrow);
     }
   };
@@ -637,7 +638,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
         const int vc = (lane % G::CH) ^ G::bswz(row);
         const uint32_t off =
             (DCH < G::CH && vc >= DCH) ? kNoChunk : (lane / G::CH) * vrow + vc * 16;
-        dma16<false>(vrs, vreg + i * 1024, off, (uint32_t)(kw + i * G::RPB) * vrow);
+        dma16(vrs, vreg + i * 1024, off, (uint32_t)(kw + i * G::RPB) * vrow);
       }
     }
     // DMA of the iteration over query head kvh * group + g, queries q0 .. q0+31, into buffer
@@ -668,8 +669,8 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
       for (int i = 0; i < BG::QLOADS; ++i) {
         const int blk = wave * BG::QLOADS + i;
         const uint32_t r0 = (uint32_t)(q0 + blk * G::RPB);
-        dma16<false>(qrs, base + blk * 1024, qoff[i], r0 * qrowb);
-        dma16<false>(ors, base + BG::QTILE + blk * 1024, goff[i], r0 * growb);
+        dma16(qrs, base + blk * 1024, qoff[i], r0 * qrowb);
+        dma16(ors, base + BG::QTILE + blk * 1024, goff[i], r0 * growb);
       }
       if (wave < 2) {
         const float* src = wave == 0 ? p.lse2 : p.delta;
@@ -679,7 +680,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
         // row range when N % 4 != 0. Lanes 32..63 are out of range and write zeros to bytes
         // 128..255 of the wave's 1 KiB slot.
         const uint32_t loff = lane < kQT ? (uint32_t)(q0 + lane) * 4 : 0x7ffffff0u;
-        dma4<false>(lrs, base + 2 * BG::QTILE + wave * 1024, loff, 0);
+        dma4(lrs, base + 2 * BG::QTILE + wave * 1024, loff, 0);
       }
     };
 
@@ -706,7 +707,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
             (short)0, (p.N - 1) * mrow + ((p.N * KM::ES + 15) & ~15), kBufferFlags);
 #pragma unroll
         for (int i = 0; i < KM::LOADS; ++i)
-          dma16<false>(mrs, smem + MOFF + wave * KM::WB + i * 1024, mlane,
+          dma16(mrs, smem + MOFF + wave * KM::WB + i * 1024, mlane,
                 (uint32_t)(q0 + i * KM::RPL) * mrow);
       }
     };

@@ -27,12 +27,13 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kBufferFlags = 0x00020000;   // raw buffer: dword data, range-checked
 
-template <int D>
+// NW: waves sharing the DMA of a tile (the workgroup's waves).
+template <int D, int NW = kWaves>
 struct Geo {
   static constexpr int CH = D / 8;                   // 16-byte chunks per row
   static constexpr int ROW = 2 * D;                  // bytes per row
   static constexpr int TILE = kBN * ROW;             // bytes per K or V tile
-  static constexpr int LOADS = TILE / 1024 / kWaves; // 1 KiB DMA blocks per wave per tile
+  static constexpr int LOADS = TILE / 1024 / NW;     // 1 KiB DMA blocks per wave per tile
   static constexpr int RPB = 1024 / ROW;             // rows per 1 KiB block
   static constexpr int KSTEPS = D / 16;              // k-steps of the score MFMA
   static constexpr int OT = D / 32;                  // 32-row tiles of O^T
@@ -139,41 +140,49 @@ __device__ inline void wait_loads_and_lds() {
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
 }
 
-// Buffer loads into LDS (16 or 4 bytes per lane, to `lds` + lane * bytes), issued through inline
-// asm rather than the buffer-load-to-LDS builtin: the compiler cannot tell a later
-// ds_read_b64_tr_b16 apart from the DMA's destination and, for the builtin, waits for the whole
+// Buffer loads into LDS (16 or 4 bytes per lane, to LDS byte address `lds` + lane * bytes).
+// The asm form (ASM = true) exists because the compiler cannot tell a later ds_read_b64_tr_b16
+// apart from the DMA's destination and, for the buffer-load-to-LDS builtin, waits for the whole
 // DMA before the first such read (measured: the forward's V reads stalled on every tile's
-// prefetch). Callers order the DMA themselves with an explicit vmcnt wait before reading the
-// destination (wait_loads_and_lds at the top of every loop step). M0 holds the LDS address; no
-// other code in these kernels uses M0.
-__device__ inline uint32_t lds_addr(const unsigned char* lds) {
-  return __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const unsigned char*)lds);
+// prefetch). Callers order the asm DMA themselves with an explicit vmcnt wait before reading the
+// destination (wait_loads_and_lds at the top of every loop step). The LDS address reaches M0
+// through the "{m0}" operand constraint, so the compiler knows M0 is written and sets it itself.
+// Addresses are 32-bit LDS byte offsets computed from lds_base() of the kernel's own __shared__
+// array: taking a generic pointer back to the LDS address space would cost a null check and a
+// v_readfirstlane per load.
+// The compiler cannot see the load inside the asm, so it does not insert the wait states the
+// hardware needs before it: one after a scalar write of M0 (the compiler sets M0 right before
+// the asm), and five after a VALU write (v_readfirstlane, v_readlane restoring a spilled scalar)
+// of an SGPR the load reads (the buffer descriptor or the scalar offset). Without them the load
+// can use the previous M0 or a stale offset and fill the wrong tile; s_nop 4 gives five.
+template <typename T>
+__device__ inline uint32_t lds_base(T& shared_array) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)(&shared_array);
 }
 
-// ASM = false keeps the builtin where the wait costs nothing measurable: loops that compute for
-// long enough between a DMA and their first transposed read (the backward's S and dP products,
-// the unpipelined D = 256 forward), where the asm form only adds scalar registers (spills at
-// D = 256). One kernel uses one form only, since with the builtin the compiler assumes M0 keeps
-// the value it set.
-template <bool ASM = true>
+__device__ inline void dma16_at(__amdgpu_buffer_rsrc_t rs, uint32_t lds, uint32_t voff,
+                                uint32_t soff) {
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rs), "s"(soff), "{m0}"(lds) : "memory");
+}
+
+__device__ inline void dma4_at(__amdgpu_buffer_rsrc_t rs, uint32_t lds, uint32_t voff,
+                               uint32_t soff) {
+  asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rs), "s"(soff), "{m0}"(lds) : "memory");
+}
+
+// The builtin form, for loops that compute long enough between a DMA and their first transposed
+// read (the backward's S and dP products, the unpipelined D = 256 forward) that its wait costs
+// nothing measurable.
 __device__ inline void dma16(__amdgpu_buffer_rsrc_t rs, unsigned char* lds, uint32_t voff,
                              uint32_t soff) {
-  if constexpr (ASM)
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 :: "s"(lds_addr(lds)), "v"(voff), "s"(rs), "s"(soff) : "memory");
-  else
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds, 16, voff, soff, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds, 16, voff, soff, 0, 0);
 }
 
-template <bool ASM = true>
 __device__ inline void dma4(__amdgpu_buffer_rsrc_t rs, unsigned char* lds, uint32_t voff,
                             uint32_t soff) {
-  if constexpr (ASM)
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
-                 :: "s"(lds_addr(lds)), "v"(voff), "s"(rs), "s"(soff) : "memory");
-  else
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds, 4, voff, soff, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds, 4, voff, soff, 0, 0);
 }
 
 // Per-wave, per-thread state of the main loop (registers).
@@ -344,7 +353,7 @@ struct F32BwdParams {
   float mscale;      // log2(e) / c: an additive mask value in raw score units
 };
 
-// Queue the fp32 backward (dQ kernel, then dK/dV kernel) for D in {16, 32, 64, 128} and
+// Queue the fp32 backward (dQ kernel, then dK/dV kernel) for D in {16, 32, 64, 128, 256} and
 // mask_type an attn_mask_t.
 hipError_t launch_bwd_f32(const F32BwdParams& p, int D, bool causal, int mask_type,
                           hipStream_t stream);

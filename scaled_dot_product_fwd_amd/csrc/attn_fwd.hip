@@ -179,14 +179,25 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
   const int bh = b * p.Hq + hq;
   const int kvh = hq / p.group;
   const int q0 = qt * kBM;
+  const int qa = q0 + wave * 32;            // first query of this wave
+  const int qrow = qa + ql;
+
+  // ---- Q fragments: B operand of S^T = K Q^T. Lane l holds Q[row][16s + 8h .. +7]. Rows past
+  // N read row N-1 (in bounds; their outputs are never stored). Issued first, so that their
+  // latency from HBM overlaps the rest of the set-up; the sign/zero masks are applied after the
+  // prologue's wait.
+  const uint16_t* __restrict__ qsrc =
+      p.q + b * p.qs_b + hq * p.qs_h + min(qrow, p.N - 1) * p.qs_n + 8 * h;
+  u32x4 qf[KSTEPS];
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s)
+    qf[s] = (DCH < G::CH && 2 * s + h >= DCH) ? u32x4{} : *(const u32x4*)(qsrc + 16 * s);
 
   int kv_end = p.N;
   if (p.valid_len) kv_end = min(max(p.valid_len[b], 0), p.N);
   int kv_stop = kv_end;
   if (CAUSAL) kv_stop = min(kv_stop, q0 + kBM);
   const int ntiles = (kv_stop + kBN - 1) / kBN;
-  const int qa = q0 + wave * 32;            // first query of this wave
-  const int qrow = qa + ql;
 
   // K and V of this (batch, KV head) as buffers spanning exactly its N rows: rows past N read
   // as zeros. Row strides in bytes (the host keeps every span below 2^31 bytes).
@@ -221,15 +232,23 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
     const int gc = (lane % G::CH) ^ G::vswz(row);
     voff[i] = (DCH < G::CH && gc >= DCH) ? kNoChunk : row * vrow + gc * 16;
   }
+  // D <= 128 issues the DMA through inline asm at scalar LDS addresses; D = 256 keeps the
+  // builtin (its unpipelined loop reads no V before computing the scores).
+  const uint32_t sbase = lds_base(smem);
+  auto dma_one = [&](__amdgpu_buffer_rsrc_t rs, int dst, uint32_t voff_, uint32_t soff) {
+    if constexpr (D <= 128)
+      dma16_at(rs, sbase + (uint32_t)dst, voff_, soff);
+    else
+      dma16(rs, smem + dst, voff_, soff);
+  };
   auto dma = [&](int tile, int kdst, int vdst) {
     const uint32_t row0 = (uint32_t)tile * kBN;
 #pragma unroll
     for (int i = 0; i < G::LOADS; ++i) {
       const int blk = (wave * G::LOADS + i) * 1024;
-      if (kdst >= 0) dma16<(D <= 128)>(krs, smem + kdst + blk, koff[i], row0 * krow);
+      if (kdst >= 0) dma_one(krs, kdst + blk, koff[i], row0 * krow);
       if (vdst >= 0)
-        dma16<(D <= 128)>(vrs, smem + vdst + blk, voff[VSHARED ? 0 : i],
-              (row0 + (VSHARED ? i * G::RPB : 0)) * vrow);
+        dma_one(vrs, vdst + blk, voff[VSHARED ? 0 : i], (row0 + (VSHARED ? i * G::RPB : 0)) * vrow);
     }
   };
 
@@ -251,8 +270,8 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
     if constexpr (MK != kMaskNone) {
 #pragma unroll
       for (int i = 0; i < MG::LOADS; ++i)
-        dma16<(D <= 128)>(mrs, smem + MOFF + wave * MG::WB + i * 1024, moff,
-              (uint32_t)tile * MG::RB + (uint32_t)(i * MG::RPL) * mrow);
+        dma_one(mrs, MOFF + wave * MG::WB + i * 1024, moff,
+                (uint32_t)tile * MG::RB + (uint32_t)(i * MG::RPL) * mrow);
     }
   };
 
@@ -275,15 +294,6 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
                    8 * (jj & 1);
   }
 
-  // ---- Q fragments: B operand of S^T = K Q^T. Lane l holds Q[row][16s + 8h .. +7]. Rows past
-  // N read row N-1 (in bounds; their outputs are never stored). All loads are issued before
-  // any result is used (the sign/zero masks are applied after the prologue's wait).
-  const uint16_t* __restrict__ qsrc =
-      p.q + b * p.qs_b + hq * p.qs_h + min(qrow, p.N - 1) * p.qs_n + 8 * h;
-  u32x4 qf[KSTEPS];
-#pragma unroll
-  for (int s = 0; s < KSTEPS; ++s)
-    qf[s] = (DCH < G::CH && 2 * s + h >= DCH) ? u32x4{} : *(const u32x4*)(qsrc + 16 * s);
 
   f32x16 acc[OT];
 #pragma unroll
@@ -541,11 +551,31 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
       step(j, I0{}, T{}, sA, mxA, sB, mxB);
       step(j + 1, I1{}, T{}, sB, mxB, sA, mxA);
     }
+    // Under causal masking the last tile lies wholly above the diagonal of the waves whose last
+    // query comes before its first key (the first two waves of a 128-row tile that reaches the
+    // diagonal): its scores are all -inf and its softmax and P V add exactly nothing, so such a
+    // wave skips them (its scores are computed with the step before, whose single program
+    // keeps the register allocation intact). It still waits, joins the barrier and issues its
+    // share of the DMA, like every wave, in every step.
+    const bool skip_last = CAUSAL && (ntiles - 1) * kBN > qa + 31;
+    auto step_sync = [&](int jj, auto parity) {
+      constexpr int P = decltype(parity)::value;
+      wait_loads_and_lds();
+      __syncthreads();
+      if (jj + 2 < ntiles) dma(jj + 2, P ? G::K1 : G::K0, -1);
+      if (jj + 1 < ntiles) dma(jj + 1, -1, P ? G::V0 : G::V1);
+    };
     if (j + 1 < ntiles) {
       step(j, I0{}, T{}, sA, mxA, sB, mxB);
-      step(j + 1, I1{}, F{}, sB, mxB, sA, mxA);
+      if (skip_last)
+        step_sync(j + 1, I1{});
+      else
+        step(j + 1, I1{}, F{}, sB, mxB, sA, mxA);
     } else if (j < ntiles) {
-      step(j, I0{}, F{}, sA, mxA, sB, mxB);
+      if (skip_last)
+        step_sync(j, I0{});
+      else
+        step(j, I0{}, F{}, sA, mxA, sB, mxB);
     }
   }
 

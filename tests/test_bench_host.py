@@ -1,6 +1,10 @@
 """bench.py on the host: the one-GPU guard, and the committed rocprofv3 records it reads are
 those of the current kernel sources (bench.py reports HBM traffic only from counters taken on
-the source it runs)."""
+the sources it runs). Every record under profiles/ names the kind of kernel it covers and the
+fingerprint (bench.source_fingerprint) of that kernel's source, the shared device header and the
+C ABI header."""
+import glob
+import json
 import os
 import re
 import subprocess
@@ -9,6 +13,7 @@ import sys
 import bench
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PROFILES = os.path.join(ROOT, "profiles")
 
 
 def test_more_than_one_gpu_is_refused():
@@ -19,15 +24,45 @@ def test_more_than_one_gpu_is_refused():
     assert r.stdout == ""
 
 
+def test_fingerprint_covers_the_shared_headers(tmp_path, monkeypatch):
+    # Changing any of the three files changes the fingerprint.
+    for kind in bench.SOURCES:
+        fp = bench.source_fingerprint(kind)
+        assert re.fullmatch(r"[0-9a-f]{64}", fp)
+    assert bench.source_fingerprint("fwd") != bench.source_fingerprint("bwd")
+    csrc = tmp_path / "csrc"
+    inc = tmp_path / "include"
+    csrc.mkdir()
+    inc.mkdir()
+    for name in ("attn_fwd.hip", "attn_common.h"):
+        (csrc / name).write_bytes(open(os.path.join(bench.CSRC, name), "rb").read())
+    (inc / "attn.h").write_bytes(open(os.path.join(ROOT, "include", "attn.h"), "rb").read())
+    monkeypatch.setattr(bench, "CSRC", str(csrc))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    base = bench.source_fingerprint("fwd")
+    for path in (csrc / "attn_fwd.hip", csrc / "attn_common.h", inc / "attn.h"):
+        old = path.read_bytes()
+        path.write_bytes(old + b"\n")
+        assert bench.source_fingerprint("fwd") != base, path
+        path.write_bytes(old)
+    assert bench.source_fingerprint("fwd") == base
+
+
 def test_traffic_records_match_the_kernel_sources():
     assert bench.traffic_for("long_gqa") is not None
     assert bench.traffic_for("long_gqa", backward=True) is not None
 
 
-def test_kernel_trace_summaries_name_the_current_sources():
-    for md, src in (("attn_fwd_long_gqa_kernel_trace.md", bench.KERNEL_SRC),
-                    ("attn_bwd_long_gqa_kernel_trace.md", bench.KERNEL_SRC_BWD)):
-        text = open(os.path.join(ROOT, "profiles", md)).read()
-        m = re.search(r"sha256\s+([0-9a-f]{64})", text)
-        assert m, md
-        assert m.group(1) == bench.kernel_sha(src), md
+def test_every_profile_names_the_current_sources():
+    files = sorted(glob.glob(os.path.join(PROFILES, "*")))
+    assert files
+    for path in files:
+        text = open(path).read()
+        if path.endswith(".json"):
+            fps = [json.loads(text)["source_fingerprint"]]
+            fps = [(f["kind"], f["sha256"]) for f in fps]
+        else:
+            fps = re.findall(r"fingerprint \((\w+)\)\s+([0-9a-f]{64})", text)
+        assert fps, path
+        for kind, sha in fps:
+            assert sha == bench.source_fingerprint(kind), (path, kind)

@@ -490,3 +490,33 @@ def test_bwd_ws_validate(lib):
     # exactly the split's size uses the partial sums; one float less drops the split
     assert wcall(dq=after, n=base + 4 + 2 * 2 * 2 * 2 * 1000 * 128) == sdp.ATTN_ERR_ALIAS
     assert wcall(dq=after, n=base + 4 + 2 * 2 * 2 * 2 * 1000 * 128 - 1) == sdp.ATTN_OK
+
+
+# ---- the status strings describe what the entry points accept
+
+def test_status_strings_match_what_the_library_accepts(lib):
+    # The head-dimension string lists exactly the D the forward and the backward accept.
+    txt = sdp.attn_status_string(sdp.ATTN_ERR_HEAD_DIM)
+    listed = sorted(int(x) for x in re.findall(r"\b\d+\b", txt))
+    fwd_ok = [D for D in range(1, 513) if call(D=D) != sdp.ATTN_ERR_HEAD_DIM]
+    bwd_ok = [D for D in range(1, 513) if bcall(D=D) != sdp.ATTN_ERR_HEAD_DIM]
+    assert listed == fwd_ok == bwd_ok, (txt, fwd_ok, bwd_ok)
+    assert "backward" not in txt
+    # The dtype string names every dtype the entry points take, and no restriction remains:
+    # each dtype is accepted with an explicit keep or additive mask, forward and backward.
+    txt = sdp.attn_status_string(sdp.ATTN_ERR_DTYPE)
+    for name in ("ATTN_F16", "ATTN_BF16", "ATTN_F32"):
+        assert name in txt
+    assert "only" not in txt
+    M = 13 * GB
+    for dt in (sdp.ATTN_F16, sdp.ATTN_BF16, sdp.ATTN_F32):
+        for mt in (sdp.ATTN_MASK_KEEP_U8, sdp.ATTN_MASK_ADD):
+            st = sdp.attn_fwd_masked_validate(Q, None, K, None, V, None, O, None, L, 2, 8, 2,
+                                              1000, 128, 0.088, 1, VL, M, mt, [0, 0, 1008], dt)
+            assert st == sdp.ATTN_OK, (dt, mt, st)
+            st = sdp.attn_bwd_masked_validate(Q, None, K, None, V, None, O, None, 15 * GB, None,
+                                              L, 17 * GB, None, 19 * GB, None, 21 * GB, None,
+                                              23 * GB, 2, 8, 2, 1000, 128, 0.088, 1, VL, M, mt,
+                                              [0, 0, 1008], dt)
+            assert st == sdp.ATTN_OK, (dt, mt, st)
+    assert call(dtype=3) == sdp.ATTN_ERR_DTYPE
