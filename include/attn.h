@@ -78,7 +78,8 @@ typedef enum {
                                multiple of 16 bytes, rows are less than D elements apart, or
                                two output rows share memory; for a mask see attn_fwd_masked */
     ATTN_ERR_MASK = -9,     /* mask_type is not one of attn_mask_t */
-    ATTN_ERR_WORKSPACE = -10 /* attn_bwd_ws: ws_floats is below 2 * B * Hq * N */
+    ATTN_ERR_WORKSPACE = -10, /* attn_bwd_ws: ws_floats is below 2 * B * Hq * N */
+    ATTN_ERR_SCRATCH = -11  /* attn_bwd_scratch: 2 * B * Hq * N exceeds ATTN_SCRATCH_FLOATS */
 } attn_status_t;
 
 /* Explicit mask kinds of attn_fwd_masked. */
@@ -369,16 +370,47 @@ int attn_bwd_ws_validate(const void *q, const int64_t *q_strides, const void *k,
  */
 int64_t attn_bwd_workspace_floats(int B, int Hq, int Hkv, int N, int D);
 
+/*
+ * attn_bwd_scratch -- attn_bwd_ws without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). The workspace is a static device array of
+ * ATTN_SCRATCH_FLOATS float32 values inside the library: each device the library runs on holds
+ * its own copy (32 MiB) until the process ends; its address is looked up once per device, on
+ * the first call for a stream of that device. The call allocates nothing (no hipMalloc, no
+ * hipFree, no allocating library routine) and, like attn_bwd_ws, only queues kernels.
+ *
+ * Every call on one device shares that device's array and leaves its contents behind (Delta and
+ * the base-2 LSE of its last call, then scratch); nothing in it needs to start at zero. Calls
+ * that overlap in time on one device (several streams or host threads) race on the array: the
+ * caller orders them, e.g. by one stream.
+ *
+ *   all arguments  as in attn_bwd_ws (same layouts, masks, dtypes; ws is the static array and
+ *                  ws_floats is ATTN_SCRATCH_FLOATS, so small shapes still get the dK/dV split).
+ *   returns        ATTN_ERR_SCRATCH when 2 * B * Hq * N > ATTN_SCRATCH_FLOATS (the sizes need
+ *                  more workspace than the array holds: use attn_bwd_ws), ATTN_ERR_LAUNCH when
+ *                  the runtime cannot give the array's device address, else as attn_bwd_ws.
+ */
+#define ATTN_SCRATCH_FLOATS (1 << 23)
+int attn_bwd_scratch(const void *q, const int64_t *q_strides, const void *k,
+                     const int64_t *k_strides, const void *v, const int64_t *v_strides,
+                     const void *out, const int64_t *out_strides, const void *dout,
+                     const int64_t *dout_strides, const float *lse, void *dq,
+                     const int64_t *dq_strides, void *dk, const int64_t *dk_strides, void *dv,
+                     const int64_t *dv_strides, int B, int Hq, int Hkv, int N, int D,
+                     float scale, int causal, const int32_t *valid_len, const void *mask,
+                     int mask_type, const int64_t *mask_strides, int dtype, void *stream);
+
 /* attn_status_string -- a static, NUL-terminated description of a return code (never NULL);
  * the error codes and the failure modes they stand for are listed at attn_status_t (the
  * article's sections 5.2 and 6.2 on launch configuration and failure symptoms). */
 const char *attn_status_string(int status);
 
-/* attn_version -- the library's interface version, currently 12 (2 added attn_fwd_strided, 3
+/* attn_version -- the library's interface version, currently 13 (2 added attn_fwd_strided, 3
  * attn_fwd_masked, 4 attn_bwd, 5 attn_bwd_strided, 6 attn_bwd_masked, 7 ATTN_F32 in attn_bwd
  * and attn_bwd_strided, 8 attn_bwd_ws and attn_bwd_workspace_floats, 9 lowered ATTN_MAX_TILES
  * to what one launch can hold, 10 ATTN_F32 in attn_fwd_masked, 11 ATTN_F32 with a mask in
- * attn_bwd_masked and attn_bwd_ws, 12 ATTN_F32 at D = 256 in the backward). */
+ * attn_bwd_masked and attn_bwd_ws, 12 ATTN_F32 at D = 256 in the backward, 13
+ * attn_bwd_scratch). */
 int attn_version(void);
 
 #ifdef __cplusplus

@@ -26,7 +26,8 @@ __all__ = ["ATTN_F16", "ATTN_BF16", "ATTN_F32", "AttnError", "attn_fwd", "attn_f
            "attn_fwd_strided", "attn_fwd_strided_validate", "attn_fwd_masked",
            "attn_fwd_masked_validate", "attn_bwd", "attn_bwd_validate", "attn_bwd_strided",
            "attn_bwd_strided_validate", "attn_bwd_masked", "attn_bwd_masked_validate",
-           "attn_bwd_ws", "attn_bwd_ws_validate", "attn_bwd_workspace_floats", "attention",
+           "attn_bwd_ws", "attn_bwd_ws_validate", "attn_bwd_workspace_floats",
+           "attn_bwd_scratch", "ATTN_SCRATCH_FLOATS", "attention",
            "backward", "attn_status_string",
            "attn_version", "forward", "library_path", "load_library"]
 
@@ -45,6 +46,9 @@ ATTN_ERR_ALIAS = -7
 ATTN_ERR_LAYOUT = -8
 ATTN_ERR_MASK = -9
 ATTN_ERR_WORKSPACE = -10
+ATTN_ERR_SCRATCH = -11
+
+ATTN_SCRATCH_FLOATS = 1 << 23   # float32 values of attn_bwd_scratch's static device workspace
 
 ATTN_MASK_NONE = 0
 ATTN_MASK_KEEP_U8 = 1
@@ -128,6 +132,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_bwd_ws_validate.argtypes = ([_vp, _i64p] * 5 + [_vp] + [_vp, _i64p] * 3 +
                                          [_vp, ctypes.c_int64] + [_c_int] * 5 +
                                          [_c_float, _c_int, _vp, _vp, _c_int, _i64p, _c_int])
+    lib.attn_bwd_scratch.restype = _c_int
+    lib.attn_bwd_scratch.argtypes = ([_vp, _i64p] * 5 + [_vp] + [_vp, _i64p] * 3 + [_c_int] * 5
+                                     + [_c_float, _c_int, _vp, _vp, _c_int, _i64p, _c_int, _vp])
     lib.attn_bwd_workspace_floats.restype = ctypes.c_int64
     lib.attn_bwd_workspace_floats.argtypes = [_c_int] * 5
     lib.attn_status_string.restype = ctypes.c_char_p
@@ -292,6 +299,19 @@ def attn_bwd_ws_validate(q, q_strides, k, k_strides, v, v_strides, out, out_stri
         _strides(out_strides), dout, _strides(dout_strides), lse, dq, _strides(dq_strides), dk,
         _strides(dk_strides), dv, _strides(dv_strides), ws, ws_floats, B, Hq, Hkv, N, D, scale,
         int(causal), valid_len, mask, mask_type, _strides(mask_strides), dtype)
+
+
+def attn_bwd_scratch(q, q_strides, k, k_strides, v, v_strides, out, out_strides, dout,
+                     dout_strides, lse, dq, dq_strides, dk, dk_strides, dv, dv_strides, B, Hq,
+                     Hkv, N, D, scale, causal, valid_len, mask, mask_type, mask_strides, dtype,
+                     stream) -> int:
+    """C ``attn_bwd_scratch``: attn_bwd_ws on the library's static device workspace (no
+    allocation); pointers as integers, strides as 3-sequences or None."""
+    return load_library().attn_bwd_scratch(
+        q, _strides(q_strides), k, _strides(k_strides), v, _strides(v_strides), out,
+        _strides(out_strides), dout, _strides(dout_strides), lse, dq, _strides(dq_strides), dk,
+        _strides(dk_strides), dv, _strides(dv_strides), B, Hq, Hkv, N, D, scale, int(causal),
+        valid_len, mask, mask_type, _strides(mask_strides), dtype, stream)
 
 
 def attn_bwd_workspace_floats(B: int, Hq: int, Hkv: int, N: int, D: int) -> int:

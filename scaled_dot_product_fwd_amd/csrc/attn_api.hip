@@ -22,8 +22,11 @@ extern "C" const char* attn_status_string(int status) {
              "bytes, rows at least D elements apart, and output rows distinct";
     case ATTN_ERR_MASK: return "unknown mask type";
     case ATTN_ERR_WORKSPACE: return "the workspace holds fewer than 2 * B * Hq * N floats";
+    case ATTN_ERR_SCRATCH:
+      return "the sizes need more than the library's static workspace: 2 * B * Hq * N must be "
+             "at most ATTN_SCRATCH_FLOATS (8388608) floats; use attn_bwd_ws";
     default: return "unknown status";
   }
 }
 
-extern "C" int attn_version(void) { return 12; }
+extern "C" int attn_version(void) { return 13; }

@@ -34,6 +34,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "attn.h"
@@ -1129,6 +1130,47 @@ int bwd_run(const BwdLayouts& t, const float* lse, float* ws, int64_t ws_floats,
 
 }  // namespace
 
+// Workspace of attn_bwd_scratch, for callers that cannot allocate: a static device array of
+// ATTN_SCRATCH_FLOATS floats that each device running this library holds until the process
+// ends. Host code never passes `scratch` itself (on the host it names a stand-in, not device
+// memory); it uses the device address scratch_ptr looks up once per device.
+static __device__ __align__(256) float scratch[ATTN_SCRATCH_FLOATS];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch[kMaxDevices];   // device address of `scratch` per device ordinal
+
+// The device address of `scratch` on the device `stream` belongs to (the current device for the
+// null stream), looked up with hipGetSymbolAddress once per device while that device is
+// current. nullptr when the runtime reports an error or the ordinal is beyond kMaxDevices.
+float* scratch_ptr(hipStream_t stream) {
+  int dev = -1;
+  if (stream) {
+    hipDevice_t d;
+    if (hipStreamGetDevice(stream, &d) != hipSuccess) return nullptr;
+    dev = (int)d;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !ptr) return nullptr;
+    g_scratch[dev] = (float*)ptr;
+  }
+  return g_scratch[dev];
+}
+
+}  // namespace
+
 extern "C" int attn_bwd_validate(const void* q, const void* k, const void* v, const void* out,
                                  const void* dout, const float* lse, const void* dq,
                                  const void* dk, const void* dv, const float* ws, int B,
@@ -1245,4 +1287,23 @@ extern "C" int attn_bwd_ws(
                              Hkv, N, D),
                  lse, ws, ws_floats, B, Hq, Hkv, N, D, scale, causal, valid_len, dtype, stream,
                  mask_arg(mask, mask_type, mask_strides, N));
+}
+
+extern "C" int attn_bwd_scratch(
+    const void* q, const int64_t* q_strides, const void* k, const int64_t* k_strides,
+    const void* v, const int64_t* v_strides, const void* out, const int64_t* out_strides,
+    const void* dout, const int64_t* dout_strides, const float* lse, void* dq,
+    const int64_t* dq_strides, void* dk, const int64_t* dk_strides, void* dv,
+    const int64_t* dv_strides, int B, int Hq, int Hkv, int N, int D, float scale, int causal,
+    const int32_t* valid_len, const void* mask, int mask_type, const int64_t* mask_strides,
+    int dtype, void* stream) {
+  if (B >= 1 && Hq >= 1 && N >= 1 && ws_base_floats(B, Hq, N) > ATTN_SCRATCH_FLOATS)
+    return ATTN_ERR_SCRATCH;
+  float* const ws = scratch_ptr((hipStream_t)stream);
+  if (!ws) return ATTN_ERR_LAUNCH;
+  return bwd_run(bwd_layouts(q, q_strides, k, k_strides, v, v_strides, out, out_strides, dout,
+                             dout_strides, dq, dq_strides, dk, dk_strides, dv, dv_strides, Hq,
+                             Hkv, N, D),
+                 lse, ws, ATTN_SCRATCH_FLOATS, B, Hq, Hkv, N, D, scale, causal, valid_len, dtype,
+                 stream, mask_arg(mask, mask_type, mask_strides, N));
 }

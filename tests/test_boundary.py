@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["attn_bwd", "attn_bwd_masked", "attn_bwd_masked_validate",
-                                    "attn_bwd_strided", "attn_bwd_strided_validate",
+                                    "attn_bwd_scratch", "attn_bwd_strided", "attn_bwd_strided_validate",
                                     "attn_bwd_validate", "attn_bwd_workspace_floats",
                                     "attn_bwd_ws", "attn_bwd_ws_validate", "attn_fwd",
                                     "attn_fwd_masked", "attn_fwd_masked_validate",
@@ -46,13 +46,14 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_version(lib):
-    assert sdp.attn_version() == 12
+    assert sdp.attn_version() == 13
 
 
 def test_status_strings(lib):
     codes = [sdp.ATTN_OK, sdp.ATTN_ERR_NULL, sdp.ATTN_ERR_SHAPE, sdp.ATTN_ERR_HEAD_DIM,
              sdp.ATTN_ERR_DTYPE, sdp.ATTN_ERR_SCALE, sdp.ATTN_ERR_LAUNCH, sdp.ATTN_ERR_ALIAS,
-             sdp.ATTN_ERR_LAYOUT, sdp.ATTN_ERR_MASK]
+             sdp.ATTN_ERR_LAYOUT, sdp.ATTN_ERR_MASK, sdp.ATTN_ERR_WORKSPACE,
+             sdp.ATTN_ERR_SCRATCH]
     texts = [sdp.attn_status_string(c) for c in codes]
     assert len(set(texts)) == len(texts)
     assert sdp.attn_status_string(12345) == "unknown status"
