@@ -37,6 +37,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -95,14 +96,22 @@ def effective_flops(w, valid_len) -> float:
     return 4.0 * w.D * w.Hq * total
 
 
+def code_only(text: bytes) -> bytes:
+    """C/C++ source without its comments, every run of white space one blank: what the compiler
+    sees, so that an edit of comments or layout keeps a profile current."""
+    out = re.sub(rb"/\*.*?\*/|//[^\n]*", b" ", text, flags=re.S)
+    return re.sub(rb"\s+", b" ", out).strip()
+
+
 def source_fingerprint(kind: str) -> str:
-    """sha256 over the names and contents of the sources a kind of kernel is built from."""
+    """sha256 over the names and code (comments and layout removed) of the sources a kind of
+    kernel is built from."""
     h = hashlib.sha256()
     for name in SOURCES[kind]:
         path = os.path.join(ROOT, "include", name) if name.endswith("attn.h") else \
             os.path.join(CSRC, name)
         with open(path, "rb") as f:
-            data = f.read()
+            data = code_only(f.read())
         h.update(name.encode() + b"\0" + str(len(data)).encode() + b"\0" + data)
     return h.hexdigest()
 

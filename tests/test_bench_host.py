@@ -25,7 +25,6 @@ def test_more_than_one_gpu_is_refused():
 
 
 def test_fingerprint_covers_the_shared_headers(tmp_path, monkeypatch):
-    # Changing any of the three files changes the fingerprint.
     for kind in bench.SOURCES:
         fp = bench.source_fingerprint(kind)
         assert re.fullmatch(r"[0-9a-f]{64}", fp)
@@ -42,10 +41,20 @@ def test_fingerprint_covers_the_shared_headers(tmp_path, monkeypatch):
     base = bench.source_fingerprint("fwd")
     for path in (csrc / "attn_fwd.hip", csrc / "attn_common.h", inc / "attn.h"):
         old = path.read_bytes()
-        path.write_bytes(old + b"\n")
+        # a code change in any of the three files changes it ...
+        path.write_bytes(old + b"\nstatic const int fingerprint_probe = 1;\n")
         assert bench.source_fingerprint("fwd") != base, path
+        # ... an edit of comments or blank space does not
+        path.write_bytes(b"/* a comment\n   on two lines */\n" + old.replace(b"\n", b"\n\n") +
+                         b"\n// another\n")
+        assert bench.source_fingerprint("fwd") == base, path
         path.write_bytes(old)
     assert bench.source_fingerprint("fwd") == base
+
+
+def test_code_only_strips_comments_and_layout():
+    src = b"int a; /* x\n y */ int  b;  // z\n\tint c;\n"
+    assert bench.code_only(src) == b"int a; int b; int c;"
 
 
 def test_traffic_records_match_the_kernel_sources():
