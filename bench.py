@@ -214,6 +214,8 @@ def main():
                     help="replace the workload's head dimension")
     ap.add_argument("--backward", action="store_true",
                     help="time attn_bwd (dQ, dK, dV) instead of the forward")
+    ap.add_argument("--no-split", action="store_true",
+                    help="keep small grids on one workgroup per query tile (no attn_fwd_ws)")
     ap.add_argument("--log-launches", action="store_true",
                     help="also print every timed launch's time (ms) to stderr")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -270,9 +272,17 @@ def main():
         else:
             amask = (-dist.float() / 256.0).to(tdt)
 
+    # grids too small to fill the device split their key ranges (attn_fwd_ws) into a workspace
+    # allocated here, once
+    split = not args.no_split and amask is None and w.dtype != "f32"
+    n_ws = sdp.attn_fwd_workspace_floats(w.B, w.Hq, w.Hkv, w.N, w.D, w.causal) if split else 0
+    fws = torch.empty((n_ws,), dtype=torch.float32, device="cuda") if n_ws > 0 else None
+    if n_ws > 0:
+        log("key ranges split over workgroups (attn_fwd_ws, %d workspace floats)" % n_ws)
+
     def step():
         sdp.forward(q, k, v, causal=w.causal, valid_len=vl, scale=w.scale, out=out, lse=lse,
-                    stream=stream, layout=args.layout, attn_mask=amask)
+                    stream=stream, layout=args.layout, attn_mask=amask, ws=fws, split=split)
 
     if args.backward:
         dout_bits = inputs.make_grad(case, [w.c])
@@ -351,6 +361,7 @@ def main():
                    "causal": w.causal, "padded": w.padded, "scale": w.scale,
                    "layout": args.layout, "explicit_mask": args.mask,
                    "pass": "backward" if args.backward else "forward",
+                   "key_split": bool(n_ws > 0) and not args.backward,
                    "flops_per_step": f,
                    "effective_flops_per_step": (
                        (2.5 if args.backward else 1.0) * effective_flops(w, case.valid_len)

@@ -38,8 +38,9 @@
  * for the same inputs and shapes.
  *
  * Threading: every call is independent and the library keeps no state between calls except
- * compiled kernels; calls on different streams may run concurrently. The library allocates no
- * memory.
+ * compiled kernels and the static device workspace of attn_bwd_scratch; calls on different
+ * streams may run concurrently (attn_bwd_scratch calls excepted, see there). The library
+ * allocates no memory.
  */
 #ifndef ATTN_H
 #define ATTN_H
@@ -78,7 +79,8 @@ typedef enum {
                                multiple of 16 bytes, rows are less than D elements apart, or
                                two output rows share memory; for a mask see attn_fwd_masked */
     ATTN_ERR_MASK = -9,     /* mask_type is not one of attn_mask_t */
-    ATTN_ERR_WORKSPACE = -10, /* attn_bwd_ws: ws_floats is below 2 * B * Hq * N */
+    ATTN_ERR_WORKSPACE = -10, /* attn_bwd_ws: ws_floats is below 2 * B * Hq * N; attn_fwd_ws:
+                                 ws_floats is negative */
     ATTN_ERR_SCRATCH = -11  /* attn_bwd_scratch: 2 * B * Hq * N exceeds ATTN_SCRATCH_FLOATS */
 } attn_status_t;
 
@@ -224,6 +226,60 @@ int attn_fwd_masked_validate(const void *q, const int64_t *q_strides, const void
                              int B, int Hq, int Hkv, int N, int D, float scale, int causal,
                              const int32_t *valid_len, const void *mask, int mask_type,
                              const int64_t *mask_strides, int dtype);
+
+/*
+ * attn_fwd_ws -- attn_fwd_strided with a caller-owned workspace, for grids that leave the
+ * device idle. With few (batch, query head, 128-row query tile) items over long key ranges, one
+ * workgroup per query tile leaves CUs idle and the call lasts as long as its longest tile's key
+ * loop. When the items fill at most a quarter of what the device runs at once (128 workgroups
+ * up to D = 128, 64 at D = 256) and the longest key range holds at least 48 key tiles of 64
+ * (3072 keys), the key range of every query tile is cut into chunks of equal numbers of key
+ * tiles (the smallest chunk for which all chunks still run at once, 512 workgroups up to
+ * D = 128 and 256 at D = 256, and whose partial results the workspace holds);
+ * one workgroup per chunk writes the chunk's fp32 output, normalised by its own sum, and its
+ * log-sum-exp, and a second kernel combines the chunks of every row:
+ *
+ *     M = max_c L_c,   O = sum_c 2^(L_c - M) O_c / sum_c 2^(L_c - M),   L = M + log2 sum_c 2^(L_c - M)
+ *
+ * (L in base 2). Below those bounds a call's time is mostly fixed costs (launch, prologue,
+ * epilogue) that a split only adds to, and the call runs as attn_fwd_strided. This is the
+ * online-softmax update of "Triton Cuda Attention" (section on the
+ * online softmax core algorithm) applied to whole chunks instead of single tiles, and the
+ * reason tiny_flash_attn_triton.py keeps the per-row log-sum-exp L. The pages' own Triton
+ * kernel fills the device with 64-row query blocks over a (cdiv(L, 64), B * H) grid
+ * ("Triton Cuda Attention", complete example); splitting the key range instead keeps the
+ * 128-row tiles and shortens the longest workgroup.
+ *
+ *   ws, ws_floats  device float32 workspace of ws_floats values, 16-byte aligned, owned by the
+ *                  caller (scratch: nothing is left in it for the caller). NULL, too small for
+ *                  any split, or a grid that fills the device: the call is attn_fwd_strided.
+ *                  ws_floats < 0 is ATTN_ERR_WORKSPACE; a used part that overlaps an input or
+ *                  output is ATTN_ERR_ALIAS.
+ *   others         as in attn_fwd_strided (16-bit dtypes split; ATTN_F32 never splits and
+ *                  ignores ws).
+ *
+ * Fully masked rows (valid_len 0) still give O = 0 and LSE = -inf; rows are combined in a fixed
+ * order, so results are deterministic, but they differ from attn_fwd_strided's by rounding.
+ */
+int attn_fwd_ws(const void *q, const int64_t *q_strides, const void *k, const int64_t *k_strides,
+                const void *v, const int64_t *v_strides, void *out, const int64_t *out_strides,
+                float *lse, float *ws, int64_t ws_floats, int B, int Hq, int Hkv, int N, int D,
+                float scale, int causal, const int32_t *valid_len, int dtype, void *stream);
+
+/* attn_fwd_ws_validate -- the host-only argument check of attn_fwd_ws. */
+int attn_fwd_ws_validate(const void *q, const int64_t *q_strides, const void *k,
+                         const int64_t *k_strides, const void *v, const int64_t *v_strides,
+                         const void *out, const int64_t *out_strides, const float *lse,
+                         const float *ws, int64_t ws_floats, int B, int Hq, int Hkv, int N, int D,
+                         float scale, int causal, const int32_t *valid_len, int dtype);
+
+/*
+ * attn_fwd_workspace_floats -- the workspace size (float32 values) with which attn_fwd_ws
+ * splits the key ranges of these sizes as far as it would (B * Hq * ceil(N / 128) * nchunk
+ * query tiles of 128 rows, D + 1 values each, plus 4); 0 when the grid fills the device and no
+ * split helps; -1 when a size is below 1. Host only.
+ */
+int64_t attn_fwd_workspace_floats(int B, int Hq, int Hkv, int N, int D, int causal);
 
 /*
  * attn_bwd -- gradients of the attn_fwd output with respect to Q, K and V (contiguous tensors,
@@ -405,12 +461,12 @@ int attn_bwd_scratch(const void *q, const int64_t *q_strides, const void *k,
  * article's sections 5.2 and 6.2 on launch configuration and failure symptoms). */
 const char *attn_status_string(int status);
 
-/* attn_version -- the library's interface version, currently 13 (2 added attn_fwd_strided, 3
+/* attn_version -- the library's interface version, currently 14 (2 added attn_fwd_strided, 3
  * attn_fwd_masked, 4 attn_bwd, 5 attn_bwd_strided, 6 attn_bwd_masked, 7 ATTN_F32 in attn_bwd
  * and attn_bwd_strided, 8 attn_bwd_ws and attn_bwd_workspace_floats, 9 lowered ATTN_MAX_TILES
  * to what one launch can hold, 10 ATTN_F32 in attn_fwd_masked, 11 ATTN_F32 with a mask in
  * attn_bwd_masked and attn_bwd_ws, 12 ATTN_F32 at D = 256 in the backward, 13
- * attn_bwd_scratch). */
+ * attn_bwd_scratch, 14 attn_fwd_ws, attn_fwd_ws_validate and attn_fwd_workspace_floats). */
 int attn_version(void);
 
 #ifdef __cplusplus

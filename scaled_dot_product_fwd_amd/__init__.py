@@ -24,7 +24,8 @@ from typing import Optional, Tuple
 
 __all__ = ["ATTN_F16", "ATTN_BF16", "ATTN_F32", "AttnError", "attn_fwd", "attn_fwd_validate",
            "attn_fwd_strided", "attn_fwd_strided_validate", "attn_fwd_masked",
-           "attn_fwd_masked_validate", "attn_bwd", "attn_bwd_validate", "attn_bwd_strided",
+           "attn_fwd_masked_validate", "attn_fwd_ws", "attn_fwd_ws_validate",
+           "attn_fwd_workspace_floats", "attn_bwd", "attn_bwd_validate", "attn_bwd_strided",
            "attn_bwd_strided_validate", "attn_bwd_masked", "attn_bwd_masked_validate",
            "attn_bwd_ws", "attn_bwd_ws_validate", "attn_bwd_workspace_floats",
            "attn_bwd_scratch", "ATTN_SCRATCH_FLOATS", "attention",
@@ -105,6 +106,14 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_fwd_masked_validate.argtypes = [_vp, _i64p, _vp, _i64p, _vp, _i64p, _vp, _i64p,
                                              _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                                              _c_float, _c_int, _vp, _vp, _c_int, _i64p, _c_int]
+    lib.attn_fwd_ws.restype = _c_int
+    lib.attn_fwd_ws.argtypes = ([_vp, _i64p] * 4 + [_vp, _vp, ctypes.c_int64] + [_c_int] * 5 +
+                                [_c_float, _c_int, _vp, _c_int, _vp])
+    lib.attn_fwd_ws_validate.restype = _c_int
+    lib.attn_fwd_ws_validate.argtypes = ([_vp, _i64p] * 4 + [_vp, _vp, ctypes.c_int64] +
+                                         [_c_int] * 5 + [_c_float, _c_int, _vp, _c_int])
+    lib.attn_fwd_workspace_floats.restype = ctypes.c_int64
+    lib.attn_fwd_workspace_floats.argtypes = [_c_int] * 6
     lib.attn_bwd.restype = _c_int
     lib.attn_bwd.argtypes = [_vp] * 10 + [_c_int] * 5 + [_c_float, _c_int, _vp, _c_int, _vp]
     lib.attn_bwd_validate.restype = _c_int
@@ -213,6 +222,34 @@ def attn_fwd_masked_validate(q: int, q_strides, k: int, k_strides, v: int, v_str
         q, _strides(q_strides), k, _strides(k_strides), v, _strides(v_strides), out,
         _strides(out_strides), lse, B, Hq, Hkv, N, D, scale, int(causal), valid_len, mask,
         mask_type, _strides(mask_strides), dtype)
+
+
+def attn_fwd_ws(q: int, q_strides, k: int, k_strides, v: int, v_strides, out: int, out_strides,
+                lse: Optional[int], ws: Optional[int], ws_floats: int, B: int, Hq: int, Hkv: int,
+                N: int, D: int, scale: float, causal: bool, valid_len: Optional[int], dtype: int,
+                stream: Optional[int]) -> int:
+    """C ``attn_fwd_ws``; pointers as integers, strides as 3-sequences or None."""
+    return load_library().attn_fwd_ws(
+        q, _strides(q_strides), k, _strides(k_strides), v, _strides(v_strides), out,
+        _strides(out_strides), lse, ws, ws_floats, B, Hq, Hkv, N, D, scale, int(causal),
+        valid_len, dtype, stream)
+
+
+def attn_fwd_ws_validate(q: int, q_strides, k: int, k_strides, v: int, v_strides, out: int,
+                         out_strides, lse: Optional[int], ws: Optional[int], ws_floats: int,
+                         B: int, Hq: int, Hkv: int, N: int, D: int, scale: float, causal: bool,
+                         valid_len: Optional[int], dtype: int) -> int:
+    """C ``attn_fwd_ws_validate``: host-only argument check, no HIP call."""
+    return load_library().attn_fwd_ws_validate(
+        q, _strides(q_strides), k, _strides(k_strides), v, _strides(v_strides), out,
+        _strides(out_strides), lse, ws, ws_floats, B, Hq, Hkv, N, D, scale, int(causal),
+        valid_len, dtype)
+
+
+def attn_fwd_workspace_floats(B: int, Hq: int, Hkv: int, N: int, D: int, causal: bool) -> int:
+    """C ``attn_fwd_workspace_floats``: float32 values of the workspace attn_fwd_ws splits with
+    (0: these sizes fill the device, no split)."""
+    return load_library().attn_fwd_workspace_floats(B, Hq, Hkv, N, D, int(bool(causal)))
 
 
 def attn_bwd(q: int, k: int, v: int, out: int, dout: int, lse: int, dq: int, dk: int, dv: int,
@@ -367,7 +404,7 @@ def _mask_view(attn_mask, dtype, B, Hq, N):
 
 def forward(q, k, v, causal: bool, valid_len=None, scale: Optional[float] = None, out=None,
             lse=None, want_lse: bool = True, stream=None, layout: str = "bhnd",
-            attn_mask=None) -> Tuple[object, Optional[object]]:
+            attn_mask=None, ws=None, split: bool = True) -> Tuple[object, Optional[object]]:
     """Run the attention forward on torch device tensors on the current (or given) stream.
 
     ``layout`` names the order of the four dimensions of q, k, v and out: "bhnd" for
@@ -381,6 +418,11 @@ def forward(q, k, v, causal: bool, valid_len=None, scale: Optional[float] = None
     dtype is added to the scaled score. Its key dimension must be contiguous and its rows
     16-byte aligned (for a ragged N, a [.., N, Npad] view of a padded tensor works). It
     combines with ``causal`` and ``valid_len``; the call then goes to attn_fwd_masked.
+
+    Without a mask, sizes whose query tiles do not fill the device (attn_fwd_workspace_floats
+    > 0, 16-bit dtypes) go to attn_fwd_ws, which splits the key ranges; ``ws`` is then its
+    float32 workspace (allocated with torch when not given). ``split=False`` keeps them on
+    attn_fwd / attn_fwd_strided (one workgroup per query tile).
 
     Allocates ``out`` (q's shape, layout and dtype, contiguous) and ``lse`` ([B, Hq, N] float32)
     with torch when they are not given. Returns (out, lse); lse is None when want_lse is False
@@ -435,7 +477,20 @@ def forward(q, k, v, causal: bool, valid_len=None, scale: Optional[float] = None
         if st != ATTN_OK:
             raise AttnError(st, "attn_fwd_masked")
         return out, lse
-    if all(t.is_contiguous() for t in (qv, kv, vv, ov)):
+    n_ws = 0
+    if split and q.dtype != torch.float32:
+        n_ws = attn_fwd_workspace_floats(B, Hq, Hkv, N, D, causal)
+    if n_ws > 0:
+        if ws is None:
+            ws = torch.empty((n_ws,), dtype=torch.float32, device=q.device)
+        if ws.dtype != torch.float32 or not ws.is_contiguous() or not ws.is_cuda:
+            raise ValueError("ws must be a contiguous float32 device tensor")
+        st = attn_fwd_ws(qv.data_ptr(), qv.stride()[:3], kv.data_ptr(), kv.stride()[:3],
+                         vv.data_ptr(), vv.stride()[:3], ov.data_ptr(), ov.stride()[:3], lse_ptr,
+                         ws.data_ptr(), ws.numel(), B, Hq, Hkv, N, D, float(scale),
+                         int(bool(causal)), vl_ptr, _dtype_code(q), stream.cuda_stream)
+        where = "attn_fwd_ws"
+    elif all(t.is_contiguous() for t in (qv, kv, vv, ov)):
         st = attn_fwd(qv.data_ptr(), kv.data_ptr(), vv.data_ptr(), ov.data_ptr(), lse_ptr, B, Hq,
                       Hkv, N, D, float(scale), int(bool(causal)), vl_ptr, _dtype_code(q),
                       stream.cuda_stream)

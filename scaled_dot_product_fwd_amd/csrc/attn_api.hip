@@ -21,7 +21,9 @@ extern "C" const char* attn_status_string(int status) {
       return "bad layout: pointers must be 16-byte aligned, strides non-negative multiples of 16 "
              "bytes, rows at least D elements apart, and output rows distinct";
     case ATTN_ERR_MASK: return "unknown mask type";
-    case ATTN_ERR_WORKSPACE: return "the workspace holds fewer than 2 * B * Hq * N floats";
+    case ATTN_ERR_WORKSPACE:
+      return "bad workspace size: attn_bwd_ws needs at least 2 * B * Hq * N floats, attn_fwd_ws "
+             "a non-negative size";
     case ATTN_ERR_SCRATCH:
       return "the sizes need more than the library's static workspace: 2 * B * Hq * N must be "
              "at most ATTN_SCRATCH_FLOATS (8388608) floats; use attn_bwd_ws";
@@ -29,4 +31,4 @@ extern "C" const char* attn_status_string(int status) {
   }
 }
 
-extern "C" int attn_version(void) { return 13; }
+extern "C" int attn_version(void) { return 14; }

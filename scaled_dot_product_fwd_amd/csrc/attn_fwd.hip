@@ -47,6 +47,8 @@
 #include "attn.h"
 #include "attn_common.h"
 
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+
 namespace {
 
 using namespace attn_detail;
@@ -76,6 +78,13 @@ struct Params {
   float c;           // |scale| * log2(e)
   uint32_t qsign;    // 0x80008000 when scale < 0: Q is negated (exactly) instead
   uint32_t qmask;    // 0 when scale == 0: all scores are exactly 0 (and c is set to 1)
+  // Split of each query tile's key range (kernels with SPLIT): chunk c of a query tile covers
+  // key tiles [c * split_tiles, (c + 1) * split_tiles) of its range and writes its fp32 partial
+  // O (normalised by its own sum) and base-2 LSE for the merge kernel.
+  int split_tiles;
+  int nchunk;        // chunks per query tile (grid = B * Hq * nqt * nchunk)
+  float* part_o;     // [B * Hq * nqt * nchunk][kBM rows][DH]
+  float* part_lse;   // [B * Hq * nqt * nchunk][kBM rows]
 };
 
 template <int DT, int D>
@@ -134,7 +143,7 @@ __device__ inline void update_max(float mx, float c, float& m, float& l,
 // the missing 16-byte chunks of every row zero-filled (their lanes' loads are out of range) and
 // never stored: zero chunks add nothing to Q.K and give zero O columns. The work per score is
 // then that of D = 64, which is bound by the softmax's VALU work, not by the MFMAs.
-template <int DT, int DH, bool CAUSAL, int MK>
+template <int DT, int DH, bool CAUSAL, int MK, bool SPLIT>
 __device__ __forceinline__ void attn_fwd_body(const Params& p) {
   constexpr int D = DH < 64 ? 64 : DH;   // geometry
   constexpr int DCH = DH / 8;            // 16-byte chunks of a row that exist
@@ -153,8 +162,18 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
   const int ql = lane & 31;
 
   // ---- work decomposition
-  int qt, b, hq;
-  {
+  int qt, b, hq, chunk = 0;
+  if constexpr (SPLIT) {
+    // small grids: (batch, query head) major, longest query tiles first, chunks minor
+    const int wid = blockIdx.x;
+    const int rest = wid / p.nchunk;
+    chunk = wid - rest * p.nchunk;
+    const int bhh = rest / p.nqt;
+    const int qi = rest - bhh * p.nqt;
+    qt = CAUSAL ? p.nqt - 1 - qi : qi;
+    b = bhh / p.Hq;
+    hq = bhh - b * p.Hq;
+  } else {
     const int wid = blockIdx.x;
     if (p.xcd_order) {
       const int xcd = wid & 7;
@@ -198,6 +217,14 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
   int kv_stop = kv_end;
   if (CAUSAL) kv_stop = min(kv_stop, q0 + kBM);
   const int ntiles = (kv_stop + kBN - 1) / kBN;
+  // Key tiles [jb, je) of this workgroup: the whole range, or one chunk of it. A chunk that
+  // starts past the range has nothing to do (the merge kernel counts the same chunks).
+  int jb = 0, je = ntiles;
+  if constexpr (SPLIT) {
+    jb = chunk * p.split_tiles;
+    je = min(jb + p.split_tiles, ntiles);
+    if (jb >= je) return;
+  }
 
   // K and V of this (batch, KV head) as buffers spanning exactly its N rows: rows past N read
   // as zeros. Row strides in bytes (the host keeps every span below 2^31 bytes).
@@ -427,16 +454,16 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
   };
 
   // ---- prologue: K_0, V_0 (and, software-pipelined, K_1) in flight; scores of tile 0
-  if (ntiles > 0) dma(0, G::K0, G::V0);
-  if (D <= 128 && ntiles > 1) dma(1, G::K1, -1);
-  if (ntiles > 0) mask_dma(0);
+  if (je > jb) dma(jb, G::K0, G::V0);
+  if (D <= 128 && je > jb + 1) dma(jb + 1, G::K1, -1);
+  if (je > jb) mask_dma(jb);
   wait_loads_and_lds();
 #pragma unroll
   for (int s = 0; s < KSTEPS; ++s) qf[s] = (qf[s] ^ p.qsign) & p.qmask;
   __syncthreads();
   f32x16 sA[2], sB[2];
   float mxA = -INFINITY, mxB = -INFINITY;
-  if (D <= 128 && ntiles > 0) {
+  if (D <= 128 && je > jb) {
     qk_tile<DT, D>(sA, smem + G::K0, f, qf);
     mxA = rowmax(sA);
   }
@@ -467,7 +494,7 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
         }
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      if (j + 1 < ntiles) mask_dma(j + 1);
+      if (j + 1 < je) mask_dma(j + 1);
       int lim = kv_end - 1 - kb - 4 * h;
       if (CAUSAL) lim = min(lim, qrow - kb - 4 * h);
 #pragma unroll
@@ -518,8 +545,8 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
     wait_loads_and_lds();
     __syncthreads();
     // K_{j+2} replaces K_j (its scores were computed last iteration); V_{j+1} replaces V_{j-1}.
-    if (j + 2 < ntiles) dma(j + 2, KCUR, -1);
-    if (j + 1 < ntiles) dma(j + 1, -1, VNXT);
+    if (j + 2 < je) dma(j + 2, KCUR, -1);
+    if (j + 1 < je) dma(j + 1, -1, VNXT);
     mask_tile(cur, mxc, j * kBN, j);
     tile(has_next, cur, mxc, nxt, mxn, smem + KNXT, smem + VCUR);
   };
@@ -535,19 +562,19 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
       constexpr int P = decltype(parity)::value;
       wait_loads_and_lds();
       __syncthreads();
-      if (j + 1 < ntiles) dma(j + 1, P ? G::K0 : G::K1, P ? G::V0 : G::V1);
+      if (j + 1 < je) dma(j + 1, P ? G::K0 : G::K1, P ? G::V0 : G::V1);
       qk_tile<DT, D>(sA, smem + (P ? G::K1 : G::K0), f, qf);
       mxA = rowmax(sA);
       mask_tile(sA, mxA, j * kBN, j);
       tile(F{}, sA, mxA, sB, mxB, nullptr, smem + (P ? G::V1 : G::V0));
     };
-    for (int j = 0; j < ntiles; j += 2) {
+    for (int j = jb; j < je; j += 2) {
       step1(j, I0{});
-      if (j + 1 < ntiles) step1(j + 1, I1{});
+      if (j + 1 < je) step1(j + 1, I1{});
     }
   } else {
-    int j = 0;
-    for (; j + 2 < ntiles; j += 2) {
+    int j = jb;
+    for (; j + 2 < je; j += 2) {
       step(j, I0{}, T{}, sA, mxA, sB, mxB);
       step(j + 1, I1{}, T{}, sB, mxB, sA, mxA);
     }
@@ -557,21 +584,21 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
     // wave skips them (its scores are computed with the step before, whose single program
     // keeps the register allocation intact). It still waits, joins the barrier and issues its
     // share of the DMA, like every wave, in every step.
-    const bool skip_last = CAUSAL && (ntiles - 1) * kBN > qa + 31;
+    const bool skip_last = CAUSAL && (je - 1) * kBN > qa + 31;
     auto step_sync = [&](int jj, auto parity) {
       constexpr int P = decltype(parity)::value;
       wait_loads_and_lds();
       __syncthreads();
-      if (jj + 2 < ntiles) dma(jj + 2, P ? G::K1 : G::K0, -1);
-      if (jj + 1 < ntiles) dma(jj + 1, -1, P ? G::V0 : G::V1);
+      if (jj + 2 < je) dma(jj + 2, P ? G::K1 : G::K0, -1);
+      if (jj + 1 < je) dma(jj + 1, -1, P ? G::V0 : G::V1);
     };
-    if (j + 1 < ntiles) {
+    if (j + 1 < je) {
       step(j, I0{}, T{}, sA, mxA, sB, mxB);
       if (skip_last)
         step_sync(j + 1, I1{});
       else
         step(j + 1, I1{}, F{}, sB, mxB, sA, mxA);
-    } else if (j < ntiles) {
+    } else if (j < je) {
       if (skip_last)
         step_sync(j, I0{});
       else
@@ -586,6 +613,24 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
   const float lt = pair_sum(l);
   const bool empty = !(lt > 0.f);
   const float inv = empty ? 0.f : 1.0f / lt;
+  if constexpr (SPLIT) {
+    // this chunk's O (normalised by its own sum, fp32) and base-2 LSE, rows of the query tile
+    // in order; the merge kernel weighs the chunks by their LSE
+    const size_t slot = ((size_t)bh * p.nqt + qt) * p.nchunk + chunk;
+    const int r = wave * 32 + ql;
+    float* po = p.part_o + (slot * kBM + r) * DH;
+#pragma unroll
+    for (int u = 0; u < OT; ++u)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d = 32 * u + 8 * r4 + 4 * h;
+        if (d < DH)
+          *(f32x4*)(po + d) = f32x4{acc[u][4 * r4 + 0] * inv, acc[u][4 * r4 + 1] * inv,
+                                    acc[u][4 * r4 + 2] * inv, acc[u][4 * r4 + 3] * inv};
+      }
+    if (h == 0) p.part_lse[slot * kBM + r] = empty ? -INFINITY : m + __builtin_log2f(lt);
+    return;
+  }
   // D <= 128: the staging rows lie in the K buffers, which the last step does not read and
   // which every wave finished reading before that step's barrier; larger head dims read K in
   // their last step and wait for every wave here.
@@ -627,14 +672,117 @@ __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(D > 128 ? 1 : 2, D > 128 ? 1 : 2)))
 void attn_fwd_kernel(Params p) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  attn_fwd_body<DT, D, CAUSAL, MK>(p);
+  attn_fwd_body<DT, D, CAUSAL, MK, false>(p);
 #endif
+}
+
+// One chunk of a query tile's key range per workgroup (no explicit mask): partial results for
+// attn_fwd_merge_kernel.
+template <int DT, int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(D > 128 ? 1 : 2, D > 128 ? 1 : 2)))
+void attn_fwd_split_kernel(Params p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  attn_fwd_body<DT, D, CAUSAL, kMaskNone, true>(p);
+#endif
+}
+
+// Combination of the chunks of every query row: with the chunks' base-2 LSEs L_c and
+// normalised outputs O_c, M = max L_c, w_c = 2^(L_c - M), O = sum w_c O_c / sum w_c and
+// LSE = (M + log2 sum w_c) ln 2; a row whose chunks are all empty (L_c = -inf) gets O = 0 and
+// LSE = -inf. One thread per 4 consecutive elements of a row.
+struct MergeParams {
+  const float* part_o;
+  const float* part_lse;
+  uint16_t* o;
+  float* lse;
+  const int32_t* valid_len;
+  int64_t os_b, os_h, os_n;
+  int B, Hq, N, DH, nqt, nchunk, split_tiles;
+};
+
+template <int DT, bool CAUSAL>
+__global__ __launch_bounds__(256) void attn_fwd_merge_kernel(MergeParams mp) {
+  using M = Mfma<DT>;
+  const int per_row = mp.DH / 4;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = idx / per_row;
+  if (row >= (int64_t)mp.B * mp.Hq * mp.N) return;
+  const int d0 = 4 * (int)(idx - row * per_row);
+  const int bh = (int)(row / mp.N);
+  const int i = (int)(row - (int64_t)bh * mp.N);
+  const int b = bh / mp.Hq;
+  const int hq = bh - b * mp.Hq;
+  const int qt = i / kBM;
+  const int r = i - qt * kBM;
+  int kv_end = mp.N;
+  if (mp.valid_len) kv_end = min(max(mp.valid_len[b], 0), mp.N);
+  int kv_stop = kv_end;
+  if (CAUSAL) kv_stop = min(kv_stop, qt * kBM + kBM);
+  const int ntiles = (kv_stop + kBN - 1) / kBN;
+  const int nch = (ntiles + mp.split_tiles - 1) / mp.split_tiles;
+  const size_t slot0 = ((size_t)bh * mp.nqt + qt) * mp.nchunk;
+  float mx = -INFINITY;
+  for (int c = 0; c < nch; ++c) mx = fmaxf(mx, mp.part_lse[(slot0 + c) * kBM + r]);
+  f32x4 o = f32x4{};
+  float lse2 = -INFINITY;
+  if (mx != -INFINITY) {
+    float ws = 0.f;
+    for (int c = 0; c < nch; ++c) {
+      const float w = __builtin_amdgcn_exp2f(mp.part_lse[(slot0 + c) * kBM + r] - mx);
+      const f32x4 x = *(const f32x4*)(mp.part_o + ((slot0 + c) * kBM + r) * mp.DH + d0);
+      ws += w;
+      o += w * x;
+    }
+    o *= 1.0f / ws;
+    lse2 = mx + __builtin_log2f(ws);
+  }
+  const uint32_t w0 = (uint32_t)M::round1(o[0]) | ((uint32_t)M::round1(o[1]) << 16);
+  const uint32_t w1 = (uint32_t)M::round1(o[2]) | ((uint32_t)M::round1(o[3]) << 16);
+  *(u32x2*)(mp.o + b * mp.os_b + hq * mp.os_h + i * mp.os_n + d0) = u32x2{w0, w1};
+  if (mp.lse && d0 == 0) mp.lse[(size_t)bh * mp.N + i] = lse2 == -INFINITY ? -INFINITY : lse2 * kLn2;
 }
 
 template <int DT, int D, bool CAUSAL, int MK>
 hipError_t launch(const Params& p, int64_t nwg, hipStream_t stream) {
   hipLaunchKernelGGL((attn_fwd_kernel<DT, D, CAUSAL, MK>), dim3((unsigned)nwg), dim3(kThreads),
                      0, stream, p);
+  return hipGetLastError();
+}
+
+template <int DT, int D, bool CAUSAL>
+hipError_t launch_split(const Params& p, int64_t nwg, hipStream_t stream) {
+  hipLaunchKernelGGL((attn_fwd_split_kernel<DT, D, CAUSAL>), dim3((unsigned)nwg),
+                     dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int DT>
+hipError_t dispatch_split(const Params& p, int D, bool causal, int64_t nwg, hipStream_t s) {
+  switch (D) {
+    case 16:
+      return causal ? launch_split<DT, 16, true>(p, nwg, s) : launch_split<DT, 16, false>(p, nwg, s);
+    case 32:
+      return causal ? launch_split<DT, 32, true>(p, nwg, s) : launch_split<DT, 32, false>(p, nwg, s);
+    case 64:
+      return causal ? launch_split<DT, 64, true>(p, nwg, s) : launch_split<DT, 64, false>(p, nwg, s);
+    case 256:
+      return causal ? launch_split<DT, 256, true>(p, nwg, s)
+                    : launch_split<DT, 256, false>(p, nwg, s);
+    default:
+      return causal ? launch_split<DT, 128, true>(p, nwg, s)
+                    : launch_split<DT, 128, false>(p, nwg, s);
+  }
+}
+
+template <int DT>
+hipError_t launch_merge(const MergeParams& mp, bool causal, hipStream_t s) {
+  const int64_t n = (int64_t)mp.B * mp.Hq * mp.N * (mp.DH / 4);
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (causal)
+    hipLaunchKernelGGL((attn_fwd_merge_kernel<DT, true>), grid, dim3(256), 0, s, mp);
+  else
+    hipLaunchKernelGGL((attn_fwd_merge_kernel<DT, false>), grid, dim3(256), 0, s, mp);
   return hipGetLastError();
 }
 
@@ -703,9 +851,63 @@ int validate(const Layout& q, const Layout& k, const Layout& v, const Layout& o,
   return ATTN_OK;
 }
 
+// ---- split of the key range for small grids
+// Workgroups the device runs at once: two per CU (256 CUs) up to D = 128, one at D = 256.
+int resident_slots(int D) { return D > 128 ? 256 : 512; }
+
+// Key tiles of query tile qt when every key is visible (the host cannot read valid_len).
+int tiles_of(int qt, int N, bool causal) {
+  const int nkt = (N + kBN - 1) / kBN;
+  return causal ? std::min(2 * (qt + 1), nkt) : nkt;
+}
+
+struct Split {
+  int tiles = 0;    // key tiles per chunk (0: no split)
+  int nchunk = 0;   // chunks per query tile
+};
+
+int64_t split_floats(int B, int Hq, int N, int D, const Split& sp) {
+  if (sp.tiles == 0) return 0;
+  const int64_t slots = (int64_t)B * Hq * ((N + kBM - 1) / kBM) * sp.nchunk;
+  return slots * kBM * (D + 1) + 4;
+}
+
+// A grid of few query tiles over long key ranges leaves CUs idle and ends when its longest
+// query tile ends. Splitting each key range into chunks of `tiles` key tiles gives one workgroup
+// per chunk: the smallest chunk for which all chunks still run at once (as far as ws_floats
+// holds their partial results). The chunks' outputs then take a second kernel to combine, and
+// every workgroup pays a fixed cost (prologue, epilogue, launch) worth several key tiles, so
+// the split runs only where the grid fills at most a quarter of the device and the longest key
+// range has at least kMinSplitTiles tiles; on the shapes measured below those bounds (e.g.
+// B = 2, H = 8, N = 1024, or 256 query tiles of N = 2048 to 4096) it was slower.
+constexpr int kMinSplitTiles = 48;
+
+Split choose_split(int B, int Hq, int N, int D, bool causal, int64_t ws_floats) {
+  Split sp;
+  const int nqt = (N + kBM - 1) / kBM;
+  const int64_t items = (int64_t)B * Hq * nqt;
+  const int slots = resident_slots(D);
+  if (items > slots / 4) return sp;
+  int tmax = 0;
+  for (int qt = 0; qt < nqt; ++qt) tmax = std::max(tmax, tiles_of(qt, N, causal));
+  if (tmax < kMinSplitTiles) return sp;
+  for (int ct = 1; ct < tmax; ++ct) {
+    int64_t chunks = 0;
+    for (int qt = 0; qt < nqt; ++qt) chunks += (tiles_of(qt, N, causal) + ct - 1) / ct;
+    chunks *= (int64_t)B * Hq;
+    if (chunks > slots) continue;
+    Split c;
+    c.tiles = ct;
+    c.nchunk = (tmax + ct - 1) / ct;
+    if (split_floats(B, Hq, N, D, c) <= ws_floats) return c;
+  }
+  return sp;
+}
+
 int run(const Layout& q, const Layout& k, const Layout& v, const Layout& o, float* lse, int B,
         int Hq, int Hkv, int N, int D, float scale, int causal, const int32_t* valid_len,
-        int dtype, void* stream, const MaskArg& mk = no_mask()) {
+        int dtype, void* stream, const MaskArg& mk = no_mask(), float* ws = nullptr,
+        int64_t ws_floats = 0) {
   const int st = validate(q, k, v, o, lse, B, Hq, Hkv, N, D, scale, valid_len, dtype, mk);
   if (st != ATTN_OK) return st;
   if (dtype == ATTN_F32) {
@@ -760,8 +962,41 @@ int run(const Layout& q, const Layout& k, const Layout& v, const Layout& o, floa
   p.qmask = scale == 0.f ? 0u : 0xffffffffu;
   if (scale == 0.f) p.c = 1.0f;
   p.mscale = kLog2e / p.c;
-  const int64_t nwg = (int64_t)B * Hq * p.nqt;
+  p.split_tiles = 0;
+  p.nchunk = 0;
+  p.part_o = p.part_lse = nullptr;
   hipStream_t s = (hipStream_t)stream;
+  const Split sp = (ws && mk.type == ATTN_MASK_NONE)
+                       ? choose_split(B, Hq, N, D, causal != 0, ws_floats) : Split{};
+  if (sp.tiles > 0) {
+    const int64_t slots = (int64_t)B * Hq * p.nqt * sp.nchunk;
+    p.split_tiles = sp.tiles;
+    p.nchunk = sp.nchunk;
+    p.part_o = ws;
+    p.part_lse = ws + slots * kBM * D;
+    hipError_t e = dtype == ATTN_BF16 ? dispatch_split<ATTN_BF16>(p, D, causal != 0, slots, s)
+                                      : dispatch_split<ATTN_F16>(p, D, causal != 0, slots, s);
+    if (e == hipSuccess) {
+      MergeParams mp;
+      mp.part_o = p.part_o;
+      mp.part_lse = p.part_lse;
+      mp.o = p.o;
+      mp.lse = lse;
+      mp.valid_len = valid_len;
+      mp.os_b = o.sb; mp.os_h = o.sh; mp.os_n = o.sn;
+      mp.B = B;
+      mp.Hq = Hq;
+      mp.N = N;
+      mp.DH = D;
+      mp.nqt = p.nqt;
+      mp.nchunk = sp.nchunk;
+      mp.split_tiles = sp.tiles;
+      e = dtype == ATTN_BF16 ? launch_merge<ATTN_BF16>(mp, causal != 0, s)
+                             : launch_merge<ATTN_F16>(mp, causal != 0, s);
+    }
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+  }
+  const int64_t nwg = (int64_t)B * Hq * p.nqt;
   const hipError_t e =
       dtype == ATTN_BF16 ? dispatch_m<ATTN_BF16>(p, D, causal != 0, mk.type, nwg, s)
                          : dispatch_m<ATTN_F16>(p, D, causal != 0, mk.type, nwg, s);
@@ -812,6 +1047,63 @@ namespace {
 
 
 }  // namespace
+
+namespace {
+
+// attn_fwd_ws's checks beyond those of attn_fwd_strided: the part of the workspace the split
+// uses is 16-byte aligned and overlaps no input or output.
+int validate_ws(const Layout& q, const Layout& k, const Layout& v, const Layout& o,
+                const float* lse, const float* ws, int64_t ws_floats, int B, int Hq, int Hkv,
+                int N, int D, float scale, int causal, const int32_t* valid_len, int dtype) {
+  const int st = validate(q, k, v, o, lse, B, Hq, Hkv, N, D, scale, valid_len, dtype);
+  if (st != ATTN_OK) return st;
+  if (ws_floats < 0) return ATTN_ERR_WORKSPACE;
+  if (!ws || dtype == ATTN_F32) return ATTN_OK;
+  if ((uintptr_t)ws % 16 != 0) return ATTN_ERR_LAYOUT;
+  const int64_t used = 4 * split_floats(B, Hq, N, D, choose_split(B, Hq, N, D, causal != 0,
+                                                                    ws_floats));
+  if (used == 0) return ATTN_OK;
+  const int es = 2;
+  const void* other[] = {q.ptr, k.ptr, v.ptr, o.ptr, lse, valid_len};
+  const int64_t size[] = {q.span(B, N, D, es), k.span(B, N, D, es), v.span(B, N, D, es),
+                          o.span(B, N, D, es), (int64_t)B * Hq * N * 4, (int64_t)B * 4};
+  for (int i = 0; i < 6; ++i)
+    if (other[i] && overlaps(ws, used, other[i], size[i])) return ATTN_ERR_ALIAS;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" int64_t attn_fwd_workspace_floats(int B, int Hq, int Hkv, int N, int D, int causal) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || D < 1) return -1;
+  return split_floats(B, Hq, N, D, choose_split(B, Hq, N, D, causal != 0, INT64_MAX));
+}
+
+extern "C" int attn_fwd_ws_validate(const void* q, const int64_t* q_strides, const void* k,
+                                    const int64_t* k_strides, const void* v,
+                                    const int64_t* v_strides, const void* out,
+                                    const int64_t* out_strides, const float* lse, const float* ws,
+                                    int64_t ws_floats, int B, int Hq, int Hkv, int N, int D,
+                                    float scale, int causal, const int32_t* valid_len,
+                                    int dtype) {
+  return validate_ws(strided(q, q_strides, Hq, N, D), strided(k, k_strides, Hkv, N, D),
+                     strided(v, v_strides, Hkv, N, D), strided(out, out_strides, Hq, N, D), lse,
+                     ws, ws_floats, B, Hq, Hkv, N, D, scale, causal, valid_len, dtype);
+}
+
+extern "C" int attn_fwd_ws(const void* q, const int64_t* q_strides, const void* k,
+                           const int64_t* k_strides, const void* v, const int64_t* v_strides,
+                           void* out, const int64_t* out_strides, float* lse, float* ws,
+                           int64_t ws_floats, int B, int Hq, int Hkv, int N, int D, float scale,
+                           int causal, const int32_t* valid_len, int dtype, void* stream) {
+  const Layout lq = strided(q, q_strides, Hq, N, D), lk = strided(k, k_strides, Hkv, N, D);
+  const Layout lv = strided(v, v_strides, Hkv, N, D), lo = strided(out, out_strides, Hq, N, D);
+  const int st = validate_ws(lq, lk, lv, lo, lse, ws, ws_floats, B, Hq, Hkv, N, D, scale, causal,
+                             valid_len, dtype);
+  if (st != ATTN_OK) return st;
+  return run(lq, lk, lv, lo, lse, B, Hq, Hkv, N, D, scale, causal, valid_len, dtype, stream,
+             no_mask(), ws, ws_floats);
+}
 
 extern "C" int attn_fwd_masked_validate(const void* q, const int64_t* q_strides, const void* k,
                                         const int64_t* k_strides, const void* v,

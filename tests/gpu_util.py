@@ -42,7 +42,7 @@ def from_device(t, dtype: str) -> np.ndarray:
     return inputs.widen(bits, dtype)
 
 
-def run_device(case: inputs.Case, want_lse=True, stream=None):
+def run_device(case: inputs.Case, want_lse=True, stream=None, split=True):
     """Returns (O float64 [B,Hq,N,D], LSE float64 [B,Hq,N] or None, device tensors)."""
     import torch
     q = to_device(case.q_bits, case.dtype)
@@ -52,7 +52,7 @@ def run_device(case: inputs.Case, want_lse=True, stream=None):
     if case.valid_len is not None:
         vl = torch.from_numpy(case.valid_len.astype(np.int32)).cuda()
     out, lse = sdp.forward(q, k, v, causal=case.causal, valid_len=vl, scale=case.scale,
-                           want_lse=want_lse, stream=stream)
+                           want_lse=want_lse, stream=stream, split=split)
     torch.cuda.synchronize()
     O = from_device(out, case.dtype)
     L = lse.cpu().numpy().astype(np.float64) if lse is not None else None

@@ -33,7 +33,9 @@ def test_header_declares_the_entry_points():
                                     "attn_bwd_ws", "attn_bwd_ws_validate", "attn_fwd",
                                     "attn_fwd_masked", "attn_fwd_masked_validate",
                                     "attn_fwd_strided", "attn_fwd_strided_validate",
-                                    "attn_fwd_validate", "attn_status_string", "attn_version"]
+                                    "attn_fwd_validate", "attn_fwd_workspace_floats",
+                                    "attn_fwd_ws", "attn_fwd_ws_validate", "attn_status_string",
+                                    "attn_version"]
 
 
 def test_library_exports_every_declared_function(lib):
@@ -46,7 +48,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_version(lib):
-    assert sdp.attn_version() == 13
+    assert sdp.attn_version() == 14
 
 
 def test_status_strings(lib):
@@ -521,3 +523,89 @@ def test_status_strings_match_what_the_library_accepts(lib):
                                               [0, 0, 1008], dt)
             assert st == sdp.ATTN_OK, (dt, mt, st)
     assert call(dtype=3) == sdp.ATTN_ERR_DTYPE
+
+
+# ---- attn_fwd_ws: the split of the key range for small grids (host-side choice and checks)
+WS = 13 * GB
+
+
+def split_rule(B, Hq, N, D, causal, ws_floats=None):
+    """The chunking the header describes, restated: where the (batch, head, 128-row query tile)
+    items fill at most a quarter of the device (128 workgroups up to D = 128, 64 at D = 256) and
+    the longest key range has at least 48 tiles of 64 keys, the smallest number of key tiles per
+    chunk for which every chunk runs at once (512 workgroups up to D = 128, 256 at D = 256)."""
+    nqt, nkt = -(-N // 128), -(-N // 64)
+    slots = 256 if D > 128 else 512
+    if B * Hq * nqt > slots // 4:
+        return 0
+    tiles = [min(2 * (qt + 1), nkt) if causal else nkt for qt in range(nqt)]
+    if max(tiles) < 48:
+        return 0
+    for ct in range(1, max(tiles)):
+        if B * Hq * sum(-(-t // ct) for t in tiles) <= slots:
+            size = B * Hq * nqt * -(-max(tiles) // ct) * 128 * (D + 1) + 4
+            if ws_floats is None or size <= ws_floats:
+                return size
+    return 0
+
+
+@pytest.mark.parametrize("shape", [
+    (1, 2, 8192, 64, True),     # 128 query tiles over up to 128 key tiles: chunks of 19
+    (1, 1, 3072, 128, True),    # chunks of 2 key tiles
+    (1, 1, 3200, 64, False),    # chunks of 3
+    (1, 1, 6000, 256, True),    # D = 256: at most 64 query tiles
+    (1, 2, 6000, 256, True),    # ... 94 are too many
+    (2, 8, 1024, 64, True),     # the causal_mha workload: too few key tiles per row
+    (8, 32, 4096, 128, True),   # the long_gqa workload fills the device
+    (4, 32, 2048, 128, True),   # causal_gqa too
+    (1, 8, 4096, 128, False),   # 256 query tiles: more than a quarter of the device
+])
+def test_fwd_workspace_floats(lib, shape):
+    B, Hq, N, D, causal = shape
+    got = sdp.attn_fwd_workspace_floats(B, Hq, 1, N, D, causal)
+    assert got == split_rule(B, Hq, N, D, causal)
+    if shape == (1, 2, 8192, 64, True):
+        assert got == 128 * 7 * 128 * 65 + 4
+    if shape == (1, 1, 3072, 128, True):
+        assert got == 24 * 24 * 128 * 129 + 4
+    if shape in ((2, 8, 1024, 64, True), (8, 32, 4096, 128, True), (4, 32, 2048, 128, True),
+                 (1, 8, 4096, 128, False), (1, 2, 6000, 256, True)):
+        assert got == 0
+
+
+def test_fwd_workspace_floats_rejects_bad_sizes(lib):
+    assert sdp.attn_fwd_workspace_floats(0, 8, 8, 1024, 64, True) == -1
+    assert sdp.attn_fwd_workspace_floats(2, 8, 8, 0, 64, True) == -1
+
+
+def wcall_fwd(**kw):
+    a = dict(q=Q, k=K, v=V, out=O, lse=L, ws=WS, n=10 ** 8, B=1, Hq=2, Hkv=2, N=8192, D=64,
+             causal=1, valid_len=VL, dtype=sdp.ATTN_F16)
+    a.update(kw)
+    return sdp.attn_fwd_ws_validate(a["q"], None, a["k"], None, a["v"], None, a["out"], None,
+                                    a["lse"], a["ws"], a["n"], a["B"], a["Hq"], a["Hkv"], a["N"],
+                                    a["D"], 0.125, a["causal"], a["valid_len"], a["dtype"])
+
+
+def test_fwd_ws_validate(lib):
+    full = sdp.attn_fwd_workspace_floats(1, 2, 2, 8192, 64, True)
+    assert wcall_fwd() == sdp.ATTN_OK
+    assert wcall_fwd(ws=None) == sdp.ATTN_OK              # no workspace: no split
+    assert wcall_fwd(n=0) == sdp.ATTN_OK                  # too small for any split
+    assert wcall_fwd(n=-1) == sdp.ATTN_ERR_WORKSPACE
+    assert wcall_fwd(ws=WS + 4) == sdp.ATTN_ERR_LAYOUT    # float4 partials: 16-byte alignment
+    # the used part of the workspace overlaps an input or output
+    assert wcall_fwd(ws=Q - 4 * full + 64) == sdp.ATTN_ERR_ALIAS
+    assert wcall_fwd(ws=O + 1024) == sdp.ATTN_ERR_ALIAS
+    assert wcall_fwd(ws=L - 16) == sdp.ATTN_ERR_ALIAS
+    assert wcall_fwd(ws=Q - 4 * full) == sdp.ATTN_OK      # just below Q
+    # a smaller workspace uses a coarser split, so only that part must be clear of Q
+    half = split_rule(1, 2, 8192, 64, True, full // 2)
+    assert 0 < half < full
+    assert wcall_fwd(ws=Q - 4 * half, n=full // 2) == sdp.ATTN_OK
+    assert wcall_fwd(ws=Q - 4 * half + 16, n=full // 2) == sdp.ATTN_ERR_ALIAS
+    # fp32 never splits: the workspace is not checked
+    assert wcall_fwd(dtype=sdp.ATTN_F32, ws=O + 1024) == sdp.ATTN_OK
+    # the attn_fwd_strided checks come first
+    assert wcall_fwd(D=96) == sdp.ATTN_ERR_HEAD_DIM
+    assert wcall_fwd(q=None) == sdp.ATTN_ERR_NULL

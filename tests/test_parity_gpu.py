@@ -34,12 +34,16 @@ SMALL = [
 ]
 
 
+# Each small case runs twice: split=True lets forward() take attn_fwd_ws (key ranges split over
+# several workgroups, then merged) where the grid is small, split=False keeps one workgroup per
+# query tile (attn_fwd).
+@pytest.mark.parametrize("split", [False, True], ids=["one-pass", "split"])
 @pytest.mark.parametrize("cfg", SMALL, ids=lambda c: "%s-D%d-c%d-p%d-B%d-H%d-%d-N%d" % c)
-def test_small_full(cfg):
+def test_small_full(cfg, split):
     dtype, D, causal, padded, B, Hq, Hkv, N = cfg
     case = inputs.make_case(B, Hq, Hkv, N, D, dtype, causal, padded, seed=[101, D, N, B])
-    log("case %s valid_len %s" % (cfg, case.valid_len))
-    O, L = run_device(case)
+    log("case %s split %s valid_len %s" % (cfg, split, case.valid_len))
+    O, L = run_device(case, split=split)
     O_ref, L_ref = run_oracle(case)
     compare(case, O, L, O_ref, L_ref, tag=str(cfg))
 
@@ -64,12 +68,13 @@ SMALL_D = [
 ]
 
 
+@pytest.mark.parametrize("split", [False, True], ids=["one-pass", "split"])
 @pytest.mark.parametrize("cfg", SMALL_D, ids=lambda c: "%s-D%d-c%d-p%d-B%d-H%d-%d-N%d" % c)
-def test_small_head_dims(cfg):
+def test_small_head_dims(cfg, split):
     dtype, D, causal, padded, B, Hq, Hkv, N = cfg
     case = inputs.make_case(B, Hq, Hkv, N, D, dtype, causal, padded, seed=[115, D, N, B])
-    log("case %s valid_len %s" % (cfg, case.valid_len))
-    O, L = run_device(case)
+    log("case %s split %s valid_len %s" % (cfg, split, case.valid_len))
+    O, L = run_device(case, split=split)
     O_ref, L_ref = run_oracle(case)
     compare(case, O, L, O_ref, L_ref, tag=str(cfg))
 
@@ -167,7 +172,17 @@ def test_workload_full(name):
     compare(case, O, L, O_ref, L_ref, tag=name)
 
 
-@pytest.mark.parametrize("name", ["causal_gqa", "long_gqa", "long_mqa"])
+def test_long_gqa_every_row():
+    """The headline workload (B=8, Hq=32, Hkv=8, N=4096, D=128, bf16, causal), in the launch
+    configuration the benchmark times, against the oracle on every one of its 1,048,576 rows
+    (about 10 s of the oracle on 16 host threads)."""
+    case = inputs.make_workload(inputs.WORKLOADS["long_gqa"])
+    O, L = run_device(case)
+    O_ref, L_ref = run_oracle(case)
+    compare(case, O, L, O_ref, L_ref, tag="long_gqa every row")
+
+
+@pytest.mark.parametrize("name", ["causal_gqa", "long_mqa"])
 def test_workload_sampled(name):
     w = inputs.WORKLOADS[name]
     case = inputs.make_workload(w)
