@@ -491,11 +491,14 @@ __device__ __forceinline__ void dkdv_f32_body(const F32BwdParams& p) {
     Offsets<D> off;
     off.init(lane);
     const float c = p.c;
-    const int g0 = it0 / ntq, qs0 = qstart + (it0 - g0 * ntq) * kT;
+    // query tile major from the last tile down, query head minor (as the 16-bit kernel: the
+    // key-tile workgroups of a KV head read each Q / dO tile at about the same time)
+    const int qlast = qstart + (ntq - 1) * kT;
+    const int t0 = it0 / p.group;
+    const int g0 = it0 - t0 * p.group, qs0 = qlast - t0 * kT;
     int g_cur = g0, q_cur = qs0, g_nxt = g0, q_nxt = qs0;
     auto advance = [&](int& g, int& q0) {
-      q0 += kT;
-      if (q0 >= p.N) { q0 = qstart; ++g; }
+      if (++g == p.group) { g = 0; q0 -= kT; }
     };
     dma(g_nxt, q_nxt, 0);
     advance(g_nxt, q_nxt);
