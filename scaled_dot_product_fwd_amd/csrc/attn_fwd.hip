@@ -606,10 +606,8 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
     }
   }
 
-  // ---- epilogue: O = acc / l (0 for a row with no visible key), LSE = m ln2 + ln l.
-  // Each wave stages its 32 x D output rows in LDS (16-byte chunk c of row q at chunk
-  // c ^ (q % CH)), then writes whole rows with 16-byte stores: consecutive lanes cover
-  // consecutive bytes of a row.
+  // ---- epilogue: O = acc / l (0 for a row with no visible key), LSE = m ln2 + ln l; each
+  // lane stores 16-byte pieces of its own row straight from registers.
   const float lt = pair_sum(l);
   const bool empty = !(lt > 0.f);
   const float inv = empty ? 0.f : 1.0f / lt;
@@ -631,34 +629,30 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
     if (h == 0) p.part_lse[slot * kBM + r] = empty ? -INFINITY : m + __builtin_log2f(lt);
     return;
   }
-  // D <= 128: the staging rows lie in the K buffers, which the last step does not read and
-  // which every wave finished reading before that step's barrier; larger head dims read K in
-  // their last step and wait for every wave here.
-  wait_loads_and_lds();
-  if constexpr (D > 128) __syncthreads();
-  unsigned char* ost = smem + wave * 32 * G::ROW;
+  // Each lane holds, per 32-column block u, the columns 32u + 8 r4 + 4h .. +3 of its query
+  // row (r4 = 0..3). One swap between the two halves of the wave gives lane l < 32 the 16
+  // contiguous bytes 32u + 16j .. +7 and lane l + 32 the 16 bytes 32u + 16j + 8 .. +15 of
+  // the same row (j = 0, 1): each lane stores them directly, no staging.
+  uint16_t* const orow = p.o + b * p.os_b + hq * p.os_h + (size_t)min(qrow, p.N - 1) * p.os_n;
 #pragma unroll
   for (int u = 0; u < OT; ++u)
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int c = 4 * u + r4;   // chunk of d = 32u + 8 r4 + 4h .. +3
-      const uint32_t w0 = (uint32_t)M::round1(acc[u][4 * r4 + 0] * inv) |
-                          ((uint32_t)M::round1(acc[u][4 * r4 + 1] * inv) << 16);
-      const uint32_t w1 = (uint32_t)M::round1(acc[u][4 * r4 + 2] * inv) |
-                          ((uint32_t)M::round1(acc[u][4 * r4 + 3] * inv) << 16);
-      *(u32x2*)(ost + ql * G::ROW + 16 * (c ^ (ql & (G::CH - 1))) + 8 * h) = u32x2{w0, w1};
+    for (int j = 0; j < 2; ++j) {
+      const int ra = 4 * (2 * j), rc = 4 * (2 * j + 1);
+      const uint32_t a0 = (uint32_t)M::round1(acc[u][ra + 0] * inv) |
+                          ((uint32_t)M::round1(acc[u][ra + 1] * inv) << 16);
+      const uint32_t a1 = (uint32_t)M::round1(acc[u][ra + 2] * inv) |
+                          ((uint32_t)M::round1(acc[u][ra + 3] * inv) << 16);
+      const uint32_t c0 = (uint32_t)M::round1(acc[u][rc + 0] * inv) |
+                          ((uint32_t)M::round1(acc[u][rc + 1] * inv) << 16);
+      const uint32_t c1 = (uint32_t)M::round1(acc[u][rc + 2] * inv) |
+                          ((uint32_t)M::round1(acc[u][rc + 3] * inv) << 16);
+      const auto x0 = __builtin_amdgcn_permlane32_swap(a0, c0, false, false);
+      const auto x1 = __builtin_amdgcn_permlane32_swap(a1, c1, false, false);
+      const int d = 32 * u + 16 * j + 8 * h;
+      if (qrow < p.N && (DCH == G::CH || d < DH))
+        *(u32x4*)(orow + d) = u32x4{x0[0], x1[0], x0[1], x1[1]};
     }
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  constexpr int RPI = 64 / G::CH;   // rows per store instruction
-  uint16_t* const obase = p.o + b * p.os_b + hq * p.os_h;
-#pragma unroll
-  for (int i = 0; i < 32 / RPI; ++i) {
-    const int r = i * RPI + lane / G::CH;
-    const int cc = lane % G::CH;
-    const u32x4 v = *(const u32x4*)(ost + r * G::ROW + 16 * (cc ^ (r & (G::CH - 1))));
-    if (qa + r < p.N && (DCH == G::CH || cc < DCH))
-      *(u32x4*)(obase + (qa + r) * p.os_n + 8 * cc) = v;
-  }
   if (p.lse && h == 0 && qrow < p.N)
     p.lse[(size_t)bh * p.N + qrow] = empty ? -INFINITY : m * kLn2 + logf(lt);
 }
