@@ -848,10 +848,13 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
 }
 
 // D = 256 holds 128 KiB of tiles in LDS: one workgroup per CU, one wave per SIMD with the
-// whole register file.
+// whole register file. D <= 64 without an explicit mask fits 168 VGPRs: three waves per SIMD.
+template <int D, int MK>
+constexpr int bwd_waves_per_eu() { return D > 128 ? 1 : (D <= 64 && MK == kMaskNone ? 3 : 2); }
+
 template <int DT, int D, bool CAUSAL, int MK, int PART>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(D > 128 ? 1 : 2, D > 128 ? 1 : 2)))
+__attribute__((amdgpu_waves_per_eu(bwd_waves_per_eu<D, MK>(), bwd_waves_per_eu<D, MK>())))
 void attn_bwd_dq_kernel(BwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   bwd_dq_body<DT, D, CAUSAL, MK, PART>(p);
@@ -860,7 +863,7 @@ void attn_bwd_dq_kernel(BwdParams p) {
 
 template <int DT, int D, bool CAUSAL, int MK, int PART>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(D > 128 ? 1 : 2, D > 128 ? 1 : 2)))
+__attribute__((amdgpu_waves_per_eu(bwd_waves_per_eu<D, MK>(), bwd_waves_per_eu<D, MK>())))
 void attn_bwd_dkdv_kernel(BwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   bwd_dkdv_body<DT, D, CAUSAL, MK, PART>(p);

@@ -660,10 +660,15 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
 // The body uses device-only types (buffer resources), so only the device pass compiles it;
 // the host pass needs no more than the kernel's signature to emit its launch stub.
 // D = 256 holds 128 KiB of K/V tiles in LDS, one workgroup per CU: one wave per SIMD, which may
-// then use the whole register file (256 VGPRs + 256 AGPRs).
+// then use the whole register file (256 VGPRs + 256 AGPRs). D <= 64 without an explicit mask
+// fits 168 VGPRs (32 KiB of LDS per workgroup): three workgroups per CU, three waves per SIMD
+// to share the softmax's VALU work, which bounds these head dimensions.
+template <int D, int MK>
+constexpr int fwd_waves_per_eu() { return D > 128 ? 1 : (D <= 64 && MK == kMaskNone ? 3 : 2); }
+
 template <int DT, int D, bool CAUSAL, int MK>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(D > 128 ? 1 : 2, D > 128 ? 1 : 2)))
+__attribute__((amdgpu_waves_per_eu(fwd_waves_per_eu<D, MK>(), fwd_waves_per_eu<D, MK>())))
 void attn_fwd_kernel(Params p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   attn_fwd_body<DT, D, CAUSAL, MK, false>(p);
