@@ -454,11 +454,19 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       if (j + 1 < ntiles) mask_dma(j + 1);
     }
-    // S^T and dP^T for the tile's two 32-key halves
+    // S^T and dP^T for the tile's two 32-key halves. An additive mask is the scores' starting
+    // value (raw score units), so that its words are not live across the MFMAs.
     f32x16 sc[2], dp[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       sc[t] = f32x16{};
+      if constexpr (MK == kMaskAdd)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          sc[t][r] = mask_add<DT, MK>(mw[4 * t + (r >> 2)], r & 3) * p.mscale;
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
       dp[t] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
@@ -476,10 +484,7 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p) {
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float x = sc[t][r];
-        if constexpr (MK == kMaskAdd)
-          x = __builtin_fmaf(mask_add<DT, MK>(mw[4 * t + (r >> 2)], r & 3), p.mscale, x);
-        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(x, c, -L));
+        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][r], c, -L));
         ds[t][r] = pr * (dp[t][r] - delta);
         if constexpr (MK == kMaskKeep)
           ds[t][r] = mask_keep<DT, MK>(mw[4 * t + (r >> 2)], r & 3) ? ds[t][r] : 0.f;
@@ -743,17 +748,24 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
       // this iteration's mask values (query rows 8 (r/4) + 4h + r%4 of the tile, the lane's
       // key), then the next iteration's DMA into the same slot. Keep masks are packed into
       // one bit per element, additive values two per register.
-      uint32_t kbits = 0, mv[8];
+      // An additive mask enters as the starting value of the score accumulator (in raw score
+      // units), so that no mask register stays live across the MFMAs.
+      uint32_t kbits = 0;
+      f32x16 s = f32x16{};
       if constexpr (MK != kMaskNone) {
         const unsigned char* ms = smem + MOFF + wave * KM::WB + KM::ES * ql;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int qi = 8 * (r >> 2) + 4 * h + (r & 3);
           if constexpr (MK == kMaskKeep) {
+            // four bytes at a time, packed into bits as they arrive
             kbits |= (ms[qi * KM::RB] != 0 ? 1u : 0u) << r;
+            if ((r & 3) == 3) asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(kbits) :: "memory");
           } else {
-            const uint32_t x = *(const uint16_t*)(ms + qi * KM::RB);
-            mv[r >> 1] = (r & 1) ? (mv[r >> 1] | (x << 16)) : x;
+            const uint32_t bits = *(const uint16_t*)(ms + qi * KM::RB);
+            const float a = DT == ATTN_BF16 ? __uint_as_float(bits << 16)
+                                            : (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+            s[r] = a * p.mscale;
           }
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -764,7 +776,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
       const float* lb = (const float*)(qb + 2 * BG::QTILE);
       const float* db = (const float*)(qb + 2 * BG::QTILE + 1024);
       // S = Q K^T and dP = dO V^T (rows: queries q0 + 8(r/4) + 4h + r%4; column: key)
-      f32x16 s = f32x16{}, dp = f32x16{};
+      f32x16 dp = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
         s = M::run(*(const u32x4*)(qb + raddr[ks]), kf[ks], s);
@@ -785,14 +797,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * r4 + e;
-          float x = s[r];
-          if constexpr (MK == kMaskAdd) {
-            const uint32_t bits = (mv[r >> 1] >> (16 * (r & 1))) & 0xffffu;
-            const float a = DT == ATTN_BF16 ? __uint_as_float(bits << 16)
-                                            : (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
-            x = __builtin_fmaf(a, p.mscale, x);
-          }
-          pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(x, c, -lv[e]));
+          pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lv[e]));
         }
         if (!full) {
 #pragma unroll
