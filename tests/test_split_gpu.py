@@ -110,3 +110,40 @@ def test_split_strided_bnhd():
     L = lse.cpu().numpy().astype(np.float64)
     O_ref, L_ref = run_oracle(case)
     compare(case, O, L, O_ref, L_ref, tag="split bnhd")
+
+
+def test_split_without_lse():
+    """forward(want_lse=False): the split writes O only (the merge kernel skips the LSE)."""
+    import torch
+    case = inputs.make_case(1, 2, 2, 4096, 64, "f16", True, True, seed=409,
+                            valid_len=np.array([3000], np.int32))
+    assert split_size(case) > 0
+    O, L = run_device(case, want_lse=False, split=True)
+    assert L is None
+    O_ref, _ = run_oracle(case)
+    err = np.abs(O - O_ref).max()
+    log("split without LSE: max|dO| %.3g" % err)
+    assert err <= 5e-3
+
+
+def test_f32_ignores_the_workspace():
+    """fp32 inputs never split: attn_fwd_ws runs the one-pass fp32 kernel and leaves the
+    workspace untouched."""
+    import torch
+    case = inputs.make_case(1, 2, 2, 3200, 64, "f32", True, False, seed=411)
+    q, k, v = (to_device(x, "f32") for x in (case.q_bits, case.k_bits, case.v_bits))
+    out = torch.empty_like(q)
+    lse = torch.empty((1, 2, 3200), dtype=torch.float32, device="cuda")
+    n = sdp.attn_fwd_workspace_floats(1, 2, 2, 3200, 64, True)
+    assert n > 0   # these sizes would split with 16-bit inputs
+    ws = torch.full((n,), 7.0, dtype=torch.float32, device="cuda")
+    st = sdp.attn_fwd_ws(q.data_ptr(), None, k.data_ptr(), None, v.data_ptr(), None,
+                         out.data_ptr(), None, lse.data_ptr(), ws.data_ptr(), n, 1, 2, 2, 3200,
+                         64, case.scale, True, None, sdp.ATTN_F32,
+                         torch.cuda.current_stream().cuda_stream)
+    assert st == sdp.ATTN_OK
+    torch.cuda.synchronize()
+    assert torch.all(ws == 7.0)
+    O, L = from_device(out, "f32"), lse.cpu().numpy().astype(np.float64)
+    O_ref, L_ref = run_oracle(case)
+    compare(case, O, L, O_ref, L_ref, tag="f32 through attn_fwd_ws")
