@@ -495,26 +495,64 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       if (j + 1 < je) mask_dma(j + 1);
-      int lim = kv_end - 1 - kb - 4 * h;
-      if (CAUSAL) lim = min(lim, qrow - kb - 4 * h);
+      if constexpr (MK == kMaskKeep) {
+        // A tile whose keep bytes are all nonzero for every lane of the wave, and which no
+        // causal, valid_len or N boundary crosses, needs nothing (a window or block mask keeps
+        // most tiles whole). (w - 0x01..01) & ~w & 0x80..80 is nonzero iff w has a zero byte.
+        // A tile with no nonzero keep byte in any lane is wholly hidden: all its scores -inf.
+        uint32_t z = 0, any = 0;
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+        for (int g = 0; g < 8; ++g) {
+          z |= (mw[g][0] - 0x01010101u) & ~mw[g][0] & 0x80808080u;
+          any |= mw[g][0];
+        }
+        const bool pos_full = (!CAUSAL || kb + kBN - 1 <= qa) && kb + kBN <= kv_end;
+        if (pos_full && __builtin_amdgcn_ballot_w64(z != 0) == 0) return;
+        if (__builtin_amdgcn_ballot_w64(any != 0) == 0) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int g = 4 * t + (r >> 2), e = r & 3;
-          bool vis = 32 * t + 8 * (r >> 2) + e <= lim;
-          float x = sc[t][r];
-          if constexpr (MK == kMaskKeep) {
-            vis = vis && ((mw[g][0] >> (8 * e)) & 0xffu) != 0;
-          } else {
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sc[t][r] = -INFINITY;
+          mxc = -INFINITY;
+          return;
+        }
+      }
+      if constexpr (MK == kMaskAdd) {
+        // Fold the additive values into every score, then hide keys by position only where a
+        // causal, valid_len or N boundary crosses the tile.
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int g = 4 * t + (r >> 2), e = r & 3;
             const uint32_t bits = (mw[g][e >> 1] >> (16 * (e & 1))) & 0xffffu;
             const float a = DT == ATTN_BF16
                                 ? __uint_as_float(bits << 16)
                                 : (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
-            x = __builtin_fmaf(a, p.mscale, x);
+            sc[t][r] = __builtin_fmaf(a, p.mscale, sc[t][r]);
           }
-          sc[t][r] = vis ? x : -INFINITY;
+        if (!((!CAUSAL || kb + kBN - 1 <= qa) && kb + kBN <= kv_end)) {
+          int lim = kv_end - 1 - kb - 4 * h;
+          if (CAUSAL) lim = min(lim, qrow - kb - 4 * h);
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              sc[t][r] = (32 * t + 8 * (r >> 2) + (r & 3) <= lim) ? sc[t][r] : -INFINITY;
         }
+      } else {
+        int lim = kv_end - 1 - kb - 4 * h;
+        if (CAUSAL) lim = min(lim, qrow - kb - 4 * h);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int g = 4 * t + (r >> 2), e = r & 3;
+            const bool vis = 32 * t + 8 * (r >> 2) + e <= lim &&
+                             ((mw[g][0] >> (8 * e)) & 0xffu) != 0;
+            sc[t][r] = vis ? sc[t][r] : -INFINITY;
+          }
+      }
       mxc = rowmax(sc);
       return;
     }
