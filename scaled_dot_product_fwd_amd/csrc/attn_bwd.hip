@@ -474,11 +474,11 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams& p) {
         dp[t] = M::run(*(const u32x4*)(vb + vaddr[ks] + t * 32 * G::ROW), dof[ks], dp[t]);
       }
     }
-    // P and dS; keys kb0 + 32t + 8(r/4) + 4h + r%4 are tested only in tiles that reach past
-    // this wave's causal diagonal or the padding boundary (a hidden element's P may be inf:
-    // the select removes it).
+    // P and dS; keys kb0 + 32t + 8(r/4) + 4h + r%4 are tested by position only in tiles that
+    // reach past this wave's causal diagonal or the padding boundary (a hidden element's P may
+    // be inf: the select removes it); a keep mask is tested on every element.
     const int kb0 = j * kBN;
-    const bool full = MK == kMaskNone && (!CAUSAL || kb0 + kBN - 1 <= qa) && kb0 + kBN <= kv_end;
+    const bool full = (!CAUSAL || kb0 + kBN - 1 <= qa) && kb0 + kBN <= kv_end;
     float ds[2][16];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -786,7 +786,8 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
       // touches the causal diagonal, the padding boundary or the end of the sequence; only then
       // is each element tested. A hidden element may have L = -inf (a row with no visible key)
       // and so x = inf: the select, not a product, removes it.
-      const bool full = MK == kMaskNone && (!CAUSAL || q0 >= kw + 31) && kw + 32 <= kv_end &&
+      // (a keep mask is tested on every element; an additive one is already in the scores)
+      const bool full = MK != kMaskKeep && (!CAUSAL || q0 >= kw + 31) && kw + 32 <= kv_end &&
                         q0 + kQT <= p.N;
       float pr[16], ds[16];
 #pragma unroll
