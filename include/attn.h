@@ -28,7 +28,7 @@
  *   on fully masked rows).
  * - LSE is the natural-log log-sum-exp of the row's visible scaled scores; a later backward pass
  *   or a merge of partial results over key shards uses it (tiny_flash_attn_triton.py stores the
- *   same quantity in base 2 "for backward").
+ *   same quantity in base 2 for its backward pass).
  * - The computation is the tiled online softmax of "Triton Cuda Attention" (section on the
  *   online softmax core algorithm): the N x N score matrix never reaches memory.
  *
@@ -284,7 +284,7 @@ int64_t attn_fwd_workspace_floats(int B, int Hq, int Hkv, int N, int D, int caus
 /*
  * attn_bwd -- gradients of the attn_fwd output with respect to Q, K and V (contiguous tensors,
  * no explicit mask), given the upstream gradient dO and the forward's own O and LSE.
- * tiny_flash_attn_triton.py stores the log-sum-exp "for backward"; the pages stop at the
+ * tiny_flash_attn_triton.py stores the log-sum-exp for its backward pass; the pages stop at the
  * forward, and this is the derivative of the forward's definition: with
  * P = exp(scale * q.k - LSE) on the visible keys (the same causal / valid_len masks) and
  * Delta_i = sum_d dO[i,d] O[i,d],

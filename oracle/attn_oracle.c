@@ -213,7 +213,7 @@ int oracle_max_threads(void)
  * Backward pass (test infrastructure only, like everything in this file): the exact gradients
  * of the forward output O with respect to Q, K and V for an upstream gradient dO, i.e. of the
  * scalar sum_{b,hq,i,d} O[b,hq,i,d] * dO[b,hq,i,d]. The pages give the forward only;
- * tiny_flash_attn_triton.py keeps the log-sum-exp "for backward". The derivative of the
+ * tiny_flash_attn_triton.py keeps the log-sum-exp for its backward pass. The derivative of the
  * definition above, with w_ij the softmax weights of row i over its visible keys J_i:
  *
  *   dV[b,kv,j]  = sum_{hq in group(kv)} sum_{i : j in J_i} w_ij dO[b,hq,i]

@@ -2,7 +2,7 @@
 //
 // What it computes: the gradients of the forward output O with respect to Q, K and V for an
 // upstream gradient dO, using the forward's log-sum-exp L (tiny_flash_attn_triton.py keeps L
-// "for backward"; the forward stores it in base e). With the weights recomputed per tile as
+// for its backward pass; the forward stores it in base e). With the weights recomputed per tile as
 // P = exp(scale * q.k - L) on the visible keys (the same causal / valid_len masks as the
 // forward), and D_i = sum_d dO[i,d] * O[i,d]:
 //
