@@ -34,7 +34,9 @@
  *
  * Numerics: 16-bit inputs with fp32 scores, softmax state and accumulation; the probabilities
  * are rounded to the input type before they multiply V; O is rounded to nearest-even in the
- * input type. fp32 inputs (ATTN_F32) stay fp32 throughout. Results are deterministic run to run
+ * input type. With fp16 inputs the row's denominator (and so LSE) is the sum of those rounded
+ * probabilities (within 2^-11 relative of the exact sum); with bf16 it is the fp32 sum of the
+ * unrounded ones. fp32 inputs (ATTN_F32) stay fp32 throughout. Results are deterministic run to run
  * for the same inputs and shapes.
  *
  * Threading: every call is independent and the library keeps no state between calls except

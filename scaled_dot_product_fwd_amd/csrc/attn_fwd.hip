@@ -48,6 +48,7 @@
 #include "attn_common.h"
 
 typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 namespace {
 
@@ -349,7 +350,8 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
   //   * the wave raises its issue priority for the program, so that of two waves sharing a
   //     SIMD the one inside its MFMA stream is served first;
   //   * the probabilities P_s of tile j are computed in the SPS slots before PV step s (P_0 in
-  //     the QK slots of step 0), so the exponentials run under the MFMAs;
+  //     the QK slots of step 0), so the exponentials run under the MFMAs; with fp16 inputs
+  //     the rounded P_s is summed in the PV slots of step s;
   //   * the row maximum of tile j+1 is taken under the last PV MFMAs.
   // Scores of hidden keys arrive as -inf (see mask_tile), whose exponential is exactly 0;
   // c > 0 always (scale 0 runs with Q = 0). mxc is the row maximum of tile j; mxn returns that
@@ -360,9 +362,24 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
     update_max<D>(mxc, c, m, l, acc);
     const float mneg = (m == -INFINITY) ? 0.f : -m;
     float lsum = 0.f, pend1 = 0.f, pend2 = 0.f;
+    // fp16: the denominator is the sum of the rounded weights that multiply V, two per dot2
+    // (relative error of each weight at most 2^-11, so the LSE moves by at most ~5e-4); bf16
+    // weights round 4x coarser, so bf16 sums the fp32 exponentials one add each.
+    constexpr bool RSUM = DT == ATTN_F16;
+    auto psum = [&](u32x4 pk, int i) {
+      // (the element is copied out first: a bit cast of the element expression itself
+      // compiles to a read of element 0)
+      const uint32_t w = pk[i];
+      lsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w),
+                                    f16x2{(_Float16)1.0f, (_Float16)1.0f}, lsum, false);
+    };
     auto prob = [&](f32x8& pe, int ps, int e) {
       const float ex =
           __builtin_amdgcn_exp2f(__builtin_fmaf(sc[ps >> 1][8 * (ps & 1) + e], c, mneg));
+      if constexpr (RSUM) {
+        pe[e] = ex;
+        return;
+      }
       // Add the exponential from two calls (slots) earlier, so that no instruction in a slot
       // waits on one issued in the same slot, and keep the running sum here: otherwise the
       // compiler sinks all the additions past the MFMA stream.
@@ -378,7 +395,11 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
         f32x8 pe;
 #pragma unroll
         for (int e = 0; e < 8; ++e) prob(pe, s, e);
-        pv_step<DT, D>(acc, vbuf, f, s, M::pack(pe));
+        const u32x4 pk = M::pack(pe);
+        if constexpr (RSUM)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) psum(pk, i);
+        pv_step<DT, D>(acc, vbuf, f, s, pk);
       }
       l += lsum + pend1 + pend2;
       return;
@@ -421,6 +442,9 @@ __device__ __forceinline__ void attn_fwd_body(const Params& p) {
         const int u = k - QPS, pvi = s * OT + u;
         if (pvi + 3 < 4 * OT) vload(pvi + 3);
         acc[u] = M::run(vf[pvi], pb[s], acc[u]);
+        if constexpr (RSUM)
+#pragma unroll
+          for (int i = u * 4 / OT; i < (u + 1) * 4 / OT; ++i) psum(pb[s], i);
       }
       int ps, e0, ne;
       if (g < QPS) {
