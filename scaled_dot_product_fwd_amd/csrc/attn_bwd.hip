@@ -19,12 +19,13 @@
 //     64-key K/V tiles through LDS: S^T = K Q^T and dP^T = V dO^T on MFMA (lane = query, as in
 //     the forward), P and dS on the VALU, and dQ^T += K^T dS^T with K^T read through
 //     ds_read_b64_tr_b16. dQ is written once (no atomics).
-//   * bwd_dkdv: one workgroup per (batch, KV head, 128-key tile), 4 waves x 32 keys. Each wave
-//     keeps its keys' K fragments in registers and their V rows in LDS, and streams 32-query
-//     tiles of Q, dO, L * log2(e) and D of every query head of the group (only queries at or after the
-//     tile's first key under causal masking): S = Q K^T and dP = dO V^T (lane = key), P and dS
-//     on the VALU, dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read through
-//     ds_read_b64_tr_b16. dK and dV are written once.
+//   * bwd_dkdv: one workgroup per (batch, KV head, 128-key tile; under causal masking a pair of
+//     tiles of equal total work), 4 waves x 32 keys. Each wave keeps its keys' K fragments in
+//     registers and their V rows in LDS, and streams 32-query tiles of Q, dO, L * log2(e) and D
+//     of every query head of the group (only queries at or after the tile's first key under
+//     causal masking): S = Q K^T and dP = dO V^T (lane = key), P and dS on the VALU,
+//     dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read through ds_read_b64_tr_b16. dK
+//     and dV are written once.
 //
 // Inputs are [B, H, N, D] tensors of one 16-bit type given by (batch, head, row) strides with
 // contiguous rows (contiguous tensors are the default); dQ, dK, dV are written in that type
@@ -570,24 +571,24 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
   const int h = lane >> 5;
   const int ql = lane & 31;
 
-  // ---- work: (batch, KV head, 128-key tile). Each XCD owns whole KV heads and takes them in
-  // blocks of two; within a block the key tiles go in order of decreasing work (under causal
-  // masking tile kt sees N - 128 kt queries), both heads' tile 0 first. Longest-first keeps the
-  // XCD's last workgroups short (one KV head after the other left a ~20 % tail); blocks of two
-  // keep the Q / dO working set to two KV heads.
-  int kt, b, kvh, sp;
+  // ---- work: (batch, KV head, item). Under causal masking key tile kt sees N - 128 kt queries;
+  // item i then pairs tiles i and nkt - 1 - i, the first swept from the last query tile down,
+  // the second from its diagonal up, so that every item has the same work and the items of a
+  // KV head that start together stay at the same query tile throughout (the second sweep of
+  // item i starts at tile 4 (nkt - 1 - i) when the others' first sweeps have reached the same
+  // distance from the end): the XCD's L2 then serves each Q / dO tile to all of them. Without
+  // causal masking an item is one key tile, all of equal work. Each XCD runs its KV heads one
+  // after another, all items of a head together.
+  const int nwk = CAUSAL ? (p.nkt + 1) >> 1 : p.nkt;   // items per KV head
+  int pi, b, kvh, sp;
   {
-    // consecutive workgroups of one XCD take the `split` parts of one key tile
+    // consecutive workgroups of one XCD take the `split` parts of one item
     if (p.xcd_order) {
       const int xcd = blockIdx.x & 7, local0 = blockIdx.x >> 3;
       const int local = local0 / p.split;
       sp = local0 - local * p.split;
-      const int hpx = (p.B * p.Hkv) >> 3;
-      const int blk = (hpx & 1) ? 1 : 2;
-      const int pair = local / (blk * p.nkt);
-      const int r = local - pair * blk * p.nkt;
-      kt = r / blk;
-      const int head_local = pair * blk + (r - kt * blk);
+      const int head_local = local / nwk;
+      pi = local - head_local * nwk;
       const int kv_head = head_local * 8 + xcd;
       b = kv_head / p.Hkv;
       kvh = kv_head - b * p.Hkv;
@@ -595,262 +596,276 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
       const int wid = blockIdx.x / p.split;
       sp = blockIdx.x - wid * p.split;
       const int BK = p.B * p.Hkv;
-      kt = wid / BK;
-      const int bk = wid - kt * BK;
+      pi = wid / BK;
+      const int bk = wid - pi * BK;
       b = bk / p.Hkv;
       kvh = bk - b * p.Hkv;
     }
   }
-  const int k0 = kt * kBM;
-  const int kw = k0 + wave * 32;   // this wave's first key
-  const int key = kw + ql;         // this lane's key (MFMA output column)
   int kv_end = p.N;
   if (p.valid_len) kv_end = min(max(p.valid_len[b], 0), p.N);
   unsigned char* vreg = smem + BG::VREG + wave * 32 * G::ROW;   // this wave's 32 V rows
 
-  f32x16 dk[OT], dv[OT];
-#pragma unroll
-  for (int u = 0; u < OT; ++u) dk[u] = dv[u] = f32x16{};
+  // One key tile: its dK and dV, sweeping the query tiles down (first tile of an item) or up.
+  auto run_tile = [&](auto upc) {
+    constexpr bool up = decltype(upc)::value;
+    const int kt = up ? p.nkt - 1 - pi : pi;
+    const int k0 = kt * kBM;
+    const int kw = k0 + wave * 32;   // this wave's first key
+    const int key = kw + ql;         // this lane's key (MFMA output column)
 
-  const int qstart = CAUSAL ? k0 : 0;
-  const int ntq = k0 < kv_end ? (p.N - qstart + kQT - 1) / kQT : 0;   // query tiles per head
-  // this workgroup's share [it0, it0 + iters) of the key tile's ntq * group iterations (query
-  // tile major, query head minor)
-  const int total = ntq * p.group;
-  const int it0 = (int)((int64_t)total * sp / p.split);
-  const int iters = (int)((int64_t)total * (sp + 1) / p.split) - it0;
+    f32x16 dk[OT], dv[OT];
+#pragma unroll
+    for (int u = 0; u < OT; ++u) dk[u] = dv[u] = f32x16{};
 
-  if (iters > 0) {
-    // K^T fragments of this lane's key (B operand: K[key][16s + 8h .. +7]), sign/zero applied.
-    u32x4 kf[KSTEPS];
-    {
-      const uint16_t* ksrc = p.k + b * p.ks_b + kvh * p.ks_h + min(key, p.N - 1) * p.ks_n + 8 * h;
+    const int qstart = CAUSAL ? k0 : 0;
+    const int ntq = k0 < kv_end ? (p.N - qstart + kQT - 1) / kQT : 0;   // query tiles per head
+    // this workgroup's share [it0, it0 + iters) of the key tile's ntq * group iterations (query
+    // tile major, query head minor)
+    const int total = ntq * p.group;
+    const int it0 = (int)((int64_t)total * sp / p.split);
+    const int iters = (int)((int64_t)total * (sp + 1) / p.split) - it0;
+
+    if (iters > 0) {
+      // K^T fragments of this lane's key (B operand: K[key][16s + 8h .. +7]), sign/zero applied.
+      u32x4 kf[KSTEPS];
+      {
+        const uint16_t* ksrc =
+            p.k + b * p.ks_b + kvh * p.ks_h + min(key, p.N - 1) * p.ks_n + 8 * h;
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s)
-        kf[s] = (DCH == G::CH || 2 * s + h < DCH)
-                    ? (*(const u32x4*)(ksrc + 16 * s) ^ p.qsign) & p.qmask
-                    : u32x4{};
-    }
-    // V rows of this wave's keys into its LDS rows (bswz layout like Q and dO, so that one set
-    // of row-fragment offsets serves all three).
-    {
-      const uint32_t vrow = (uint32_t)p.vs_n * 2;
-      const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(p.v + b * p.vs_b + kvh * p.vs_h), (short)0, (p.N - 1) * vrow + 2 * DH,
-          kBufferFlags);
-#pragma unroll
-      for (int i = 0; i < 32 / G::RPB; ++i) {
-        const int row = i * G::RPB + lane / G::CH;
-        const int vc = (lane % G::CH) ^ G::bswz(row);
-        const uint32_t off =
-            (DCH < G::CH && vc >= DCH) ? kNoChunk : (lane / G::CH) * vrow + vc * 16;
-        dma16(vrs, vreg + i * 1024, off, (uint32_t)(kw + i * G::RPB) * vrow);
+        for (int s = 0; s < KSTEPS; ++s)
+          kf[s] = (DCH == G::CH || 2 * s + h < DCH)
+                      ? (*(const u32x4*)(ksrc + 16 * s) ^ p.qsign) & p.qmask
+                      : u32x4{};
       }
-    }
-    // DMA of the iteration over query head kvh * group + g, queries q0 .. q0+31, into buffer
-    // `buf`: Q and dO tiles (bswz layout), L and D (wave 0 and 1).
-    // Q and dO rows may have different strides: one chunk position per block, the row offsets
-    // applied per tensor.
-    const uint32_t qrowb = (uint32_t)p.qs_n * 2, growb = (uint32_t)p.gs_n * 2;
-    uint32_t qoff[BG::QLOADS], goff[BG::QLOADS];
+      // V rows of this wave's keys into its LDS rows (bswz layout like Q and dO, so that one set
+      // of row-fragment offsets serves all three).
+      {
+        const uint32_t vrow = (uint32_t)p.vs_n * 2;
+        const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(p.v + b * p.vs_b + kvh * p.vs_h), (short)0, (p.N - 1) * vrow + 2 * DH,
+            kBufferFlags);
 #pragma unroll
-    for (int i = 0; i < BG::QLOADS; ++i) {
-      const int row = (wave * BG::QLOADS + i) * G::RPB + lane / G::CH;   // row in the tile
-      const int qc = (lane % G::CH) ^ G::bswz(row);
-      const bool none = DCH < G::CH && qc >= DCH;
-      qoff[i] = none ? kNoChunk : (lane / G::CH) * qrowb + qc * 16;
-      goff[i] = none ? kNoChunk : (lane / G::CH) * growb + qc * 16;
-    }
-    auto dma = [&](int g, int q0, int buf) {
-      const int hq = kvh * p.group + g;
-      const int bh = b * p.Hq + hq;
-      const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(p.q + b * p.qs_b + hq * p.qs_h), (short)0, (p.N - 1) * qrowb + 2 * DH,
-          kBufferFlags);
-      const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(p.dout + b * p.gs_b + hq * p.gs_h), (short)0, (p.N - 1) * growb + 2 * DH,
-          kBufferFlags);
-      unsigned char* base = smem + buf * BG::BUF;
+        for (int i = 0; i < 32 / G::RPB; ++i) {
+          const int row = i * G::RPB + lane / G::CH;
+          const int vc = (lane % G::CH) ^ G::bswz(row);
+          const uint32_t off =
+              (DCH < G::CH && vc >= DCH) ? kNoChunk : (lane / G::CH) * vrow + vc * 16;
+          dma16(vrs, vreg + i * 1024, off, (uint32_t)(kw + i * G::RPB) * vrow);
+        }
+      }
+      // DMA of the iteration over query head kvh * group + g, queries q0 .. q0+31, into buffer
+      // `buf`: Q and dO tiles (bswz layout), L and D (wave 0 and 1).
+      // Q and dO rows may have different strides: one chunk position per block, the row offsets
+      // applied per tensor.
+      const uint32_t qrowb = (uint32_t)p.qs_n * 2, growb = (uint32_t)p.gs_n * 2;
+      uint32_t qoff[BG::QLOADS], goff[BG::QLOADS];
 #pragma unroll
       for (int i = 0; i < BG::QLOADS; ++i) {
-        const int blk = wave * BG::QLOADS + i;
-        const uint32_t r0 = (uint32_t)(q0 + blk * G::RPB);
-        dma16(qrs, base + blk * 1024, qoff[i], r0 * qrowb);
-        dma16(ors, base + BG::QTILE + blk * 1024, goff[i], r0 * growb);
+        const int row = (wave * BG::QLOADS + i) * G::RPB + lane / G::CH;   // row in the tile
+        const int qc = (lane % G::CH) ^ G::bswz(row);
+        const bool none = DCH < G::CH && qc >= DCH;
+        qoff[i] = none ? kNoChunk : (lane / G::CH) * qrowb + qc * 16;
+        goff[i] = none ? kNoChunk : (lane / G::CH) * growb + qc * 16;
       }
-      if (wave < 2) {
-        const float* src = wave == 0 ? p.lse2 : p.delta;
-        const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(src + (size_t)bh * p.N), (short)0, (uint32_t)p.N * 4, kBufferFlags);
-        // one dword per query row (lanes 0..31); a 16-byte load would straddle the end of the
-        // row range when N % 4 != 0. Lanes 32..63 are out of range and write zeros to bytes
-        // 128..255 of the wave's 1 KiB slot.
-        const uint32_t loff = lane < kQT ? (uint32_t)(q0 + lane) * 4 : 0x7ffffff0u;
-        dma4(lrs, base + 2 * BG::QTILE + wave * 1024, loff, 0);
-      }
-    };
-
-    // Fragment offsets: rows of Q / dO / V (A of S and dP, B of dP), transposed Q / dO.
-    uint32_t raddr[KSTEPS], taddr[OT];
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) raddr[ks] = ql * G::ROW + 16 * ((2 * ks + h) ^ G::bswz(ql));
-#pragma unroll
-    for (int u = 0; u < OT; ++u) taddr[u] = tr_offset<D>(lane, U0 + u);
-    const float c = p.c;
-
-    // Explicit mask: rows q0 .. q0+31 (query head g) x this wave's keys kw .. kw+31 into the
-    // wave's slot; lane L of block i writes row i * RPL + L / CPR, chunk L % CPR.
-    const uint32_t mrow = MK != kMaskNone ? (uint32_t)(p.ms_n * KM::ES) : 0;
-    const uint32_t mlane = MK != kMaskNone
-                               ? (uint32_t)(lane / KM::CPR) * mrow + (uint32_t)kw * KM::ES +
-                                     16 * (lane % KM::CPR)
-                               : 0;
-    auto mask_dma = [&](int g, int q0) {
-      if constexpr (MK != kMaskNone) {
+      auto dma = [&](int g, int q0, int buf) {
         const int hq = kvh * p.group + g;
-        const __amdgpu_buffer_rsrc_t mrs = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)((const unsigned char*)p.mask + (b * p.ms_b + hq * p.ms_h) * KM::ES),
-            (short)0, (p.N - 1) * mrow + ((p.N * KM::ES + 15) & ~15), kBufferFlags);
+        const int bh = b * p.Hq + hq;
+        const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(p.q + b * p.qs_b + hq * p.qs_h), (short)0, (p.N - 1) * qrowb + 2 * DH,
+            kBufferFlags);
+        const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(p.dout + b * p.gs_b + hq * p.gs_h), (short)0, (p.N - 1) * growb + 2 * DH,
+            kBufferFlags);
+        unsigned char* base = smem + buf * BG::BUF;
 #pragma unroll
-        for (int i = 0; i < KM::LOADS; ++i)
-          dma16(mrs, smem + MOFF + wave * KM::WB + i * 1024, mlane,
-                (uint32_t)(q0 + i * KM::RPL) * mrow);
-      }
-    };
+        for (int i = 0; i < BG::QLOADS; ++i) {
+          const int blk = wave * BG::QLOADS + i;
+          const uint32_t r0 = (uint32_t)(q0 + blk * G::RPB);
+          dma16(qrs, base + blk * 1024, qoff[i], r0 * qrowb);
+          dma16(ors, base + BG::QTILE + blk * 1024, goff[i], r0 * growb);
+        }
+        if (wave < 2) {
+          const float* src = wave == 0 ? p.lse2 : p.delta;
+          const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
+              (void*)(src + (size_t)bh * p.N), (short)0, (uint32_t)p.N * 4, kBufferFlags);
+          // one dword per query row (lanes 0..31); a 16-byte load would straddle the end of the
+          // row range when N % 4 != 0. Lanes 32..63 are out of range and write zeros to bytes
+          // 128..255 of the wave's 1 KiB slot.
+          const uint32_t loff = lane < kQT ? (uint32_t)(q0 + lane) * 4 : 0x7ffffff0u;
+          dma4(lrs, base + 2 * BG::QTILE + wave * 1024, loff, 0);
+        }
+      };
 
-    // Iteration order: query tile major, from the last tile down, query head minor. The
-    // key-tile workgroups of a KV head that run at the same time then read the same Q / dO tile
-    // at the same step, and the XCD's L2 serves all but the first (query head major, each head
-    // from qstart up, every workgroup read a different tile: 1.8x the HBM bytes, same time).
-    // State: (g, q0) of the tile being computed and of the next one to fetch.
-    const int qlast = qstart + (ntq - 1) * kQT;
-    const int t0 = it0 / p.group;
-    const int g0 = it0 - t0 * p.group, qs0 = qlast - t0 * kQT;
-    int g_cur = g0, q_cur = qs0, g_nxt = g0, q_nxt = qs0;
-    auto advance = [&](int& g, int& q0) {
-      if (++g == p.group) { g = 0; q0 -= kQT; }
-    };
-    dma(g_nxt, q_nxt, 0);
-    mask_dma(g_nxt, q_nxt);
-    advance(g_nxt, q_nxt);
-
-    auto step = [&](auto bufc, int it) {
-      constexpr int buf = decltype(bufc)::value;
-      wait_loads_and_lds();
-      __syncthreads();
-      const int gn = g_nxt, qn = q_nxt;   // the next iteration's tile
-      if (it + 1 < iters) {
-        dma(gn, qn, buf ^ 1);
-        advance(g_nxt, q_nxt);
-      }
-      const int q0 = q_cur;
-      advance(g_cur, q_cur);
-      // this iteration's mask values (query rows 8 (r/4) + 4h + r%4 of the tile, the lane's
-      // key), then the next iteration's DMA into the same slot. Keep masks are packed into
-      // one bit per element, additive values two per register.
-      // An additive mask enters as the starting value of the score accumulator (in raw score
-      // units), so that no mask register stays live across the MFMAs.
-      uint32_t kbits = 0;
-      f32x16 s = f32x16{};
-      if constexpr (MK != kMaskNone) {
-        const unsigned char* ms = smem + MOFF + wave * KM::WB + KM::ES * ql;
+      // Fragment offsets: rows of Q / dO / V (A of S and dP, B of dP), transposed Q / dO.
+      uint32_t raddr[KSTEPS], taddr[OT];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qi = 8 * (r >> 2) + 4 * h + (r & 3);
-          if constexpr (MK == kMaskKeep) {
-            // four bytes at a time, packed into bits as they arrive
-            kbits |= (ms[qi * KM::RB] != 0 ? 1u : 0u) << r;
-            if ((r & 3) == 3) asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(kbits) :: "memory");
-          } else {
-            const uint32_t bits = *(const uint16_t*)(ms + qi * KM::RB);
-            const float a = DT == ATTN_BF16 ? __uint_as_float(bits << 16)
-                                            : (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
-            s[r] = a * p.mscale;
+      for (int ks = 0; ks < KSTEPS; ++ks)
+        raddr[ks] = ql * G::ROW + 16 * ((2 * ks + h) ^ G::bswz(ql));
+#pragma unroll
+      for (int u = 0; u < OT; ++u) taddr[u] = tr_offset<D>(lane, U0 + u);
+      const float c = p.c;
+
+      // Explicit mask: rows q0 .. q0+31 (query head g) x this wave's keys kw .. kw+31 into the
+      // wave's slot; lane L of block i writes row i * RPL + L / CPR, chunk L % CPR.
+      const uint32_t mrow = MK != kMaskNone ? (uint32_t)(p.ms_n * KM::ES) : 0;
+      const uint32_t mlane = MK != kMaskNone
+                                 ? (uint32_t)(lane / KM::CPR) * mrow + (uint32_t)kw * KM::ES +
+                                       16 * (lane % KM::CPR)
+                                 : 0;
+      auto mask_dma = [&](int g, int q0) {
+        if constexpr (MK != kMaskNone) {
+          const int hq = kvh * p.group + g;
+          const __amdgpu_buffer_rsrc_t mrs = __builtin_amdgcn_make_buffer_rsrc(
+              (void*)((const unsigned char*)p.mask + (b * p.ms_b + hq * p.ms_h) * KM::ES),
+              (short)0, (p.N - 1) * mrow + ((p.N * KM::ES + 15) & ~15), kBufferFlags);
+#pragma unroll
+          for (int i = 0; i < KM::LOADS; ++i)
+            dma16(mrs, smem + MOFF + wave * KM::WB + i * 1024, mlane,
+                  (uint32_t)(q0 + i * KM::RPL) * mrow);
+        }
+      };
+
+      // Iteration order: query tile major (from the last tile down, or from qstart up in the
+      // second sweep of an item), query head minor. The key-tile workgroups of a KV head that run
+      // at the same time then read the same Q / dO tile at the same step, and the XCD's L2 serves
+      // all but the first (query head major, every workgroup reading a different tile, took 1.8x
+      // the HBM bytes). State: (g, q0) of the tile being computed and of the next one to fetch.
+      const int qlast = qstart + (ntq - 1) * kQT;
+      const int t0 = it0 / p.group;
+      const int dstep = up ? kQT : -kQT;
+      const int g0 = it0 - t0 * p.group, qs0 = up ? qstart + t0 * kQT : qlast - t0 * kQT;
+      int g_cur = g0, q_cur = qs0, g_nxt = g0, q_nxt = qs0;
+      auto advance = [&](int& g, int& q0) {
+        if (++g == p.group) { g = 0; q0 += dstep; }
+      };
+      dma(g_nxt, q_nxt, 0);
+      mask_dma(g_nxt, q_nxt);
+      advance(g_nxt, q_nxt);
+
+      auto step = [&](auto bufc, int it) {
+        constexpr int buf = decltype(bufc)::value;
+        wait_loads_and_lds();
+        __syncthreads();
+        const int gn = g_nxt, qn = q_nxt;   // the next iteration's tile
+        if (it + 1 < iters) {
+          dma(gn, qn, buf ^ 1);
+          advance(g_nxt, q_nxt);
+        }
+        const int q0 = q_cur;
+        advance(g_cur, q_cur);
+        // this iteration's mask values (query rows 8 (r/4) + 4h + r%4 of the tile, the lane's
+        // key), then the next iteration's DMA into the same slot. Keep masks are packed into
+        // one bit per element, additive values two per register.
+        // An additive mask enters as the starting value of the score accumulator (in raw score
+        // units), so that no mask register stays live across the MFMAs.
+        uint32_t kbits = 0;
+        f32x16 s = f32x16{};
+        if constexpr (MK != kMaskNone) {
+          const unsigned char* ms = smem + MOFF + wave * KM::WB + KM::ES * ql;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int qi = 8 * (r >> 2) + 4 * h + (r & 3);
+            if constexpr (MK == kMaskKeep) {
+              // four bytes at a time, packed into bits as they arrive
+              kbits |= (ms[qi * KM::RB] != 0 ? 1u : 0u) << r;
+              if ((r & 3) == 3) asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(kbits) :: "memory");
+            } else {
+              const uint32_t bits = *(const uint16_t*)(ms + qi * KM::RB);
+              const float a = DT == ATTN_BF16 ? __uint_as_float(bits << 16)
+                                              : (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+              s[r] = a * p.mscale;
+            }
           }
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          if (it + 1 < iters) mask_dma(gn, qn);
         }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        if (it + 1 < iters) mask_dma(gn, qn);
-      }
-      const unsigned char* qb = smem + buf * BG::BUF;
-      const unsigned char* ob = qb + BG::QTILE;
-      const float* lb = (const float*)(qb + 2 * BG::QTILE);
-      const float* db = (const float*)(qb + 2 * BG::QTILE + 1024);
-      // S = Q K^T and dP = dO V^T (rows: queries q0 + 8(r/4) + 4h + r%4; column: key)
-      f32x16 dp = f32x16{};
+        const unsigned char* qb = smem + buf * BG::BUF;
+        const unsigned char* ob = qb + BG::QTILE;
+        const float* lb = (const float*)(qb + 2 * BG::QTILE);
+        const float* db = (const float*)(qb + 2 * BG::QTILE + 1024);
+        // S = Q K^T and dP = dO V^T (rows: queries q0 + 8(r/4) + 4h + r%4; column: key)
+        f32x16 dp = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        s = M::run(*(const u32x4*)(qb + raddr[ks]), kf[ks], s);
-        dp = M::run(*(const u32x4*)(ob + raddr[ks]), *(const u32x4*)(vreg + raddr[ks]), dp);
-      }
-      // P and dS. The wave's 32 keys are all visible to the tile's 32 queries unless the tile
-      // touches the causal diagonal, the padding boundary or the end of the sequence; only then
-      // is each element tested. A hidden element may have L = -inf (a row with no visible key)
-      // and so x = inf: the select, not a product, removes it.
-      // (a keep mask is tested on every element; an additive one is already in the scores)
-      const bool full = MK != kMaskKeep && (!CAUSAL || q0 >= kw + 31) && kw + 32 <= kv_end &&
-                        q0 + kQT <= p.N;
-      float pr[16], ds[16];
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int qi0 = 8 * r4 + 4 * h;   // first of this group's 4 query rows in the tile
-        const f32x4 lv = *(const f32x4*)(lb + qi0);
-        const f32x4 dv4 = *(const f32x4*)(db + qi0);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * r4 + e;
-          pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lv[e]));
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+          s = M::run(*(const u32x4*)(qb + raddr[ks]), kf[ks], s);
+          dp = M::run(*(const u32x4*)(ob + raddr[ks]), *(const u32x4*)(vreg + raddr[ks]), dp);
         }
-        if (!full) {
+        // P and dS. The wave's 32 keys are all visible to the tile's 32 queries unless the tile
+        // touches the causal diagonal, the padding boundary or the end of the sequence; only then
+        // is each element tested. A hidden element may have L = -inf (a row with no visible key)
+        // and so x = inf: the select, not a product, removes it.
+        // (a keep mask is tested on every element; an additive one is already in the scores)
+        const bool full = MK != kMaskKeep && (!CAUSAL || q0 >= kw + 31) && kw + 32 <= kv_end &&
+                          q0 + kQT <= p.N;
+        float pr[16], ds[16];
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int qi0 = 8 * r4 + 4 * h;   // first of this group's 4 query rows in the tile
+          const f32x4 lv = *(const f32x4*)(lb + qi0);
+          const f32x4 dv4 = *(const f32x4*)(db + qi0);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int qi = q0 + qi0 + e;
-            bool vis = (!CAUSAL || key <= qi) && key < kv_end && qi < p.N;
-            if constexpr (MK == kMaskKeep) vis = vis && ((kbits >> (4 * r4 + e)) & 1u);
-            pr[4 * r4 + e] = vis ? pr[4 * r4 + e] : 0.f;
+            const int r = 4 * r4 + e;
+            pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lv[e]));
+          }
+          if (!full) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int qi = q0 + qi0 + e;
+              bool vis = (!CAUSAL || key <= qi) && key < kv_end && qi < p.N;
+              if constexpr (MK == kMaskKeep) vis = vis && ((kbits >> (4 * r4 + e)) & 1u);
+              pr[4 * r4 + e] = vis ? pr[4 * r4 + e] : 0.f;
+            }
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ds[4 * r4 + e] = pr[4 * r4 + e] * (dp[4 * r4 + e] - dv4[e]);
+        }
+        // dV^T += dO^T P and dK^T += Q^T dS over the two 16-query k-steps
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const u32x4 bp = pack8<DT>(pr, k2);
+          const u32x4 bs = pack8<DT>(ds, k2);
+#pragma unroll
+          for (int u = 0; u < OT; ++u) {
+            dv[u] = M::run(tr_frag(ob, taddr[u] + 16 * k2 * G::ROW, 8 * G::ROW), bp, dv[u]);
+            dk[u] = M::run(tr_frag(qb, taddr[u] + 16 * k2 * G::ROW, 8 * G::ROW), bs, dk[u]);
           }
         }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ds[4 * r4 + e] = pr[4 * r4 + e] * (dp[4 * r4 + e] - dv4[e]);
+      };
+      // two iterations per trip, one per buffer, so that the buffer offsets are constants
+      for (int it = 0; it < iters; it += 2) {
+        step(std::integral_constant<int, 0>{}, it);
+        if (it + 1 < iters) step(std::integral_constant<int, 1>{}, it + 1);
       }
-      // dV^T += dO^T P and dK^T += Q^T dS over the two 16-query k-steps
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        const u32x4 bp = pack8<DT>(pr, k2);
-        const u32x4 bs = pack8<DT>(ds, k2);
-#pragma unroll
-        for (int u = 0; u < OT; ++u) {
-          dv[u] = M::run(tr_frag(ob, taddr[u] + 16 * k2 * G::ROW, 8 * G::ROW), bp, dv[u]);
-          dk[u] = M::run(tr_frag(qb, taddr[u] + 16 * k2 * G::ROW, 8 * G::ROW), bs, dk[u]);
-        }
+      wait_loads_and_lds();
+    }
+    if (p.split > 1) {
+      // fp32 partial sums of this part; rows past N are not written
+      const size_t plane = (size_t)p.B * p.Hkv * p.N * DH;
+      float* pk = p.part + (size_t)sp * plane + ((size_t)b * p.Hkv + kvh) * p.N * DH;
+      if (key < p.N) {
+        store_part<D, DH, PART>(dk, p.scale, pk + (size_t)key * DH, h);
+        store_part<D, DH, PART>(dv, 1.0f, pk + (size_t)p.split * plane + (size_t)key * DH, h);
       }
-    };
-    // two iterations per trip, one per buffer, so that the buffer offsets are constants
-    for (int it = 0; it < iters; it += 2) {
-      step(std::integral_constant<int, 0>{}, it);
-      if (it + 1 < iters) step(std::integral_constant<int, 1>{}, it + 1);
+      return;
     }
-    wait_loads_and_lds();
+    __syncthreads();
+    // dK = scale * (dK^T)^T, dV = (dV^T)^T; rows past N are not written. Staging reuses the Q/dO
+    // buffers (every wave is past its last read).
+    unsigned char* ost = smem + wave * 32 * G::ROW;
+    store_rows<DT, D, DH, PART>(dk, p.scale, ost, p.dk + b * p.dks_b + kvh * p.dks_h, p.dks_n, kw,
+                                p.N,
+                          lane);
+    store_rows<DT, D, DH, PART>(dv, 1.0f, ost, p.dv + b * p.dvs_b + kvh * p.dvs_h, p.dvs_n, kw,
+                                p.N,
+                          lane);
+  };
+  run_tile(std::false_type{});
+  if (CAUSAL && p.nkt - 1 - pi != pi) {
+    __syncthreads();   // every wave is done with the first tile's buffers and staging
+    run_tile(std::true_type{});
   }
-  if (p.split > 1) {
-    // fp32 partial sums of this part; rows past N are not written
-    const size_t plane = (size_t)p.B * p.Hkv * p.N * DH;
-    float* pk = p.part + (size_t)sp * plane + ((size_t)b * p.Hkv + kvh) * p.N * DH;
-    if (key < p.N) {
-      store_part<D, DH, PART>(dk, p.scale, pk + (size_t)key * DH, h);
-      store_part<D, DH, PART>(dv, 1.0f, pk + (size_t)p.split * plane + (size_t)key * DH, h);
-    }
-    return;
-  }
-  __syncthreads();
-  // dK = scale * (dK^T)^T, dV = (dV^T)^T; rows past N are not written. Staging reuses the Q/dO
-  // buffers (every wave is past its last read).
-  unsigned char* ost = smem + wave * 32 * G::ROW;
-  store_rows<DT, D, DH, PART>(dk, p.scale, ost, p.dk + b * p.dks_b + kvh * p.dks_h, p.dks_n, kw,
-                              p.N,
-                        lane);
-  store_rows<DT, D, DH, PART>(dv, 1.0f, ost, p.dv + b * p.dvs_b + kvh * p.dvs_h, p.dvs_n, kw,
-                              p.N,
-                        lane);
 }
 
 // D = 256 holds 128 KiB of tiles in LDS: one workgroup per CU, one wave per SIMD with the
@@ -881,7 +896,7 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
 template <int DT, int D, bool CAUSAL, int MK>
 hipError_t launch_bwd(const BwdParams& p, hipStream_t s) {
   const int64_t nq = (int64_t)p.B * p.Hq * p.nqt;
-  const int64_t nk = (int64_t)p.B * p.Hkv * p.nkt * p.split;
+  const int64_t nk = (int64_t)p.B * p.Hkv * (CAUSAL ? (p.nkt + 1) / 2 : p.nkt) * p.split;
   hipLaunchKernelGGL((attn_bwd_dq_kernel<DT, D, CAUSAL, MK, 0>), dim3((unsigned)nq),
                      dim3(kThreads), 0, s, p);
   if constexpr (Parts<D>::NP > 1)
