@@ -93,6 +93,9 @@ struct BwdParams {
   // to part[2][split][B][Hkv][N][DH] and bwd_reduce adds them in split order.
   int split;
   float* part;
+  // 1: under causal masking each dK/dV workgroup takes key tiles i and nkt - 1 - i (see
+  // bwd_pairs); 0: one key tile each, longest first
+  int pair;
 };
 
 // The 4 keys 8g + 4h .. +3 of one mask row as read from a slot: uint8 bytes (keep) or 16-bit
@@ -551,7 +554,7 @@ struct KMaskGeo {
   static constexpr int RPL = 1024 / RB;                       // rows per DMA block
 };
 
-template <int DT, int DH, bool CAUSAL, int MK, int PART>
+template <int DT, int DH, bool CAUSAL, int MK, int PART, bool PAIR>
 __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
   constexpr int D = DH < 64 ? 64 : DH;   // geometry (as in the dQ kernel)
   constexpr int DCH = DH / 8;
@@ -571,15 +574,17 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
   const int h = lane >> 5;
   const int ql = lane & 31;
 
-  // ---- work: (batch, KV head, item). Under causal masking key tile kt sees N - 128 kt queries;
-  // item i then pairs tiles i and nkt - 1 - i, the first swept from the last query tile down,
-  // the second from its diagonal up, so that every item has the same work and the items of a
-  // KV head that start together stay at the same query tile throughout (the second sweep of
-  // item i starts at tile 4 (nkt - 1 - i) when the others' first sweeps have reached the same
-  // distance from the end): the XCD's L2 then serves each Q / dO tile to all of them. Without
-  // causal masking an item is one key tile, all of equal work. Each XCD runs its KV heads one
-  // after another, all items of a head together.
-  const int nwk = CAUSAL ? (p.nkt + 1) >> 1 : p.nkt;   // items per KV head
+  // ---- work: (batch, KV head, item). Under causal masking key tile kt sees N - 128 kt queries.
+  // Paired (PAIR, causal only): item i is the pair of key tiles i and nkt - 1 - i, the first swept from
+  // the last query tile down, the second from its diagonal up, so that every item has the same
+  // work and the items of a KV head that start together stay at the same query tile throughout
+  // (the second sweep of item i starts at tile 4 (nkt - 1 - i) when the others' first sweeps
+  // have reached the same distance from the end): the XCD's L2 then serves each Q / dO tile to
+  // all of them. Each XCD runs its KV heads one after another, all items of a head together.
+  // Unpaired: an item is one key tile, swept down; each XCD takes its KV heads in blocks of two,
+  // longest tiles first within a block (one head after another would leave a tail of long
+  // workgroups), both heads' tile 0 first.
+  const int nwk = PAIR ? (p.nkt + 1) >> 1 : p.nkt;   // items per KV head
   int pi, b, kvh, sp;
   {
     // consecutive workgroups of one XCD take the `split` parts of one item
@@ -587,8 +592,18 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
       const int xcd = blockIdx.x & 7, local0 = blockIdx.x >> 3;
       const int local = local0 / p.split;
       sp = local0 - local * p.split;
-      const int head_local = local / nwk;
-      pi = local - head_local * nwk;
+      int head_local;
+      if constexpr (PAIR) {
+        head_local = local / nwk;
+        pi = local - head_local * nwk;
+      } else {
+        const int hpx = (p.B * p.Hkv) >> 3;
+        const int blk = (hpx & 1) ? 1 : 2;
+        const int pair = local / (blk * nwk);
+        const int r = local - pair * blk * nwk;
+        pi = r / blk;
+        head_local = pair * blk + (r - pi * blk);
+      }
       const int kv_head = head_local * 8 + xcd;
       b = kv_head / p.Hkv;
       kvh = kv_head - b * p.Hkv;
@@ -862,9 +877,11 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
                           lane);
   };
   run_tile(std::false_type{});
-  if (CAUSAL && p.nkt - 1 - pi != pi) {
-    __syncthreads();   // every wave is done with the first tile's buffers and staging
-    run_tile(std::true_type{});
+  if constexpr (PAIR) {
+    if (p.nkt - 1 - pi != pi) {
+      __syncthreads();   // every wave is done with the first tile's buffers and staging
+      run_tile(std::true_type{});
+    }
   }
 }
 
@@ -882,13 +899,24 @@ void attn_bwd_dq_kernel(BwdParams p) {
 #endif
 }
 
-template <int DT, int D, bool CAUSAL, int MK, int PART>
+template <int DT, int D, bool CAUSAL, int MK, int PART, bool PAIR>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(bwd_waves_per_eu<D, MK>(), bwd_waves_per_eu<D, MK>())))
 void attn_bwd_dkdv_kernel(BwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  bwd_dkdv_body<DT, D, CAUSAL, MK, PART>(p);
+  bwd_dkdv_body<DT, D, CAUSAL, MK, PART, PAIR>(p);
 #endif
+}
+
+// The dK/dV kernel's parts, one workgroup per key tile or (PAIR) per pair of key tiles.
+template <int DT, int D, bool CAUSAL, int MK, bool PAIR>
+void launch_dkdv(const BwdParams& p, hipStream_t s) {
+  const int64_t nk = (int64_t)p.B * p.Hkv * (PAIR ? (p.nkt + 1) / 2 : p.nkt) * p.split;
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DT, D, CAUSAL, MK, 0, PAIR>), dim3((unsigned)nk),
+                     dim3(kThreads), 0, s, p);
+  if constexpr (Parts<D>::NP > 1)
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DT, D, CAUSAL, MK, 1, PAIR>), dim3((unsigned)nk),
+                       dim3(kThreads), 0, s, p);
 }
 
 // The dQ kernel's parts, then the dK/dV kernel's (it reads the workspace the first dQ part
@@ -896,7 +924,6 @@ void attn_bwd_dkdv_kernel(BwdParams p) {
 template <int DT, int D, bool CAUSAL, int MK>
 hipError_t launch_bwd(const BwdParams& p, hipStream_t s) {
   const int64_t nq = (int64_t)p.B * p.Hq * p.nqt;
-  const int64_t nk = (int64_t)p.B * p.Hkv * (CAUSAL ? (p.nkt + 1) / 2 : p.nkt) * p.split;
   hipLaunchKernelGGL((attn_bwd_dq_kernel<DT, D, CAUSAL, MK, 0>), dim3((unsigned)nq),
                      dim3(kThreads), 0, s, p);
   if constexpr (Parts<D>::NP > 1)
@@ -904,11 +931,14 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t s) {
                        dim3(kThreads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DT, D, CAUSAL, MK, 0>), dim3((unsigned)nk),
-                     dim3(kThreads), 0, s, p);
-  if constexpr (Parts<D>::NP > 1)
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DT, D, CAUSAL, MK, 1>), dim3((unsigned)nk),
-                       dim3(kThreads), 0, s, p);
+  if constexpr (CAUSAL && MK != kMaskAdd) {   // (bwd_pairs never pairs an additive mask)
+    if (p.pair)
+      launch_dkdv<DT, D, true, MK, true>(p, s);
+    else
+      launch_dkdv<DT, D, true, MK, false>(p, s);
+  } else {
+    launch_dkdv<DT, D, CAUSAL, MK, false>(p, s);
+  }
   return hipGetLastError();
 }
 
@@ -966,6 +996,21 @@ int64_t ws_floats_for(int B, int Hq, int Hkv, int N, int D, int split) {
 // (twice the 512 the device holds at once), as long as a part keeps about 32 iterations of a
 // key tile's average (half of its group * N / 32 query tiles) to pay for writing and reading
 // its partial sums, and as far as the workspace holds them.
+// Paired dK/dV items under causal masking all take the same time, so they run in whole rounds
+// of the device's resident workgroups (256 CUs x the kernel's workgroups per CU): pair only
+// when the items fill their last round (at least 15/16 of it) and no additive mask is given
+// (measured on the headline shape: unmasked same time with a third of the HBM bytes, keep mask
+// -10 %, additive mask +3 %, D = 64 with 1.33 rounds +6.5 %).
+int bwd_pairs(int B, int Hkv, int N, int D, int split, int mask_type) {
+  if (mask_type == ATTN_MASK_ADD) return 0;
+  const int64_t nkt = (N + kBM - 1) / kBM;
+  const int64_t items = (int64_t)B * Hkv * ((nkt + 1) / 2) * split;
+  const int per_cu = D > 128 ? 1 : (D <= 64 && mask_type == ATTN_MASK_NONE ? 3 : 2);
+  const int64_t slots = 256 * (int64_t)per_cu;
+  const int64_t rounds = (items + slots - 1) / slots;
+  return items * 16 >= rounds * slots * 15 ? 1 : 0;
+}
+
 int bwd_split(int B, int Hq, int Hkv, int N, int D, int64_t ws_floats) {
   const int64_t tiles = (int64_t)B * Hkv * ((N + kBM - 1) / kBM);
   const int64_t avg_iters = (int64_t)(Hq / Hkv) * ((N + kQT - 1) / kQT) / 2;
@@ -1148,6 +1193,7 @@ int bwd_run(const BwdLayouts& t, const float* lse, float* ws, int64_t ws_floats,
   p.mscale = kLog2e / p.c;
   p.split = split;
   p.part = part;
+  p.pair = causal ? bwd_pairs(B, Hkv, N, D, split, mk.type) : 0;
   hipError_t e = dtype == ATTN_BF16 ? dispatch_bwd<ATTN_BF16>(p, D, causal != 0, mk.type, hs)
                                     : dispatch_bwd<ATTN_F16>(p, D, causal != 0, mk.type, hs);
   if (e == hipSuccess && split > 1) e = launch_reduce(t, part, B, Hkv, N, D, split, dtype, hs);

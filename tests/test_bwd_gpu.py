@@ -382,6 +382,66 @@ def test_bwd_f32_split_masked(kind):
     log("f32 split masked %s: rel err dQ %.2e dK %.2e dV %.2e" % (kind, *e))
 
 
+def pairs_key_tiles(case, split, mask="none"):
+    """Whether the dK/dV kernel pairs key tiles i and nkt - 1 - i for this call: under causal
+    masking, without an additive mask, when the pairs fill at least 15/16 of their last round of
+    resident workgroups (256 CUs x 1, 2 or 3 per CU by head dim and mask)."""
+    nkt = -(-case.N // 128)
+    items = case.B * case.Hkv * ((nkt + 1) // 2) * split
+    per_cu = 1 if case.D > 128 else (3 if case.D <= 64 and mask == "none" else 2)
+    slots = 256 * per_cu
+    rounds = -(-items // slots)
+    return bool(case.causal) and mask != "add" and items * 16 >= rounds * slots * 15
+
+
+# (dtype, D, padded, B, Hq, Hkv, N, split workspace): paired dK/dV items at small N: an even
+# key-tile count (tiles 0 and 1), an odd one (0 with 2, 1 alone) with padding, and pairs whose
+# work is also split over two workgroups each.
+BWD_PAIRED = [
+    ("bf16", 128, False, 8, 64, 64, 256, False),
+    ("f16", 128, True, 4, 64, 64, 384, False),
+    ("bf16", 128, False, 2, 128, 32, 1024, True),
+]
+
+
+@pytest.mark.parametrize("cfg", BWD_PAIRED, ids=lambda c: "%s-D%d-p%d-B%d-H%d-%d-N%d-ws%d" % c)
+def test_bwd_paired_key_tiles(cfg):
+    dtype, D, padded, B, Hq, Hkv, N, split_ws = cfg
+    case = inputs.make_case(B, Hq, Hkv, N, D, dtype, True, padded, seed=[251, N, B])
+    split = split_of(case) if split_ws else 1
+    assert pairs_key_tiles(case, split), "shape %s does not pair its key tiles" % (cfg,)
+    if split_ws:
+        assert split > 1
+    dout = inputs.make_grad(case, [251, N, B])
+    log("bwd paired case %s (split %d) valid_len %s" % (cfg, split, case.valid_len))
+    compare_case(case, dout, "%s paired" % (cfg,), split_ws=split_ws)
+
+
+def test_bwd_paired_key_tiles_keep_mask():
+    """Paired dK/dV items with a keep mask (random per head) on top of the causal mask."""
+    import torch
+    from gpu_util import device_mask, mask_values
+    case = inputs.make_case(8, 64, 64, 256, 128, "bf16", True, False, seed=253)
+    assert pairs_key_tiles(case, 1, "keep")
+    dout_bits = inputs.make_grad(case, 253)
+    rng = np.random.default_rng(255)
+    mv = mask_values("keep", "random_bh", "bf16", 8, 64, 256, rng)
+    dmask = device_mask("keep", "random_bh", "bf16", mv, 256)
+    q, k, v, do = (to_device(x, "bf16") for x in (case.q_bits, case.k_bits, case.v_bits,
+                                                   dout_bits))
+    out, lse = sdp.forward(q, k, v, causal=True, scale=case.scale, attn_mask=dmask)
+    dq, dk, dv = sdp.backward(q, k, v, out, do, lse, causal=True, scale=case.scale,
+                              attn_mask=dmask)
+    torch.cuda.synchronize()
+    got = [from_device(t, "bf16") for t in (dq, dk, dv)]
+    qw, kw, vw = case.widened()
+    ref = oracle.attn_bwd(qw, kw, vw, inputs.widen(dout_bits, "bf16"), case.scale, True, None,
+                          keep_mask=mv)
+    e = [check_grad(n, g, r, "bf16", "paired keep mask") for n, g, r in
+         zip(("dQ", "dK", "dV"), got, ref)]
+    log("paired keep mask: rel err dQ %.2e dK %.2e dV %.2e" % tuple(e))
+
+
 def test_bwd_rising_row_maximum():
     """Keys scaled up along the sequence: rows whose maximum moves from tile to tile, so P
     rebuilt from the forward's LSE must still match."""
