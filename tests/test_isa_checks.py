@@ -4,7 +4,8 @@ The forward issues its K/V/mask buffer loads into LDS through inline asm (attn_c
 dma16_at): the compiler sets M0 for it (an operand constraint) but cannot see the load itself,
 so the asm carries the wait states the hardware needs after a scalar write of M0 or a VALU write
 of an SGPR the load reads; and the point of the asm form is that the compiler inserts no vmcnt
-wait before the transposed V reads. Both are properties of the generated code, checked here.
+wait before the transposed V reads. Both are properties of the generated code, checked here,
+as is the fp16 row sum's use of every weight register (a compiler pitfall seen once).
 """
 import os
 import re
@@ -81,3 +82,35 @@ def test_no_dma_wait_before_transposed_reads(fwd_asm):
         for i, line in enumerate(body[:-1]):
             if "s_waitcnt vmcnt" in line:
                 assert "ds_read_b64_tr_b16" not in body[i + 1], (name, line, body[i + 1])
+
+
+def test_fp16_row_sum_reads_every_weight(fwd_asm):
+    # fp16 kernels sum the rounded weights of a tile with v_dot2 (two per instruction): no dot2
+    # may read the same register as the previous dot2 into its accumulator unless something
+    # wrote that register in between (a bit cast of a vector element once compiled to a read
+    # of element 0 for all four words of a weight fragment)
+    seen = 0
+    for name, body in kernels(fwd_asm):
+        if "attn_fwd_kernelILi0E" not in name:   # ATTN_F16 = 0
+            continue
+        last = {}   # accumulator -> (source register, line index) within one basic block
+        for i, line in enumerate(body):
+            if re.match(r"^\.LBB|\s*s_(c?branch|setpc)", line):
+                last = {}
+                continue
+            m = re.match(r"\s*v_dot2c?_f32_f16\S*\s+(v\d+),\s*\S+,\s*(v\d+)", line)
+            if not m:
+                continue
+            acc, src = m.groups()
+            seen += 1
+            if acc in last and last[acc][0] == src:
+                between = body[last[acc][1] + 1:i]
+                wrote = any(re.match(r"\s*[vsd]\S*\s+%s\b" % src, t) or
+                            re.match(r"\s*[vsd]\S*\s+v\[(\d+):(\d+)\]", t) and
+                            int(re.match(r"\s*[vsd]\S*\s+v\[(\d+):(\d+)\]", t).group(1)) <=
+                            int(src[1:]) <=
+                            int(re.match(r"\s*[vsd]\S*\s+v\[(\d+):(\d+)\]", t).group(2))
+                            for t in between)
+                assert wrote, (name, line.strip())
+            last[acc] = (src, i)
+    assert seen > 0
