@@ -396,11 +396,14 @@ def pairs_key_tiles(case, split, mask="none"):
 
 # (dtype, D, padded, B, Hq, Hkv, N, split workspace): paired dK/dV items at small N: an even
 # key-tile count (tiles 0 and 1), an odd one (0 with 2, 1 alone) with padding and a ragged last
-# tile, and pairs whose work is also split over two workgroups each.
+# tile, pairs whose work is also split over two workgroups each, and the D = 256 and D = 64
+# kernels.
 BWD_PAIRED = [
     ("bf16", 128, False, 8, 64, 64, 256, False),
     ("f16", 128, True, 4, 64, 64, 380, False),
     ("bf16", 128, False, 2, 128, 32, 1024, True),
+    ("bf16", 256, False, 4, 64, 64, 129, False),   # two head-dim parts, one workgroup per CU
+    ("f16", 64, True, 8, 96, 96, 200, False),      # three workgroups per CU
 ]
 
 
