@@ -931,7 +931,7 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t s) {
                        dim3(kThreads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if constexpr (CAUSAL && MK != kMaskAdd) {   // (bwd_pairs never pairs an additive mask)
+  if constexpr (CAUSAL && MK != kMaskAdd && D <= 128) {   // (bwd_pairs pairs no others)
     if (p.pair)
       launch_dkdv<DT, D, true, MK, true>(p, s);
     else
@@ -998,14 +998,15 @@ int64_t ws_floats_for(int B, int Hq, int Hkv, int N, int D, int split) {
 // its partial sums, and as far as the workspace holds them.
 // Paired dK/dV items under causal masking all take the same time, so they run in whole rounds
 // of the device's resident workgroups (256 CUs x the kernel's workgroups per CU): pair only
-// when the items fill their last round (at least 15/16 of it) and no additive mask is given
-// (measured on the headline shape: unmasked same time with a third of the HBM bytes, keep mask
-// -10 %, additive mask +3 %, D = 64 with 1.33 rounds +6.5 %).
+// when the items fill their last round (at least 15/16 of it), up to D = 128 and without an
+// additive mask (measured on the headline shape: unmasked same time with a third of the HBM
+// bytes, keep mask -10 %, additive mask +3 %, D = 64 with 1.33 rounds +6.5 %, D = 256 in four
+// whole rounds +2.7 %).
 int bwd_pairs(int B, int Hkv, int N, int D, int split, int mask_type) {
-  if (mask_type == ATTN_MASK_ADD) return 0;
+  if (mask_type == ATTN_MASK_ADD || D > 128) return 0;
   const int64_t nkt = (N + kBM - 1) / kBM;
   const int64_t items = (int64_t)B * Hkv * ((nkt + 1) / 2) * split;
-  const int per_cu = D > 128 ? 1 : (D <= 64 && mask_type == ATTN_MASK_NONE ? 3 : 2);
+  const int per_cu = D <= 64 && mask_type == ATTN_MASK_NONE ? 3 : 2;
   const int64_t slots = 256 * (int64_t)per_cu;
   const int64_t rounds = (items + slots - 1) / slots;
   return items * 16 >= rounds * slots * 15 ? 1 : 0;

@@ -384,25 +384,24 @@ def test_bwd_f32_split_masked(kind):
 
 def pairs_key_tiles(case, split, mask="none"):
     """Whether the dK/dV kernel pairs key tiles i and nkt - 1 - i for this call: under causal
-    masking, without an additive mask, when the pairs fill at least 15/16 of their last round of
-    resident workgroups (256 CUs x 1, 2 or 3 per CU by head dim and mask)."""
+    masking, up to D = 128, without an additive mask, when the pairs fill at least 15/16 of their
+    last round of resident workgroups (256 CUs x 2 or 3 per CU by head dim and mask)."""
     nkt = -(-case.N // 128)
     items = case.B * case.Hkv * ((nkt + 1) // 2) * split
-    per_cu = 1 if case.D > 128 else (3 if case.D <= 64 and mask == "none" else 2)
+    per_cu = 3 if case.D <= 64 and mask == "none" else 2
     slots = 256 * per_cu
     rounds = -(-items // slots)
-    return bool(case.causal) and mask != "add" and items * 16 >= rounds * slots * 15
+    return (bool(case.causal) and mask != "add" and case.D <= 128 and
+            items * 16 >= rounds * slots * 15)
 
 
 # (dtype, D, padded, B, Hq, Hkv, N, split workspace): paired dK/dV items at small N: an even
 # key-tile count (tiles 0 and 1), an odd one (0 with 2, 1 alone) with padding and a ragged last
-# tile, pairs whose work is also split over two workgroups each, and the D = 256 and D = 64
-# kernels.
+# tile, pairs whose work is also split over two workgroups each, and the D = 64 kernel.
 BWD_PAIRED = [
     ("bf16", 128, False, 8, 64, 64, 256, False),
     ("f16", 128, True, 4, 64, 64, 380, False),
     ("bf16", 128, False, 2, 128, 32, 1024, True),
-    ("bf16", 256, False, 4, 64, 64, 129, False),   # two head-dim parts, one workgroup per CU
     ("f16", 64, True, 8, 96, 96, 200, False),      # three workgroups per CU
 ]
 
