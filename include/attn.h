@@ -165,11 +165,12 @@ int attn_fwd_validate(const void *q, const void *k, const void *v, const void *o
  *   all else       as in attn_fwd.
  *
  * Every stride must be >= 0 and a multiple of 16 bytes (8 elements of a 16-bit type, 4 of fp32),
- * and row strides >= D (ATTN_ERR_LAYOUT otherwise). Inputs may share memory with each other (for instance Q, K and V as views of one
- * packed tensor, or a zero batch stride). The output's rows must be distinct (its strides,
- * ordered, must each step past the extent of the smaller ones). For the alias check each tensor
- * counts as the whole byte range from its pointer to the end of its last row, so out must lie
- * outside the ranges of q, k, v and lse. Returns as attn_fwd.
+ * and row strides >= D (ATTN_ERR_LAYOUT otherwise). Inputs may share memory with each other
+ * (for instance Q, K and V as views of one packed tensor, or a zero batch stride). The output's
+ * rows must be distinct (its strides, ordered, must each step past the extent of the smaller
+ * ones). For the alias check each tensor counts as the whole byte range from its pointer to the
+ * end of its last row, so out must lie outside the ranges of q, k, v and lse. Returns as
+ * attn_fwd.
  */
 int attn_fwd_strided(const void *q, const int64_t *q_strides, const void *k,
                      const int64_t *k_strides, const void *v, const int64_t *v_strides,
@@ -241,7 +242,8 @@ int attn_fwd_masked_validate(const void *q, const int64_t *q_strides, const void
  * one workgroup per chunk writes the chunk's fp32 output, normalised by its own sum, and its
  * log-sum-exp, and a second kernel combines the chunks of every row:
  *
- *     M = max_c L_c,   O = sum_c 2^(L_c - M) O_c / sum_c 2^(L_c - M),   L = M + log2 sum_c 2^(L_c - M)
+ *     M = max_c L_c,   O = sum_c 2^(L_c - M) O_c / sum_c 2^(L_c - M),
+ *     L = M + log2 sum_c 2^(L_c - M)
  *
  * (L in base 2). Below those bounds a call's time is mostly fixed costs (launch, prologue,
  * epilogue) that a split only adds to, and the call runs as attn_fwd_strided. This is the

@@ -575,12 +575,13 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
   const int ql = lane & 31;
 
   // ---- work: (batch, KV head, item). Under causal masking key tile kt sees N - 128 kt queries.
-  // Paired (PAIR, causal only): item i is the pair of key tiles i and nkt - 1 - i, the first swept from
-  // the last query tile down, the second from its diagonal up, so that every item has the same
-  // work and the items of a KV head that start together stay at the same query tile throughout
-  // (the second sweep of item i starts at tile 4 (nkt - 1 - i) when the others' first sweeps
-  // have reached the same distance from the end): the XCD's L2 then serves each Q / dO tile to
-  // all of them. Each XCD runs its KV heads one after another, all items of a head together.
+  // Paired (PAIR, causal only): item i is the pair of key tiles i and nkt - 1 - i, the first
+  // swept from the last query tile down, the second from its diagonal up, so that every item
+  // has the same work and the items of a KV head that start together stay at the same query
+  // tile throughout (the second sweep of item i starts at tile 4 (nkt - 1 - i) when the others'
+  // first sweeps have reached the same distance from the end): the XCD's L2 then serves each
+  // Q / dO tile to all of them. Each XCD runs its KV heads one after another, all items of a
+  // head together.
   // Unpaired: an item is one key tile, swept down; each XCD takes its KV heads in blocks of two,
   // longest tiles first within a block (one head after another would leave a tail of long
   // workgroups), both heads' tile 0 first.
@@ -599,10 +600,10 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
       } else {
         const int hpx = (p.B * p.Hkv) >> 3;
         const int blk = (hpx & 1) ? 1 : 2;
-        const int pair = local / (blk * nwk);
-        const int r = local - pair * blk * nwk;
+        const int block = local / (blk * nwk);
+        const int r = local - block * blk * nwk;
         pi = r / blk;
-        head_local = pair * blk + (r - pi * blk);
+        head_local = block * blk + (r - pi * blk);
       }
       const int kv_head = head_local * 8 + xcd;
       b = kv_head / p.Hkv;

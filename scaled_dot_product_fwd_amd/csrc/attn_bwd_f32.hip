@@ -2,8 +2,8 @@
 // with dtype ATTN_F32.
 //
 // Same gradients and the same two-kernel, atomic-free split as the 16-bit backward (attn_bwd.hip;
-// tiny_flash_attn_triton.py keeps the forward's L for its backward pass): with P = exp(scale * q.k - L)
-// on the visible keys and D_i = sum_d dO[i,d] O[i,d],
+// tiny_flash_attn_triton.py keeps the forward's L for its backward pass): with
+// P = exp(scale * q.k - L) on the visible keys and D_i = sum_d dO[i,d] O[i,d],
 //
 //   dP = dO V^T,  dS = P o (dP - D),  dQ = scale * dS K,  dK = scale * dS^T Q,  dV = P^T dO,
 //

@@ -801,7 +801,8 @@ __global__ __launch_bounds__(256) void attn_fwd_merge_kernel(MergeParams mp) {
   const uint32_t w0 = (uint32_t)M::round1(o[0]) | ((uint32_t)M::round1(o[1]) << 16);
   const uint32_t w1 = (uint32_t)M::round1(o[2]) | ((uint32_t)M::round1(o[3]) << 16);
   *(u32x2*)(mp.o + b * mp.os_b + hq * mp.os_h + i * mp.os_n + d0) = u32x2{w0, w1};
-  if (mp.lse && d0 == 0) mp.lse[(size_t)bh * mp.N + i] = lse2 == -INFINITY ? -INFINITY : lse2 * kLn2;
+  if (mp.lse && d0 == 0)
+    mp.lse[(size_t)bh * mp.N + i] = lse2 == -INFINITY ? -INFINITY : lse2 * kLn2;
 }
 
 template <int DT, int D, bool CAUSAL, int MK>
@@ -822,11 +823,14 @@ template <int DT>
 hipError_t dispatch_split(const Params& p, int D, bool causal, int64_t nwg, hipStream_t s) {
   switch (D) {
     case 16:
-      return causal ? launch_split<DT, 16, true>(p, nwg, s) : launch_split<DT, 16, false>(p, nwg, s);
+      return causal ? launch_split<DT, 16, true>(p, nwg, s)
+                    : launch_split<DT, 16, false>(p, nwg, s);
     case 32:
-      return causal ? launch_split<DT, 32, true>(p, nwg, s) : launch_split<DT, 32, false>(p, nwg, s);
+      return causal ? launch_split<DT, 32, true>(p, nwg, s)
+                    : launch_split<DT, 32, false>(p, nwg, s);
     case 64:
-      return causal ? launch_split<DT, 64, true>(p, nwg, s) : launch_split<DT, 64, false>(p, nwg, s);
+      return causal ? launch_split<DT, 64, true>(p, nwg, s)
+                    : launch_split<DT, 64, false>(p, nwg, s);
     case 256:
       return causal ? launch_split<DT, 256, true>(p, nwg, s)
                     : launch_split<DT, 256, false>(p, nwg, s);

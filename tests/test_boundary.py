@@ -23,12 +23,14 @@ def lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attn_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attn_\w+)\s*\(", text,
+                                 flags=re.M)))
 
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["attn_bwd", "attn_bwd_masked", "attn_bwd_masked_validate",
-                                    "attn_bwd_scratch", "attn_bwd_strided", "attn_bwd_strided_validate",
+                                    "attn_bwd_scratch", "attn_bwd_strided",
+                                    "attn_bwd_strided_validate",
                                     "attn_bwd_validate", "attn_bwd_workspace_floats",
                                     "attn_bwd_ws", "attn_bwd_ws_validate", "attn_fwd",
                                     "attn_fwd_masked", "attn_fwd_masked_validate",
