@@ -247,6 +247,32 @@ def test_rising_row_maximum():
         compare(case, O, L, O_ref, L_ref, tag="rising causal=%d" % causal)
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("where", ["first", "last"])
+def test_weights_below_the_fp16_normal_range(dtype, where):
+    """One key scores 10.4 above the 4095 others, whose weights e^-10.4 ~ 3.0e-5 lie below the
+    smallest normal fp16 value (6.1e-5) once rounded for P V (and, with fp16 inputs, for the row
+    sum): together they hold 11 % of each row's mass, so flushing them to zero would move O by
+    0.11 and LSE by 0.12. V is 0 on the large key and 1 elsewhere. With the large key last, the
+    reference maximum jumps by 15 (log2 units) at the last tile and the accumulated state is
+    rescaled."""
+    import torch
+    N, D = 4096, 64
+    j = 0 if where == "first" else N - 1
+    q = np.zeros((1, 2, N, D), np.float32)
+    q[..., 0] = 1.0
+    k = np.zeros((1, 1, N, D), np.float32)
+    k[0, 0, j, 0] = 10.4
+    v = np.ones((1, 1, N, D), np.float32)
+    v[0, 0, j, :] = 0.0
+    case = inputs.make_case(1, 2, 1, N, D, dtype, False, False, seed=12, scale=1.0)
+    case.q_bits, case.k_bits, case.v_bits = (inputs.round_bits(x, dtype) for x in (q, k, v))
+    O, L = run_device(case)
+    O_ref, L_ref = run_oracle(case)
+    assert O_ref[0, 0, 0, 0] > 0.1
+    compare(case, O, L, O_ref, L_ref, tag="small weights %s %s" % (dtype, where))
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_tiny_flash_attn_triton_workload(causal):
     """The workload of the Triton file's own test: B=1, H=2, N=1024, D=64, fp16 values drawn
