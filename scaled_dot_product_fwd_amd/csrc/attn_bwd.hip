@@ -622,6 +622,16 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
   if (p.valid_len) kv_end = min(max(p.valid_len[b], 0), p.N);
   unsigned char* vreg = smem + BG::VREG + wave * 32 * G::ROW;   // this wave's 32 V rows
 
+  // Rows of the group's first query head in Q, dO and (waves 0 and 1) the base-2 LSE or Delta;
+  // query head kvh * group + g is g head strides further.
+  const uint16_t* const qhead = p.q + b * p.qs_b + (int64_t)kvh * p.group * p.qs_h;
+  const uint16_t* const ohead = p.dout + b * p.gs_b + (int64_t)kvh * p.group * p.gs_h;
+  const float* const lhead =
+      (wave == 0 ? p.lse2 : p.delta) + ((size_t)b * p.Hq + (size_t)kvh * p.group) * p.N;
+  const unsigned char* const mhead =
+      MK != kMaskNone ? (const unsigned char*)p.mask +
+                            (b * p.ms_b + (int64_t)kvh * p.group * p.ms_h) * KM::ES
+                      : nullptr;
   // One key tile: its dK and dV, sweeping the query tiles down (first tile of an item) or up.
   auto run_tile = [&](auto upc) {
     constexpr bool up = decltype(upc)::value;
@@ -685,14 +695,10 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
         goff[i] = none ? kNoChunk : (lane / G::CH) * growb + qc * 16;
       }
       auto dma = [&](int g, int q0, int buf) {
-        const int hq = kvh * p.group + g;
-        const int bh = b * p.Hq + hq;
         const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(p.q + b * p.qs_b + hq * p.qs_h), (short)0, (p.N - 1) * qrowb + 2 * DH,
-            kBufferFlags);
+            (void*)(qhead + g * p.qs_h), (short)0, (p.N - 1) * qrowb + 2 * DH, kBufferFlags);
         const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(p.dout + b * p.gs_b + hq * p.gs_h), (short)0, (p.N - 1) * growb + 2 * DH,
-            kBufferFlags);
+            (void*)(ohead + g * p.gs_h), (short)0, (p.N - 1) * growb + 2 * DH, kBufferFlags);
         unsigned char* base = smem + buf * BG::BUF;
 #pragma unroll
         for (int i = 0; i < BG::QLOADS; ++i) {
@@ -702,9 +708,8 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
           dma16(ors, base + BG::QTILE + blk * 1024, goff[i], r0 * growb);
         }
         if (wave < 2) {
-          const float* src = wave == 0 ? p.lse2 : p.delta;
           const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
-              (void*)(src + (size_t)bh * p.N), (short)0, (uint32_t)p.N * 4, kBufferFlags);
+              (void*)(lhead + (size_t)g * p.N), (short)0, (uint32_t)p.N * 4, kBufferFlags);
           // one dword per query row (lanes 0..31); a 16-byte load would straddle the end of the
           // row range when N % 4 != 0. Lanes 32..63 are out of range and write zeros to bytes
           // 128..255 of the wave's 1 KiB slot.
@@ -731,10 +736,9 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams& p) {
                                  : 0;
       auto mask_dma = [&](int g, int q0) {
         if constexpr (MK != kMaskNone) {
-          const int hq = kvh * p.group + g;
           const __amdgpu_buffer_rsrc_t mrs = __builtin_amdgcn_make_buffer_rsrc(
-              (void*)((const unsigned char*)p.mask + (b * p.ms_b + hq * p.ms_h) * KM::ES),
-              (short)0, (p.N - 1) * mrow + ((p.N * KM::ES + 15) & ~15), kBufferFlags);
+              (void*)(mhead + g * p.ms_h * KM::ES), (short)0,
+              (p.N - 1) * mrow + ((p.N * KM::ES + 15) & ~15), kBufferFlags);
 #pragma unroll
           for (int i = 0; i < KM::LOADS; ++i)
             dma16(mrs, smem + MOFF + wave * KM::WB + i * 1024, mlane,
@@ -932,7 +936,7 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t s) {
                        dim3(kThreads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if constexpr (CAUSAL && MK != kMaskAdd && D <= 128) {   // (bwd_pairs pairs no others)
+  if constexpr (CAUSAL && D <= 128) {   // (bwd_pairs pairs nothing above D = 128)
     if (p.pair)
       launch_dkdv<DT, D, true, MK, true>(p, s);
     else
@@ -999,12 +1003,12 @@ int64_t ws_floats_for(int B, int Hq, int Hkv, int N, int D, int split) {
 // its partial sums, and as far as the workspace holds them.
 // Paired dK/dV items under causal masking all take the same time, so they run in whole rounds
 // of the device's resident workgroups (256 CUs x the kernel's workgroups per CU): pair only
-// when the items fill their last round (at least 15/16 of it), up to D = 128 and without an
-// additive mask (measured on the headline shape: unmasked same time with a third of the HBM
-// bytes, keep mask -10 %, additive mask +3 %, D = 64 with 1.33 rounds +6.5 %, D = 256 in four
-// whole rounds +2.7 %).
+// when the items fill their last round (at least 15/16 of it), and up to D = 128 (measured on
+// the headline shape: unmasked the same time with a third of the HBM bytes, keep mask -10 %,
+// additive mask the same time, D = 64 with 1.33 rounds +6.5 %, D = 256 in four whole rounds
+// +2.7 %).
 int bwd_pairs(int B, int Hkv, int N, int D, int split, int mask_type) {
-  if (mask_type == ATTN_MASK_ADD || D > 128) return 0;
+  if (D > 128) return 0;
   const int64_t nkt = (N + kBM - 1) / kBM;
   const int64_t items = (int64_t)B * Hkv * ((nkt + 1) / 2) * split;
   const int per_cu = D <= 64 && mask_type == ATTN_MASK_NONE ? 3 : 2;

@@ -384,15 +384,14 @@ def test_bwd_f32_split_masked(kind):
 
 def pairs_key_tiles(case, split, mask="none"):
     """Whether the dK/dV kernel pairs key tiles i and nkt - 1 - i for this call: under causal
-    masking, up to D = 128, without an additive mask, when the pairs fill at least 15/16 of their
-    last round of resident workgroups (256 CUs x 2 or 3 per CU by head dim and mask)."""
+    masking, up to D = 128, when the pairs fill at least 15/16 of their last round of resident
+    workgroups (256 CUs x 2 or 3 per CU by head dim and mask)."""
     nkt = -(-case.N // 128)
     items = case.B * case.Hkv * ((nkt + 1) // 2) * split
     per_cu = 3 if case.D <= 64 and mask == "none" else 2
     slots = 256 * per_cu
     rounds = -(-items // slots)
-    return (bool(case.causal) and mask != "add" and case.D <= 128 and
-            items * 16 >= rounds * slots * 15)
+    return bool(case.causal) and case.D <= 128 and items * 16 >= rounds * slots * 15
 
 
 # (dtype, D, padded, B, Hq, Hkv, N, split workspace): paired dK/dV items at small N: an even
@@ -419,16 +418,18 @@ def test_bwd_paired_key_tiles(cfg):
     compare_case(case, dout, "%s paired" % (cfg,), split_ws=split_ws)
 
 
-def test_bwd_paired_key_tiles_keep_mask():
-    """Paired dK/dV items with a keep mask (random per head) on top of the causal mask."""
+@pytest.mark.parametrize("kind", ["keep", "add"])
+def test_bwd_paired_key_tiles_masked(kind):
+    """Paired dK/dV items with an explicit mask (random per head: a keep mask, or additive values
+    with -inf entries) on top of the causal mask."""
     import torch
     from gpu_util import device_mask, mask_values
     case = inputs.make_case(8, 64, 64, 256, 128, "bf16", True, False, seed=253)
-    assert pairs_key_tiles(case, 1, "keep")
+    assert pairs_key_tiles(case, 1, kind)
     dout_bits = inputs.make_grad(case, 253)
     rng = np.random.default_rng(255)
-    mv = mask_values("keep", "random_bh", "bf16", 8, 64, 256, rng)
-    dmask = device_mask("keep", "random_bh", "bf16", mv, 256)
+    mv = mask_values(kind, "random_bh", "bf16", 8, 64, 256, rng)
+    dmask = device_mask(kind, "random_bh", "bf16", mv, 256)
     q, k, v, do = (to_device(x, "bf16") for x in (case.q_bits, case.k_bits, case.v_bits,
                                                    dout_bits))
     out, lse = sdp.forward(q, k, v, causal=True, scale=case.scale, attn_mask=dmask)
@@ -437,11 +438,12 @@ def test_bwd_paired_key_tiles_keep_mask():
     torch.cuda.synchronize()
     got = [from_device(t, "bf16") for t in (dq, dk, dv)]
     qw, kw, vw = case.widened()
+    mk = {"keep_mask": mv} if kind == "keep" else {"add_mask": inputs.widen(mv, "bf16")}
     ref = oracle.attn_bwd(qw, kw, vw, inputs.widen(dout_bits, "bf16"), case.scale, True, None,
-                          keep_mask=mv)
-    e = [check_grad(n, g, r, "bf16", "paired keep mask") for n, g, r in
+                          **mk)
+    e = [check_grad(n, g, r, "bf16", "paired %s mask" % kind) for n, g, r in
          zip(("dQ", "dK", "dV"), got, ref)]
-    log("paired keep mask: rel err dQ %.2e dK %.2e dV %.2e" % tuple(e))
+    log("paired %s mask: rel err dQ %.2e dK %.2e dV %.2e" % (kind, *e))
 
 
 def test_bwd_rising_row_maximum():
