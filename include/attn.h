@@ -389,9 +389,10 @@ int attn_bwd_masked_validate(const void *q, const int64_t *q_strides, const void
 /*
  * attn_bwd_ws -- attn_bwd_masked with the workspace's size, so that the library may use more of
  * it: with room for fp32 partial sums the dK/dV kernel splits each 128-key tile's (query head,
- * query tile) iterations over up to 16 workgroups (enough for at least 1024 workgroups), and a
- * third kernel adds the parts in a fixed order (deterministic) and rounds once. This fills the
- * device where few key tiles exist (MQA, short sequences, small batches). mask_type
+ * query tile) iterations over up to 16 workgroups (enough for at least four workgroups per
+ * compute unit, 1024 on a whole MI355X), and a third kernel adds the parts in a fixed order
+ * (deterministic) and rounds once. This fills the device where few key tiles exist (MQA, short
+ * sequences, small batches). mask_type
  * ATTN_MASK_NONE (mask and mask_strides ignored) gives attn_bwd_strided; NULL strides mean
  * contiguous tensors, as there.
  *

@@ -997,12 +997,8 @@ int64_t ws_floats_for(int B, int Hq, int Hkv, int N, int D, int split) {
   return base + 4 + 2 * (int64_t)split * B * Hkv * N * D;
 }
 
-// Parts per key tile: powers of two up to 16 until there are at least 1024 dK/dV workgroups
-// (twice the 512 the device holds at once), as long as a part keeps about 32 iterations of a
-// key tile's average (half of its group * N / 32 query tiles) to pay for writing and reading
-// its partial sums, and as far as the workspace holds them.
 // Paired dK/dV items under causal masking all take the same time, so they run in whole rounds
-// of the device's resident workgroups (256 CUs x the kernel's workgroups per CU): pair only
+// of the device's resident workgroups (its CUs x the kernel's workgroups per CU): pair only
 // when the items fill their last round (at least 15/16 of it), and up to D = 128 (measured on
 // the headline shape: unmasked the same time with a third of the HBM bytes, keep mask -10 %,
 // additive mask the same time, D = 64 with 1.33 rounds +6.5 %, D = 256 in four whole rounds
@@ -1012,16 +1008,21 @@ int bwd_pairs(int B, int Hkv, int N, int D, int split, int mask_type) {
   const int64_t nkt = (N + kBM - 1) / kBM;
   const int64_t items = (int64_t)B * Hkv * ((nkt + 1) / 2) * split;
   const int per_cu = D <= 64 && mask_type == ATTN_MASK_NONE ? 3 : 2;
-  const int64_t slots = 256 * (int64_t)per_cu;
+  const int64_t slots = (int64_t)device_cus() * per_cu;
   const int64_t rounds = (items + slots - 1) / slots;
   return items * 16 >= rounds * slots * 15 ? 1 : 0;
 }
 
+// Parts per key tile: powers of two up to 16 until there are at least four dK/dV workgroups per
+// CU (twice the two the device holds at once: 1024 on a whole MI355X), as long as a part keeps
+// about 32 iterations of a key tile's average (half of its group * N / 32 query tiles) to pay
+// for writing and reading its partial sums, and as far as the workspace holds them.
 int bwd_split(int B, int Hq, int Hkv, int N, int D, int64_t ws_floats) {
   const int64_t tiles = (int64_t)B * Hkv * ((N + kBM - 1) / kBM);
   const int64_t avg_iters = (int64_t)(Hq / Hkv) * ((N + kQT - 1) / kQT) / 2;
   int split = 1;
-  while (split < 16 && tiles * split < 1024 && avg_iters / (2 * split) >= 32) split *= 2;
+  const int64_t target = 4 * (int64_t)device_cus();
+  while (split < 16 && tiles * split < target && avg_iters / (2 * split) >= 32) split *= 2;
   while (split > 1 && ws_floats_for(B, Hq, Hkv, N, D, split) > ws_floats) split /= 2;
   return split;
 }

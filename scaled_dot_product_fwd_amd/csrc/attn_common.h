@@ -1,10 +1,13 @@
 // Definitions shared by the forward (attn_fwd.hip) and backward (attn_bwd.hip) kernels for
 // CDNA4 (gfx950): vector types, tile geometry and LDS swizzles of the K/V tiles, the 32x32x16
-// MFMA wrappers, lane-pair reductions and LDS helpers. Device code only; no host state.
+// MFMA wrappers, lane-pair reductions and LDS helpers; on the host, tensor layouts, mask
+// arguments and the device's compute-unit count (the only state: one number per device).
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <atomic>
 
 #include "attn.h"
 
@@ -357,5 +360,26 @@ struct F32BwdParams {
 // mask_type an attn_mask_t.
 hipError_t launch_bwd_f32(const F32BwdParams& p, int D, bool causal, int mask_type,
                           hipStream_t stream);
+
+// Compute units of the current device: 256 on a whole MI355X, fewer on a partition of one.
+// Read once per device; 256 where no device answers (a host without one). Only the launch
+// heuristics use it (how many workgroups run at once); no result depends on it.
+inline int device_cus() {
+  static std::atomic<int> known[64];   // 0: not read yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  int n = known[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n <= 0) {
+    (void)hipGetLastError();
+    n = 256;
+  }
+  known[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
 
 }  // namespace attn_detail

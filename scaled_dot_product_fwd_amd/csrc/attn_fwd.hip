@@ -917,8 +917,9 @@ int validate(const Layout& q, const Layout& k, const Layout& v, const Layout& o,
 }
 
 // ---- split of the key range for small grids
-// Workgroups the device runs at once: two per CU (256 CUs) up to D = 128, one at D = 256.
-int resident_slots(int D) { return D > 128 ? 256 : 512; }
+// Workgroups the device runs at once: two per CU up to D = 128, one at D = 256 (512 and 256 on
+// a whole MI355X).
+int resident_slots(int D) { return (D > 128 ? 1 : 2) * device_cus(); }
 
 // Key tiles of query tile qt when every key is visible (the host cannot read valid_len).
 int tiles_of(int qt, int N, bool causal) {

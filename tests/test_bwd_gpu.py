@@ -385,7 +385,7 @@ def test_bwd_f32_split_masked(kind):
 def pairs_key_tiles(case, split, mask="none"):
     """Whether the dK/dV kernel pairs key tiles i and nkt - 1 - i for this call: under causal
     masking, up to D = 128, when the pairs fill at least 15/16 of their last round of resident
-    workgroups (256 CUs x 2 or 3 per CU by head dim and mask)."""
+    workgroups (256 CUs of a whole MI355X x 2 or 3 per CU by head dim and mask)."""
     nkt = -(-case.N // 128)
     items = case.B * case.Hkv * ((nkt + 1) // 2) * split
     per_cu = 3 if case.D <= 64 and mask == "none" else 2
